@@ -1,0 +1,407 @@
+"""fp64 reference for structured sparse causal attention (test infrastructure only).
+
+Sources, cited by page title and section:
+
+* SepLLM page ("SepLLM: Accelerate Large Language Models by Compressing One
+  Segment into One Separator"), part 五 item 2: the mask M keeps, for query i,
+  the initial ``a`` tokens, the separators before i and the ``n`` neighbouring
+  tokens; every other entry is set to -inf before the softmax.  Part 六 6.1:
+  ``O = Softmax(Q K^T / sqrt(d_k), masked by M) V``.
+* LM-Infinite page (NAACL 2024, hyper.ai summary), section 方法: the
+  Lambda-shaped set ``A_i = {j<=i : j<n_starting} U {j<=i : i-j<=L_pretrain}``;
+  the distance cap ``d'_ij = min(i-j, L_pretrain)`` inside the logit
+  ``w(q_i, k_j, d'_ij)``; and its RoPE realisation (window keys rotated as
+  usual; starting-span keys outside the window unrotated with the query
+  rotated to the fixed distance L_pretrain).
+* Segmented-execution page ("Training-Inference Consistent Segmented Execution
+  for Long-Context LLMs"), 方法详解 / 整体框架 and 关键设计: a segment attends
+  causally to [prefix | segment]; prefix positions are re-indexed to 0..P-1 and
+  the segment is shifted by P; the long-range heads' prefix is the top-k of a
+  detached pool scored by the segment-end query (forward only).
+
+Readings where the pages are silent or garbled (each is listed in the design doc):
+rotate-half RoPE with ``theta_c = base**(-2c/d)``; SepLLM neighbours are
+``0 <= i-j < w`` (the query itself included); "separator before i" includes
+j = i; masked means -inf (the printed elementwise product with M is not taken
+literally); the Lambda window keeps ``i-j <= L`` literally; softmax scale
+``1/sqrt(d)`` everywhere; GQA head h reads kv head ``h // (h_q/h_kv)``; the
+top-k score is the fp64 chain ``((0 + q0 k0) + q1 k1) + ...`` with ties to the
+lower index, and the retrieved rows keep ascending pool order.
+
+Everything is plain numpy in fp64; the only library primitives are matrix
+products, sorting and elementwise transcendental functions.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+SEPLLM, LAMBDA, SEGMENT = "sepllm", "lambda", "segment"
+TQ = 128          # queries per plan tile
+BK = 64           # keys per plan block
+FLAG_FULL = 1     # every (i, j) of tile x block is visible
+FLAG_CAPPED = 2   # some visible (i, j) of tile x block has i - j > L_pretrain
+
+__all__ = [
+    "SEPLLM", "LAMBDA", "SEGMENT", "TQ", "BK", "FLAG_FULL", "FLAG_CAPPED", "MaskSpec",
+    "visible", "capped", "key_set", "pos_q", "pos_k", "mask_rows", "rope_theta", "rotate",
+    "attention_rows", "attention_fast", "attention", "plan", "plan_items_of_tile",
+    "topk_scores", "topk_select", "pair_counts", "pair_count_total", "q0_closed_form",
+]
+
+
+@dataclasses.dataclass
+class MaskSpec:
+    """The pages' mask parameters for one sequence (shared by all heads)."""
+    mode: str
+    n_q: int
+    n_k: int
+    a: int = 0                       # SepLLM: initial tokens
+    w: int = 1                       # SepLLM: neighbouring tokens (0 <= i-j < w)
+    sep: Optional[np.ndarray] = None  # SepLLM: uint8 flags [n_k]; None = no separators
+    n_s: int = 0                     # LM-Infinite: n_starting
+    L: int = 0                       # LM-Infinite: L_pretrain
+    P: int = 0                       # segment: prefix length (n_k = P + n_q)
+
+    def sep_flags(self) -> np.ndarray:
+        if self.sep is None:
+            return np.zeros(self.n_k, dtype=np.uint8)
+        return np.asarray(self.sep, dtype=np.uint8)
+
+
+# ----------------------------------------------------------------------------
+# Key sets and positions
+# ----------------------------------------------------------------------------
+
+def visible(spec: MaskSpec, i, j) -> np.ndarray:
+    """Element-wise membership ``j in A_i`` (arrays broadcast).
+
+    SepLLM (part 五 item 2): ``j <= i and (j < a or i-j < w or sep[j])``.
+    LM-Infinite (方法, Lambda mask): ``j <= i and (j < n_starting or i-j <= L)``.
+    Segment (整体框架): the prefix is fully visible and the segment causal,
+    i.e. ``j <= P + i`` over keys ``[prefix | segment]``.
+    """
+    i = np.asarray(i, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
+    inside = (i >= 0) & (i < spec.n_q) & (j >= 0) & (j < spec.n_k)
+    if spec.mode == SEPLLM:
+        flags = spec.sep_flags()
+        sep_j = flags[np.clip(j, 0, spec.n_k - 1)] == 1
+        return inside & (j <= i) & ((j < spec.a) | (i - j < spec.w) | sep_j)
+    if spec.mode == LAMBDA:
+        return inside & (j <= i) & ((j < spec.n_s) | (i - j <= spec.L))
+    if spec.mode == SEGMENT:
+        return inside & (j <= spec.P + i)
+    raise ValueError(spec.mode)
+
+
+def capped(spec: MaskSpec, i, j) -> np.ndarray:
+    """Visible pairs whose distance is capped: ``i - j > L`` (LM-Infinite only)."""
+    if spec.mode != LAMBDA:
+        return np.zeros(np.broadcast(np.asarray(i), np.asarray(j)).shape, dtype=bool)
+    i = np.asarray(i, dtype=np.int64)
+    j = np.asarray(j, dtype=np.int64)
+    return visible(spec, i, j) & (i - j > spec.L)
+
+
+def key_set(spec: MaskSpec, i: int) -> np.ndarray:
+    """Ascending key indices of ``A_i``, evaluated element by element."""
+    return np.flatnonzero(visible(spec, i, np.arange(spec.n_k)))
+
+
+def pos_q(spec: MaskSpec, i):
+    """RoPE position of query i: i, or P + i for a segment (segment shifted by P)."""
+    return np.asarray(i, dtype=np.int64) + (spec.P if spec.mode == SEGMENT else 0)
+
+
+def pos_k(spec: MaskSpec, j):
+    """RoPE position of key j: its index (prefix re-indexed to 0..P-1 in segment mode)."""
+    return np.asarray(j, dtype=np.int64)
+
+
+def mask_rows(spec: MaskSpec, rows: Sequence[int]) -> np.ndarray:
+    """bool [len(rows), n_k]: the visible keys of each listed query."""
+    rows = np.asarray(rows, dtype=np.int64)
+    return visible(spec, rows[:, None], np.arange(spec.n_k)[None, :])
+
+
+# ----------------------------------------------------------------------------
+# Rotary position embedding (rotate-half pairing, fp64)
+# ----------------------------------------------------------------------------
+
+def rope_theta(d: int, base: float) -> np.ndarray:
+    """Frequencies ``theta_c = base ** (-2c/d)`` for c = 0 .. d/2-1 (fp64)."""
+    c = np.arange(d // 2, dtype=np.float64)
+    return np.power(np.float64(base), -2.0 * c / d)
+
+
+def rotate(x: np.ndarray, angle: np.ndarray) -> np.ndarray:
+    """Rotate each pair (x[c], x[c+d/2]) by ``angle[..., c]`` (counter-clockwise)."""
+    h = x.shape[-1] // 2
+    x1, x2 = x[..., :h], x[..., h:]
+    cs, sn = np.cos(angle), np.sin(angle)
+    return np.concatenate([x1 * cs - x2 * sn, x2 * cs + x1 * sn], axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# Attention, definition mode: one query row at a time, relative rotation per pair
+# ----------------------------------------------------------------------------
+
+def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: Sequence[int],
+                   spec: MaskSpec, rope_base: Optional[float], scale: float):
+    """Masked softmax attention for the listed query rows of one head.
+
+    q [n_q, d], k and v [n_k, d] (fp64).  For every key j in A_i the logit is
+    ``scale * <Rot(delta) q_i, k_j>`` with ``delta = pos_q(i) - pos_k(j)``
+    (LM-Infinite: ``delta' = min(delta, L)``), i.e. the page's
+    ``w(q_i, k_j, d'_ij)`` for RoPE.  Masked keys take no part (-inf logit).
+    Returns O [len(rows), d] and the natural-log LSE [len(rows)].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d = q.shape[1]
+    theta = rope_theta(d, rope_base) if rope_base else None
+    O = np.zeros((len(rows), v.shape[1]))
+    lse = np.zeros(len(rows))
+    for r, i in enumerate(rows):
+        A = key_set(spec, int(i))
+        if theta is None:
+            s = k[A] @ q[i]
+        else:
+            delta = pos_q(spec, int(i)) - pos_k(spec, A)
+            if spec.mode == LAMBDA:
+                delta = np.minimum(delta, spec.L)
+            ang = delta.astype(np.float64)[:, None] * theta[None, :]
+            qr = rotate(np.broadcast_to(q[i], (len(A), d)), ang)
+            s = np.einsum("jd,jd->j", qr, k[A])
+        s = s * scale
+        mu = s.max()
+        e = np.exp(s - mu)
+        z = e.sum()
+        O[r] = (e @ v[A]) / z
+        lse[r] = mu + math.log(z)
+    return O, lse
+
+
+# ----------------------------------------------------------------------------
+# Attention, fast mode: absolute rotations, one query tile at a time
+# ----------------------------------------------------------------------------
+
+def attention_fast(q: np.ndarray, k: np.ndarray, v: np.ndarray, spec: MaskSpec,
+                   rope_base: Optional[float], scale: float,
+                   row_blocks: Optional[Sequence[Sequence[int]]] = None):
+    """Same result as :func:`attention_rows`, computed tile-wise for speed.
+
+    q and k are rotated once at their absolute positions, using
+    ``<R(a) q, R(b) k> = <R(a-b) q, k>``; capped LM-Infinite pairs use the
+    page's realisation ``<R(L) q_i, k_j>`` with the raw key.  Each block of
+    query rows takes the union of its visible keys, a dense product, the mask
+    (-inf), then the softmax.  ``row_blocks`` defaults to consecutive groups
+    of 128 rows.  Returns (O, LSE) for the rows covered, in order.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    n_q, d = q.shape
+    if row_blocks is None:
+        row_blocks = [np.arange(s, min(n_q, s + TQ)) for s in range(0, n_q, TQ)]
+    if rope_base:
+        theta = rope_theta(d, rope_base)
+        kr = rotate(k, pos_k(spec, np.arange(spec.n_k)).astype(np.float64)[:, None] * theta[None, :])
+    outs, lses = [], []
+    for rows in row_blocks:
+        rows = np.asarray(rows, dtype=np.int64)
+        M = mask_rows(spec, rows)
+        U = np.flatnonzero(M.any(axis=0))
+        Mu = M[:, U]
+        if rope_base:
+            qr = rotate(q[rows], pos_q(spec, rows).astype(np.float64)[:, None] * theta[None, :])
+            S = qr @ kr[U].T
+            if spec.mode == LAMBDA:
+                C = capped(spec, rows[:, None], U[None, :])
+                if C.any():
+                    qcap = rotate(q[rows], float(spec.L) * theta[None, :])
+                    S = np.where(C, qcap @ k[U].T, S)
+        else:
+            S = q[rows] @ k[U].T
+        S = S * scale
+        S = np.where(Mu, S, -np.inf)
+        mu = S.max(axis=1)
+        E = np.exp(S - mu[:, None])
+        z = E.sum(axis=1)
+        outs.append((E @ v[U]) / z[:, None])
+        lses.append(mu + np.log(z))
+    return np.concatenate(outs, axis=0), np.concatenate(lses, axis=0)
+
+
+def attention(Q, K, V, spec: MaskSpec, rope_base: Optional[float], scale: float,
+              heads: Optional[Sequence[int]] = None, rows: Optional[Sequence[int]] = None,
+              mode: str = "fast"):
+    """Multi-head wrapper: Q [h_q, n_q, d], K and V [h_kv, n_k, d] (batch squeezed).
+
+    Query head h reads kv head ``h // (h_q // h_kv)``.  ``rows`` restricts the
+    query rows (definition mode evaluates them one by one; fast mode groups
+    them 128 at a time).  Returns O [len(heads), len(rows), d], LSE [..].
+    """
+    h_q, h_kv = Q.shape[0], K.shape[0]
+    group = h_q // h_kv
+    heads = list(range(h_q)) if heads is None else list(heads)
+    rows = np.arange(Q.shape[1]) if rows is None else np.asarray(rows)
+    Os, Ls = [], []
+    for h in heads:
+        g = h // group
+        if mode == "definition":
+            o, l = attention_rows(Q[h], K[g], V[g], rows, spec, rope_base, scale)
+        else:
+            blocks = [rows[s:s + TQ] for s in range(0, len(rows), TQ)]
+            o, l = attention_fast(Q[h], K[g], V[g], spec, rope_base, scale, blocks)
+        Os.append(o)
+        Ls.append(l)
+    return np.stack(Os), np.stack(Ls)
+
+
+# ----------------------------------------------------------------------------
+# Plan: per 128-query tile, the 64-key blocks to visit and the separators to gather
+# ----------------------------------------------------------------------------
+
+def plan_items_of_tile(spec: MaskSpec, t: int) -> List[int]:
+    """Encoded items ``block | flags << 24`` of tile t, from the predicates.
+
+    Candidate blocks: SepLLM visits the sink blocks ``b < ceil(a/64)`` and the
+    blocks from ``floor(win_lo/64)`` on, where ``win_lo = max(0, q0-w+1)``
+    (keys in between are reached through the gathered separator list);
+    LM-Infinite and segment mode consider every block.  A candidate is kept
+    when some (i, j) of tile x block is visible; FULL when all are (and the
+    block has 64 keys); CAPPED when some visible pair has i - j > L.
+    """
+    n_q, n_k = spec.n_q, spec.n_k
+    n_blocks = -(-n_k // BK)
+    q0 = TQ * t
+    q1 = min(n_q, q0 + TQ) - 1
+    rows = np.arange(q0, q1 + 1, dtype=np.int64)
+    if spec.mode == SEPLLM:
+        nsb = -(-spec.a // BK)
+        win_lo = max(0, q0 - spec.w + 1)
+        cands = sorted(set(range(min(nsb, n_blocks))) | set(range(win_lo // BK, n_blocks)))
+    else:
+        cands = list(range(n_blocks))
+    out = []
+    for b in cands:
+        j = np.arange(BK * b, min(n_k, BK * b + BK), dtype=np.int64)
+        vis = visible(spec, rows[:, None], j[None, :])
+        if not vis.any():
+            continue
+        flags = 0
+        if BK * b + BK <= n_k and vis.all():
+            flags |= FLAG_FULL
+        if spec.mode == LAMBDA and (vis & (rows[:, None] - j[None, :] > spec.L)).any():
+            flags |= FLAG_CAPPED
+        out.append(b | (flags << 24))
+    return out
+
+
+def plan(spec: MaskSpec) -> Dict[str, np.ndarray]:
+    """The plan the GPU must reproduce bit for bit.
+
+    Returns tile_ptr int32 [n_tiles+1] (CSR into items), items int32,
+    sep_count int32 [n_tiles], sep_idx int32 [n_sep] (ascending separator
+    positions j >= g0 = 64*ceil(a/64)), sep_bits uint64 [n_blocks] (bit r of
+    word b is sep[64b+r]).  ``sep_count[t]`` counts the separators in
+    ``[g0, gh)`` with ``gh = 64*floor(win_lo/64)``; every such key precedes
+    and lies outside the window of every query of the tile, so it is visible
+    to all of them exactly when it is a separator.
+    """
+    n_q, n_k = spec.n_q, spec.n_k
+    n_tiles = -(-n_q // TQ)
+    n_blocks = -(-n_k // BK)
+    tile_ptr = [0]
+    items: List[int] = []
+    sep_count = np.zeros(n_tiles, dtype=np.int32)
+    sep_bits = np.zeros(n_blocks, dtype=np.uint64)
+    sep_idx = np.zeros(0, dtype=np.int32)
+    if spec.mode == SEPLLM:
+        flags = spec.sep_flags()
+        g0 = BK * (-(-spec.a // BK))
+        sep_idx = np.array([j for j in range(g0, n_k) if flags[j] == 1], dtype=np.int32)
+        for b in range(n_blocks):
+            word = 0
+            for r in range(BK):
+                if BK * b + r < n_k and flags[BK * b + r] == 1:
+                    word |= 1 << r
+            sep_bits[b] = np.uint64(word)
+    for t in range(n_tiles):
+        it = plan_items_of_tile(spec, t)
+        items.extend(it)
+        tile_ptr.append(len(items))
+        if spec.mode == SEPLLM:
+            q0 = TQ * t
+            win_lo = max(0, q0 - spec.w + 1)
+            gh = BK * (win_lo // BK)
+            g0 = BK * (-(-spec.a // BK))
+            sep_count[t] = int(np.count_nonzero(sep_idx < gh)) if gh > g0 else 0
+    return {
+        "n_tiles": n_tiles, "n_blocks": n_blocks,
+        "tile_ptr": np.array(tile_ptr, dtype=np.int32),
+        "items": np.array(items, dtype=np.int32),
+        "sep_count": sep_count,
+        "sep_idx": sep_idx,
+        "sep_bits": sep_bits,
+    }
+
+
+# ----------------------------------------------------------------------------
+# Top-k retrieval of the prefix (segmented execution, long-range heads)
+# ----------------------------------------------------------------------------
+
+def topk_scores(q: np.ndarray, pool_k: np.ndarray) -> np.ndarray:
+    """fp64 scores ``s_j = ((0 + q_0 k_j0) + q_1 k_j1) + ... + q_{d-1} k_j,d-1``.
+
+    Inputs are bf16 or fp32 values upcast to fp64, so every product is exact
+    and each step is one round-to-nearest addition (the same as an fma).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    pool_k = np.asarray(pool_k, dtype=np.float64)
+    s = np.zeros(pool_k.shape[0], dtype=np.float64)
+    for c in range(q.shape[0]):
+        s = s + q[c] * pool_k[:, c]
+    return s
+
+
+def topk_select(scores: np.ndarray, k: int) -> np.ndarray:
+    """The k largest scores, ties to the lower index, returned in ascending index order."""
+    n = scores.shape[0]
+    order = np.lexsort((np.arange(n), -scores))
+    return np.sort(order[:k]).astype(np.int32)
+
+
+# ----------------------------------------------------------------------------
+# Counts and closed forms used by the measurement and the pins
+# ----------------------------------------------------------------------------
+
+def pair_counts(spec: MaskSpec) -> np.ndarray:
+    """|A_i| for every query i (int64), from the predicates."""
+    out = np.zeros(spec.n_q, dtype=np.int64)
+    for s in range(0, spec.n_q, TQ):
+        rows = np.arange(s, min(spec.n_q, s + TQ))
+        out[rows] = mask_rows(spec, rows).sum(axis=1)
+    return out
+
+
+def pair_count_total(spec: MaskSpec) -> int:
+    return int(pair_counts(spec).sum())
+
+
+def q0_closed_form(v: np.ndarray, spec: MaskSpec, rows: Sequence[int]):
+    """With Q = 0 every visible logit is 0: O_i = mean of v_j over A_i, LSE_i = ln |A_i|."""
+    v = np.asarray(v, dtype=np.float64)
+    O = np.zeros((len(rows), v.shape[1]))
+    lse = np.zeros(len(rows))
+    for r, i in enumerate(rows):
+        A = key_set(spec, int(i))
+        O[r] = v[A].mean(axis=0)
+        lse[r] = math.log(len(A))
+    return O, lse
