@@ -1,0 +1,201 @@
+/*
+ * sparse_attn.h -- C ABI of libsparse_attn.so: causal attention restricted to a
+ * structured sparse key set, for AMD Instinct MI355X (gfx950).
+ *
+ * For each query i the visible keys A_i are
+ *   SepLLM      j <= i and (j < a  or  0 <= i-j < w  or  sep[j] = 1)
+ *               (SepLLM page, part 5 item 2: initial a, separators before i,
+ *               n neighbouring tokens; masked logits are -inf, part 6.1);
+ *   LM-Infinite j <= i and (j < n_starting  or  i-j <= L_pretrain)
+ *               (LM-Infinite page, section "method", Lambda-shaped mask), with
+ *               the logit taken at the capped distance min(i-j, L_pretrain);
+ *   segment     keys are [prefix P | segment]; query i sees j <= P + i, RoPE
+ *               positions 0..P-1 for the prefix and P+i for query i
+ *               (segmented-execution page, method / overall framework).
+ * Logits are scale * <R(pos_q) q_i, R(pos_k) k_j> with rotate-half RoPE,
+ * theta_c = base^(-2c/d); output O_i = softmax over A_i of the logits times V.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or keeps a pointer after the call returns.
+ *  - Work is enqueued on the given stream (0 = the null stream) and is
+ *    asynchronous; results are ready after the caller synchronises the stream.
+ *  - Every argument is checked on the host before anything is launched.  On a
+ *    bad argument the call returns SA_EINVAL / SA_EUNSUPPORTED / SA_ENOSPACE,
+ *    launches nothing and sets a message readable with sa_last_error().
+ *    A failed launch returns SA_EHIP.  Device faults surface at the caller's
+ *    next synchronisation.
+ *  - Calls are thread-safe; the only global state is the per-thread message.
+ *  - Code objects are built for gfx950 only; on another device the calls that
+ *    launch work return SA_EUNSUPPORTED.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum { SA_OK = 0, SA_EINVAL = -1, SA_EUNSUPPORTED = -2, SA_ENOSPACE = -3, SA_EHIP = -4 };
+enum { SA_MASK_SEPLLM = 0, SA_MASK_LAMBDA = 1, SA_MASK_SEGMENT = 2 };
+enum { SA_F32 = 0, SA_BF16 = 1 };
+enum { SA_ROPE_NONE = 0, SA_ROPE_HALF = 1 };
+
+/* Plan geometry: 128-query tiles, 64-key blocks. */
+enum { SA_TQ = 128, SA_BK = 64 };
+/* Item flags (bits 24..31 of an item; bits 0..23 hold the block index). */
+enum { SA_ITEM_FULL = 1, SA_ITEM_CAPPED = 2 };
+
+/*
+ * The pages' mask parameters for one sequence; shared by every head, layer
+ * and batch row that uses the same plan.
+ *   kind        SA_MASK_*.
+ *   n_q, n_k    query and key counts.  SEPLLM / LAMBDA: n_q == n_k (= m).
+ *               SEGMENT: n_k == prefix_len + n_q.  1 <= n_q, n_k < 2^24 * 64.
+ *   a, w        SEPLLM: initial tokens a >= 0, neighbours w >= 1 (the query
+ *               itself counts as a neighbour).
+ *   sep         SEPLLM: device uint8 [n_k], nonzero = separator; NULL = none.
+ *   n_starting  LAMBDA: starting span >= 0.
+ *   L_pretrain  LAMBDA: window i-j <= L_pretrain and distance cap, >= 0.
+ *   prefix_len  SEGMENT: P >= 0.
+ * Fields that do not belong to `kind` are ignored.
+ */
+typedef struct {
+  int32_t kind;
+  int32_t n_q, n_k;
+  int32_t a, w;
+  const uint8_t *sep;
+  int32_t n_starting, L_pretrain;
+  int32_t prefix_len;
+} sa_mask_t;
+
+/*
+ * Plan buffer layout (a POD byte buffer built on the device by
+ * sparse_attn_plan; it holds offsets, never pointers).  The section offsets
+ * are a function of the mask scalars only and are reported by
+ * sa_plan_layout(); the header at offset 0 repeats them and adds the
+ * data-dependent counts.
+ *   tile_ptr  int32 [n_tiles+1]   CSR offsets of each tile's items
+ *   items     int32 [cap_items]   block | flags << 24, ascending per tile
+ *   sep_count int32 [n_tiles]     separators gathered by tile t: those in
+ *                                 [g0, 64*floor(max(0,q0-w+1)/64)), g0 = 64*ceil(a/64)
+ *   sep_idx   int32 [cap_sep]     ascending positions j >= g0 with sep[j] != 0
+ *   sep_bits  uint64 [n_blocks]   bit r of word b = (sep[64b+r] != 0)
+ *   blk_sep   int32 [n_blocks+1]  separators (j >= g0) before block b
+ * LAMBDA and SEGMENT plans have sep_count, sep_bits and blk_sep all zero.
+ */
+typedef struct {
+  uint32_t magic;        /* 0x31504153 'SAP1' */
+  int32_t version;       /* 1 */
+  int32_t kind, tq, bk, n_q, n_k, n_tiles, n_blocks;
+  int32_t n_items;       /* written by the device */
+  int32_t n_sep;         /* written by the device */
+  int32_t g0, cap_items, cap_sep, max_items_per_tile, reserved;
+  int64_t off_tile_ptr, off_items, off_sep_count, off_sep_idx, off_sep_bits, off_blk_sep;
+  int64_t total_bytes;
+} sa_plan_header_t;
+
+/*
+ * Forward arguments.  Tensors are [batch, heads, tokens, d] with the last
+ * dimension contiguous; *_stride give the element strides of the batch, head
+ * and token dimensions.
+ *   dtype       SA_F32 or SA_BF16 for q, k, v and o.
+ *   d           head dimension: 128 (bf16 and f32) or 64 (f32).
+ *   h_q, h_kv   h_q % h_kv == 0; query head h reads kv head h / (h_q/h_kv).
+ *   rope        SA_ROPE_NONE or SA_ROPE_HALF (rotate-half, theta_c = base^(-2c/d)).
+ *   scale       logit scale, normally 1/sqrt(d).
+ *   q           [batch, h_q, n_q, d] raw (unrotated) queries.
+ *   k, v        [batch, h_kv, n_k, d] raw keys and values.
+ *   o           [batch, h_q, n_q, d] output (written).
+ *   lse         optional fp32 [batch, h_q, n_q] contiguous natural-log
+ *               log-sum-exp of the scaled logits; NULL = not written.
+ */
+typedef struct {
+  int32_t dtype;
+  int32_t batch, h_q, h_kv, d;
+  int32_t rope;
+  float rope_base;
+  float scale;
+  const void *q; int64_t q_stride[3];
+  const void *k; int64_t k_stride[3];
+  const void *v; int64_t v_stride[3];
+  void *o; int64_t o_stride[3];
+  float *lse;
+} sa_fwd_args_t;
+
+/* Message of the last failed call on this thread ("" if none); never NULL. */
+const char *sa_last_error(void);
+
+/* Host only: section offsets and capacities of the plan for mask m. */
+int sa_plan_layout(const sa_mask_t *m, sa_plan_header_t *layout);
+
+/* Host only: bytes a plan buffer for mask m needs. */
+int sa_plan_bytes(const sa_mask_t *m, size_t *bytes);
+
+/*
+ * Build the plan for mask m into the device buffer `plan` (plan_bytes >=
+ * sa_plan_bytes).  Per 128-query tile it lists the 64-key blocks holding a
+ * visible pair (sink blocks and window blocks for SepLLM; every such block
+ * for LAMBDA and SEGMENT) with FULL / CAPPED flags, and for SepLLM the
+ * compacted separator list each tile gathers instead of visiting the blocks
+ * between its sinks and its window (SepLLM page, part 5 item 2 and part 6.2:
+ * only the kept entries of Q K^T are computed).  The plan depends on the mask
+ * only and serves every head and layer.  Errors: SA_EINVAL (bad mask, NULL
+ * plan), SA_ENOSPACE (plan_bytes too small), SA_EHIP.
+ */
+int sparse_attn_plan(const sa_mask_t *m, void *plan, size_t plan_bytes, hipStream_t stream);
+
+/* Host only: bytes of device workspace sparse_attn_fwd needs for (m, args). */
+int sa_fwd_workspace_bytes(const sa_mask_t *m, const sa_fwd_args_t *args, size_t *bytes);
+
+/*
+ * Sparse attention forward for every batch row and head: a RoPE stage
+ * (queries at pos_q, keys at pos_k, the LM-Infinite capped keys R(-L) k_j for
+ * j < n_starting, and the SepLLM separator rows gathered), then the fused
+ * forward over the plan's live blocks only (online softmax in fp32).  `plan`
+ * must have been built for the same mask on this stream (or be complete).
+ * ws: device workspace of ws_bytes >= sa_fwd_workspace_bytes; its contents
+ * are scratch.  Errors: SA_EINVAL, SA_EUNSUPPORTED (dtype/d/device),
+ * SA_ENOSPACE (plan or workspace too small), SA_EHIP.
+ */
+int sparse_attn_fwd(const sa_mask_t *m, const void *plan, size_t plan_bytes,
+                    const sa_fwd_args_t *args, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Host only: bytes of device workspace topk_retrieve needs. */
+int sa_topk_workspace_bytes(int32_t n_heads, int32_t pool_len, size_t *bytes);
+
+/*
+ * Forward-only top-k retrieval of the prefix (segmented-execution page, key
+ * design 3: the segment-end query picks R keys of a detached read-only pool
+ * for the long-range heads).  For each head h < n_heads:
+ *   s_j = ((0 + q_0 k_j0) + q_1 k_j1) + ... + q_{d-1} k_{j,d-1}  in fp64 (every
+ *   product of bf16/fp32 inputs is exact), j < pool_len;
+ *   idx[h, 0..k-1] = the k largest s_j, ties to the smaller j, in ascending j.
+ * Arguments:
+ *   dtype        SA_F32 or SA_BF16 for q_score, pool_k, pool_v, pref_k, pref_v.
+ *   q_score      row h at q_score + h*q_head_stride elements, d contiguous (raw).
+ *   pool_k       row j of head h at pool_k + h*pool_head_stride + j*pool_row_stride.
+ *   pool_v       same strides; NULL = no gather.
+ *   idx          out int32 [n_heads, k] contiguous.
+ *   score        out fp64 [n_heads, k] contiguous (s at idx), or NULL.
+ *   pref_k/v     if pool_v != NULL: pool rows idx[h, r] are copied to row r of
+ *                head h at pref_* + h*pref_head_stride + r*pref_row_stride.
+ *   ws           device workspace of ws_bytes >= sa_topk_workspace_bytes.
+ * Limits: 1 <= k <= pool_len, d in {64, 128}.  Errors as above.
+ */
+int topk_retrieve(int32_t dtype, int32_t n_heads, int32_t pool_len, int32_t d, int32_t k,
+                  const void *q_score, int64_t q_head_stride,
+                  const void *pool_k, const void *pool_v,
+                  int64_t pool_head_stride, int64_t pool_row_stride,
+                  int32_t *idx, double *score,
+                  void *pref_k, void *pref_v, int64_t pref_head_stride, int64_t pref_row_stride,
+                  void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPARSE_ATTN_H */

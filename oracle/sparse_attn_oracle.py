@@ -271,36 +271,39 @@ def attention(Q, K, V, spec: MaskSpec, rope_base: Optional[float], scale: float,
 def plan_items_of_tile(spec: MaskSpec, t: int) -> List[int]:
     """Encoded items ``block | flags << 24`` of tile t, from the predicates.
 
-    Candidate blocks: SepLLM visits the sink blocks ``b < ceil(a/64)`` and the
-    blocks from ``floor(win_lo/64)`` on, where ``win_lo = max(0, q0-w+1)``
-    (keys in between are reached through the gathered separator list);
-    LM-Infinite and segment mode consider every block.  A candidate is kept
+    Candidate blocks hold a key ``j <= q1`` (``j <= P + q1`` for a segment).
+    SepLLM only visits the sink blocks ``b < ceil(a/64)`` and the blocks from
+    ``floor(win_lo/64)`` on, where ``win_lo = max(0, q0-w+1)``: keys in between
+    are reached through the gathered separator list.  A candidate is kept
     when some (i, j) of tile x block is visible; FULL when all are (and the
     block has 64 keys); CAPPED when some visible pair has i - j > L.
     """
     n_q, n_k = spec.n_q, spec.n_k
-    n_blocks = -(-n_k // BK)
     q0 = TQ * t
     q1 = min(n_q, q0 + TQ) - 1
     rows = np.arange(q0, q1 + 1, dtype=np.int64)
+    last_key = min(n_k - 1, q1 + (spec.P if spec.mode == SEGMENT else 0))
+    last_blk = last_key // BK
     if spec.mode == SEPLLM:
         nsb = -(-spec.a // BK)
         win_lo = max(0, q0 - spec.w + 1)
-        cands = sorted(set(range(min(nsb, n_blocks))) | set(range(win_lo // BK, n_blocks)))
+        cands = sorted(set(range(min(nsb, last_blk + 1))) | set(range(win_lo // BK, last_blk + 1)))
     else:
-        cands = list(range(n_blocks))
+        cands = list(range(last_blk + 1))
+    cands = np.array(cands, dtype=np.int64)
+    # all candidate keys at once: [rows, candidates, 64]
+    j = cands[:, None] * BK + np.arange(BK)[None, :]
+    vis = visible(spec, rows[:, None, None], j[None, :, :])
+    live = vis.any(axis=(0, 2))
+    full = vis.all(axis=(0, 2)) & (cands * BK + BK <= n_k)
+    if spec.mode == LAMBDA:
+        cap = (vis & (rows[:, None, None] - j[None, :, :] > spec.L)).any(axis=(0, 2))
+    else:
+        cap = np.zeros(len(cands), dtype=bool)
     out = []
-    for b in cands:
-        j = np.arange(BK * b, min(n_k, BK * b + BK), dtype=np.int64)
-        vis = visible(spec, rows[:, None], j[None, :])
-        if not vis.any():
-            continue
-        flags = 0
-        if BK * b + BK <= n_k and vis.all():
-            flags |= FLAG_FULL
-        if spec.mode == LAMBDA and (vis & (rows[:, None] - j[None, :] > spec.L)).any():
-            flags |= FLAG_CAPPED
-        out.append(b | (flags << 24))
+    for b, lv, fl, cp in zip(cands.tolist(), live, full, cap):
+        if lv:
+            out.append(b | ((FLAG_FULL if fl else 0) | (FLAG_CAPPED if cp else 0)) << 24)
     return out
 
 

@@ -1,0 +1,200 @@
+"""Python binding of libsparse_attn.so (ctypes; argument marshalling only).
+
+The functions below carry the C ABI's names and call it directly; every step
+of the computation runs in the library's HIP kernels.  torch tensors supply
+device memory and the current HIP stream.  Importing this module fails loudly
+when the library has not been built: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m structured_sparse_attention_attn_amd.build` "
+        "(the sparse attention path has no fallback)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ENOSPACE, SA_EHIP = 0, -1, -2, -3, -4
+SA_MASK_SEPLLM, SA_MASK_LAMBDA, SA_MASK_SEGMENT = 0, 1, 2
+SA_F32, SA_BF16 = 0, 1
+SA_ROPE_NONE, SA_ROPE_HALF = 0, 1
+SA_TQ, SA_BK = 128, 64
+SA_ITEM_FULL, SA_ITEM_CAPPED = 1, 2
+
+_i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class sa_mask_t(ctypes.Structure):
+    _fields_ = [("kind", _i32), ("n_q", _i32), ("n_k", _i32), ("a", _i32), ("w", _i32),
+                ("sep", _vp), ("n_starting", _i32), ("L_pretrain", _i32), ("prefix_len", _i32)]
+
+
+class sa_plan_header_t(ctypes.Structure):
+    _fields_ = [("magic", ctypes.c_uint32), ("version", _i32), ("kind", _i32), ("tq", _i32),
+                ("bk", _i32), ("n_q", _i32), ("n_k", _i32), ("n_tiles", _i32), ("n_blocks", _i32),
+                ("n_items", _i32), ("n_sep", _i32), ("g0", _i32), ("cap_items", _i32),
+                ("cap_sep", _i32), ("max_items_per_tile", _i32), ("reserved", _i32),
+                ("off_tile_ptr", _i64), ("off_items", _i64), ("off_sep_count", _i64),
+                ("off_sep_idx", _i64), ("off_sep_bits", _i64), ("off_blk_sep", _i64),
+                ("total_bytes", _i64)]
+
+
+class sa_fwd_args_t(ctypes.Structure):
+    _fields_ = [("dtype", _i32), ("batch", _i32), ("h_q", _i32), ("h_kv", _i32), ("d", _i32),
+                ("rope", _i32), ("rope_base", _f32), ("scale", _f32),
+                ("q", _vp), ("q_stride", _i64 * 3), ("k", _vp), ("k_stride", _i64 * 3),
+                ("v", _vp), ("v_stride", _i64 * 3), ("o", _vp), ("o_stride", _i64 * 3),
+                ("lse", _vp)]
+
+
+_MASKP = ctypes.POINTER(sa_mask_t)
+_ARGSP = ctypes.POINTER(sa_fwd_args_t)
+_lib.sa_last_error.restype = ctypes.c_char_p
+_lib.sa_last_error.argtypes = []
+_lib.sa_plan_layout.argtypes = [_MASKP, ctypes.POINTER(sa_plan_header_t)]
+_lib.sa_plan_bytes.argtypes = [_MASKP, ctypes.POINTER(_sz)]
+_lib.sparse_attn_plan.argtypes = [_MASKP, _vp, _sz, _vp]
+_lib.sa_fwd_workspace_bytes.argtypes = [_MASKP, _ARGSP, ctypes.POINTER(_sz)]
+_lib.sparse_attn_fwd.argtypes = [_MASKP, _vp, _sz, _ARGSP, _vp, _sz, _vp]
+_lib.sa_topk_workspace_bytes.argtypes = [_i32, _i32, ctypes.POINTER(_sz)]
+_lib.topk_retrieve.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp, _i64, _i64,
+                               _vp, _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]
+for _name in ("sa_plan_layout", "sa_plan_bytes", "sparse_attn_plan", "sa_fwd_workspace_bytes",
+              "sparse_attn_fwd", "sa_topk_workspace_bytes", "topk_retrieve"):
+    getattr(_lib, _name).restype = ctypes.c_int
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def _check(code: int) -> None:
+    if code != SA_OK:
+        raise SparseAttnError(code, sa_last_error())
+
+
+def sa_last_error() -> str:
+    return _lib.sa_last_error().decode()
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def mask(kind: int, n_q: int, n_k: int, *, a: int = 0, w: int = 1, sep=None, n_starting: int = 0,
+         L_pretrain: int = 0, prefix_len: int = 0) -> sa_mask_t:
+    """Build an sa_mask_t; `sep` is a device uint8 tensor [n_k] (kept alive by the caller)."""
+    return sa_mask_t(kind, n_q, n_k, a, w, _ptr(sep), n_starting, L_pretrain, prefix_len)
+
+
+def sa_plan_layout(m: sa_mask_t) -> sa_plan_header_t:
+    out = sa_plan_header_t()
+    _check(_lib.sa_plan_layout(ctypes.byref(m), ctypes.byref(out)))
+    return out
+
+
+def sa_plan_bytes(m: sa_mask_t) -> int:
+    out = _sz()
+    _check(_lib.sa_plan_bytes(ctypes.byref(m), ctypes.byref(out)))
+    return out.value
+
+
+def sparse_attn_plan(m: sa_mask_t, plan, stream=None) -> None:
+    """Enqueue the plan kernels for mask m into the uint8 device tensor `plan`."""
+    _check(_lib.sparse_attn_plan(ctypes.byref(m), _ptr(plan), plan.numel(), _stream(stream)))
+
+
+def fwd_args(q, k, v, o, *, lse=None, rope_base: Optional[float] = None,
+             scale: Optional[float] = None) -> sa_fwd_args_t:
+    """sa_fwd_args_t for [B,H,T,d] tensors (last dimension contiguous)."""
+    import torch
+    dtype = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}[q.dtype]
+    B, h_q, _, d = q.shape
+    h_kv = k.shape[1]
+    a = sa_fwd_args_t()
+    a.dtype, a.batch, a.h_q, a.h_kv, a.d = dtype, B, h_q, h_kv, d
+    a.rope = SA_ROPE_HALF if rope_base else SA_ROPE_NONE
+    a.rope_base = float(rope_base or 0.0)
+    a.scale = float(scale if scale is not None else d ** -0.5)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name}: last dimension must be contiguous")
+        setattr(a, name, t.data_ptr())
+        getattr(a, name + "_stride")[:] = list(t.stride()[:3])
+    a.lse = _ptr(lse)
+    return a
+
+
+def sa_fwd_workspace_bytes(m: sa_mask_t, args: sa_fwd_args_t) -> int:
+    out = _sz()
+    _check(_lib.sa_fwd_workspace_bytes(ctypes.byref(m), ctypes.byref(args), ctypes.byref(out)))
+    return out.value
+
+
+def sparse_attn_fwd(m: sa_mask_t, plan, args: sa_fwd_args_t, ws, stream=None) -> None:
+    """Enqueue the RoPE stage and the fused forward (see include/sparse_attn.h)."""
+    _check(_lib.sparse_attn_fwd(ctypes.byref(m), _ptr(plan), plan.numel(), ctypes.byref(args),
+                                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                _stream(stream)))
+
+
+def sa_topk_workspace_bytes(n_heads: int, pool_len: int) -> int:
+    out = _sz()
+    _check(_lib.sa_topk_workspace_bytes(n_heads, pool_len, ctypes.byref(out)))
+    return out.value
+
+
+def topk_retrieve(q_score, pool_k, k: int, idx, ws, *, score=None, pool_v=None, pref_k=None,
+                  pref_v=None, stream=None) -> None:
+    """Top-k pool rows per head (see include/sparse_attn.h).
+
+    q_score [n_heads, d] (row stride free, d contiguous); pool_k / pool_v
+    [n_heads, pool_len, d]; idx int32 [n_heads, k]; score float64 [n_heads, k]
+    or None; pref_k / pref_v [n_heads, >=k, d] views receiving the rows.
+    """
+    import torch
+    dtype = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}[pool_k.dtype]
+    n_heads, pool_len, d = pool_k.shape
+    prs = pref_k.stride() if pref_k is not None else (0, 0, 1)
+    _check(_lib.topk_retrieve(dtype, n_heads, pool_len, d, k, _ptr(q_score), q_score.stride(0),
+                              _ptr(pool_k), _ptr(pool_v), pool_k.stride(0), pool_k.stride(1),
+                              _ptr(idx), _ptr(score), _ptr(pref_k), _ptr(pref_v), prs[0], prs[1],
+                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def plan_to_host(m: sa_mask_t, plan) -> dict:
+    """Copy a plan to the host and split it into its sections (numpy arrays)."""
+    import numpy as np
+    lay = sa_plan_layout(m)
+    raw = plan.cpu().numpy().view(np.uint8)
+    hdr = sa_plan_header_t.from_buffer_copy(raw[:ctypes.sizeof(sa_plan_header_t)].tobytes())
+
+    def sec(off, n, dt):
+        return raw[off:off + n * np.dtype(dt).itemsize].view(dt).copy()
+
+    return {
+        "header": hdr,
+        "n_tiles": lay.n_tiles, "n_blocks": lay.n_blocks,
+        "tile_ptr": sec(lay.off_tile_ptr, lay.n_tiles + 1, np.int32),
+        "items": sec(lay.off_items, hdr.n_items, np.int32),
+        "sep_count": sec(lay.off_sep_count, lay.n_tiles, np.int32),
+        "sep_idx": sec(lay.off_sep_idx, hdr.n_sep, np.int32),
+        "sep_bits": sec(lay.off_sep_bits, lay.n_blocks, np.uint64),
+        "blk_sep": sec(lay.off_blk_sep, lay.n_blocks + 1, np.int32),
+    }

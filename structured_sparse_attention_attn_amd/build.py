@@ -1,0 +1,77 @@
+"""Build libsparse_attn.so in-tree with hipcc for gfx950.
+
+Usage: ``python -m structured_sparse_attention_attn_amd.build`` (or call
+:func:`build`).  Objects go to ``_build/`` next to this file; the library is
+written next to this file, where the binding loads it.
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+OUT_DIR = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libsparse_attn.so")
+SOURCES = ["sa_api.cpp", "sa_plan.hip", "sa_rope.hip", "sa_fwd.hip", "sa_topk.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for cand in (os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "bin", "hipcc"),
+                 shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (set ROCM_PATH)")
+
+
+def common_flags():
+    return ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+            f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}"]
+
+
+def device_flags():
+    # packed fp32 ops (v_pk_*_f32) are kept out of the generated code
+    return [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-munsafe-fp-atomics"]
+
+
+def _compile(src: str, verbose: bool) -> str:
+    obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
+    path = os.path.join(CSRC, src)
+    cmd = [hipcc()] + common_flags()
+    if src.endswith(".hip"):
+        cmd += device_flags() + ["-x", "hip"]
+    cmd += ["-c", path, "-o", obj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
+    if verbose and r.stderr.strip():
+        print(r.stderr, flush=True)
+    return obj
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link the shared library; returns its path."""
+    os.makedirs(OUT_DIR, exist_ok=True)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp] + objs
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

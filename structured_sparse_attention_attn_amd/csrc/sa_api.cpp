@@ -1,0 +1,273 @@
+// C ABI of libsparse_attn.so: argument checks, workspace layout and launches.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "sa_common.h"
+
+namespace {
+
+thread_local char g_msg[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_msg, sizeof(g_msg), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_msg[0] = '\0';
+  return SA_OK;
+}
+
+constexpr int kMaxDev = 64;
+std::atomic<int> g_arch[kMaxDev];  // 0 unknown, 1 gfx950, 2 other
+
+// The code objects are built for gfx950 only.
+int check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDev) return fail(SA_EUNSUPPORTED, "device index %d out of range", dev);
+  int st = g_arch[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return fail(SA_EHIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+    st = strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(SA_EUNSUPPORTED, "libsparse_attn is built for gfx950 only");
+  return SA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_mask(const sa_mask_t* m) {
+  if (m == nullptr) return fail(SA_EINVAL, "mask is NULL");
+  if (m->n_q < 1 || m->n_k < 1) return fail(SA_EINVAL, "n_q and n_k must be >= 1 (got %d, %d)", m->n_q, m->n_k);
+  if ((int64_t)m->n_k > ((int64_t)1 << 24) * sa::BK - 1)
+    return fail(SA_EINVAL, "n_k too large (%d)", m->n_k);
+  switch (m->kind) {
+    case SA_MASK_SEPLLM:
+      if (m->n_q != m->n_k) return fail(SA_EINVAL, "SEPLLM needs n_q == n_k (got %d, %d)", m->n_q, m->n_k);
+      if (m->a < 0) return fail(SA_EINVAL, "SEPLLM initial count a must be >= 0 (got %d)", m->a);
+      if (m->w < 1) return fail(SA_EINVAL, "SEPLLM neighbour count w must be >= 1 (got %d)", m->w);
+      break;
+    case SA_MASK_LAMBDA:
+      if (m->n_q != m->n_k) return fail(SA_EINVAL, "LAMBDA needs n_q == n_k (got %d, %d)", m->n_q, m->n_k);
+      if (m->n_starting < 0) return fail(SA_EINVAL, "n_starting must be >= 0 (got %d)", m->n_starting);
+      if (m->L_pretrain < 0) return fail(SA_EINVAL, "L_pretrain must be >= 0 (got %d)", m->L_pretrain);
+      break;
+    case SA_MASK_SEGMENT:
+      if (m->prefix_len < 0) return fail(SA_EINVAL, "prefix_len must be >= 0 (got %d)", m->prefix_len);
+      if ((int64_t)m->prefix_len + m->n_q != m->n_k)
+        return fail(SA_EINVAL, "SEGMENT needs n_k == prefix_len + n_q (got %d != %d + %d)", m->n_k,
+                    m->prefix_len, m->n_q);
+      break;
+    default:
+      return fail(SA_EINVAL, "unknown mask kind %d", m->kind);
+  }
+  return SA_OK;
+}
+
+int check_tensor(const char* name, const void* p, const int64_t st[3], int esz) {
+  if (p == nullptr) return fail(SA_EINVAL, "%s is NULL", name);
+  if (!aligned16(p)) return fail(SA_EINVAL, "%s must be 16-byte aligned", name);
+  for (int i = 0; i < 3; ++i)
+    if (st[i] < 0 || (st[i] * esz) % 16 != 0)
+      return fail(SA_EINVAL, "%s stride[%d] = %lld must be >= 0 and a multiple of 16 bytes", name, i,
+                  (long long)st[i]);
+  return SA_OK;
+}
+
+int check_args(const sa_mask_t* m, const sa_fwd_args_t* a) {
+  if (a == nullptr) return fail(SA_EINVAL, "args is NULL");
+  if (a->dtype != SA_F32 && a->dtype != SA_BF16) return fail(SA_EINVAL, "unknown dtype %d", a->dtype);
+  if (a->dtype == SA_BF16 && a->d != 128)
+    return fail(SA_EUNSUPPORTED, "bf16 supports d = 128 (got %d)", a->d);
+  if (a->dtype == SA_F32 && a->d != 64 && a->d != 128)
+    return fail(SA_EUNSUPPORTED, "f32 supports d = 64 or 128 (got %d)", a->d);
+  if (a->batch < 1 || a->h_q < 1 || a->h_kv < 1)
+    return fail(SA_EINVAL, "batch, h_q and h_kv must be >= 1");
+  if (a->h_q % a->h_kv != 0) return fail(SA_EINVAL, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
+  if ((int64_t)a->batch * a->h_q * sa::ceil_div(m->n_q, sa::TQ) > 0x7fffffffLL)
+    return fail(SA_EINVAL, "too many tiles");
+  if (a->rope != SA_ROPE_NONE && a->rope != SA_ROPE_HALF) return fail(SA_EINVAL, "unknown rope mode %d", a->rope);
+  if (a->rope == SA_ROPE_HALF && !(std::isfinite(a->rope_base) && a->rope_base > 1.0f))
+    return fail(SA_EINVAL, "rope_base must be finite and > 1");
+  if (!std::isfinite(a->scale)) return fail(SA_EINVAL, "scale must be finite");
+  const int esz = a->dtype == SA_BF16 ? 2 : 4;
+  int r;
+  if ((r = check_tensor("q", a->q, a->q_stride, esz)) != SA_OK) return r;
+  if ((r = check_tensor("k", a->k, a->k_stride, esz)) != SA_OK) return r;
+  if ((r = check_tensor("v", a->v, a->v_stride, esz)) != SA_OK) return r;
+  if ((r = check_tensor("o", a->o, a->o_stride, esz)) != SA_OK) return r;
+  return SA_OK;
+}
+
+// Workspace sections of sparse_attn_fwd (byte offsets from the base).
+struct WsLayout {
+  int64_t qrot = -1, krot = -1, ksep = -1, vsep = -1, kcap = -1;
+  int64_t sep_rows = 0, cap_rows = 0;
+  int n_cap = 0;
+  int64_t total = 0;
+};
+
+WsLayout ws_layout(const sa_mask_t& m, const sa_fwd_args_t& a) {
+  WsLayout w;
+  const int64_t esz = a.dtype == SA_BF16 ? 2 : 4;
+  const int64_t row = esz * a.d;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = sa::align_up(off + bytes, 256);
+    return o;
+  };
+  if (a.rope == SA_ROPE_HALF) {
+    w.qrot = take((int64_t)a.batch * a.h_q * m.n_q * row);
+    w.krot = take((int64_t)a.batch * a.h_kv * m.n_k * row);
+  }
+  if (m.kind == SA_MASK_SEPLLM && m.sep != nullptr) {
+    w.sep_rows = sa::align_up(m.n_k, sa::BK);
+    w.ksep = take((int64_t)a.batch * a.h_kv * w.sep_rows * row);
+    w.vsep = take((int64_t)a.batch * a.h_kv * w.sep_rows * row);
+  }
+  if (m.kind == SA_MASK_LAMBDA && a.rope == SA_ROPE_HALF && m.n_starting > 0) {
+    w.n_cap = m.n_starting < m.n_k ? m.n_starting : m.n_k;
+    w.cap_rows = sa::align_up(w.n_cap, sa::BK);
+    w.kcap = take((int64_t)a.batch * a.h_kv * w.cap_rows * row);
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sa_last_error(void) { return g_msg; }
+
+int sa_plan_layout(const sa_mask_t* m, sa_plan_header_t* layout) {
+  int r = check_mask(m);
+  if (r != SA_OK) return r;
+  if (layout == nullptr) return fail(SA_EINVAL, "layout is NULL");
+  *layout = sa::plan_layout(*m);
+  return ok();
+}
+
+int sa_plan_bytes(const sa_mask_t* m, size_t* bytes) {
+  int r = check_mask(m);
+  if (r != SA_OK) return r;
+  if (bytes == nullptr) return fail(SA_EINVAL, "bytes is NULL");
+  *bytes = (size_t)sa::plan_layout(*m).total_bytes;
+  return ok();
+}
+
+int sparse_attn_plan(const sa_mask_t* m, void* plan, size_t plan_bytes, hipStream_t stream) {
+  int r = check_mask(m);
+  if (r != SA_OK) return r;
+  if (plan == nullptr) return fail(SA_EINVAL, "plan is NULL");
+  if (!aligned16(plan)) return fail(SA_EINVAL, "plan must be 16-byte aligned");
+  const sa_plan_header_t lay = sa::plan_layout(*m);
+  if (plan_bytes < (size_t)lay.total_bytes)
+    return fail(SA_ENOSPACE, "plan buffer too small: %zu < %lld bytes", plan_bytes, (long long)lay.total_bytes);
+  if ((r = check_device()) != SA_OK) return r;
+  hipError_t e = sa::launch_plan(*m, lay, plan, stream);
+  if (e != hipSuccess) return fail(SA_EHIP, "plan launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int sa_fwd_workspace_bytes(const sa_mask_t* m, const sa_fwd_args_t* a, size_t* bytes) {
+  int r = check_mask(m);
+  if (r != SA_OK) return r;
+  if (a == nullptr || bytes == nullptr) return fail(SA_EINVAL, "args or bytes is NULL");
+  *bytes = (size_t)ws_layout(*m, *a).total;
+  return ok();
+}
+
+int sparse_attn_fwd(const sa_mask_t* m, const void* plan, size_t plan_bytes, const sa_fwd_args_t* a,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  int r = check_mask(m);
+  if (r != SA_OK) return r;
+  if ((r = check_args(m, a)) != SA_OK) return r;
+  if (plan == nullptr) return fail(SA_EINVAL, "plan is NULL");
+  const sa_plan_header_t lay = sa::plan_layout(*m);
+  if (plan_bytes < (size_t)lay.total_bytes)
+    return fail(SA_ENOSPACE, "plan buffer too small: %zu < %lld bytes", plan_bytes, (long long)lay.total_bytes);
+  const WsLayout w = ws_layout(*m, *a);
+  if (ws_bytes < (size_t)w.total)
+    return fail(SA_ENOSPACE, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)w.total);
+  if (w.total > 0 && (ws == nullptr || !aligned16(ws)))
+    return fail(SA_EINVAL, "workspace must be a 16-byte aligned device pointer");
+  if ((r = check_device()) != SA_OK) return r;
+  char* base = static_cast<char*>(ws);
+  sa::RopeOut ro;
+  memset(&ro, 0, sizeof(ro));
+  ro.qrot = w.qrot >= 0 ? base + w.qrot : nullptr;
+  ro.krot = w.krot >= 0 ? base + w.krot : nullptr;
+  ro.ksep = w.ksep >= 0 ? base + w.ksep : nullptr;
+  ro.vsep = w.vsep >= 0 ? base + w.vsep : nullptr;
+  ro.sep_rows = w.sep_rows;
+  ro.kcap = w.kcap >= 0 ? base + w.kcap : nullptr;
+  ro.cap_rows = w.cap_rows;
+  ro.n_cap = w.n_cap;
+  sa::ThetaTable th;
+  memset(&th, 0, sizeof(th));
+  if (a->rope == SA_ROPE_HALF)
+    for (int c = 0; c < a->d / 2; ++c) th.th[c] = std::pow((double)a->rope_base, -2.0 * c / a->d);
+  hipError_t e = sa::launch_rope(*m, lay, plan, *a, th, ro, stream);
+  if (e != hipSuccess) return fail(SA_EHIP, "rope launch: %s", hipGetErrorString(e));
+  e = sa::launch_fwd(*m, lay, plan, *a, ro, stream);
+  if (e != hipSuccess) return fail(SA_EHIP, "forward launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int sa_topk_workspace_bytes(int32_t n_heads, int32_t pool_len, size_t* bytes) {
+  if (bytes == nullptr) return fail(SA_EINVAL, "bytes is NULL");
+  if (n_heads < 1 || pool_len < 1) return fail(SA_EINVAL, "n_heads and pool_len must be >= 1");
+  *bytes = sa::topk_workspace_bytes(n_heads, pool_len);
+  return ok();
+}
+
+int topk_retrieve(int32_t dtype, int32_t n_heads, int32_t pool_len, int32_t d, int32_t k,
+                  const void* q_score, int64_t q_head_stride, const void* pool_k, const void* pool_v,
+                  int64_t pool_head_stride, int64_t pool_row_stride, int32_t* idx, double* score,
+                  void* pref_k, void* pref_v, int64_t pref_head_stride, int64_t pref_row_stride,
+                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_EINVAL, "unknown dtype %d", dtype);
+  if (n_heads < 1 || pool_len < 1) return fail(SA_EINVAL, "n_heads and pool_len must be >= 1");
+  if (d != 64 && d != 128) return fail(SA_EUNSUPPORTED, "d must be 64 or 128 (got %d)", d);
+  if (k < 1 || k > pool_len) return fail(SA_EINVAL, "k must be in [1, pool_len] (got %d)", k);
+  if (q_score == nullptr || pool_k == nullptr || idx == nullptr)
+    return fail(SA_EINVAL, "q_score, pool_k and idx must not be NULL");
+  if (q_head_stride < 0 || pool_head_stride < 0 || pool_row_stride < 0)
+    return fail(SA_EINVAL, "strides must be >= 0");
+  const int esz = dtype == SA_BF16 ? 2 : 4;
+  if (pool_v != nullptr) {
+    if (pref_k == nullptr || pref_v == nullptr)
+      return fail(SA_EINVAL, "pref_k and pref_v are required when pool_v is given");
+    if (!aligned16(pool_k) || !aligned16(pool_v) || !aligned16(pref_k) || !aligned16(pref_v))
+      return fail(SA_EINVAL, "pool and prefix buffers must be 16-byte aligned for the gather");
+    if ((pool_head_stride * esz) % 16 || (pool_row_stride * esz) % 16 || (pref_head_stride * esz) % 16 ||
+        (pref_row_stride * esz) % 16 || pref_head_stride < 0 || pref_row_stride < 0)
+      return fail(SA_EINVAL, "pool and prefix strides must be multiples of 16 bytes");
+  }
+  const size_t need = sa::topk_workspace_bytes(n_heads, pool_len);
+  if (ws_bytes < need) return fail(SA_ENOSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 7u))
+    return fail(SA_EINVAL, "workspace must be an 8-byte aligned device pointer");
+  int r = check_device();
+  if (r != SA_OK) return r;
+  hipError_t e = sa::launch_topk(dtype, n_heads, pool_len, d, k, q_score, q_head_stride, pool_k, pool_v,
+                                 pool_head_stride, pool_row_stride, idx, score, pref_k, pref_v,
+                                 pref_head_stride, pref_row_stride, ws, stream);
+  if (e != hipSuccess) return fail(SA_EHIP, "top-k launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,170 @@
+"""CPU tests of the C ABI: the library loads, exports every declared symbol,
+its structs match the header, and argument checks fail before any launch.
+No test here launches device work."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+sa = pytest.importorskip("structured_sparse_attention_attn_amd")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"sparse_attn_plan", "sparse_attn_fwd", "topk_retrieve", "sa_last_error"} <= set(names)
+    lib = ctypes.CDLL(sa.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", sa.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if " T " in line)
+    assert set(names) <= exported
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc missing")
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "lay.c"
+    src.write_text(r"""
+#include <stdio.h>
+#include <stddef.h>
+#include "sparse_attn.h"
+#define P(T, f) printf(#T "." #f " %zu\n", offsetof(T, f));
+int main(void) {
+  printf("sa_mask_t %zu\nsa_fwd_args_t %zu\nsa_plan_header_t %zu\n", sizeof(sa_mask_t),
+         sizeof(sa_fwd_args_t), sizeof(sa_plan_header_t));
+  P(sa_mask_t, sep) P(sa_mask_t, prefix_len) P(sa_fwd_args_t, q) P(sa_fwd_args_t, k_stride)
+  P(sa_fwd_args_t, o_stride) P(sa_fwd_args_t, lse) P(sa_plan_header_t, off_tile_ptr)
+  P(sa_plan_header_t, total_bytes)
+  return 0;
+}
+""")
+    exe = tmp_path / "lay"
+    r = subprocess.run(["gcc", "-D__HIP_PLATFORM_AMD__", f"-I{ROOT}/include", "-I/opt/rocm/include",
+                        str(src), "-o", str(exe)], capture_output=True, text=True)
+    if r.returncode != 0:
+        pytest.skip("HIP headers not usable with gcc: " + r.stderr[:200])
+    got = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], capture_output=True,
+                                                              text=True).stdout.splitlines())
+    assert int(got["sa_mask_t"]) == ctypes.sizeof(sa.sa_mask_t)
+    assert int(got["sa_fwd_args_t"]) == ctypes.sizeof(sa.sa_fwd_args_t)
+    assert int(got["sa_plan_header_t"]) == ctypes.sizeof(sa.sa_plan_header_t)
+    for key, val in got.items():
+        if "." in key:
+            T, f = key.split(".")
+            assert getattr(getattr(sa, T), f).offset == int(val), key
+
+
+def _code(fn, *args):
+    return fn(*args)
+
+
+def test_plan_layout_and_validation():
+    m = sa.mask(sa.SA_MASK_SEPLLM, 131072, 131072, a=4, w=1024)
+    lay = sa.sa_plan_layout(m)
+    assert lay.n_tiles == 1024 and lay.n_blocks == 2048 and lay.g0 == 64
+    assert lay.max_items_per_tile == 1 + (1024 + 127 + 63) // 64 + 2
+    assert lay.total_bytes == sa.sa_plan_bytes(m) and lay.total_bytes % 256 == 0
+    offs = [lay.off_tile_ptr, lay.off_items, lay.off_sep_count, lay.off_sep_idx, lay.off_sep_bits,
+            lay.off_blk_sep, lay.total_bytes]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    bad = [
+        sa.mask(sa.SA_MASK_SEPLLM, 100, 100, a=4, w=0),
+        sa.mask(sa.SA_MASK_SEPLLM, 100, 101, a=4, w=3),
+        sa.mask(sa.SA_MASK_LAMBDA, 100, 100, n_starting=-1, L_pretrain=5),
+        sa.mask(sa.SA_MASK_SEGMENT, 100, 150, prefix_len=49),
+        sa.mask(7, 100, 100),
+        sa.mask(sa.SA_MASK_LAMBDA, 0, 0),
+    ]
+    for b in bad:
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sa_plan_bytes(b)
+        assert e.value.code == sa.SA_EINVAL and sa.sa_last_error()
+    lib = sa._lib
+    # plan: NULL buffer and too-small buffer are refused before any launch
+    assert lib.sparse_attn_plan(ctypes.byref(m), None, 1 << 30, None) == sa.SA_EINVAL
+    assert lib.sparse_attn_plan(ctypes.byref(m), 256, 1024, None) == sa.SA_ENOSPACE
+    assert "too small" in sa.sa_last_error()
+
+
+def _args(**kw):
+    a = sa.sa_fwd_args_t()
+    a.dtype, a.batch, a.h_q, a.h_kv, a.d = sa.SA_BF16, 1, 4, 2, 128
+    a.rope, a.rope_base, a.scale = sa.SA_ROPE_HALF, 10000.0, 0.088
+    for name in ("q", "k", "v", "o"):
+        setattr(a, name, 4096)
+        getattr(a, name + "_stride")[:] = [4 * 300 * 128, 300 * 128, 128]
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_fwd_workspace_and_validation():
+    lib = sa._lib
+    m = sa.mask(sa.SA_MASK_LAMBDA, 300, 300, n_starting=10, L_pretrain=100)
+    a = _args()
+    ws = sa.sa_fwd_workspace_bytes(m, a)
+    # rotated q (4 heads) and k (2 heads), plus 64 capped-key rows per kv head
+    expect = 4 * 300 * 256 + 2 * 300 * 256 + 2 * 64 * 256
+    assert ws >= expect and ws - expect < 3 * 256
+    plan_bytes = sa.sa_plan_bytes(m)
+    cases = [
+        (dict(dtype=5), sa.SA_EINVAL),
+        (dict(d=64), sa.SA_EUNSUPPORTED),
+        (dict(h_q=3), sa.SA_EINVAL),
+        (dict(rope=9), sa.SA_EINVAL),
+        (dict(rope_base=0.5), sa.SA_EINVAL),
+        (dict(q=None), sa.SA_EINVAL),
+        (dict(k=4100), sa.SA_EINVAL),  # misaligned
+        (dict(batch=0), sa.SA_EINVAL),
+    ]
+    for kw, code in cases:
+        assert lib.sparse_attn_fwd(ctypes.byref(m), 256, plan_bytes, ctypes.byref(_args(**kw)), 512,
+                                   ws, None) == code, kw
+    bad_stride = _args()
+    bad_stride.v_stride[2] = 100  # 200 bytes: not a multiple of 16
+    assert lib.sparse_attn_fwd(ctypes.byref(m), 256, plan_bytes, ctypes.byref(bad_stride), 512, ws,
+                               None) == sa.SA_EINVAL
+    assert lib.sparse_attn_fwd(ctypes.byref(m), 256, plan_bytes - 1, ctypes.byref(a), 512, ws,
+                               None) == sa.SA_ENOSPACE
+    assert lib.sparse_attn_fwd(ctypes.byref(m), 256, plan_bytes, ctypes.byref(a), 512, ws - 1,
+                               None) == sa.SA_ENOSPACE
+    assert lib.sparse_attn_fwd(ctypes.byref(m), None, plan_bytes, ctypes.byref(a), 512, ws,
+                               None) == sa.SA_EINVAL
+
+
+def test_topk_validation():
+    lib = sa._lib
+    assert sa.sa_topk_workspace_bytes(8, 32768) == 8 * 32768 * 8
+    args = [sa.SA_BF16, 8, 32768, 128, 1024, 256, 128, 512, None, 32768 * 128, 128, 768, None,
+            None, None, 0, 0, 1024, 8 * 32768 * 8, None]
+    for pos, val, code in [(4, 0, sa.SA_EINVAL), (4, 32769, sa.SA_EINVAL), (3, 96, sa.SA_EUNSUPPORTED),
+                           (0, 3, sa.SA_EINVAL), (18, 100, sa.SA_ENOSPACE), (5, None, sa.SA_EINVAL)]:
+        a = list(args)
+        a[pos] = val
+        assert lib.topk_retrieve(*a) == code, (pos, val)
+    # gather requested without destination rows
+    a = list(args)
+    a[8] = 4096
+    assert lib.topk_retrieve(*a) == sa.SA_EINVAL
+
+
+def test_import_fails_loudly_without_library(tmp_path):
+    # a copy of the binding next to no library must refuse to import
+    pkg = tmp_path / "sa_copy"
+    pkg.mkdir()
+    shutil.copy(os.path.join(os.path.dirname(sa.__file__), "__init__.py"), pkg / "__init__.py")
+    r = subprocess.run(["python", "-c", "import sa_copy"], cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0 and "is missing" in r.stderr

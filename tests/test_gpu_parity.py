@@ -1,0 +1,284 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Plans and index lists must match bit for bit.  Outputs must be within
+max-abs 1e-2 / mean-abs 1e-3 for bf16 inputs and max-abs 1e-5 for fp32.
+Small cases are compared in full; the five workloads at their real sizes are
+compared on every row of the first and last two tiles plus random rows.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+from _helpers import compare, device_mask, log, oracle_rows, sample_rows, spec_of, to64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import structured_sparse_attention_attn_amd as m
+    return m
+
+
+def _plan_compare(sa, wl, sep_cpu):
+    sa_obj = device_mask(wl, None if sep_cpu is None else sep_cpu.cuda())
+    sa_obj.build_plan()
+    torch.cuda.synchronize()
+    got = sa.plan_to_host(sa_obj.mask, sa_obj.plan)
+    ref = O.plan(spec_of(wl, None if sep_cpu is None else sep_cpu.numpy()))
+    hdr = got["header"]
+    assert hdr.magic == 0x31504153 and hdr.n_items == len(ref["items"])
+    assert hdr.n_sep == len(ref["sep_idx"])
+    for key in ("tile_ptr", "items", "sep_count", "sep_idx", "sep_bits"):
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    return sa_obj, got
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_plan_bitexact_workloads(sa, cid):
+    wl = W.WORKLOADS[cid]
+    log(f"plan workload {cid}")
+    sep = W.sep_flags(wl.n_k, wl.p_sep, wl.seed + 7) if wl.mode == W.SEPLLM else None
+    _plan_compare(sa, wl, sep)
+
+
+def _random_masks():
+    r = np.random.default_rng(7)
+    out = []
+    for m in [1, 2, 63, 64, 65, 127, 128, 129, 700, 1000]:
+        for kind in (W.SEPLLM, W.LAMBDA, W.SEGMENT):
+            if kind == W.SEPLLM:
+                a = int(r.choice([0, 1, 4, 63, 64, 65, 200]))
+                w = int(r.choice([1, 2, 63, 64, 100, 5000]))
+                p = float(r.choice([0.0, 0.05, 0.5, 1.0]))
+                out.append((W.small(kind, seed=int(r.integers(1 << 30)), m=m, a=a, w=w, p_sep=p), p))
+            elif kind == W.LAMBDA:
+                out.append((W.small(kind, seed=1, m=m, n_s=int(r.choice([0, 1, 10, 64, 100])),
+                                    L=int(r.choice([0, 1, 63, 64, 300, 5000]))), None))
+            else:
+                out.append((W.small(kind, seed=1, m=m, P=int(r.choice([0, 1, 64, 200]))), None))
+    return out
+
+
+def test_plan_bitexact_random(sa):
+    for wl, p in _random_masks():
+        sep = W.sep_flags(wl.n_k, p, wl.seed + 7) if wl.mode == W.SEPLLM else None
+        _plan_compare(sa, wl, sep)
+
+
+def _run_small(sa, wl, *, strided=False, q_zero=False, check_canary=False):
+    inp = W.make_small_inputs(wl)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    if q_zero:
+        q = torch.zeros_like(q)
+    sep = inp.get("sep")
+    dev = "cuda"
+    if strided:
+        # [B,T,H,d] storage viewed as [B,H,T,d]
+        qd = q.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+        kd = k.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+        vd = v.permute(0, 2, 1, 3).contiguous().to(dev).permute(0, 2, 1, 3)
+    else:
+        qd, kd, vd = q.to(dev), k.to(dev), v.to(dev)
+    sa_obj = device_mask(wl, None if sep is None else sep.to(dev))
+    sa_obj.build_plan()
+    guard = 4096
+    o_store = torch.full((guard * 2 + q.numel(),), 7.0, dtype=q.dtype, device=dev)
+    o = o_store[guard:guard + q.numel()].view(q.shape)
+    lse = torch.full((wl.batch, wl.h_q, wl.n_q), 7.0, dtype=torch.float32, device=dev)
+    sa_obj.forward(qd, kd, vd, o=o, lse=lse, rope_base=wl.rope_base, scale=wl.scale)
+    torch.cuda.synchronize()
+    if check_canary:
+        assert torch.all(o_store[:guard] == 7.0) and torch.all(o_store[-guard:] == 7.0)
+    spec = spec_of(wl, None if sep is None else sep.numpy())
+    for b in range(wl.batch):
+        Q, K, V = to64(q[b]), to64(k[b]), to64(v[b])
+        ref_o, ref_l = O.attention(Q, K, V, spec, wl.rope_base, wl.scale)
+        compare(to64(o[b]), ref_o, to64(lse[b]), ref_l, wl.dtype)
+        if q_zero:
+            cnt = O.pair_counts(spec)
+            np.testing.assert_allclose(to64(lse[b]), np.broadcast_to(np.log(cnt), ref_l.shape),
+                                       rtol=0, atol=2e-6)
+    return o, lse
+
+
+SMALL = [
+    # (mode, kwargs)
+    (W.SEPLLM, dict(m=700, a=4, w=64, p_sep=0.1)),
+    (W.SEPLLM, dict(m=700, a=70, w=100, p_sep=0.2, h_q=4, h_kv=2)),
+    (W.SEPLLM, dict(m=333, a=0, w=1, p_sep=0.3)),
+    (W.SEPLLM, dict(m=257, a=4, w=5000, p_sep=0.0)),
+    (W.SEPLLM, dict(m=500, a=200, w=17, p_sep=1.0, batch=2)),
+    (W.SEPLLM, dict(m=1, a=4, w=64, p_sep=0.5)),
+    (W.LAMBDA, dict(m=900, n_s=10, L=300)),
+    (W.LAMBDA, dict(m=700, n_s=0, L=100, h_q=4, h_kv=1)),
+    (W.LAMBDA, dict(m=600, n_s=100, L=64)),
+    (W.LAMBDA, dict(m=300, n_s=10, L=0)),
+    (W.LAMBDA, dict(m=300, n_s=5, L=5000)),
+    (W.SEGMENT, dict(m=600, P=200)),
+    (W.SEGMENT, dict(m=300, P=0)),
+    (W.SEGMENT, dict(m=129, P=1, h_q=4, h_kv=2, batch=2)),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_fwd_small(sa, case, dtype):
+    mode, kw = SMALL[case]
+    for rope in (10000.0, None):
+        d = 128 if dtype == "bf16" else 64
+        wl = W.small(mode, seed=100 + case, dtype=dtype, d=d, rope_base=rope, **kw)
+        log(f"small {case} {dtype} rope={rope}")
+        _run_small(sa, wl, check_canary=True)
+
+
+def test_fwd_f32_d128_and_strided(sa):
+    wl = W.small(W.SEPLLM, seed=5, dtype="f32", d=128, m=300, a=4, w=50, p_sep=0.1)
+    _run_small(sa, wl)
+    wl = W.small(W.LAMBDA, seed=6, dtype="bf16", m=500, n_s=10, L=100, h_q=4, h_kv=2)
+    _run_small(sa, wl, strided=True)
+
+
+@pytest.mark.parametrize("mode", [W.SEPLLM, W.LAMBDA, W.SEGMENT])
+def test_q_zero_counts(sa, mode):
+    # Q = 0: every visible logit is 0, so LSE_i = ln |A_i| and O_i = mean of v over A_i
+    kw = dict(m=640, a=4, w=64, p_sep=0.1) if mode == W.SEPLLM else (
+        dict(m=640, n_s=10, L=100) if mode == W.LAMBDA else dict(m=640, P=100))
+    wl = W.small(mode, seed=9, **kw)
+    _run_small(sa, wl, q_zero=True)
+
+
+def test_determinism(sa):
+    wl = W.small(W.SEPLLM, seed=11, m=1000, a=4, w=128, p_sep=0.1, h_q=4, h_kv=2)
+    o1, l1 = _run_small(sa, wl)
+    o2, l2 = _run_small(sa, wl)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def _workload_parity(sa, cid, heads, n_random):
+    wl = W.WORKLOADS[cid]
+    log(f"workload {cid}: inputs")
+    inp = W.make_inputs(wl)
+    sep = inp.get("sep")
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    sa_obj = device_mask(wl, None if sep is None else sep.cuda())
+    sa_obj.build_plan()
+    lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
+    o = sa_obj.forward(q, k, v, lse=lse, rope_base=wl.rope_base, scale=wl.scale)
+    torch.cuda.synchronize()
+    log(f"workload {cid}: oracle")
+    spec = spec_of(wl, None if sep is None else sep.numpy())
+    rows = np.arange(wl.n_q) if n_random is None else sample_rows(wl.n_q, n_random, cid)
+    group = wl.h_q // wl.h_kv
+    kv_heads = sorted(set(h // group for h in heads))
+    K = {g: to64(inp["k"][0, g]) for g in kv_heads}
+    V = {g: to64(inp["v"][0, g]) for g in kv_heads}
+    for h in heads:
+        g = h // group
+        Qh = to64(inp["q"][0, h])
+        ref_o, ref_l = oracle_rows(Qh[None], K[g][None], V[g][None], spec, wl.rope_base, wl.scale,
+                                   [0], rows)
+        got_o = to64(o[0, h][torch.from_numpy(rows).cuda()])
+        got_l = to64(lse[0, h][torch.from_numpy(rows).cuda()])
+        stats = compare(got_o, ref_o[0], got_l, ref_l[0], wl.dtype)
+        log(f"workload {cid} head {h}: max-abs {stats[0]:.2e} mean-abs {stats[1]:.2e} lse {stats[2]:.2e}")
+
+
+def test_workload1_full(sa):
+    _workload_parity(sa, 1, heads=[0, 1], n_random=None)
+
+
+def test_workload2_full_rows(sa):
+    _workload_parity(sa, 2, heads=[0, 13, 31], n_random=None)
+
+
+def test_workload3_sampled(sa):
+    _workload_parity(sa, 3, heads=[0, 31], n_random=192)
+
+
+def test_workload5_sampled(sa):
+    _workload_parity(sa, 5, heads=[0, 5, 31], n_random=96)
+
+
+def test_workload4_segment_with_topk(sa):
+    from structured_sparse_attention_attn_amd.pipeline import TopK
+    wl = W.WORKLOADS[4]
+    log("workload 4: inputs")
+    inp = W.make_inputs(wl)
+    S, P, H, d = wl.n_q, wl.P, wl.h_q, wl.d
+    n_long = H - wl.n_local
+    dev = "cuda"
+    q = inp["q"].to(dev)
+    kcat = torch.empty((1, H, P + S, d), dtype=torch.bfloat16, device=dev)
+    vcat = torch.empty_like(kcat)
+    kcat[:, :, P:] = inp["k_seg"].to(dev)
+    vcat[:, :, P:] = inp["v_seg"].to(dev)
+    kcat[:, :wl.n_local, :P] = inp["k_tail"].to(dev)
+    vcat[:, :wl.n_local, :P] = inp["v_tail"].to(dev)
+    kpool, vpool = inp["k_pool"][0].to(dev), inp["v_pool"][0].to(dev)
+    idx = torch.empty((n_long, P), dtype=torch.int32, device=dev)
+    score = torch.empty((n_long, P), dtype=torch.float64, device=dev)
+    topk = TopK(n_long, wl.pool_len)
+    topk(q[0, wl.n_local:, S - 1, :], kpool, P, idx, score=score, pool_v=vpool,
+         pref_k=kcat[0, wl.n_local:, :P], pref_v=vcat[0, wl.n_local:, :P])
+    sa_obj = device_mask(wl)
+    sa_obj.build_plan()
+    lse = torch.empty((1, H, S), dtype=torch.float32, device=dev)
+    o = sa_obj.forward(q, kcat, vcat, lse=lse, rope_base=wl.rope_base, scale=wl.scale)
+    torch.cuda.synchronize()
+    log("workload 4: oracle top-k")
+    spec = spec_of(wl)
+    ref_idx = []
+    for hh in range(n_long):
+        s = O.topk_scores(to64(inp["q"][0, wl.n_local + hh, S - 1]), to64(inp["k_pool"][0, hh]))
+        ri = O.topk_select(s, P)
+        np.testing.assert_array_equal(idx[hh].cpu().numpy(), ri)
+        np.testing.assert_array_equal(score[hh].cpu().numpy(), s[ri])
+        ref_idx.append(ri)
+    rows = sample_rows(S, 128, 4)
+    for h in [0, 23, 24, 31]:
+        if h < wl.n_local:
+            Kh = np.concatenate([to64(inp["k_tail"][0, h]), to64(inp["k_seg"][0, h])])
+            Vh = np.concatenate([to64(inp["v_tail"][0, h]), to64(inp["v_seg"][0, h])])
+        else:
+            ri = ref_idx[h - wl.n_local]
+            Kh = np.concatenate([to64(inp["k_pool"][0, h - wl.n_local])[ri], to64(inp["k_seg"][0, h])])
+            Vh = np.concatenate([to64(inp["v_pool"][0, h - wl.n_local])[ri], to64(inp["v_seg"][0, h])])
+        ref_o, ref_l = oracle_rows(to64(inp["q"][0, h])[None], Kh[None], Vh[None], spec,
+                                   wl.rope_base, wl.scale, [0], rows)
+        rr = torch.from_numpy(rows).cuda()
+        stats = compare(to64(o[0, h][rr]), ref_o[0], to64(lse[0, h][rr]), ref_l[0], wl.dtype)
+        log(f"workload 4 head {h}: max-abs {stats[0]:.2e} mean-abs {stats[1]:.2e} lse {stats[2]:.2e}")
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_topk_bitexact(sa, dtype):
+    from structured_sparse_attention_attn_amd.pipeline import TopK
+    for n_heads, pool_len, d, ks, seed in [(8, 32768, 128, (1, 1024, 32768), 1), (3, 1000, 64, (1, 7, 999, 1000), 2),
+                                           (2, 5000, 128, (100,), 3)]:
+        q, kp, vp = W.make_pool_inputs(n_heads, pool_len, d, seed, dtype)
+        if seed == 3:
+            kp = (kp * 2).round() / 2  # coarse values: many exactly tied scores
+            q = q.round()
+        qd, kd, vd = q.cuda(), kp.cuda(), vp.cuda()
+        topk = TopK(n_heads, pool_len)
+        for k in ks:
+            idx = torch.empty((n_heads, k), dtype=torch.int32, device="cuda")
+            score = torch.empty((n_heads, k), dtype=torch.float64, device="cuda")
+            pk = torch.zeros((n_heads, k, d), dtype=dtype, device="cuda")
+            pv = torch.zeros_like(pk)
+            topk(qd, kd, k, idx, score=score, pool_v=vd, pref_k=pk, pref_v=pv)
+            torch.cuda.synchronize()
+            for h in range(n_heads):
+                s = O.topk_scores(q[h].double().numpy(), kp[h].double().numpy())
+                ri = O.topk_select(s, k)
+                np.testing.assert_array_equal(idx[h].cpu().numpy(), ri)
+                np.testing.assert_array_equal(score[h].cpu().numpy(), s[ri])
+                assert torch.equal(pk[h].cpu(), kp[h][torch.from_numpy(ri).long()])
+                assert torch.equal(pv[h].cpu(), vp[h][torch.from_numpy(ri).long()])
