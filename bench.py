@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark: one layer of structured sparse causal attention on one MI355X.
+
+A step is one pass of the whole hot path over one batch of seeded synthetic
+input already resident in HBM: the plan, the RoPE stage and the fused sparse
+forward (plus the top-k retrieval for the segment workload), all 32 heads of
+one layer.  The default workload is the 32K LM-Infinite Lambda mask (batch 1,
+32 heads, d = 128, n_starting = 10, L_pretrain = 4096, RoPE base 10000), the
+configuration the "ms/layer at 32K" figure is quoted on.
+
+Prints one JSON line: effective TFLOP/s over the unmasked pairs
+(4 * d * pairs * heads per step / step time), the per-stage times measured
+with HIP events on the launch stream, the roofline of the fused forward and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "effective TFLOP/s (unmasked pairs) & % bf16 MFMA peak; ms/layer at 32K"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def pair_count_per_head(wl, sep_np):
+    """Exact |A| summed over queries (closed forms of the three key sets)."""
+    import numpy as np
+    i = np.arange(wl.n_q, dtype=np.int64)
+    if wl.mode == "lambda":
+        return int((np.minimum(i, wl.L) + 1 + np.minimum(wl.n_s, np.maximum(0, i - wl.L))).sum())
+    if wl.mode == "segment":
+        return wl.n_q * wl.P + wl.n_q * (wl.n_q + 1) // 2
+    # SepLLM: window min(i+1, w) + sinks and separators at j <= i - w
+    flags = sep_np.astype(np.int64) * (np.arange(wl.n_k) >= wl.a)
+    cs = np.concatenate([[0], np.cumsum(flags)])
+    far = i - wl.w
+    ok = far >= 0
+    extra = np.where(ok, np.minimum(wl.a, far + 1) + cs[np.clip(far + 1, 0, wl.n_k)], 0)
+    return int((np.minimum(i + 1, wl.w) + extra).sum())
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload_name):
+    """HBM bytes per launch of the fused forward from committed rocprofv3 PMC
+    counters, or None when absent or taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", f"attend_{workload_name}_pmc.json")
+    src = os.path.join(ROOT, "structured_sparse_attention_attn_amd", "csrc", "sa_fwd.hip")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("source_sha") != source_sha(src):
+        return None
+    return (d["fetch_kib"] * d["copy_factor_fetch"] + d["write_kib"] * d["copy_factor_write"]) * 1024.0
+
+
+def cpu_baseline(wl, inp, budget_s):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload."""
+    import numpy as np
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    sep = inp.get("sep")
+    spec = O.MaskSpec(wl.mode, wl.n_q, wl.n_k, a=wl.a, w=wl.w,
+                      sep=None if sep is None else sep.numpy(), n_s=wl.n_s, L=wl.L, P=wl.P)
+    if wl.mode == "segment":
+        k = np.concatenate([inp["k_tail"][0, 0].double().numpy(), inp["k_seg"][0, 0].double().numpy()])
+        v = np.concatenate([inp["v_tail"][0, 0].double().numpy(), inp["v_seg"][0, 0].double().numpy()])
+    else:
+        k = inp["k"][0, 0].double().numpy()
+        v = inp["v"][0, 0].double().numpy()
+    q = inp["q"][0, 0].double().numpy()
+    n_tiles = -(-wl.n_q // 128)
+    # tiles from the last one backwards: the ones with the most keys
+    pairs = 0
+    done = 0
+    t0 = time.perf_counter()
+    for t in range(n_tiles - 1, -1, -1):
+        rows = np.arange(128 * t, min(wl.n_q, 128 * t + 128))
+        O.attention_fast(q, k, v, spec, wl.rope_base, wl.scale, [rows])
+        pairs += int(O.mask_rows(spec, rows).sum())
+        done += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": 4.0 * wl.d * pairs / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"head 0, last {done} of {n_tiles} query tiles (128 rows each), fast mode fp64, "
+                      f"{el:.1f} s; rate scaled to effective FLOPs of the sampled rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="1..5 (default: the 32K Lambda layer)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 256 MiB device copy (scale for PMC byte counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(heads or query tiles would shard with no or one exchange step)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from structured_sparse_attention_attn_amd import (fwd_args, sparse_attn_attend, sparse_attn_plan,
+                                                      sparse_attn_rope)
+    from structured_sparse_attention_attn_amd.pipeline import SparseAttention, TopK
+
+    wl = W.WORKLOADS[args.workload]
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    inp = W.make_inputs(wl)
+    sep = inp.get("sep")
+    stream = torch.cuda.current_stream()
+
+    topk = None
+    if wl.mode == "segment":
+        S, P, H, d = wl.n_q, wl.P, wl.h_q, wl.d
+        nl = wl.n_local
+        q = inp["q"].to(dev)
+        k = torch.empty((1, H, P + S, d), dtype=torch.bfloat16, device=dev)
+        v = torch.empty_like(k)
+        k[:, :, P:] = inp["k_seg"].to(dev)
+        v[:, :, P:] = inp["v_seg"].to(dev)
+        k[:, :nl, :P] = inp["k_tail"].to(dev)
+        v[:, :nl, :P] = inp["v_tail"].to(dev)
+        kpool, vpool = inp["k_pool"][0].to(dev), inp["v_pool"][0].to(dev)
+        idx = torch.empty((H - nl, P), dtype=torch.int32, device=dev)
+        topk = TopK(H - nl, wl.pool_len)
+
+        def run_topk():
+            topk(q[0, nl:, S - 1, :], kpool, P, idx, pool_v=vpool, pref_k=k[0, nl:, :P],
+                 pref_v=v[0, nl:, :P])
+    else:
+        q, k, v = (inp[x].to(dev) for x in ("q", "k", "v"))
+    sa = SparseAttention(wl.mode, wl.n_q, wl.n_k, a=wl.a, w=wl.w,
+                         sep=None if sep is None else sep.to(dev), n_starting=wl.n_s,
+                         L_pretrain=wl.L, prefix_len=wl.P)
+    o = torch.empty_like(q)
+    lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device=dev)
+    fa = fwd_args(q, k, v, o, lse=lse, rope_base=wl.rope_base, scale=wl.scale)
+    sa.ensure_workspace(fa)
+    torch.cuda.synchronize()
+
+    def step(ev):
+        ev[0].record(stream)
+        if topk is not None:
+            run_topk()
+        ev[1].record(stream)
+        sparse_attn_plan(sa.mask, sa.plan)
+        ev[2].record(stream)
+        sparse_attn_rope(sa.mask, sa.plan, fa, sa.ws)
+        ev[3].record(stream)
+        sparse_attn_attend(sa.mask, sa.plan, fa, sa.ws)
+        ev[4].record(stream)
+
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]  # noqa: E731
+    for _ in range(args.warmup):
+        step(mk())
+    torch.cuda.synchronize()
+    evs = [mk() for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for e in evs:
+        step(e)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    stage = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+             for i, name in enumerate(["topk", "plan", "rope", "attend"])}
+    if topk is None:
+        stage.pop("topk")
+
+    if args.copy_calib:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+
+    pairs_head = pair_count_per_head(wl, None if sep is None else sep.numpy())
+    flops = 4.0 * wl.d * pairs_head * wl.h_q * wl.batch
+    value = flops / (ms_step * 1e-3) / 1e12
+    attend_tflops = flops / (stage["attend"] * 1e-3) / 1e12
+    traffic = load_traffic(wl.name)
+    roofline = {"bound": "mfma", "achieved": round(attend_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(attend_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic}
+    props = torch.cuda.get_device_properties(0)
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) Q/K/V" + (", Bernoulli separator flags" if sep is not None else "")
+                + ", resident in HBM)",
+        "config": {"workload": wl.name, "mode": wl.mode, "batch": wl.batch, "h_q": wl.h_q,
+                   "h_kv": wl.h_kv, "head_dim": wl.d, "n_q": wl.n_q, "n_k": wl.n_k,
+                   "a": wl.a, "w": wl.w, "p_sep": wl.p_sep, "n_starting": wl.n_s,
+                   "L_pretrain": wl.L, "prefix_len": wl.P, "rope_base": wl.rope_base,
+                   "pairs_per_head": pairs_head},
+        "ms_per_layer": round(stage["rope"] + stage["attend"], 4),
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "stages_ms": {k_: round(v_, 4) for k_, v_ in stage.items()},
+        "roofline": roofline,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

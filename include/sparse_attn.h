@@ -165,6 +165,19 @@ int sa_fwd_workspace_bytes(const sa_mask_t *m, const sa_fwd_args_t *args, size_t
 int sparse_attn_fwd(const sa_mask_t *m, const void *plan, size_t plan_bytes,
                     const sa_fwd_args_t *args, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * The two stages of sparse_attn_fwd as separate calls (same arguments, same
+ * workspace), so a caller can time or schedule them apart.  sparse_attn_rope
+ * writes the rotated queries and keys, the gathered separator rows and the
+ * capped keys into ws; sparse_attn_attend then reads them.  Calling
+ * sparse_attn_rope then sparse_attn_attend on one stream equals
+ * sparse_attn_fwd.  Errors as for sparse_attn_fwd.
+ */
+int sparse_attn_rope(const sa_mask_t *m, const void *plan, size_t plan_bytes,
+                     const sa_fwd_args_t *args, void *ws, size_t ws_bytes, hipStream_t stream);
+int sparse_attn_attend(const sa_mask_t *m, const void *plan, size_t plan_bytes,
+                       const sa_fwd_args_t *args, void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* Host only: bytes of device workspace topk_retrieve needs. */
 int sa_topk_workspace_bytes(int32_t n_heads, int32_t pool_len, size_t *bytes);
 

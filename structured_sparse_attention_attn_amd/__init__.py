@@ -16,8 +16,14 @@ LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m structured_sparse_attention_attn_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python structured_sparse_attention_attn_amd/build.py` "
         "(the sparse attention path has no fallback)")
+
+# torch is imported first so the library binds to the HIP runtime torch
+# already loaded (same SONAME): one runtime per process, shared device
+# pointers and streams.  Loading a second copy of the runtime next to torch's
+# leaves one of the two without a device.
+import torch  # noqa: E402,F401
 
 _lib = ctypes.CDLL(LIB_PATH)
 
@@ -63,11 +69,13 @@ _lib.sa_plan_bytes.argtypes = [_MASKP, ctypes.POINTER(_sz)]
 _lib.sparse_attn_plan.argtypes = [_MASKP, _vp, _sz, _vp]
 _lib.sa_fwd_workspace_bytes.argtypes = [_MASKP, _ARGSP, ctypes.POINTER(_sz)]
 _lib.sparse_attn_fwd.argtypes = [_MASKP, _vp, _sz, _ARGSP, _vp, _sz, _vp]
+_lib.sparse_attn_rope.argtypes = [_MASKP, _vp, _sz, _ARGSP, _vp, _sz, _vp]
+_lib.sparse_attn_attend.argtypes = [_MASKP, _vp, _sz, _ARGSP, _vp, _sz, _vp]
 _lib.sa_topk_workspace_bytes.argtypes = [_i32, _i32, ctypes.POINTER(_sz)]
 _lib.topk_retrieve.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp, _i64, _i64,
                                _vp, _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]
 for _name in ("sa_plan_layout", "sa_plan_bytes", "sparse_attn_plan", "sa_fwd_workspace_bytes",
-              "sparse_attn_fwd", "sa_topk_workspace_bytes", "topk_retrieve"):
+              "sparse_attn_fwd", "sparse_attn_rope", "sparse_attn_attend", "sa_topk_workspace_bytes", "topk_retrieve"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -152,6 +160,20 @@ def sparse_attn_fwd(m: sa_mask_t, plan, args: sa_fwd_args_t, ws, stream=None) ->
     _check(_lib.sparse_attn_fwd(ctypes.byref(m), _ptr(plan), plan.numel(), ctypes.byref(args),
                                 _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
                                 _stream(stream)))
+
+
+def sparse_attn_rope(m: sa_mask_t, plan, args: sa_fwd_args_t, ws, stream=None) -> None:
+    """Enqueue only the RoPE stage of sparse_attn_fwd."""
+    _check(_lib.sparse_attn_rope(ctypes.byref(m), _ptr(plan), plan.numel(), ctypes.byref(args),
+                                 _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                 _stream(stream)))
+
+
+def sparse_attn_attend(m: sa_mask_t, plan, args: sa_fwd_args_t, ws, stream=None) -> None:
+    """Enqueue only the fused forward of sparse_attn_fwd (after sparse_attn_rope)."""
+    _check(_lib.sparse_attn_attend(ctypes.byref(m), _ptr(plan), plan.numel(), ctypes.byref(args),
+                                   _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                   _stream(stream)))
 
 
 def sa_topk_workspace_bytes(n_heads: int, pool_len: int) -> int:

@@ -1,7 +1,7 @@
 """Build libsparse_attn.so in-tree with hipcc for gfx950.
 
-Usage: ``python -m structured_sparse_attention_attn_amd.build`` (or call
-:func:`build`).  Objects go to ``_build/`` next to this file; the library is
+Usage: ``python structured_sparse_attention_attn_amd/build.py`` (a plain
+script: it does not import the package, whose import needs the library).  Objects go to ``_build/`` next to this file; the library is
 written next to this file, where the binding loads it.
 """
 from __future__ import annotations

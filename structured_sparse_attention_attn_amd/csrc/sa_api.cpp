@@ -190,8 +190,14 @@ int sa_fwd_workspace_bytes(const sa_mask_t* m, const sa_fwd_args_t* a, size_t* b
   return ok();
 }
 
-int sparse_attn_fwd(const sa_mask_t* m, const void* plan, size_t plan_bytes, const sa_fwd_args_t* a,
-                    void* ws, size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+enum { STAGE_ROPE = 1, STAGE_ATTEND = 2 };
+
+int run_fwd(const sa_mask_t* m, const void* plan, size_t plan_bytes, const sa_fwd_args_t* a,
+            void* ws, size_t ws_bytes, hipStream_t stream, int stages) {
   int r = check_mask(m);
   if (r != SA_OK) return r;
   if ((r = check_args(m, a)) != SA_OK) return r;
@@ -216,15 +222,38 @@ int sparse_attn_fwd(const sa_mask_t* m, const void* plan, size_t plan_bytes, con
   ro.kcap = w.kcap >= 0 ? base + w.kcap : nullptr;
   ro.cap_rows = w.cap_rows;
   ro.n_cap = w.n_cap;
-  sa::ThetaTable th;
-  memset(&th, 0, sizeof(th));
-  if (a->rope == SA_ROPE_HALF)
-    for (int c = 0; c < a->d / 2; ++c) th.th[c] = std::pow((double)a->rope_base, -2.0 * c / a->d);
-  hipError_t e = sa::launch_rope(*m, lay, plan, *a, th, ro, stream);
-  if (e != hipSuccess) return fail(SA_EHIP, "rope launch: %s", hipGetErrorString(e));
-  e = sa::launch_fwd(*m, lay, plan, *a, ro, stream);
-  if (e != hipSuccess) return fail(SA_EHIP, "forward launch: %s", hipGetErrorString(e));
+  if (stages & STAGE_ROPE) {
+    sa::ThetaTable th;
+    memset(&th, 0, sizeof(th));
+    if (a->rope == SA_ROPE_HALF)
+      for (int c = 0; c < a->d / 2; ++c) th.th[c] = std::pow((double)a->rope_base, -2.0 * c / a->d);
+    hipError_t e = sa::launch_rope(*m, lay, plan, *a, th, ro, stream);
+    if (e != hipSuccess) return fail(SA_EHIP, "rope launch: %s", hipGetErrorString(e));
+  }
+  if (stages & STAGE_ATTEND) {
+    hipError_t e = sa::launch_fwd(*m, lay, plan, *a, ro, stream);
+    if (e != hipSuccess) return fail(SA_EHIP, "forward launch: %s", hipGetErrorString(e));
+  }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_attn_fwd(const sa_mask_t* m, const void* plan, size_t plan_bytes, const sa_fwd_args_t* a,
+                    void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_fwd(m, plan, plan_bytes, a, ws, ws_bytes, stream, STAGE_ROPE | STAGE_ATTEND);
+}
+
+int sparse_attn_rope(const sa_mask_t* m, const void* plan, size_t plan_bytes, const sa_fwd_args_t* a,
+                     void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_fwd(m, plan, plan_bytes, a, ws, ws_bytes, stream, STAGE_ROPE);
+}
+
+int sparse_attn_attend(const sa_mask_t* m, const void* plan, size_t plan_bytes, const sa_fwd_args_t* a,
+                       void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_fwd(m, plan, plan_bytes, a, ws, ws_bytes, stream, STAGE_ATTEND);
 }
 
 int sa_topk_workspace_bytes(int32_t n_heads, int32_t pool_len, size_t* bytes) {

@@ -13,7 +13,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from _helpers import compare, device_mask, log, oracle_rows, sample_rows, spec_of, to64
+from _helpers import (compare, device_mask, log, oracle_rows, row_counts, sample_rows, spec_of,
+                      to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -97,12 +98,12 @@ def _run_small(sa, wl, *, strided=False, q_zero=False, check_canary=False):
     if check_canary:
         assert torch.all(o_store[:guard] == 7.0) and torch.all(o_store[-guard:] == 7.0)
     spec = spec_of(wl, None if sep is None else sep.numpy())
+    cnt = O.pair_counts(spec)
     for b in range(wl.batch):
         Q, K, V = to64(q[b]), to64(k[b]), to64(v[b])
         ref_o, ref_l = O.attention(Q, K, V, spec, wl.rope_base, wl.scale)
-        compare(to64(o[b]), ref_o, to64(lse[b]), ref_l, wl.dtype)
+        compare(to64(o[b]), ref_o, to64(lse[b]), ref_l, wl.dtype, nkeys=cnt[None, :])
         if q_zero:
-            cnt = O.pair_counts(spec)
             np.testing.assert_allclose(to64(lse[b]), np.broadcast_to(np.log(cnt), ref_l.shape),
                                        rtol=0, atol=2e-6)
     return o, lse
@@ -177,6 +178,7 @@ def _workload_parity(sa, cid, heads, n_random):
     rows = np.arange(wl.n_q) if n_random is None else sample_rows(wl.n_q, n_random, cid)
     group = wl.h_q // wl.h_kv
     kv_heads = sorted(set(h // group for h in heads))
+    nkeys = row_counts(spec, rows)
     K = {g: to64(inp["k"][0, g]) for g in kv_heads}
     V = {g: to64(inp["v"][0, g]) for g in kv_heads}
     for h in heads:
@@ -186,7 +188,7 @@ def _workload_parity(sa, cid, heads, n_random):
                                    [0], rows)
         got_o = to64(o[0, h][torch.from_numpy(rows).cuda()])
         got_l = to64(lse[0, h][torch.from_numpy(rows).cuda()])
-        stats = compare(got_o, ref_o[0], got_l, ref_l[0], wl.dtype)
+        stats = compare(got_o, ref_o[0], got_l, ref_l[0], wl.dtype, nkeys=nkeys)
         log(f"workload {cid} head {h}: max-abs {stats[0]:.2e} mean-abs {stats[1]:.2e} lse {stats[2]:.2e}")
 
 
@@ -242,6 +244,7 @@ def test_workload4_segment_with_topk(sa):
         np.testing.assert_array_equal(score[hh].cpu().numpy(), s[ri])
         ref_idx.append(ri)
     rows = sample_rows(S, 128, 4)
+    nkeys = row_counts(spec, rows)
     for h in [0, 23, 24, 31]:
         if h < wl.n_local:
             Kh = np.concatenate([to64(inp["k_tail"][0, h]), to64(inp["k_seg"][0, h])])
@@ -253,7 +256,8 @@ def test_workload4_segment_with_topk(sa):
         ref_o, ref_l = oracle_rows(to64(inp["q"][0, h])[None], Kh[None], Vh[None], spec,
                                    wl.rope_base, wl.scale, [0], rows)
         rr = torch.from_numpy(rows).cuda()
-        stats = compare(to64(o[0, h][rr]), ref_o[0], to64(lse[0, h][rr]), ref_l[0], wl.dtype)
+        stats = compare(to64(o[0, h][rr]), ref_o[0], to64(lse[0, h][rr]), ref_l[0], wl.dtype,
+                        nkeys=nkeys)
         log(f"workload 4 head {h}: max-abs {stats[0]:.2e} mean-abs {stats[1]:.2e} lse {stats[2]:.2e}")
 
 
