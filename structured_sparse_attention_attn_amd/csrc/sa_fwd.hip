@@ -201,21 +201,137 @@ __device__ inline void for_each_unit(const FwdArgs& p, int b, int kvh, int t, in
 
 // ===========================================================================
 // bf16, d = 128: MFMA 32x32x16.  4 waves x 32 queries = one 128-query tile.
-// S^T = K Q^T (keys as rows) so every lane owns one query's logits; then
-// O^T += V^T P^T with the key order permuted to match the logits' registers.
+// S^T = K Q^T (keys as rows) so every lane owns one query's logits and the
+// row max / row sum stay in the lane (plus one swap between the two 32-lane
+// halves); then O^T += V^T P^T, the key order inside each 16-key step permuted
+// to match the registers the logits already sit in.  K and V blocks are
+// double-buffered in LDS (row-major, 16-byte chunks XOR-swizzled by row); the
+// next unit's global loads are in flight while the current one computes.  V^T
+// operands come straight from the row-major V block through the LDS transpose
+// read (ds_read_b64_tr_b16).
 // ===========================================================================
 
 constexpr int D128 = 128;
-constexpr int KS_BYTES = BK * 256;        // K block, 256 B per row, 16 B chunks XOR-swizzled
-constexpr int VT_ROW = 68;                // V^T row: 64 keys + 4 pad (bf16 elements)
-constexpr int VT_BYTES = D128 * VT_ROW * 2;
+constexpr int BLK_BYTES = BK * 256;  // one 64 x 128 bf16 block
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ inline uint4 ld16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
 
+__device__ inline int swz(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
+
+__device__ inline float swap_halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float swap_halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Per-tile unit list: [capped items] [gathered separator chunks] [items].
+struct TileUnits {
+  int it0, n_items, n_capu, n_ch, nsep;
+  const char* kb;      // dense keys of this (batch, kv head)
+  const char* vb;
+  int64_t kst, vst;
+  const char* capb;    // capped keys
+  const char* ksb;     // gathered separator keys / values
+  const char* vsb;
+};
+
+__device__ inline Unit unit_at(const FwdArgs& p, const TileUnits& tu, int u) {
+  Unit x;
+  x.count = 0;
+  x.sbits = 0;
+  if (u < tu.n_capu) {
+    const int blk = p.items[tu.it0 + u] & 0xffffff;
+    x.kbase = tu.capb + (int64_t)blk * BK * (D128 * 2);
+    x.kstride = D128 * 2;
+    x.kvalid = min(BK, p.n_cap - blk * BK);
+    x.vbase = tu.vb + (int64_t)blk * BK * tu.vst;
+    x.vstride = tu.vst;
+    x.vvalid = min(BK, p.n_k - blk * BK);
+    x.key0 = blk * BK;
+    x.mk = MK_LCAP;
+    return x;
+  }
+  u -= tu.n_capu;
+  if (u < tu.n_ch) {
+    const int c0 = u * BK;
+    x.kbase = tu.ksb + (int64_t)c0 * (D128 * 2);
+    x.kstride = D128 * 2;
+    x.vbase = tu.vsb + (int64_t)c0 * (D128 * 2);
+    x.vstride = D128 * 2;
+    x.kvalid = x.vvalid = min(BK, tu.nsep - c0);
+    x.key0 = 0;
+    x.count = x.kvalid;
+    x.mk = x.kvalid == BK ? MK_NONE : MK_COUNT;
+    return x;
+  }
+  u -= tu.n_ch;
+  const int item = p.items[tu.it0 + u];
+  const int blk = item & 0xffffff;
+  const int fl = item >> 24;
+  x.kbase = tu.kb + (int64_t)blk * BK * tu.kst;
+  x.kstride = tu.kst;
+  x.vbase = tu.vb + (int64_t)blk * BK * tu.vst;
+  x.vstride = tu.vst;
+  x.kvalid = x.vvalid = min(BK, p.n_k - blk * BK);
+  x.key0 = blk * BK;
+  if (p.use_cap && (fl & SA_ITEM_CAPPED)) {
+    x.mk = MK_LNORM;
+  } else if (fl & SA_ITEM_FULL) {
+    x.mk = MK_NONE;
+  } else if (p.kind == SA_MASK_SEPLLM) {
+    x.mk = MK_SEPLLM;
+    x.sbits = p.sep_bits[blk];
+  } else if (p.kind == SA_MASK_LAMBDA) {
+    x.mk = MK_LALL;
+  } else {
+    x.mk = MK_SEG;
+  }
+  return x;
+}
+
+// Masks the raw logits of one unit.  Register r of half mb holds key slot
+// kk = 32 mb + 8 (r / 4) + 4 hl + r % 4; everything lane-dependent is folded
+// into one base so the per-element tests use compile-time offsets, and the
+// conditions use non-short-circuit operators (no branches).
+template <int MK>
+__device__ inline void apply_mask(const FwdArgs& p, const Unit& u, int qi, int hl, f32x16 (&s)[2]) {
+  const int jb = u.key0 + 4 * hl;                    // key index of slot offset 0
+  const unsigned long long sb = u.sbits >> (4 * hl);  // separator bits from slot offset 0
+  const int cb = u.count - 4 * hl;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = 32 * mb + 8 * (r >> 2) + (r & 3);  // compile-time slot offset
+      const int j = jb + c;
+      bool vis;
+      if (MK == MK_COUNT) {
+        vis = c < cb;
+      } else if (MK == MK_SEPLLM) {
+        const bool sepb = (sb >> c) & 1ull;
+        vis = (j <= qi) & (j < p.n_k) & ((j < p.a) | (qi - j < p.w) | sepb);
+      } else if (MK == MK_LALL) {
+        vis = (j <= qi) & (j < p.n_k) & ((j < p.n_s) | (qi - j <= p.L));
+      } else if (MK == MK_LNORM) {
+        vis = (j <= qi) & (j < p.n_k) & (qi - j <= p.L);
+      } else if (MK == MK_LCAP) {
+        vis = (j < p.n_s) & (j < p.n_k) & (qi - j > p.L);
+      } else {
+        vis = (j <= p.P + qi) & (j < p.n_k);
+      }
+      s[mb][r] = vis ? s[mb][r] : NEG_INF;
+    }
+  }
+}
+
 __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[KS_BYTES + VT_BYTES];
-  char* Ks = smem;
-  unsigned short* Vt = reinterpret_cast<unsigned short*>(smem + KS_BYTES);
+  __shared__ __attribute__((aligned(16))) char smem[4 * BLK_BYTES];  // [buf][K|V]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
   int b, kvh, t, hq;
@@ -223,6 +339,24 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   const int q0 = t * TQ;
   const int qi = q0 + wid * 32 + l32;  // this lane's query
   const bool qok = qi < p.n_q;
+
+  TileUnits tu;
+  tu.it0 = p.tile_ptr[t];
+  tu.n_items = p.tile_ptr[t + 1] - tu.it0;
+  tu.n_capu = 0;
+  if (p.use_cap)
+    while (tu.n_capu < tu.n_items && ((p.items[tu.it0 + tu.n_capu] >> 24) & SA_ITEM_CAPPED)) ++tu.n_capu;
+  tu.nsep = p.gather ? p.sep_count[t] : 0;
+  tu.n_ch = (tu.nsep + BK - 1) / BK;
+  tu.kb = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH) * 2;
+  tu.vb = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH) * 2;
+  tu.kst = p.ksT * 2;
+  tu.vst = p.vsT * 2;
+  tu.capb = static_cast<const char*>(p.kcap) + ((int64_t)b * p.h_kv + kvh) * p.cap_rows * (D128 * 2);
+  const int64_t sep_off = ((int64_t)b * p.h_kv + kvh) * p.sep_rows * (D128 * 2);
+  tu.ksb = static_cast<const char*>(p.ksep) + sep_off;
+  tu.vsb = static_cast<const char*>(p.vsep) + sep_off;
+  const int n_units = tu.n_capu + tu.n_ch + tu.n_items;
 
   bf16x8 qf[8];
   auto load_q = [&](const void* base, int64_t sB, int64_t sH, int64_t sT) {
@@ -234,41 +368,54 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       qf[s] = __builtin_bit_cast(bf16x8, x);
     }
   };
-  load_q(p.q, p.qsB, p.qsH, p.qsT);
-  bool q_is_raw = false;
+  if (tu.n_capu > 0) load_q(p.qraw, p.qrB, p.qrH, p.qrT);
+  else load_q(p.q, p.qsB, p.qsH, p.qsT);
 
   float m_run = NEG_INF, l_run = 0.f;
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
 
-  auto unit = [&](const Unit& u, bool raw_q) {
-    if (raw_q != q_is_raw) {
-      if (raw_q) load_q(p.qraw, p.qrB, p.qrH, p.qrT);
-      else load_q(p.q, p.qsB, p.qsH, p.qsT);
-      q_is_raw = raw_q;
-    }
-    // --- global -> LDS: K row-major swizzled, V transposed ---
+  // global -> LDS without register staging: each wave moves 16 rows of K and
+  // of V (4 rows of 256 bytes per instruction, lane l -> 16-byte slot l).  The
+  // slot a lane fills is fixed, so the lane fetches the logical chunk that the
+  // row's XOR swizzle puts there.  Rows past the unit's valid count repeat its
+  // last valid row: finite values whose logits are masked out.
+  auto issue_loads = [&](const Unit& u, int buf) {
+    char* Kb = smem + buf * 2 * BLK_BYTES;
+    char* Vb = Kb + BLK_BYTES;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int row = it * 16 + (tid >> 4), ch = tid & 15;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (row < u.kvalid) x = ld16(u.kbase + row * u.kstride + ch * 16);
-      *reinterpret_cast<uint4*>(Ks + row * 256 + ((ch ^ (row & 15)) * 16)) = x;
+      const int r0 = wid * 16 + it * 4;
+      const int row = r0 + (lane >> 4);
+      const int ch = (lane & 15) ^ (row & 15);
+      const int kr = min(row, u.kvalid - 1), vr = min(row, u.vvalid - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(u.kbase + kr * u.kstride + ch * 16),
+                                       (__attribute__((address_space(3))) void*)(Kb + r0 * 256), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)(u.vbase + vr * u.vstride + ch * 16),
+                                       (__attribute__((address_space(3))) void*)(Vb + r0 * 256), 16, 0, 0);
     }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int key = lane, ch = wid + 4 * it;
-      uint4 x = make_uint4(0, 0, 0, 0);
-      if (key < u.vvalid) x = ld16(u.vbase + key * u.vstride + ch * 16);
-      const unsigned w4[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(ch * 8 + 2 * e) * VT_ROW + key] = (unsigned short)(w4[e] & 0xffffu);
-        Vt[(ch * 8 + 2 * e + 1) * VT_ROW + key] = (unsigned short)(w4[e] >> 16);
-      }
-    }
+  };
+
+  Unit cur;
+  if (n_units > 0) {
+    cur = unit_at(p, tu, 0);
+    issue_loads(cur, 0);
+  }
+  for (int u = 0; u < n_units; ++u) {
+    const int buf = u & 1;
+    // this wave's loads of unit u have landed; the barrier makes every wave's
+    // visible and frees the other buffer (its last reader was unit u-1)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+    Unit nxt;
+    if (u + 1 < n_units) {
+      nxt = unit_at(p, tu, u + 1);
+      issue_loads(nxt, buf ^ 1);
+    }
+    if (u == tu.n_capu && tu.n_capu > 0) load_q(p.q, p.qsB, p.qsH, p.qsT);  // rotated Q from here on
+    const char* Kb = smem + buf * 2 * BLK_BYTES;
+    const char* Vb = Kb + BLK_BYTES;
     // --- S^T = K Q^T : two 32-key halves ---
     f32x16 s[2];
 #pragma unroll
@@ -277,44 +424,50 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       const int row = mb * 32 + l32;
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const int ch = 2 * ks + hl;
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Ks + row * 256 + ((ch ^ (row & 15)) * 16)));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kb + swz(row, 2 * ks + hl)));
         c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], c, 0, 0, 0);
       }
       s[mb] = c;
     }
-    // --- scale, mask, online softmax ---
+    // --- mask (raw logits), then the online softmax in base 2 ---
+    switch (cur.mk) {
+      case MK_NONE: break;
+      case MK_COUNT: apply_mask<MK_COUNT>(p, cur, qi, hl, s); break;
+      case MK_SEPLLM: apply_mask<MK_SEPLLM>(p, cur, qi, hl, s); break;
+      case MK_LALL: apply_mask<MK_LALL>(p, cur, qi, hl, s); break;
+      case MK_LNORM: apply_mask<MK_LNORM>(p, cur, qi, hl, s); break;
+      case MK_LCAP: apply_mask<MK_LCAP>(p, cur, qi, hl, s); break;
+      default: apply_mask<MK_SEG>(p, cur, qi, hl, s); break;
+    }
     float mx = NEG_INF;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
-        float x = s[mb][r] * p.scale_log2;
-        if (u.mk != MK_NONE && !visible(p, u, qi, kk)) x = NEG_INF;
-        s[mb][r] = x;
-        mx = fmaxf(mx, x);
-      }
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+    mx = swap_halves_max(mx) * p.scale_log2;
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == NEG_INF ? 0.f : m_new;
-    const float alpha = exp2f(m_run - m_use);
+    if (__any(m_new > m_run)) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      l_run *= alpha;
+#pragma unroll
+      for (int dm = 0; dm < 4; ++dm) acc[dm] *= alpha;
+    }
+    m_run = m_new;
     float psum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float e = exp2f(s[mb][r] - m_use);
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[mb][r], p.scale_log2, -m_use));
         s[mb][r] = e;
         psum += e;
       }
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int dm = 0; dm < 4; ++dm) acc[dm] *= alpha;
+    l_run += psum;
     // --- O^T += V^T P^T ---
+    const int g16 = lane >> 4, s16 = lane & 15;
+    const int dsub = 16 * (g16 & 1);             // d offset of this 16-lane group
+    const int trow = s16 >> 2, tcol = 4 * (s16 & 3);  // piece this lane points at
 #pragma unroll
     for (int kstep = 0; kstep < 4; ++kstep) {
       const int mb = kstep >> 1, uu = kstep & 1;
@@ -329,20 +482,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       const int kA = 32 * mb + 16 * uu + 4 * hl;
 #pragma unroll
       for (int dm = 0; dm < 4; ++dm) {
-        const unsigned short* vr = Vt + (dm * 32 + l32) * VT_ROW;
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr + kA);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vr + kA + 8);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        const int col = 32 * dm + dsub + tcol;  // d of the piece
+        const int r0 = kA + trow, r1 = kA + 8 + trow;
+        const char* a0 = Vb + swz(r0, col >> 3) + ((col & 7) << 1);
+        const char* a1 = Vb + swz(r1, col >> 3) + ((col & 7) << 1);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1));
+        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[dm], 0, 0, 0);
       }
     }
-    __syncthreads();
-  };
-
-  for_each_unit(p, b, kvh, t, 2, (int64_t)D128 * 2, unit);
+    cur = nxt;
+  }
 
   // --- epilogue ---
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  const float l_tot = swap_halves_sum(l_run);
   if (qok) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     char* orow = static_cast<char*>(p.o) + (b * p.osB + hq * p.osH + (int64_t)qi * p.osT) * 2;
@@ -362,7 +516,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       }
     }
     if (p.lse != nullptr && hl == 0)
-      p.lse[((int64_t)b * p.h_q + hq) * p.n_q + qi] = (m_run + log2f(l_tot)) * LN2;
+      p.lse[((int64_t)b * p.h_q + hq) * p.n_q + qi] = (m_run + __log2f(l_tot)) * LN2;
   }
 }
 
