@@ -100,7 +100,7 @@ int check_args(const sa_mask_t* m, const sa_fwd_args_t* a) {
   if (a->rope != SA_ROPE_NONE && a->rope != SA_ROPE_HALF) return fail(SA_EINVAL, "unknown rope mode %d", a->rope);
   if (a->rope == SA_ROPE_HALF && !(std::isfinite(a->rope_base) && a->rope_base > 1.0f))
     return fail(SA_EINVAL, "rope_base must be finite and > 1");
-  if (!std::isfinite(a->scale)) return fail(SA_EINVAL, "scale must be finite");
+  if (!(std::isfinite(a->scale) && a->scale > 0.0f)) return fail(SA_EINVAL, "scale must be finite and > 0");
   const int esz = a->dtype == SA_BF16 ? 2 : 4;
   int r;
   if ((r = check_tensor("q", a->q, a->q_stride, esz)) != SA_OK) return r;
@@ -128,10 +128,9 @@ WsLayout ws_layout(const sa_mask_t& m, const sa_fwd_args_t& a) {
     off = sa::align_up(off + bytes, 256);
     return o;
   };
-  if (a.rope == SA_ROPE_HALF) {
+  if (a.rope == SA_ROPE_HALF || a.dtype == SA_BF16)  // bf16 always reads a scaled query copy
     w.qrot = take((int64_t)a.batch * a.h_q * m.n_q * row);
-    w.krot = take((int64_t)a.batch * a.h_kv * m.n_k * row);
-  }
+  if (a.rope == SA_ROPE_HALF) w.krot = take((int64_t)a.batch * a.h_kv * m.n_k * row);
   if (m.kind == SA_MASK_SEPLLM && m.sep != nullptr) {
     w.sep_rows = sa::align_up(m.n_k, sa::BK);
     w.ksep = take((int64_t)a.batch * a.h_kv * w.sep_rows * row);

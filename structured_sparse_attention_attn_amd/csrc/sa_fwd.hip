@@ -15,6 +15,8 @@
 //   2. SepLLM gathered separator chunks of 64 rows (no mask but the count);
 //   3. the plan's blocks: unmasked when FULL, otherwise the key-set predicate
 //      (LM-Infinite CAPPED blocks exclude their capped pairs here).
+#include <type_traits>
+
 #include "sa_common.h"
 
 namespace sa {
@@ -212,13 +214,18 @@ __device__ inline void for_each_unit(const FwdArgs& p, int b, int kvh, int t, in
 // ===========================================================================
 
 constexpr int D128 = 128;
-constexpr int BLK_BYTES = BK * 256;  // one 64 x 128 bf16 block
+constexpr int BLK_BYTES = BK * 256;        // one 64 x 128 bf16 block
+constexpr int BUF_BYTES = 2 * BLK_BYTES;   // K then V
+
+// 16-byte chunk c of row r sits at chunk c ^ f(r & 15), f swapping the two
+// 2-bit halves of its argument.  Any 16 consecutive rows then spread one
+// logical chunk over all 16 positions (conflict-free K fragment reads), and
+// the 8 rows x 64 bytes of one V^T transpose read cover every bank twice.
+__device__ inline int swzf(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ inline uint4 ld16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
-
-__device__ inline int swz(int row, int chunk) { return row * 256 + ((chunk ^ (row & 15)) << 4); }
 
 __device__ inline float swap_halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -331,7 +338,7 @@ __device__ inline void apply_mask(const FwdArgs& p, const Unit& u, int qi, int h
 }
 
 __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * BLK_BYTES];  // [buf][K|V]
+  __shared__ __attribute__((aligned(16))) char smem[2 * BUF_BYTES];  // [buf][K|V]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
   int b, kvh, t, hq;
@@ -371,29 +378,41 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   if (tu.n_capu > 0) load_q(p.qraw, p.qrB, p.qrH, p.qrT);
   else load_q(p.q, p.qsB, p.qsH, p.qsT);
 
-  float m_run = NEG_INF, l_run = 0.f;
+  // Online softmax against a reference max m_ref per query (base-2 logits:
+  // the queries and capped keys carry scale * log2(e)).  -m_ref enters the
+  // QK^T MFMA as its initial accumulator, so the logits leave the MFMA
+  // already shifted; the reference is raised only when a row's running sum
+  // of one unit passes 2^10 (or while some row has no finite reference yet),
+  // which keeps every p <= ~2^10 and the shift exact in the final O and LSE.
+  bool has_ref = false;
+  float m_ref = 0.f, l_run = 0.f;
+  f32x16 negm = f32x16{};
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
 
-  // global -> LDS without register staging: each wave moves 16 rows of K and
-  // of V (4 rows of 256 bytes per instruction, lane l -> 16-byte slot l).  The
-  // slot a lane fills is fixed, so the lane fetches the logical chunk that the
-  // row's XOR swizzle puts there.  Rows past the unit's valid count repeat its
-  // last valid row: finite values whose logits are masked out.
+  // global -> LDS without register staging: one instruction moves rows
+  // 4i .. 4i+3 (lane l -> row 4i + l/16, stored chunk l%16); the lane fetches
+  // the logical chunk that the row's swizzle puts in that slot, which is
+  // lchunk ^ (i & 3) for a per-lane lchunk.  Rows past the unit's valid count
+  // repeat its last valid row: finite values whose logits are masked out.
+  const int lrow = lane >> 4;
+  const int lchunk = (lane & 15) ^ (lrow << 2);
   auto issue_loads = [&](const Unit& u, int buf) {
-    char* Kb = smem + buf * 2 * BLK_BYTES;
+    char* Kb = smem + buf * BUF_BYTES;
     char* Vb = Kb + BLK_BYTES;
+    const bool kfull = u.kvalid == BK, vfull = u.vvalid == BK;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int r0 = wid * 16 + it * 4;
-      const int row = r0 + (lane >> 4);
-      const int ch = (lane & 15) ^ (row & 15);
-      const int kr = min(row, u.kvalid - 1), vr = min(row, u.vvalid - 1);
+    for (int j = 0; j < 4; ++j) {
+      const int i = wid * 4 + j;  // rows 4i .. 4i+3
+      const int row = 4 * i + lrow;
+      const int ch = lchunk ^ (j & 3);
+      const int kr = kfull ? row : min(row, u.kvalid - 1);
+      const int vr = vfull ? row : min(row, u.vvalid - 1);
       __builtin_amdgcn_global_load_lds((const void*)(u.kbase + kr * u.kstride + ch * 16),
-                                       (__attribute__((address_space(3))) void*)(Kb + r0 * 256), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(Kb + i * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(u.vbase + vr * u.vstride + ch * 16),
-                                       (__attribute__((address_space(3))) void*)(Vb + r0 * 256), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void*)(Vb + i * 1024), 16, 0, 0);
     }
   };
 
@@ -402,98 +421,165 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
     cur = unit_at(p, tu, 0);
     issue_loads(cur, 0);
   }
-  for (int u = 0; u < n_units; ++u) {
-    const int buf = u & 1;
-    // this wave's loads of unit u have landed; the barrier makes every wave's
-    // visible and frees the other buffer (its last reader was unit u-1)
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    __syncthreads();
-    Unit nxt;
-    if (u + 1 < n_units) {
-      nxt = unit_at(p, tu, u + 1);
-      issue_loads(nxt, buf ^ 1);
-    }
-    if (u == tu.n_capu && tu.n_capu > 0) load_q(p.q, p.qsB, p.qsH, p.qsT);  // rotated Q from here on
-    const char* Kb = smem + buf * 2 * BLK_BYTES;
-    const char* Vb = Kb + BLK_BYTES;
-    // --- S^T = K Q^T : two 32-key halves ---
-    f32x16 s[2];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x16 c = f32x16{};
-      const int row = mb * 32 + l32;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(Kb + swz(row, 2 * ks + hl)));
-        c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], c, 0, 0, 0);
+  // One unit: the exact-max softmax (full_path) runs while some row of the
+  // wave has no finite reference yet, the fast path afterwards.  Every wave
+  // runs exactly one barrier per unit, whichever loop it is in.
+  auto step = [&](int u, auto full_path) {
+      const int buf = u & 1;
+      // this wave's loads of unit u have landed; the barrier makes every wave's
+      // visible and frees the other buffer (its last reader was unit u-1)
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      Unit nxt;
+      if (u + 1 < n_units) {
+        nxt = unit_at(p, tu, u + 1);
+        issue_loads(nxt, buf ^ 1);
       }
-      s[mb] = c;
-    }
-    // --- mask (raw logits), then the online softmax in base 2 ---
-    switch (cur.mk) {
-      case MK_NONE: break;
-      case MK_COUNT: apply_mask<MK_COUNT>(p, cur, qi, hl, s); break;
-      case MK_SEPLLM: apply_mask<MK_SEPLLM>(p, cur, qi, hl, s); break;
-      case MK_LALL: apply_mask<MK_LALL>(p, cur, qi, hl, s); break;
-      case MK_LNORM: apply_mask<MK_LNORM>(p, cur, qi, hl, s); break;
-      case MK_LCAP: apply_mask<MK_LCAP>(p, cur, qi, hl, s); break;
-      default: apply_mask<MK_SEG>(p, cur, qi, hl, s); break;
-    }
-    float mx = NEG_INF;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-    mx = swap_halves_max(mx) * p.scale_log2;
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == NEG_INF ? 0.f : m_new;
-    if (__any(m_new > m_run)) {
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      l_run *= alpha;
-#pragma unroll
-      for (int dm = 0; dm < 4; ++dm) acc[dm] *= alpha;
-    }
-    m_run = m_new;
-    float psum = 0.f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[mb][r], p.scale_log2, -m_use));
-        s[mb][r] = e;
-        psum += e;
+      if (u == tu.n_capu && tu.n_capu > 0) load_q(p.q, p.qsB, p.qsH, p.qsT);  // rotated Q from here on
+      const char* Kb = smem + buf * BUF_BYTES;
+      const char* Vb = Kb + BLK_BYTES;
+      // --- S^T = K Q^T - m_ref : both 32-key halves interleaved, K fragments
+      //     read from LDS two k-steps ahead of their MFMAs ---
+      f32x16 s[2];
+      {
+        // rows l32 and 32 + l32 share row & 15, hence the swizzle; the k-step's
+        // logical chunk is 2 ks + hl
+        const char* kl = Kb + l32 * 256;
+        const int kf = swzf(l32) ^ hl;
+        auto kfrag = [&](int mb, int ks) {
+          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + mb * 32 * 256 + (((2 * ks) ^ kf) << 4)));
+        };
+        bf16x8 a0[3], a1[3];
+        a0[0] = kfrag(0, 0); a1[0] = kfrag(1, 0);
+        a0[1] = kfrag(0, 1); a1[1] = kfrag(1, 1);
+        f32x16 c0 = negm, c1 = negm;
+  #pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          if (ks + 2 < 8) {
+            a0[(ks + 2) % 3] = kfrag(0, ks + 2);
+            a1[(ks + 2) % 3] = kfrag(1, ks + 2);
+          }
+          c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[ks % 3], qf[ks], c0, 0, 0, 0);
+          c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[ks % 3], qf[ks], c1, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        s[0] = c0;
+        s[1] = c1;
       }
-    l_run += psum;
-    // --- O^T += V^T P^T ---
-    const int g16 = lane >> 4, s16 = lane & 15;
-    const int dsub = 16 * (g16 & 1);             // d offset of this 16-lane group
-    const int trow = s16 >> 2, tcol = 4 * (s16 & 3);  // piece this lane points at
-#pragma unroll
-    for (int kstep = 0; kstep < 4; ++kstep) {
-      const int mb = kstep >> 1, uu = kstep & 1;
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const f32x2 two = {s[mb][8 * uu + e], s[mb][8 * uu + e + 1]};
-        const bf16x2 c2 = __builtin_convertvector(two, bf16x2);
-        pb[e] = c2[0];
-        pb[e + 1] = c2[1];
+      // --- mask, then the online softmax ---
+      switch (cur.mk) {
+        case MK_NONE: break;
+        case MK_COUNT: apply_mask<MK_COUNT>(p, cur, qi, hl, s); break;
+        case MK_SEPLLM: apply_mask<MK_SEPLLM>(p, cur, qi, hl, s); break;
+        case MK_LALL: apply_mask<MK_LALL>(p, cur, qi, hl, s); break;
+        case MK_LNORM: apply_mask<MK_LNORM>(p, cur, qi, hl, s); break;
+        case MK_LCAP: apply_mask<MK_LCAP>(p, cur, qi, hl, s); break;
+        default: apply_mask<MK_SEG>(p, cur, qi, hl, s); break;
       }
-      const int kA = 32 * mb + 16 * uu + 4 * hl;
-#pragma unroll
-      for (int dm = 0; dm < 4; ++dm) {
-        const int col = 32 * dm + dsub + tcol;  // d of the piece
-        const int r0 = kA + trow, r1 = kA + 8 + trow;
-        const char* a0 = Vb + swz(r0, col >> 3) + ((col & 7) << 1);
-        const char* a1 = Vb + swz(r1, col >> 3) + ((col & 7) << 1);
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1));
-        const bf16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, acc[dm], 0, 0, 0);
+      if constexpr (!decltype(full_path)::value) {
+        // common path: p = 2^(s - m_ref) straight from the MFMA output
+        float psum = 0.f;
+  #pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(s[mb][r]);
+            s[mb][r] = e;
+            psum += e;
+          }
+        if (__any(psum > 1024.f)) {
+          // rare: raise the reference of the rows whose values grew
+          float pm = 0.f;
+  #pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+  #pragma unroll
+            for (int r = 0; r < 16; ++r) pm = fmaxf(pm, s[mb][r]);
+          pm = swap_halves_max(pm);
+          if (pm > 1.f) {
+            const float f = 1.f / pm;
+  #pragma unroll
+            for (int mb = 0; mb < 2; ++mb) s[mb] *= f;
+  #pragma unroll
+            for (int dm = 0; dm < 4; ++dm) acc[dm] *= f;
+            psum *= f;
+            l_run *= f;
+            m_ref += __log2f(pm);
+            negm = f32x16{} - m_ref;
+          }
+        }
+        l_run += psum;
+      } else {
+        // some row has no finite reference yet: exact max of this unit
+        float mx = NEG_INF;
+  #pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+        mx = swap_halves_max(mx);  // relative to m_ref
+        float delta = 0.f;
+        if (mx != NEG_INF) delta = has_ref ? fmaxf(mx, 0.f) : mx;
+        const float alpha = __builtin_amdgcn_exp2f(-delta);
+        float psum = 0.f;
+  #pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+  #pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = __builtin_amdgcn_exp2f(s[mb][r] - delta);
+            s[mb][r] = e;
+            psum += e;
+          }
+  #pragma unroll
+        for (int dm = 0; dm < 4; ++dm) acc[dm] *= alpha;
+        l_run = l_run * alpha + psum;
+        m_ref += delta;
+        has_ref = has_ref || mx != NEG_INF;
+        negm = f32x16{} - m_ref;
+          }
+      // --- O^T += V^T P^T: V^T fragments by LDS transpose reads, one MFMA ahead ---
+      {
+        // lane (16-lane group g, index s) points at keys kA + s/4 (+8 for the
+        // upper half of the k-step), columns 32 dm + 16 (g & 1) + 4 (s & 3) .. +3;
+        // kA = 32 mb + 16 uu + 4 hl, so row & 15 is 4 hl + s/4 (+8)
+        const int s16 = lane & 15;
+        const int vrow = 4 * hl + (s16 >> 2);
+        const int vf0 = swzf(vrow), vf1 = swzf(vrow + 8);
+        const int vcol = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);  // within a 32-column group
+        const char* vl = Vb + vrow * 256 + ((vcol & 7) << 1);
+        auto vfrag = [&](int kstep, int dm) {
+          const int c = (32 * dm + vcol) >> 3;
+          const char* a0 = vl + (32 * (kstep >> 1) + 16 * (kstep & 1)) * 256 + ((c ^ vf0) << 4);
+          const char* a1 = vl + (32 * (kstep >> 1) + 16 * (kstep & 1) + 8) * 256 + ((c ^ vf1) << 4);
+          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
+          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1));
+          return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
+        bf16x8 pb[4];
+  #pragma unroll
+        for (int kstep = 0; kstep < 4; ++kstep) {
+          const int mb = kstep >> 1, uu = kstep & 1;
+  #pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const f32x2 two = {s[mb][8 * uu + e], s[mb][8 * uu + e + 1]};
+            const bf16x2 c2 = __builtin_convertvector(two, bf16x2);
+            pb[kstep][e] = c2[0];
+            pb[kstep][e + 1] = c2[1];
+          }
+        }
+        bf16x8 va[2];
+        va[0] = vfrag(0, 0);
+  #pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kstep = i >> 2, dm = i & 3;
+          if (i + 1 < 16) va[(i + 1) & 1] = vfrag((i + 1) >> 2, (i + 1) & 3);
+          acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pb[kstep], acc[dm], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
-    cur = nxt;
-  }
+      cur = nxt;
+  };
+  int u = 0;
+  for (; u < n_units && !__all(has_ref); ++u) step(u, std::true_type{});
+  for (; u < n_units; ++u) step(u, std::false_type{});
 
   // --- epilogue ---
   const float l_tot = swap_halves_sum(l_run);
@@ -516,7 +602,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       }
     }
     if (p.lse != nullptr && hl == 0)
-      p.lse[((int64_t)b * p.h_q + hq) * p.n_q + qi] = (m_run + __log2f(l_tot)) * LN2;
+      p.lse[((int64_t)b * p.h_q + hq) * p.n_q + qi] = (m_ref + __log2f(l_tot)) * LN2;
   }
 }
 
@@ -616,14 +702,17 @@ hipError_t launch_fwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   FwdArgs p;
   memset(&p, 0, sizeof(p));
   const bool rope = a.rope == SA_ROPE_HALF;
-  if (rope) {
+  if (ro.qrot != nullptr) {  // rotated (bf16: also scaled) query copy
     p.q = ro.qrot;
     p.qsT = a.d; p.qsH = (int64_t)m.n_q * a.d; p.qsB = p.qsH * a.h_q;
-    p.k = ro.krot;
-    p.ksT = a.d; p.ksH = (int64_t)m.n_k * a.d; p.ksB = p.ksH * a.h_kv;
   } else {
     p.q = a.q;
     p.qsB = a.q_stride[0]; p.qsH = a.q_stride[1]; p.qsT = a.q_stride[2];
+  }
+  if (rope) {
+    p.k = ro.krot;
+    p.ksT = a.d; p.ksH = (int64_t)m.n_k * a.d; p.ksB = p.ksH * a.h_kv;
+  } else {
     p.k = a.k;
     p.ksB = a.k_stride[0]; p.ksH = a.k_stride[1]; p.ksT = a.k_stride[2];
   }

@@ -41,6 +41,9 @@ struct RopeArgs {
   int64_t cap_rows;
   int n_cap, L;
   int n_pos;
+  int write_q;      // write the query copy (rotated when rotate is set)
+  float q_scale;    // factor applied to the stored queries
+  float cap_scale;  // factor applied to the stored capped keys
   ThetaTable theta;
 };
 
@@ -165,8 +168,8 @@ __global__ __launch_bounds__(256) void rope_qk(RopeArgs p) {
           float z1[4], z2[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            z1[e] = x1[e] * ccs[e] - x2[e] * csn[e];
-            z2[e] = x2[e] * ccs[e] + x1[e] * csn[e];
+            z1[e] = (x1[e] * ccs[e] - x2[e] * csn[e]) * p.cap_scale;
+            z2[e] = (x2[e] * ccs[e] + x1[e] * csn[e]) * p.cap_scale;
           }
           const int64_t crow = ((int64_t)b * p.h_kv + h) * p.cap_rows + pos;
           char* cd = static_cast<char*>(p.kcap) + crow * p.d * esz;
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(256) void rope_qk(RopeArgs p) {
   }
   // queries
   const int i = pos - p.q_pos0;
-  if (p.rotate && i >= 0 && i < p.n_q) {
+  if (p.write_q && i >= 0 && i < p.n_q) {
     for (int b = 0; b < p.B; ++b) {
       for (int h = 0; h < p.h_q; ++h) {
         const char* src = static_cast<const char*>(p.q) + (b * p.qsB + h * p.qsH + i * p.qsT) * esz;
@@ -187,8 +190,13 @@ __global__ __launch_bounds__(256) void rope_qk(RopeArgs p) {
         Vec4<T>::load(src + (c0 + half) * esz, x2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          y1[e] = x1[e] * cs[e] - x2[e] * sn[e];
-          y2[e] = x2[e] * cs[e] + x1[e] * sn[e];
+          if (p.rotate) {
+            y1[e] = (x1[e] * cs[e] - x2[e] * sn[e]) * p.q_scale;
+            y2[e] = (x2[e] * cs[e] + x1[e] * sn[e]) * p.q_scale;
+          } else {
+            y1[e] = x1[e] * p.q_scale;
+            y2[e] = x2[e] * p.q_scale;
+          }
         }
         const int64_t orow = ((int64_t)b * p.h_q + h) * p.n_q + i;
         char* dst = static_cast<char*>(p.qrot) + orow * p.d * esz;
@@ -208,7 +216,11 @@ hipError_t launch_rope(const sa_mask_t& m, const sa_plan_header_t& lay, const vo
   memset(&p, 0, sizeof(p));
   const bool rotate = a.rope == SA_ROPE_HALF;
   const bool gather = m.kind == SA_MASK_SEPLLM && m.sep != nullptr;
-  if (!rotate && !gather) return hipSuccess;
+  // bf16: the forward reads queries pre-multiplied by scale * log2(e) (its
+  // logits come out of the MFMA in base-2 units), so the query copy is always
+  // written; fp32 keeps the scale in the forward.
+  const bool write_q = rotate || a.dtype == SA_BF16;
+  if (!write_q && !gather) return hipSuccess;
   const char* pb = static_cast<const char*>(plan);
   p.q = a.q;
   p.qsB = a.q_stride[0]; p.qsH = a.q_stride[1]; p.qsT = a.q_stride[2];
@@ -237,8 +249,11 @@ hipError_t launch_rope(const sa_mask_t& m, const sa_plan_header_t& lay, const vo
   p.cap_rows = ro.cap_rows;
   p.n_cap = ro.n_cap;
   p.L = m.L_pretrain;
+  p.write_q = write_q ? 1 : 0;
+  p.q_scale = a.dtype == SA_BF16 ? a.scale * 1.4426950408889634f : 1.0f;
+  p.cap_scale = p.q_scale;
   p.n_pos = m.n_k;
-  if (rotate && p.q_pos0 + m.n_q > p.n_pos) p.n_pos = p.q_pos0 + m.n_q;
+  if (write_q && p.q_pos0 + m.n_q > p.n_pos) p.n_pos = p.q_pos0 + m.n_q;
   p.theta = theta;
   const int64_t threads = (int64_t)p.n_pos * (a.d / 8);
   const unsigned wg = (unsigned)ceil_div(threads, 256);
