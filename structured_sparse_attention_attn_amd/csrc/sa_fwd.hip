@@ -237,6 +237,37 @@ __device__ inline float swap_halves_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Packs the 32 weights of one lane (two 32-key halves) into the four bf16x8
+// B operands of the PV product: k-step ks takes registers 8 (ks % 2) .. +7 of
+// half ks / 2.
+__device__ inline void pack_p(const f32x16 (&s)[2], bf16x8 (&pb)[4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const f32x2 two = {s[ks >> 1][8 * (ks & 1) + e], s[ks >> 1][8 * (ks & 1) + e + 1]};
+      const bf16x2 c2 = __builtin_convertvector(two, bf16x2);
+      pb[ks][e] = c2[0];
+      pb[ks][e + 1] = c2[1];
+    }
+  }
+}
+
+// Sum of the packed (rounded) weights: O is normalised by the same bf16
+// weights it accumulates.
+__device__ inline float sum_p(const bf16x8 (&pb)[4]) {
+  const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks], pb[ks], 0, 1), one, a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks], pb[ks], 2, 3), one, a1, false);
+    a0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks], pb[ks], 4, 5), one, a0, false);
+    a1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(pb[ks], pb[ks], 6, 7), one, a1, false);
+  }
+  return a0 + a1;
+}
+
 // Per-tile unit list: [capped items] [gathered separator chunks] [items].
 struct TileUnits {
   int it0, n_items, n_capu, n_ch, nsep;
@@ -398,17 +429,32 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   // repeat its last valid row: finite values whose logits are masked out.
   const int lrow = lane >> 4;
   const int lchunk = (lane & 15) ^ (lrow << 2);
+  // byte offset of this lane's chunk in rows 4i.. for i = 4 wid + j, when a
+  // block's rows are contiguous 256-byte rows (j * 1024 is added as an immediate)
+  uint32_t loff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) loff[j] = (uint32_t)((16 * wid + lrow) * 256 + ((lchunk ^ j) << 4));
   auto issue_loads = [&](const Unit& u, int buf) {
     char* Kb = smem + buf * BUF_BYTES;
     char* Vb = Kb + BLK_BYTES;
-    const bool kfull = u.kvalid == BK, vfull = u.vvalid == BK;
+    if (u.kvalid == BK && u.vvalid == BK && u.kstride == 256 && u.vstride == 256) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = wid * 4 + j;
+        __builtin_amdgcn_global_load_lds((const void*)(u.kbase + loff[j] + j * 1024),
+                                         (__attribute__((address_space(3))) void*)(Kb + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(u.vbase + loff[j] + j * 1024),
+                                         (__attribute__((address_space(3))) void*)(Vb + i * 1024), 16, 0, 0);
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = wid * 4 + j;  // rows 4i .. 4i+3
       const int row = 4 * i + lrow;
       const int ch = lchunk ^ (j & 3);
-      const int kr = kfull ? row : min(row, u.kvalid - 1);
-      const int vr = vfull ? row : min(row, u.vvalid - 1);
+      const int kr = min(row, u.kvalid - 1);
+      const int vr = min(row, u.vvalid - 1);
       __builtin_amdgcn_global_load_lds((const void*)(u.kbase + kr * u.kstride + ch * 16),
                                        (__attribute__((address_space(3))) void*)(Kb + i * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(u.vbase + vr * u.vstride + ch * 16),
@@ -416,166 +462,161 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
     }
   };
 
+  // Per-lane LDS read bases.  K fragment (half mb, k-step ks): row 32 mb + l32,
+  // logical chunk 2 ks + hl; rows l32 and 32 + l32 share row & 15, so the
+  // swizzle is one per-lane XOR.  V^T fragment (k-step kst, d block dm) by
+  // transpose reads: lane (16-lane group g, index i) points at key
+  // kA + i/4 (+8 for the upper half of the k-step), columns
+  // 32 dm + 16 (g & 1) + 4 (i & 3) .. +3, with kA = 32 (kst/2) + 16 (kst%2) + 4 hl,
+  // so row & 15 is 4 hl + i/4 (+8).
+  const int kf = swzf(l32) ^ hl;
+  const int vrow = 4 * hl + ((lane & 15) >> 2);
+  const int vf0 = swzf(vrow), vf1 = swzf(vrow + 8);
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int vcb = vcol >> 3;  // chunk of the column within its 32-column group
+
+  // One unit.  The exact-max softmax (full_path) runs while some row of the
+  // wave has no finite reference yet, the fast path afterwards.  Every wave
+  // runs exactly one barrier per unit, whichever loop it is in.
   Unit cur;
   if (n_units > 0) {
     cur = unit_at(p, tu, 0);
     issue_loads(cur, 0);
   }
-  // One unit: the exact-max softmax (full_path) runs while some row of the
-  // wave has no finite reference yet, the fast path afterwards.  Every wave
-  // runs exactly one barrier per unit, whichever loop it is in.
   auto step = [&](int u, auto full_path) {
-      const int buf = u & 1;
-      // this wave's loads of unit u have landed; the barrier makes every wave's
-      // visible and frees the other buffer (its last reader was unit u-1)
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      __syncthreads();
-      Unit nxt;
-      if (u + 1 < n_units) {
-        nxt = unit_at(p, tu, u + 1);
-        issue_loads(nxt, buf ^ 1);
-      }
-      if (u == tu.n_capu && tu.n_capu > 0) load_q(p.q, p.qsB, p.qsH, p.qsT);  // rotated Q from here on
-      const char* Kb = smem + buf * BUF_BYTES;
-      const char* Vb = Kb + BLK_BYTES;
-      // --- S^T = K Q^T - m_ref : both 32-key halves interleaved, K fragments
-      //     read from LDS two k-steps ahead of their MFMAs ---
-      f32x16 s[2];
-      {
-        // rows l32 and 32 + l32 share row & 15, hence the swizzle; the k-step's
-        // logical chunk is 2 ks + hl
-        const char* kl = Kb + l32 * 256;
-        const int kf = swzf(l32) ^ hl;
-        auto kfrag = [&](int mb, int ks) {
-          return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + mb * 32 * 256 + (((2 * ks) ^ kf) << 4)));
-        };
-        bf16x8 a0[3], a1[3];
-        a0[0] = kfrag(0, 0); a1[0] = kfrag(1, 0);
-        a0[1] = kfrag(0, 1); a1[1] = kfrag(1, 1);
-        f32x16 c0 = negm, c1 = negm;
-  #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          if (ks + 2 < 8) {
-            a0[(ks + 2) % 3] = kfrag(0, ks + 2);
-            a1[(ks + 2) % 3] = kfrag(1, ks + 2);
-          }
-          c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[ks % 3], qf[ks], c0, 0, 0, 0);
-          c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[ks % 3], qf[ks], c1, 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
+    const int buf = u & 1;
+    // this wave's loads of unit u have landed; the barrier makes every wave's
+    // visible and frees the other buffer (its last reader was unit u-1)
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    Unit nxt;
+    if (u + 1 < n_units) {
+      nxt = unit_at(p, tu, u + 1);
+      issue_loads(nxt, buf ^ 1);
+    }
+    if (u == tu.n_capu && tu.n_capu > 0) load_q(p.q, p.qsB, p.qsH, p.qsT);  // rotated Q from here on
+    const char* Kb = smem + buf * BUF_BYTES;
+    const char* Vb = Kb + BLK_BYTES;
+
+    // --- S^T = K Q^T - m_ref: both 32-key halves interleaved, K fragments
+    //     read two k-steps ahead of their MFMAs ---
+    f32x16 s[2];
+    {
+      const char* kl = Kb + l32 * 256;
+      auto kfrag = [&](int mb, int ks) {
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + mb * 32 * 256 + (((2 * ks) ^ kf) << 4)));
+      };
+      bf16x8 a0[3], a1[3];
+      a0[0] = kfrag(0, 0);
+      a1[0] = kfrag(1, 0);
+      a0[1] = kfrag(0, 1);
+      a1[1] = kfrag(1, 1);
+      a0[2] = kfrag(0, 2);
+      a1[2] = kfrag(1, 2);
+      // the first k-step reads -m_ref as C and writes fresh accumulators
+      f32x16 c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[0], qf[0], negm, 0, 0, 0);
+      f32x16 c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[0], qf[0], negm, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 1; ks < 8; ++ks) {
+        if (ks + 2 < 8) {
+          a0[(ks + 2) % 3] = kfrag(0, ks + 2);
+          a1[(ks + 2) % 3] = kfrag(1, ks + 2);
         }
-        s[0] = c0;
-        s[1] = c1;
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[ks % 3], qf[ks], c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[ks % 3], qf[ks], c1, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      // --- mask, then the online softmax ---
-      switch (cur.mk) {
-        case MK_NONE: break;
-        case MK_COUNT: apply_mask<MK_COUNT>(p, cur, qi, hl, s); break;
-        case MK_SEPLLM: apply_mask<MK_SEPLLM>(p, cur, qi, hl, s); break;
-        case MK_LALL: apply_mask<MK_LALL>(p, cur, qi, hl, s); break;
-        case MK_LNORM: apply_mask<MK_LNORM>(p, cur, qi, hl, s); break;
-        case MK_LCAP: apply_mask<MK_LCAP>(p, cur, qi, hl, s); break;
-        default: apply_mask<MK_SEG>(p, cur, qi, hl, s); break;
-      }
-      if constexpr (!decltype(full_path)::value) {
-        // common path: p = 2^(s - m_ref) straight from the MFMA output
-        float psum = 0.f;
-  #pragma unroll
+      s[0] = c0;
+      s[1] = c1;
+    }
+
+    // --- mask, then the online softmax ---
+    switch (cur.mk) {
+      case MK_NONE: break;
+      case MK_COUNT: apply_mask<MK_COUNT>(p, cur, qi, hl, s); break;
+      case MK_SEPLLM: apply_mask<MK_SEPLLM>(p, cur, qi, hl, s); break;
+      case MK_LALL: apply_mask<MK_LALL>(p, cur, qi, hl, s); break;
+      case MK_LNORM: apply_mask<MK_LNORM>(p, cur, qi, hl, s); break;
+      case MK_LCAP: apply_mask<MK_LCAP>(p, cur, qi, hl, s); break;
+      default: apply_mask<MK_SEG>(p, cur, qi, hl, s); break;
+    }
+    bf16x8 pb[4];
+    if constexpr (!decltype(full_path)::value) {
+      // common path: p = 2^(s - m_ref) straight from the MFMA output
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r]);
+      pack_p(s, pb);
+      float psum = sum_p(pb);
+      if (__any(psum > 1024.f)) {
+        // rare: raise the reference of the rows whose values grew
+        float pm = 0.f;
+#pragma unroll
         for (int mb = 0; mb < 2; ++mb)
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(s[mb][r]);
-            s[mb][r] = e;
-            psum += e;
-          }
-        if (__any(psum > 1024.f)) {
-          // rare: raise the reference of the rows whose values grew
-          float pm = 0.f;
-  #pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-  #pragma unroll
-            for (int r = 0; r < 16; ++r) pm = fmaxf(pm, s[mb][r]);
-          pm = swap_halves_max(pm);
-          if (pm > 1.f) {
-            const float f = 1.f / pm;
-  #pragma unroll
-            for (int mb = 0; mb < 2; ++mb) s[mb] *= f;
-  #pragma unroll
-            for (int dm = 0; dm < 4; ++dm) acc[dm] *= f;
-            psum *= f;
-            l_run *= f;
-            m_ref += __log2f(pm);
-            negm = f32x16{} - m_ref;
-          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pm = fmaxf(pm, s[mb][r]);
+        pm = swap_halves_max(pm);
+        if (pm > 1.f) {
+          const float f = 1.f / pm;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) s[mb] *= f;
+#pragma unroll
+          for (int dm = 0; dm < 4; ++dm) acc[dm] *= f;
+          l_run *= f;
+          m_ref += __log2f(pm);
+          negm = f32x16{} - m_ref;
         }
-        l_run += psum;
-      } else {
-        // some row has no finite reference yet: exact max of this unit
-        float mx = NEG_INF;
-  #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-        mx = swap_halves_max(mx);  // relative to m_ref
-        float delta = 0.f;
-        if (mx != NEG_INF) delta = has_ref ? fmaxf(mx, 0.f) : mx;
-        const float alpha = __builtin_amdgcn_exp2f(-delta);
-        float psum = 0.f;
-  #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-  #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(s[mb][r] - delta);
-            s[mb][r] = e;
-            psum += e;
-          }
-  #pragma unroll
-        for (int dm = 0; dm < 4; ++dm) acc[dm] *= alpha;
-        l_run = l_run * alpha + psum;
-        m_ref += delta;
-        has_ref = has_ref || mx != NEG_INF;
-        negm = f32x16{} - m_ref;
-          }
-      // --- O^T += V^T P^T: V^T fragments by LDS transpose reads, one MFMA ahead ---
-      {
-        // lane (16-lane group g, index s) points at keys kA + s/4 (+8 for the
-        // upper half of the k-step), columns 32 dm + 16 (g & 1) + 4 (s & 3) .. +3;
-        // kA = 32 mb + 16 uu + 4 hl, so row & 15 is 4 hl + s/4 (+8)
-        const int s16 = lane & 15;
-        const int vrow = 4 * hl + (s16 >> 2);
-        const int vf0 = swzf(vrow), vf1 = swzf(vrow + 8);
-        const int vcol = 16 * ((lane >> 4) & 1) + 4 * (s16 & 3);  // within a 32-column group
-        const char* vl = Vb + vrow * 256 + ((vcol & 7) << 1);
-        auto vfrag = [&](int kstep, int dm) {
-          const int c = (32 * dm + vcol) >> 3;
-          const char* a0 = vl + (32 * (kstep >> 1) + 16 * (kstep & 1)) * 256 + ((c ^ vf0) << 4);
-          const char* a1 = vl + (32 * (kstep >> 1) + 16 * (kstep & 1) + 8) * 256 + ((c ^ vf1) << 4);
-          const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
-          const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1));
-          return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        };
-        bf16x8 pb[4];
-  #pragma unroll
-        for (int kstep = 0; kstep < 4; ++kstep) {
-          const int mb = kstep >> 1, uu = kstep & 1;
-  #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const f32x2 two = {s[mb][8 * uu + e], s[mb][8 * uu + e + 1]};
-            const bf16x2 c2 = __builtin_convertvector(two, bf16x2);
-            pb[kstep][e] = c2[0];
-            pb[kstep][e + 1] = c2[1];
-          }
-        }
-        bf16x8 va[2];
-        va[0] = vfrag(0, 0);
-  #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kstep = i >> 2, dm = i & 3;
-          if (i + 1 < 16) va[(i + 1) & 1] = vfrag((i + 1) >> 2, (i + 1) & 3);
-          acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pb[kstep], acc[dm], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        pack_p(s, pb);
+        psum = sum_p(pb);
       }
-      cur = nxt;
+      l_run += psum;
+    } else {
+      // some row has no finite reference yet: exact max of this unit
+      float mx = NEG_INF;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+      mx = swap_halves_max(mx);  // relative to m_ref
+      float delta = 0.f;
+      if (mx != NEG_INF) delta = has_ref ? fmaxf(mx, 0.f) : mx;
+      const float alpha = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r] - delta);
+      pack_p(s, pb);
+#pragma unroll
+      for (int dm = 0; dm < 4; ++dm) acc[dm] *= alpha;
+      l_run = l_run * alpha + sum_p(pb);
+      m_ref += delta;
+      has_ref = has_ref || mx != NEG_INF;
+      negm = f32x16{} - m_ref;
+    }
+
+    // --- O^T += V^T P^T: V^T fragments one MFMA ahead ---
+    {
+      const char* vl = Vb + vrow * 256 + ((vcol & 7) << 1);
+      auto vfrag = [&](int kst, int dm) {
+        const char* a0 = vl + (32 * (kst >> 1) + 16 * (kst & 1)) * 256 + (((4 * dm + vcb) ^ vf0) << 4);
+        const char* a1 = vl + (32 * (kst >> 1) + 16 * (kst & 1) + 8) * 256 + (((4 * dm + vcb) ^ vf1) << 4);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1));
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 va[2];
+      va[0] = vfrag(0, 0);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kst = i >> 2, dm = i & 3;
+        if (i + 1 < 16) va[(i + 1) & 1] = vfrag((i + 1) >> 2, (i + 1) & 3);
+        acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pb[kst], acc[dm], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    cur = nxt;
   };
   int u = 0;
   for (; u < n_units && !__all(has_ref); ++u) step(u, std::true_type{});
