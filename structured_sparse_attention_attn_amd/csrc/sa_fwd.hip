@@ -514,6 +514,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       a0[2] = kfrag(0, 2);
       a1[2] = kfrag(1, 2);
       // the first k-step reads -m_ref as C and writes fresh accumulators
+      __builtin_amdgcn_s_setprio(1);
       f32x16 c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[0], qf[0], negm, 0, 0, 0);
       f32x16 c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[0], qf[0], negm, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -527,6 +528,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
         c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[ks % 3], qf[ks], c1, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
       s[0] = c0;
       s[1] = c1;
     }
@@ -608,6 +610,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       };
       bf16x8 va[2];
       va[0] = vfrag(0, 0);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kst = i >> 2, dm = i & 3;
@@ -615,6 +618,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
         acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pb[kst], acc[dm], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     cur = nxt;
   };
