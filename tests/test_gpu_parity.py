@@ -125,6 +125,7 @@ SMALL = [
     (W.SEGMENT, dict(m=600, P=200)),
     (W.SEGMENT, dict(m=300, P=0)),
     (W.SEGMENT, dict(m=129, P=1, h_q=4, h_kv=2, batch=2)),
+    (W.SEGMENT, dict(m=200, P=33000)),  # > 512 blocks per tile: items read from the plan directly
 ]
 
 
