@@ -206,16 +206,18 @@ __device__ inline void for_each_unit(const FwdArgs& p, int b, int kvh, int t, in
 // S^T = K Q^T (keys as rows) so every lane owns one query's logits and the
 // row max / row sum stay in the lane (plus one swap between the two 32-lane
 // halves); then O^T += V^T P^T, the key order inside each 16-key step permuted
-// to match the registers the logits already sit in.  K and V blocks are
-// double-buffered in LDS (row-major, 16-byte chunks XOR-swizzled by row); the
-// next unit's global loads are in flight while the current one computes.  V^T
-// operands come straight from the row-major V block through the LDS transpose
-// read (ds_read_b64_tr_b16).
+// to match the registers the logits already sit in.  K blocks are double- and
+// V blocks triple-buffered in LDS (row-major, 16-byte chunks XOR-swizzled by
+// row), filled by direct global-to-LDS loads; the next unit's loads are in
+// flight while the current one computes.  V^T operands come straight from the
+// row-major V block through the LDS transpose read (ds_read_b64_tr_b16).  The
+// PV product runs one unit behind, before the next loads are issued: the
+// compiler orders a transpose read after every LDS-bound load in flight, so
+// issuing them afterwards keeps those reads from waiting on HBM.
 // ===========================================================================
 
 constexpr int D128 = 128;
 constexpr int BLK_BYTES = BK * 256;        // one 64 x 128 bf16 block
-constexpr int BUF_BYTES = 2 * BLK_BYTES;   // K then V
 
 // 16-byte chunk c of row r sits at chunk c ^ f(r & 15), f swapping the two
 // 2-bit halves of its argument.  Any 16 consecutive rows then spread one
@@ -226,6 +228,13 @@ __device__ inline int swzf(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ inline uint4 ld16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// Loads of plan data that no kernel of this launch writes, through the scalar
+// data cache (uniform addresses, results in scalar registers).
+template <class T>
+__device__ inline T ld_uniform(const T* p) {
+  return *reinterpret_cast<const __attribute__((address_space(4))) T*>(reinterpret_cast<uintptr_t>(p));
+}
 
 __device__ inline float swap_halves_max(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -284,7 +293,7 @@ __device__ inline Unit unit_at(const FwdArgs& p, const TileUnits& tu, int u) {
   x.count = 0;
   x.sbits = 0;
   if (u < tu.n_capu) {
-    const int blk = p.items[tu.it0 + u] & 0xffffff;
+    const int blk = ld_uniform(p.items + tu.it0 + u) & 0xffffff;
     x.kbase = tu.capb + (int64_t)blk * BK * (D128 * 2);
     x.kstride = D128 * 2;
     x.kvalid = min(BK, p.n_cap - blk * BK);
@@ -309,7 +318,7 @@ __device__ inline Unit unit_at(const FwdArgs& p, const TileUnits& tu, int u) {
     return x;
   }
   u -= tu.n_ch;
-  const int item = p.items[tu.it0 + u];
+  const int item = ld_uniform(p.items + tu.it0 + u);
   const int blk = item & 0xffffff;
   const int fl = item >> 24;
   x.kbase = tu.kb + (int64_t)blk * BK * tu.kst;
@@ -324,7 +333,7 @@ __device__ inline Unit unit_at(const FwdArgs& p, const TileUnits& tu, int u) {
     x.mk = MK_NONE;
   } else if (p.kind == SA_MASK_SEPLLM) {
     x.mk = MK_SEPLLM;
-    x.sbits = p.sep_bits[blk];
+    x.sbits = ld_uniform(p.sep_bits + blk);
   } else if (p.kind == SA_MASK_LAMBDA) {
     x.mk = MK_LALL;
   } else {
@@ -369,8 +378,10 @@ __device__ inline void apply_mask(const FwdArgs& p, const Unit& u, int qi, int h
 }
 
 __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF_BYTES];  // [buf][K|V]
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // K blocks double-buffered, V blocks triple-buffered: [K0 K1 V0 V1 V2]
+  __shared__ __attribute__((aligned(16))) char smem[5 * BLK_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hl = lane >> 5;
   int b, kvh, t, hq;
   map_unit(p, b, kvh, t, hq);
@@ -379,12 +390,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   const bool qok = qi < p.n_q;
 
   TileUnits tu;
-  tu.it0 = p.tile_ptr[t];
-  tu.n_items = p.tile_ptr[t + 1] - tu.it0;
+  tu.it0 = ld_uniform(p.tile_ptr + t);
+  tu.n_items = ld_uniform(p.tile_ptr + t + 1) - tu.it0;
   tu.n_capu = 0;
   if (p.use_cap)
-    while (tu.n_capu < tu.n_items && ((p.items[tu.it0 + tu.n_capu] >> 24) & SA_ITEM_CAPPED)) ++tu.n_capu;
-  tu.nsep = p.gather ? p.sep_count[t] : 0;
+    while (tu.n_capu < tu.n_items && ((ld_uniform(p.items + tu.it0 + tu.n_capu) >> 24) & SA_ITEM_CAPPED)) ++tu.n_capu;
+  tu.nsep = p.gather ? ld_uniform(p.sep_count + t) : 0;
   tu.n_ch = (tu.nsep + BK - 1) / BK;
   tu.kb = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH) * 2;
   tu.vb = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH) * 2;
@@ -429,35 +440,42 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   // repeat its last valid row: finite values whose logits are masked out.
   const int lrow = lane >> 4;
   const int lchunk = (lane & 15) ^ (lrow << 2);
-  // byte offset of this lane's chunk in rows 4i.. for i = 4 wid + j, when a
-  // block's rows are contiguous 256-byte rows (j * 1024 is added as an immediate)
-  uint32_t loff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) loff[j] = (uint32_t)((16 * wid + lrow) * 256 + ((lchunk ^ j) << 4));
-  auto issue_loads = [&](const Unit& u, int buf) {
-    char* Kb = smem + buf * BUF_BYTES;
-    char* Vb = Kb + BLK_BYTES;
+  // this lane's row (bits 8+) and logical chunk (bits 4..7) for j = 0; the
+  // j-th instruction's offset is lofs ^ (j << 4) + j * 1024.  The offsets are
+  // recomputed from lofs at each use (a 32-bit offset next to a uniform base
+  // address, so each load is one instruction with no address arithmetic).
+  const uint32_t lofs = (uint32_t)((16 * wid + lrow) * 256 + (lchunk << 4));
+  auto issue_loads = [&](const Unit& u, int kslot, int vslot) {
+    char* Kb = smem + kslot * BLK_BYTES;
+    char* Vb = smem + (2 + vslot) * BLK_BYTES;
+    uint32_t lo = lofs;
+    __asm__ volatile("" : "+v"(lo));
     if (u.kvalid == BK && u.vvalid == BK && u.kstride == 256 && u.vstride == 256) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int i = wid * 4 + j;
-        __builtin_amdgcn_global_load_lds((const void*)(u.kbase + loff[j] + j * 1024),
+        const uint32_t o = lo ^ (uint32_t)(j << 4);
+        const char* kj = u.kbase + j * 1024;
+        const char* vj = u.vbase + j * 1024;
+        __asm__ volatile("" : "+s"(kj), "+s"(vj));  // uniform bases: one scalar add each
+        __builtin_amdgcn_global_load_lds((const void*)(kj + o),
                                          (__attribute__((address_space(3))) void*)(Kb + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(u.vbase + loff[j] + j * 1024),
+        __builtin_amdgcn_global_load_lds((const void*)(vj + o),
                                          (__attribute__((address_space(3))) void*)(Vb + i * 1024), 16, 0, 0);
       }
       return;
     }
+    const int r0 = (int)(lo >> 8);
+    const uint32_t c0 = lo & 0xF0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = wid * 4 + j;  // rows 4i .. 4i+3
-      const int row = 4 * i + lrow;
-      const int ch = lchunk ^ (j & 3);
-      const int kr = min(row, u.kvalid - 1);
-      const int vr = min(row, u.vvalid - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(u.kbase + kr * u.kstride + ch * 16),
+      const uint32_t ch = c0 ^ (uint32_t)(j << 4);
+      const int kr = min(r0 + 4 * j, u.kvalid - 1);
+      const int vr = min(r0 + 4 * j, u.vvalid - 1);
+      __builtin_amdgcn_global_load_lds((const void*)(u.kbase + (int64_t)kr * u.kstride + ch),
                                        (__attribute__((address_space(3))) void*)(Kb + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(u.vbase + vr * u.vstride + ch * 16),
+      __builtin_amdgcn_global_load_lds((const void*)(u.vbase + (int64_t)vr * u.vstride + ch),
                                        (__attribute__((address_space(3))) void*)(Vb + i * 1024), 16, 0, 0);
     }
   };
@@ -475,28 +493,61 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int vcb = vcol >> 3;  // chunk of the column within its 32-column group
 
-  // One unit.  The exact-max softmax (full_path) runs while some row of the
-  // wave has no finite reference yet, the fast path afterwards.  Every wave
-  // runs exactly one barrier per unit, whichever loop it is in.
+  // O^T += V^T P^T for the unit whose weights are in pb and whose V block is
+  // in slot vslot: V^T fragments two MFMAs ahead
+  auto pv = [&](const bf16x8 (&pb)[4], int vslot) {
+    const char* vl = smem + (2 + vslot) * BLK_BYTES + vrow * 256 + ((vcol & 7) << 1);
+    auto vfrag = [&](int kst, int dm) {
+      const char* a0 = vl + (32 * (kst >> 1) + 16 * (kst & 1)) * 256 + (((4 * dm + vcb) ^ vf0) << 4);
+      const char* a1 = vl + (32 * (kst >> 1) + 16 * (kst & 1) + 8) * 256 + (((4 * dm + vcb) ^ vf1) << 4);
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 va[3];
+    va[0] = vfrag(0, 0);
+    va[1] = vfrag(0, 1);
+    __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kst = i >> 2, dm = i & 3;
+      if (i + 2 < 16) va[(i + 2) % 3] = vfrag((i + 2) >> 2, (i + 2) & 3);
+      acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], pb[kst], acc[dm], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // One unit per step, the PV product one unit behind: step u accumulates
+  // P(u-1) V(u-1) first (no block load is in flight then), issues the loads
+  // of unit u+1, and computes S(u) and P(u).  K(u+1) goes to the K slot that
+  // S(u-1) read, V(u+1) to the V slot that P(u-2) V(u-2) read, both finished
+  // before this step's barrier.  The exact-max softmax (full_path) runs while
+  // some row of the wave has no finite reference yet, the fast path
+  // afterwards.  Every wave runs exactly one barrier per unit, whichever loop
+  // it is in.
   Unit cur;
   if (n_units > 0) {
     cur = unit_at(p, tu, 0);
-    issue_loads(cur, 0);
+    issue_loads(cur, 0, 0);
   }
+  bf16x8 pb[4];  // P(u-1), carried into step u
+  int vs_prev = 2, vs_next = 1;  // V slots of units u-1 and u+1 (u % 3 = 0 at u = 0)
   auto step = [&](int u, auto full_path) {
     const int buf = u & 1;
     // this wave's loads of unit u have landed; the barrier makes every wave's
-    // visible and frees the other buffer (its last reader was unit u-1)
+    // visible and ends every read of the slots the next loads overwrite
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
+    if (u > 0) pv(pb, vs_prev);
     Unit nxt;
     if (u + 1 < n_units) {
       nxt = unit_at(p, tu, u + 1);
-      issue_loads(nxt, buf ^ 1);
+      issue_loads(nxt, buf ^ 1, vs_next);
     }
-    if (u == tu.n_capu && tu.n_capu > 0) load_q(p.q, p.qsB, p.qsH, p.qsT);  // rotated Q from here on
-    const char* Kb = smem + buf * BUF_BYTES;
-    const char* Vb = Kb + BLK_BYTES;
+    vs_prev = vs_prev == 2 ? 0 : vs_prev + 1;
+    vs_next = vs_next == 2 ? 0 : vs_next + 1;
+    const char* Kb = smem + buf * BLK_BYTES;
 
     // --- S^T = K Q^T - m_ref: both 32-key halves interleaved, K fragments
     //     read two k-steps ahead of their MFMAs ---
@@ -543,7 +594,6 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       case MK_LCAP: apply_mask<MK_LCAP>(p, cur, qi, hl, s); break;
       default: apply_mask<MK_SEG>(p, cur, qi, hl, s); break;
     }
-    bf16x8 pb[4];
     if constexpr (!decltype(full_path)::value) {
       // common path: p = 2^(s - m_ref) straight from the MFMA output
 #pragma unroll
@@ -598,33 +648,16 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       negm = f32x16{} - m_ref;
     }
 
-    // --- O^T += V^T P^T: V^T fragments one MFMA ahead ---
-    {
-      const char* vl = Vb + vrow * 256 + ((vcol & 7) << 1);
-      auto vfrag = [&](int kst, int dm) {
-        const char* a0 = vl + (32 * (kst >> 1) + 16 * (kst & 1)) * 256 + (((4 * dm + vcb) ^ vf0) << 4);
-        const char* a1 = vl + (32 * (kst >> 1) + 16 * (kst & 1) + 8) * 256 + (((4 * dm + vcb) ^ vf1) << 4);
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1));
-        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      };
-      bf16x8 va[2];
-      va[0] = vfrag(0, 0);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kst = i >> 2, dm = i & 3;
-        if (i + 1 < 16) va[(i + 1) & 1] = vfrag((i + 1) >> 2, (i + 1) & 3);
-        acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pb[kst], acc[dm], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
+    // the rotated queries for the units after the capped ones: loaded once Q
+    // is no longer read by this step, and waited for with the next unit's
+    // K/V at the top of the next step
+    if (u + 1 == tu.n_capu) load_q(p.q, p.qsB, p.qsH, p.qsT);
     cur = nxt;
   };
   int u = 0;
   for (; u < n_units && !__all(has_ref); ++u) step(u, std::true_type{});
   for (; u < n_units; ++u) step(u, std::false_type{});
+  if (n_units > 0) pv(pb, vs_prev);  // the last unit (its V landed before the last barrier)
 
   // --- epilogue ---
   const float l_tot = swap_halves_sum(l_run);
