@@ -47,6 +47,60 @@ def pair_count_per_head(wl, sep_np):
     return int((np.minimum(i + 1, wl.w) + extra).sum())
 
 
+def issued_flops(wl, host_plan):
+    """MFMA work the fused forward issues: every unit of a tile is a full
+    64-key x 128-query block (both products), masked pairs included."""
+    import numpy as np
+    tp = host_plan["tile_ptr"].astype(np.int64)
+    items = host_plan["items"]
+    n_items = tp[1:] - tp[:-1]
+    n_cap = np.zeros_like(n_items)
+    if wl.mode == "lambda":
+        capped = ((items >> 24) & 2) != 0
+        cs = np.concatenate([[0], np.cumsum(capped)])
+        n_cap = cs[tp[1:]] - cs[tp[:-1]]
+    n_ch = (host_plan["sep_count"].astype(np.int64) + 63) // 64 if wl.mode == "sepllm" else 0
+    units = int((n_items + n_cap + n_ch).sum())
+    return 4.0 * 64 * 128 * wl.d * units * wl.h_q * wl.batch
+
+
+def stage_bytes(wl, sep_np, plan_bytes):
+    """Algorithmic HBM bytes per launch of the plan, RoPE and top-k stages."""
+    import numpy as np
+    esz = 2 if wl.dtype == "bf16" else 4
+    d, B = wl.d, wl.batch
+    n_sep = 0
+    if wl.mode == "sepllm" and sep_np is not None:
+        g0 = 64 * ((wl.a + 63) // 64)
+        n_sep = int(sep_np[g0:].astype(np.int64).sum())
+    n_cap = min(wl.n_s, wl.n_k) if wl.mode == "lambda" else 0
+    rope = esz * d * B * (2 * wl.h_q * wl.n_q + 2 * wl.h_kv * wl.n_k + 3 * wl.h_kv * n_sep + wl.h_kv * n_cap)
+    plan = (wl.n_k if sep_np is not None else 0) + plan_bytes
+    out = {"plan": plan, "rope": rope}
+    if wl.mode == "segment":
+        nl = wl.n_local
+        out["topk"] = esz * d * (wl.h_q - nl) * (wl.pool_len + 1 + 4 * wl.P)
+    return out
+
+
+def gemm_ceiling_tflops(torch):
+    """Dense bf16 GEMM through torch (hipBLASLt): a measured MFMA ceiling."""
+    n = 8192
+    a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+    for _ in range(3):
+        torch.matmul(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
 def source_sha(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -112,6 +166,8 @@ def main():
     ap.add_argument("--workload", type=int, default=3, help="1..5 (default: the 32K Lambda layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--no-gemm-ceiling", action="store_true",
+                    help="skip the dense bf16 GEMM reference measurement")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB device copy (scale for PMC byte counters)")
     args = ap.parse_args()
@@ -125,8 +181,8 @@ def main():
     import torch
 
     import workloads as W
-    from structured_sparse_attention_attn_amd import (fwd_args, sparse_attn_attend, sparse_attn_plan,
-                                                      sparse_attn_rope)
+    from structured_sparse_attention_attn_amd import (fwd_args, plan_to_host, sparse_attn_attend,
+                                                      sparse_attn_plan, sparse_attn_rope)
     from structured_sparse_attention_attn_amd.pipeline import SparseAttention, TopK
 
     wl = W.WORKLOADS[args.workload]
@@ -210,6 +266,18 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(attend_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attend_tflops / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic}
+    host_plan = plan_to_host(sa.mask, sa.plan)
+    iflops = issued_flops(wl, host_plan)
+    issued = {"flops_per_launch": iflops, "ratio_to_effective": round(iflops / flops, 4),
+              "tflops": round(iflops / (stage["attend"] * 1e-3) / 1e12, 2),
+              "frac": round(iflops / (stage["attend"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    sb = stage_bytes(wl, None if sep is None else sep.numpy(), int(host_plan["header"].total_bytes))
+    stage_roofline = {}
+    for name_, nbytes in sb.items():
+        if name_ in stage:
+            gbs = nbytes / (stage[name_] * 1e-3) / 1e9
+            stage_roofline[name_] = {"bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
+                                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
     props = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC,
@@ -234,8 +302,12 @@ def main():
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {k_: round(v_, 4) for k_, v_ in stage.items()},
         "roofline": roofline,
+        "issued_mfma": issued,
+        "stages_roofline": stage_roofline,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    if not args.no_gemm_ceiling:
+        out["gemm_ceiling_tflops"] = round(gemm_ceiling_tflops(torch), 1)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget_s)
     print(json.dumps(out), flush=True)

@@ -191,7 +191,8 @@ int sa_topk_workspace_bytes(int32_t n_heads, int32_t pool_len, size_t *bytes);
  * Arguments:
  *   dtype        SA_F32 or SA_BF16 for q_score, pool_k, pool_v, pref_k, pref_v.
  *   q_score      row h at q_score + h*q_head_stride elements, d contiguous (raw).
- *   pool_k       row j of head h at pool_k + h*pool_head_stride + j*pool_row_stride.
+ *   pool_k       row j of head h at pool_k + h*pool_head_stride + j*pool_row_stride;
+ *                16-byte aligned, strides (in elements) multiples of 16 bytes.
  *   pool_v       same strides; NULL = no gather.
  *   idx          out int32 [n_heads, k] contiguous.
  *   score        out fp64 [n_heads, k] contiguous (s at idx), or NULL.

@@ -276,6 +276,8 @@ int topk_retrieve(int32_t dtype, int32_t n_heads, int32_t pool_len, int32_t d, i
   if (q_head_stride < 0 || pool_head_stride < 0 || pool_row_stride < 0)
     return fail(SA_EINVAL, "strides must be >= 0");
   const int esz = dtype == SA_BF16 ? 2 : 4;
+  if (!aligned16(pool_k) || (pool_head_stride * esz) % 16 || (pool_row_stride * esz) % 16)
+    return fail(SA_EINVAL, "pool_k must be 16-byte aligned with strides that are multiples of 16 bytes");
   if (pool_v != nullptr) {
     if (pref_k == nullptr || pref_v == nullptr)
       return fail(SA_EINVAL, "pref_k and pref_v are required when pool_v is given");

@@ -54,39 +54,6 @@ __device__ inline u16 f2bf(float f) {  // round to nearest even (inputs are fini
   return (u16)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-template <typename T>
-struct Vec4;
-template <>
-struct Vec4<float> {
-  __device__ static void load(const void* p, float* x) {
-    const float4 t = *reinterpret_cast<const float4*>(p);
-    x[0] = t.x; x[1] = t.y; x[2] = t.z; x[3] = t.w;
-  }
-  __device__ static void store(void* p, const float* x) {
-    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
-  }
-  __device__ static void copy(void* dst, const void* src) {
-    *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
-  }
-};
-template <>
-struct Vec4<u16> {
-  __device__ static void load(const void* p, float* x) {
-    const uint2 t = *reinterpret_cast<const uint2*>(p);
-    x[0] = bf2f((u16)(t.x & 0xffffu)); x[1] = bf2f((u16)(t.x >> 16));
-    x[2] = bf2f((u16)(t.y & 0xffffu)); x[3] = bf2f((u16)(t.y >> 16));
-  }
-  __device__ static void store(void* p, const float* x) {
-    uint2 t;
-    t.x = (unsigned)f2bf(x[0]) | ((unsigned)f2bf(x[1]) << 16);
-    t.y = (unsigned)f2bf(x[2]) | ((unsigned)f2bf(x[3]) << 16);
-    *reinterpret_cast<uint2*>(p) = t;
-  }
-  __device__ static void copy(void* dst, const void* src) {
-    *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
-  }
-};
-
 // cos and sin of pos * theta: fp64 product and reduction, fp32 sincos.
 __device__ inline void angle_sincos(double pos, double th, float* c, float* s) {
   const double TWO_PI_HI = 6.283185307179586232;     // nearest double to 2*pi
@@ -99,110 +66,192 @@ __device__ inline void angle_sincos(double pos, double th, float* c, float* s) {
   sincosf((float)r, s, c);
 }
 
-// Thread = (position p, group of 4 rotation pairs).  The sincos values are
-// computed once per thread and reused for every batch row and head.
+// 8 consecutive elements of a row: 16 bytes (bf16) or 32 bytes (fp32).
+template <typename T>
+struct Row8;
+template <>
+struct Row8<u16> {
+  uint4 w;
+  __device__ void load(const void* p) { w = *reinterpret_cast<const uint4*>(p); }
+  __device__ void store(void* p) const { *reinterpret_cast<uint4*>(p) = w; }
+  __device__ void get(float* x) const {
+    const unsigned u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf2f((u16)(u[e] & 0xffffu));
+      x[2 * e + 1] = bf2f((u16)(u[e] >> 16));
+    }
+  }
+  __device__ void set(const float* x) {
+    unsigned u[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = (unsigned)f2bf(x[2 * e]) | ((unsigned)f2bf(x[2 * e + 1]) << 16);
+    w = make_uint4(u[0], u[1], u[2], u[3]);
+  }
+};
+template <>
+struct Row8<float> {
+  float4 a, b;
+  __device__ void load(const void* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ void store(void* p) const {
+    reinterpret_cast<float4*>(p)[0] = a;
+    reinterpret_cast<float4*>(p)[1] = b;
+  }
+  __device__ void get(float* x) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+  __device__ void set(const float* x) {
+    a = make_float4(x[0], x[1], x[2], x[3]);
+    b = make_float4(x[4], x[5], x[6], x[7]);
+  }
+};
+
+constexpr int ROPE_ROWS = 8;  // rows (batch x head) per thread
+
+// Thread = (position, group of 8 rotation pairs, chunk of ROPE_ROWS rows).
+// Rows 0 .. B*h_kv-1 are the key rows of the position, the rest its query
+// rows.  The sincos values are computed once per thread and reused for its
+// rows; all of a thread's row loads are issued before its first store.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_qk(RopeArgs p) {
   const int esz = sizeof(T);
-  const int tpr = p.d / 8;  // threads per position: d/2 pairs, 4 per thread
+  const int tpr = p.d / 16;  // threads per position: d/2 pairs, 8 per thread
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int pos = (int)(gid / tpr);
   if (pos >= p.n_pos) return;
-  const int c0 = (int)(gid % tpr) * 4;
+  const int c0 = (int)(gid % tpr) * 8;
   const int half = p.d / 2;
-  float cs[4], sn[4];
+  const int n_krows = pos < p.n_k ? p.B * p.h_kv : 0;
+  const int i = pos - p.q_pos0;
+  const int n_qrows = (p.write_q && i >= 0 && i < p.n_q) ? p.B * p.h_q : 0;
+  const int r_begin = blockIdx.y * ROPE_ROWS;
+  if (r_begin >= p.B * (p.h_kv + p.h_q)) return;
+  float cs[8], sn[8];
   if (p.rotate) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) angle_sincos((double)pos, p.theta.th[c0 + e], &cs[e], &sn[e]);
+    for (int e = 0; e < 8; ++e) angle_sincos((double)pos, p.theta.th[c0 + e], &cs[e], &sn[e]);
   }
-  // keys
-  if (pos < p.n_k) {
+  // key-row extras of this position: separator rank, capped rotation
+  bool is_sep = false;
+  int64_t rank = 0;
+  if (pos < p.n_k && p.gather && pos >= p.g0) {
     const int blk = pos / BK;
-    bool is_sep = false;
-    int64_t rank = 0;
-    if (p.gather && pos >= p.g0) {
-      const unsigned long long word = p.sep_bits[blk];
-      const int r = pos - blk * BK;
-      if ((word >> r) & 1ull) {
-        is_sep = true;
-        rank = p.blk_sep[blk] + __popcll(word & ((r == 0) ? 0ull : (~0ull >> (64 - r))));
-      }
-    }
-    const bool is_cap = p.rotate && pos < p.n_cap;
-    float ccs[4], csn[4];
-    if (is_cap) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) angle_sincos(-(double)p.L, p.theta.th[c0 + e], &ccs[e], &csn[e]);
-    }
-    for (int b = 0; b < p.B; ++b) {
-      for (int h = 0; h < p.h_kv; ++h) {
-        const char* src = static_cast<const char*>(p.k) + (b * p.ksB + h * p.ksH + pos * p.ksT) * esz;
-        const int64_t orow = ((int64_t)b * p.h_kv + h) * p.n_k + pos;
-        float x1[4], x2[4], y1[4], y2[4];
-        Vec4<T>::load(src + c0 * esz, x1);
-        Vec4<T>::load(src + (c0 + half) * esz, x2);
-        if (p.rotate) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            y1[e] = x1[e] * cs[e] - x2[e] * sn[e];
-            y2[e] = x2[e] * cs[e] + x1[e] * sn[e];
-          }
-          char* dst = static_cast<char*>(p.krot) + orow * p.d * esz;
-          Vec4<T>::store(dst + c0 * esz, y1);
-          Vec4<T>::store(dst + (c0 + half) * esz, y2);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { y1[e] = x1[e]; y2[e] = x2[e]; }
-        }
-        if (is_sep) {
-          const int64_t srow = ((int64_t)b * p.h_kv + h) * p.sep_rows + rank;
-          char* kd = static_cast<char*>(p.ksep) + srow * p.d * esz;
-          Vec4<T>::store(kd + c0 * esz, y1);
-          Vec4<T>::store(kd + (c0 + half) * esz, y2);
-          const char* vs = static_cast<const char*>(p.v) + (b * p.vsB + h * p.vsH + pos * p.vsT) * esz;
-          char* vd = static_cast<char*>(p.vsep) + srow * p.d * esz;
-          Vec4<T>::copy(vd + c0 * esz, vs + c0 * esz);
-          Vec4<T>::copy(vd + (c0 + half) * esz, vs + (c0 + half) * esz);
-        }
-        if (is_cap) {
-          float z1[4], z2[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            z1[e] = (x1[e] * ccs[e] - x2[e] * csn[e]) * p.cap_scale;
-            z2[e] = (x2[e] * ccs[e] + x1[e] * csn[e]) * p.cap_scale;
-          }
-          const int64_t crow = ((int64_t)b * p.h_kv + h) * p.cap_rows + pos;
-          char* cd = static_cast<char*>(p.kcap) + crow * p.d * esz;
-          Vec4<T>::store(cd + c0 * esz, z1);
-          Vec4<T>::store(cd + (c0 + half) * esz, z2);
-        }
-      }
+    const unsigned long long word = p.sep_bits[blk];
+    const int r = pos - blk * BK;
+    if ((word >> r) & 1ull) {
+      is_sep = true;
+      rank = p.blk_sep[blk] + __popcll(word & ((r == 0) ? 0ull : (~0ull >> (64 - r))));
     }
   }
-  // queries
-  const int i = pos - p.q_pos0;
-  if (p.write_q && i >= 0 && i < p.n_q) {
-    for (int b = 0; b < p.B; ++b) {
-      for (int h = 0; h < p.h_q; ++h) {
-        const char* src = static_cast<const char*>(p.q) + (b * p.qsB + h * p.qsH + i * p.qsT) * esz;
-        float x1[4], x2[4], y1[4], y2[4];
-        Vec4<T>::load(src + c0 * esz, x1);
-        Vec4<T>::load(src + (c0 + half) * esz, x2);
+  const bool is_cap = p.rotate && pos < p.n_cap;
+  float ccs[8], csn[8];
+  if (is_cap) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (p.rotate) {
-            y1[e] = (x1[e] * cs[e] - x2[e] * sn[e]) * p.q_scale;
-            y2[e] = (x2[e] * cs[e] + x1[e] * sn[e]) * p.q_scale;
-          } else {
-            y1[e] = x1[e] * p.q_scale;
-            y2[e] = x2[e] * p.q_scale;
-          }
-        }
-        const int64_t orow = ((int64_t)b * p.h_q + h) * p.n_q + i;
-        char* dst = static_cast<char*>(p.qrot) + orow * p.d * esz;
-        Vec4<T>::store(dst + c0 * esz, y1);
-        Vec4<T>::store(dst + (c0 + half) * esz, y2);
+    for (int e = 0; e < 8; ++e) angle_sincos(-(double)p.L, p.theta.th[c0 + e], &ccs[e], &csn[e]);
+  }
+  const int hk = p.B * p.h_kv;
+  Row8<T> in1[ROPE_ROWS], in2[ROPE_ROWS];
+#pragma unroll
+  for (int rr = 0; rr < ROPE_ROWS; ++rr) {
+    const int r = r_begin + rr;
+    const char* src = nullptr;
+    if (r < hk) {
+      if (r < n_krows) {
+        const int b = r / p.h_kv, h = r - b * p.h_kv;
+        src = static_cast<const char*>(p.k) + (b * p.ksB + h * p.ksH + pos * p.ksT) * esz;
       }
+    } else if (r - hk < n_qrows) {
+      const int b = (r - hk) / p.h_q, h = (r - hk) - b * p.h_q;
+      src = static_cast<const char*>(p.q) + (b * p.qsB + h * p.qsH + (int64_t)i * p.qsT) * esz;
+    }
+    if (src) {
+      in1[rr].load(src + c0 * esz);
+      in2[rr].load(src + (c0 + half) * esz);
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < ROPE_ROWS; ++rr) {
+    const int r = r_begin + rr;
+    float x1[8], x2[8], y1[8], y2[8];
+    if (r < hk) {
+      if (r >= n_krows) continue;
+      const int b = r / p.h_kv, h = r - b * p.h_kv;
+      in1[rr].get(x1);
+      in2[rr].get(x2);
+      const int64_t orow = ((int64_t)b * p.h_kv + h) * p.n_k + pos;
+      if (p.rotate) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y1[e] = x1[e] * cs[e] - x2[e] * sn[e];
+          y2[e] = x2[e] * cs[e] + x1[e] * sn[e];
+        }
+        Row8<T> o1, o2;
+        o1.set(y1);
+        o2.set(y2);
+        char* dst = static_cast<char*>(p.krot) + orow * p.d * esz;
+        o1.store(dst + c0 * esz);
+        o2.store(dst + (c0 + half) * esz);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { y1[e] = x1[e]; y2[e] = x2[e]; }
+      }
+      if (is_sep) {
+        const int64_t srow = ((int64_t)b * p.h_kv + h) * p.sep_rows + rank;
+        char* kd = static_cast<char*>(p.ksep) + srow * p.d * esz;
+        Row8<T> o1, o2;
+        o1.set(y1);
+        o2.set(y2);
+        o1.store(kd + c0 * esz);
+        o2.store(kd + (c0 + half) * esz);
+        const char* vs = static_cast<const char*>(p.v) + (b * p.vsB + h * p.vsH + pos * p.vsT) * esz;
+        char* vd = static_cast<char*>(p.vsep) + srow * p.d * esz;
+        Row8<T> v1, v2;
+        v1.load(vs + c0 * esz);
+        v2.load(vs + (c0 + half) * esz);
+        v1.store(vd + c0 * esz);
+        v2.store(vd + (c0 + half) * esz);
+      }
+      if (is_cap) {
+        float z1[8], z2[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          z1[e] = (x1[e] * ccs[e] - x2[e] * csn[e]) * p.cap_scale;
+          z2[e] = (x2[e] * ccs[e] + x1[e] * csn[e]) * p.cap_scale;
+        }
+        const int64_t crow = ((int64_t)b * p.h_kv + h) * p.cap_rows + pos;
+        char* cd = static_cast<char*>(p.kcap) + crow * p.d * esz;
+        Row8<T> o1, o2;
+        o1.set(z1);
+        o2.set(z2);
+        o1.store(cd + c0 * esz);
+        o2.store(cd + (c0 + half) * esz);
+      }
+    } else {
+      if (r - hk >= n_qrows) continue;
+      const int b = (r - hk) / p.h_q, h = (r - hk) - b * p.h_q;
+      in1[rr].get(x1);
+      in2[rr].get(x2);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        if (p.rotate) {
+          y1[e] = (x1[e] * cs[e] - x2[e] * sn[e]) * p.q_scale;
+          y2[e] = (x2[e] * cs[e] + x1[e] * sn[e]) * p.q_scale;
+        } else {
+          y1[e] = x1[e] * p.q_scale;
+          y2[e] = x2[e] * p.q_scale;
+        }
+      }
+      const int64_t orow = ((int64_t)b * p.h_q + h) * p.n_q + i;
+      char* dst = static_cast<char*>(p.qrot) + orow * p.d * esz;
+      Row8<T> o1, o2;
+      o1.set(y1);
+      o2.set(y2);
+      o1.store(dst + c0 * esz);
+      o2.store(dst + (c0 + half) * esz);
     }
   }
 }
@@ -255,12 +304,13 @@ hipError_t launch_rope(const sa_mask_t& m, const sa_plan_header_t& lay, const vo
   p.n_pos = m.n_k;
   if (write_q && p.q_pos0 + m.n_q > p.n_pos) p.n_pos = p.q_pos0 + m.n_q;
   p.theta = theta;
-  const int64_t threads = (int64_t)p.n_pos * (a.d / 8);
+  const int64_t threads = (int64_t)p.n_pos * (a.d / 16);
   const unsigned wg = (unsigned)ceil_div(threads, 256);
+  const unsigned chunks = (unsigned)ceil_div((int64_t)a.batch * (a.h_kv + a.h_q), ROPE_ROWS);
   if (a.dtype == SA_BF16)
-    hipLaunchKernelGGL(rope_qk<unsigned short>, dim3(wg), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(rope_qk<unsigned short>, dim3(wg, chunks), dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL(rope_qk<float>, dim3(wg), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(rope_qk<float>, dim3(wg, chunks), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

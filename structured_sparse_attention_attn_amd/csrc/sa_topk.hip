@@ -6,8 +6,9 @@
 //    (each bf16/fp32 product is exact in fp64, so the chain equals plain
 //    multiply-then-add in the same order); stored as an order-preserving
 //    64-bit key (+0 and -0 share one key).
-// 2. topk_select: one work group per head; radix select (8 passes of 8 bits)
-//    finds the k-th largest key T; then each thread takes a contiguous run of
+// 2. topk_select: one work group per head; radix select (a 12-bit digit over
+//    all keys, the rest over the keys sharing that prefix, in LDS when they
+//    fit) finds the k-th largest key T; then each thread takes a contiguous run of
 //    keys and one block scan gives every selected index its output slot, so
 //    idx comes out in ascending pool order with ties at T taken from the
 //    lowest indices.
@@ -41,6 +42,8 @@ __device__ inline double elem<float>(const float* p, int c) {
   return (double)p[c];
 }
 
+// Thread = one pool key: its row in 16-byte pieces (rows are 16-byte
+// aligned), the fp64 chain in c order.
 template <typename T>
 __global__ __launch_bounds__(256) void topk_score(const T* q, int64_t q_hs, const T* pool,
                                                   int64_t p_hs, int64_t p_rs, int n, int d,
@@ -52,8 +55,14 @@ __global__ __launch_bounds__(256) void topk_score(const T* q, int64_t q_hs, cons
   const int j = blockIdx.x * 256 + threadIdx.x;
   if (j >= n) return;
   const T* row = pool + h * p_hs + (int64_t)j * p_rs;
+  constexpr int PER = 16 / sizeof(T);
   double acc = 0.0;
-  for (int c = 0; c < d; ++c) acc = fma(qs[c], elem<T>(row, c), acc);
+  for (int c0 = 0; c0 < d; c0 += PER) {
+    const uint4 w = *reinterpret_cast<const uint4*>(row + c0);
+    const T* e = reinterpret_cast<const T*>(&w);
+#pragma unroll
+    for (int c = 0; c < PER; ++c) acc = fma(qs[c0 + c], elem<T>(e, c), acc);
+  }
   keys[(int64_t)h * n + j] = order_key(acc);
 }
 
@@ -86,56 +95,81 @@ __device__ int block_excl_scan(int v, int* wave_tot, int* total) {
   return r;
 }
 
+constexpr int SEL_CAND = 4096;  // candidates kept in LDS after the first digit
+
 __global__ __launch_bounds__(SEL_THREADS) void topk_select(const unsigned long long* keys_all,
                                                            int n, int k, int32_t* idx_all,
                                                            double* score_all) {
-  __shared__ int hist[256];
+  __shared__ int hist[4096];
+  __shared__ unsigned long long cand[SEL_CAND];
   __shared__ int wave_tot[40];
   __shared__ unsigned long long sh_prefix;
-  __shared__ int sh_remaining;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  __shared__ int sh_remaining, sh_ncand;
+  const int tid = threadIdx.x;
   const int h = blockIdx.x;
   const unsigned long long* keys = keys_all + (int64_t)h * n;
+  // Radix select of the k-th largest key, most significant digit first: a
+  // 12-bit digit over all keys, then 8-bit digits (a 4-bit one last).  After
+  // the first digit the keys sharing the selected prefix are copied to LDS
+  // when they fit, and the remaining digits run there.
   unsigned long long prefix = 0, pmask = 0;
   int remaining = k;  // how many of the largest keys with this prefix are still wanted
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    if (tid < 256) hist[tid] = 0;
+  // one digit: histogram of (key >> shift) & (nb-1) over the keys matching the
+  // prefix, then the bin holding the remaining-th largest
+  auto digit = [&](auto&& for_keys, int shift, int nb) {
+    for (int b = tid; b < nb; b += SEL_THREADS) hist[b] = 0;
     __syncthreads();
-    for (int j = tid; j < n; j += SEL_THREADS) {
-      const unsigned long long key = keys[j];
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
-    }
+    for_keys([&](unsigned long long key) {
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1);
+    });
     __syncthreads();
-    if (wid == 0) {
-      // lane owns bins 4*lane .. 4*lane+3; suffix sums from the top bin down
-      const int b0 = 4 * lane;
-      const int c3 = hist[b0 + 3], c2 = hist[b0 + 2], c1 = hist[b0 + 1], c0 = hist[b0];
-      const int mine = c0 + c1 + c2 + c3;
-      int suf = mine;  // inclusive suffix over lanes >= lane
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_down(suf, o);
-        if (lane + o < 64) suf += y;
+    // thread t owns bins t*per .. t*per+per-1; counts above a thread's bins
+    // come from an exclusive scan of the per-thread sums
+    const int per = nb / SEL_THREADS > 0 ? nb / SEL_THREADS : 1;
+    const int b0 = tid * per;
+    int mine = 0;
+    if (b0 < nb)
+      for (int e = 0; e < per; ++e) mine += hist[b0 + e];
+    int tot;
+    const int below = block_excl_scan(mine, wave_tot, &tot);
+    const int above = tot - below - mine;  // keys in bins above this thread's
+    if (b0 < nb && above < remaining && remaining <= above + mine) {
+      int acc = above, sel = b0;
+      for (int e = per - 1; e >= 0; --e) {
+        if (acc + hist[b0 + e] >= remaining) { sel = b0 + e; break; }
+        acc += hist[b0 + e];
       }
-      const int above = suf - mine;  // count in bins above this lane's bins
-      // the bin holding the remaining-th largest: above < remaining <= suf
-      if (above < remaining && remaining <= suf) {
-        int acc = above, sel = b0;
-        const int cs[4] = {c3, c2, c1, c0};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (acc + cs[e] >= remaining) { sel = b0 + 3 - e; break; }
-          acc += cs[e];
-        }
-        sh_prefix = prefix | ((unsigned long long)sel << shift);
-        sh_remaining = remaining - acc;
-      }
+      sh_prefix = prefix | ((unsigned long long)sel << shift);
+      sh_remaining = remaining - acc;
     }
     __syncthreads();
     prefix = sh_prefix;
     remaining = sh_remaining;
-    pmask |= 255ull << shift;
+    pmask |= (unsigned long long)(nb - 1) << shift;
     __syncthreads();
+  };
+  auto global_keys = [&](auto&& f) {
+    for (int j = tid; j < n; j += SEL_THREADS) f(keys[j]);
+  };
+  digit(global_keys, 52, 4096);
+  if (tid == 0) sh_ncand = 0;
+  __syncthreads();
+  const int n_match = hist[(int)((prefix >> 52) & 4095)];
+  if (n_match <= SEL_CAND) {
+    for (int j = tid; j < n; j += SEL_THREADS) {
+      const unsigned long long key = keys[j];
+      if ((key & pmask) == prefix) cand[atomicAdd(&sh_ncand, 1)] = key;
+    }
+    __syncthreads();
+    const int nc = sh_ncand;
+    auto lds_keys = [&](auto&& f) {
+      for (int j = tid; j < nc; j += SEL_THREADS) f(cand[j]);
+    };
+    for (int shift = 44; shift >= 4; shift -= 8) digit(lds_keys, shift, 256);
+    digit(lds_keys, 0, 16);
+  } else {
+    for (int shift = 44; shift >= 4; shift -= 8) digit(global_keys, shift, 256);
+    digit(global_keys, 0, 16);
   }
   const unsigned long long T = prefix;
   const int need = remaining;  // keys equal to T to take, lowest indices first

@@ -263,6 +263,33 @@ def test_workload4_segment_with_topk(sa):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_topk_narrow_scores(sa, dtype):
+    """Scores that all share their leading exponent bits (every score in
+    [1, 2), or all equal): the selection runs its later digits over a
+    candidate set of 4000 keys (kept on chip) or over more keys than that
+    (read again from memory), with heavy ties resolved by the lower index."""
+    from structured_sparse_attention_attn_amd.pipeline import TopK
+    for n_heads, pool_len, k, seed, all_equal in [(2, 4000, 777, 11, False), (2, 10000, 5000, 12, False),
+                                                  (1, 10000, 4321, 13, True)]:
+        q, kp, vp = W.make_pool_inputs(n_heads, pool_len, 128, seed, dtype)
+        q = torch.zeros_like(q)
+        if not all_equal:
+            q[:, 0] = 1.0
+            g = torch.Generator().manual_seed(seed)
+            kp[:, :, 0] = (1.0 + 0.99 * torch.rand((n_heads, pool_len), generator=g)).to(dtype)
+        topk = TopK(n_heads, pool_len)
+        idx = torch.empty((n_heads, k), dtype=torch.int32, device="cuda")
+        score = torch.empty((n_heads, k), dtype=torch.float64, device="cuda")
+        topk(q.cuda(), kp.cuda(), k, idx, score=score)
+        torch.cuda.synchronize()
+        for h in range(n_heads):
+            s_ = O.topk_scores(q[h].double().numpy(), kp[h].double().numpy())
+            ri = O.topk_select(s_, k)
+            np.testing.assert_array_equal(idx[h].cpu().numpy(), ri)
+            np.testing.assert_array_equal(score[h].cpu().numpy(), s_[ri])
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 def test_topk_bitexact(sa, dtype):
     from structured_sparse_attention_attn_amd.pipeline import TopK
     for n_heads, pool_len, d, ks, seed in [(8, 32768, 128, (1, 1024, 32768), 1), (3, 1000, 64, (1, 7, 999, 1000), 2),
