@@ -84,15 +84,15 @@ def stage_bytes(wl, sep_np, plan_bytes):
 
 
 def gemm_ceiling_tflops(torch):
-    """Dense bf16 GEMM through torch (hipBLASLt): a measured MFMA ceiling."""
-    n = 8192
+    """Dense bf16 GEMM through torch (hipBLASLt), 16384^3: a measured MFMA ceiling."""
+    n = 16384
     a = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
     b = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
     for _ in range(3):
         torch.matmul(a, b)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    reps = 20
+    reps = 10
     e0.record()
     for _ in range(reps):
         torch.matmul(a, b)
