@@ -12,7 +12,8 @@ Sources, cited by page title and section:
   the distance cap ``d'_ij = min(i-j, L_pretrain)`` inside the logit
   ``w(q_i, k_j, d'_ij)``; and its RoPE realisation (window keys rotated as
   usual; starting-span keys outside the window unrotated with the query
-  rotated to the fixed distance L_pretrain).
+  rotated to the fixed distance L_pretrain); for ALiBi-style models, the
+  linear distance bias clipped to the same cap, then the Lambda mask.
 * Segmented-execution page ("Training-Inference Consistent Segmented Execution
   for Long-Context LLMs"), 方法详解 / 整体框架 and 关键设计: a segment attends
   causally to [prefix | segment]; prefix positions are re-indexed to 0..P-1 and
@@ -26,7 +27,10 @@ j = i; masked means -inf (the printed elementwise product with M is not taken
 literally); the Lambda window keeps ``i-j <= L`` literally; softmax scale
 ``1/sqrt(d)`` everywhere; GQA head h reads kv head ``h // (h_q/h_kv)``; the
 top-k score is the fp64 chain ``((0 + q0 k0) + q1 k1) + ...`` with ties to the
-lower index, and the retrieved rows keep ascending pool order.
+lower index, and the retrieved rows keep ascending pool order; the ALiBi
+variant adds ``-m_h * d'_ij`` to the scaled logit (no rotation), with the
+geometric head slopes ``m_h = 2**(-E (h+1) / h_q)`` (E = 8 is the usual
+choice; the page names no slopes).
 
 Everything is plain numpy in fp64; the only library primitives are matrix
 products, sorting and elementwise transcendental functions.
@@ -50,6 +54,7 @@ __all__ = [
     "visible", "capped", "key_set", "pos_q", "pos_k", "mask_rows", "rope_theta", "rotate",
     "attention_rows", "attention_fast", "attention", "plan", "plan_items_of_tile",
     "topk_scores", "topk_select", "pair_counts", "pair_count_total", "q0_closed_form",
+    "alibi_slope", "q0_alibi_closed_form",
 ]
 
 
@@ -151,14 +156,17 @@ def rotate(x: np.ndarray, angle: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: Sequence[int],
-                   spec: MaskSpec, rope_base: Optional[float], scale: float):
+                   spec: MaskSpec, rope_base: Optional[float], scale: float,
+                   alibi: Optional[float] = None):
     """Masked softmax attention for the listed query rows of one head.
 
     q [n_q, d], k and v [n_k, d] (fp64).  For every key j in A_i the logit is
     ``scale * <Rot(delta) q_i, k_j>`` with ``delta = pos_q(i) - pos_k(j)``
     (LM-Infinite: ``delta' = min(delta, L)``), i.e. the page's
-    ``w(q_i, k_j, d'_ij)`` for RoPE.  Masked keys take no part (-inf logit).
-    Returns O [len(rows), d] and the natural-log LSE [len(rows)].
+    ``w(q_i, k_j, d'_ij)`` for RoPE.  With ``alibi`` = m (and no RoPE) the
+    logit is ``scale * <q_i, k_j> - m * delta'`` instead: the ALiBi bias with
+    its distance clipped to the same cap.  Masked keys take no part (-inf
+    logit).  Returns O [len(rows), d] and the natural-log LSE [len(rows)].
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -179,6 +187,11 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: Sequence[i
             qr = rotate(np.broadcast_to(q[i], (len(A), d)), ang)
             s = np.einsum("jd,jd->j", qr, k[A])
         s = s * scale
+        if alibi is not None:
+            dist = pos_q(spec, int(i)) - pos_k(spec, A)
+            if spec.mode == LAMBDA:
+                dist = np.minimum(dist, spec.L)
+            s = s - alibi * dist.astype(np.float64)
         mu = s.max()
         e = np.exp(s - mu)
         z = e.sum()
@@ -193,7 +206,8 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: Sequence[i
 
 def attention_fast(q: np.ndarray, k: np.ndarray, v: np.ndarray, spec: MaskSpec,
                    rope_base: Optional[float], scale: float,
-                   row_blocks: Optional[Sequence[Sequence[int]]] = None):
+                   row_blocks: Optional[Sequence[Sequence[int]]] = None,
+                   alibi: Optional[float] = None):
     """Same result as :func:`attention_rows`, computed tile-wise for speed.
 
     q and k are rotated once at their absolute positions, using
@@ -201,7 +215,8 @@ def attention_fast(q: np.ndarray, k: np.ndarray, v: np.ndarray, spec: MaskSpec,
     page's realisation ``<R(L) q_i, k_j>`` with the raw key.  Each block of
     query rows takes the union of its visible keys, a dense product, the mask
     (-inf), then the softmax.  ``row_blocks`` defaults to consecutive groups
-    of 128 rows.  Returns (O, LSE) for the rows covered, in order.
+    of 128 rows.  ``alibi`` adds the clipped distance bias as in
+    :func:`attention_rows`.  Returns (O, LSE) for the rows covered, in order.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -229,6 +244,11 @@ def attention_fast(q: np.ndarray, k: np.ndarray, v: np.ndarray, spec: MaskSpec,
         else:
             S = q[rows] @ k[U].T
         S = S * scale
+        if alibi is not None:
+            dist = pos_q(spec, rows)[:, None] - pos_k(spec, U)[None, :]
+            if spec.mode == LAMBDA:
+                dist = np.minimum(dist, spec.L)
+            S = S - alibi * dist.astype(np.float64)
         S = np.where(Mu, S, -np.inf)
         mu = S.max(axis=1)
         E = np.exp(S - mu[:, None])
@@ -240,25 +260,30 @@ def attention_fast(q: np.ndarray, k: np.ndarray, v: np.ndarray, spec: MaskSpec,
 
 def attention(Q, K, V, spec: MaskSpec, rope_base: Optional[float], scale: float,
               heads: Optional[Sequence[int]] = None, rows: Optional[Sequence[int]] = None,
-              mode: str = "fast"):
+              mode: str = "fast", alibi_exp: Optional[float] = None):
     """Multi-head wrapper: Q [h_q, n_q, d], K and V [h_kv, n_k, d] (batch squeezed).
 
     Query head h reads kv head ``h // (h_q // h_kv)``.  ``rows`` restricts the
     query rows (definition mode evaluates them one by one; fast mode groups
-    them 128 at a time).  Returns O [len(heads), len(rows), d], LSE [..].
+    them 128 at a time).  ``alibi_exp`` = E selects the ALiBi bias with slope
+    ``alibi_slope(h, h_q, E)`` for head h (``rope_base`` must then be None).
+    Returns O [len(heads), len(rows), d], LSE [..].
     """
     h_q, h_kv = Q.shape[0], K.shape[0]
     group = h_q // h_kv
+    if alibi_exp is not None and rope_base:
+        raise ValueError("the ALiBi bias replaces RoPE: pass rope_base=None")
     heads = list(range(h_q)) if heads is None else list(heads)
     rows = np.arange(Q.shape[1]) if rows is None else np.asarray(rows)
     Os, Ls = [], []
     for h in heads:
         g = h // group
+        m = None if alibi_exp is None else alibi_slope(h, h_q, alibi_exp)
         if mode == "definition":
-            o, l = attention_rows(Q[h], K[g], V[g], rows, spec, rope_base, scale)
+            o, l = attention_rows(Q[h], K[g], V[g], rows, spec, rope_base, scale, m)
         else:
             blocks = [rows[s:s + TQ] for s in range(0, len(rows), TQ)]
-            o, l = attention_fast(Q[h], K[g], V[g], spec, rope_base, scale, blocks)
+            o, l = attention_fast(Q[h], K[g], V[g], spec, rope_base, scale, blocks, m)
         Os.append(o)
         Ls.append(l)
     return np.stack(Os), np.stack(Ls)
@@ -408,3 +433,36 @@ def q0_closed_form(v: np.ndarray, spec: MaskSpec, rows: Sequence[int]):
         O[r] = v[A].mean(axis=0)
         lse[r] = math.log(len(A))
     return O, lse
+
+
+# ----------------------------------------------------------------------------
+# ALiBi-style bias (LM-Infinite page, section 方法: distance clipped to L_pretrain)
+# ----------------------------------------------------------------------------
+
+def alibi_slope(h: int, h_q: int, exp: float) -> float:
+    """Slope of query head h: ``2 ** (-exp * (h + 1) / h_q)``, a geometric sequence."""
+    return 2.0 ** (-float(exp) * (h + 1) / h_q)
+
+
+def q0_alibi_closed_form(v: np.ndarray, spec: MaskSpec, rows: Sequence[int], m: float):
+    """Lambda mask with Q = 0: key j's logit is ``-m * min(i-j, L)``.
+
+    The partition function is summed in closed form, not over A_i: the window
+    keys ``i-j = 0..min(i, L)`` make the geometric series
+    ``(1 - e^{-m (W+1)}) / (1 - e^{-m})`` and each of the
+    ``min(n_s, max(0, i-L))`` starting-span keys outside the window adds
+    ``e^{-m L}``.  O_i is the bias-weighted mean of v over A_i."""
+    v = np.asarray(v, dtype=np.float64)
+    O = np.zeros((len(rows), v.shape[1]))
+    lse = np.zeros(len(rows))
+    for r, i in enumerate(rows):
+        i = int(i)
+        W = min(i, spec.L)
+        n_far = min(spec.n_s, max(0, i - spec.L))
+        win = -math.expm1(-m * (W + 1)) / -math.expm1(-m) if m > 0 else float(W + 1)
+        lse[r] = math.log(win + n_far * math.exp(-m * spec.L))
+        A = key_set(spec, i)
+        wgt = np.exp(-m * np.minimum(i - A, spec.L))
+        O[r] = (wgt @ v[A]) / wgt.sum()
+    return O, lse
+

@@ -19,6 +19,12 @@ Pins, by oracle function:
                         heapq.nlargest; k=N and k=1 special cases.
   pair counts           closed forms for LM-Infinite, segment and SepLLM; the
                         segmented page's effective context S + aM + b(1-a)R.
+  ALiBi (Lambda)        the textbook geometric slopes (h_q = 8: 1/2 .. 1/256);
+                        torch SDPA with an additive bias built by torch where
+                        no distance reaches the cap; Q = 0 closed forms (the
+                        geometric-series partition function and the weight at
+                        distance 0, at the cap and beyond it); a steep slope
+                        that leaves only the diagonal.
 """
 import heapq
 import json
@@ -431,3 +437,103 @@ def test_topk_select_rules():
     # ties: all equal -> the lowest indices
     assert O.topk_select(np.zeros(50), 5).tolist() == [0, 1, 2, 3, 4]
     assert O.topk_select(np.array([0.0, -0.0, 0.0, -1.0]), 2).tolist() == [0, 1]
+
+
+# ---------------------------------------------------------------------------
+# ALiBi bias clipped at L (LM-Infinite page, section 方法)
+# ---------------------------------------------------------------------------
+
+def test_alibi_slopes_textbook():
+    # the geometric ALiBi slopes: for 8 heads 1/2, 1/4, ..., 1/256
+    assert [O.alibi_slope(h, 8, 8.0) for h in range(8)] == [2.0 ** -(h + 1) for h in range(8)]
+    s16 = [O.alibi_slope(h, 16, 8.0) for h in range(16)]
+    assert s16[-1] == 2.0 ** -8
+    np.testing.assert_allclose(np.array(s16[1:]) / np.array(s16[:-1]), 2.0 ** -0.5, rtol=1e-15)
+
+
+@pytest.mark.parametrize("n_s,L", [(5, 199), (0, 31)])
+def test_alibi_without_cap_vs_sdpa(n_s, L):
+    # no visible pair has i - j > L (full causal, or a pure window), so the bias is the
+    # textbook ALiBi -m (i - j), built here by torch as an additive SDPA mask
+    d, m, slope = 64, 200, 0.0625
+    scale = 1.0 / math.sqrt(d)
+    q, k, v = rand(m, d), rand(m, d), rand(m, d)
+    ar = torch.arange(m)
+    dist = (ar[:, None] - ar[None, :]).to(torch.float64)
+    keep = (dist >= 0) & (dist <= L)
+    bias = torch.where(keep, -slope * dist, torch.tensor(-math.inf, dtype=torch.float64))
+    tq, tk = torch.from_numpy(q), torch.from_numpy(k)
+    ref = sdpa(tq, tk, torch.from_numpy(v), bias, scale).numpy()
+    ref_lse = torch.logsumexp(tq @ tk.T * scale + bias, dim=1).numpy()
+    spec = O.MaskSpec(O.LAMBDA, m, m, n_s=n_s, L=L)
+    o, lse = O.attention_fast(q, k, v, spec, None, scale, alibi=slope)
+    o2, lse2 = O.attention_rows(q, k, v, range(m), spec, None, scale, slope)
+    for a, b in ((o, ref), (o2, ref), (lse, ref_lse), (lse2, ref_lse)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("n_s,L,slope", [(5, 30, 0.05), (12, 7, 0.3), (3, 64, 2.0 ** -8)])
+def test_alibi_q_zero_closed_form(n_s, L, slope):
+    # Q = 0: logit of key j is -m min(i-j, L).  Partition function: the window keys at
+    # distances 0..W give a geometric series, each starting-span key beyond the window
+    # gives e^{-mL}.  Value columns that mark one distance class read that class's weight.
+    d, m = 16, 260
+    spec = O.MaskSpec(O.LAMBDA, m, m, n_s=n_s, L=L)
+    q, k = np.zeros((m, d)), rand(m, d)
+    v = rand(m, d)
+    i = np.arange(m)
+    W = np.minimum(i, L)
+    n_far = np.minimum(n_s, np.maximum(0, i - L))
+    Z = np.array([sum(math.exp(-slope * t) for t in range(w + 1)) for w in W]) \
+        + n_far * math.exp(-slope * L)
+    # column 0: keys beyond the window (all in the starting span); column 1: j == i;
+    # column 2: the key at distance exactly L
+    vf = v.copy()
+    v[:, :3] = 0.0
+    o_parts = []
+    for r in range(m):
+        vr = v.copy()
+        vr[: max(0, r - L), 0] = 1.0
+        vr[r, 1] = 1.0
+        if r >= L:
+            vr[r - L, 2] = 1.0
+        o_r, l_r = O.attention_rows(q, k, vr, [r], spec, None, 0.1, slope)
+        o_parts.append((o_r[0], l_r[0]))
+    o = np.array([p[0] for p in o_parts])
+    lse = np.array([p[1] for p in o_parts])
+    np.testing.assert_allclose(lse, np.log(Z), rtol=0, atol=1e-13)
+    np.testing.assert_allclose(o[:, 0], n_far * math.exp(-slope * L) / Z, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(o[:, 1], 1.0 / Z, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(o[:, 2], np.where(i >= L, math.exp(-slope * L), 0.0) / Z,
+                               rtol=0, atol=1e-15)
+    # the helper's closed form and the fast mode agree with the definition
+    o_cf, l_cf = O.q0_alibi_closed_form(vf, spec, range(m), slope)
+    o_f, l_f = O.attention_fast(q, k, vf, spec, None, 0.1, alibi=slope)
+    o_d, l_d = O.attention_rows(q, k, vf, range(m), spec, None, 0.1, slope)
+    np.testing.assert_allclose(l_cf, np.log(Z), rtol=0, atol=1e-13)
+    for a, b in ((o_f, o_d), (o_cf, o_d), (l_f, l_d)):
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-12)
+
+
+def test_alibi_steep_slope_keeps_the_diagonal():
+    # with m = 60 every key but j = i is suppressed by e^{-60} or less
+    d, m = 32, 150
+    q, k, v = rand(m, d), rand(m, d), rand(m, d)
+    spec = O.MaskSpec(O.LAMBDA, m, m, n_s=4, L=20)
+    o, lse = O.attention_fast(q, k, v, spec, None, 0.05, alibi=60.0)
+    np.testing.assert_allclose(o, v, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, 0.05 * np.einsum("id,id->i", q, k), rtol=0, atol=1e-14)
+
+
+def test_alibi_heads_use_their_slopes():
+    d, m = 32, 140
+    Q, K, V = rand(8, m, d), rand(2, m, d), rand(2, m, d)
+    spec = O.MaskSpec(O.LAMBDA, m, m, n_s=3, L=40)
+    o, lse = O.attention(Q, K, V, spec, None, 0.2, alibi_exp=8.0)
+    for h in (0, 5, 7):
+        o_h, l_h = O.attention_rows(Q[h], K[h // 4], V[h // 4], range(m), spec, None, 0.2,
+                                    2.0 ** -(h + 1))
+        np.testing.assert_allclose(o[h], o_h, rtol=0, atol=1e-12)
+        np.testing.assert_allclose(lse[h], l_h, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.attention(Q, K, V, spec, 10000.0, 0.2, alibi_exp=8.0)
