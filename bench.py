@@ -73,8 +73,13 @@ def stage_bytes(wl, sep_np, plan_bytes):
     if wl.mode == "sepllm" and sep_np is not None:
         g0 = 64 * ((wl.a + 63) // 64)
         n_sep = int(sep_np[g0:].astype(np.int64).sum())
-    n_cap = min(wl.n_s, wl.n_k) if wl.mode == "lambda" else 0
-    rope = esz * d * B * (2 * wl.h_q * wl.n_q + 2 * wl.h_kv * wl.n_k + 3 * wl.h_kv * n_sep + wl.h_kv * n_cap)
+    rot = wl.rope_base is not None
+    n_cap = min(wl.n_s, wl.n_k) if (wl.mode == "lambda" and rot) else 0
+    # the query copy (rotated and/or pre-scaled for bf16), rotated keys, the
+    # gathered separator rows (read K and V, write both) and the capped keys
+    n_qrows = 2 * wl.h_q * wl.n_q if (rot or wl.dtype == "bf16") else 0
+    n_krows = 2 * wl.h_kv * wl.n_k if rot else 0
+    rope = esz * d * B * (n_qrows + n_krows + 3 * wl.h_kv * n_sep + wl.h_kv * n_cap)
     plan = (wl.n_k if sep_np is not None else 0) + plan_bytes
     out = {"plan": plan, "rope": rope}
     if wl.mode == "segment":
@@ -139,6 +144,7 @@ def cpu_baseline(wl, inp, budget_s):
         k = inp["k"][0, 0].double().numpy()
         v = inp["v"][0, 0].double().numpy()
     q = inp["q"][0, 0].double().numpy()
+    slope = None if wl.alibi_exp is None else O.alibi_slope(0, wl.h_q, wl.alibi_exp)
     n_tiles = -(-wl.n_q // 128)
     # tiles from the last one backwards: the ones with the most keys
     pairs = 0
@@ -146,7 +152,7 @@ def cpu_baseline(wl, inp, budget_s):
     t0 = time.perf_counter()
     for t in range(n_tiles - 1, -1, -1):
         rows = np.arange(128 * t, min(wl.n_q, 128 * t + 128))
-        O.attention_fast(q, k, v, spec, wl.rope_base, wl.scale, [rows])
+        O.attention_fast(q, k, v, spec, wl.rope_base, wl.scale, [rows], alibi=slope)
         pairs += int(O.mask_rows(spec, rows).sum())
         done += 1
         if time.perf_counter() - t0 > budget_s:
@@ -163,7 +169,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, help="1..5 (default: the 32K Lambda layer)")
+    ap.add_argument("--workload", type=int, default=3, help="1..6 (default: the 32K Lambda layer)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--no-gemm-ceiling", action="store_true",
@@ -217,7 +223,8 @@ def main():
                          L_pretrain=wl.L, prefix_len=wl.P)
     o = torch.empty_like(q)
     lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device=dev)
-    fa = fwd_args(q, k, v, o, lse=lse, rope_base=wl.rope_base, scale=wl.scale)
+    fa = fwd_args(q, k, v, o, lse=lse, rope_base=wl.rope_base, scale=wl.scale,
+                  alibi_exp=wl.alibi_exp)
     sa.ensure_workspace(fa)
     torch.cuda.synchronize()
 
@@ -297,6 +304,7 @@ def main():
                    "h_kv": wl.h_kv, "head_dim": wl.d, "n_q": wl.n_q, "n_k": wl.n_k,
                    "a": wl.a, "w": wl.w, "p_sep": wl.p_sep, "n_starting": wl.n_s,
                    "L_pretrain": wl.L, "prefix_len": wl.P, "rope_base": wl.rope_base,
+                   "alibi_exp": wl.alibi_exp,
                    "pairs_per_head": pairs_head},
         "ms_per_layer": round(stage["rope"] + stage["attend"], 4),
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),

@@ -43,7 +43,7 @@ extern "C" {
 enum { SA_OK = 0, SA_EINVAL = -1, SA_EUNSUPPORTED = -2, SA_ENOSPACE = -3, SA_EHIP = -4 };
 enum { SA_MASK_SEPLLM = 0, SA_MASK_LAMBDA = 1, SA_MASK_SEGMENT = 2 };
 enum { SA_F32 = 0, SA_BF16 = 1 };
-enum { SA_ROPE_NONE = 0, SA_ROPE_HALF = 1 };
+enum { SA_ROPE_NONE = 0, SA_ROPE_HALF = 1, SA_ALIBI = 2 };
 
 /* Plan geometry: 128-query tiles, 64-key blocks. */
 enum { SA_TQ = 128, SA_BK = 64 };
@@ -106,7 +106,13 @@ typedef struct {
  *   dtype       SA_F32 or SA_BF16 for q, k, v and o.
  *   d           head dimension: 128 (bf16 and f32) or 64 (f32).
  *   h_q, h_kv   h_q % h_kv == 0; query head h reads kv head h / (h_q/h_kv).
- *   rope        SA_ROPE_NONE or SA_ROPE_HALF (rotate-half, theta_c = base^(-2c/d)).
+ *   rope        position encoding: SA_ROPE_NONE; SA_ROPE_HALF (rotate-half RoPE,
+ *               theta_c = rope_base^(-2c/d)); or SA_ALIBI (LAMBDA masks only,
+ *               else SA_EUNSUPPORTED): no rotation, and the logit of query
+ *               head h gains the ALiBi-style bias -m_h * min(i-j, L_pretrain)
+ *               with m_h = 2^(-E (h+1) / h_q), E = rope_base > 0 (8 is the
+ *               usual value) -- the LM-Infinite page, section "method": the
+ *               bias matrix of ALiBi-style models clipped at the same cap.
  *   scale       logit scale, normally 1/sqrt(d).
  *   q           [batch, h_q, n_q, d] raw (unrotated) queries.
  *   k, v        [batch, h_kv, n_k, d] raw keys and values.

@@ -30,7 +30,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 SA_OK, SA_EINVAL, SA_EUNSUPPORTED, SA_ENOSPACE, SA_EHIP = 0, -1, -2, -3, -4
 SA_MASK_SEPLLM, SA_MASK_LAMBDA, SA_MASK_SEGMENT = 0, 1, 2
 SA_F32, SA_BF16 = 0, 1
-SA_ROPE_NONE, SA_ROPE_HALF = 0, 1
+SA_ROPE_NONE, SA_ROPE_HALF, SA_ALIBI = 0, 1, 2
 SA_TQ, SA_BK = 128, 64
 SA_ITEM_FULL, SA_ITEM_CAPPED = 1, 2
 
@@ -129,16 +129,24 @@ def sparse_attn_plan(m: sa_mask_t, plan, stream=None) -> None:
 
 
 def fwd_args(q, k, v, o, *, lse=None, rope_base: Optional[float] = None,
-             scale: Optional[float] = None) -> sa_fwd_args_t:
-    """sa_fwd_args_t for [B,H,T,d] tensors (last dimension contiguous)."""
+             scale: Optional[float] = None, alibi_exp: Optional[float] = None) -> sa_fwd_args_t:
+    """sa_fwd_args_t for [B,H,T,d] tensors (last dimension contiguous).
+
+    ``alibi_exp`` = E selects SA_ALIBI (slopes 2^(-E (h+1) / h_q)) instead of RoPE.
+    """
     import torch
     dtype = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}[q.dtype]
     B, h_q, _, d = q.shape
     h_kv = k.shape[1]
     a = sa_fwd_args_t()
     a.dtype, a.batch, a.h_q, a.h_kv, a.d = dtype, B, h_q, h_kv, d
-    a.rope = SA_ROPE_HALF if rope_base else SA_ROPE_NONE
-    a.rope_base = float(rope_base or 0.0)
+    if alibi_exp is not None:
+        if rope_base:
+            raise ValueError("rope_base and alibi_exp are exclusive")
+        a.rope, a.rope_base = SA_ALIBI, float(alibi_exp)
+    else:
+        a.rope = SA_ROPE_HALF if rope_base else SA_ROPE_NONE
+        a.rope_base = float(rope_base or 0.0)
     a.scale = float(scale if scale is not None else d ** -0.5)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
         if t.stride(-1) != 1:

@@ -97,9 +97,15 @@ int check_args(const sa_mask_t* m, const sa_fwd_args_t* a) {
   if (a->h_q % a->h_kv != 0) return fail(SA_EINVAL, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
   if ((int64_t)a->batch * a->h_q * sa::ceil_div(m->n_q, sa::TQ) > 0x7fffffffLL)
     return fail(SA_EINVAL, "too many tiles");
-  if (a->rope != SA_ROPE_NONE && a->rope != SA_ROPE_HALF) return fail(SA_EINVAL, "unknown rope mode %d", a->rope);
+  if (a->rope != SA_ROPE_NONE && a->rope != SA_ROPE_HALF && a->rope != SA_ALIBI)
+    return fail(SA_EINVAL, "unknown position encoding %d", a->rope);
   if (a->rope == SA_ROPE_HALF && !(std::isfinite(a->rope_base) && a->rope_base > 1.0f))
     return fail(SA_EINVAL, "rope_base must be finite and > 1");
+  if (a->rope == SA_ALIBI) {
+    if (m->kind != SA_MASK_LAMBDA) return fail(SA_EUNSUPPORTED, "the ALiBi bias is supported with the LAMBDA mask only");
+    if (!(std::isfinite(a->rope_base) && a->rope_base > 0.0f))
+      return fail(SA_EINVAL, "ALiBi slope exponent (rope_base) must be finite and > 0");
+  }
   if (!(std::isfinite(a->scale) && a->scale > 0.0f)) return fail(SA_EINVAL, "scale must be finite and > 0");
   const int esz = a->dtype == SA_BF16 ? 2 : 4;
   int r;

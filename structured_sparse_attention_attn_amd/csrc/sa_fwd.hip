@@ -57,7 +57,15 @@ struct FwdArgs {
   int a, w, n_s, L, P, n_cap;
   int use_cap, gather;
   float scale_log2;
+  int alibi;          // ALiBi-style bias -m_h * min(i-j, L) instead of RoPE (Lambda only)
+  float alibi_e;      // slope exponent E: m_h = 2^(-E (h+1) / h_q)
 };
+
+// Slope of query head h in base-2 logit units, m_h * log2(e), evaluated in
+// double and rounded once.
+__device__ inline float alibi_slope_log2(const FwdArgs& p, int hq) {
+  return (float)(exp2(-(double)p.alibi_e * (hq + 1) / p.h_q) * 1.4426950408889634);
+}
 
 enum MaskKind : int {
   MK_NONE = 0,    // every pair visible
@@ -288,6 +296,8 @@ struct TileUnits {
   const char* vsb;
 };
 
+// REV visits the plan's blocks last to first (the diagonal block first).
+template <bool REV>
 __device__ inline Unit unit_at(const FwdArgs& p, const TileUnits& tu, int u) {
   Unit x;
   x.count = 0;
@@ -318,7 +328,7 @@ __device__ inline Unit unit_at(const FwdArgs& p, const TileUnits& tu, int u) {
     return x;
   }
   u -= tu.n_ch;
-  const int item = ld_uniform(p.items + tu.it0 + u);
+  const int item = ld_uniform(p.items + tu.it0 + (REV ? tu.n_items - 1 - u : u));
   const int blk = item & 0xffffff;
   const int fl = item >> 24;
   x.kbase = tu.kb + (int64_t)blk * BK * tu.kst;
@@ -377,6 +387,25 @@ __device__ inline void apply_mask(const FwdArgs& p, const Unit& u, int qi, int h
   }
 }
 
+// Adds the ALiBi-style bias -m2 * min(i - j, L) to one unit's logits (same
+// register layout as apply_mask).  Masked logits stay -inf.
+__device__ inline void add_alibi(const Unit& u, int qi, int hl, float m2, float Lf, f32x16 (&s)[2]) {
+  const float dist0 = (float)(qi - u.key0 - 4 * hl);  // i - j at slot offset 0 (exact)
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = 32 * mb + 8 * (r >> 2) + (r & 3);
+      s[mb][r] = fmaf(-m2, fminf(dist0 - (float)c, Lf), s[mb][r]);
+    }
+  }
+}
+
+// ALIBI: the bias is added to every unit's logits and the blocks are visited
+// from the diagonal down, so a row's first reference already includes its
+// largest bias (0 at j = i): every later logit is at most the query-key spread
+// above it, and the reference stays the size of a query-key logit.
+template <bool ALIBI>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   // K blocks double-buffered, V blocks triple-buffered: [K0 K1 V0 V1 V2]
   __shared__ __attribute__((aligned(16))) char smem[5 * BLK_BYTES];
@@ -406,6 +435,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   tu.ksb = static_cast<const char*>(p.ksep) + sep_off;
   tu.vsb = static_cast<const char*>(p.vsep) + sep_off;
   const int n_units = tu.n_capu + tu.n_ch + tu.n_items;
+  const float m2 = ALIBI ? alibi_slope_log2(p, hq) : 0.f;
+  const float Lf = (float)p.L;
 
   bf16x8 qf[8];
   auto load_q = [&](const void* base, int64_t sB, int64_t sH, int64_t sT) {
@@ -528,7 +559,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   // it is in.
   Unit cur;
   if (n_units > 0) {
-    cur = unit_at(p, tu, 0);
+    cur = unit_at<ALIBI>(p, tu, 0);
     issue_loads(cur, 0, 0);
   }
   bf16x8 pb[4];  // P(u-1), carried into step u
@@ -542,7 +573,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
     if (u > 0) pv(pb, vs_prev);
     Unit nxt;
     if (u + 1 < n_units) {
-      nxt = unit_at(p, tu, u + 1);
+      nxt = unit_at<ALIBI>(p, tu, u + 1);
       issue_loads(nxt, buf ^ 1, vs_next);
     }
     vs_prev = vs_prev == 2 ? 0 : vs_prev + 1;
@@ -594,6 +625,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       case MK_LCAP: apply_mask<MK_LCAP>(p, cur, qi, hl, s); break;
       default: apply_mask<MK_SEG>(p, cur, qi, hl, s); break;
     }
+    if constexpr (ALIBI) add_alibi(cur, qi, hl, m2, Lf, s);
     if constexpr (!decltype(full_path)::value) {
       // common path: p = 2^(s - m_ref) straight from the MFMA output
 #pragma unroll
@@ -710,6 +742,8 @@ __global__ __launch_bounds__(128) void fwd_f32(FwdArgs p) {
   };
   load_q(p.q, p.qsB, p.qsH, p.qsT);
   bool q_is_raw = false;
+  const float m2 = p.alibi ? alibi_slope_log2(p, hq) : 0.f;
+  const float Lf = (float)p.L;
   float m_run = NEG_INF, l_run = 0.f;
   float acc[D];
 #pragma unroll
@@ -738,6 +772,7 @@ __global__ __launch_bounds__(128) void fwd_f32(FwdArgs p) {
 #pragma unroll
       for (int c = 0; c < D; ++c) acc_s = fmaf(q[c], Ks[r][c], acc_s);
       float x = acc_s * p.scale_log2;
+      if (p.alibi) x = fmaf(-m2, fminf((float)(qi - u.key0 - r), Lf), x);
       if (u.mk != MK_NONE && !visible(p, u, qi, r)) x = NEG_INF;
       s[r] = x;
       mx = fmaxf(mx, x);
@@ -827,9 +862,14 @@ hipError_t launch_fwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   p.use_cap = (m.kind == SA_MASK_LAMBDA && rope && ro.n_cap > 0) ? 1 : 0;
   p.gather = (m.kind == SA_MASK_SEPLLM && m.sep != nullptr) ? 1 : 0;
   p.scale_log2 = a.scale * LOG2E;
+  p.alibi = a.rope == SA_ALIBI ? 1 : 0;
+  p.alibi_e = p.alibi ? a.rope_base : 0.f;
   const unsigned grid = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
   if (a.dtype == SA_BF16) {
-    hipLaunchKernelGGL(fwd_bf16_d128, dim3(grid), dim3(256), 0, s, p);
+    if (p.alibi)
+      hipLaunchKernelGGL(fwd_bf16_d128<true>, dim3(grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(fwd_bf16_d128<false>, dim3(grid), dim3(256), 0, s, p);
   } else if (a.d == 64) {
     hipLaunchKernelGGL(fwd_f32<64>, dim3(grid), dim3(128), 0, s, p);
   } else {

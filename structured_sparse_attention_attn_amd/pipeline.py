@@ -32,19 +32,21 @@ class SparseAttention:
     def build_plan(self) -> None:
         sparse_attn_plan(self.mask, self.plan)
 
-    def args(self, q, k, v, o, lse=None, rope_base=None, scale=None):
-        return fwd_args(q, k, v, o, lse=lse, rope_base=rope_base, scale=scale)
+    def args(self, q, k, v, o, lse=None, rope_base=None, scale=None, alibi_exp=None):
+        return fwd_args(q, k, v, o, lse=lse, rope_base=rope_base, scale=scale,
+                        alibi_exp=alibi_exp)
 
     def ensure_workspace(self, args) -> None:
         need = sa_fwd_workspace_bytes(self.mask, args)
         if self.ws is None or self.ws.numel() < need:
             self.ws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
 
-    def forward(self, q, k, v, o=None, lse=None, rope_base=None, scale=None, args=None):
+    def forward(self, q, k, v, o=None, lse=None, rope_base=None, scale=None, args=None,
+                alibi_exp=None):
         if o is None:
             o = torch.empty_like(q)
         if args is None:
-            args = self.args(q, k, v, o, lse, rope_base, scale)
+            args = self.args(q, k, v, o, lse, rope_base, scale, alibi_exp)
         self.ensure_workspace(args)
         sparse_attn_fwd(self.mask, self.plan, args, self.ws)
         return o

@@ -27,8 +27,10 @@ def sample_rows(n_q, n_random, seed):
     return np.array(sorted(edge | rnd))
 
 
-def oracle_rows(Q, K, V, spec, rope_base, scale, heads, rows, kv_of=None):
-    """Fast-mode oracle for the given heads and rows (rows grouped by tile)."""
+def oracle_rows(Q, K, V, spec, rope_base, scale, heads, rows, kv_of=None, slope_of=None):
+    """Fast-mode oracle for the given heads and rows (rows grouped by tile).
+
+    slope_of(h): the ALiBi slope of head h (None: no bias)."""
     rows = np.asarray(rows)
     groups = {}
     for i in rows.tolist():
@@ -38,13 +40,21 @@ def oracle_rows(Q, K, V, spec, rope_base, scale, heads, rows, kv_of=None):
     for h in heads:
         g = kv_of(h) if kv_of else h // (h_q // h_kv)
         o, l = O.attention_fast(Q[h], K[g], V[g], spec, rope_base, scale,
-                                [np.array(v) for _, v in sorted(groups.items())])
+                                [np.array(v) for _, v in sorted(groups.items())],
+                                alibi=slope_of(h) if slope_of else None)
         Os.append(o)
         Ls.append(l)
     return np.stack(Os), np.stack(Ls)
 
 
 FEW_KEYS = 16
+
+
+def effective_keys(lse, lse2):
+    """Participation ratio 1 / sum_j p_ij^2 of each row's softmax weights, from the oracle's
+    LSE of the logits (lse) and of the doubled logits (lse2): sum_j p_j^2 = e^{lse2 - 2 lse}.
+    Equals |A_i| for uniform weights."""
+    return np.exp(2.0 * np.asarray(lse) - np.asarray(lse2))
 
 
 def row_counts(spec, rows):
@@ -65,7 +75,10 @@ def compare(o_gpu, o_ref, lse_gpu, lse_ref, dtype, nkeys=None):
     softmax averages over so few values that the bf16 rounding of the rotated
     q and k (relative 2^-9 each) and of O itself is not averaged away; a CPU
     model of exactly these roundings reproduces the kernel's error on such a
-    row (0.0117 on a 3-key row) bit for bit.  LSE (no stated bar): the logits
+    row (0.0117 on a 3-key row) bit for bit.  With the ALiBi bias a steep slope
+    puts nearly all the weight on the few keys next to the diagonal whatever
+    |A_i| is; for those runs ``nkeys`` is the participation ratio
+    (effective_keys) instead of |A_i|.  LSE (no stated bar): the logits
     see only the bf16 rounding of the rotated q and k, |d logit| of order
     2^-8 * scale * sum_c |q_c k_c|, a few 1e-3 for N(0,1) inputs; 2e-2.
     """

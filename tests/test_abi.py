@@ -129,6 +129,8 @@ def test_fwd_workspace_and_validation():
         (dict(q=None), sa.SA_EINVAL),
         (dict(k=4100), sa.SA_EINVAL),  # misaligned
         (dict(batch=0), sa.SA_EINVAL),
+        (dict(rope=sa.SA_ALIBI, rope_base=0.0), sa.SA_EINVAL),
+        (dict(rope=sa.SA_ALIBI, rope_base=float("inf")), sa.SA_EINVAL),
     ]
     for kw, code in cases:
         assert lib.sparse_attn_fwd(ctypes.byref(m), 256, plan_bytes, ctypes.byref(_args(**kw)), 512,
@@ -143,6 +145,13 @@ def test_fwd_workspace_and_validation():
                                None) == sa.SA_ENOSPACE
     assert lib.sparse_attn_fwd(ctypes.byref(m), None, plan_bytes, ctypes.byref(a), 512, ws,
                                None) == sa.SA_EINVAL
+    # the ALiBi bias: Lambda masks only; no rotated keys and no capped-key rows in the workspace
+    al = _args(rope=sa.SA_ALIBI, rope_base=8.0)
+    assert sa.sa_fwd_workspace_bytes(m, al) == 4 * 300 * 256
+    ms = sa.mask(sa.SA_MASK_SEPLLM, 300, 300, a=4, w=16)
+    assert lib.sparse_attn_fwd(ctypes.byref(ms), 256, sa.sa_plan_bytes(ms), ctypes.byref(al), 512,
+                               1 << 20, None) == sa.SA_EUNSUPPORTED
+    assert "LAMBDA" in sa.sa_last_error()
 
 
 def test_topk_validation():

@@ -13,8 +13,8 @@ import torch
 
 import oracle as O
 import workloads as W
-from _helpers import (compare, device_mask, log, oracle_rows, row_counts, sample_rows, spec_of,
-                      to64)
+from _helpers import (compare, device_mask, effective_keys, log, oracle_rows, row_counts,
+                      sample_rows, spec_of, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -93,7 +93,8 @@ def _run_small(sa, wl, *, strided=False, q_zero=False, check_canary=False):
     o_store = torch.full((guard * 2 + q.numel(),), 7.0, dtype=q.dtype, device=dev)
     o = o_store[guard:guard + q.numel()].view(q.shape)
     lse = torch.full((wl.batch, wl.h_q, wl.n_q), 7.0, dtype=torch.float32, device=dev)
-    sa_obj.forward(qd, kd, vd, o=o, lse=lse, rope_base=wl.rope_base, scale=wl.scale)
+    sa_obj.forward(qd, kd, vd, o=o, lse=lse, rope_base=wl.rope_base, scale=wl.scale,
+                   alibi_exp=wl.alibi_exp)
     torch.cuda.synchronize()
     if check_canary:
         assert torch.all(o_store[:guard] == 7.0) and torch.all(o_store[-guard:] == 7.0)
@@ -101,11 +102,26 @@ def _run_small(sa, wl, *, strided=False, q_zero=False, check_canary=False):
     cnt = O.pair_counts(spec)
     for b in range(wl.batch):
         Q, K, V = to64(q[b]), to64(k[b]), to64(v[b])
-        ref_o, ref_l = O.attention(Q, K, V, spec, wl.rope_base, wl.scale)
-        compare(to64(o[b]), ref_o, to64(lse[b]), ref_l, wl.dtype, nkeys=cnt[None, :])
-        if q_zero:
+        ref_o, ref_l = O.attention(Q, K, V, spec, wl.rope_base, wl.scale, alibi_exp=wl.alibi_exp)
+        nkeys = cnt[None, :]
+        if wl.alibi_exp is not None:
+            _, l2 = oracle_rows(Q, K, V, spec, None, 2 * wl.scale, range(wl.h_q), range(wl.n_q),
+                                slope_of=lambda h: 2 * O.alibi_slope(h, wl.h_q, wl.alibi_exp))
+            nkeys = effective_keys(ref_l, l2)
+        compare(to64(o[b]), ref_o, to64(lse[b]), ref_l, wl.dtype, nkeys=nkeys)
+        if q_zero and wl.alibi_exp is None:
             np.testing.assert_allclose(to64(lse[b]), np.broadcast_to(np.log(cnt), ref_l.shape),
                                        rtol=0, atol=2e-6)
+        elif q_zero:
+            # the closed-form partition function of the clipped bias (geometric series).
+            # fp32: the bias carries a relative error of ~2^-24.  bf16: the sum is taken over
+            # the bf16-rounded weights (relative error <= 2^-9 each), so
+            # |d LSE| <= -ln(1 - 2^-9) < 2e-3.
+            tol = 2e-3 if wl.dtype == "bf16" else 2e-5
+            for h in range(wl.h_q):
+                _, l_cf = O.q0_alibi_closed_form(V[h // (wl.h_q // wl.h_kv)], spec,
+                                                 range(wl.n_q), O.alibi_slope(h, wl.h_q, wl.alibi_exp))
+                np.testing.assert_allclose(to64(lse[b, h]), l_cf, rtol=0, atol=tol)
     return o, lse
 
 
@@ -172,7 +188,8 @@ def _workload_parity(sa, cid, heads, n_random):
     sa_obj = device_mask(wl, None if sep is None else sep.cuda())
     sa_obj.build_plan()
     lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
-    o = sa_obj.forward(q, k, v, lse=lse, rope_base=wl.rope_base, scale=wl.scale)
+    o = sa_obj.forward(q, k, v, lse=lse, rope_base=wl.rope_base, scale=wl.scale,
+                       alibi_exp=wl.alibi_exp)
     torch.cuda.synchronize()
     log(f"workload {cid}: oracle")
     spec = spec_of(wl, None if sep is None else sep.numpy())
@@ -185,11 +202,17 @@ def _workload_parity(sa, cid, heads, n_random):
     for h in heads:
         g = h // group
         Qh = to64(inp["q"][0, h])
+        slope = None if wl.alibi_exp is None else O.alibi_slope(h, wl.h_q, wl.alibi_exp)
         ref_o, ref_l = oracle_rows(Qh[None], K[g][None], V[g][None], spec, wl.rope_base, wl.scale,
-                                   [0], rows)
+                                   [0], rows, slope_of=lambda _h: slope)
         got_o = to64(o[0, h][torch.from_numpy(rows).cuda()])
         got_l = to64(lse[0, h][torch.from_numpy(rows).cuda()])
-        stats = compare(got_o, ref_o[0], got_l, ref_l[0], wl.dtype, nkeys=nkeys)
+        nk = nkeys
+        if slope is not None:
+            _, l2 = oracle_rows(Qh[None], K[g][None], V[g][None], spec, None, 2 * wl.scale, [0],
+                                rows, slope_of=lambda _h: 2 * slope)
+            nk = effective_keys(ref_l[0], l2[0])
+        stats = compare(got_o, ref_o[0], got_l, ref_l[0], wl.dtype, nkeys=nk)
         log(f"workload {cid} head {h}: max-abs {stats[0]:.2e} mean-abs {stats[1]:.2e} lse {stats[2]:.2e}")
 
 
@@ -207,6 +230,42 @@ def test_workload3_sampled(sa):
 
 def test_workload5_sampled(sa):
     _workload_parity(sa, 5, heads=[0, 5, 31], n_random=96)
+
+
+def test_workload6_alibi_sampled(sa):
+    _workload_parity(sa, 6, heads=[0, 17, 31], n_random=192)
+
+
+# The ALiBi bias clipped at L_pretrain under the Lambda mask (LM-Infinite page, section
+# "method").  Slopes 2^(-E (h+1) / h_q): E = 8 with 2 heads gives 1/16 and 1/256 (starting-span
+# keys beyond the cap keep real weight); E = 0.5 gives slopes near 1, where the bias spans
+# hundreds of base-2 units across a row.
+ALIBI_SMALL = [
+    dict(m=900, n_s=10, L=300, h_q=8, h_kv=2, alibi_exp=8.0),
+    dict(m=700, n_s=0, L=100, alibi_exp=8.0),
+    dict(m=600, n_s=100, L=64, alibi_exp=8.0),
+    dict(m=300, n_s=10, L=0, alibi_exp=8.0),
+    dict(m=300, n_s=5, L=5000, alibi_exp=8.0),
+    dict(m=1, n_s=10, L=100, alibi_exp=8.0),
+    dict(m=129, n_s=3, L=40, alibi_exp=2.0, batch=2),
+    dict(m=900, n_s=10, L=300, alibi_exp=0.5),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("case", range(len(ALIBI_SMALL)))
+def test_fwd_alibi_small(sa, case, dtype):
+    d = 128 if dtype == "bf16" else 64
+    wl = W.small(W.LAMBDA, seed=300 + case, dtype=dtype, d=d, rope_base=None, **ALIBI_SMALL[case])
+    log(f"alibi small {case} {dtype}")
+    _run_small(sa, wl, check_canary=True)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_alibi_q_zero_closed_form(sa, dtype):
+    wl = W.small(W.LAMBDA, seed=19, dtype=dtype, d=128 if dtype == "bf16" else 64, m=640, n_s=10,
+                 L=100, rope_base=None, alibi_exp=8.0)
+    _run_small(sa, wl, q_zero=True)
 
 
 def test_workload4_segment_with_topk(sa):

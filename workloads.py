@@ -1,6 +1,6 @@
 """Seeded synthetic inputs shared by the tests, the benchmark and the CPU baseline.
 
-This module only draws random tensors and describes the five workloads (shapes,
+This module only draws random tensors and describes the workloads (shapes,
 mask parameters, seeds).  It holds none of the method's arithmetic: no key sets,
 no positions, no rotations, no attention.  Both the HIP path and the fp64 oracle
 consume what it returns; neither is imported here.
@@ -42,6 +42,7 @@ class Workload:
     L: int = 0          # LM-Infinite pre-training length (distance cap)
     P: int = 0          # segment prefix length
     rope_base: Optional[float] = None
+    alibi_exp: Optional[float] = None  # ALiBi slope exponent E (instead of RoPE)
     # segment workload extras
     n_local: int = 0    # heads 0..n_local-1 see the carried tail
     pool_len: int = 0   # detached retrieval pool length
@@ -67,6 +68,10 @@ WORKLOADS: Dict[int, Workload] = {
                 P=1024, rope_base=10000.0, n_local=24, pool_len=32768, seed=4000),
     5: Workload(5, "sepllm_llama3_gqa_128k", SEPLLM, "bf16", 1, 32, 8, 128, 131072, 131072,
                 a=4, w=1024, p_sep=0.06, rope_base=500000.0, seed=5000),
+    # an ALiBi model (MPT-7B shape: 32 heads, head_dim 128, pre-trained on 2K tokens) under the
+    # Lambda mask with its bias clipped at L_pretrain
+    6: Workload(6, "lminfinite_alibi_lambda_32k", LAMBDA, "bf16", 1, 32, 32, 128, 32768, 32768,
+                n_s=10, L=2048, alibi_exp=8.0, seed=6000),
 }
 
 
@@ -111,12 +116,13 @@ def make_inputs(wl: Workload) -> Dict[str, torch.Tensor]:
 def small(mode: str, *, seed: int, dtype: str = "bf16", batch: int = 1, h_q: int = 2,
           h_kv: int = 2, d: int = 128, m: int = 300, a: int = 4, w: int = 64,
           p_sep: float = 0.1, n_s: int = 10, L: int = 100, P: int = 0,
-          rope_base: Optional[float] = 10000.0) -> Workload:
+          rope_base: Optional[float] = 10000.0, alibi_exp: Optional[float] = None) -> Workload:
     """A small workload for parity tests (several tiles plus a ragged tail)."""
     n_q = m
     n_k = m + P if mode == SEGMENT else m
     return Workload(0, f"small_{mode}_{seed}", mode, dtype, batch, h_q, h_kv, d, n_q, n_k,
-                    a=a, w=w, p_sep=p_sep, n_s=n_s, L=L, P=P, rope_base=rope_base, seed=seed)
+                    a=a, w=w, p_sep=p_sep, n_s=n_s, L=L, P=P, rope_base=rope_base,
+                    alibi_exp=alibi_exp, seed=seed)
 
 
 def make_small_inputs(wl: Workload) -> Dict[str, torch.Tensor]:
