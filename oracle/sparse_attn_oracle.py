@@ -54,7 +54,7 @@ __all__ = [
     "visible", "capped", "key_set", "pos_q", "pos_k", "mask_rows", "rope_theta", "rotate",
     "attention_rows", "attention_fast", "attention", "plan", "plan_items_of_tile",
     "topk_scores", "topk_select", "pair_counts", "pair_count_total", "q0_closed_form",
-    "alibi_slope", "q0_alibi_closed_form",
+    "alibi_slope", "q0_alibi_closed_form", "segmented_run",
 ]
 
 
@@ -465,4 +465,72 @@ def q0_alibi_closed_form(v: np.ndarray, spec: MaskSpec, rows: Sequence[int], m: 
         wgt = np.exp(-m * np.minimum(i - A, spec.L))
         O[r] = (wgt @ v[A]) / wgt.sum()
     return O, lse
+
+
+# ----------------------------------------------------------------------------
+# Several segments end to end (segmented-execution page, 方法详解 / 整体框架 and
+# 关键设计: (C_i, o_i) = F(x_i, C_{i-1}, R_{i-1}))
+# ----------------------------------------------------------------------------
+
+def segmented_run(Q_segs, K_segs, V_segs, n_local: int, M: int, R: int,
+                  rope_base: Optional[float], scale: float):
+    """Runs N segments through the segment recurrence, one head set per call.
+
+    Q_segs[i], K_segs[i], V_segs[i]: [H, S, d] raw projections of segment i.
+    Heads 0..n_local-1 are local: they attend to [C_{i-1} | segment], C being
+    the latest M raw keys/values they have seen (the tail carried across
+    segments).  Heads n_local..H-1 are long-range: they attend to
+    [R_{i-1} | segment], R_{i-1} being the top-R rows of a read-only pool that
+    holds every earlier segment's raw keys/values of those heads, scored by
+    the segment-end raw query and kept in pool order.  Segment 1 has no
+    prefix.  The prefix takes positions 0..P-1 and the segment P..P+S-1
+    (attention in SEGMENT mode); the carried tail and the retrieved prefix
+    have the same length, so M == R is required.
+
+    Order after segment i: the tail becomes the last M rows of
+    [C_{i-1} | segment]; the segment's long-head rows are appended to the
+    pool; the next prefix is retrieved from the updated pool with the last
+    query of segment i.
+
+    Returns a list of per-segment dicts {"O", "LSE", "P", "idx"} (idx: the
+    retrieved pool rows the segment's long heads read, or None) and the final
+    state {"tail_k", "tail_v", "pool_k", "pool_v"}.
+    """
+    if M != R:
+        raise ValueError("the carried tail and the retrieved prefix must have one length")
+    H, S, d = np.asarray(Q_segs[0]).shape
+    n_long = H - n_local
+    tail_k = np.zeros((n_local, 0, d))
+    tail_v = np.zeros((n_local, 0, d))
+    pool_k = np.zeros((n_long, 0, d))
+    pool_v = np.zeros((n_long, 0, d))
+    pref_k = np.zeros((n_long, 0, d))
+    pref_v = np.zeros((n_long, 0, d))
+    idx = None
+    out = []
+    for Qi, Ki, Vi in zip(Q_segs, K_segs, V_segs):
+        Qi = np.asarray(Qi, dtype=np.float64)
+        Ki = np.asarray(Ki, dtype=np.float64)
+        Vi = np.asarray(Vi, dtype=np.float64)
+        P = tail_k.shape[1]
+        assert pref_k.shape[1] == P
+        Kc = np.concatenate([np.concatenate([tail_k, pref_k], axis=0), Ki], axis=1)
+        Vc = np.concatenate([np.concatenate([tail_v, pref_v], axis=0), Vi], axis=1)
+        spec = MaskSpec(SEGMENT, S, P + S, P=P)
+        O, L = attention(Qi, Kc, Vc, spec, rope_base, scale)
+        out.append({"O": O, "LSE": L, "P": P, "idx": idx})
+        # carry: the latest M keys/values of the local heads
+        keep = min(M, P + S)
+        tail_k = Kc[:n_local, P + S - keep:]
+        tail_v = Vc[:n_local, P + S - keep:]
+        # the detached pool gains this segment's long-head rows
+        pool_k = np.concatenate([pool_k, Ki[n_local:]], axis=1)
+        pool_v = np.concatenate([pool_v, Vi[n_local:]], axis=1)
+        # the next prefix: top-R pool rows scored by this segment's last query
+        k_sel = min(R, pool_k.shape[1])
+        idx = np.stack([topk_select(topk_scores(Qi[n_local + j, S - 1], pool_k[j]), k_sel)
+                        for j in range(n_long)]) if n_long else np.zeros((0, k_sel), dtype=np.int64)
+        pref_k = np.stack([pool_k[j, idx[j]] for j in range(n_long)]) if n_long else np.zeros((0, k_sel, d))
+        pref_v = np.stack([pool_v[j, idx[j]] for j in range(n_long)]) if n_long else np.zeros((0, k_sel, d))
+    return out, {"tail_k": tail_k, "tail_v": tail_v, "pool_k": pool_k, "pool_v": pool_v}
 

@@ -25,6 +25,12 @@ Pins, by oracle function:
                         geometric-series partition function and the weight at
                         distance 0, at the cap and beyond it); a steep slope
                         that leaves only the diagonal.
+  segmented_run         the whole history of raw projections: the final tail
+                        is the latest M history rows, the pool every long-head
+                        row; each retrieved prefix is heapq's top-M of the
+                        history under a pure-Python score chain; every
+                        segment's output equals torch SDPA on explicitly
+                        rotated [prefix | segment] rows.
 """
 import heapq
 import json
@@ -537,3 +543,61 @@ def test_alibi_heads_use_their_slopes():
         np.testing.assert_allclose(lse[h], l_h, rtol=0, atol=1e-12)
     with pytest.raises(ValueError):
         O.attention(Q, K, V, spec, 10000.0, 0.2, alibi_exp=8.0)
+
+
+# ---------------------------------------------------------------------------
+# several segments end to end (segmented-execution page, method / overall framework)
+# ---------------------------------------------------------------------------
+
+def _py_chain(q, k):
+    acc = 0.0
+    for c in range(len(q)):
+        acc = acc + float(q[c]) * float(k[c])
+    return acc
+
+
+@pytest.mark.parametrize("S,M", [(150, 100), (60, 100)])
+def test_segmented_run_against_history(S, M):
+    # Everything a segment reads is stated here in terms of the whole history of raw
+    # projections: local heads see the latest M history rows, long heads the top-M history
+    # rows by the previous segment's last query, both at positions 0..P-1 before the
+    # segment at P..P+S-1 (causal), checked with torch SDPA on explicitly rotated inputs.
+    H, nl, d, N, base = 4, 2, 32, 3, 10000.0
+    scale = 1.0 / math.sqrt(d)
+    Qs = [torch.randn(H, S, d, dtype=torch.float64).to(torch.bfloat16).double().numpy() for _ in range(N)]
+    Ks = [torch.randn(H, S, d, dtype=torch.float64).to(torch.bfloat16).double().numpy() for _ in range(N)]
+    Vs = [torch.randn(H, S, d, dtype=torch.float64).numpy() for _ in range(N)]
+    out, state = O.segmented_run(Qs, Ks, Vs, nl, M, M, base, scale)
+    K_all = np.concatenate(Ks, axis=1)
+    V_all = np.concatenate(Vs, axis=1)
+    # final state: the last M rows of the local heads' history; the whole long-head history
+    keep = min(M, N * S)
+    np.testing.assert_array_equal(state["tail_k"], K_all[:nl, N * S - keep:])
+    np.testing.assert_array_equal(state["tail_v"], V_all[:nl, N * S - keep:])
+    np.testing.assert_array_equal(state["pool_k"], K_all[nl:])
+    np.testing.assert_array_equal(state["pool_v"], V_all[nl:])
+    for i in range(N):
+        seg = out[i]
+        hist = i * S
+        P = min(M, hist)
+        assert seg["P"] == P
+        if i == 0:
+            assert seg["idx"] is None
+        for h in range(H):
+            if h < nl or i == 0:
+                pk, pv = K_all[h, hist - P:hist], V_all[h, hist - P:hist]
+            else:
+                j = h - nl
+                scores = [_py_chain(Qs[i - 1][h, S - 1], K_all[h, r]) for r in range(hist)]
+                top = heapq.nlargest(P, range(hist), key=lambda r: (scores[r], -r))
+                assert seg["idx"][j].tolist() == sorted(top)
+                pk, pv = K_all[h, sorted(top)], V_all[h, sorted(top)]
+            kc = np.concatenate([pk, Ks[i][h]])
+            vc = np.concatenate([pv, Vs[i][h]])
+            qr = complex_rope(torch.from_numpy(Qs[i][h]), torch.arange(P, P + S), base)
+            kr = complex_rope(torch.from_numpy(kc), torch.arange(P + S), base)
+            mask = torch.ones(S, P + S, dtype=torch.bool).tril(P)
+            ref = sdpa(qr, kr, torch.from_numpy(vc), mask, scale).numpy()
+            np.testing.assert_allclose(seg["O"][h], ref, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        O.segmented_run(Qs, Ks, Vs, nl, M, M + 1, base, scale)
