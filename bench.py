@@ -106,6 +106,41 @@ def gemm_ceiling_tflops(torch):
     return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
 
 
+def multi_segment(wl, inp, n_seg, torch):
+    """The segment workload run as n_seg consecutive segments of one layer: forward
+    (RoPE stage + fused forward), tail carry, pool append and retrieval per segment.
+    Every segment reuses the workload's q / K / V (timing only); the pool grows to
+    n_seg * S rows."""
+    from structured_sparse_attention_attn_amd.pipeline import SegmentRunner
+    S, M, H, d, nl = wl.n_q, wl.P, wl.h_q, wl.d, wl.n_local
+    run = SegmentRunner(H, nl, d, S, M, n_seg * S, rope_base=wl.rope_base, scale=wl.scale)
+    for kb, vb in run.bufs:
+        kb[:, :, M:] = inp["k_seg"].to("cuda")
+        vb[:, :, M:] = inp["v_seg"].to("cuda")
+    q = inp["q"].to("cuda")
+    o = torch.empty_like(q)
+
+    def one_pass():
+        run.reset()
+        for _ in range(n_seg):
+            run.step(q, o=o)
+
+    one_pass()  # builds the plans, warms up
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    one_pass()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    pairs = sum(S * min(M, i * S) + S * (S + 1) // 2 for i in range(n_seg)) * H
+    return {"segments": n_seg, "ms_per_segment": round(ms / n_seg, 4),
+            "effective_tflops": round(4.0 * d * pairs / (ms * 1e-3) / 1e12, 2),
+            "pool_rows_final": n_seg * S,
+            "note": "forward + tail carry + pool append + top-k retrieval per segment"}
+
+
 def source_sha(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -174,6 +209,8 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--no-gemm-ceiling", action="store_true",
                     help="skip the dense bf16 GEMM reference measurement")
+    ap.add_argument("--segments", type=int, default=8,
+                    help="segment workload: also run this many consecutive segments (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 256 MiB device copy (scale for PMC byte counters)")
     args = ap.parse_args()
@@ -314,6 +351,8 @@ def main():
         "stages_roofline": stage_roofline,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    if wl.mode == "segment" and args.segments > 0:
+        out["multi_segment"] = multi_segment(wl, inp, args.segments, torch)
     if not args.no_gemm_ceiling:
         out["gemm_ceiling_tflops"] = round(gemm_ceiling_tflops(torch), 1)
     if not args.no_cpu_baseline:

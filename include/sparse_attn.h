@@ -215,6 +215,37 @@ int topk_retrieve(int32_t dtype, int32_t n_heads, int32_t pool_len, int32_t d, i
                   void *pref_k, void *pref_v, int64_t pref_head_stride, int64_t pref_row_stride,
                   void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Segment carry (segmented-execution page, overall framework and key designs
+ * 2-3: (C_i, o_i) = F(x_i, C_{i-1}, R_{i-1})): the state one segment hands to
+ * the next, taken after the segment's forward.
+ *   k, v      [n_heads, prefix_len + seg_len, d] raw keys and values the
+ *             segment attended to ([prefix | segment] per head), strides in
+ *             elements; heads 0..n_local-1 are local, the rest long-range.
+ *   tail_k/_v [n_local, >= keep, d] receive the local heads' latest
+ *             keep = min(tail_len, prefix_len + seg_len) rows, in order (the
+ *             carried tail C_i; the next segment reads it as its prefix).
+ *   pool_k/_v [n_heads - n_local, pool_cap, d] receive the long-range heads'
+ *             segment rows (k, v rows prefix_len .. prefix_len+seg_len-1) at
+ *             pool rows pool_len .. pool_len+seg_len-1 (the detached pool the
+ *             next prefix is retrieved from with topk_retrieve).
+ * dtype SA_BF16 or SA_F32; d * element size a multiple of 16 bytes; every
+ * pointer 16-byte aligned and every stride a multiple of 16 bytes; row
+ * strides of the destinations >= d.  Tail pointers may be NULL when
+ * n_local == 0, pool pointers when n_local == n_heads.  No destination row
+ * may overlap a source row or another destination row (checked on the host
+ * per head over the span from its first to its last row; use separate or
+ * alternating buffers).  Errors: SA_EINVAL, SA_ENOSPACE (pool_len + seg_len >
+ * pool_cap), SA_EUNSUPPORTED (device), SA_EHIP.
+ */
+int sparse_attn_segment_carry(int32_t dtype, int32_t n_heads, int32_t n_local, int32_t d,
+                              int32_t prefix_len, int32_t seg_len, int32_t tail_len,
+                              const void *k, const void *v, int64_t kv_head_stride,
+                              int64_t kv_row_stride, void *tail_k, void *tail_v,
+                              int64_t tail_head_stride, int64_t tail_row_stride, void *pool_k,
+                              void *pool_v, int64_t pool_head_stride, int64_t pool_row_stride,
+                              int64_t pool_len, int64_t pool_cap, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -74,8 +74,12 @@ _lib.sparse_attn_attend.argtypes = [_MASKP, _vp, _sz, _ARGSP, _vp, _sz, _vp]
 _lib.sa_topk_workspace_bytes.argtypes = [_i32, _i32, ctypes.POINTER(_sz)]
 _lib.topk_retrieve.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp, _i64, _i64,
                                _vp, _vp, _vp, _vp, _i64, _i64, _vp, _sz, _vp]
+_lib.sparse_attn_segment_carry.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
+                                           _i64, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64,
+                                           _i64, _vp]
 for _name in ("sa_plan_layout", "sa_plan_bytes", "sparse_attn_plan", "sa_fwd_workspace_bytes",
-              "sparse_attn_fwd", "sparse_attn_rope", "sparse_attn_attend", "sa_topk_workspace_bytes", "topk_retrieve"):
+              "sparse_attn_fwd", "sparse_attn_rope", "sparse_attn_attend", "sa_topk_workspace_bytes",
+              "topk_retrieve", "sparse_attn_segment_carry"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -228,3 +232,27 @@ def plan_to_host(m: sa_mask_t, plan) -> dict:
         "sep_bits": sec(lay.off_sep_bits, lay.n_blocks, np.uint64),
         "blk_sep": sec(lay.off_blk_sep, lay.n_blocks + 1, np.int32),
     }
+
+
+def sparse_attn_segment_carry(k, v, n_local: int, prefix_len: int, seg_len: int, tail_len: int,
+                              tail_k, tail_v, pool_k, pool_v, pool_len: int, stream=None) -> None:
+    """Tail and pool update after a segment (see include/sparse_attn.h).
+
+    k, v [n_heads, prefix_len + seg_len, d]; tail_k / tail_v [n_local, >=keep, d] or None;
+    pool_k / pool_v [n_heads - n_local, pool_cap, d] or None (d contiguous everywhere).
+    """
+    import torch
+    dtype = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}[k.dtype]
+    n_heads, _, d = k.shape
+    for a, b in ((k, v), (tail_k, tail_v), (pool_k, pool_v)):
+        if a is not None and (b is None or a.stride() != b.stride() or a.stride(-1) != 1):
+            raise ValueError("k/v, tail_k/tail_v and pool_k/pool_v pairs need equal strides, "
+                             "d contiguous")
+    ts = tail_k.stride()[:2] if tail_k is not None else (0, 0)
+    ps = pool_k.stride()[:2] if pool_k is not None else (0, 0)
+    cap = pool_k.shape[1] if pool_k is not None else 0
+    _check(_lib.sparse_attn_segment_carry(dtype, n_heads, n_local, d, prefix_len, seg_len, tail_len,
+                                          _ptr(k), _ptr(v), k.stride(0), k.stride(1), _ptr(tail_k),
+                                          _ptr(tail_v), ts[0], ts[1], _ptr(pool_k), _ptr(pool_v),
+                                          ps[0], ps[1], pool_len, cap, _stream(stream)))
+

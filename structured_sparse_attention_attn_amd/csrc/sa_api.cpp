@@ -1,9 +1,11 @@
 // C ABI of libsparse_attn.so: argument checks, workspace layout and launches.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <vector>
 
 #include "sa_common.h"
 
@@ -303,6 +305,119 @@ int topk_retrieve(int32_t dtype, int32_t n_heads, int32_t pool_len, int32_t d, i
                                  pool_head_stride, pool_row_stride, idx, score, pref_k, pref_v,
                                  pref_head_stride, pref_row_stride, ws, stream);
   if (e != hipSuccess) return fail(SA_EHIP, "top-k launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"
+
+namespace {
+
+// Byte span of `rows` rows starting at row r0 of each of `heads` heads.
+struct Span {
+  uintptr_t lo, hi;
+  bool dst;
+};
+
+void add_spans(std::vector<Span>& out, const void* base, int heads, int64_t hs, int64_t rs, int64_t r0,
+               int64_t rows, int64_t row_bytes, int esz, bool dst) {
+  if (rows <= 0) return;
+  for (int h = 0; h < heads; ++h) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(base) + (uintptr_t)((h * hs + r0 * rs) * esz);
+    out.push_back({lo, lo + (uintptr_t)((rows - 1) * rs * esz + row_bytes), dst});
+  }
+}
+
+// True when some destination span meets any other span.
+bool dst_overlap(std::vector<Span>& v) {
+  std::sort(v.begin(), v.end(), [](const Span& a, const Span& b) { return a.lo < b.lo; });
+  uintptr_t end_all = 0, end_dst = 0;
+  for (const Span& s : v) {
+    if (s.lo < end_dst || (s.dst && s.lo < end_all)) return true;
+    end_all = std::max(end_all, s.hi);
+    if (s.dst) end_dst = std::max(end_dst, s.hi);
+  }
+  return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_attn_segment_carry(int32_t dtype, int32_t n_heads, int32_t n_local, int32_t d, int32_t prefix_len,
+                              int32_t seg_len, int32_t tail_len, const void* k, const void* v,
+                              int64_t kv_head_stride, int64_t kv_row_stride, void* tail_k, void* tail_v,
+                              int64_t tail_head_stride, int64_t tail_row_stride, void* pool_k, void* pool_v,
+                              int64_t pool_head_stride, int64_t pool_row_stride, int64_t pool_len,
+                              int64_t pool_cap, hipStream_t stream) {
+  if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_EINVAL, "unknown dtype %d", dtype);
+  const int esz = dtype == SA_BF16 ? 2 : 4;
+  if (n_heads < 1 || n_local < 0 || n_local > n_heads)
+    return fail(SA_EINVAL, "need n_heads >= 1 and 0 <= n_local <= n_heads (got %d, %d)", n_heads, n_local);
+  if (d < 1 || ((int64_t)d * esz) % 16 != 0) return fail(SA_EINVAL, "d * element size must be a multiple of 16 bytes");
+  if (prefix_len < 0 || seg_len < 0 || tail_len < 0)
+    return fail(SA_EINVAL, "prefix_len, seg_len and tail_len must be >= 0");
+  if (pool_len < 0 || pool_cap < 0) return fail(SA_EINVAL, "pool_len and pool_cap must be >= 0");
+  const int n_long = n_heads - n_local;
+  const int keep = std::min<int64_t>(tail_len, (int64_t)prefix_len + seg_len);
+  const bool do_tail = n_local > 0 && keep > 0;
+  const bool do_pool = n_long > 0 && seg_len > 0;
+  if (do_pool && pool_len + seg_len > pool_cap)
+    return fail(SA_ENOSPACE, "pool too small: %lld + %d > %lld rows", (long long)pool_len, seg_len,
+                (long long)pool_cap);
+  if (!do_tail && !do_pool) return ok();
+  if (k == nullptr || v == nullptr) return fail(SA_EINVAL, "k and v must not be NULL");
+  auto bad_stride = [&](int64_t s) { return s < 0 || (s * esz) % 16 != 0; };
+  if (!aligned16(k) || !aligned16(v) || bad_stride(kv_head_stride) || bad_stride(kv_row_stride))
+    return fail(SA_EINVAL, "k and v must be 16-byte aligned with strides that are multiples of 16 bytes");
+  if (do_tail && (tail_k == nullptr || tail_v == nullptr || !aligned16(tail_k) || !aligned16(tail_v) ||
+                  bad_stride(tail_head_stride) || bad_stride(tail_row_stride) || tail_row_stride < d))
+    return fail(SA_EINVAL, "tail buffers: 16-byte aligned, strides multiples of 16 bytes, row stride >= d");
+  if (do_pool && (pool_k == nullptr || pool_v == nullptr || !aligned16(pool_k) || !aligned16(pool_v) ||
+                  bad_stride(pool_head_stride) || bad_stride(pool_row_stride) || pool_row_stride < d))
+    return fail(SA_EINVAL, "pool buffers: 16-byte aligned, strides multiples of 16 bytes, row stride >= d");
+  const int64_t row_bytes = (int64_t)d * esz;
+  std::vector<Span> spans;
+  if (do_tail) {
+    const int64_t r0 = (int64_t)prefix_len + seg_len - keep;
+    add_spans(spans, k, n_local, kv_head_stride, kv_row_stride, r0, keep, row_bytes, esz, false);
+    add_spans(spans, v, n_local, kv_head_stride, kv_row_stride, r0, keep, row_bytes, esz, false);
+    add_spans(spans, tail_k, n_local, tail_head_stride, tail_row_stride, 0, keep, row_bytes, esz, true);
+    add_spans(spans, tail_v, n_local, tail_head_stride, tail_row_stride, 0, keep, row_bytes, esz, true);
+  }
+  if (do_pool) {
+    const char* kl = static_cast<const char*>(k) + (int64_t)n_local * kv_head_stride * esz;
+    const char* vl = static_cast<const char*>(v) + (int64_t)n_local * kv_head_stride * esz;
+    add_spans(spans, kl, n_long, kv_head_stride, kv_row_stride, prefix_len, seg_len, row_bytes, esz, false);
+    add_spans(spans, vl, n_long, kv_head_stride, kv_row_stride, prefix_len, seg_len, row_bytes, esz, false);
+    add_spans(spans, pool_k, n_long, pool_head_stride, pool_row_stride, pool_len, seg_len, row_bytes, esz, true);
+    add_spans(spans, pool_v, n_long, pool_head_stride, pool_row_stride, pool_len, seg_len, row_bytes, esz, true);
+  }
+  if (dst_overlap(spans)) return fail(SA_EINVAL, "a destination of the carry overlaps a source or another destination");
+  int r = check_device();
+  if (r != SA_OK) return r;
+  sa::CarryDesc c;
+  c.esz = esz;
+  c.n_local = n_local;
+  c.n_pool_heads = do_pool ? n_long : 0;
+  c.d = d;
+  c.prefix_len = prefix_len;
+  c.seg_len = seg_len;
+  c.keep = do_tail ? keep : 0;
+  c.k = k;
+  c.v = v;
+  c.kv_hs = kv_head_stride;
+  c.kv_rs = kv_row_stride;
+  c.tail_k = tail_k;
+  c.tail_v = tail_v;
+  c.t_hs = tail_head_stride;
+  c.t_rs = tail_row_stride;
+  c.pool_k = pool_k;
+  c.pool_v = pool_v;
+  c.p_hs = pool_head_stride;
+  c.p_rs = pool_row_stride;
+  c.pool_len = pool_len;
+  hipError_t e = sa::launch_carry(c, stream);
+  if (e != hipSuccess) return fail(SA_EHIP, "carry launch: %s", hipGetErrorString(e));
   return ok();
 }
 

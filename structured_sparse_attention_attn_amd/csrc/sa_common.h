@@ -90,4 +90,21 @@ hipError_t launch_topk(int dtype, int n_heads, int pool_len, int d, int k, const
 
 size_t topk_workspace_bytes(int n_heads, int pool_len);
 
+// Segment carry: strides in elements, sizes validated by the caller.
+struct CarryDesc {
+  int esz, n_local, n_pool_heads, d, prefix_len, seg_len, keep;  // keep: tail rows (0: none)
+  const void* k;
+  const void* v;
+  int64_t kv_hs, kv_rs;
+  void* tail_k;
+  void* tail_v;
+  int64_t t_hs, t_rs;
+  void* pool_k;
+  void* pool_v;
+  int64_t p_hs, p_rs;
+  int64_t pool_len;
+};
+
+hipError_t launch_carry(const CarryDesc& c, hipStream_t s);
+
 }  // namespace sa

@@ -41,6 +41,7 @@ struct RopeArgs {
   int64_t cap_rows;
   int n_cap, L;
   int n_pos;
+  int row0;         // first row handled: B*h_kv when no key row needs work
   int write_q;      // write the query copy (rotated when rotate is set)
   float q_scale;    // factor applied to the stored queries
   float cap_scale;  // factor applied to the stored capped keys
@@ -114,7 +115,8 @@ constexpr int ROPE_ROWS = 8;  // rows (batch x head) per thread
 
 // Thread = (position, group of 8 rotation pairs, chunk of ROPE_ROWS rows).
 // Rows 0 .. B*h_kv-1 are the key rows of the position, the rest its query
-// rows.  The sincos values are computed once per thread and reused for its
+// rows; chunks start at row0, past the key rows when they need no work (no
+// rotation and no separator gather).  The sincos values are computed once per thread and reused for its
 // rows; all of a thread's row loads are issued before its first store.
 template <typename T>
 __global__ __launch_bounds__(256) void rope_qk(RopeArgs p) {
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void rope_qk(RopeArgs p) {
   const int n_krows = pos < p.n_k ? p.B * p.h_kv : 0;
   const int i = pos - p.q_pos0;
   const int n_qrows = (p.write_q && i >= 0 && i < p.n_q) ? p.B * p.h_q : 0;
-  const int r_begin = blockIdx.y * ROPE_ROWS;
+  const int r_begin = p.row0 + blockIdx.y * ROPE_ROWS;
   if (r_begin >= p.B * (p.h_kv + p.h_q)) return;
   float cs[8], sn[8];
   if (p.rotate) {
@@ -306,7 +308,8 @@ hipError_t launch_rope(const sa_mask_t& m, const sa_plan_header_t& lay, const vo
   p.theta = theta;
   const int64_t threads = (int64_t)p.n_pos * (a.d / 16);
   const unsigned wg = (unsigned)ceil_div(threads, 256);
-  const unsigned chunks = (unsigned)ceil_div((int64_t)a.batch * (a.h_kv + a.h_q), ROPE_ROWS);
+  p.row0 = (rotate || gather) ? 0 : a.batch * a.h_kv;
+  const unsigned chunks = (unsigned)ceil_div((int64_t)a.batch * (a.h_kv + a.h_q) - p.row0, ROPE_ROWS);
   if (a.dtype == SA_BF16)
     hipLaunchKernelGGL(rope_qk<unsigned short>, dim3(wg, chunks), dim3(256), 0, s, p);
   else

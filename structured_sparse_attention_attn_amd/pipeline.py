@@ -11,7 +11,7 @@ import torch
 
 from . import (SA_MASK_LAMBDA, SA_MASK_SEGMENT, SA_MASK_SEPLLM, fwd_args, mask,
                sa_fwd_workspace_bytes, sa_plan_bytes, sa_topk_workspace_bytes,
-               sparse_attn_fwd, sparse_attn_plan, topk_retrieve)
+               sparse_attn_fwd, sparse_attn_plan, sparse_attn_segment_carry, topk_retrieve)
 
 KINDS = {"sepllm": SA_MASK_SEPLLM, "lambda": SA_MASK_LAMBDA, "segment": SA_MASK_SEGMENT}
 
@@ -62,3 +62,87 @@ class TopK:
     def __call__(self, q_score, pool_k, k, idx, score=None, pool_v=None, pref_k=None, pref_v=None):
         topk_retrieve(q_score, pool_k, k, idx, self.ws, score=score, pool_v=pool_v,
                       pref_k=pref_k, pref_v=pref_v)
+
+
+class SegmentRunner:
+    """Several segments of one layer end to end: (C_i, o_i) = F(x_i, C_{i-1}, R_{i-1})
+    (segmented-execution page, overall framework and key designs 2-3).
+
+    Heads 0..n_local-1 attend to [tail | segment], the tail being their latest
+    M raw keys/values; the other heads attend to [prefix | segment], the prefix
+    being the top-M rows of a detached pool of their earlier segments, scored
+    by the previous segment's last raw query.  The first segment has no prefix.
+    K/V live in two alternating buffers [1, H, M+S, d]: the caller writes the
+    segment's raw K/V into the views seg_kv() returns (rows M..M+S-1), the
+    prefix occupies rows M-P..M-1, and after the forward the carry and the
+    retrieval fill the other buffer's prefix rows for the next segment.
+    """
+
+    def __init__(self, n_heads: int, n_local: int, d: int, seg_len: int, tail_len: int,
+                 pool_cap: int, *, rope_base=None, scale=None, dtype=torch.bfloat16,
+                 device: str = "cuda"):
+        self.H, self.nl, self.d, self.S, self.M = n_heads, n_local, d, seg_len, tail_len
+        self.n_long = n_heads - n_local
+        self.rope_base, self.scale = rope_base, scale
+        shape = (1, n_heads, tail_len + seg_len, d)
+        self.bufs = [(torch.empty(shape, dtype=dtype, device=device),
+                      torch.empty(shape, dtype=dtype, device=device)) for _ in range(2)]
+        self.cur = 0
+        self.P = 0
+        self.pool_len = 0
+        self.pool_k = self.pool_v = None
+        self.topk = None
+        if self.n_long:
+            self.pool_k = torch.empty((self.n_long, pool_cap, d), dtype=dtype, device=device)
+            self.pool_v = torch.empty_like(self.pool_k)
+            self.topk = TopK(self.n_long, pool_cap, device=device)
+        self.idx = None  # pool rows of the prefix the next segment's long heads read
+        self._attn = {}
+        self.device = device
+
+    def reset(self) -> None:
+        """Start a new sequence: no tail, empty pool (plans and buffers are kept)."""
+        self.cur = 0
+        self.P = 0
+        self.pool_len = 0
+        self.idx = None
+
+    def seg_kv(self):
+        """Views [1, H, S, d] of the current buffer receiving the segment's raw K and V."""
+        k, v = self.bufs[self.cur]
+        return k[:, :, self.M:], v[:, :, self.M:]
+
+    def attention(self, P: int) -> SparseAttention:
+        if P not in self._attn:
+            sa = SparseAttention("segment", self.S, P + self.S, prefix_len=P, device=self.device)
+            sa.build_plan()
+            self._attn[P] = sa
+        return self._attn[P]
+
+    def step(self, q, o=None, lse=None):
+        """Forward of one segment (q [1, H, S, d] raw), then the carry and the retrieval."""
+        M, S, P, nl = self.M, self.S, self.P, self.nl
+        k, v = self.bufs[self.cur]
+        kc, vc = k[:, :, M - P:], v[:, :, M - P:]
+        o = self.attention(P).forward(q, kc, vc, o=o, lse=lse, rope_base=self.rope_base,
+                                      scale=self.scale)
+        nk, nv = self.bufs[1 - self.cur]
+        keep = min(M, P + S)
+        sparse_attn_segment_carry(kc[0], vc[0], nl, P, S, M,
+                                  nk[0, :nl, M - keep:M] if nl else None,
+                                  nv[0, :nl, M - keep:M] if nl else None,
+                                  self.pool_k, self.pool_v, self.pool_len)
+        nxt = keep
+        if self.n_long:
+            self.pool_len += S
+            ksel = min(M, self.pool_len)
+            self.idx = torch.empty((self.n_long, ksel), dtype=torch.int32, device=self.device)
+            self.topk(q[0, nl:, S - 1, :], self.pool_k[:, :self.pool_len], ksel, self.idx,
+                      pool_v=self.pool_v[:, :self.pool_len], pref_k=nk[0, nl:, M - ksel:M],
+                      pref_v=nv[0, nl:, M - ksel:M])
+            assert nl == 0 or ksel == keep
+            nxt = ksel
+        self.cur ^= 1
+        self.P = nxt
+        return o
+

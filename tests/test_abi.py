@@ -177,3 +177,41 @@ def test_import_fails_loudly_without_library(tmp_path):
     shutil.copy(os.path.join(os.path.dirname(sa.__file__), "__init__.py"), pkg / "__init__.py")
     r = subprocess.run(["python", "-c", "import sa_copy"], cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0 and "is missing" in r.stderr
+
+
+def test_segment_carry_validation():
+    lib = sa._lib
+    H, nl, d, P, S, M = 4, 2, 128, 64, 100, 64
+    row = d * 2
+    kv = 1 << 20                       # fake device addresses: only host checks run
+    hs = (P + S) * d
+    args = dict(dtype=sa.SA_BF16, n_heads=H, n_local=nl, d=d, prefix_len=P, seg_len=S, tail_len=M,
+                k=kv, v=kv + (1 << 24), kv_hs=hs, kv_rs=d,
+                tail_k=kv + (2 << 24), tail_v=kv + (3 << 24), t_hs=M * d, t_rs=d,
+                pool_k=kv + (4 << 24), pool_v=kv + (5 << 24), p_hs=1000 * d, p_rs=d,
+                pool_len=0, pool_cap=1000)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.sparse_attn_segment_carry(
+            a["dtype"], a["n_heads"], a["n_local"], a["d"], a["prefix_len"], a["seg_len"],
+            a["tail_len"], a["k"], a["v"], a["kv_hs"], a["kv_rs"], a["tail_k"], a["tail_v"],
+            a["t_hs"], a["t_rs"], a["pool_k"], a["pool_v"], a["p_hs"], a["p_rs"], a["pool_len"],
+            a["pool_cap"], None)
+    assert call(dtype=7) == sa.SA_EINVAL
+    assert call(n_local=5) == sa.SA_EINVAL
+    assert call(d=4) == sa.SA_EINVAL                       # 8 bytes: not a multiple of 16
+    assert call(pool_len=950) == sa.SA_ENOSPACE            # 950 + 100 > 1000
+    assert call(t_rs=d - 8) == sa.SA_EINVAL                # destination rows overlap
+    assert call(k=kv + 8) == sa.SA_EINVAL                  # misaligned
+    assert call(tail_k=0) == sa.SA_EINVAL                  # NULL tail with local heads
+    # in place: the tail written to rows 0..M-1 of the same buffer whose rows
+    # P+S-M .. P+S-1 are read overlaps when P + S < 2 M
+    assert call(tail_k=kv, tail_v=kv + (1 << 24), t_hs=(60 + 40) * d, kv_hs=100 * d, prefix_len=60,
+                seg_len=40, tail_len=64) == sa.SA_EINVAL
+    assert "overlap" in sa.sa_last_error()
+    # the pool written over the segment rows it reads
+    assert call(pool_k=kv + nl * hs * 2 + P * row, p_hs=hs) == sa.SA_EINVAL
+    # nothing to do (no local rows kept, no long heads): returns before any device call
+    assert call(n_local=H, tail_len=0) == sa.SA_OK
+

@@ -373,3 +373,47 @@ def test_topk_bitexact(sa, dtype):
                 np.testing.assert_array_equal(score[h].cpu().numpy(), s[ri])
                 assert torch.equal(pk[h].cpu(), kp[h][torch.from_numpy(ri).long()])
                 assert torch.equal(pv[h].cpu(), vp[h][torch.from_numpy(ri).long()])
+
+
+# Several segments end to end: forward, tail carry, pool append, retrieval by the
+# segment-end query (segmented-execution page, overall framework), against the oracle's
+# segment recurrence.
+@pytest.mark.parametrize("dtype,S,M,N", [("bf16", 300, 128, 3), ("bf16", 100, 128, 4),
+                                         ("f32", 200, 64, 3)])
+def test_segment_runner_vs_oracle(sa, dtype, S, M, N):
+    from structured_sparse_attention_attn_amd.pipeline import SegmentRunner
+    H, nl, base = 4, 2, 10000.0
+    d = 128 if dtype == "bf16" else 64
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    scale = d ** -0.5
+    stream = W.make_segment_stream(H, S, d, N, seed=77 + S, dtype=tdt)
+    runner = SegmentRunner(H, nl, d, S, M, N * S, rope_base=base, scale=scale, dtype=tdt)
+    got = []
+    for i, (q, k, v) in enumerate(stream):
+        log(f"segment runner {dtype} S={S} M={M}: segment {i}")
+        ks, vs = runner.seg_kv()
+        ks.copy_(k.cuda())
+        vs.copy_(v.cuda())
+        lse = torch.empty((1, H, S), dtype=torch.float32, device="cuda")
+        P = runner.P
+        o = runner.step(q.cuda(), lse=lse)
+        torch.cuda.synchronize()
+        got.append((to64(o[0]), to64(lse[0]), P, runner.idx.cpu().numpy().copy()))
+    ref, state = O.segmented_run([to64(x[0][0]) for x in stream], [to64(x[1][0]) for x in stream],
+                                 [to64(x[2][0]) for x in stream], nl, M, M, base, scale)
+    for i in range(N):
+        o_g, l_g, P, idx_g = got[i]
+        assert P == ref[i]["P"]
+        compare(o_g, ref[i]["O"], l_g, ref[i]["LSE"], dtype, nkeys=(P + np.arange(S) + 1)[None, :])
+        if i + 1 < N:
+            np.testing.assert_array_equal(idx_g, ref[i + 1]["idx"])
+    # the final state is a byte copy of the history
+    k_long = torch.cat([x[1][0, nl:] for x in stream], dim=1)
+    assert torch.equal(runner.pool_k[:, :N * S].cpu(), k_long)
+    keep = runner.P
+    nk, nv = runner.bufs[runner.cur]
+    k_loc = torch.cat([x[1][0, :nl] for x in stream], dim=1)
+    v_loc = torch.cat([x[2][0, :nl] for x in stream], dim=1)
+    assert torch.equal(nk[0, :nl, M - keep:M].cpu(), k_loc[:, N * S - keep:])
+    assert torch.equal(nv[0, :nl, M - keep:M].cpu(), v_loc[:, N * S - keep:])
+    np.testing.assert_array_equal(to64(nk[0, :nl, M - keep:M]), state["tail_k"])

@@ -137,6 +137,16 @@ def make_small_inputs(wl: Workload) -> Dict[str, torch.Tensor]:
     return out
 
 
+def make_segment_stream(n_heads: int, seg_len: int, d: int, n_segments: int, seed: int,
+                        dtype=torch.bfloat16):
+    """Raw q, k, v [1, n_heads, seg_len, d] for each of n_segments segments (drawn in that order)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    out = []
+    for _ in range(n_segments):
+        out.append(tuple(_randn((1, n_heads, seg_len, d), g).to(dtype) for _ in range(3)))
+    return out
+
+
 def make_pool_inputs(n_heads: int, pool_len: int, d: int, seed: int, dtype=torch.bfloat16):
     """Scoring queries [n_heads,d] and pool keys/values [n_heads,pool_len,d] for top-k tests."""
     g = torch.Generator("cpu").manual_seed(seed)
