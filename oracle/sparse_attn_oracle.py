@@ -54,7 +54,8 @@ __all__ = [
     "visible", "capped", "key_set", "pos_q", "pos_k", "mask_rows", "rope_theta", "rotate",
     "attention_rows", "attention_fast", "attention", "plan", "plan_items_of_tile",
     "topk_scores", "topk_select", "pair_counts", "pair_count_total", "q0_closed_form",
-    "alibi_slope", "q0_alibi_closed_form", "segmented_run",
+    "alibi_slope", "q0_alibi_closed_form", "segmented_run", "attention_grad_rows",
+    "attention_backward",
 ]
 
 
@@ -533,4 +534,84 @@ def segmented_run(Q_segs, K_segs, V_segs, n_local: int, M: int, R: int,
         pref_k = np.stack([pool_k[j, idx[j]] for j in range(n_long)]) if n_long else np.zeros((0, k_sel, d))
         pref_v = np.stack([pool_v[j, idx[j]] for j in range(n_long)]) if n_long else np.zeros((0, k_sel, d))
     return out, {"tail_k": tail_k, "tail_v": tail_v, "pool_k": pool_k, "pool_v": pool_v}
+
+
+# ----------------------------------------------------------------------------
+# Backward of the masked attention (gradients of O with respect to q, k, v)
+# ----------------------------------------------------------------------------
+
+def attention_grad_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, dO: np.ndarray,
+                        rows: Sequence[int], spec: MaskSpec, rope_base: Optional[float],
+                        scale: float, alibi: Optional[float] = None):
+    """Gradients of the listed rows' outputs, one head, definition mode.
+
+    For query i with key set A_i, logits s_j as in :func:`attention_rows`
+    (``s_j = scale <R(delta'_ij) q_i, k_j>``, plus ``-m delta'`` with ALiBi),
+    p = softmax(s), o_i = sum_j p_j v_j.  With the upstream gradient dO_i:
+    dp_j = <dO_i, v_j>, D_i = <dO_i, o_i>, ds_j = p_j (dp_j - D_i), and
+      dq_i  = sum_j ds_j * scale * R(-delta'_ij) k_j,
+      dk_j += ds_j * scale * R(delta'_ij) q_i,
+      dv_j += p_j * dO_i
+    (the rotation is orthogonal, so the transpose of R(delta) is R(-delta)).
+    Returns dq [len(rows), d] and the contributions of these rows to dk, dv
+    [n_k, d]; summed over every query row they are the full dk, dv.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    d = q.shape[1]
+    theta = rope_theta(d, rope_base) if rope_base else None
+    dq = np.zeros((len(rows), d))
+    dk = np.zeros((k.shape[0], d))
+    dv = np.zeros((v.shape[0], v.shape[1]))
+    for r, i in enumerate(rows):
+        i = int(i)
+        A = key_set(spec, i)
+        delta = pos_q(spec, i) - pos_k(spec, A)
+        if spec.mode == LAMBDA:
+            delta = np.minimum(delta, spec.L)
+        if theta is None:
+            qr = np.broadcast_to(q[i], (len(A), d))
+            kr = k[A]
+        else:
+            ang = delta.astype(np.float64)[:, None] * theta[None, :]
+            qr = rotate(np.broadcast_to(q[i], (len(A), d)), ang)   # R(delta) q_i per key
+            kr = rotate(k[A], -ang)                                 # R(-delta) k_j per key
+        s = scale * np.einsum("jd,jd->j", qr, k[A])
+        if alibi is not None:
+            s = s - alibi * delta.astype(np.float64)
+        p = np.exp(s - s.max())
+        p = p / p.sum()
+        o = p @ v[A]
+        dp = v[A] @ dO[i]
+        ds = p * (dp - dO[i] @ o)
+        dq[r] = scale * (ds @ kr)
+        np.add.at(dk, A, scale * ds[:, None] * qr)
+        np.add.at(dv, A, p[:, None] * dO[i][None, :])
+    return dq, dk, dv
+
+
+def attention_backward(Q, K, V, dO, spec: MaskSpec, rope_base: Optional[float], scale: float,
+                       alibi_exp: Optional[float] = None, rows: Optional[Sequence[int]] = None):
+    """Multi-head gradients: Q, dO [h_q, n_q, d]; K, V [h_kv, n_k, d] (batch squeezed).
+
+    dK and dV of kv head g sum the contributions of its query heads
+    h in [g*G, (g+1)*G), G = h_q / h_kv.  ``rows`` restricts the query rows
+    (dQ is returned for those rows; dK, dV then hold only their contributions).
+    """
+    h_q, h_kv = Q.shape[0], K.shape[0]
+    group = h_q // h_kv
+    rows = np.arange(Q.shape[1]) if rows is None else np.asarray(rows)
+    dQ = np.zeros((h_q, len(rows), Q.shape[2]))
+    dK = np.zeros(K.shape, dtype=np.float64)
+    dV = np.zeros(V.shape, dtype=np.float64)
+    for h in range(h_q):
+        g = h // group
+        m = None if alibi_exp is None else alibi_slope(h, h_q, alibi_exp)
+        dq, dk, dv = attention_grad_rows(Q[h], K[g], V[g], dO[h], rows, spec, rope_base, scale, m)
+        dQ[h] = dq
+        dK[g] += dk
+        dV[g] += dv
+    return dQ, dK, dV
 

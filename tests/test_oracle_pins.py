@@ -31,6 +31,11 @@ Pins, by oracle function:
                         history under a pure-Python score chain; every
                         segment's output equals torch SDPA on explicitly
                         rotated [prefix | segment] rows.
+  attention_grad_rows / attention_backward
+                        torch.autograd (fp64) through forwards built here from
+                        torch primitives (SepLLM, segment, capped Lambda via
+                        the RoPE realisation, capped ALiBi, GQA); central
+                        finite differences through the definition-mode forward.
 """
 import heapq
 import json
@@ -601,3 +606,97 @@ def test_segmented_run_against_history(S, M):
             np.testing.assert_allclose(seg["O"][h], ref, rtol=0, atol=1e-12)
     with pytest.raises(ValueError):
         O.segmented_run(Qs, Ks, Vs, nl, M, M + 1, base, scale)
+
+
+# ---------------------------------------------------------------------------
+# backward (gradients of O)
+# ---------------------------------------------------------------------------
+
+def _torch_rot_angles(pos, d, base):
+    inv = 1.0 / (base ** (torch.arange(0, d, 2, dtype=torch.float64) / d))
+    return pos.to(torch.float64)[:, None] * inv[None, :]
+
+
+def _torch_rotate(x, ang):
+    """rotate-half RoPE applied with per-row angles ang [n, d/2] (autograd-friendly)."""
+    h = x.shape[-1] // 2
+    c, s = torch.cos(ang), torch.sin(ang)
+    return torch.cat([x[..., :h] * c - x[..., h:] * s, x[..., h:] * c + x[..., :h] * s], dim=-1)
+
+
+def _torch_masked_attention(q, k, v, logits_fn, mask):
+    s = logits_fn(q, k).masked_fill(~mask, -math.inf)
+    return torch.softmax(s, dim=-1) @ v
+
+
+@pytest.mark.parametrize("case", ["sepllm", "segment", "lambda_capped", "alibi_capped", "gqa"])
+def test_backward_vs_torch_autograd(case):
+    # the forward is built here from torch primitives (rotations, a boolean mask, softmax) and
+    # differentiated by torch.autograd in fp64; the oracle's gradient formulas must agree
+    d, m, base = 16, 150, 500.0
+    scale = 1.0 / math.sqrt(d)
+    h_q, h_kv = (4, 2) if case == "gqa" else (1, 1)
+    P = 40 if case == "segment" else 0
+    n_k = m + P
+    Q = torch.randn(h_q, m, d, dtype=torch.float64)
+    K = torch.randn(h_kv, n_k, d, dtype=torch.float64)
+    V = torch.randn(h_kv, n_k, d, dtype=torch.float64)
+    dO = torch.randn(h_q, m, d, dtype=torch.float64)
+    i = torch.arange(m)[:, None] + P
+    j = torch.arange(n_k)[None, :]
+    rope, slope_exp = base, None
+    if case in ("sepllm", "gqa"):
+        flags = (RNG.random(n_k) < 0.15).astype(np.uint8)
+        spec = O.MaskSpec(O.SEPLLM, m, n_k, a=3, w=20, sep=flags)
+        mask = (j <= i) & ((j < 3) | (i - j < 20) | torch.from_numpy(flags).bool()[None, :])
+    elif case == "segment":
+        spec = O.MaskSpec(O.SEGMENT, m, n_k, P=P)
+        mask = j <= i
+    else:
+        spec = O.MaskSpec(O.LAMBDA, m, n_k, n_s=6, L=25)
+        mask = (j <= i) & ((j < 6) | (i - j <= 25))
+        if case == "alibi_capped":
+            rope, slope_exp = None, 2.0
+    capped = mask & (i - j > 25) if case in ("lambda_capped", "alibi_capped") else torch.zeros_like(mask)
+    Qg, Kg, Vg = (t.clone().requires_grad_(True) for t in (Q, K, V))
+    outs = []
+    for h in range(h_q):
+        g = h // (h_q // h_kv)
+        qh, kh, vh = Qg[h], Kg[g], Vg[g]
+        if rope:
+            qr = _torch_rotate(qh, _torch_rot_angles(torch.arange(P, P + m), d, base))
+            kr = _torch_rotate(kh, _torch_rot_angles(torch.arange(n_k), d, base))
+            qcap = _torch_rotate(qh, _torch_rot_angles(torch.full((m,), 25), d, base))
+            fn = lambda a, b: torch.where(capped, scale * (qcap @ kh.T), scale * (qr @ kr.T))  # noqa: E731
+        else:
+            slope = 2.0 ** (-slope_exp * (h + 1) / h_q) if slope_exp else 0.0
+            dist = torch.clamp(i - j, max=25).to(torch.float64) if slope_exp else 0.0
+            fn = lambda a, b, s_=slope, d_=dist: scale * (a @ b.T) - s_ * d_  # noqa: E731
+        outs.append(_torch_masked_attention(qh, kh, vh, fn, mask))
+    (torch.stack(outs) * dO).sum().backward()
+    dq, dk, dv = O.attention_backward(Q.numpy(), K.numpy(), V.numpy(), dO.numpy(), spec, rope, scale,
+                                      alibi_exp=slope_exp)
+    np.testing.assert_allclose(dq, Qg.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dk, Kg.grad.numpy(), rtol=0, atol=1e-11)
+    np.testing.assert_allclose(dv, Vg.grad.numpy(), rtol=0, atol=1e-11)
+
+
+def test_backward_capped_finite_differences():
+    # central differences of <dO, O> through the oracle's (pinned) definition-mode forward
+    d, m = 8, 60
+    spec = O.MaskSpec(O.LAMBDA, m, m, n_s=4, L=10)
+    q, k, v, do = (RNG.standard_normal((m, d)) for _ in range(4))
+    dq, dk, dv = O.attention_grad_rows(q, k, v, do, range(m), spec, 100.0, 0.3)
+
+    def f(q_, k_, v_):
+        o, _ = O.attention_rows(q_, k_, v_, range(m), spec, 100.0, 0.3)
+        return float((o * do).sum())
+    eps = 1e-6
+    for name, g in (("q", dq), ("k", dk), ("v", dv)):
+        for a, b in [(3, 1), (17, 5), (40, 0), (59, 7), (0, 2)]:
+            args = {"q_": q.copy(), "k_": k.copy(), "v_": v.copy()}
+            args[name + "_"][a, b] += eps
+            fp = f(**args)
+            args[name + "_"][a, b] -= 2 * eps
+            fm = f(**args)
+            assert abs((fp - fm) / (2 * eps) - g[a, b]) < 1e-7, (name, a, b)
