@@ -184,6 +184,43 @@ int sparse_attn_rope(const sa_mask_t *m, const void *plan, size_t plan_bytes,
 int sparse_attn_attend(const sa_mask_t *m, const void *plan, size_t plan_bytes,
                        const sa_fwd_args_t *args, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Backward of sparse_attn_fwd: the gradients of O with respect to the raw q,
+ * k and v, given the upstream gradient dO (the textbook gradient of a masked
+ * softmax, over the same key sets: SepLLM page, part 6.2, which trains with
+ * the mask; LM-Infinite's capped distance and the segment prefix enter the
+ * same way as in the forward, the rotations being undone at the end).
+ *   dout  [batch, h_q, n_q, d] upstream gradient (dtype of the forward).
+ *   dq    [batch, h_q, n_q, d], dk, dv [batch, h_kv, n_k, d]: written (not
+ *         accumulated); GQA heads sum into their kv head's dk, dv.
+ * Strides in elements, last dimension contiguous, 16-byte aligned.
+ */
+typedef struct {
+  const void *dout; int64_t dout_stride[3];
+  void *dq; int64_t dq_stride[3];
+  void *dk; int64_t dk_stride[3];
+  void *dv; int64_t dv_stride[3];
+} sa_bwd_args_t;
+
+/* Host only: bytes of device workspace sparse_attn_bwd needs for (m, args). */
+int sa_bwd_workspace_bytes(const sa_mask_t *m, const sa_fwd_args_t *args, size_t *bytes);
+
+/*
+ * Computes dq, dk, dv for the forward described by (m, plan, args): args is
+ * the forward's argument block with o and lse as that forward wrote them
+ * (lse is required here).  It reruns the RoPE stage into ws, then a row-sum
+ * kernel (D = rowsum(dO * O)), a query-major dQ kernel over the plan's units,
+ * a key-major dK/dV kernel (one work group per 64-key group: dense block,
+ * gathered separator chunk or capped block; every sum in a fixed order, no
+ * atomics) and a per-row finishing kernel (inverse rotations, separator and
+ * capped contributions).  bf16 with d = 128 only (else SA_EUNSUPPORTED).
+ * ws: ws_bytes >= sa_bwd_workspace_bytes; scratch.  Errors: SA_EINVAL,
+ * SA_EUNSUPPORTED, SA_ENOSPACE, SA_EHIP.
+ */
+int sparse_attn_bwd(const sa_mask_t *m, const void *plan, size_t plan_bytes,
+                    const sa_fwd_args_t *args, const sa_bwd_args_t *grads, void *ws,
+                    size_t ws_bytes, hipStream_t stream);
+
 /* Host only: bytes of device workspace topk_retrieve needs. */
 int sa_topk_workspace_bytes(int32_t n_heads, int32_t pool_len, size_t *bytes);
 

@@ -60,6 +60,11 @@ class sa_fwd_args_t(ctypes.Structure):
                 ("lse", _vp)]
 
 
+class sa_bwd_args_t(ctypes.Structure):
+    _fields_ = [("dout", _vp), ("dout_stride", _i64 * 3), ("dq", _vp), ("dq_stride", _i64 * 3),
+                ("dk", _vp), ("dk_stride", _i64 * 3), ("dv", _vp), ("dv_stride", _i64 * 3)]
+
+
 _MASKP = ctypes.POINTER(sa_mask_t)
 _ARGSP = ctypes.POINTER(sa_fwd_args_t)
 _lib.sa_last_error.restype = ctypes.c_char_p
@@ -77,9 +82,12 @@ _lib.topk_retrieve.argtypes = [_i32, _i32, _i32, _i32, _i32, _vp, _i64, _vp, _vp
 _lib.sparse_attn_segment_carry.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
                                            _i64, _vp, _vp, _i64, _i64, _vp, _vp, _i64, _i64, _i64,
                                            _i64, _vp]
+_lib.sa_bwd_workspace_bytes.argtypes = [_MASKP, _ARGSP, ctypes.POINTER(_sz)]
+_lib.sparse_attn_bwd.argtypes = [_MASKP, _vp, _sz, _ARGSP, ctypes.POINTER(sa_bwd_args_t), _vp, _sz, _vp]
 for _name in ("sa_plan_layout", "sa_plan_bytes", "sparse_attn_plan", "sa_fwd_workspace_bytes",
               "sparse_attn_fwd", "sparse_attn_rope", "sparse_attn_attend", "sa_topk_workspace_bytes",
-              "topk_retrieve", "sparse_attn_segment_carry"):
+              "topk_retrieve", "sparse_attn_segment_carry", "sa_bwd_workspace_bytes",
+              "sparse_attn_bwd"):
     getattr(_lib, _name).restype = ctypes.c_int
 
 
@@ -255,4 +263,30 @@ def sparse_attn_segment_carry(k, v, n_local: int, prefix_len: int, seg_len: int,
                                           _ptr(k), _ptr(v), k.stride(0), k.stride(1), _ptr(tail_k),
                                           _ptr(tail_v), ts[0], ts[1], _ptr(pool_k), _ptr(pool_v),
                                           ps[0], ps[1], pool_len, cap, _stream(stream)))
+
+
+def bwd_args(dout, dq, dk, dv) -> sa_bwd_args_t:
+    """sa_bwd_args_t for [B,H,T,d] tensors (last dimension contiguous)."""
+    g = sa_bwd_args_t()
+    for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        if t.stride(-1) != 1:
+            raise ValueError(f"{name}: last dimension must be contiguous")
+        setattr(g, name, t.data_ptr())
+        getattr(g, name + "_stride")[:] = list(t.stride()[:3])
+    return g
+
+
+def sa_bwd_workspace_bytes(m: sa_mask_t, args: sa_fwd_args_t) -> int:
+    out = _sz()
+    _check(_lib.sa_bwd_workspace_bytes(ctypes.byref(m), ctypes.byref(args), ctypes.byref(out)))
+    return out.value
+
+
+def sparse_attn_bwd(m: sa_mask_t, plan, args: sa_fwd_args_t, grads: sa_bwd_args_t, ws,
+                    stream=None) -> None:
+    """Enqueue the backward (see include/sparse_attn.h)."""
+    _check(_lib.sparse_attn_bwd(ctypes.byref(m), _ptr(plan), plan.numel(), ctypes.byref(args),
+                                ctypes.byref(grads), _ptr(ws),
+                                0 if ws is None else ws.numel() * ws.element_size(),
+                                _stream(stream)))
 

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["sa_api.cpp", "sa_plan.hip", "sa_rope.hip", "sa_fwd.hip", "sa_topk.hip", "sa_carry.hip"]
+SOURCES = ["sa_api.cpp", "sa_plan.hip", "sa_rope.hip", "sa_fwd.hip", "sa_topk.hip", "sa_carry.hip",
+           "sa_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -153,6 +153,44 @@ WsLayout ws_layout(const sa_mask_t& m, const sa_fwd_args_t& a) {
   return w;
 }
 
+// Backward workspace: the forward's sections, then the fp32 gradient sections.
+struct BwdLayout {
+  WsLayout fwd;
+  int64_t D = -1, dq_acc = -1, dq_cap = -1, dk_acc = -1, dv_acc = -1;
+  int64_t dksep = -1, dvsep = -1, dkcap = -1, dvcap = -1;
+  int64_t total = 0;
+};
+
+BwdLayout bwd_layout(const sa_mask_t& m, const sa_fwd_args_t& a) {
+  BwdLayout L;
+  L.fwd = ws_layout(m, a);
+  int64_t off = sa::align_up(L.fwd.total, 256);
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = sa::align_up(off + bytes, 256);
+    return o;
+  };
+  const int64_t qrows = (int64_t)a.batch * a.h_q * m.n_q;
+  const int64_t krows = (int64_t)a.batch * a.h_kv * m.n_k;
+  const int64_t row = 4 * (int64_t)a.d;
+  const bool use_cap = m.kind == SA_MASK_LAMBDA && a.rope == SA_ROPE_HALF && L.fwd.n_cap > 0;
+  L.D = take(4 * qrows);
+  L.dq_acc = take(row * qrows);
+  if (use_cap) L.dq_cap = take(row * qrows);
+  L.dk_acc = take(row * krows);
+  L.dv_acc = take(row * krows);
+  if (L.fwd.sep_rows > 0) {
+    L.dksep = take(row * a.batch * a.h_kv * L.fwd.sep_rows);
+    L.dvsep = take(row * a.batch * a.h_kv * L.fwd.sep_rows);
+  }
+  if (use_cap) {
+    L.dkcap = take(row * a.batch * a.h_kv * L.fwd.cap_rows);
+    L.dvcap = take(row * a.batch * a.h_kv * L.fwd.cap_rows);
+  }
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -261,6 +299,70 @@ int sparse_attn_rope(const sa_mask_t* m, const void* plan, size_t plan_bytes, co
 int sparse_attn_attend(const sa_mask_t* m, const void* plan, size_t plan_bytes, const sa_fwd_args_t* a,
                        void* ws, size_t ws_bytes, hipStream_t stream) {
   return run_fwd(m, plan, plan_bytes, a, ws, ws_bytes, stream, STAGE_ATTEND);
+}
+
+int sa_bwd_workspace_bytes(const sa_mask_t* m, const sa_fwd_args_t* a, size_t* bytes) {
+  int r = check_mask(m);
+  if (r != SA_OK) return r;
+  if (a == nullptr || bytes == nullptr) return fail(SA_EINVAL, "args or bytes is NULL");
+  *bytes = (size_t)bwd_layout(*m, *a).total;
+  return ok();
+}
+
+int sparse_attn_bwd(const sa_mask_t* m, const void* plan, size_t plan_bytes, const sa_fwd_args_t* a,
+                    const sa_bwd_args_t* g, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int r = check_mask(m);
+  if (r != SA_OK) return r;
+  if ((r = check_args(m, a)) != SA_OK) return r;
+  if (a->dtype != SA_BF16 || a->d != 128)
+    return fail(SA_EUNSUPPORTED, "the backward supports bf16 with d = 128");
+  if (a->lse == nullptr) return fail(SA_EINVAL, "the backward needs the forward's lse");
+  if (!aligned16(a->lse)) return fail(SA_EINVAL, "lse must be 16-byte aligned");
+  if (g == nullptr) return fail(SA_EINVAL, "grads is NULL");
+  if ((r = check_tensor("dout", g->dout, g->dout_stride, 2)) != SA_OK) return r;
+  if ((r = check_tensor("dq", g->dq, g->dq_stride, 2)) != SA_OK) return r;
+  if ((r = check_tensor("dk", g->dk, g->dk_stride, 2)) != SA_OK) return r;
+  if ((r = check_tensor("dv", g->dv, g->dv_stride, 2)) != SA_OK) return r;
+  if (plan == nullptr) return fail(SA_EINVAL, "plan is NULL");
+  const sa_plan_header_t lay = sa::plan_layout(*m);
+  if (plan_bytes < (size_t)lay.total_bytes)
+    return fail(SA_ENOSPACE, "plan buffer too small: %zu < %lld bytes", plan_bytes, (long long)lay.total_bytes);
+  const BwdLayout L = bwd_layout(*m, *a);
+  if (ws_bytes < (size_t)L.total)
+    return fail(SA_ENOSPACE, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)L.total);
+  if (ws == nullptr || !aligned16(ws)) return fail(SA_EINVAL, "workspace must be a 16-byte aligned device pointer");
+  if ((r = check_device()) != SA_OK) return r;
+  char* base = static_cast<char*>(ws);
+  sa::RopeOut ro;
+  memset(&ro, 0, sizeof(ro));
+  ro.qrot = L.fwd.qrot >= 0 ? base + L.fwd.qrot : nullptr;
+  ro.krot = L.fwd.krot >= 0 ? base + L.fwd.krot : nullptr;
+  ro.ksep = L.fwd.ksep >= 0 ? base + L.fwd.ksep : nullptr;
+  ro.vsep = L.fwd.vsep >= 0 ? base + L.fwd.vsep : nullptr;
+  ro.sep_rows = L.fwd.sep_rows;
+  ro.kcap = L.fwd.kcap >= 0 ? base + L.fwd.kcap : nullptr;
+  ro.cap_rows = L.fwd.cap_rows;
+  ro.n_cap = L.fwd.n_cap;
+  sa::ThetaTable th;
+  memset(&th, 0, sizeof(th));
+  if (a->rope == SA_ROPE_HALF)
+    for (int c = 0; c < a->d / 2; ++c) th.th[c] = std::pow((double)a->rope_base, -2.0 * c / a->d);
+  hipError_t e = sa::launch_rope(*m, lay, plan, *a, th, ro, stream);
+  if (e != hipSuccess) return fail(SA_EHIP, "rope launch: %s", hipGetErrorString(e));
+  auto sec = [&](int64_t off) { return off >= 0 ? reinterpret_cast<float*>(base + off) : nullptr; };
+  sa::BwdWs w;
+  w.D = sec(L.D);
+  w.dq_acc = sec(L.dq_acc);
+  w.dq_cap = sec(L.dq_cap);
+  w.dk_acc = sec(L.dk_acc);
+  w.dv_acc = sec(L.dv_acc);
+  w.dksep = sec(L.dksep);
+  w.dvsep = sec(L.dvsep);
+  w.dkcap = sec(L.dkcap);
+  w.dvcap = sec(L.dvcap);
+  e = sa::launch_bwd(*m, lay, plan, *a, *g, ro, w, th, stream);
+  if (e != hipSuccess) return fail(SA_EHIP, "backward launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int sa_topk_workspace_bytes(int32_t n_heads, int32_t pool_len, size_t* bytes) {

@@ -1,0 +1,923 @@
+// Backward of the sparse attention forward: dQ, dK and dV over the same plan.
+//
+// What is computed (the forward's logits and softmax as in sa_fwd.hip; the
+// gradient is the textbook one of a masked softmax): with P_ij =
+// exp(s_ij - LSE_i) over the visible pairs, D_i = <dO_i, O_i>,
+// dP_ij = <dO_i, v_j> and dS_ij = P_ij (dP_ij - D_i):
+//   dq~_i = scale sum_j dS_ij k~_j        dk~_j = scale sum_i dS_ij q~_i
+//   dv_j  = sum_i P_ij dO_i
+// in the rotated frame (q~ = R(pos_q) q, k~ = R(pos_k) k); the raw gradients
+// are dq = R(-pos_q) dq~ and dk = R(-pos_k) dk~.  LM-Infinite capped pairs
+// (logit scale <q_i, R(-L) k_j>) add scale R(-L) k_j dS_ij to dq_i and
+// scale R(L) q_i dS_ij to dk_j.  SepLLM pairs read from the gathered
+// separator rows add to those rows' gradients, which are added back to the
+// separator positions.  Every sum runs in a fixed order: no atomics, the
+// result is the same bit for bit from run to run.
+//
+// Kernels:
+//   bwd_rowdot     D_i = <dO_i, O_i> (fp32).
+//   bwd_dq_bf16    query-major, the forward's work units per 128-query tile:
+//                  S^T = K Q^T, P = 2^(S - LSE log2 e), dP^T = V dO^T,
+//                  dS, then dQ^T += K^T dS^T (K^T by LDS transpose reads).
+//   bwd_dkdv_bf16  key-major: one work group per (batch, kv head, 64-key
+//                  group), the group being a dense key block, a chunk of 64
+//                  gathered separator rows or a block of capped keys.  It
+//                  visits every (tile, query head) that reads the group, 64
+//                  queries at a time: S = Q K^T, P, dP = dO V^T, dS, then
+//                  dV^T += dO^T P and dK^T += Q^T dS (transpose reads of the
+//                  query-side tiles).
+//   bwd_finish     per row: the inverse rotations, the separator and capped
+//                  contributions, the output dtype.
+#include <type_traits>
+
+#include "sa_common.h"
+#include "sa_device.h"
+
+namespace sa {
+namespace {
+
+struct BwdArgs {
+  const void* q;      // rotated queries, scaled by scale * log2(e) (the forward's copy)
+  int64_t qsB, qsH, qsT;
+  const void* qraw;   // raw queries (capped pairs)
+  int64_t qrB, qrH, qrT;
+  const void* k;      // rotated keys (raw when rope is off)
+  int64_t ksB, ksH, ksT;
+  const void* v;
+  int64_t vsB, vsH, vsT;
+  const void* ksep;   // [B, h_kv, sep_rows, d] gathered separator keys (rotated) / values
+  const void* vsep;
+  int64_t sep_rows;
+  const void* kcap;   // [B, h_kv, cap_rows, d] R(-L) k * scale * log2(e)
+  int64_t cap_rows;
+  const void* dout;
+  int64_t dsB, dsH, dsT;
+  const float* lse;   // [B, h_q, n_q]
+  const float* Dv;    // [B, h_q, n_q]
+  float* dq_acc;      // [B, h_q, n_q, d]: scale * sum dS k~ (rotated frame)
+  float* dq_cap;      // [B, h_q, n_q, d]: scale * sum dS R(-L) k (capped pairs), or null
+  float* dk_acc;      // [B, h_kv, n_k, d]: sum dS q~s over the dense blocks
+  float* dv_acc;      // [B, h_kv, n_k, d]
+  float* dksep;       // [B, h_kv, sep_rows, d]
+  float* dvsep;
+  float* dkcap;       // [B, h_kv, cap_rows, d]: sum dS q (raw) over the capped pairs
+  float* dvcap;       // [B, h_kv, cap_rows, d]: sum P dO over the capped pairs
+  const int* tile_ptr;
+  const int* items;
+  const int* sep_count;
+  const unsigned long long* sep_bits;
+  const int* n_sep;   // the plan header's separator count
+  int kind, B, h_q, h_kv, n_q, n_k, n_tiles, n_blocks, group;
+  int a, w, n_s, L, P, n_cap;
+  int use_cap, gather;
+  float scale;
+  int alibi;
+  float alibi_e;
+  int n_sep_chunks, n_cap_blocks;  // group counts of the key-major kernel
+};
+
+// ---------------------------------------------------------------------------
+// D_i = <dO_i, O_i>: one thread per row, 16-byte pieces.
+// ---------------------------------------------------------------------------
+
+struct RowDotArgs {
+  const char* dout;
+  int64_t dsB, dsH, dsT;
+  const char* o;
+  int64_t osB, osH, osT;
+  float* D;
+  int B, h, n, d, esz;
+};
+
+__device__ inline float bf_lo(unsigned x) { return __uint_as_float(x << 16); }
+__device__ inline float bf_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
+
+__global__ __launch_bounds__(256) void bwd_rowdot(RowDotArgs p) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t rows = (int64_t)p.B * p.h * p.n;
+  if (row >= rows) return;
+  const int i = (int)(row % p.n);
+  const int64_t bh = row / p.n;
+  const int h = (int)(bh % p.h), b = (int)(bh / p.h);
+  const char* a = p.dout + (b * p.dsB + h * p.dsH + (int64_t)i * p.dsT) * p.esz;
+  const char* c = p.o + (b * p.osB + h * p.osH + (int64_t)i * p.osT) * p.esz;
+  float acc = 0.f;
+  const int bytes = p.d * p.esz;
+  for (int off = 0; off < bytes; off += 16) {
+    const uint4 x = *reinterpret_cast<const uint4*>(a + off);
+    const uint4 y = *reinterpret_cast<const uint4*>(c + off);
+    if (p.esz == 2) {
+      const unsigned xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(bf_lo(xs[e]), bf_lo(ys[e]), acc);
+        acc = fmaf(bf_hi(xs[e]), bf_hi(ys[e]), acc);
+      }
+    } else {
+      acc = fmaf(__uint_as_float(x.x), __uint_as_float(y.x), acc);
+      acc = fmaf(__uint_as_float(x.y), __uint_as_float(y.y), acc);
+      acc = fmaf(__uint_as_float(x.z), __uint_as_float(y.z), acc);
+      acc = fmaf(__uint_as_float(x.w), __uint_as_float(y.w), acc);
+    }
+  }
+  p.D[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// LDS staging through registers: a 64-row x 256-byte block, rows swizzled as
+// in the forward (16-byte chunk c of row r at chunk c ^ swzf(r & 15)).  Rows
+// at or past `valid` repeat row valid-1 (finite values, masked later).
+// ---------------------------------------------------------------------------
+
+struct Stage4 {
+  uint4 x[4];
+};
+
+__device__ inline void stage_load(Stage4& st, const char* base, int64_t stride, int valid, int tid) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int piece = tid + 256 * e;  // 1024 pieces of 16 bytes
+    const int r = piece >> 4, c = piece & 15;
+    const int rr = min(r, valid - 1);
+    st.x[e] = *reinterpret_cast<const uint4*>(base + (int64_t)rr * stride + c * 16);
+  }
+}
+
+__device__ inline void stage_store(const Stage4& st, char* lds, int tid) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int piece = tid + 256 * e;
+    const int r = piece >> 4, c = piece & 15;
+    *reinterpret_cast<uint4*>(lds + r * 256 + ((c ^ swzf(r & 15)) << 4)) = st.x[e];
+  }
+}
+
+// Packs one 32-row C tile (rows = the MFMA contraction index) into the two
+// bf16x8 B operands: k-step ks takes registers 8 ks .. 8 ks + 7.
+__device__ inline void pack_tile(const f32x16& s, bf16x8 (&pb)[2]) {
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) {
+      const f32x2 two = {s[8 * ks + e], s[8 * ks + e + 1]};
+      const bf16x2 c2 = __builtin_convertvector(two, bf16x2);
+      pb[ks][e] = c2[0];
+      pb[ks][e + 1] = c2[1];
+    }
+  }
+}
+
+// ===========================================================================
+// dQ: query-major, 4 waves x 32 queries per 128-query tile (the forward's
+// layout: S^T = K Q^T, one query per lane).
+// ===========================================================================
+
+template <bool ALIBI>
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * BLK_BYTES];  // [K | V] of the unit
+  char* const Ks = smem;
+  char* const Vs = smem + BLK_BYTES;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  int b, kvh, t, hq;
+  map_unit(p, b, kvh, t, hq);
+  const int qi = t * TQ + wid * 32 + l32;
+  const bool qok = qi < p.n_q;
+
+  TileUnits tu;
+  tu.it0 = ld_uniform(p.tile_ptr + t);
+  tu.n_items = ld_uniform(p.tile_ptr + t + 1) - tu.it0;
+  tu.n_capu = 0;
+  if (p.use_cap)
+    while (tu.n_capu < tu.n_items && ((ld_uniform(p.items + tu.it0 + tu.n_capu) >> 24) & SA_ITEM_CAPPED)) ++tu.n_capu;
+  tu.nsep = p.gather ? ld_uniform(p.sep_count + t) : 0;
+  tu.n_ch = (tu.nsep + BK - 1) / BK;
+  tu.kb = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH) * 2;
+  tu.vb = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH) * 2;
+  tu.kst = p.ksT * 2;
+  tu.vst = p.vsT * 2;
+  tu.capb = static_cast<const char*>(p.kcap) + ((int64_t)b * p.h_kv + kvh) * p.cap_rows * (D128 * 2);
+  const int64_t sep_off = ((int64_t)b * p.h_kv + kvh) * p.sep_rows * (D128 * 2);
+  tu.ksb = static_cast<const char*>(p.ksep) + sep_off;
+  tu.vsb = static_cast<const char*>(p.vsep) + sep_off;
+  const int n_units = tu.n_capu + tu.n_ch + tu.n_items;
+  const float m2 = ALIBI ? alibi_slope_log2(p, hq) : 0.f;
+  const float Lf = (float)p.L;
+
+  bf16x8 qf[8], df[8];
+  auto load_rows = [&](bf16x8 (&f)[8], const void* base, int64_t sB, int64_t sH, int64_t sT) {
+    const char* row = static_cast<const char*>(base) + (b * sB + hq * sH + (int64_t)qi * sT) * 2;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      uint4 x = make_uint4(0, 0, 0, 0);
+      if (qok) x = ld16(row + (16 * s + 8 * hl) * 2);
+      f[s] = __builtin_bit_cast(bf16x8, x);
+    }
+  };
+  if (tu.n_capu > 0) load_rows(qf, p.qraw, p.qrB, p.qrH, p.qrT);
+  else load_rows(qf, p.q, p.qsB, p.qsH, p.qsT);
+  load_rows(df, p.dout, p.dsB, p.dsH, p.dsT);
+  const int64_t rowi = ((int64_t)b * p.h_q + hq) * p.n_q + (qok ? qi : 0);
+  const float lse2 = qok ? p.lse[rowi] * LOG2E : 0.f;
+  const float Dq = qok ? p.Dv[rowi] : 0.f;
+  const f32x16 neg_lse = f32x16{} - lse2;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+
+  // Row-fragment reads (K for S, V for dP) and transpose reads (K^T for dQ),
+  // the forward's per-lane addressing.
+  const int kf = swzf(l32) ^ hl;
+  const int vrow = 4 * hl + ((lane & 15) >> 2);
+  const int vf0 = swzf(vrow), vf1 = swzf(vrow + 8);
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int vcb = vcol >> 3;
+
+  auto store_acc = [&](float* dst, float f) {
+    if (!qok) return;
+    float* row = dst + rowi * D128;
+#pragma unroll
+    for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dm + 8 * g + 4 * hl;
+        *reinterpret_cast<float4*>(row + d0) =
+            make_float4(acc[dm][4 * g] * f, acc[dm][4 * g + 1] * f, acc[dm][4 * g + 2] * f, acc[dm][4 * g + 3] * f);
+      }
+  };
+
+  for (int u = 0; u < n_units; ++u) {
+    if (u == tu.n_capu && u > 0) {
+      // capped units done: their dq (raw frame) goes to dq_cap, the rest is rotated-frame
+      store_acc(p.dq_cap, LN2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+      load_rows(qf, p.q, p.qsB, p.qsH, p.qsT);
+    }
+    const Unit cur = unit_at<ALIBI>(p, tu, u);
+    {
+      Stage4 sk, sv;
+      stage_load(sk, cur.kbase, cur.kstride, cur.kvalid, tid);
+      stage_load(sv, cur.vbase, cur.vstride, cur.vvalid, tid);
+      __syncthreads();  // the previous unit's reads are done
+      stage_store(sk, Ks, tid);
+      stage_store(sv, Vs, tid);
+      __syncthreads();
+    }
+    // --- S^T = K Q^T - lse2 and dP^T = V dO^T ---
+    f32x16 s[2], dp[2];
+    {
+      const char* kl = Ks + l32 * 256;
+      const char* vl = Vs + l32 * 256;
+      f32x16 c0 = neg_lse, c1 = neg_lse, e0 = f32x16{}, e1 = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int off = ((2 * ks) ^ kf) << 4;
+        const bf16x8 k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + off));
+        const bf16x8 k1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + 32 * 256 + off));
+        const bf16x8 v0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vl + off));
+        const bf16x8 v1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vl + 32 * 256 + off));
+        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], c1, 0, 0, 0);
+        e0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, df[ks], e0, 0, 0, 0);
+        e1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, df[ks], e1, 0, 0, 0);
+      }
+      s[0] = c0;
+      s[1] = c1;
+      dp[0] = e0;
+      dp[1] = e1;
+    }
+    switch (cur.mk) {
+      case MK_NONE: break;
+      case MK_COUNT: apply_mask<MK_COUNT>(p, cur, qi, hl, s); break;
+      case MK_SEPLLM: apply_mask<MK_SEPLLM>(p, cur, qi, hl, s); break;
+      case MK_LALL: apply_mask<MK_LALL>(p, cur, qi, hl, s); break;
+      case MK_LNORM: apply_mask<MK_LNORM>(p, cur, qi, hl, s); break;
+      case MK_LCAP: apply_mask<MK_LCAP>(p, cur, qi, hl, s); break;
+      default: apply_mask<MK_SEG>(p, cur, qi, hl, s); break;
+    }
+    if constexpr (ALIBI) add_alibi(cur, qi, hl, m2, Lf, s);
+    // --- dS = P (dP - D), masked pairs exactly 0 ---
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r]) * (dp[mb][r] - Dq);
+    bf16x8 dsb[4];
+    pack_p(s, dsb);
+    // --- dQ^T += K^T dS^T ---
+    {
+      const char* tl = Ks + vrow * 256 + ((vcol & 7) << 1);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kst = i >> 2, dm = i & 3;
+        const char* a0 = tl + (16 * kst) * 256 + (((4 * dm + vcb) ^ vf0) << 4);
+        const char* a1 = tl + (16 * kst + 8) * 256 + (((4 * dm + vcb) ^ vf1) << 4);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1));
+        acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                         dsb[kst], acc[dm], 0, 0, 0);
+      }
+    }
+  }
+  if (p.use_cap) {
+    if (tu.n_capu == n_units && n_units > 0) {
+      store_acc(p.dq_cap, LN2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+    } else if (tu.n_capu == 0) {
+      f32x16 keep[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { keep[i] = acc[i]; acc[i] = f32x16{}; }
+      store_acc(p.dq_cap, 0.f);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = keep[i];
+    }
+  }
+  store_acc(p.dq_acc, p.scale);
+}
+
+// ===========================================================================
+// dK, dV: key-major.  Work group = (batch, kv head, key group); 4 waves, wave
+// w owns keys 32 (w & 1) .. +31 of the group and queries 32 (w >> 1) .. +31 of
+// each 64-query chunk; S = Q K^T has queries as rows and one key per lane, so
+// the gradient accumulators dK^T, dV^T (d x 32 keys) stay in the lane.
+// ===========================================================================
+
+enum GroupKind : int { G_DENSE = 0, G_SEP = 1, G_CAP = 2 };
+
+// Key-on-lane masks: register r of the tile holds query i0 + 8 (r / 4) + r % 4
+// (i0 = the tile's first query + 4 hl), the lane's key is j.
+template <int MK>
+__device__ inline void mask_keys(const BwdArgs& p, int i0, int j, bool jsep, int count_ok, f32x16& s) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int i = i0 + 8 * (r >> 2) + (r & 3);
+    bool vis = i < p.n_q;
+    if (MK == MK_COUNT) {
+      vis = vis & (count_ok != 0);
+    } else if (MK == MK_NONE) {
+    } else if (MK == MK_SEPLLM) {
+      vis = vis & (j <= i) & (j < p.n_k) & ((j < p.a) | (i - j < p.w) | jsep);
+    } else if (MK == MK_LALL) {
+      vis = vis & (j <= i) & (j < p.n_k) & ((j < p.n_s) | (i - j <= p.L));
+    } else if (MK == MK_LNORM) {
+      vis = vis & (j <= i) & (j < p.n_k) & (i - j <= p.L);
+    } else if (MK == MK_LCAP) {
+      vis = vis & (j < p.n_s) & (j < p.n_k) & (i - j > p.L);
+    } else {
+      vis = vis & (j <= p.P + i) & (j < p.n_k);
+    }
+    s[r] = vis ? s[r] : NEG_INF;
+  }
+}
+
+// First tile t in [lo, n_tiles) with sep_count[t] > c0 (sep_count is
+// nondecreasing in t); n_tiles if none.
+__device__ inline int first_gathering_tile(const BwdArgs& p, int c0) {
+  int lo = 0, hi = p.n_tiles;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (ld_uniform(p.sep_count + mid) > c0) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// The item of block blk in tile t, or -1 (items are ascending by block).
+__device__ inline int find_item(const BwdArgs& p, int t, int blk) {
+  int lo = ld_uniform(p.tile_ptr + t), hi = ld_uniform(p.tile_ptr + t + 1);
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    const int it = ld_uniform(p.items + mid);
+    const int bb = it & 0xffffff;
+    if (bb == blk) return it;
+    if (bb < blk) lo = mid + 1;
+    else hi = mid;
+  }
+  return -1;
+}
+
+template <bool ALIBI>
+__global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
+  // [K group | V group | Q chunk | dO chunk], 64 rows x 256 bytes each
+  __shared__ __attribute__((aligned(16))) char smem[4 * BLK_BYTES];
+  char* const Kg = smem;
+  char* const Vg = smem + BLK_BYTES;
+  char* const Qc = smem + 2 * BLK_BYTES;
+  char* const Dc = smem + 3 * BLK_BYTES;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hl = lane >> 5;
+  const int kw = wid & 1, qw = wid >> 1;
+  const int BH = p.B * p.h_kv;
+  const int bh = blockIdx.x % BH;
+  const int gi = blockIdx.x / BH;
+  const int b = bh / p.h_kv, kvh = bh % p.h_kv;
+
+  int kind, idx;
+  if (gi < p.n_sep_chunks) { kind = G_SEP; idx = gi; }
+  else if (gi < p.n_sep_chunks + p.n_cap_blocks) { kind = G_CAP; idx = gi - p.n_sep_chunks; }
+  else { kind = G_DENSE; idx = gi - p.n_sep_chunks - p.n_cap_blocks; }
+
+  // the group's key / value rows, row count and output rows
+  const char* kbase;
+  const char* vbase;
+  int64_t kstr, vstr;
+  int valid;
+  float* dk_out;
+  float* dv_out;
+  int key0 = 0;        // key index of row 0 (dense and capped groups)
+  int n_sep_all = 0;
+  if (kind == G_SEP) {
+    n_sep_all = ld_uniform(p.n_sep);
+    if (idx * BK >= n_sep_all) return;
+    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.sep_rows;
+    kbase = static_cast<const char*>(p.ksep) + (ho + (int64_t)idx * BK) * (D128 * 2);
+    vbase = static_cast<const char*>(p.vsep) + (ho + (int64_t)idx * BK) * (D128 * 2);
+    kstr = vstr = D128 * 2;
+    valid = min(BK, n_sep_all - idx * BK);
+    dk_out = p.dksep + (ho + (int64_t)idx * BK) * D128;
+    dv_out = p.dvsep + (ho + (int64_t)idx * BK) * D128;
+  } else if (kind == G_CAP) {
+    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.cap_rows;
+    kbase = static_cast<const char*>(p.kcap) + (ho + (int64_t)idx * BK) * (D128 * 2);
+    kstr = D128 * 2;
+    vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)idx * BK * p.vsT) * 2;
+    vstr = p.vsT * 2;
+    valid = min(BK, p.n_cap - idx * BK);
+    key0 = idx * BK;
+    dk_out = p.dkcap + (ho + (int64_t)idx * BK) * D128;
+    dv_out = p.dvcap + (ho + (int64_t)idx * BK) * D128;
+  } else {
+    kbase = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH + (int64_t)idx * BK * p.ksT) * 2;
+    vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)idx * BK * p.vsT) * 2;
+    kstr = p.ksT * 2;
+    vstr = p.vsT * 2;
+    valid = min(BK, p.n_k - idx * BK);
+    key0 = idx * BK;
+    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.n_k + (int64_t)idx * BK;
+    dk_out = p.dk_acc + ho * D128;
+    dv_out = p.dv_acc + ho * D128;
+  }
+  {
+    Stage4 sk, sv;
+    stage_load(sk, kbase, kstr, valid, tid);
+    stage_load(sv, vbase, vstr, valid, tid);
+    stage_store(sk, Kg, tid);
+    stage_store(sv, Vg, tid);
+  }
+
+  // this lane's key
+  const int kslot = 32 * kw + l32;
+  const int j = key0 + kslot;
+  bool jsep = false;
+  if (kind == G_DENSE && p.kind == SA_MASK_SEPLLM && j < p.n_k)
+    jsep = (p.sep_bits[idx] >> kslot) & 1ull;
+
+  f32x16 dka[4], dva[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { dka[i] = f32x16{}; dva[i] = f32x16{}; }
+
+  const int kf = swzf(l32) ^ hl;
+  const int vrow = 4 * hl + ((lane & 15) >> 2);
+  const int vf0 = swzf(vrow), vf1 = swzf(vrow + 8);
+  const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int vcb = vcol >> 3;
+
+  // visits
+  int t_begin, t_end;
+  if (kind == G_SEP) {
+    t_begin = first_gathering_tile(p, idx * BK);
+    t_end = p.n_tiles;
+  } else {
+    t_begin = max(0, key0 - (p.kind == SA_MASK_SEGMENT ? p.P : 0)) / TQ;
+    t_end = p.n_tiles;
+  }
+  const bool q_raw = kind == G_CAP;
+  const void* qsrc = q_raw ? p.qraw : p.q;
+  const int64_t qB = q_raw ? p.qrB : p.qsB, qH = q_raw ? p.qrH : p.qsH, qT = q_raw ? p.qrT : p.qsT;
+
+  for (int t = t_begin; t < t_end; ++t) {
+    int mk = MK_NONE;
+    int count = 0;
+    if (kind == G_SEP) {
+      mk = MK_COUNT;
+      count = ld_uniform(p.sep_count + t) - idx * BK;
+    } else {
+      const int it = find_item(p, t, idx);
+      if (it < 0) {
+        if (kind == G_DENSE) break;  // the tiles reading a dense block are consecutive
+        continue;
+      }
+      const int fl = it >> 24;
+      if (kind == G_CAP) {
+        if (!(fl & SA_ITEM_CAPPED)) continue;
+        mk = MK_LCAP;
+      } else if (p.use_cap && (fl & SA_ITEM_CAPPED)) {
+        mk = MK_LNORM;
+      } else if (fl & SA_ITEM_FULL) {
+        mk = MK_NONE;
+      } else if (p.kind == SA_MASK_SEPLLM) {
+        mk = MK_SEPLLM;
+      } else if (p.kind == SA_MASK_LAMBDA) {
+        mk = MK_LALL;
+      } else {
+        mk = MK_SEG;
+      }
+    }
+    const int count_ok = kslot < count;
+    for (int gq = 0; gq < p.group; ++gq) {
+      const int hq = kvh * p.group + gq;
+      const float m2 = ALIBI ? alibi_slope_log2(p, hq) : 0.f;
+      const int64_t rowh = ((int64_t)b * p.h_q + hq) * p.n_q;
+      for (int ch = 0; ch < 2; ++ch) {
+        const int qc0 = t * TQ + 64 * ch;
+        if (qc0 >= p.n_q) break;
+        const int qvalid = min(64, p.n_q - qc0);
+        {
+          Stage4 sq, sd;
+          stage_load(sq, static_cast<const char*>(qsrc) + (b * qB + hq * qH + (int64_t)qc0 * qT) * 2, qT * 2,
+                     qvalid, tid);
+          stage_load(sd, static_cast<const char*>(p.dout) + (b * p.dsB + hq * p.dsH + (int64_t)qc0 * p.dsT) * 2,
+                     p.dsT * 2, qvalid, tid);
+          __syncthreads();  // the previous chunk's reads are done
+          stage_store(sq, Qc, tid);
+          stage_store(sd, Dc, tid);
+          __syncthreads();
+        }
+        // per-row lse2 and D of this lane's 16 query rows
+        const int i0 = qc0 + 32 * qw + 4 * hl;
+        float lr[16], dr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = min(i0 + 8 * (r >> 2) + (r & 3), p.n_q - 1);
+          lr[r] = p.lse[rowh + i] * LOG2E;
+          dr[r] = p.Dv[rowh + i];
+        }
+        // S = Q K^T, dP = dO V^T (queries as rows, this wave's 32 keys as columns)
+        f32x16 s = f32x16{}, dp = f32x16{};
+        {
+          const char* ql = Qc + (32 * qw + l32) * 256;
+          const char* dl = Dc + (32 * qw + l32) * 256;
+          const char* kl = Kg + kslot * 256;
+          const char* vl = Vg + kslot * 256;
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            const int off = ((2 * ks) ^ kf) << 4;
+            const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ql + off));
+            const bf16x8 da = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dl + off));
+            const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + off));
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vl + off));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, s, 0, 0, 0);
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, dp, 0, 0, 0);
+          }
+        }
+        switch (mk) {
+          case MK_NONE: mask_keys<MK_NONE>(p, i0, j, jsep, count_ok, s); break;
+          case MK_COUNT: mask_keys<MK_COUNT>(p, i0, j, jsep, count_ok, s); break;
+          case MK_SEPLLM: mask_keys<MK_SEPLLM>(p, i0, j, jsep, count_ok, s); break;
+          case MK_LALL: mask_keys<MK_LALL>(p, i0, j, jsep, count_ok, s); break;
+          case MK_LNORM: mask_keys<MK_LNORM>(p, i0, j, jsep, count_ok, s); break;
+          case MK_LCAP: mask_keys<MK_LCAP>(p, i0, j, jsep, count_ok, s); break;
+          default: mask_keys<MK_SEG>(p, i0, j, jsep, count_ok, s); break;
+        }
+        f32x16 pr, ds;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = s[r];
+          if constexpr (ALIBI) {
+            const int i = i0 + 8 * (r >> 2) + (r & 3);
+            x = fmaf(-m2, fminf((float)(i - j), (float)p.L), x);
+          }
+          const float e = __builtin_amdgcn_exp2f(x - lr[r]);
+          pr[r] = e;
+          ds[r] = e * (dp[r] - dr[r]);
+        }
+        bf16x8 pb[2], db[2];
+        pack_tile(pr, pb);
+        pack_tile(ds, db);
+        // dV^T += dO^T P, dK^T += Q^T dS (transpose reads of the chunk rows 32 qw ..)
+        {
+          const char* dt = Dc + (32 * qw + vrow) * 256 + ((vcol & 7) << 1);
+          const char* qt = Qc + (32 * qw + vrow) * 256 + ((vcol & 7) << 1);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const int ks = i >> 2, dm = i & 3;
+            const int o0 = (16 * ks) * 256 + (((4 * dm + vcb) ^ vf0) << 4);
+            const int o1 = (16 * ks + 8) * 256 + (((4 * dm + vcb) ^ vf1) << 4);
+            const bf16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(dt + o0));
+            const bf16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(dt + o1));
+            const bf16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qt + o0));
+            const bf16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qt + o1));
+            dva[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                             pb[ks], dva[dm], 0, 0, 0);
+            dka[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                             db[ks], dka[dm], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  // waves qw = 1 hand their partial sums to waves qw = 0 through LDS, which
+  // add them and store the group's rows
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem) + kw * (2 * 4 * 16 * 64);
+  if (qw == 1) {
+#pragma unroll
+    for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        red[(dm * 16 + r) * 64 + lane] = dka[dm][r];
+        red[(64 + dm * 16 + r) * 64 + lane] = dva[dm][r];
+      }
+  }
+  __syncthreads();
+  if (qw == 0 && kslot < valid) {
+    float* krow = dk_out + (int64_t)kslot * D128;
+    float* vrow_o = dv_out + (int64_t)kslot * D128;
+#pragma unroll
+    for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dm + 8 * g + 4 * hl;
+        float4 kx, vx;
+        kx.x = dka[dm][4 * g] + red[(dm * 16 + 4 * g) * 64 + lane];
+        kx.y = dka[dm][4 * g + 1] + red[(dm * 16 + 4 * g + 1) * 64 + lane];
+        kx.z = dka[dm][4 * g + 2] + red[(dm * 16 + 4 * g + 2) * 64 + lane];
+        kx.w = dka[dm][4 * g + 3] + red[(dm * 16 + 4 * g + 3) * 64 + lane];
+        *reinterpret_cast<float4*>(krow + d0) = kx;
+        {
+          vx.x = dva[dm][4 * g] + red[(64 + dm * 16 + 4 * g) * 64 + lane];
+          vx.y = dva[dm][4 * g + 1] + red[(64 + dm * 16 + 4 * g + 1) * 64 + lane];
+          vx.z = dva[dm][4 * g + 2] + red[(64 + dm * 16 + 4 * g + 2) * 64 + lane];
+          vx.w = dva[dm][4 * g + 3] + red[(64 + dm * 16 + 4 * g + 3) * 64 + lane];
+          *reinterpret_cast<float4*>(vrow_o + d0) = vx;
+        }
+      }
+  }
+}
+
+// ===========================================================================
+// Finish: per row, the inverse rotation of the rotated-frame sums, the
+// separator and capped contributions, the output dtype.
+//   dq_i = R(-pos_q(i)) dq_acc_i + dq_cap_i
+//   dk_j = R(-j) ln2 (dk_acc_j + dksep_rank(j)) + scale R(L) dkcap_j
+//   dv_j = dv_acc_j + dvsep_rank(j) + dvcap_j
+// Thread = (row, 8 rotation pairs), as in the RoPE stage.
+// ===========================================================================
+
+struct FinishArgs {
+  int which;             // 0: dq, 1: dk, 2: dv
+  const float* acc;      // [B, h, n, d]
+  const float* sep;      // [B, h, sep_rows, d] or null
+  int64_t sep_rows;
+  const float* cap;      // dq: [B, h, n, d]; dk, dv: [B, h, cap_rows, d]; or null
+  int64_t cap_rows;
+  int n_cap;
+  char* out;
+  int64_t osB, osH, osT;
+  int B, h, n, d, esz;
+  int rotate, pos0, L;
+  float acc_scale, cap_scale;
+  const unsigned long long* sep_bits;
+  const int* blk_sep;
+  int g0;
+  ThetaTable theta;
+};
+
+__device__ inline void angle_sc(double pos, double th, float* c, float* s) {
+  const double TWO_PI_HI = 6.283185307179586232;
+  const double TWO_PI_LO = 2.4492935982947064e-16;
+  const double INV_TWO_PI = 0.15915494309189535;
+  const double ang = pos * th;
+  const double kq = rint(ang * INV_TWO_PI);
+  double r = fma(-kq, TWO_PI_HI, ang);
+  r = fma(-kq, TWO_PI_LO, r);
+  sincosf((float)r, s, c);
+}
+
+__device__ inline unsigned short to_bf16(float f) {  // round to nearest even (finite inputs)
+  const unsigned u = __float_as_uint(f);
+  return (unsigned short)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__global__ __launch_bounds__(256) void bwd_finish(FinishArgs p) {
+  const int tpr = p.d / 16;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = gid / tpr;
+  if (row >= (int64_t)p.B * p.h * p.n) return;
+  const int c0 = (int)(gid % tpr) * 8;
+  const int half = p.d / 2;
+  const int i = (int)(row % p.n);
+  const int64_t bh = row / p.n;
+  const int h = (int)(bh % p.h), b = (int)(bh / p.h);
+  const float* a = p.acc + row * p.d;
+  float x1[8], x2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x1[e] = a[c0 + e];
+    x2[e] = a[c0 + half + e];
+  }
+  if (p.sep != nullptr && i >= p.g0) {
+    const int blk = i / BK, r = i - blk * BK;
+    const unsigned long long word = p.sep_bits[blk];
+    if ((word >> r) & 1ull) {
+      const int64_t rank = p.blk_sep[blk] + __popcll(word & ((r == 0) ? 0ull : (~0ull >> (64 - r))));
+      const float* sr = p.sep + (bh * p.sep_rows + rank) * p.d;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x1[e] += sr[c0 + e];
+        x2[e] += sr[c0 + half + e];
+      }
+    }
+  }
+  float y1[8], y2[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x1[e] *= p.acc_scale;
+    x2[e] *= p.acc_scale;
+  }
+  if (p.rotate) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float c, s;
+      angle_sc(-(double)(p.pos0 + i), p.theta.th[c0 + e], &c, &s);
+      y1[e] = x1[e] * c - x2[e] * s;
+      y2[e] = x2[e] * c + x1[e] * s;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { y1[e] = x1[e]; y2[e] = x2[e]; }
+  }
+  if (p.cap != nullptr) {
+    const float* cr = nullptr;
+    if (p.which == 0) cr = p.cap + row * p.d;
+    else if (i < p.n_cap) cr = p.cap + (bh * p.cap_rows + i) * p.d;
+    if (cr != nullptr) {
+      if (p.which == 1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          float c, s;
+          angle_sc((double)p.L, p.theta.th[c0 + e], &c, &s);
+          const float z1 = cr[c0 + e], z2 = cr[c0 + half + e];
+          y1[e] += p.cap_scale * (z1 * c - z2 * s);
+          y2[e] += p.cap_scale * (z2 * c + z1 * s);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          y1[e] += p.cap_scale * cr[c0 + e];
+          y2[e] += p.cap_scale * cr[c0 + half + e];
+        }
+      }
+    }
+  }
+  char* o = p.out + (b * p.osB + h * p.osH + (int64_t)i * p.osT) * p.esz;
+  if (p.esz == 2) {
+    unsigned short* o16 = reinterpret_cast<unsigned short*>(o);
+    uint4 w1, w2;
+    w1.x = to_bf16(y1[0]) | ((unsigned)to_bf16(y1[1]) << 16);
+    w1.y = to_bf16(y1[2]) | ((unsigned)to_bf16(y1[3]) << 16);
+    w1.z = to_bf16(y1[4]) | ((unsigned)to_bf16(y1[5]) << 16);
+    w1.w = to_bf16(y1[6]) | ((unsigned)to_bf16(y1[7]) << 16);
+    w2.x = to_bf16(y2[0]) | ((unsigned)to_bf16(y2[1]) << 16);
+    w2.y = to_bf16(y2[2]) | ((unsigned)to_bf16(y2[3]) << 16);
+    w2.z = to_bf16(y2[4]) | ((unsigned)to_bf16(y2[5]) << 16);
+    w2.w = to_bf16(y2[6]) | ((unsigned)to_bf16(y2[7]) << 16);
+    *reinterpret_cast<uint4*>(o16 + c0) = w1;
+    *reinterpret_cast<uint4*>(o16 + c0 + half) = w2;
+  } else {
+    float* of = reinterpret_cast<float*>(o);
+    *reinterpret_cast<float4*>(of + c0) = make_float4(y1[0], y1[1], y1[2], y1[3]);
+    *reinterpret_cast<float4*>(of + c0 + 4) = make_float4(y1[4], y1[5], y1[6], y1[7]);
+    *reinterpret_cast<float4*>(of + c0 + half) = make_float4(y2[0], y2[1], y2[2], y2[3]);
+    *reinterpret_cast<float4*>(of + c0 + half + 4) = make_float4(y2[4], y2[5], y2[6], y2[7]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const void* plan,
+                      const sa_fwd_args_t& a, const sa_bwd_args_t& g, const RopeOut& ro,
+                      const BwdWs& w, const ThetaTable& theta, hipStream_t s) {
+  const char* pb = static_cast<const char*>(plan);
+  const bool rope = a.rope == SA_ROPE_HALF;
+  const bool alibi = a.rope == SA_ALIBI;
+  const int64_t rows_q = (int64_t)a.batch * a.h_q * m.n_q;
+  // 1. D = rowsum(dO * O)
+  {
+    RowDotArgs r;
+    r.dout = static_cast<const char*>(g.dout);
+    r.dsB = g.dout_stride[0]; r.dsH = g.dout_stride[1]; r.dsT = g.dout_stride[2];
+    r.o = static_cast<const char*>(a.o);
+    r.osB = a.o_stride[0]; r.osH = a.o_stride[1]; r.osT = a.o_stride[2];
+    r.D = w.D;
+    r.B = a.batch; r.h = a.h_q; r.n = m.n_q; r.d = a.d; r.esz = 2;
+    hipLaunchKernelGGL(bwd_rowdot, dim3((unsigned)ceil_div(rows_q, 256)), dim3(256), 0, s, r);
+  }
+  BwdArgs p;
+  memset(&p, 0, sizeof(p));
+  p.q = ro.qrot;
+  p.qsT = a.d; p.qsH = (int64_t)m.n_q * a.d; p.qsB = p.qsH * a.h_q;
+  p.qraw = a.q;
+  p.qrB = a.q_stride[0]; p.qrH = a.q_stride[1]; p.qrT = a.q_stride[2];
+  if (rope) {
+    p.k = ro.krot;
+    p.ksT = a.d; p.ksH = (int64_t)m.n_k * a.d; p.ksB = p.ksH * a.h_kv;
+  } else {
+    p.k = a.k;
+    p.ksB = a.k_stride[0]; p.ksH = a.k_stride[1]; p.ksT = a.k_stride[2];
+  }
+  p.v = a.v;
+  p.vsB = a.v_stride[0]; p.vsH = a.v_stride[1]; p.vsT = a.v_stride[2];
+  p.ksep = ro.ksep; p.vsep = ro.vsep; p.sep_rows = ro.sep_rows;
+  p.kcap = ro.kcap; p.cap_rows = ro.cap_rows;
+  p.dout = g.dout;
+  p.dsB = g.dout_stride[0]; p.dsH = g.dout_stride[1]; p.dsT = g.dout_stride[2];
+  p.lse = a.lse;
+  p.Dv = w.D;
+  p.dq_acc = w.dq_acc; p.dq_cap = w.dq_cap;
+  p.dk_acc = w.dk_acc; p.dv_acc = w.dv_acc;
+  p.dksep = w.dksep; p.dvsep = w.dvsep;
+  p.dkcap = w.dkcap; p.dvcap = w.dvcap;
+  p.tile_ptr = reinterpret_cast<const int*>(pb + lay.off_tile_ptr);
+  p.items = reinterpret_cast<const int*>(pb + lay.off_items);
+  p.sep_count = reinterpret_cast<const int*>(pb + lay.off_sep_count);
+  p.sep_bits = reinterpret_cast<const unsigned long long*>(pb + lay.off_sep_bits);
+  p.n_sep = reinterpret_cast<const int*>(pb + offsetof(sa_plan_header_t, n_sep));
+  p.kind = m.kind; p.B = a.batch; p.h_q = a.h_q; p.h_kv = a.h_kv;
+  p.n_q = m.n_q; p.n_k = m.n_k; p.n_tiles = lay.n_tiles; p.n_blocks = lay.n_blocks;
+  p.group = a.h_q / a.h_kv;
+  p.a = m.a; p.w = m.w; p.n_s = m.n_starting; p.L = m.L_pretrain; p.P = m.prefix_len;
+  p.n_cap = ro.n_cap;
+  p.use_cap = (m.kind == SA_MASK_LAMBDA && rope && ro.n_cap > 0) ? 1 : 0;
+  p.gather = (m.kind == SA_MASK_SEPLLM && m.sep != nullptr) ? 1 : 0;
+  p.scale = a.scale;
+  p.alibi = alibi ? 1 : 0;
+  p.alibi_e = alibi ? a.rope_base : 0.f;
+  p.n_sep_chunks = p.gather ? (int)(ro.sep_rows / BK) : 0;
+  p.n_cap_blocks = p.use_cap ? (int)ceil_div(ro.n_cap, BK) : 0;
+  // 2. dQ (query-major)
+  {
+    const unsigned grid = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
+    if (alibi) hipLaunchKernelGGL(bwd_dq_bf16<true>, dim3(grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(bwd_dq_bf16<false>, dim3(grid), dim3(256), 0, s, p);
+  }
+  // 3. dK, dV (key-major): separator chunks, then capped blocks, then dense blocks
+  {
+    const int64_t groups = (int64_t)p.n_sep_chunks + p.n_cap_blocks + lay.n_blocks;
+    const unsigned grid = (unsigned)(groups * a.batch * a.h_kv);
+    if (alibi) hipLaunchKernelGGL(bwd_dkdv_bf16<true>, dim3(grid), dim3(256), 0, s, p);
+    else hipLaunchKernelGGL(bwd_dkdv_bf16<false>, dim3(grid), dim3(256), 0, s, p);
+  }
+  // 4. finish: dq, dk, dv
+  for (int which = 0; which < 3; ++which) {
+    FinishArgs f;
+    memset(&f, 0, sizeof(f));
+    f.which = which;
+    f.d = a.d;
+    f.esz = 2;
+    f.L = m.L_pretrain;
+    f.theta = theta;
+    f.sep_bits = p.sep_bits;
+    f.blk_sep = reinterpret_cast<const int*>(pb + lay.off_blk_sep);
+    f.g0 = lay.g0;
+    f.B = a.batch;
+    if (which == 0) {
+      f.acc = w.dq_acc;
+      f.cap = p.use_cap ? w.dq_cap : nullptr;
+      f.h = a.h_q; f.n = m.n_q;
+      f.out = static_cast<char*>(g.dq);
+      f.osB = g.dq_stride[0]; f.osH = g.dq_stride[1]; f.osT = g.dq_stride[2];
+      f.rotate = rope;
+      f.pos0 = m.kind == SA_MASK_SEGMENT ? m.prefix_len : 0;
+      f.acc_scale = 1.f;
+      f.cap_scale = 1.f;
+      f.g0 = 0x7fffffff;  // no separator rows on the query side
+    } else {
+      f.acc = which == 1 ? w.dk_acc : w.dv_acc;
+      f.sep = p.gather ? (which == 1 ? w.dksep : w.dvsep) : nullptr;
+      f.sep_rows = ro.sep_rows;
+      f.cap = p.use_cap ? (which == 1 ? w.dkcap : w.dvcap) : nullptr;
+      f.cap_rows = ro.cap_rows;
+      f.n_cap = ro.n_cap;
+      f.h = a.h_kv; f.n = m.n_k;
+      char* dst = static_cast<char*>(which == 1 ? g.dk : g.dv);
+      const int64_t* st = which == 1 ? g.dk_stride : g.dv_stride;
+      f.out = dst;
+      f.osB = st[0]; f.osH = st[1]; f.osT = st[2];
+      f.rotate = which == 1 && rope;
+      f.pos0 = 0;
+      f.acc_scale = which == 1 ? LN2 : 1.f;
+      f.cap_scale = which == 1 ? a.scale : 1.f;
+    }
+    const int64_t threads = (int64_t)f.B * f.h * f.n * (a.d / 16);
+    hipLaunchKernelGGL(bwd_finish, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s, f);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

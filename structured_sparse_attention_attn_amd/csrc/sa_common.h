@@ -107,4 +107,21 @@ struct CarryDesc {
 
 hipError_t launch_carry(const CarryDesc& c, hipStream_t s);
 
+// Backward workspace sections (fp32), see sparse_attn_bwd.
+struct BwdWs {
+  float* D;        // [B, h_q, n_q]
+  float* dq_acc;   // [B, h_q, n_q, d]
+  float* dq_cap;   // [B, h_q, n_q, d] or null
+  float* dk_acc;   // [B, h_kv, n_k, d]
+  float* dv_acc;
+  float* dksep;    // [B, h_kv, sep_rows, d] or null
+  float* dvsep;
+  float* dkcap;    // [B, h_kv, cap_rows, d] or null
+  float* dvcap;
+};
+
+hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const void* plan,
+                      const sa_fwd_args_t& a, const sa_bwd_args_t& g, const RopeOut& ro,
+                      const BwdWs& w, const ThetaTable& theta, hipStream_t s);
+
 }  // namespace sa

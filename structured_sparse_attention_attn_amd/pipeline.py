@@ -9,9 +9,10 @@ from typing import Optional
 
 import torch
 
-from . import (SA_MASK_LAMBDA, SA_MASK_SEGMENT, SA_MASK_SEPLLM, fwd_args, mask,
-               sa_fwd_workspace_bytes, sa_plan_bytes, sa_topk_workspace_bytes,
-               sparse_attn_fwd, sparse_attn_plan, sparse_attn_segment_carry, topk_retrieve)
+from . import (SA_MASK_LAMBDA, SA_MASK_SEGMENT, SA_MASK_SEPLLM, bwd_args, fwd_args, mask,
+               sa_bwd_workspace_bytes, sa_fwd_workspace_bytes, sa_plan_bytes,
+               sa_topk_workspace_bytes, sparse_attn_bwd, sparse_attn_fwd, sparse_attn_plan,
+               sparse_attn_segment_carry, topk_retrieve)
 
 KINDS = {"sepllm": SA_MASK_SEPLLM, "lambda": SA_MASK_LAMBDA, "segment": SA_MASK_SEGMENT}
 
@@ -27,6 +28,7 @@ class SparseAttention:
                          L_pretrain=L_pretrain, prefix_len=prefix_len)
         self.plan = torch.empty(sa_plan_bytes(self.mask), dtype=torch.uint8, device=device)
         self.ws: Optional[torch.Tensor] = None
+        self.bws: Optional[torch.Tensor] = None
         self.device = device
 
     def build_plan(self) -> None:
@@ -50,6 +52,19 @@ class SparseAttention:
         self.ensure_workspace(args)
         sparse_attn_fwd(self.mask, self.plan, args, self.ws)
         return o
+
+    def backward(self, q, k, v, o, lse, dout, rope_base=None, scale=None, alibi_exp=None,
+                 dq=None, dk=None, dv=None):
+        """Gradients (dq, dk, dv) of the forward that wrote o and lse."""
+        dq = torch.empty_like(q) if dq is None else dq
+        dk = torch.empty_like(k) if dk is None else dk
+        dv = torch.empty_like(v) if dv is None else dv
+        args = self.args(q, k, v, o, lse, rope_base, scale, alibi_exp)
+        need = sa_bwd_workspace_bytes(self.mask, args)
+        if self.bws is None or self.bws.numel() < need:
+            self.bws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        sparse_attn_bwd(self.mask, self.plan, args, bwd_args(dout, dq, dk, dv), self.bws)
+        return dq, dk, dv
 
 
 class TopK:

@@ -417,3 +417,64 @@ def test_segment_runner_vs_oracle(sa, dtype, S, M, N):
     assert torch.equal(nk[0, :nl, M - keep:M].cpu(), k_loc[:, N * S - keep:])
     assert torch.equal(nv[0, :nl, M - keep:M].cpu(), v_loc[:, N * S - keep:])
     np.testing.assert_array_equal(to64(nk[0, :nl, M - keep:M]), state["tail_k"])
+
+
+# Backward (dQ, dK, dV) against the oracle's gradient formulas.
+BWD_SMALL = [
+    (W.SEPLLM, dict(m=700, a=4, w=64, p_sep=0.1), 10000.0, None),
+    (W.SEPLLM, dict(m=500, a=70, w=100, p_sep=0.2, h_q=4, h_kv=2, batch=2), 10000.0, None),
+    (W.SEPLLM, dict(m=300, a=0, w=1, p_sep=0.3), None, None),
+    (W.LAMBDA, dict(m=900, n_s=10, L=300), 10000.0, None),
+    (W.LAMBDA, dict(m=600, n_s=100, L=64, h_q=4, h_kv=1), 10000.0, None),
+    (W.LAMBDA, dict(m=300, n_s=10, L=0), 10000.0, None),
+    (W.LAMBDA, dict(m=700, n_s=10, L=100), None, 8.0),
+    (W.SEGMENT, dict(m=600, P=200), 10000.0, None),
+    (W.SEGMENT, dict(m=129, P=1, h_q=4, h_kv=2), 10000.0, None),
+    (W.SEPLLM, dict(m=1, a=4, w=64, p_sep=0.5), 10000.0, None),
+]
+
+
+def _bwd_stats(got, ref):
+    err = np.abs(got - ref)
+    return float(err.max()), float(err.mean()), float(np.abs(ref).max()), float(np.abs(ref).mean())
+
+
+def bwd_compare(name, got, ref):
+    """Gradient bar, relative to the gradient's own size (gradients have no fixed scale).
+
+    The outputs are bf16 (rounding alone: relative 2^-9 per element); P, dS and the
+    rotated q, k enter the products as bf16 (relative 2^-9 each) and P carries the
+    forward's logit error (a few 1e-3), so elements sit within a few 2^-9 of the
+    reference relative to the terms they sum.  Bar: max-abs <= 1e-2 * max|ref| and
+    mean-abs <= 1e-2 * mean|ref| (floor 1e-3 for vanishing references).
+    """
+    mx, mean, rmx, rmean = _bwd_stats(got, ref)
+    log(f"  {name}: max-abs {mx:.3e} mean-abs {mean:.3e} | ref max {rmx:.3e} mean {rmean:.3e}")
+    assert np.isfinite(got).all(), name
+    assert mx <= 1e-2 * max(rmx, 0.1), (name, mx, rmx)
+    assert mean <= 1e-2 * max(rmean, 0.1), (name, mean, rmean)
+
+
+@pytest.mark.parametrize("case", range(len(BWD_SMALL)))
+def test_bwd_small(sa, case):
+    mode, kw, rope, alibi = BWD_SMALL[case]
+    wl = W.small(mode, seed=500 + case, rope_base=rope, alibi_exp=alibi, **kw)
+    log(f"bwd small {case}: {mode} {kw} rope={rope} alibi={alibi}")
+    inp = W.make_small_inputs(wl)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    sep = inp.get("sep")
+    sa_obj = device_mask(wl, None if sep is None else sep.cuda())
+    sa_obj.build_plan()
+    lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
+    o = sa_obj.forward(q, k, v, lse=lse, rope_base=wl.rope_base, scale=wl.scale, alibi_exp=wl.alibi_exp)
+    dout = W.make_grad(tuple(q.shape), seed=900 + case).cuda()
+    dq, dk, dv = sa_obj.backward(q, k, v, o, lse, dout, rope_base=wl.rope_base, scale=wl.scale,
+                                 alibi_exp=wl.alibi_exp)
+    torch.cuda.synchronize()
+    spec = spec_of(wl, None if sep is None else sep.numpy())
+    for b in range(wl.batch):
+        rq, rk, rv = O.attention_backward(to64(inp["q"][b]), to64(inp["k"][b]), to64(inp["v"][b]),
+                                          to64(dout[b]), spec, wl.rope_base, wl.scale,
+                                          alibi_exp=wl.alibi_exp)
+        for name, got, ref in (("dq", dq[b], rq), ("dk", dk[b], rk), ("dv", dv[b], rv)):
+            bwd_compare(f"b{b} {name}", to64(got), ref)

@@ -137,6 +137,12 @@ def make_small_inputs(wl: Workload) -> Dict[str, torch.Tensor]:
     return out
 
 
+def make_grad(shape, seed: int, dtype=torch.bfloat16) -> torch.Tensor:
+    """An upstream gradient dO: fp32 torch.randn from its own seed, rounded to dtype."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    return _randn(shape, g).to(dtype)
+
+
 def make_segment_stream(n_heads: int, seg_len: int, d: int, n_segments: int, seed: int,
                         dtype=torch.bfloat16):
     """Raw q, k, v [1, n_heads, seg_len, d] for each of n_segments segments (drawn in that order)."""
