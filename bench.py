@@ -141,6 +141,29 @@ def multi_segment(wl, inp, n_seg, torch):
             "note": "forward + tail carry + pool append + top-k retrieval per segment"}
 
 
+def backward_timing(sa_mod, sa, q, k, v, o, lse, wl, steps, torch):
+    """The backward (sparse_attn_bwd: RoPE stage, row sums, dQ, dK/dV, finish) on the
+    forward's outputs, timed with HIP events on the launch stream."""
+    from structured_sparse_attention_attn_amd import bwd_args, sparse_attn_bwd
+    import workloads as W
+    dout = W.make_grad(tuple(q.shape), seed=wl.seed + 11).to("cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fa = sa.args(q, k, v, o, lse, wl.rope_base, wl.scale, wl.alibi_exp)
+    ga = bwd_args(dout, dq, dk, dv)
+    need = sa_mod.sa_bwd_workspace_bytes(sa.mask, fa)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    sparse_attn_bwd(sa.mask, sa.plan, fa, ga, ws)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        sparse_attn_bwd(sa.mask, sa.plan, fa, ga, ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, need
+
+
 def source_sha(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -209,6 +232,8 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--no-gemm-ceiling", action="store_true",
                     help="skip the dense bf16 GEMM reference measurement")
+    ap.add_argument("--backward", type=int, default=0,
+                    help="also time the backward over this many steps (0: skip)")
     ap.add_argument("--segments", type=int, default=8,
                     help="segment workload: also run this many consecutive segments (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -351,6 +376,14 @@ def main():
         "stages_roofline": stage_roofline,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
+    if args.backward > 0 and wl.dtype == "bf16":
+        import structured_sparse_attention_attn_amd as sa_mod
+        bms, bws = backward_timing(sa_mod, sa, q, k, v, o, lse, wl, args.backward, torch)
+        bflops = 2.5 * flops  # five products per visible pair (S, dP, dV, dQ, dK) against two
+        out["backward"] = {"ms": round(bms, 4), "effective_tflops": round(bflops / (bms * 1e-3) / 1e12, 2),
+                           "frac": round(bflops / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                           "workspace_bytes": bws,
+                           "note": "2.5x the forward's effective flops (5 products per pair vs 2)"}
     if wl.mode == "segment" and args.segments > 0:
         out["multi_segment"] = multi_segment(wl, inp, args.segments, torch)
     if not args.no_gemm_ceiling:

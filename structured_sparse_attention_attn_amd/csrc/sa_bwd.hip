@@ -77,7 +77,8 @@ struct BwdArgs {
 };
 
 // ---------------------------------------------------------------------------
-// D_i = <dO_i, O_i>: one thread per row, 16-byte pieces.
+// D_i = <dO_i, O_i>: 16 consecutive lanes per row, one 16-byte piece each,
+// then a butterfly sum over the 16 lanes.
 // ---------------------------------------------------------------------------
 
 struct RowDotArgs {
@@ -93,62 +94,44 @@ __device__ inline float bf_lo(unsigned x) { return __uint_as_float(x << 16); }
 __device__ inline float bf_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
 __global__ __launch_bounds__(256) void bwd_rowdot(RowDotArgs p) {
-  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int pieces = p.d * p.esz / 16;  // 16 for bf16 d = 128
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t row = g / pieces;
+  const int pc = (int)(g % pieces);
   const int64_t rows = (int64_t)p.B * p.h * p.n;
-  if (row >= rows) return;
-  const int i = (int)(row % p.n);
-  const int64_t bh = row / p.n;
-  const int h = (int)(bh % p.h), b = (int)(bh / p.h);
-  const char* a = p.dout + (b * p.dsB + h * p.dsH + (int64_t)i * p.dsT) * p.esz;
-  const char* c = p.o + (b * p.osB + h * p.osH + (int64_t)i * p.osT) * p.esz;
   float acc = 0.f;
-  const int bytes = p.d * p.esz;
-  for (int off = 0; off < bytes; off += 16) {
-    const uint4 x = *reinterpret_cast<const uint4*>(a + off);
-    const uint4 y = *reinterpret_cast<const uint4*>(c + off);
-    if (p.esz == 2) {
-      const unsigned xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+  if (row < rows) {
+    const int i = (int)(row % p.n);
+    const int64_t bh = row / p.n;
+    const int h = (int)(bh % p.h), b = (int)(bh / p.h);
+    const uint4 x = *reinterpret_cast<const uint4*>(p.dout + (b * p.dsB + h * p.dsH + (int64_t)i * p.dsT) * p.esz + pc * 16);
+    const uint4 y = *reinterpret_cast<const uint4*>(p.o + (b * p.osB + h * p.osH + (int64_t)i * p.osT) * p.esz + pc * 16);
+    const unsigned xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        acc = fmaf(bf_lo(xs[e]), bf_lo(ys[e]), acc);
-        acc = fmaf(bf_hi(xs[e]), bf_hi(ys[e]), acc);
-      }
-    } else {
-      acc = fmaf(__uint_as_float(x.x), __uint_as_float(y.x), acc);
-      acc = fmaf(__uint_as_float(x.y), __uint_as_float(y.y), acc);
-      acc = fmaf(__uint_as_float(x.z), __uint_as_float(y.z), acc);
-      acc = fmaf(__uint_as_float(x.w), __uint_as_float(y.w), acc);
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(bf_lo(xs[e]), bf_lo(ys[e]), acc);
+      acc = fmaf(bf_hi(xs[e]), bf_hi(ys[e]), acc);
     }
   }
-  p.D[row] = acc;
+  for (int m = 1; m < pieces; m <<= 1) acc += __shfl_xor(acc, m, 16);
+  if (row < rows && pc == 0) p.D[row] = acc;
 }
 
-// ---------------------------------------------------------------------------
-// LDS staging through registers: a 64-row x 256-byte block, rows swizzled as
-// in the forward (16-byte chunk c of row r at chunk c ^ swzf(r & 15)).  Rows
-// at or past `valid` repeat row valid-1 (finite values, masked later).
-// ---------------------------------------------------------------------------
-
-struct Stage4 {
-  uint4 x[4];
-};
-
-__device__ inline void stage_load(Stage4& st, const char* base, int64_t stride, int valid, int tid) {
+// Direct global -> LDS loads of a 64-row x 256-byte block into the swizzled
+// layout (16-byte chunk c of row r at chunk c ^ swzf(r & 15)): wave w moves
+// rows 16w .. 16w+15, four rows per instruction, each lane fetching the
+// logical chunk that lands in its slot.  Rows at or past `valid` repeat row
+// valid-1 (finite values, masked later).
+__device__ __attribute__((always_inline)) inline void dma_block(const char* base, int64_t stride, int valid,
+                                                                char* lds, int wid, int lane) {
+  const int lrow = lane >> 4;
+  const int lchunk = (lane & 15) ^ (lrow << 2);
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int piece = tid + 256 * e;  // 1024 pieces of 16 bytes
-    const int r = piece >> 4, c = piece & 15;
-    const int rr = min(r, valid - 1);
-    st.x[e] = *reinterpret_cast<const uint4*>(base + (int64_t)rr * stride + c * 16);
-  }
-}
-
-__device__ inline void stage_store(const Stage4& st, char* lds, int tid) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int piece = tid + 256 * e;
-    const int r = piece >> 4, c = piece & 15;
-    *reinterpret_cast<uint4*>(lds + r * 256 + ((c ^ swzf(r & 15)) << 4)) = st.x[e];
+  for (int j = 0; j < 4; ++j) {
+    const int i = wid * 4 + j;
+    const int r = min(4 * i + lrow, valid - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)r * stride + ((lchunk ^ j) << 4)),
+                                     (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0, 0);
   }
 }
 
@@ -174,9 +157,12 @@ __device__ inline void pack_tile(const f32x16& s, bf16x8 (&pb)[2]) {
 
 template <bool ALIBI>
 __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * BLK_BYTES];  // [K | V] of the unit
-  char* const Ks = smem;
-  char* const Vs = smem + BLK_BYTES;
+  // K and V of the current unit and of the next one (separate arrays, so a
+  // read of one slot never waits for the loads into the other)
+  __shared__ __attribute__((aligned(16))) char K0[BLK_BYTES];
+  __shared__ __attribute__((aligned(16))) char V0[BLK_BYTES];
+  __shared__ __attribute__((aligned(16))) char K1[BLK_BYTES];
+  __shared__ __attribute__((aligned(16))) char V1[BLK_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
@@ -221,14 +207,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
   const int64_t rowi = ((int64_t)b * p.h_q + hq) * p.n_q + (qok ? qi : 0);
   const float lse2 = qok ? p.lse[rowi] * LOG2E : 0.f;
   const float Dq = qok ? p.Dv[rowi] : 0.f;
-  const f32x16 neg_lse = f32x16{} - lse2;
 
   f32x16 acc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
 
-  // Row-fragment reads (K for S, V for dP) and transpose reads (K^T for dQ),
-  // the forward's per-lane addressing.
   const int kf = swzf(l32) ^ hl;
   const int vrow = 4 * hl + ((lane & 15) >> 2);
   const int vf0 = swzf(vrow), vf1 = swzf(vrow + 8);
@@ -248,7 +231,30 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
       }
   };
 
-  for (int u = 0; u < n_units; ++u) {
+  // C = A B over the 8 k-steps of d for the 32-key half mb of an LDS block
+  // (A rows 32 mb + l32), fragments one k-step ahead
+  auto half_product = [&](const char* blk, const bf16x8 (&bop)[8], int mb) __attribute__((always_inline)) {
+    const char* kl = blk + (32 * mb + l32) * 256;
+    auto frag = [&](int ks) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + (((2 * ks) ^ kf) << 4)));
+    };
+    bf16x8 a[2];
+    a[0] = frag(0);
+    f32x16 c = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if (ks + 1 < 8) a[(ks + 1) % 2] = frag(ks + 1);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks % 2], bop[ks], c, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return c;
+  };
+
+  auto step = [&](int u, char* Kc, char* Vc, char* Kn, char* Vn) __attribute__((always_inline)) {
+    // this wave's loads of unit u have landed; the barrier makes every wave's
+    // visible and ends the reads of the slot the next loads overwrite
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
     if (u == tu.n_capu && u > 0) {
       // capped units done: their dq (raw frame) goes to dq_cap, the rest is rotated-frame
       store_acc(p.dq_cap, LN2);
@@ -257,38 +263,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
       load_rows(qf, p.q, p.qsB, p.qsH, p.qsT);
     }
     const Unit cur = unit_at<ALIBI>(p, tu, u);
-    {
-      Stage4 sk, sv;
-      stage_load(sk, cur.kbase, cur.kstride, cur.kvalid, tid);
-      stage_load(sv, cur.vbase, cur.vstride, cur.vvalid, tid);
-      __syncthreads();  // the previous unit's reads are done
-      stage_store(sk, Ks, tid);
-      stage_store(sv, Vs, tid);
-      __syncthreads();
+    if (u + 1 < n_units) {
+      const Unit nx = unit_at<ALIBI>(p, tu, u + 1);
+      dma_block(nx.kbase, nx.kstride, nx.kvalid, Kn, wid, lane);
+      dma_block(nx.vbase, nx.vstride, nx.vvalid, Vn, wid, lane);
     }
-    // --- S^T = K Q^T - lse2 and dP^T = V dO^T ---
-    f32x16 s[2], dp[2];
-    {
-      const char* kl = Ks + l32 * 256;
-      const char* vl = Vs + l32 * 256;
-      f32x16 c0 = neg_lse, c1 = neg_lse, e0 = f32x16{}, e1 = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int off = ((2 * ks) ^ kf) << 4;
-        const bf16x8 k0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + off));
-        const bf16x8 k1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + 32 * 256 + off));
-        const bf16x8 v0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vl + off));
-        const bf16x8 v1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vl + 32 * 256 + off));
-        c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k0, qf[ks], c0, 0, 0, 0);
-        c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(k1, qf[ks], c1, 0, 0, 0);
-        e0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v0, df[ks], e0, 0, 0, 0);
-        e1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v1, df[ks], e1, 0, 0, 0);
-      }
-      s[0] = c0;
-      s[1] = c1;
-      dp[0] = e0;
-      dp[1] = e1;
-    }
+    // S^T = K Q^T - lse2 (base 2), masked, exponentiated
+    f32x16 s[2];
+    s[0] = half_product(Kc, qf, 0);
+    s[1] = half_product(Kc, qf, 1);
     switch (cur.mk) {
       case MK_NONE: break;
       case MK_COUNT: apply_mask<MK_COUNT>(p, cur, qi, hl, s); break;
@@ -299,28 +282,52 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
       default: apply_mask<MK_SEG>(p, cur, qi, hl, s); break;
     }
     if constexpr (ALIBI) add_alibi(cur, qi, hl, m2, Lf, s);
-    // --- dS = P (dP - D), masked pairs exactly 0 ---
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r]) * (dp[mb][r] - Dq);
+      for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r] - lse2);
+    // dP^T = V dO^T; dS = P (dP - D), masked pairs exactly 0
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      const f32x16 dp = half_product(Vc, df, mb);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[mb][r] = s[mb][r] * (dp[r] - Dq);
+    }
     bf16x8 dsb[4];
     pack_p(s, dsb);
-    // --- dQ^T += K^T dS^T ---
-    {
-      const char* tl = Ks + vrow * 256 + ((vcol & 7) << 1);
+    // dQ^T += K^T dS^T, K^T fragments by transpose reads two MFMAs ahead
+    const char* tl = Kc + vrow * 256 + ((vcol & 7) << 1);
+    auto tfrag = [&](int kst, int dm) {
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4*)(tl + (16 * kst) * 256 + (((4 * dm + vcb) ^ vf0) << 4)));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4*)(tl + (16 * kst + 8) * 256 + (((4 * dm + vcb) ^ vf1) << 4)));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 ta[3];
+    ta[0] = tfrag(0, 0);
+    ta[1] = tfrag(0, 1);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kst = i >> 2, dm = i & 3;
-        const char* a0 = tl + (16 * kst) * 256 + (((4 * dm + vcb) ^ vf0) << 4);
-        const char* a1 = tl + (16 * kst + 8) * 256 + (((4 * dm + vcb) ^ vf1) << 4);
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1));
-        acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                         dsb[kst], acc[dm], 0, 0, 0);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int kst = i >> 2, dm = i & 3;
+      if (i + 2 < 16) ta[(i + 2) % 3] = tfrag((i + 2) >> 2, (i + 2) & 3);
+      acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[i % 3], dsb[kst], acc[dm], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  if (n_units > 0) {
+    const Unit u0 = unit_at<ALIBI>(p, tu, 0);
+    dma_block(u0.kbase, u0.kstride, u0.kvalid, K0, wid, lane);
+    dma_block(u0.vbase, u0.vstride, u0.vvalid, V0, wid, lane);
   }
+  int u = 0;
+  for (; u + 1 < n_units; u += 2) {
+    step(u, K0, V0, K1, V1);
+    step(u + 1, K1, V1, K0, V0);
+  }
+  if (u < n_units) step(u, K0, V0, K1, V1);
+
   if (p.use_cap) {
     if (tu.n_capu == n_units && n_units > 0) {
       store_acc(p.dq_cap, LN2);
@@ -401,12 +408,11 @@ __device__ inline int find_item(const BwdArgs& p, int t, int blk) {
 
 template <bool ALIBI>
 __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
-  // [K group | V group | Q chunk | dO chunk], 64 rows x 256 bytes each
-  __shared__ __attribute__((aligned(16))) char smem[4 * BLK_BYTES];
-  char* const Kg = smem;
-  char* const Vg = smem + BLK_BYTES;
-  char* const Qc = smem + 2 * BLK_BYTES;
-  char* const Dc = smem + 3 * BLK_BYTES;
+  __shared__ __attribute__((aligned(16))) char Kg[BLK_BYTES];  // the group's keys
+  __shared__ __attribute__((aligned(16))) char Vg[BLK_BYTES];  // and values
+  __shared__ __attribute__((aligned(16))) char Qc[BLK_BYTES];  // 64 queries of a tile
+  __shared__ __attribute__((aligned(16))) char Dc[BLK_BYTES];  // their dO rows
+  __shared__ __attribute__((aligned(16))) float LD[2][64];     // their lse * log2(e) and D
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
@@ -428,28 +434,27 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
   int valid;
   float* dk_out;
   float* dv_out;
-  int key0 = 0;        // key index of row 0 (dense and capped groups)
-  int n_sep_all = 0;
+  int key0 = 0;  // key index of row 0 (dense and capped groups)
   if (kind == G_SEP) {
-    n_sep_all = ld_uniform(p.n_sep);
+    const int n_sep_all = ld_uniform(p.n_sep);
     if (idx * BK >= n_sep_all) return;
-    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.sep_rows;
-    kbase = static_cast<const char*>(p.ksep) + (ho + (int64_t)idx * BK) * (D128 * 2);
-    vbase = static_cast<const char*>(p.vsep) + (ho + (int64_t)idx * BK) * (D128 * 2);
+    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.sep_rows + (int64_t)idx * BK;
+    kbase = static_cast<const char*>(p.ksep) + ho * (D128 * 2);
+    vbase = static_cast<const char*>(p.vsep) + ho * (D128 * 2);
     kstr = vstr = D128 * 2;
     valid = min(BK, n_sep_all - idx * BK);
-    dk_out = p.dksep + (ho + (int64_t)idx * BK) * D128;
-    dv_out = p.dvsep + (ho + (int64_t)idx * BK) * D128;
+    dk_out = p.dksep + ho * D128;
+    dv_out = p.dvsep + ho * D128;
   } else if (kind == G_CAP) {
-    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.cap_rows;
-    kbase = static_cast<const char*>(p.kcap) + (ho + (int64_t)idx * BK) * (D128 * 2);
+    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.cap_rows + (int64_t)idx * BK;
+    kbase = static_cast<const char*>(p.kcap) + ho * (D128 * 2);
     kstr = D128 * 2;
     vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)idx * BK * p.vsT) * 2;
     vstr = p.vsT * 2;
     valid = min(BK, p.n_cap - idx * BK);
     key0 = idx * BK;
-    dk_out = p.dkcap + (ho + (int64_t)idx * BK) * D128;
-    dv_out = p.dvcap + (ho + (int64_t)idx * BK) * D128;
+    dk_out = p.dkcap + ho * D128;
+    dv_out = p.dvcap + ho * D128;
   } else {
     kbase = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH + (int64_t)idx * BK * p.ksT) * 2;
     vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)idx * BK * p.vsT) * 2;
@@ -461,13 +466,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
     dk_out = p.dk_acc + ho * D128;
     dv_out = p.dv_acc + ho * D128;
   }
-  {
-    Stage4 sk, sv;
-    stage_load(sk, kbase, kstr, valid, tid);
-    stage_load(sv, vbase, vstr, valid, tid);
-    stage_store(sk, Kg, tid);
-    stage_store(sv, Vg, tid);
-  }
+  dma_block(kbase, kstr, valid, Kg, wid, lane);
+  dma_block(vbase, vstr, valid, Vg, wid, lane);
 
   // this lane's key
   const int kslot = 32 * kw + l32;
@@ -486,20 +486,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
   const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int vcb = vcol >> 3;
 
-  // visits
-  int t_begin, t_end;
-  if (kind == G_SEP) {
-    t_begin = first_gathering_tile(p, idx * BK);
-    t_end = p.n_tiles;
-  } else {
-    t_begin = max(0, key0 - (p.kind == SA_MASK_SEGMENT ? p.P : 0)) / TQ;
-    t_end = p.n_tiles;
-  }
+  int t_begin;
+  if (kind == G_SEP) t_begin = first_gathering_tile(p, idx * BK);
+  else t_begin = max(0, key0 - (p.kind == SA_MASK_SEGMENT ? p.P : 0)) / TQ;
   const bool q_raw = kind == G_CAP;
   const void* qsrc = q_raw ? p.qraw : p.q;
   const int64_t qB = q_raw ? p.qrB : p.qsB, qH = q_raw ? p.qrH : p.qsH, qT = q_raw ? p.qrT : p.qsT;
 
-  for (int t = t_begin; t < t_end; ++t) {
+  for (int t = t_begin; t < p.n_tiles; ++t) {
     int mk = MK_NONE;
     int count = 0;
     if (kind == G_SEP) {
@@ -536,27 +530,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
         const int qc0 = t * TQ + 64 * ch;
         if (qc0 >= p.n_q) break;
         const int qvalid = min(64, p.n_q - qc0);
-        {
-          Stage4 sq, sd;
-          stage_load(sq, static_cast<const char*>(qsrc) + (b * qB + hq * qH + (int64_t)qc0 * qT) * 2, qT * 2,
-                     qvalid, tid);
-          stage_load(sd, static_cast<const char*>(p.dout) + (b * p.dsB + hq * p.dsH + (int64_t)qc0 * p.dsT) * 2,
-                     p.dsT * 2, qvalid, tid);
-          __syncthreads();  // the previous chunk's reads are done
-          stage_store(sq, Qc, tid);
-          stage_store(sd, Dc, tid);
-          __syncthreads();
+        __syncthreads();  // the previous chunk's reads are done
+        dma_block(static_cast<const char*>(qsrc) + (b * qB + hq * qH + (int64_t)qc0 * qT) * 2, qT * 2, qvalid,
+                  Qc, wid, lane);
+        dma_block(static_cast<const char*>(p.dout) + (b * p.dsB + hq * p.dsH + (int64_t)qc0 * p.dsT) * 2,
+                  p.dsT * 2, qvalid, Dc, wid, lane);
+        if (tid < 128) {
+          const int r = tid & 63;
+          const int64_t ri = rowh + qc0 + min(r, qvalid - 1);
+          LD[tid >> 6][r] = tid < 64 ? p.lse[ri] * LOG2E : p.Dv[ri];
         }
-        // per-row lse2 and D of this lane's 16 query rows
-        const int i0 = qc0 + 32 * qw + 4 * hl;
-        float lr[16], dr[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = min(i0 + 8 * (r >> 2) + (r & 3), p.n_q - 1);
-          lr[r] = p.lse[rowh + i] * LOG2E;
-          dr[r] = p.Dv[rowh + i];
-        }
-        // S = Q K^T, dP = dO V^T (queries as rows, this wave's 32 keys as columns)
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+        __syncthreads();
+        // S = Q K^T and dP = dO V^T: queries as rows, this wave's 32 keys as columns
         f32x16 s = f32x16{}, dp = f32x16{};
         {
           const char* ql = Qc + (32 * qw + l32) * 256;
@@ -567,13 +553,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
           for (int ks = 0; ks < 8; ++ks) {
             const int off = ((2 * ks) ^ kf) << 4;
             const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ql + off));
-            const bf16x8 da = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dl + off));
             const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + off));
-            const bf16x8 vb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vl + off));
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, s, 0, 0, 0);
+            const bf16x8 da = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dl + off));
+            const bf16x8 vb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vl + off));
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, dp, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
+        const int i0 = qc0 + 32 * qw + 4 * hl;
         switch (mk) {
           case MK_NONE: mask_keys<MK_NONE>(p, i0, j, jsep, count_ok, s); break;
           case MK_COUNT: mask_keys<MK_COUNT>(p, i0, j, jsep, count_ok, s); break;
@@ -583,22 +571,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
           case MK_LCAP: mask_keys<MK_LCAP>(p, i0, j, jsep, count_ok, s); break;
           default: mask_keys<MK_SEG>(p, i0, j, jsep, count_ok, s); break;
         }
-        f32x16 pr, ds;
+        // P = 2^(S - lse2) (s), dS = P (dP - D) (dp), in place
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[r];
-          if constexpr (ALIBI) {
-            const int i = i0 + 8 * (r >> 2) + (r & 3);
-            x = fmaf(-m2, fminf((float)(i - j), (float)p.L), x);
+        for (int g = 0; g < 4; ++g) {
+          const float4 l4 = *reinterpret_cast<const float4*>(&LD[0][32 * qw + 8 * g + 4 * hl]);
+          const float4 d4 = *reinterpret_cast<const float4*>(&LD[1][32 * qw + 8 * g + 4 * hl]);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            float x = s[r];
+            if constexpr (ALIBI) x = fmaf(-m2, fminf((float)(i0 + 8 * g + e - j), (float)p.L), x);
+            const float pe = __builtin_amdgcn_exp2f(x - lv[e]);
+            s[r] = pe;
+            dp[r] = pe * (dp[r] - dv4[e]);
           }
-          const float e = __builtin_amdgcn_exp2f(x - lr[r]);
-          pr[r] = e;
-          ds[r] = e * (dp[r] - dr[r]);
         }
         bf16x8 pb[2], db[2];
-        pack_tile(pr, pb);
-        pack_tile(ds, db);
-        // dV^T += dO^T P, dK^T += Q^T dS (transpose reads of the chunk rows 32 qw ..)
+        pack_tile(s, pb);
+        pack_tile(dp, db);
+        // dV^T += dO^T P and dK^T += Q^T dS: transpose reads of this wave's 32 chunk rows
         {
           const char* dt = Dc + (32 * qw + vrow) * 256 + ((vcol & 7) << 1);
           const char* qt = Qc + (32 * qw + vrow) * 256 + ((vcol & 7) << 1);
@@ -609,29 +601,31 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
             const int o1 = (16 * ks + 8) * 256 + (((4 * dm + vcb) ^ vf1) << 4);
             const bf16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(dt + o0));
             const bf16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(dt + o1));
-            const bf16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qt + o0));
-            const bf16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qt + o1));
             dva[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7),
                                                              pb[ks], dva[dm], 0, 0, 0);
+            const bf16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qt + o0));
+            const bf16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qt + o1));
             dka[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7),
                                                              db[ks], dka[dm], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
       }
     }
   }
 
-  // waves qw = 1 hand their partial sums to waves qw = 0 through LDS, which
-  // add them and store the group's rows
+  // waves qw = 1 hand their partial sums to waves qw = 0 through LDS (the four
+  // 16 KB arrays are contiguous per kw pair once the loop is over)
   __syncthreads();
-  float* red = reinterpret_cast<float*>(smem) + kw * (2 * 4 * 16 * 64);
+  float* red = reinterpret_cast<float*>(kw == 0 ? Kg : Qc);
+  float* red2 = reinterpret_cast<float*>(kw == 0 ? Vg : Dc);
   if (qw == 1) {
 #pragma unroll
     for (int dm = 0; dm < 4; ++dm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         red[(dm * 16 + r) * 64 + lane] = dka[dm][r];
-        red[(64 + dm * 16 + r) * 64 + lane] = dva[dm][r];
+        red2[(dm * 16 + r) * 64 + lane] = dva[dm][r];
       }
   }
   __syncthreads();
@@ -643,19 +637,18 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * dm + 8 * g + 4 * hl;
+        const int r0 = dm * 16 + 4 * g;
         float4 kx, vx;
-        kx.x = dka[dm][4 * g] + red[(dm * 16 + 4 * g) * 64 + lane];
-        kx.y = dka[dm][4 * g + 1] + red[(dm * 16 + 4 * g + 1) * 64 + lane];
-        kx.z = dka[dm][4 * g + 2] + red[(dm * 16 + 4 * g + 2) * 64 + lane];
-        kx.w = dka[dm][4 * g + 3] + red[(dm * 16 + 4 * g + 3) * 64 + lane];
+        kx.x = dka[dm][4 * g] + red[(r0) * 64 + lane];
+        kx.y = dka[dm][4 * g + 1] + red[(r0 + 1) * 64 + lane];
+        kx.z = dka[dm][4 * g + 2] + red[(r0 + 2) * 64 + lane];
+        kx.w = dka[dm][4 * g + 3] + red[(r0 + 3) * 64 + lane];
+        vx.x = dva[dm][4 * g] + red2[(r0) * 64 + lane];
+        vx.y = dva[dm][4 * g + 1] + red2[(r0 + 1) * 64 + lane];
+        vx.z = dva[dm][4 * g + 2] + red2[(r0 + 2) * 64 + lane];
+        vx.w = dva[dm][4 * g + 3] + red2[(r0 + 3) * 64 + lane];
         *reinterpret_cast<float4*>(krow + d0) = kx;
-        {
-          vx.x = dva[dm][4 * g] + red[(64 + dm * 16 + 4 * g) * 64 + lane];
-          vx.y = dva[dm][4 * g + 1] + red[(64 + dm * 16 + 4 * g + 1) * 64 + lane];
-          vx.z = dva[dm][4 * g + 2] + red[(64 + dm * 16 + 4 * g + 2) * 64 + lane];
-          vx.w = dva[dm][4 * g + 3] + red[(64 + dm * 16 + 4 * g + 3) * 64 + lane];
-          *reinterpret_cast<float4*>(vrow_o + d0) = vx;
-        }
+        *reinterpret_cast<float4*>(vrow_o + d0) = vx;
       }
   }
 }
@@ -816,7 +809,8 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
     r.osB = a.o_stride[0]; r.osH = a.o_stride[1]; r.osT = a.o_stride[2];
     r.D = w.D;
     r.B = a.batch; r.h = a.h_q; r.n = m.n_q; r.d = a.d; r.esz = 2;
-    hipLaunchKernelGGL(bwd_rowdot, dim3((unsigned)ceil_div(rows_q, 256)), dim3(256), 0, s, r);
+    const int64_t threads = rows_q * (a.d * 2 / 16);
+    hipLaunchKernelGGL(bwd_rowdot, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s, r);
   }
   BwdArgs p;
   memset(&p, 0, sizeof(p));
