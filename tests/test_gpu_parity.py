@@ -478,3 +478,68 @@ def test_bwd_small(sa, case):
                                           alibi_exp=wl.alibi_exp)
         for name, got, ref in (("dq", dq[b], rq), ("dk", dk[b], rk), ("dv", dv[b], rv)):
             bwd_compare(f"b{b} {name}", to64(got), ref)
+
+
+def _workload_bwd_parity(sa, cid, dq_heads, n_random, key_block, dk_kv_head, nonsep_only=False):
+    """Backward at a workload's full size: dQ on sampled rows of some heads; dK, dV on one
+    key block of one kv head, from every query row that sees a key of that block (the
+    oracle sums those rows' contributions, over the kv head's whole GQA group)."""
+    wl = W.WORKLOADS[cid]
+    log(f"workload {cid} backward: inputs")
+    inp = W.make_inputs(wl)
+    sep = inp.get("sep")
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    sa_obj = device_mask(wl, None if sep is None else sep.cuda())
+    sa_obj.build_plan()
+    lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
+    o = sa_obj.forward(q, k, v, lse=lse, rope_base=wl.rope_base, scale=wl.scale, alibi_exp=wl.alibi_exp)
+    dout = W.make_grad(tuple(q.shape), seed=wl.seed + 11).cuda()
+    dq, dk, dv = sa_obj.backward(q, k, v, o, lse, dout, rope_base=wl.rope_base, scale=wl.scale,
+                                 alibi_exp=wl.alibi_exp)
+    torch.cuda.synchronize()
+    spec = spec_of(wl, None if sep is None else sep.numpy())
+    group = wl.h_q // wl.h_kv
+    slope = (lambda h: None) if wl.alibi_exp is None else (lambda h: O.alibi_slope(h, wl.h_q, wl.alibi_exp))
+    r_ = np.random.default_rng(cid)
+    rows = np.array(sorted(set(range(64)) | set(range(wl.n_q - 64, wl.n_q))
+                           | set(r_.choice(wl.n_q, size=n_random, replace=False).tolist())))
+    for h in dq_heads:
+        g = h // group
+        log(f"workload {cid} backward: dq head {h}")
+        rq, _, _ = O.attention_grad_rows(to64(inp["q"][0, h]), to64(inp["k"][0, g]), to64(inp["v"][0, g]),
+                                         to64(dout[0, h]), rows, spec, wl.rope_base, wl.scale, slope(h))
+        bwd_compare(f"w{cid} dq h{h}", to64(dq[0, h][torch.from_numpy(rows).cuda()]), rq)
+    keys = np.arange(64 * key_block, min(wl.n_k, 64 * key_block + 64))
+    sel = np.ones(len(keys), dtype=bool)
+    if nonsep_only:  # separators are read by every later query: only the other keys are checked
+        sel = sep.numpy()[keys] == 0
+    cand = np.arange(max(0, keys[0] - wl.P), wl.n_q)
+    seen = O.visible(spec, cand[:, None], keys[sel][None, :]).any(axis=1)
+    qrows = cand[seen]
+    log(f"workload {cid} backward: dk/dv kv head {dk_kv_head}, block {key_block}, {len(qrows)} query rows")
+    rk = np.zeros((len(keys), wl.d))
+    rv = np.zeros((len(keys), wl.d))
+    Kg, Vg = to64(inp["k"][0, dk_kv_head]), to64(inp["v"][0, dk_kv_head])
+    for h in range(dk_kv_head * group, (dk_kv_head + 1) * group):
+        _, dkc, dvc = O.attention_grad_rows(to64(inp["q"][0, h]), Kg, Vg, to64(dout[0, h]), qrows, spec,
+                                            wl.rope_base, wl.scale, slope(h))
+        rk += dkc[keys]
+        rv += dvc[keys]
+    gk = to64(dk[0, dk_kv_head, torch.from_numpy(keys).cuda()])
+    gv = to64(dv[0, dk_kv_head, torch.from_numpy(keys).cuda()])
+    bwd_compare(f"w{cid} dk g{dk_kv_head} blk{key_block}", gk[sel], rk[sel])
+    bwd_compare(f"w{cid} dv g{dk_kv_head} blk{key_block}", gv[sel], rv[sel])
+
+
+# key blocks near the end keep the oracle's share small (fewer query rows read them)
+def test_workload3_backward_sampled(sa):
+    _workload_bwd_parity(sa, 3, dq_heads=[0, 31], n_random=64, key_block=505, dk_kv_head=31)
+
+
+def test_workload5_backward_sampled(sa):
+    _workload_bwd_parity(sa, 5, dq_heads=[31], n_random=32, key_block=2040, dk_kv_head=7,
+                         nonsep_only=True)
+
+
+def test_workload6_backward_sampled(sa):
+    _workload_bwd_parity(sa, 6, dq_heads=[0], n_random=64, key_block=505, dk_kv_head=0)
