@@ -55,7 +55,7 @@ __all__ = [
     "attention_rows", "attention_fast", "attention", "plan", "plan_items_of_tile",
     "topk_scores", "topk_select", "pair_counts", "pair_count_total", "q0_closed_form",
     "alibi_slope", "q0_alibi_closed_form", "segmented_run", "attention_grad_rows",
-    "attention_backward",
+    "attention_backward", "StreamCache", "stream_cache_tokens", "decode_attention",
 ]
 
 
@@ -614,4 +614,98 @@ def attention_backward(Q, K, V, dO, spec: MaskSpec, rope_base: Optional[float], 
         dK[g] += dk
         dV[g] += dv
     return dQ, dK, dV
+
+
+# ----------------------------------------------------------------------------
+# Streaming decode with the four-part cache (SepLLM page, part 6.2, generation)
+# ----------------------------------------------------------------------------
+
+class StreamCache:
+    """Which tokens the generation-time cache holds, one token at a time.
+
+    Parts: Initial (the first ``a`` tokens), Separator (at most ``s``
+    separators, the most recent kept), Local window (the last ``w`` tokens,
+    the newest one included) and Past (tokens that left the local window
+    since the last compression).  The run size ``a + s + w + |Past|`` may
+    not exceed ``c``: when a token entering Past brings it to ``c``, the
+    separators of Past move to the Separator part (the oldest separators
+    beyond ``s`` are dropped) and the rest of Past is discarded.  Positions
+    are the tokens' original indices.  Holds token indices only.
+    """
+
+    def __init__(self, a: int, s: int, w: int, c: int):
+        if not (a >= 0 and s >= 1 and w >= 1 and c > a + s + w):
+            raise ValueError("need a >= 0, s >= 1, w >= 1 and c > a + s + w")
+        self.a, self.s, self.w, self.c = a, s, w, c
+        self.initial: List[int] = []
+        self.sep: List[int] = []
+        self.local: List[int] = []
+        self.past: List[int] = []
+        self.flags: List[int] = []
+        self.t = 0
+
+    @property
+    def run_size(self) -> int:
+        return self.a + self.s + self.w + len(self.past)
+
+    def append(self, is_sep: bool) -> int:
+        """Adds token ``t`` (the next index) and applies the policy; returns t."""
+        t = self.t
+        self.flags.append(1 if is_sep else 0)
+        if t < self.a:
+            self.initial.append(t)
+        else:
+            self.local.append(t)
+            if len(self.local) > self.w:
+                self.past.append(self.local.pop(0))
+                if self.run_size >= self.c:
+                    moved = [j for j in self.past if self.flags[j]]
+                    self.sep = (self.sep + moved)[-self.s:]
+                    self.past = []
+        self.t = t + 1
+        return t
+
+    def tokens(self) -> np.ndarray:
+        return np.array(sorted(self.initial + self.sep + self.past + self.local), dtype=np.int64)
+
+
+def stream_cache_tokens(t: int, flags: np.ndarray, a: int, s: int, w: int, c: int) -> np.ndarray:
+    """The same set in closed form, after token t has been added.
+
+    Tokens a, a+1, ... leave the local window in order: after token t,
+    e = max(0, t + 1 - a - w) of them have.  Every P = c - a - s - w of them
+    a compression empties Past, so Past holds the last e mod P of them and
+    the first P * floor(e / P) were compressed; the Separator part holds the
+    last s separators among the compressed tokens.
+    """
+    P = c - a - s - w
+    e = max(0, t + 1 - a - w)
+    comp = P * (e // P)
+    init = np.arange(0, min(a, t + 1))
+    local = np.arange(max(a, t - w + 1), t + 1) if t >= a else np.arange(0)
+    past = np.arange(a + comp, a + e)
+    compressed = np.arange(a, a + comp)
+    seps = compressed[np.asarray(flags)[compressed] == 1][-s:] if comp > 0 else np.arange(0)
+    return np.array(sorted(set(init.tolist()) | set(seps.tolist()) | set(past.tolist())
+                           | set(local.tolist())), dtype=np.int64)
+
+
+def decode_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, t: int, tokens: np.ndarray,
+                     rope_base: Optional[float], scale: float):
+    """One decode step of one head: query t over the cached tokens (SepLLM page,
+    part 6.1 restricted to the held keys), RoPE at the original positions.
+    q [d] raw; k, v [n, d] raw rows of every token so far.  Returns o [d], lse."""
+    q = np.asarray(q, dtype=np.float64)
+    kk = np.asarray(k, dtype=np.float64)[tokens]
+    vv = np.asarray(v, dtype=np.float64)[tokens]
+    if rope_base:
+        d = q.shape[0]
+        theta = rope_theta(d, rope_base)
+        ang = (float(t) - tokens.astype(np.float64))[:, None] * theta[None, :]
+        s_ = scale * np.einsum("jd,jd->j", rotate(np.broadcast_to(q, kk.shape), ang), kk)
+    else:
+        s_ = scale * (kk @ q)
+    mu = s_.max()
+    e = np.exp(s_ - mu)
+    return (e @ vv) / e.sum(), mu + math.log(e.sum())
 

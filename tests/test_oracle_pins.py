@@ -36,6 +36,14 @@ Pins, by oracle function:
                         torch primitives (SepLLM, segment, capped Lambda via
                         the RoPE realisation, capped ALiBi, GQA); central
                         finite differences through the definition-mode forward.
+  StreamCache / stream_cache_tokens / decode_attention
+                        a ten-step hand trace of the generation-time cache
+                        (tests/golden/stream_cache_hand.json); the state
+                        machine against the independently written closed form
+                        on long random streams; the run size never above c and
+                        its mean over whole periods under the page's bound
+                        (w+c+a+s)/2; decode output against torch SDPA on
+                        explicitly rotated rows with a mask over the held set.
 """
 import heapq
 import json
@@ -700,3 +708,58 @@ def test_backward_capped_finite_differences():
             args[name + "_"][a, b] -= 2 * eps
             fm = f(**args)
             assert abs((fp - fm) / (2 * eps) - g[a, b]) < 1e-7, (name, a, b)
+
+
+# ---------------------------------------------------------------------------
+# streaming decode with the four-part cache (SepLLM page, part 6.2, generation)
+# ---------------------------------------------------------------------------
+
+def test_stream_cache_hand_trace():
+    g = json.load(open(os.path.join(GOLDEN, "stream_cache_hand.json")))
+    sc = O.StreamCache(g["a"], g["s"], g["w"], g["c"])
+    for t, f in enumerate(g["flags"]):
+        sc.append(bool(f))
+        assert sc.tokens().tolist() == g["tokens_after_step"][t], t
+        assert sc.run_size == g["run_size_after_step"][t], t
+        assert O.stream_cache_tokens(t, np.array(g["flags"]), g["a"], g["s"], g["w"], g["c"]).tolist() \
+            == g["tokens_after_step"][t]
+
+
+@pytest.mark.parametrize("a,s,w,c,p", [(4, 64, 128, 324, 0.1), (4, 8, 16, 40, 0.6), (0, 1, 1, 3, 0.5),
+                                       (2, 3, 5, 20, 0.0), (3, 4, 6, 30, 1.0)])
+def test_stream_cache_closed_form_and_occupancy(a, s, w, c, p):
+    n = 2500
+    flags = (RNG.random(n) < p).astype(np.uint8)
+    sc = O.StreamCache(a, s, w, c)
+    P = c - a - s - w
+    sizes = []
+    for t in range(n):
+        sc.append(bool(flags[t]))
+        np.testing.assert_array_equal(sc.tokens(), O.stream_cache_tokens(t, flags, a, s, w, c))
+        assert sc.run_size <= c
+        sizes.append(sc.run_size)
+    # after the warm-up the run size cycles a+s+w .. c-1: its mean over whole periods is
+    # a+s+w+(P-1)/2, under the page's bound (w+c+a+s)/2
+    t0 = a + w + P  # first compression
+    m = (n - t0) // P * P
+    mean = float(np.mean(sizes[t0:t0 + m]))
+    assert mean == pytest.approx(a + s + w + (P - 1) / 2) and mean < (w + c + a + s) / 2
+
+
+def test_decode_attention_vs_sdpa():
+    d, n, base = 32, 400, 10000.0
+    a, s, w, c = 4, 8, 16, 60
+    flags = (RNG.random(n) < 0.3).astype(np.uint8)
+    q, k, v = rand(n, d), rand(n, d), rand(n, d)
+    scale = d ** -0.5
+    for t in (0, 3, 20, 57, 150, 399):
+        toks = O.stream_cache_tokens(t, flags, a, s, w, c)
+        o, lse = O.decode_attention(q[t], k[:t + 1], v[:t + 1], t, toks, base, scale)
+        qr = complex_rope(torch.from_numpy(q[t:t + 1]), torch.tensor([t]), base)
+        kr = complex_rope(torch.from_numpy(k[:t + 1]), torch.arange(t + 1), base)
+        mask = torch.zeros(1, t + 1, dtype=torch.bool)
+        mask[0, torch.from_numpy(toks)] = True
+        ref = sdpa(qr, kr, torch.from_numpy(v[:t + 1]), mask, scale).numpy()[0]
+        np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
+        ref_l = torch.logsumexp((qr @ kr.T * scale).masked_fill(~mask, -math.inf), dim=1).item()
+        assert abs(lse - ref_l) < 1e-12
