@@ -221,6 +221,60 @@ int sparse_attn_bwd(const sa_mask_t *m, const void *plan, size_t plan_bytes,
                     const sa_fwd_args_t *args, const sa_bwd_args_t *grads, void *ws,
                     size_t ws_bytes, hipStream_t stream);
 
+/*
+ * Streaming decode with the generation-time cache of the SepLLM page (part
+ * 6.2, generation): per sequence, Initial (the first a tokens), Separator (at
+ * most s separators, the most recent), Local window (the last w tokens, the
+ * newest included) and Past (tokens that left the local window since the last
+ * compression).  When a + s + w + |Past| reaches c, Past's separators join the
+ * Separator part in order (the oldest beyond s dropped) and Past is emptied;
+ * then the new query attends to every held token.  Keys are stored rotated at
+ * their original positions.
+ *   batch, h_q, h_kv, d   sizes (bf16, d = 128; h_q % h_kv == 0).
+ *   a, s, w, c            a >= 0, s >= 1, w >= 1, c > a + s + w, c <= 4096.
+ *   rope, rope_base       SA_ROPE_NONE or SA_ROPE_HALF.
+ *   scale                 logit scale.
+ */
+typedef struct {
+  int32_t batch, h_q, h_kv, d;
+  int32_t a, s, w, c;
+  int32_t rope;
+  float rope_base;
+  float scale;
+} sa_stream_cfg_t;
+
+/*
+ * Host only: bytes of the cache state (caller-owned device memory, one buffer:
+ * the K and V rows [batch, h_kv, c, d], per-slot token index and separator
+ * flag, per-sequence counters) and of the per-step workspace.
+ */
+int sa_stream_state_bytes(const sa_stream_cfg_t *cfg, size_t *bytes);
+int sa_decode_workspace_bytes(const sa_stream_cfg_t *cfg, size_t *bytes);
+
+/* Empties every sequence's cache (a fill kernel on the stream). */
+int sparse_attn_stream_reset(const sa_stream_cfg_t *cfg, void *state, size_t state_bytes,
+                             hipStream_t stream);
+
+/*
+ * One decode step for every sequence: q [batch, h_q, d], k, v [batch, h_kv, d]
+ * (raw projections of the new token, contiguous), is_sep uint8 [batch] (the
+ * new token is a separator), o [batch, h_q, d] written, lse fp32 [batch, h_q]
+ * or NULL.  The new token takes position t = the number of tokens the
+ * sequence has seen.  Steps on one state must be stream-ordered.  Errors:
+ * SA_EINVAL, SA_EUNSUPPORTED, SA_ENOSPACE, SA_EHIP.
+ */
+int sparse_attn_decode_step(const sa_stream_cfg_t *cfg, void *state, size_t state_bytes,
+                            const void *q, const void *k, const void *v, const uint8_t *is_sep,
+                            void *o, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Host only: the state layout (byte offsets of the K rows, V rows, per-slot
+ * token index int32 [batch, c], per-slot flag uint8 [batch, c] and the
+ * per-sequence counters int32 [batch, 8]: t, n_init, n_sep, sep_head, n_past,
+ * n_local, local_head, reserved).
+ */
+int sa_stream_layout(const sa_stream_cfg_t *cfg, int64_t offsets[5]);
+
 /* Host only: bytes of device workspace topk_retrieve needs. */
 int sa_topk_workspace_bytes(int32_t n_heads, int32_t pool_len, size_t *bytes);
 

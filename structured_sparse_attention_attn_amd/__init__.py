@@ -65,6 +65,11 @@ class sa_bwd_args_t(ctypes.Structure):
                 ("dk", _vp), ("dk_stride", _i64 * 3), ("dv", _vp), ("dv_stride", _i64 * 3)]
 
 
+class sa_stream_cfg_t(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("h_q", _i32), ("h_kv", _i32), ("d", _i32), ("a", _i32), ("s", _i32),
+                ("w", _i32), ("c", _i32), ("rope", _i32), ("rope_base", _f32), ("scale", _f32)]
+
+
 _MASKP = ctypes.POINTER(sa_mask_t)
 _ARGSP = ctypes.POINTER(sa_fwd_args_t)
 _lib.sa_last_error.restype = ctypes.c_char_p
@@ -84,6 +89,15 @@ _lib.sparse_attn_segment_carry.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _
                                            _i64, _vp]
 _lib.sa_bwd_workspace_bytes.argtypes = [_MASKP, _ARGSP, ctypes.POINTER(_sz)]
 _lib.sparse_attn_bwd.argtypes = [_MASKP, _vp, _sz, _ARGSP, ctypes.POINTER(sa_bwd_args_t), _vp, _sz, _vp]
+_CFGP = ctypes.POINTER(sa_stream_cfg_t)
+_lib.sa_stream_state_bytes.argtypes = [_CFGP, ctypes.POINTER(_sz)]
+_lib.sa_decode_workspace_bytes.argtypes = [_CFGP, ctypes.POINTER(_sz)]
+_lib.sa_stream_layout.argtypes = [_CFGP, ctypes.POINTER(_i64)]
+_lib.sparse_attn_stream_reset.argtypes = [_CFGP, _vp, _sz, _vp]
+_lib.sparse_attn_decode_step.argtypes = [_CFGP, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+for _name in ("sa_stream_state_bytes", "sa_decode_workspace_bytes", "sa_stream_layout",
+              "sparse_attn_stream_reset", "sparse_attn_decode_step"):
+    getattr(_lib, _name).restype = ctypes.c_int
 for _name in ("sa_plan_layout", "sa_plan_bytes", "sparse_attn_plan", "sa_fwd_workspace_bytes",
               "sparse_attn_fwd", "sparse_attn_rope", "sparse_attn_attend", "sa_topk_workspace_bytes",
               "topk_retrieve", "sparse_attn_segment_carry", "sa_bwd_workspace_bytes",
@@ -289,4 +303,43 @@ def sparse_attn_bwd(m: sa_mask_t, plan, args: sa_fwd_args_t, grads: sa_bwd_args_
                                 ctypes.byref(grads), _ptr(ws),
                                 0 if ws is None else ws.numel() * ws.element_size(),
                                 _stream(stream)))
+
+
+def stream_cfg(batch: int, h_q: int, h_kv: int, d: int, a: int, s: int, w: int, c: int, *,
+               rope_base: Optional[float] = None, scale: Optional[float] = None) -> sa_stream_cfg_t:
+    return sa_stream_cfg_t(batch, h_q, h_kv, d, a, s, w, c, SA_ROPE_HALF if rope_base else SA_ROPE_NONE,
+                           float(rope_base or 0.0), float(scale if scale is not None else d ** -0.5))
+
+
+def sa_stream_state_bytes(cfg: sa_stream_cfg_t) -> int:
+    out = _sz()
+    _check(_lib.sa_stream_state_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def sa_decode_workspace_bytes(cfg: sa_stream_cfg_t) -> int:
+    out = _sz()
+    _check(_lib.sa_decode_workspace_bytes(ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+def sa_stream_layout(cfg: sa_stream_cfg_t):
+    out = (_i64 * 5)()
+    _check(_lib.sa_stream_layout(ctypes.byref(cfg), out))
+    return list(out)
+
+
+def sparse_attn_stream_reset(cfg: sa_stream_cfg_t, state, stream=None) -> None:
+    _check(_lib.sparse_attn_stream_reset(ctypes.byref(cfg), _ptr(state), state.numel(), _stream(stream)))
+
+
+def sparse_attn_decode_step(cfg: sa_stream_cfg_t, state, q, k, v, is_sep, o, ws, lse=None,
+                            stream=None) -> None:
+    """One decode step (see include/sparse_attn.h): q [B,h_q,d], k, v [B,h_kv,d], is_sep uint8 [B]."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _check(_lib.sparse_attn_decode_step(ctypes.byref(cfg), _ptr(state), state.numel(), _ptr(q), _ptr(k),
+                                        _ptr(v), _ptr(is_sep), _ptr(o), _ptr(lse), _ptr(ws),
+                                        ws.numel(), _stream(stream)))
 

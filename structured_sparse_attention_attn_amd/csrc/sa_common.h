@@ -120,6 +120,19 @@ struct BwdWs {
   float* dvcap;
 };
 
+// Streaming decode state and workspace (byte offsets).
+struct StreamLayout {
+  int64_t k, v, pos, flag, ctrl, total;
+  int n_split;
+  int64_t ws_qrot, ws_part, ws_total;
+};
+
+StreamLayout stream_layout(const sa_stream_cfg_t& cfg);
+hipError_t launch_stream_reset(const sa_stream_cfg_t& cfg, void* state, hipStream_t s);
+hipError_t launch_decode_step(const sa_stream_cfg_t& cfg, void* state, const void* q, const void* k,
+                              const void* v, const uint8_t* is_sep, void* o, float* lse, void* ws,
+                              const ThetaTable& theta, hipStream_t s);
+
 hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const void* plan,
                       const sa_fwd_args_t& a, const sa_bwd_args_t& g, const RopeOut& ro,
                       const BwdWs& w, const ThetaTable& theta, hipStream_t s);

@@ -1,0 +1,474 @@
+// Streaming decode with the generation-time cache (SepLLM page, part 6.2,
+// generation): Initial (the first a tokens), Separator (at most s separators),
+// Local window (the last w tokens) and Past (tokens that left the local window
+// since the last compression).  When a + s + w + |Past| reaches c, Past's
+// separators join the Separator part in order, its oldest beyond s dropped,
+// and Past is emptied; then the new query attends to every held token.
+//
+// Slot layout per (sequence, kv head): [0, a) Initial, [a, a+s) Separator
+// ring, [a+s, a+s+P) Past (P = c - a - s - w), [a+s+P, c) Local ring.  Both
+// rings fill from slot 0 and start to wrap only once full, so the held slots
+// are always four contiguous ranges.  Keys are stored rotated at their
+// original positions; a query never needs them moved again.
+//
+// Per step: stream_insert (one work group per (sequence, kv head): the moved
+// and compressed rows, the new key and value, the rotated queries), then
+// stream_ctrl (one wave per sequence: token index and separator flag of each
+// slot, the counters), then decode_attn (split over slots: partial softmax
+// per 64 slots) and decode_combine.
+#include "sa_common.h"
+
+namespace sa {
+namespace {
+
+typedef unsigned short u16;
+
+enum { C_T = 0, C_NINIT = 1, C_NSEP = 2, C_SEPHEAD = 3, C_NPAST = 4, C_NLOCAL = 5, C_LOCALHEAD = 6 };
+constexpr int SPLIT = 64;   // slots per decode work group
+constexpr int MAX_G = 8;    // query heads per kv head
+
+struct StreamArgs {
+  char* kc;                  // [B, h_kv, c, d] bf16 rows
+  char* vc;
+  int* pos;                  // [B, c] token index of each slot
+  unsigned char* flag;       // [B, c] separator flag of each slot
+  int* ctrl;                 // [B, 8] counters
+  const u16* q;              // [B, h_q, d]
+  const u16* k;              // [B, h_kv, d]
+  const u16* v;
+  const unsigned char* is_sep;  // [B]
+  float* qrot;               // [B, h_q, d] rotated, scaled by scale * log2(e)
+  float* part;               // [B, h_q, n_split, d + 2]
+  u16* o;                    // [B, h_q, d]
+  float* lse;                // [B, h_q] or null
+  int B, h_q, h_kv, d, a, s, w, c, P, group, rotate, n_split;
+  float scale_log2;
+  ThetaTable theta;
+};
+
+__device__ inline float bf2f(u16 x) { return __uint_as_float(((unsigned)x) << 16); }
+__device__ inline u16 f2bf(float f) {  // round to nearest even (finite inputs)
+  const unsigned u = __float_as_uint(f);
+  return (u16)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ inline void angle_sincos(double pos, double th, float* c, float* s) {
+  const double TWO_PI_HI = 6.283185307179586232;
+  const double TWO_PI_LO = 2.4492935982947064e-16;
+  const double INV_TWO_PI = 0.15915494309189535;
+  const double ang = pos * th;
+  const double kq = rint(ang * INV_TWO_PI);
+  double r = fma(-kq, TWO_PI_HI, ang);
+  r = fma(-kq, TWO_PI_LO, r);
+  sincosf((float)r, s, c);
+}
+
+// What this step does to one sequence's cache, from its counters.
+struct StepPlan {
+  int t, ns;          // new token index and slot
+  bool evict;         // the oldest local token leaves the window (slot ms)
+  int ms;
+  bool compress;      // ... and fills Past: compression
+  int n_past;         // Past size before the step
+};
+
+__device__ inline StepPlan plan_step(const StreamArgs& p, const int* ct) {
+  StepPlan sp;
+  sp.t = ct[C_T];
+  sp.n_past = ct[C_NPAST];
+  const int n_local = ct[C_NLOCAL], head = ct[C_LOCALHEAD];
+  const int L0 = p.a + p.s + p.P;
+  sp.evict = false;
+  sp.compress = false;
+  sp.ms = 0;
+  if (sp.t < p.a) {
+    sp.ns = sp.t;
+  } else if (n_local < p.w) {
+    sp.ns = L0 + n_local;
+  } else {
+    sp.evict = true;
+    sp.ms = L0 + head;
+    sp.ns = sp.ms;
+    sp.compress = sp.n_past + 1 == p.P;
+  }
+  return sp;
+}
+
+// Compression of one sequence, computed by one wave: Past items i < P are the
+// Past slots a+s+i (i < n_past) and the evicted local token (i = n_past).  The
+// separators among them, in order, are appended to the Separator ring; the
+// k-th goes to ring slot (head + n_sep + k) mod s and survives only if it is
+// among the last s appended.  Writes the survivors' (source slot, ring slot)
+// to list[] and returns their count; n_new receives the separator count.
+__device__ inline int compress_list(const StreamArgs& p, int b, const int* ct, const StepPlan& sp, int lane,
+                                    int* list_src, int* list_dst, int* n_new_out) {
+  const unsigned char* fl = p.flag + (int64_t)b * p.c;
+  auto src_of = [&](int i) { return i < sp.n_past ? p.a + p.s + i : sp.ms; };
+  int n_new = 0;
+  for (int i0 = 0; i0 < p.P; i0 += 64) {
+    const int i = i0 + lane;
+    const bool f = i < p.P && fl[src_of(i)] != 0;
+    n_new += __popcll(__ballot(f));
+  }
+  const int n_sep = ct[C_NSEP], head = ct[C_SEPHEAD];
+  const int first = max(0, n_new - p.s);  // appends before this one are overwritten
+  int rank0 = 0;
+  for (int i0 = 0; i0 < p.P; i0 += 64) {
+    const int i = i0 + lane;
+    const bool f = i < p.P && fl[src_of(i)] != 0;
+    const unsigned long long m = __ballot(f);
+    const int k = rank0 + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+    if (f && k >= first) {
+      list_src[k - first] = src_of(i);
+      list_dst[k - first] = p.a + (head + n_sep + k) % p.s;
+    }
+    rank0 += __popcll(m);
+  }
+  *n_new_out = n_new;
+  return n_new - first;
+}
+
+__global__ __launch_bounds__(256) void stream_insert(StreamArgs p) {
+  __shared__ int list_src[4096];
+  __shared__ int list_dst[4096];
+  __shared__ int n_list;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int b = blockIdx.x / p.h_kv, g = blockIdx.x % p.h_kv;
+  const int* ct = p.ctrl + b * 8;
+  const StepPlan sp = plan_step(p, ct);
+  char* K = p.kc + ((int64_t)b * p.h_kv + g) * p.c * 256;
+  char* V = p.vc + ((int64_t)b * p.h_kv + g) * p.c * 256;
+
+  // phase A: every read of a slot this step overwrites
+  if (sp.compress && wid == 0) {
+    int n_new;
+    const int n = compress_list(p, b, ct, sp, lane, list_src, list_dst, &n_new);
+    if (lane == 0) n_list = n;
+  }
+  __syncthreads();
+  if (sp.compress) {
+    // survivors to the Separator ring (ring slots are read by nobody here)
+    const int n = n_list;
+    for (int e = tid; e < n * 32; e += 256) {
+      const int r = e >> 5, piece = e & 31;
+      const char* srcb = piece < 16 ? K : V;
+      char* dstb = piece < 16 ? K : V;
+      const int pc = piece & 15;
+      *reinterpret_cast<uint4*>(dstb + (int64_t)list_dst[r] * 256 + pc * 16) =
+          *reinterpret_cast<const uint4*>(srcb + (int64_t)list_src[r] * 256 + pc * 16);
+    }
+  } else if (sp.evict && tid < 32) {
+    // the evicted local token enters Past
+    const int pc = tid & 15;
+    char* base = tid < 16 ? K : V;
+    *reinterpret_cast<uint4*>(base + (int64_t)(p.a + p.s + sp.n_past) * 256 + pc * 16) =
+        *reinterpret_cast<const uint4*>(base + (int64_t)sp.ms * 256 + pc * 16);
+  }
+  __syncthreads();
+
+  // phase B: the new token's key (rotated at t) and value, and the rotated queries
+  const int half = p.d / 2;
+  if (tid < half) {
+    const int c0 = tid;
+    const u16* kr = p.k + ((int64_t)b * p.h_kv + g) * p.d;
+    float x1 = bf2f(kr[c0]), x2 = bf2f(kr[c0 + half]);
+    if (p.rotate) {
+      float cs, sn;
+      angle_sincos((double)sp.t, p.theta.th[c0], &cs, &sn);
+      const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+      x1 = y1;
+      x2 = y2;
+    }
+    u16* dst = reinterpret_cast<u16*>(K + (int64_t)sp.ns * 256);
+    dst[c0] = f2bf(x1);
+    dst[c0 + half] = f2bf(x2);
+  } else if (tid < half + 16) {
+    const int pc = tid - half;
+    const char* vr = reinterpret_cast<const char*>(p.v + ((int64_t)b * p.h_kv + g) * p.d);
+    *reinterpret_cast<uint4*>(V + (int64_t)sp.ns * 256 + pc * 16) = *reinterpret_cast<const uint4*>(vr + pc * 16);
+  }
+  for (int e = tid; e < p.group * half; e += 256) {
+    const int gq = e / half, c0 = e % half;
+    const int hq = g * p.group + gq;
+    const u16* qr = p.q + ((int64_t)b * p.h_q + hq) * p.d;
+    float x1 = bf2f(qr[c0]), x2 = bf2f(qr[c0 + half]);
+    if (p.rotate) {
+      float cs, sn;
+      angle_sincos((double)sp.t, p.theta.th[c0], &cs, &sn);
+      const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+      x1 = y1;
+      x2 = y2;
+    }
+    float* qd = p.qrot + ((int64_t)b * p.h_q + hq) * p.d;
+    qd[c0] = x1 * p.scale_log2;
+    qd[c0 + half] = x2 * p.scale_log2;
+  }
+}
+
+// Token index, flag and counters of each sequence after the step (one wave).
+__global__ __launch_bounds__(64) void stream_ctrl(StreamArgs p) {
+  __shared__ int list_src[4096];
+  __shared__ int list_dst[4096];
+  const int lane = threadIdx.x;
+  const int b = blockIdx.x;
+  int* ct = p.ctrl + b * 8;
+  const StepPlan sp = plan_step(p, ct);
+  int* pos = p.pos + (int64_t)b * p.c;
+  unsigned char* fl = p.flag + (int64_t)b * p.c;
+  int n_sep = ct[C_NSEP], head = ct[C_SEPHEAD], n_past = ct[C_NPAST];
+  int n_local = ct[C_NLOCAL], lhead = ct[C_LOCALHEAD], n_init = ct[C_NINIT];
+  if (sp.compress) {
+    int n_new;
+    const int n = compress_list(p, b, ct, sp, lane, list_src, list_dst, &n_new);
+    __syncthreads();
+    for (int r = lane; r < n; r += 64) {
+      pos[list_dst[r]] = pos[list_src[r]];
+      fl[list_dst[r]] = fl[list_src[r]];
+    }
+    __syncthreads();
+    head = (head + max(0, n_sep + n_new - p.s)) % p.s;
+    n_sep = min(p.s, n_sep + n_new);
+    n_past = 0;
+  } else if (sp.evict) {
+    if (lane == 0) {
+      pos[p.a + p.s + n_past] = pos[sp.ms];
+      fl[p.a + p.s + n_past] = fl[sp.ms];
+    }
+    n_past += 1;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    if (sp.t < p.a) {
+      n_init = sp.t + 1;
+    } else if (!sp.evict) {
+      n_local += 1;
+    } else {
+      lhead = (lhead + 1) % p.w;
+    }
+    pos[sp.ns] = sp.t;
+    fl[sp.ns] = p.is_sep[b] != 0 ? 1 : 0;
+    ct[C_T] = sp.t + 1;
+    ct[C_NINIT] = n_init;
+    ct[C_NSEP] = n_sep;
+    ct[C_SEPHEAD] = head;
+    ct[C_NPAST] = n_past;
+    ct[C_NLOCAL] = n_local;
+    ct[C_LOCALHEAD] = lhead;
+  }
+}
+
+// The held slots as one virtual range: Initial, Separator, Past, Local.
+struct Held {
+  int n_init, n_sep, n_past, n_local;
+  __device__ int count() const { return n_init + n_sep + n_past + n_local; }
+};
+
+__device__ inline int held_slot(const StreamArgs& p, const Held& h, int v) {
+  if (v < h.n_init) return v;
+  v -= h.n_init;
+  if (v < h.n_sep) return p.a + v;
+  v -= h.n_sep;
+  if (v < h.n_past) return p.a + p.s + v;
+  v -= h.n_past;
+  return p.a + p.s + p.P + v;
+}
+
+// Partial softmax of the group's queries over 64 held slots: (m, l, o) per
+// query head in base 2.  Thread (slot r, quarter qq) for the logits, thread
+// (column, half of the slots) for the weighted values.
+__global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
+  __shared__ float qs[MAX_G][128];
+  __shared__ float ps[MAX_G][SPLIT];
+  __shared__ float mrow[MAX_G], lrow[MAX_G];
+  __shared__ float ohalf[MAX_G][128];
+  const int tid = threadIdx.x;
+  const int bg = blockIdx.x / p.n_split, spl = blockIdx.x % p.n_split;
+  const int b = bg / p.h_kv, g = bg % p.h_kv;
+  const int* ct = p.ctrl + b * 8;
+  Held h;
+  h.n_init = ct[C_NINIT];
+  h.n_sep = ct[C_NSEP];
+  h.n_past = ct[C_NPAST];
+  h.n_local = ct[C_NLOCAL];
+  const int nv = h.count();
+  const int v0 = spl * SPLIT;
+  const int nslot = max(0, min(SPLIT, nv - v0));
+  const char* K = p.kc + ((int64_t)b * p.h_kv + g) * p.c * 256;
+  const char* V = p.vc + ((int64_t)b * p.h_kv + g) * p.c * 256;
+  for (int e = tid; e < p.group * 128; e += 256)
+    qs[e >> 7][e & 127] = p.qrot[((int64_t)b * p.h_q + g * p.group + (e >> 7)) * 128 + (e & 127)];
+  __syncthreads();
+  // logits
+  {
+    const int r = tid >> 2, qq = tid & 3;
+    float kx[32];
+    const bool ok = r < nslot;
+    const int slot = ok ? held_slot(p, h, v0 + r) : 0;
+    const uint4* kp = reinterpret_cast<const uint4*>(K + (int64_t)slot * 256 + qq * 64);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint4 x = ok ? kp[e] : make_uint4(0, 0, 0, 0);
+      const unsigned xs[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        kx[8 * e + 2 * f] = bf2f((u16)(xs[f] & 0xffffu));
+        kx[8 * e + 2 * f + 1] = bf2f((u16)(xs[f] >> 16));
+      }
+    }
+    for (int gq = 0; gq < p.group; ++gq) {
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) acc = fmaf(kx[e], qs[gq][qq * 32 + e], acc);
+      acc += __shfl_xor(acc, 1, 4);
+      acc += __shfl_xor(acc, 2, 4);
+      if (qq == 0) ps[gq][r] = ok ? acc : -__builtin_huge_valf();
+    }
+  }
+  __syncthreads();
+  // softmax pieces: wave gq % 4 handles query head gq
+  {
+    const int lane = tid & 63, wv = tid >> 6;
+    for (int gq = wv; gq < p.group; gq += 4) {
+      const float x = ps[gq][lane];
+      float m = x;
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+      const float e = (lane < nslot) ? __builtin_amdgcn_exp2f(x - m) : 0.f;
+      float l = e;
+      for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+      ps[gq][lane] = e;
+      if (lane == 0) {
+        mrow[gq] = nslot > 0 ? m : -__builtin_huge_valf();
+        lrow[gq] = l;
+      }
+    }
+  }
+  __syncthreads();
+  // weighted values
+  {
+    const int col = tid & 127, hh = tid >> 7;
+    float acc[MAX_G];
+#pragma unroll
+    for (int gq = 0; gq < MAX_G; ++gq) acc[gq] = 0.f;
+    for (int r = hh * 32; r < min(nslot, hh * 32 + 32); ++r) {
+      const int slot = held_slot(p, h, v0 + r);
+      const float x = bf2f(reinterpret_cast<const u16*>(V + (int64_t)slot * 256)[col]);
+#pragma unroll
+      for (int gq = 0; gq < MAX_G; ++gq)
+        if (gq < p.group) acc[gq] = fmaf(ps[gq][r], x, acc[gq]);
+    }
+    if (hh == 1)
+      for (int gq = 0; gq < p.group; ++gq) ohalf[gq][col] = acc[gq];
+    __syncthreads();
+    if (hh == 0) {
+      for (int gq = 0; gq < p.group; ++gq) {
+        const int hq = g * p.group + gq;
+        float* dst = p.part + (((int64_t)b * p.h_q + hq) * p.n_split + spl) * (128 + 2);
+        dst[2 + col] = acc[gq] + ohalf[gq][col];
+        if (col == 0) {
+          dst[0] = mrow[gq];
+          dst[1] = lrow[gq];
+        }
+      }
+    }
+  }
+}
+
+// o = sum_i 2^(m_i - m) o_i / sum_i 2^(m_i - m) l_i over the splits.
+__global__ __launch_bounds__(128) void decode_combine(StreamArgs p) {
+  const int row = blockIdx.x;  // b * h_q + hq
+  const int col = threadIdx.x;
+  const float* pr = p.part + (int64_t)row * p.n_split * (128 + 2);
+  float m = -__builtin_huge_valf();
+  for (int i = 0; i < p.n_split; ++i) m = fmaxf(m, pr[i * 130]);
+  float l = 0.f, acc = 0.f;
+  for (int i = 0; i < p.n_split; ++i) {
+    const float mi = pr[i * 130];
+    if (mi == -__builtin_huge_valf()) continue;
+    const float f = __builtin_amdgcn_exp2f(mi - m);
+    l = fmaf(pr[i * 130 + 1], f, l);
+    acc = fmaf(pr[i * 130 + 2 + col], f, acc);
+  }
+  p.o[(int64_t)row * 128 + col] = f2bf(acc / l);
+  if (p.lse != nullptr && col == 0) p.lse[row] = (m + __log2f(l)) * 0.6931471805599453f;
+}
+
+__global__ void stream_zero(int* ctrl, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) ctrl[i] = 0;
+}
+
+}  // namespace
+
+StreamLayout stream_layout(const sa_stream_cfg_t& cfg) {
+  StreamLayout L;
+  const int64_t rows = (int64_t)cfg.batch * cfg.h_kv * cfg.c;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = align_up(off + bytes, 256);
+    return o;
+  };
+  L.k = take(rows * cfg.d * 2);
+  L.v = take(rows * cfg.d * 2);
+  L.pos = take((int64_t)cfg.batch * cfg.c * 4);
+  L.flag = take((int64_t)cfg.batch * cfg.c);
+  L.ctrl = take((int64_t)cfg.batch * 8 * 4);
+  L.total = off;
+  L.n_split = (int)ceil_div(cfg.c, SPLIT);
+  L.ws_qrot = 0;
+  L.ws_part = align_up((int64_t)cfg.batch * cfg.h_q * cfg.d * 4, 256);
+  L.ws_total = L.ws_part + (int64_t)cfg.batch * cfg.h_q * L.n_split * (cfg.d + 2) * 4;
+  return L;
+}
+
+hipError_t launch_stream_reset(const sa_stream_cfg_t& cfg, void* state, hipStream_t s) {
+  const StreamLayout L = stream_layout(cfg);
+  int* ctrl = reinterpret_cast<int*>(static_cast<char*>(state) + L.ctrl);
+  const int n = cfg.batch * 8;
+  hipLaunchKernelGGL(stream_zero, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, ctrl, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const sa_stream_cfg_t& cfg, void* state, const void* q, const void* k,
+                              const void* v, const uint8_t* is_sep, void* o, float* lse, void* ws,
+                              const ThetaTable& theta, hipStream_t s) {
+  const StreamLayout L = stream_layout(cfg);
+  char* st = static_cast<char*>(state);
+  char* w = static_cast<char*>(ws);
+  StreamArgs p;
+  memset(&p, 0, sizeof(p));
+  p.kc = st + L.k;
+  p.vc = st + L.v;
+  p.pos = reinterpret_cast<int*>(st + L.pos);
+  p.flag = reinterpret_cast<unsigned char*>(st + L.flag);
+  p.ctrl = reinterpret_cast<int*>(st + L.ctrl);
+  p.q = static_cast<const u16*>(q);
+  p.k = static_cast<const u16*>(k);
+  p.v = static_cast<const u16*>(v);
+  p.is_sep = is_sep;
+  p.qrot = reinterpret_cast<float*>(w + L.ws_qrot);
+  p.part = reinterpret_cast<float*>(w + L.ws_part);
+  p.o = static_cast<u16*>(o);
+  p.lse = lse;
+  p.B = cfg.batch;
+  p.h_q = cfg.h_q;
+  p.h_kv = cfg.h_kv;
+  p.d = cfg.d;
+  p.a = cfg.a;
+  p.s = cfg.s;
+  p.w = cfg.w;
+  p.c = cfg.c;
+  p.P = cfg.c - cfg.a - cfg.s - cfg.w;
+  p.group = cfg.h_q / cfg.h_kv;
+  p.rotate = cfg.rope == SA_ROPE_HALF ? 1 : 0;
+  p.n_split = L.n_split;
+  p.scale_log2 = cfg.scale * 1.4426950408889634f;
+  p.theta = theta;
+  hipLaunchKernelGGL(stream_insert, dim3((unsigned)(cfg.batch * cfg.h_kv)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(stream_ctrl, dim3((unsigned)cfg.batch), dim3(64), 0, s, p);
+  hipLaunchKernelGGL(decode_attn, dim3((unsigned)(cfg.batch * cfg.h_kv * L.n_split)), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(decode_combine, dim3((unsigned)(cfg.batch * cfg.h_q)), dim3(128), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace sa

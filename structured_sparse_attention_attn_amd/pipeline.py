@@ -10,9 +10,10 @@ from typing import Optional
 import torch
 
 from . import (SA_MASK_LAMBDA, SA_MASK_SEGMENT, SA_MASK_SEPLLM, bwd_args, fwd_args, mask,
-               sa_bwd_workspace_bytes, sa_fwd_workspace_bytes, sa_plan_bytes,
-               sa_topk_workspace_bytes, sparse_attn_bwd, sparse_attn_fwd, sparse_attn_plan,
-               sparse_attn_segment_carry, topk_retrieve)
+               sa_bwd_workspace_bytes, sa_decode_workspace_bytes, sa_fwd_workspace_bytes,
+               sa_plan_bytes, sa_stream_layout, sa_stream_state_bytes, sa_topk_workspace_bytes,
+               sparse_attn_bwd, sparse_attn_decode_step, sparse_attn_fwd, sparse_attn_plan,
+               sparse_attn_segment_carry, sparse_attn_stream_reset, stream_cfg, topk_retrieve)
 
 KINDS = {"sepllm": SA_MASK_SEPLLM, "lambda": SA_MASK_LAMBDA, "segment": SA_MASK_SEGMENT}
 
@@ -160,4 +161,37 @@ class SegmentRunner:
         self.cur ^= 1
         self.P = nxt
         return o
+
+
+class StreamDecoder:
+    """Decode with the generation-time cache (Initial, Separator, Local, Past) for a batch
+    of sequences: one state buffer and one workspace, both device memory."""
+
+    def __init__(self, batch, h_q, h_kv, d, a, s, w, c, *, rope_base=None, scale=None,
+                 device: str = "cuda"):
+        self.cfg = stream_cfg(batch, h_q, h_kv, d, a, s, w, c, rope_base=rope_base, scale=scale)
+        self.state = torch.empty(sa_stream_state_bytes(self.cfg), dtype=torch.uint8, device=device)
+        self.ws = torch.empty(sa_decode_workspace_bytes(self.cfg), dtype=torch.uint8, device=device)
+        self.layout = sa_stream_layout(self.cfg)
+        self.reset()
+
+    def reset(self) -> None:
+        sparse_attn_stream_reset(self.cfg, self.state)
+
+    def step(self, q, k, v, is_sep, o=None, lse=None):
+        o = torch.empty_like(q) if o is None else o
+        sparse_attn_decode_step(self.cfg, self.state, q, k, v, is_sep, o, self.ws, lse=lse)
+        return o
+
+    def held(self, b: int):
+        """Token indices sequence b's cache holds (reads the state back; for inspection)."""
+        c, a, s_, w = self.cfg.c, self.cfg.a, self.cfg.s, self.cfg.w
+        P = c - a - s_ - w
+        st = self.state.cpu()
+        ctrl = st[self.layout[4]:self.layout[4] + self.cfg.batch * 32].view(torch.int32).view(-1, 8)[b]
+        pos = st[self.layout[2]:self.layout[2] + self.cfg.batch * c * 4].view(torch.int32).view(-1, c)[b]
+        n_init, n_sep, n_past, n_local = (int(ctrl[i]) for i in (1, 2, 4, 5))
+        slots = (list(range(n_init)) + list(range(a, a + n_sep)) + list(range(a + s_, a + s_ + n_past))
+                 + list(range(a + s_ + P, a + s_ + P + n_local)))
+        return sorted(int(pos[x]) for x in slots)
 

@@ -543,3 +543,42 @@ def test_workload5_backward_sampled(sa):
 
 def test_workload6_backward_sampled(sa):
     _workload_bwd_parity(sa, 6, dq_heads=[0], n_random=64, key_block=505, dk_kv_head=0)
+
+
+# Streaming decode with the generation-time cache (SepLLM page, part 6.2), against the
+# oracle's closed-form held set and decode attention, every step.
+STREAM_CASES = [
+    dict(B=2, h_q=8, h_kv=2, a=4, s=8, w=16, c=60, n=300, p=0.3, rope=10000.0),
+    dict(B=1, h_q=4, h_kv=1, a=4, s=64, w=128, c=324, n=700, p=0.1, rope=10000.0),
+    dict(B=1, h_q=2, h_kv=2, a=0, s=1, w=1, c=3, n=60, p=0.5, rope=None),
+    dict(B=1, h_q=8, h_kv=1, a=3, s=4, w=6, c=30, n=200, p=1.0, rope=500000.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(STREAM_CASES)))
+def test_stream_decode(sa, case):
+    from structured_sparse_attention_attn_amd.pipeline import StreamDecoder
+    cfg = STREAM_CASES[case]
+    B, hq, hkv, d = cfg["B"], cfg["h_q"], cfg["h_kv"], 128
+    log(f"stream decode {case}: {cfg}")
+    q, k, v, flags = W.make_decode_stream(B, hq, hkv, d, cfg["n"], seed=1300 + case, p_sep=cfg["p"])
+    dec = StreamDecoder(B, hq, hkv, d, cfg["a"], cfg["s"], cfg["w"], cfg["c"], rope_base=cfg["rope"])
+    scale = d ** -0.5
+    group = hq // hkv
+    lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
+    errs = []
+    for t in range(cfg["n"]):
+        o = dec.step(q[t].cuda(), k[t].cuda(), v[t].cuda(), flags[t].cuda(), lse=lse)
+        torch.cuda.synchronize()
+        for b in range(B):
+            fl = flags[:t + 1, b].numpy()
+            toks = O.stream_cache_tokens(t, fl, cfg["a"], cfg["s"], cfg["w"], cfg["c"])
+            if t % 7 == 0 or t == cfg["n"] - 1:
+                assert dec.held(b) == toks.tolist(), (t, b)
+            ro = np.zeros((hq, d))
+            rl = np.zeros(hq)
+            for h in range(hq):
+                ro[h], rl[h] = O.decode_attention(to64(q[t, b, h]), to64(k[:t + 1, b, h // group]),
+                                                  to64(v[:t + 1, b, h // group]), t, toks, cfg["rope"], scale)
+            errs.append(compare(to64(o[b]), ro, to64(lse[b]), rl, "bf16", nkeys=np.full(hq, len(toks))))
+    log(f"  max-abs {max(e[0] for e in errs):.3e}, lse {max(e[2] for e in errs):.3e}")

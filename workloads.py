@@ -153,6 +153,19 @@ def make_segment_stream(n_heads: int, seg_len: int, d: int, n_segments: int, see
     return out
 
 
+def make_decode_stream(batch: int, h_q: int, h_kv: int, d: int, n_steps: int, seed: int,
+                       p_sep: float, dtype=torch.bfloat16):
+    """Per-step raw q [n, B, h_q, d], k, v [n, B, h_kv, d] (fp32 randn in that order, rounded to
+    dtype) and i.i.d. Bernoulli(p_sep) separator flags uint8 [n, B] from seed + 7."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = _randn((n_steps, batch, h_q, d), g).to(dtype)
+    k = _randn((n_steps, batch, h_kv, d), g).to(dtype)
+    v = _randn((n_steps, batch, h_kv, d), g).to(dtype)
+    gf = torch.Generator("cpu").manual_seed(seed + 7)
+    flags = (torch.rand((n_steps, batch), generator=gf) < p_sep).to(torch.uint8)
+    return q, k, v, flags
+
+
 def make_pool_inputs(n_heads: int, pool_len: int, d: int, seed: int, dtype=torch.bfloat16):
     """Scoring queries [n_heads,d] and pool keys/values [n_heads,pool_len,d] for top-k tests."""
     g = torch.Generator("cpu").manual_seed(seed)
