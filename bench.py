@@ -164,6 +164,54 @@ def backward_timing(sa_mod, sa, q, k, v, o, lse, wl, steps, torch):
     return e0.elapsed_time(e1) / steps, need
 
 
+def decode_timing(steps, torch, batch=64, graph=False):
+    """Streaming decode with the generation-time cache (SepLLM page, part 6.2) for a
+    Llama-3-8B-shaped layer (32 query heads on 8 kv heads, d = 128, RoPE 500000): a = 4,
+    s = 64, w = 128, c = 324 (the page's PG19 setting s = 64, c = 324).  The cache is run
+    to its steady state (several compressions) untimed, then `steps` decode steps are timed.
+    Bytes per step: the held K and V rows read once, plus the new rows, queries and
+    outputs."""
+    import workloads as W
+    from structured_sparse_attention_attn_amd.pipeline import StreamDecoder
+    B, hq, hkv, d = batch, 32, 8, 128
+    a, s, w, c = 4, 64, 128, 324
+    dec = StreamDecoder(B, hq, hkv, d, a, s, w, c, rope_base=500000.0)
+    q, k, v, flags = W.make_decode_stream(B, hq, hkv, d, 1, seed=7000, p_sep=0.06)
+    q, k, v = q[0].cuda(), k[0].cuda(), v[0].cuda()
+    fl = (torch.arange(B) % 16 == 0).to(torch.uint8).cuda()  # every 16th sequence sees a separator
+    o = torch.empty_like(q)
+    for _ in range(600):
+        dec.step(q, k, v, fl, o=o)
+    torch.cuda.synchronize()
+    held = [len(dec.held(b)) for b in range(B)]
+    run = (lambda: dec.step(q, k, v, fl, o=o))
+    g = None
+    if graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            run()
+        run = g.replay
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = (sum(held) * hkv * 2 * d * 2 + B * (2 * hq + 2 * hkv) * d * 2)
+    return {"config": {"batch": B, "h_q": hq, "h_kv": hkv, "head_dim": d, "a": a, "s": s, "w": w, "c": c,
+                       "rope_base": 500000.0},
+            "graph": graph, "ms_per_step": round(ms, 5), "tokens_per_s": round(B / (ms * 1e-3), 1),
+            "held_slots_mean": round(sum(held) / B, 1),
+            "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_per_step": nbytes}
+
+
 def source_sha(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -234,6 +282,8 @@ def main():
                     help="skip the dense bf16 GEMM reference measurement")
     ap.add_argument("--backward", type=int, default=0,
                     help="also time the backward over this many steps (0: skip)")
+    ap.add_argument("--decode", type=int, default=0,
+                    help="also time this many streaming decode steps (0: skip)")
     ap.add_argument("--segments", type=int, default=8,
                     help="segment workload: also run this many consecutive segments (0: skip)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -384,6 +434,9 @@ def main():
                            "frac": round(bflops / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                            "workspace_bytes": bws,
                            "note": "2.5x the forward's effective flops (5 products per pair vs 2)"}
+    if args.decode > 0:
+        out["decode"] = decode_timing(args.decode, torch)
+        out["decode_graph"] = decode_timing(args.decode, torch, graph=True)
     if wl.mode == "segment" and args.segments > 0:
         out["multi_segment"] = multi_segment(wl, inp, args.segments, torch)
     if not args.no_gemm_ceiling:

@@ -13,9 +13,10 @@
 //
 // Per step: stream_insert (one work group per (sequence, kv head): the moved
 // and compressed rows, the new key and value, the rotated queries), then
-// stream_ctrl (one wave per sequence: token index and separator flag of each
-// slot, the counters), then decode_attn (split over slots: partial softmax
-// per 64 slots) and decode_combine.
+// decode_attn (split over slots: partial softmax per 64 slots, over the held
+// ranges the step leaves) and decode_combine (the splits merged; then one
+// work group per sequence records each slot's token index and separator flag
+// and advances the counters).
 #include "sa_common.h"
 
 namespace sa {
@@ -205,12 +206,11 @@ __global__ __launch_bounds__(256) void stream_insert(StreamArgs p) {
   }
 }
 
-// Token index, flag and counters of each sequence after the step (one wave).
-__global__ __launch_bounds__(64) void stream_ctrl(StreamArgs p) {
-  __shared__ int list_src[4096];
-  __shared__ int list_dst[4096];
-  const int lane = threadIdx.x;
-  const int b = blockIdx.x;
+// Token index, flag and counters of sequence b after the step.  Called by
+// every thread of a work group (its barriers are uniform); wave 0 works.
+__device__ inline void update_ctrl(const StreamArgs& p, int b, int* list_src, int* list_dst) {
+  const int lane = threadIdx.x & 63;
+  const bool w0 = threadIdx.x < 64;
   int* ct = p.ctrl + b * 8;
   const StepPlan sp = plan_step(p, ct);
   int* pos = p.pos + (int64_t)b * p.c;
@@ -218,26 +218,27 @@ __global__ __launch_bounds__(64) void stream_ctrl(StreamArgs p) {
   int n_sep = ct[C_NSEP], head = ct[C_SEPHEAD], n_past = ct[C_NPAST];
   int n_local = ct[C_NLOCAL], lhead = ct[C_LOCALHEAD], n_init = ct[C_NINIT];
   if (sp.compress) {
-    int n_new;
-    const int n = compress_list(p, b, ct, sp, lane, list_src, list_dst, &n_new);
+    int n_new = 0, n = 0;
+    if (w0) n = compress_list(p, b, ct, sp, lane, list_src, list_dst, &n_new);
     __syncthreads();
-    for (int r = lane; r < n; r += 64) {
-      pos[list_dst[r]] = pos[list_src[r]];
-      fl[list_dst[r]] = fl[list_src[r]];
-    }
+    if (w0)
+      for (int r = lane; r < n; r += 64) {
+        pos[list_dst[r]] = pos[list_src[r]];
+        fl[list_dst[r]] = fl[list_src[r]];
+      }
     __syncthreads();
     head = (head + max(0, n_sep + n_new - p.s)) % p.s;
     n_sep = min(p.s, n_sep + n_new);
     n_past = 0;
   } else if (sp.evict) {
-    if (lane == 0) {
+    if (threadIdx.x == 0) {
       pos[p.a + p.s + n_past] = pos[sp.ms];
       fl[p.a + p.s + n_past] = fl[sp.ms];
     }
     n_past += 1;
   }
   __syncthreads();
-  if (lane == 0) {
+  if (threadIdx.x == 0) {
     if (sp.t < p.a) {
       n_init = sp.t + 1;
     } else if (!sp.evict) {
@@ -274,41 +275,81 @@ __device__ inline int held_slot(const StreamArgs& p, const Held& h, int v) {
 }
 
 // Partial softmax of the group's queries over 64 held slots: (m, l, o) per
-// query head in base 2.  Thread (slot r, quarter qq) for the logits, thread
-// (column, half of the slots) for the weighted values.
+// query head in base 2.  Every K and V byte of the slots is requested at the
+// start: thread (slot r, quarter qq) holds a quarter of r's key for the
+// logits; thread (slot group sg, column chunk cc) holds columns 8 cc .. +7 of
+// the values of slots 4 sg .. 4 sg + 3 for the weighted sum, reduced over the
+// 16 slot groups by shuffles within a wave and LDS across the 4 waves.
 __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
   __shared__ float qs[MAX_G][128];
   __shared__ float ps[MAX_G][SPLIT];
   __shared__ float mrow[MAX_G], lrow[MAX_G];
-  __shared__ float ohalf[MAX_G][128];
-  const int tid = threadIdx.x;
+  __shared__ float ored[4][MAX_G][128];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bg = blockIdx.x / p.n_split, spl = blockIdx.x % p.n_split;
   const int b = bg / p.h_kv, g = bg % p.h_kv;
+  // the held ranges after this step, from the counters before it (they are
+  // updated by decode_combine, after every read of them in this step)
+  __shared__ int n_new_s;
   const int* ct = p.ctrl + b * 8;
+  const StepPlan sp = plan_step(p, ct);
   Held h;
   h.n_init = ct[C_NINIT];
   h.n_sep = ct[C_NSEP];
   h.n_past = ct[C_NPAST];
   h.n_local = ct[C_NLOCAL];
+  if (sp.t < p.a) h.n_init = sp.t + 1;
+  else if (!sp.evict) h.n_local += 1;
+  if (sp.compress) {
+    if (wv == 0) {
+      const unsigned char* fl = p.flag + (int64_t)b * p.c;
+      int n_new = 0;
+      for (int i0 = 0; i0 < p.P; i0 += 64) {
+        const int i = i0 + lane;
+        const bool f = i < p.P && fl[i < sp.n_past ? p.a + p.s + i : sp.ms] != 0;
+        n_new += __popcll(__ballot(f));
+      }
+      if (lane == 0) n_new_s = n_new;
+    }
+    __syncthreads();
+    h.n_sep = min(p.s, h.n_sep + n_new_s);
+    h.n_past = 0;
+  } else if (sp.evict) {
+    h.n_past += 1;
+  }
   const int nv = h.count();
   const int v0 = spl * SPLIT;
   const int nslot = max(0, min(SPLIT, nv - v0));
   const char* K = p.kc + ((int64_t)b * p.h_kv + g) * p.c * 256;
   const char* V = p.vc + ((int64_t)b * p.h_kv + g) * p.c * 256;
+  // loads
+  const int r = tid >> 2, qq = tid & 3;
+  const bool kok = r < nslot;
+  uint4 kx4[4];
+  {
+    const int slot = kok ? held_slot(p, h, v0 + r) : 0;
+    const uint4* kp = reinterpret_cast<const uint4*>(K + (int64_t)slot * 256 + qq * 64);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kx4[e] = kok ? kp[e] : make_uint4(0, 0, 0, 0);
+  }
+  const int sg = tid >> 4, cc = tid & 15;
+  uint4 vx4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = 4 * sg + i;
+    const bool ok = rr < nslot;
+    const int slot = ok ? held_slot(p, h, v0 + rr) : 0;
+    vx4[i] = ok ? *reinterpret_cast<const uint4*>(V + (int64_t)slot * 256 + cc * 16) : make_uint4(0, 0, 0, 0);
+  }
   for (int e = tid; e < p.group * 128; e += 256)
     qs[e >> 7][e & 127] = p.qrot[((int64_t)b * p.h_q + g * p.group + (e >> 7)) * 128 + (e & 127)];
   __syncthreads();
   // logits
   {
-    const int r = tid >> 2, qq = tid & 3;
     float kx[32];
-    const bool ok = r < nslot;
-    const int slot = ok ? held_slot(p, h, v0 + r) : 0;
-    const uint4* kp = reinterpret_cast<const uint4*>(K + (int64_t)slot * 256 + qq * 64);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint4 x = ok ? kp[e] : make_uint4(0, 0, 0, 0);
-      const unsigned xs[4] = {x.x, x.y, x.z, x.w};
+      const unsigned xs[4] = {kx4[e].x, kx4[e].y, kx4[e].z, kx4[e].w};
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
         kx[8 * e + 2 * f] = bf2f((u16)(xs[f] & 0xffffu));
@@ -321,60 +362,74 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
       for (int e = 0; e < 32; ++e) acc = fmaf(kx[e], qs[gq][qq * 32 + e], acc);
       acc += __shfl_xor(acc, 1, 4);
       acc += __shfl_xor(acc, 2, 4);
-      if (qq == 0) ps[gq][r] = ok ? acc : -__builtin_huge_valf();
+      if (qq == 0) ps[gq][r] = kok ? acc : -__builtin_huge_valf();
     }
   }
   __syncthreads();
   // softmax pieces: wave gq % 4 handles query head gq
-  {
-    const int lane = tid & 63, wv = tid >> 6;
-    for (int gq = wv; gq < p.group; gq += 4) {
-      const float x = ps[gq][lane];
-      float m = x;
-      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-      const float e = (lane < nslot) ? __builtin_amdgcn_exp2f(x - m) : 0.f;
-      float l = e;
-      for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
-      ps[gq][lane] = e;
-      if (lane == 0) {
-        mrow[gq] = nslot > 0 ? m : -__builtin_huge_valf();
-        lrow[gq] = l;
-      }
+  for (int gq = wv; gq < p.group; gq += 4) {
+    const float x = ps[gq][lane];
+    float m = x;
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float e = (lane < nslot) ? __builtin_amdgcn_exp2f(x - m) : 0.f;
+    float l = e;
+    for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+    ps[gq][lane] = e;
+    if (lane == 0) {
+      mrow[gq] = nslot > 0 ? m : -__builtin_huge_valf();
+      lrow[gq] = l;
     }
   }
   __syncthreads();
-  // weighted values
-  {
-    const int col = tid & 127, hh = tid >> 7;
-    float acc[MAX_G];
+  // weighted values: this thread's 4 slots x 8 columns, then the reductions
+  float vf[4][8];
 #pragma unroll
-    for (int gq = 0; gq < MAX_G; ++gq) acc[gq] = 0.f;
-    for (int r = hh * 32; r < min(nslot, hh * 32 + 32); ++r) {
-      const int slot = held_slot(p, h, v0 + r);
-      const float x = bf2f(reinterpret_cast<const u16*>(V + (int64_t)slot * 256)[col]);
+  for (int i = 0; i < 4; ++i) {
+    const unsigned xs[4] = {vx4[i].x, vx4[i].y, vx4[i].z, vx4[i].w};
 #pragma unroll
-      for (int gq = 0; gq < MAX_G; ++gq)
-        if (gq < p.group) acc[gq] = fmaf(ps[gq][r], x, acc[gq]);
+    for (int f = 0; f < 4; ++f) {
+      vf[i][2 * f] = bf2f((u16)(xs[f] & 0xffffu));
+      vf[i][2 * f + 1] = bf2f((u16)(xs[f] >> 16));
     }
-    if (hh == 1)
-      for (int gq = 0; gq < p.group; ++gq) ohalf[gq][col] = acc[gq];
-    __syncthreads();
-    if (hh == 0) {
-      for (int gq = 0; gq < p.group; ++gq) {
-        const int hq = g * p.group + gq;
-        float* dst = p.part + (((int64_t)b * p.h_q + hq) * p.n_split + spl) * (128 + 2);
-        dst[2 + col] = acc[gq] + ohalf[gq][col];
-        if (col == 0) {
-          dst[0] = mrow[gq];
-          dst[1] = lrow[gq];
-        }
-      }
+  }
+  for (int gq = 0; gq < p.group; ++gq) {
+    float acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float pw = ps[gq][4 * sg + i];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = fmaf(pw, vf[i][c], acc[c]);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      acc[c] += __shfl_xor(acc[c], 16);
+      acc[c] += __shfl_xor(acc[c], 32);
+    }
+    if (lane < 16) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) ored[wv][gq][cc * 8 + c] = acc[c];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < p.group * 128; e += 256) {
+    const int gq = e >> 7, col = e & 127;
+    const int hq = g * p.group + gq;
+    float* dst = p.part + (((int64_t)b * p.h_q + hq) * p.n_split + spl) * (128 + 2);
+    dst[2 + col] = ored[0][gq][col] + ored[1][gq][col] + ored[2][gq][col] + ored[3][gq][col];
+    if (col == 0) {
+      dst[0] = mrow[gq];
+      dst[1] = lrow[gq];
     }
   }
 }
 
-// o = sum_i 2^(m_i - m) o_i / sum_i 2^(m_i - m) l_i over the splits.
+// o = sum_i 2^(m_i - m) o_i / sum_i 2^(m_i - m) l_i over the splits; the work
+// group of each sequence's first query head then advances its counters.
 __global__ __launch_bounds__(128) void decode_combine(StreamArgs p) {
+  __shared__ int list_src[4096];
+  __shared__ int list_dst[4096];
   const int row = blockIdx.x;  // b * h_q + hq
   const int col = threadIdx.x;
   const float* pr = p.part + (int64_t)row * p.n_split * (128 + 2);
@@ -390,6 +445,7 @@ __global__ __launch_bounds__(128) void decode_combine(StreamArgs p) {
   }
   p.o[(int64_t)row * 128 + col] = f2bf(acc / l);
   if (p.lse != nullptr && col == 0) p.lse[row] = (m + __log2f(l)) * 0.6931471805599453f;
+  if (row % p.h_q == 0) update_ctrl(p, row / p.h_q, list_src, list_dst);
 }
 
 __global__ void stream_zero(int* ctrl, int n) {
@@ -465,7 +521,6 @@ hipError_t launch_decode_step(const sa_stream_cfg_t& cfg, void* state, const voi
   p.scale_log2 = cfg.scale * 1.4426950408889634f;
   p.theta = theta;
   hipLaunchKernelGGL(stream_insert, dim3((unsigned)(cfg.batch * cfg.h_kv)), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(stream_ctrl, dim3((unsigned)cfg.batch), dim3(64), 0, s, p);
   hipLaunchKernelGGL(decode_attn, dim3((unsigned)(cfg.batch * cfg.h_kv * L.n_split)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(decode_combine, dim3((unsigned)(cfg.batch * cfg.h_q)), dim3(128), 0, s, p);
   return hipGetLastError();
