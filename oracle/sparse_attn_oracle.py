@@ -56,6 +56,7 @@ __all__ = [
     "topk_scores", "topk_select", "pair_counts", "pair_count_total", "q0_closed_form",
     "alibi_slope", "q0_alibi_closed_form", "segmented_run", "attention_grad_rows",
     "attention_backward", "StreamCache", "stream_cache_tokens", "decode_attention",
+    "middle_scores", "attention_topk_middle",
 ]
 
 
@@ -708,4 +709,58 @@ def decode_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, t: int, tokens
     mu = s_.max()
     e = np.exp(s_ - mu)
     return (e @ vv) / e.sum(), mu + math.log(e.sum())
+
+
+# ----------------------------------------------------------------------------
+# LM-Infinite's optional top-k middle tokens (LM-Infinite page, section 方法)
+# ----------------------------------------------------------------------------
+
+def middle_scores(q: np.ndarray, k: np.ndarray, spec: MaskSpec, i: int, rope_base: Optional[float],
+                  scale: float):
+    """The middle tokens of query i, ``n_starting <= j < i - L`` (outside both
+    spans of the Lambda mask), and their logits at the capped distance L:
+    ``scale <R(L) q_i, k_j>`` (or ``scale <q_i, k_j>`` without RoPE).
+    Returns (j ascending, logits)."""
+    assert spec.mode == LAMBDA
+    j = np.arange(spec.n_s, max(spec.n_s, i - spec.L))
+    q = np.asarray(q, dtype=np.float64)
+    qi = q[i]
+    if rope_base:
+        qi = rotate(qi, float(spec.L) * rope_theta(q.shape[1], rope_base))
+    return j, scale * (np.asarray(k, dtype=np.float64)[j] @ qi)
+
+
+def attention_topk_middle(q: np.ndarray, k: np.ndarray, v: np.ndarray, rows: Sequence[int],
+                          spec: MaskSpec, rope_base: Optional[float], scale: float, k_mid: int):
+    """Lambda-mask attention with the k largest-logit middle tokens of each query
+    added to its key set (ties to the lower index); every key beyond the
+    window, selected middle tokens included, takes the capped distance L.
+    Returns O [len(rows), d], LSE and the selected indices [len(rows), <= k_mid]
+    (ascending)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    d = q.shape[1]
+    theta = rope_theta(d, rope_base) if rope_base else None
+    O = np.zeros((len(rows), v.shape[1]))
+    lse = np.zeros(len(rows))
+    sels = []
+    for r, i in enumerate(rows):
+        i = int(i)
+        jm, sm = middle_scores(q, k, spec, i, rope_base, scale)
+        sel = jm[topk_select(sm, min(k_mid, len(jm)))] if len(jm) else jm
+        sels.append(sel)
+        A = np.union1d(key_set(spec, i), sel)
+        delta = np.minimum(pos_q(spec, i) - pos_k(spec, A), spec.L)
+        if theta is None:
+            s_ = k[A] @ q[i]
+        else:
+            ang = delta.astype(np.float64)[:, None] * theta[None, :]
+            s_ = np.einsum("jd,jd->j", rotate(np.broadcast_to(q[i], (len(A), d)), ang), k[A])
+        s_ = s_ * scale
+        mu = s_.max()
+        e = np.exp(s_ - mu)
+        O[r] = (e @ v[A]) / e.sum()
+        lse[r] = mu + math.log(e.sum())
+    return O, lse, sels
 

@@ -44,6 +44,11 @@ Pins, by oracle function:
                         its mean over whole periods under the page's bound
                         (w+c+a+s)/2; decode output against torch SDPA on
                         explicitly rotated rows with a mask over the held set.
+  middle_scores / attention_topk_middle
+                        k at least the middle size: the capped realisation over
+                        the whole causal mask built in torch; the selection
+                        against heapq over pure-Python scores (exact ties);
+                        k = 0 equals the Lambda attention.
 """
 import heapq
 import json
@@ -763,3 +768,52 @@ def test_decode_attention_vs_sdpa():
         np.testing.assert_allclose(o, ref, rtol=0, atol=1e-12)
         ref_l = torch.logsumexp((qr @ kr.T * scale).masked_fill(~mask, -math.inf), dim=1).item()
         assert abs(lse - ref_l) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# LM-Infinite top-k middle tokens (LM-Infinite page, section 方法)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("base", [None, 10000.0])
+def test_topk_middle_all_selected_is_capped_causal(base):
+    # with k at least the middle size every j <= i is attended, each at min(i-j, L): the
+    # page's capped realisation over the whole causal mask, built here in torch
+    d, m, n_s, L = 32, 160, 5, 20
+    scale = d ** -0.5
+    q, k, v = rand(m, d), rand(m, d), rand(m, d)
+    spec = O.MaskSpec(O.LAMBDA, m, m, n_s=n_s, L=L)
+    o, lse, _ = O.attention_topk_middle(q, k, v, range(m), spec, base, scale, k_mid=m)
+    tq, tk = torch.from_numpy(q), torch.from_numpy(k)
+    i = torch.arange(m)[:, None]
+    j = torch.arange(m)[None, :]
+    if base:
+        qr = complex_rope(tq, torch.arange(m), base)
+        kr = complex_rope(tk, torch.arange(m), base)
+        qL = complex_rope(tq, torch.full((m,), L), base)
+        logits = torch.where(i - j > L, scale * (qL @ tk.T), scale * (qr @ kr.T))
+    else:
+        logits = scale * (tq @ tk.T)
+    logits = logits.masked_fill(j > i, -math.inf)
+    ref = torch.softmax(logits, dim=1) @ torch.from_numpy(v)
+    np.testing.assert_allclose(o, ref.numpy(), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, torch.logsumexp(logits, dim=1).numpy(), rtol=0, atol=1e-12)
+
+
+def test_topk_middle_selection_brute_force():
+    # the selected set is heapq's k largest of a pure-Python score list (lower index on ties),
+    # k = 0 leaves the Lambda attention unchanged
+    d, m, n_s, L, kk = 8, 90, 3, 10, 4
+    q = np.round(rand(m, d) * 4) / 4  # coarse values: exact ties occur
+    k = np.round(rand(m, d) * 4) / 4
+    v = rand(m, d)
+    spec = O.MaskSpec(O.LAMBDA, m, m, n_s=n_s, L=L)
+    _, _, sels = O.attention_topk_middle(q, k, v, range(m), spec, None, 1.0, kk)
+    for i in range(m):
+        cand = list(range(n_s, max(n_s, i - L)))
+        sc = {j: sum(float(q[i, c]) * float(k[j, c]) for c in range(d)) for j in cand}
+        best = sorted(heapq.nlargest(kk, cand, key=lambda j: (sc[j], -j)))
+        assert sels[i].tolist() == best, i
+    o0, l0, _ = O.attention_topk_middle(q, k, v, range(m), spec, 10000.0, 0.3, 0)
+    o1, l1 = O.attention_rows(q, k, v, range(m), spec, 10000.0, 0.3)
+    np.testing.assert_allclose(o0, o1, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(l0, l1, rtol=0, atol=1e-12)
