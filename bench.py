@@ -212,6 +212,34 @@ def decode_timing(steps, torch, batch=64, graph=False):
             "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_per_step": nbytes}
 
 
+def topk_middle_timing(sa, q, k, v, o, lse, wl, kmid, steps, torch):
+    """LM-Infinite top-k middle tokens on the Lambda layer's forward output: scoring
+    of every middle pair (n_starting <= j < i - L) on MFMA, per-query selection, merge."""
+    import numpy as np
+    from structured_sparse_attention_attn_amd import sparse_attn_topk_middle
+    B, h_q, n_q, _ = q.shape
+    sel = torch.empty((B, h_q, n_q, kmid), dtype=torch.int32, device="cuda")
+    score = torch.empty((B, h_q, n_q, kmid), dtype=torch.float32, device="cuda")
+    fa = sa.args(q, k, v, o, lse, wl.rope_base, wl.scale)
+    sparse_attn_topk_middle(sa.mask, fa, kmid, sel, score)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        sparse_attn_topk_middle(sa.mask, fa, kmid, sel, score)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    i = np.arange(n_q, dtype=np.int64)
+    mid_pairs = int(np.maximum(0, i - wl.L - wl.n_s).sum()) * h_q * B
+    flops = 2.0 * wl.d * mid_pairs  # one product per middle pair (the kernel issues two: q high, q low)
+    return {"k_mid": kmid, "ms": round(ms, 4), "middle_pairs": mid_pairs,
+            "effective_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+            "issued_tflops": round(2 * flops / (ms * 1e-3) / 1e12, 2),
+            "note": "scoring + selection + merge; o, lse rewritten in place (run after the timed forward steps)"}
+
+
 def source_sha(path):
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -282,6 +310,8 @@ def main():
                     help="skip the dense bf16 GEMM reference measurement")
     ap.add_argument("--backward", type=int, default=0,
                     help="also time the backward over this many steps (0: skip)")
+    ap.add_argument("--topk-middle", type=int, default=0,
+                    help="Lambda workloads: also time the top-k middle tokens with this k (0: skip)")
     ap.add_argument("--decode", type=int, default=0,
                     help="also time this many streaming decode steps (0: skip)")
     ap.add_argument("--segments", type=int, default=8,
@@ -434,6 +464,8 @@ def main():
                            "frac": round(bflops / (bms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                            "workspace_bytes": bws,
                            "note": "2.5x the forward's effective flops (5 products per pair vs 2)"}
+    if args.topk_middle > 0 and wl.mode == "lambda" and wl.alibi_exp is None:
+        out["topk_middle"] = topk_middle_timing(sa, q, k, v, o, lse, wl, args.topk_middle, 3, torch)
     if args.decode > 0:
         out["decode"] = decode_timing(args.decode, torch)
         out["decode_graph"] = decode_timing(args.decode, torch, graph=True)

@@ -275,6 +275,21 @@ int sparse_attn_decode_step(const sa_stream_cfg_t *cfg, void *state, size_t stat
  */
 int sa_stream_layout(const sa_stream_cfg_t *cfg, int64_t offsets[5]);
 
+/*
+ * LM-Infinite's optional top-k middle tokens (LM-Infinite page, section
+ * "method"), applied to the output of sparse_attn_fwd for a LAMBDA mask
+ * (bf16, d = 128, SA_ROPE_HALF or SA_ROPE_NONE): for every head and query i,
+ * the k_mid middle tokens n_starting <= j < i - L_pretrain with the largest
+ * logits scale <R(L) q_i, k_j> (ties to the lower j) join the key set, with
+ * that same logit.  args must be the forward's (raw q, k, v; its o and lse,
+ * which are rewritten in place to the extended attention).  sel int32 and
+ * score fp32 [batch, h_q, n_q, k_mid] receive the chosen j (ascending score
+ * order, -1 when a query has fewer middle tokens) and their base-2 logits.
+ * 1 <= k_mid <= 8.  Errors: SA_EINVAL, SA_EUNSUPPORTED, SA_EHIP.
+ */
+int sparse_attn_topk_middle(const sa_mask_t *m, const sa_fwd_args_t *args, int32_t k_mid,
+                            int32_t *sel, float *score, hipStream_t stream);
+
 /* Host only: bytes of device workspace topk_retrieve needs. */
 int sa_topk_workspace_bytes(int32_t n_heads, int32_t pool_len, size_t *bytes);
 

@@ -95,6 +95,8 @@ _lib.sa_decode_workspace_bytes.argtypes = [_CFGP, ctypes.POINTER(_sz)]
 _lib.sa_stream_layout.argtypes = [_CFGP, ctypes.POINTER(_i64)]
 _lib.sparse_attn_stream_reset.argtypes = [_CFGP, _vp, _sz, _vp]
 _lib.sparse_attn_decode_step.argtypes = [_CFGP, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.sparse_attn_topk_middle.argtypes = [_MASKP, _ARGSP, _i32, _vp, _vp, _vp]
+_lib.sparse_attn_topk_middle.restype = ctypes.c_int
 for _name in ("sa_stream_state_bytes", "sa_decode_workspace_bytes", "sa_stream_layout",
               "sparse_attn_stream_reset", "sparse_attn_decode_step"):
     getattr(_lib, _name).restype = ctypes.c_int
@@ -342,4 +344,10 @@ def sparse_attn_decode_step(cfg: sa_stream_cfg_t, state, q, k, v, is_sep, o, ws,
     _check(_lib.sparse_attn_decode_step(ctypes.byref(cfg), _ptr(state), state.numel(), _ptr(q), _ptr(k),
                                         _ptr(v), _ptr(is_sep), _ptr(o), _ptr(lse), _ptr(ws),
                                         ws.numel(), _stream(stream)))
+
+
+def sparse_attn_topk_middle(m: sa_mask_t, args: sa_fwd_args_t, k_mid: int, sel, score, stream=None) -> None:
+    """LM-Infinite top-k middle tokens on a forward's o and lse (see include/sparse_attn.h)."""
+    _check(_lib.sparse_attn_topk_middle(ctypes.byref(m), ctypes.byref(args), k_mid, _ptr(sel), _ptr(score),
+                                        _stream(stream)))
 

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsparse_attn.so")
 SOURCES = ["sa_api.cpp", "sa_plan.hip", "sa_rope.hip", "sa_fwd.hip", "sa_topk.hip", "sa_carry.hip",
-           "sa_bwd.hip", "sa_stream.hip"]
+           "sa_bwd.hip", "sa_stream.hip", "sa_mid.hip"]
 ARCH = "gfx950"
 
 

@@ -615,5 +615,22 @@ int sparse_attn_decode_step(const sa_stream_cfg_t* cfg, void* state, size_t stat
   return ok();
 }
 
+int sparse_attn_topk_middle(const sa_mask_t* m, const sa_fwd_args_t* a, int32_t k_mid, int32_t* sel,
+                            float* score, hipStream_t stream) {
+  int r = check_mask(m);
+  if (r != SA_OK) return r;
+  if ((r = check_args(m, a)) != SA_OK) return r;
+  if (m->kind != SA_MASK_LAMBDA) return fail(SA_EINVAL, "top-k middle tokens apply to the LAMBDA mask");
+  if (a->dtype != SA_BF16 || a->d != 128 || a->rope == SA_ALIBI)
+    return fail(SA_EUNSUPPORTED, "top-k middle tokens: bf16, d = 128, RoPE or none");
+  if (k_mid < 1 || k_mid > 8) return fail(SA_EINVAL, "k_mid must be in [1, 8] (got %d)", k_mid);
+  if (a->lse == nullptr || sel == nullptr || score == nullptr)
+    return fail(SA_EINVAL, "lse, sel and score must not be NULL");
+  if ((r = check_device()) != SA_OK) return r;
+  hipError_t e = sa::launch_topk_middle(*m, *a, k_mid, sel, score, stream);
+  if (e != hipSuccess) return fail(SA_EHIP, "top-k middle launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 }  // extern "C"
 

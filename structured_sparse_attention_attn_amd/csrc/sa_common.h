@@ -133,6 +133,9 @@ hipError_t launch_decode_step(const sa_stream_cfg_t& cfg, void* state, const voi
                               const void* v, const uint8_t* is_sep, void* o, float* lse, void* ws,
                               const ThetaTable& theta, hipStream_t s);
 
+hipError_t launch_topk_middle(const sa_mask_t& m, const sa_fwd_args_t& a, int kmid, int32_t* sel, float* score,
+                              hipStream_t s);
+
 hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const void* plan,
                       const sa_fwd_args_t& a, const sa_bwd_args_t& g, const RopeOut& ro,
                       const BwdWs& w, const ThetaTable& theta, hipStream_t s);

@@ -263,6 +263,24 @@ __device__ inline void add_alibi(const Unit& u, int qi, int hl, float m2, float 
   }
 }
 
+// Direct global -> LDS loads of a 64-row x 256-byte block into the swizzled
+// layout (16-byte chunk c of row r at chunk c ^ swzf(r & 15)): wave w moves
+// rows 16w .. 16w+15, four rows per instruction, each lane fetching the
+// logical chunk that lands in its slot.  Rows at or past `valid` repeat row
+// valid-1 (finite values, masked later).
+__device__ __attribute__((always_inline)) inline void dma_block(const char* base, int64_t stride, int valid,
+                                                                char* lds, int wid, int lane) {
+  const int lrow = lane >> 4;
+  const int lchunk = (lane & 15) ^ (lrow << 2);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = wid * 4 + j;
+    const int r = min(4 * i + lrow, valid - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)r * stride + ((lchunk ^ j) << 4)),
+                                     (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0, 0);
+  }
+}
+
 }  // namespace
 }  // namespace sa
 

@@ -13,7 +13,8 @@ from . import (SA_MASK_LAMBDA, SA_MASK_SEGMENT, SA_MASK_SEPLLM, bwd_args, fwd_ar
                sa_bwd_workspace_bytes, sa_decode_workspace_bytes, sa_fwd_workspace_bytes,
                sa_plan_bytes, sa_stream_layout, sa_stream_state_bytes, sa_topk_workspace_bytes,
                sparse_attn_bwd, sparse_attn_decode_step, sparse_attn_fwd, sparse_attn_plan,
-               sparse_attn_segment_carry, sparse_attn_stream_reset, stream_cfg, topk_retrieve)
+               sparse_attn_segment_carry, sparse_attn_stream_reset, sparse_attn_topk_middle, stream_cfg,
+               topk_retrieve)
 
 KINDS = {"sepllm": SA_MASK_SEPLLM, "lambda": SA_MASK_LAMBDA, "segment": SA_MASK_SEGMENT}
 
@@ -53,6 +54,15 @@ class SparseAttention:
         self.ensure_workspace(args)
         sparse_attn_fwd(self.mask, self.plan, args, self.ws)
         return o
+
+    def topk_middle(self, q, k, v, o, lse, k_mid, rope_base=None, scale=None):
+        """Adds each query's k_mid largest-logit middle tokens (LAMBDA masks) to the
+        forward's o and lse in place; returns the chosen indices and their base-2 logits."""
+        B, h_q, n_q, _ = q.shape
+        sel = torch.empty((B, h_q, n_q, k_mid), dtype=torch.int32, device=self.device)
+        score = torch.empty((B, h_q, n_q, k_mid), dtype=torch.float32, device=self.device)
+        sparse_attn_topk_middle(self.mask, self.args(q, k, v, o, lse, rope_base, scale), k_mid, sel, score)
+        return sel, score
 
     def backward(self, q, k, v, o, lse, dout, rope_base=None, scale=None, alibi_exp=None,
                  dq=None, dk=None, dv=None):

@@ -582,3 +582,98 @@ def test_stream_decode(sa, case):
                                                   to64(v[:t + 1, b, h // group]), t, toks, cfg["rope"], scale)
             errs.append(compare(to64(o[b]), ro, to64(lse[b]), rl, "bf16", nkeys=np.full(hq, len(toks))))
     log(f"  max-abs {max(e[0] for e in errs):.3e}, lse {max(e[2] for e in errs):.3e}")
+
+
+# LM-Infinite top-k middle tokens against the oracle.  The selection is decided by
+# floating point: indices must agree except where the oracle's score lies within the
+# scores' error band of the k-th best (either choice is then correct), and the GPU's
+# scores of its choices must match the oracle's within that band.
+MID_CASES = [
+    (dict(m=900, n_s=10, L=100), 8, 10000.0),
+    (dict(m=700, n_s=0, L=64, h_q=4, h_kv=1), 3, 10000.0),
+    (dict(m=300, n_s=10, L=0), 1, None),
+    (dict(m=200, n_s=10, L=250), 4, 10000.0),
+    (dict(m=600, n_s=70, L=130, batch=2), 5, 500000.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(MID_CASES)))
+def test_topk_middle(sa, case):
+    kw, kmid, rope = MID_CASES[case]
+    wl = W.small(W.LAMBDA, seed=700 + case, rope_base=rope, **kw)
+    log(f"topk middle {case}: {kw} k={kmid} rope={rope}")
+    inp = W.make_small_inputs(wl)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    sa_obj = device_mask(wl)
+    sa_obj.build_plan()
+    lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
+    o = sa_obj.forward(q, k, v, lse=lse, rope_base=wl.rope_base, scale=wl.scale)
+    sel, score = sa_obj.topk_middle(q, k, v, o, lse, kmid, rope_base=wl.rope_base, scale=wl.scale)
+    torch.cuda.synchronize()
+    spec = spec_of(wl)
+    group = wl.h_q // wl.h_kv
+    n_near = 0
+    for b in range(wl.batch):
+        for h in range(wl.h_q):
+            Q, K, V = to64(inp["q"][b, h]), to64(inp["k"][b, h // group]), to64(inp["v"][b, h // group])
+            ro, rl, rsel = O.attention_topk_middle(Q, K, V, range(wl.n_q), spec, wl.rope_base, wl.scale, kmid)
+            gsel = sel[b, h].cpu().numpy()
+            gsc = score[b, h].cpu().numpy().astype(np.float64) * math.log(2.0)
+            for i in range(wl.n_q):
+                jm, sm = O.middle_scores(Q, K, spec, i, wl.rope_base, wl.scale)
+                g = gsel[i][gsel[i] >= 0]
+                assert len(g) == min(kmid, len(jm)), (i, g)
+                if not len(jm):
+                    continue
+                sc = dict(zip(jm.tolist(), sm.tolist()))
+                kth = float(np.sort(sm)[::-1][len(g) - 1])
+                eps = 1e-3 * max(1.0, abs(kth))
+                for jj, gs in zip(gsel[i][:len(g)], gsc[i][:len(g)]):
+                    assert abs(gs - sc[int(jj)]) <= eps, (i, jj, gs, sc[int(jj)])
+                diff = set(g.tolist()) ^ set(rsel[i].tolist())
+                for jj in diff:
+                    assert abs(sc[jj] - kth) <= eps, (i, jj, sc[jj], kth)
+                n_near += len(diff) > 0
+            compare(to64(o[b, h]), ro, to64(lse[b, h]), rl, "bf16",
+                    nkeys=O.pair_counts(spec) + np.minimum(kmid, np.maximum(0, np.arange(wl.n_q) - wl.L - wl.n_s)))
+    log(f"  queries with a near-tie swap: {n_near}")
+
+
+def test_workload3_topk_middle_sampled(sa):
+    wl = W.WORKLOADS[3]
+    kmid = 8
+    log("workload 3 top-k middle: inputs")
+    inp = W.make_inputs(wl)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    sa_obj = device_mask(wl)
+    sa_obj.build_plan()
+    lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
+    o = sa_obj.forward(q, k, v, lse=lse, rope_base=wl.rope_base, scale=wl.scale)
+    sel, score = sa_obj.topk_middle(q, k, v, o, lse, kmid, rope_base=wl.rope_base, scale=wl.scale)
+    torch.cuda.synchronize()
+    spec = spec_of(wl)
+    r_ = np.random.default_rng(3)
+    rows = np.array(sorted(set(range(4090, 4230)) | set(range(wl.n_q - 64, wl.n_q))
+                           | set(r_.choice(np.arange(4200, wl.n_q), size=48, replace=False).tolist())))
+    for h in (0, 31):
+        log(f"workload 3 top-k middle: head {h}")
+        Q, K, V = to64(inp["q"][0, h]), to64(inp["k"][0, h]), to64(inp["v"][0, h])
+        ro, rl, rsel = O.attention_topk_middle(Q, K, V, rows, spec, wl.rope_base, wl.scale, kmid)
+        gsel = sel[0, h].cpu().numpy()
+        gsc = score[0, h].cpu().numpy().astype(np.float64) * math.log(2.0)
+        for r, i in enumerate(rows):
+            jm, sm = O.middle_scores(Q, K, spec, int(i), wl.rope_base, wl.scale)
+            g = gsel[i][gsel[i] >= 0]
+            assert len(g) == min(kmid, len(jm))
+            if not len(jm):
+                continue
+            sc = dict(zip(jm.tolist(), sm.tolist()))
+            kth = float(np.sort(sm)[::-1][len(g) - 1])
+            eps = 1e-3 * max(1.0, abs(kth))
+            for jj, gs in zip(gsel[i][:len(g)], gsc[i][:len(g)]):
+                assert abs(gs - sc[int(jj)]) <= eps
+            for jj in set(g.tolist()) ^ set(rsel[r].tolist()):
+                assert abs(sc[jj] - kth) <= eps
+        nk = O.pair_counts(spec)[rows] + np.minimum(kmid, np.maximum(0, rows - wl.L - wl.n_s))
+        compare(to64(o[0, h][torch.from_numpy(rows).cuda()]), ro, to64(lse[0, h][torch.from_numpy(rows).cuda()]),
+                rl, "bf16", nkeys=nk)
