@@ -19,13 +19,14 @@
 //   bwd_dq_bf16    query-major, the forward's work units per 128-query tile:
 //                  S^T = K Q^T, P = 2^(S - LSE log2 e), dP^T = V dO^T,
 //                  dS, then dQ^T += K^T dS^T (K^T by LDS transpose reads).
-//   bwd_dkdv_bf16  key-major: one work group per (batch, kv head, 64-key
-//                  group), the group being a dense key block, a chunk of 64
-//                  gathered separator rows or a block of capped keys.  It
-//                  visits every (tile, query head) that reads the group, 64
-//                  queries at a time: S = Q K^T, P, dP = dO V^T, dS, then
-//                  dV^T += dO^T P and dK^T += Q^T dS (transpose reads of the
-//                  query-side tiles).
+//   bwd_dkdv_bf16  key-major: one 8-wave work group per (batch, kv head,
+//                  128-key group), the group being two dense key blocks, two
+//                  chunks of 64 gathered separator rows or two blocks of
+//                  capped keys.  It visits every (tile, query head) that
+//                  reads the group, 64 queries at a time, the next chunk's
+//                  loads in flight while the current one computes: S = Q K^T,
+//                  P, dP = dO V^T, dS, then dV^T += dO^T P and
+//                  dK^T += Q^T dS (transpose reads of the query-side tiles).
 //   bwd_finish     per row: the inverse rotations, the separator and capped
 //                  contributions, the output dtype.
 #include <type_traits>
@@ -388,75 +389,99 @@ __device__ inline int find_item(const BwdArgs& p, int t, int blk) {
   return -1;
 }
 
+// One 64-row unit of a 128-key group (dense block, separator chunk or capped block).
+struct KeyUnit {
+  const char* kbase;
+  const char* vbase;
+  int64_t kstr, vstr;
+  int valid;       // rows held (0: the unit does not exist)
+  int key0;        // key index of row 0 (dense and capped units)
+  int idx;         // block / chunk index
+  float* dk_out;
+  float* dv_out;
+};
+
 template <bool ALIBI>
-__global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
-  __shared__ __attribute__((aligned(16))) char Kg[BLK_BYTES];  // the group's keys
-  __shared__ __attribute__((aligned(16))) char Vg[BLK_BYTES];  // and values
-  __shared__ __attribute__((aligned(16))) char Qc[BLK_BYTES];  // 64 queries of a tile
-  __shared__ __attribute__((aligned(16))) char Dc[BLK_BYTES];  // their dO rows
-  __shared__ __attribute__((aligned(16))) float LD[2][64];     // their lse * log2(e) and D
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p) {
+  // the group's 128 keys and values; two buffers of (64 queries, their dO rows,
+  // their lse * log2(e) and D), one filled while the other is read
+  __shared__ __attribute__((aligned(16))) char Kg[2 * BLK_BYTES];
+  __shared__ __attribute__((aligned(16))) char Vg[2 * BLK_BYTES];
+  __shared__ __attribute__((aligned(16))) char Qb0[BLK_BYTES];
+  __shared__ __attribute__((aligned(16))) char Db0[BLK_BYTES];
+  __shared__ __attribute__((aligned(16))) char Qb1[BLK_BYTES];
+  __shared__ __attribute__((aligned(16))) char Db1[BLK_BYTES];
+  __shared__ __attribute__((aligned(16))) float LD0[2][64];
+  __shared__ __attribute__((aligned(16))) float LD1[2][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
-  const int kw = wid & 1, qw = wid >> 1;
+  const int kw = wid & 3, qw = wid >> 2;  // keys 32 kw .. of the group; query half of a chunk
+  const int hu = kw >> 1;                 // this wave's unit
   const int BH = p.B * p.h_kv;
   const int bh = blockIdx.x % BH;
   const int gi = blockIdx.x / BH;
   const int b = bh / p.h_kv, kvh = bh % p.h_kv;
+  const int n_sep_pairs = (p.n_sep_chunks + 1) / 2, n_cap_pairs = (p.n_cap_blocks + 1) / 2;
 
-  int kind, idx;
-  if (gi < p.n_sep_chunks) { kind = G_SEP; idx = gi; }
-  else if (gi < p.n_sep_chunks + p.n_cap_blocks) { kind = G_CAP; idx = gi - p.n_sep_chunks; }
-  else { kind = G_DENSE; idx = gi - p.n_sep_chunks - p.n_cap_blocks; }
+  int kind, pi;
+  if (gi < n_sep_pairs) { kind = G_SEP; pi = gi; }
+  else if (gi < n_sep_pairs + n_cap_pairs) { kind = G_CAP; pi = gi - n_sep_pairs; }
+  else { kind = G_DENSE; pi = gi - n_sep_pairs - n_cap_pairs; }
 
-  // the group's key / value rows, row count and output rows
-  const char* kbase;
-  const char* vbase;
-  int64_t kstr, vstr;
-  int valid;
-  float* dk_out;
-  float* dv_out;
-  int key0 = 0;  // key index of row 0 (dense and capped groups)
-  if (kind == G_SEP) {
-    const int n_sep_all = ld_uniform(p.n_sep);
-    if (idx * BK >= n_sep_all) return;
-    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.sep_rows + (int64_t)idx * BK;
-    kbase = static_cast<const char*>(p.ksep) + ho * (D128 * 2);
-    vbase = static_cast<const char*>(p.vsep) + ho * (D128 * 2);
-    kstr = vstr = D128 * 2;
-    valid = min(BK, n_sep_all - idx * BK);
-    dk_out = p.dksep + ho * D128;
-    dv_out = p.dvsep + ho * D128;
-  } else if (kind == G_CAP) {
-    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.cap_rows + (int64_t)idx * BK;
-    kbase = static_cast<const char*>(p.kcap) + ho * (D128 * 2);
-    kstr = D128 * 2;
-    vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)idx * BK * p.vsT) * 2;
-    vstr = p.vsT * 2;
-    valid = min(BK, p.n_cap - idx * BK);
-    key0 = idx * BK;
-    dk_out = p.dkcap + ho * D128;
-    dv_out = p.dvcap + ho * D128;
-  } else {
-    kbase = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH + (int64_t)idx * BK * p.ksT) * 2;
-    vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)idx * BK * p.vsT) * 2;
-    kstr = p.ksT * 2;
-    vstr = p.vsT * 2;
-    valid = min(BK, p.n_k - idx * BK);
-    key0 = idx * BK;
-    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.n_k + (int64_t)idx * BK;
-    dk_out = p.dk_acc + ho * D128;
-    dv_out = p.dv_acc + ho * D128;
+  const int n_sep_all = kind == G_SEP ? ld_uniform(p.n_sep) : 0;
+  if (kind == G_SEP && pi * 2 * BK >= n_sep_all) return;
+  KeyUnit U0, U1;
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    KeyUnit& u = x ? U1 : U0;
+    u.idx = 2 * pi + x;
+    u.key0 = u.idx * BK;
+    if (kind == G_SEP) {
+      const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.sep_rows + (int64_t)u.idx * BK;
+      u.kbase = static_cast<const char*>(p.ksep) + ho * (D128 * 2);
+      u.vbase = static_cast<const char*>(p.vsep) + ho * (D128 * 2);
+      u.kstr = u.vstr = D128 * 2;
+      u.valid = max(0, min(BK, n_sep_all - u.idx * BK));
+      u.dk_out = p.dksep + ho * D128;
+      u.dv_out = p.dvsep + ho * D128;
+      u.key0 = 0;
+    } else if (kind == G_CAP) {
+      const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.cap_rows + (int64_t)u.idx * BK;
+      u.kbase = static_cast<const char*>(p.kcap) + ho * (D128 * 2);
+      u.kstr = D128 * 2;
+      u.vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)u.idx * BK * p.vsT) * 2;
+      u.vstr = p.vsT * 2;
+      u.valid = max(0, min(BK, p.n_cap - u.idx * BK));
+      u.dk_out = p.dkcap + ho * D128;
+      u.dv_out = p.dvcap + ho * D128;
+    } else {
+      u.kbase = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH + (int64_t)u.idx * BK * p.ksT) * 2;
+      u.vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)u.idx * BK * p.vsT) * 2;
+      u.kstr = p.ksT * 2;
+      u.vstr = p.vsT * 2;
+      u.valid = max(0, min(BK, p.n_k - u.idx * BK));
+      const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.n_k + (int64_t)u.idx * BK;
+      u.dk_out = p.dk_acc + ho * D128;
+      u.dv_out = p.dv_acc + ho * D128;
+    }
   }
-  dma_block(kbase, kstr, valid, Kg, wid, lane);
-  dma_block(vbase, vstr, valid, Vg, wid, lane);
+  // keys of unit x by waves 4x .. 4x+3 (dma_block moves rows 16 w' .. 16 w' + 15)
+  {
+    const KeyUnit u = (wid >> 2) ? U1 : U0;
+    if (u.valid > 0) {
+      dma_block(u.kbase, u.kstr, u.valid, Kg + (wid >> 2) * BLK_BYTES, wid & 3, lane);
+      dma_block(u.vbase, u.vstr, u.valid, Vg + (wid >> 2) * BLK_BYTES, wid & 3, lane);
+    }
+  }
 
-  // this lane's key
-  const int kslot = 32 * kw + l32;
-  const int j = key0 + kslot;
+  const KeyUnit mu = hu ? U1 : U0;
+  const int kslot64 = 32 * (kw & 1) + l32;  // row within this wave's unit
+  const int kslot = 32 * kw + l32;          // row within the group
+  const int j = mu.key0 + kslot64;
   bool jsep = false;
-  if (kind == G_DENSE && p.kind == SA_MASK_SEPLLM && j < p.n_k)
-    jsep = (p.sep_bits[idx] >> kslot) & 1ull;
+  if (kind == G_DENSE && p.kind == SA_MASK_SEPLLM && j < p.n_k && mu.valid > 0)
+    jsep = (p.sep_bits[mu.idx] >> kslot64) & 1ull;
 
   f32x16 dka[4], dva[4];
 #pragma unroll
@@ -468,152 +493,201 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
   const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int vcb = vcol >> 3;
 
-  int t_begin;
-  if (kind == G_SEP) t_begin = first_gathering_tile(p, idx * BK);
-  else t_begin = max(0, key0 - (p.kind == SA_MASK_SEGMENT ? p.P : 0)) / TQ;
   const bool q_raw = kind == G_CAP;
   const void* qsrc = q_raw ? p.qraw : p.q;
   const int64_t qB = q_raw ? p.qrB : p.qsB, qH = q_raw ? p.qrH : p.qsH, qT = q_raw ? p.qrT : p.qsT;
 
-  for (int t = t_begin; t < p.n_tiles; ++t) {
-    int mk = MK_NONE;
-    int count = 0;
+  // mask kind of unit x in tile t (-1: not read by the tile)
+  auto unit_mk = [&](int x, int t, int& count) -> int {
+    const int valid = x ? U1.valid : U0.valid;
+    const int uidx = x ? U1.idx : U0.idx;
+    count = 0;
+    if (valid <= 0) return -1;
     if (kind == G_SEP) {
-      mk = MK_COUNT;
-      count = ld_uniform(p.sep_count + t) - idx * BK;
-    } else {
-      const int it = find_item(p, t, idx);
-      if (it < 0) {
-        if (kind == G_DENSE) break;  // the tiles reading a dense block are consecutive
-        continue;
+      count = ld_uniform(p.sep_count + t) - uidx * BK;
+      return count > 0 ? MK_COUNT : -1;
+    }
+    const int it = find_item(p, t, uidx);
+    if (it < 0) return -1;
+    const int fl = it >> 24;
+    if (kind == G_CAP) return (fl & SA_ITEM_CAPPED) ? MK_LCAP : -1;
+    if (p.use_cap && (fl & SA_ITEM_CAPPED)) return MK_LNORM;
+    if (fl & SA_ITEM_FULL) return MK_NONE;
+    if (p.kind == SA_MASK_SEPLLM) return MK_SEPLLM;
+    if (p.kind == SA_MASK_LAMBDA) return MK_LALL;
+    return MK_SEG;
+  };
+  // chunk cursor: (tile, query head of the group, 64-query half) and the
+  // tile's mask kind and separator count per unit
+  struct Cur {
+    int t, gq, ch;
+    int mk0, mk1, cnt0, cnt1;
+  };
+  // first tile at or after t that reads the group (t = n_tiles when none)
+  auto tile_from = [&](int t) -> Cur {
+    Cur c{p.n_tiles, 0, 0, -1, -1, 0, 0};
+    for (; t < p.n_tiles; ++t) {
+      int c0, c1;
+      const int m0 = unit_mk(0, t, c0), m1 = unit_mk(1, t, c1);
+      if (m0 >= 0 || m1 >= 0) {
+        c.t = t;
+        c.mk0 = m0;
+        c.mk1 = m1;
+        c.cnt0 = c0;
+        c.cnt1 = c1;
+        return c;
       }
-      const int fl = it >> 24;
-      if (kind == G_CAP) {
-        if (!(fl & SA_ITEM_CAPPED)) continue;
-        mk = MK_LCAP;
-      } else if (p.use_cap && (fl & SA_ITEM_CAPPED)) {
-        mk = MK_LNORM;
-      } else if (fl & SA_ITEM_FULL) {
-        mk = MK_NONE;
-      } else if (p.kind == SA_MASK_SEPLLM) {
-        mk = MK_SEPLLM;
-      } else if (p.kind == SA_MASK_LAMBDA) {
-        mk = MK_LALL;
-      } else {
-        mk = MK_SEG;
+      if (kind == G_DENSE) return c;  // the tiles reading a dense block are consecutive
+    }
+    return c;
+  };
+
+  int t0;
+  if (kind == G_SEP) t0 = first_gathering_tile(p, pi * 2 * BK);
+  else t0 = max(0, U0.key0 - (p.kind == SA_MASK_SEGMENT ? p.P : 0)) / TQ;
+
+  auto advance = [&](Cur c) -> Cur {
+    ++c.ch;
+    if (c.ch == 2 || c.t * TQ + 64 * c.ch >= p.n_q) {
+      c.ch = 0;
+      if (++c.gq == p.group) return tile_from(c.t + 1);
+    }
+    return c;
+  };
+  auto issue = [&](const Cur& c, char* Qd, char* Dd, float (*LDd)[64]) __attribute__((always_inline)) {
+    const int hq = kvh * p.group + c.gq;
+    const int qc0 = c.t * TQ + 64 * c.ch;
+    const int qvalid = min(64, p.n_q - qc0);
+    if (wid < 4)
+      dma_block(static_cast<const char*>(qsrc) + (b * qB + hq * qH + (int64_t)qc0 * qT) * 2, qT * 2, qvalid, Qd,
+                wid, lane);
+    else
+      dma_block(static_cast<const char*>(p.dout) + (b * p.dsB + hq * p.dsH + (int64_t)qc0 * p.dsT) * 2, p.dsT * 2,
+                qvalid, Dd, wid & 3, lane);
+    if (wid == 0 || wid == 4) {
+      const int64_t ri = ((int64_t)b * p.h_q + hq) * p.n_q + qc0 + min(lane, qvalid - 1);
+      const float* src = wid == 0 ? p.lse + ri : p.Dv + ri;
+      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(LDd[wid >> 2]),
+                                       4, 0, 0);
+    }
+  };
+
+  auto compute = [&](const Cur& c, const char* Qc, const char* Dc, const float (*LDc)[64]) __attribute__((always_inline)) {
+    const int mk = hu ? c.mk1 : c.mk0;
+    const int count = hu ? c.cnt1 : c.cnt0;
+    if (mk < 0) return;
+    const int hq = kvh * p.group + c.gq;
+    const float m2 = ALIBI ? alibi_slope_log2(p, hq) : 0.f;
+    const int qc0 = c.t * TQ + 64 * c.ch;
+    const int count_ok = kslot64 < count;
+    f32x16 s = f32x16{}, dp = f32x16{};
+    {
+      const char* ql = Qc + (32 * qw + l32) * 256;
+      const char* dl = Dc + (32 * qw + l32) * 256;
+      const char* kl = Kg + kslot * 256;
+      const char* vl = Vg + kslot * 256;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int off = ((2 * ks) ^ kf) << 4;
+        const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ql + off));
+        const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + off));
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, s, 0, 0, 0);
+        const bf16x8 da = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dl + off));
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vl + off));
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, dp, 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    const int count_ok = kslot < count;
-    for (int gq = 0; gq < p.group; ++gq) {
-      const int hq = kvh * p.group + gq;
-      const float m2 = ALIBI ? alibi_slope_log2(p, hq) : 0.f;
-      const int64_t rowh = ((int64_t)b * p.h_q + hq) * p.n_q;
-      for (int ch = 0; ch < 2; ++ch) {
-        const int qc0 = t * TQ + 64 * ch;
-        if (qc0 >= p.n_q) break;
-        const int qvalid = min(64, p.n_q - qc0);
-        __syncthreads();  // the previous chunk's reads are done
-        dma_block(static_cast<const char*>(qsrc) + (b * qB + hq * qH + (int64_t)qc0 * qT) * 2, qT * 2, qvalid,
-                  Qc, wid, lane);
-        dma_block(static_cast<const char*>(p.dout) + (b * p.dsB + hq * p.dsH + (int64_t)qc0 * p.dsT) * 2,
-                  p.dsT * 2, qvalid, Dc, wid, lane);
-        if (tid < 128) {
-          const int r = tid & 63;
-          const int64_t ri = rowh + qc0 + min(r, qvalid - 1);
-          LD[tid >> 6][r] = tid < 64 ? p.lse[ri] * LOG2E : p.Dv[ri];
-        }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-        __syncthreads();
-        // S = Q K^T and dP = dO V^T: queries as rows, this wave's 32 keys as columns
-        f32x16 s = f32x16{}, dp = f32x16{};
-        {
-          const char* ql = Qc + (32 * qw + l32) * 256;
-          const char* dl = Dc + (32 * qw + l32) * 256;
-          const char* kl = Kg + kslot * 256;
-          const char* vl = Vg + kslot * 256;
+    const int i0 = qc0 + 32 * qw + 4 * hl;
+    switch (mk) {
+      case MK_NONE: mask_keys<MK_NONE>(p, i0, j, jsep, count_ok, s); break;
+      case MK_COUNT: mask_keys<MK_COUNT>(p, i0, j, jsep, count_ok, s); break;
+      case MK_SEPLLM: mask_keys<MK_SEPLLM>(p, i0, j, jsep, count_ok, s); break;
+      case MK_LALL: mask_keys<MK_LALL>(p, i0, j, jsep, count_ok, s); break;
+      case MK_LNORM: mask_keys<MK_LNORM>(p, i0, j, jsep, count_ok, s); break;
+      case MK_LCAP: mask_keys<MK_LCAP>(p, i0, j, jsep, count_ok, s); break;
+      default: mask_keys<MK_SEG>(p, i0, j, jsep, count_ok, s); break;
+    }
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
-            const int off = ((2 * ks) ^ kf) << 4;
-            const bf16x8 qa = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ql + off));
-            const bf16x8 kb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + off));
-            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa, kb, s, 0, 0, 0);
-            const bf16x8 da = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(dl + off));
-            const bf16x8 vb = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vl + off));
-            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da, vb, dp, 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-        const int i0 = qc0 + 32 * qw + 4 * hl;
-        switch (mk) {
-          case MK_NONE: mask_keys<MK_NONE>(p, i0, j, jsep, count_ok, s); break;
-          case MK_COUNT: mask_keys<MK_COUNT>(p, i0, j, jsep, count_ok, s); break;
-          case MK_SEPLLM: mask_keys<MK_SEPLLM>(p, i0, j, jsep, count_ok, s); break;
-          case MK_LALL: mask_keys<MK_LALL>(p, i0, j, jsep, count_ok, s); break;
-          case MK_LNORM: mask_keys<MK_LNORM>(p, i0, j, jsep, count_ok, s); break;
-          case MK_LCAP: mask_keys<MK_LCAP>(p, i0, j, jsep, count_ok, s); break;
-          default: mask_keys<MK_SEG>(p, i0, j, jsep, count_ok, s); break;
-        }
-        // P = 2^(S - lse2) (s), dS = P (dP - D) (dp), in place
+    for (int g = 0; g < 4; ++g) {
+      const float4 l4 = *reinterpret_cast<const float4*>(&LDc[0][32 * qw + 8 * g + 4 * hl]);
+      const float4 d4 = *reinterpret_cast<const float4*>(&LDc[1][32 * qw + 8 * g + 4 * hl]);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const float4 l4 = *reinterpret_cast<const float4*>(&LD[0][32 * qw + 8 * g + 4 * hl]);
-          const float4 d4 = *reinterpret_cast<const float4*>(&LD[1][32 * qw + 8 * g + 4 * hl]);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * g + e;
-            float x = s[r];
-            if constexpr (ALIBI) x = fmaf(-m2, fminf((float)(i0 + 8 * g + e - j), (float)p.L), x);
-            const float pe = __builtin_amdgcn_exp2f(x - lv[e]);
-            s[r] = pe;
-            dp[r] = pe * (dp[r] - dv4[e]);
-          }
-        }
-        bf16x8 pb[2], db[2];
-        pack_tile(s, pb);
-        pack_tile(dp, db);
-        // dV^T += dO^T P and dK^T += Q^T dS: transpose reads of this wave's 32 chunk rows
-        {
-          const char* dt = Dc + (32 * qw + vrow) * 256 + ((vcol & 7) << 1);
-          const char* qt = Qc + (32 * qw + vrow) * 256 + ((vcol & 7) << 1);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int ks = i >> 2, dm = i & 3;
-            const int o0 = (16 * ks) * 256 + (((4 * dm + vcb) ^ vf0) << 4);
-            const int o1 = (16 * ks + 8) * 256 + (((4 * dm + vcb) ^ vf1) << 4);
-            const bf16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(dt + o0));
-            const bf16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(dt + o1));
-            dva[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                             pb[ks], dva[dm], 0, 0, 0);
-            const bf16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qt + o0));
-            const bf16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qt + o1));
-            dka[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7),
-                                                             db[ks], dka[dm], 0, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-          }
-        }
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * g + e;
+        float x = s[r];
+        if constexpr (ALIBI) x = fmaf(-m2, fminf((float)(i0 + 8 * g + e - j), (float)p.L), x);
+        const float pe = __builtin_amdgcn_exp2f(x - lv[e] * LOG2E);
+        s[r] = pe;
+        dp[r] = pe * (dp[r] - dv4[e]);
       }
+    }
+    bf16x8 pb[2], db[2];
+    pack_tile(s, pb);
+    pack_tile(dp, db);
+    const char* dt = Dc + (32 * qw + vrow) * 256 + ((vcol & 7) << 1);
+    const char* qt = Qc + (32 * qw + vrow) * 256 + ((vcol & 7) << 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int ks = i >> 2, dm = i & 3;
+      const int o0 = (16 * ks) * 256 + (((4 * dm + vcb) ^ vf0) << 4);
+      const int o1 = (16 * ks + 8) * 256 + (((4 * dm + vcb) ^ vf1) << 4);
+      const bf16x4 dlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(dt + o0));
+      const bf16x4 dhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(dt + o1));
+      dva[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(dlo, dhi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                       pb[ks], dva[dm], 0, 0, 0);
+      const bf16x4 qlo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qt + o0));
+      const bf16x4 qhi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(qt + o1));
+      dka[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_shufflevector(qlo, qhi, 0, 1, 2, 3, 4, 5, 6, 7),
+                                                       db[ks], dka[dm], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  // chunk loop: wait for chunk c and for every read of the other buffers, start
+  // chunk c+1 into them, compute chunk c
+  Cur cur = tile_from(t0);
+  if (cur.t < p.n_tiles) issue(cur, Qb0, Db0, LD0);
+  while (cur.t < p.n_tiles) {
+    {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+      const Cur nx = advance(cur);
+      if (nx.t < p.n_tiles) issue(nx, Qb1, Db1, LD1);
+      compute(cur, Qb0, Db0, LD0);
+      cur = nx;
+    }
+    if (cur.t >= p.n_tiles) break;
+    {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      const Cur nx = advance(cur);
+      if (nx.t < p.n_tiles) issue(nx, Qb0, Db0, LD0);
+      compute(cur, Qb1, Db1, LD1);
+      cur = nx;
     }
   }
 
-  // waves qw = 1 hand their partial sums to waves qw = 0 through LDS (the four
-  // 16 KB arrays are contiguous per kw pair once the loop is over)
+  // waves qw = 1 hand their sums to waves qw = 0 through LDS (32 KB per key
+  // quarter: Kg, Vg, Qb0 + Db0, Qb1 + Db1), which add them and store
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
-  float* red = reinterpret_cast<float*>(kw == 0 ? Kg : Qc);
-  float* red2 = reinterpret_cast<float*>(kw == 0 ? Vg : Dc);
+  float* redk = reinterpret_cast<float*>(kw == 0 ? Kg : kw == 1 ? Vg : kw == 2 ? Qb0 : Qb1);
+  float* redv = kw < 2 ? redk + 4096 : reinterpret_cast<float*>(kw == 2 ? Db0 : Db1);
   if (qw == 1) {
 #pragma unroll
     for (int dm = 0; dm < 4; ++dm)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        red[(dm * 16 + r) * 64 + lane] = dka[dm][r];
-        red2[(dm * 16 + r) * 64 + lane] = dva[dm][r];
+        redk[(dm * 16 + r) * 64 + lane] = dka[dm][r];
+        redv[(dm * 16 + r) * 64 + lane] = dva[dm][r];
       }
   }
   __syncthreads();
-  if (qw == 0 && kslot < valid) {
-    float* krow = dk_out + (int64_t)kslot * D128;
-    float* vrow_o = dv_out + (int64_t)kslot * D128;
+  if (qw == 0 && kslot64 < mu.valid) {
+    float* krow = mu.dk_out + (int64_t)kslot64 * D128;
+    float* vrow_o = mu.dv_out + (int64_t)kslot64 * D128;
 #pragma unroll
     for (int dm = 0; dm < 4; ++dm)
 #pragma unroll
@@ -621,14 +695,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dkdv_bf16(BwdArgs p) {
         const int d0 = 32 * dm + 8 * g + 4 * hl;
         const int r0 = dm * 16 + 4 * g;
         float4 kx, vx;
-        kx.x = dka[dm][4 * g] + red[(r0) * 64 + lane];
-        kx.y = dka[dm][4 * g + 1] + red[(r0 + 1) * 64 + lane];
-        kx.z = dka[dm][4 * g + 2] + red[(r0 + 2) * 64 + lane];
-        kx.w = dka[dm][4 * g + 3] + red[(r0 + 3) * 64 + lane];
-        vx.x = dva[dm][4 * g] + red2[(r0) * 64 + lane];
-        vx.y = dva[dm][4 * g + 1] + red2[(r0 + 1) * 64 + lane];
-        vx.z = dva[dm][4 * g + 2] + red2[(r0 + 2) * 64 + lane];
-        vx.w = dva[dm][4 * g + 3] + red2[(r0 + 3) * 64 + lane];
+        kx.x = dka[dm][4 * g] + redk[(r0) * 64 + lane];
+        kx.y = dka[dm][4 * g + 1] + redk[(r0 + 1) * 64 + lane];
+        kx.z = dka[dm][4 * g + 2] + redk[(r0 + 2) * 64 + lane];
+        kx.w = dka[dm][4 * g + 3] + redk[(r0 + 3) * 64 + lane];
+        vx.x = dva[dm][4 * g] + redv[(r0) * 64 + lane];
+        vx.y = dva[dm][4 * g + 1] + redv[(r0 + 1) * 64 + lane];
+        vx.z = dva[dm][4 * g + 2] + redv[(r0 + 2) * 64 + lane];
+        vx.w = dva[dm][4 * g + 3] + redv[(r0 + 3) * 64 + lane];
         *reinterpret_cast<float4*>(krow + d0) = kx;
         *reinterpret_cast<float4*>(vrow_o + d0) = vx;
       }
@@ -844,10 +918,10 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   }
   // 3. dK, dV (key-major): separator chunks, then capped blocks, then dense blocks
   {
-    const int64_t groups = (int64_t)p.n_sep_chunks + p.n_cap_blocks + lay.n_blocks;
+    const int64_t groups = (int64_t)(p.n_sep_chunks + 1) / 2 + (p.n_cap_blocks + 1) / 2 + (lay.n_blocks + 1) / 2;
     const unsigned grid = (unsigned)(groups * a.batch * a.h_kv);
-    if (alibi) hipLaunchKernelGGL(bwd_dkdv_bf16<true>, dim3(grid), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(bwd_dkdv_bf16<false>, dim3(grid), dim3(256), 0, s, p);
+    if (alibi) hipLaunchKernelGGL(bwd_dkdv_bf16<true>, dim3(grid), dim3(512), 0, s, p);
+    else hipLaunchKernelGGL(bwd_dkdv_bf16<false>, dim3(grid), dim3(512), 0, s, p);
   }
   // 4. finish: dq, dk, dv
   for (int which = 0; which < 3; ++which) {
