@@ -240,20 +240,62 @@ def topk_middle_timing(sa, q, k, v, o, lse, wl, kmid, steps, torch):
             "note": "scoring + selection + merge; o, lse rewritten in place (run after the timed forward steps)"}
 
 
-def source_sha(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def lambda_decode_timing(steps, torch, batch=16):
+    """LM-Infinite decode (Lambda set of the new query: starting span + window, starting
+    keys capped) for a Llama-2-7B-shaped layer: 32 heads, d = 128, n_starting = 10,
+    L_pretrain = 4096, RoPE 10000; timed once the window is full (4107 held slots)."""
+    import workloads as W
+    from structured_sparse_attention_attn_amd.pipeline import StreamDecoder
+    B, hq, hkv, d, n_s, L = batch, 32, 32, 128, 10, 4096
+    dec = StreamDecoder(B, hq, hkv, d, n_s, rope_base=10000.0, kind="lambda", L_pretrain=L)
+    q, k, v, _ = W.make_decode_stream(B, hq, hkv, d, 1, seed=7100, p_sep=0.0)
+    q, k, v = q[0].cuda(), k[0].cuda(), v[0].cuda()
+    o = torch.empty_like(q)
+    for _ in range(n_s + L + 200):
+        dec.step(q, k, v, o=o)
+    torch.cuda.synchronize()
+    held = [len(dec.held(b)) for b in range(B)]
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        dec.step(q, k, v, o=o)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = sum(held) * hkv * 2 * d * 2 + B * (2 * hq + 2 * hkv) * d * 2
+    return {"config": {"batch": B, "h_q": hq, "h_kv": hkv, "head_dim": d, "n_starting": n_s, "L_pretrain": L,
+                       "rope_base": 10000.0},
+            "ms_per_step": round(ms, 5), "tokens_per_s": round(B / (ms * 1e-3), 1),
+            "held_slots_mean": round(sum(held) / B, 1),
+            "hbm_gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_per_step": nbytes}
+
+
+FWD_SOURCES = ("sa_fwd.hip", "sa_device.h", "sa_common.h")
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def fwd_source_sha():
+    """Hash of the sources the fused forward is compiled from."""
+    csrc = os.path.join(ROOT, "structured_sparse_attention_attn_amd", "csrc")
+    return source_sha([os.path.join(csrc, f) for f in FWD_SOURCES])
 
 
 def load_traffic(workload_name):
     """HBM bytes per launch of the fused forward from committed rocprofv3 PMC
     counters, or None when absent or taken on a different kernel source."""
     p = os.path.join(ROOT, "profiles", f"attend_{workload_name}_pmc.json")
-    src = os.path.join(ROOT, "structured_sparse_attention_attn_amd", "csrc", "sa_fwd.hip")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("source_sha") != source_sha(src):
+    if d.get("source_sha") != fwd_source_sha():
         return None
     return (d["fetch_kib"] * d["copy_factor_fetch"] + d["write_kib"] * d["copy_factor_write"]) * 1024.0
 
@@ -469,6 +511,7 @@ def main():
     if args.decode > 0:
         out["decode"] = decode_timing(args.decode, torch)
         out["decode_graph"] = decode_timing(args.decode, torch, graph=True)
+        out["decode_lambda"] = lambda_decode_timing(args.decode, torch)
     if wl.mode == "segment" and args.segments > 0:
         out["multi_segment"] = multi_segment(wl, inp, args.segments, torch)
     if not args.no_gemm_ceiling:

@@ -222,18 +222,28 @@ int sparse_attn_bwd(const sa_mask_t *m, const void *plan, size_t plan_bytes,
                     size_t ws_bytes, hipStream_t stream);
 
 /*
- * Streaming decode with the generation-time cache of the SepLLM page (part
- * 6.2, generation): per sequence, Initial (the first a tokens), Separator (at
- * most s separators, the most recent), Local window (the last w tokens, the
- * newest included) and Past (tokens that left the local window since the last
- * compression).  When a + s + w + |Past| reaches c, Past's separators join the
- * Separator part in order (the oldest beyond s dropped) and Past is emptied;
- * then the new query attends to every held token.  Keys are stored rotated at
- * their original positions.
- *   batch, h_q, h_kv, d   sizes (bf16, d = 128; h_q % h_kv == 0).
- *   a, s, w, c            a >= 0, s >= 1, w >= 1, c > a + s + w, c <= 4096.
+ * Streaming decode, one new token per sequence per step, keys stored rotated
+ * at their original positions.
+ * kind SA_MASK_SEPLLM: the generation-time cache of the SepLLM page (part
+ *   6.2, generation): Initial (the first a tokens), Separator (at most s
+ *   separators, the most recent), Local window (the last w tokens, the newest
+ *   included) and Past (tokens that left the local window since the last
+ *   compression).  When a + s + w + |Past| reaches c, Past's separators join
+ *   the Separator part in order (the oldest beyond s dropped) and Past is
+ *   emptied; then the new query attends to every held token.
+ * kind SA_MASK_LAMBDA: LM-Infinite's Lambda set for the new query t (LM-Infinite
+ *   page, section "method"): the first a = n_starting tokens and the window
+ *   t - L_pretrain .. t (w = L_pretrain + 1 slots; s and c are ignored).  A
+ *   starting token farther than L_pretrain takes the capped logit
+ *   scale <R(L) q_t, k_j>.
+ *   batch, h_q, h_kv, d   sizes (bf16, d = 128; h_q % h_kv == 0, at most 8
+ *                         query heads per kv head).
+ *   a, s, w, c            SEPLLM: a >= 0, s >= 1, w >= 1, c > a + s + w,
+ *                         c <= 4096.  LAMBDA: a = n_starting >= 0.
  *   rope, rope_base       SA_ROPE_NONE or SA_ROPE_HALF.
  *   scale                 logit scale.
+ *   kind                  SA_MASK_SEPLLM or SA_MASK_LAMBDA.
+ *   L_pretrain            LAMBDA: the window and cap, a + L_pretrain + 1 <= 65536.
  */
 typedef struct {
   int32_t batch, h_q, h_kv, d;
@@ -241,6 +251,8 @@ typedef struct {
   int32_t rope;
   float rope_base;
   float scale;
+  int32_t kind;
+  int32_t L_pretrain;
 } sa_stream_cfg_t;
 
 /*

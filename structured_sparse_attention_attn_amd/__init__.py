@@ -67,7 +67,8 @@ class sa_bwd_args_t(ctypes.Structure):
 
 class sa_stream_cfg_t(ctypes.Structure):
     _fields_ = [("batch", _i32), ("h_q", _i32), ("h_kv", _i32), ("d", _i32), ("a", _i32), ("s", _i32),
-                ("w", _i32), ("c", _i32), ("rope", _i32), ("rope_base", _f32), ("scale", _f32)]
+                ("w", _i32), ("c", _i32), ("rope", _i32), ("rope_base", _f32), ("scale", _f32),
+                ("kind", _i32), ("L_pretrain", _i32)]
 
 
 _MASKP = ctypes.POINTER(sa_mask_t)
@@ -308,9 +309,13 @@ def sparse_attn_bwd(m: sa_mask_t, plan, args: sa_fwd_args_t, grads: sa_bwd_args_
 
 
 def stream_cfg(batch: int, h_q: int, h_kv: int, d: int, a: int, s: int, w: int, c: int, *,
-               rope_base: Optional[float] = None, scale: Optional[float] = None) -> sa_stream_cfg_t:
+               rope_base: Optional[float] = None, scale: Optional[float] = None,
+               kind: int = SA_MASK_SEPLLM, L_pretrain: int = 0) -> sa_stream_cfg_t:
+    """SEPLLM: the four-part cache (a, s, w, c).  LAMBDA: a = n_starting and L_pretrain
+    (s, w, c unused)."""
     return sa_stream_cfg_t(batch, h_q, h_kv, d, a, s, w, c, SA_ROPE_HALF if rope_base else SA_ROPE_NONE,
-                           float(rope_base or 0.0), float(scale if scale is not None else d ** -0.5))
+                           float(rope_base or 0.0), float(scale if scale is not None else d ** -0.5),
+                           kind, L_pretrain)
 
 
 def sa_stream_state_bytes(cfg: sa_stream_cfg_t) -> int:

@@ -527,8 +527,35 @@ int sparse_attn_segment_carry(int32_t dtype, int32_t n_heads, int32_t n_local, i
 
 namespace {
 
+// The cache geometry a kernel sees: for LAMBDA, Initial = the starting span,
+// Local = the window of L_pretrain + 1 slots, no Separator or Past part.
+sa_stream_cfg_t stream_geometry(const sa_stream_cfg_t& c) {
+  sa_stream_cfg_t g = c;
+  if (c.kind == SA_MASK_LAMBDA) {
+    g.s = 0;
+    g.w = c.L_pretrain + 1;
+    g.c = c.a + g.w;
+  }
+  return g;
+}
+
 int check_stream_cfg(const sa_stream_cfg_t* c) {
   if (c == nullptr) return fail(SA_EINVAL, "cfg is NULL");
+  if (c->kind != SA_MASK_SEPLLM && c->kind != SA_MASK_LAMBDA)
+    return fail(SA_EINVAL, "streaming decode kind must be SEPLLM or LAMBDA");
+  if (c->kind == SA_MASK_LAMBDA) {
+    if (c->a < 0 || c->L_pretrain < 0 || (int64_t)c->a + c->L_pretrain + 1 > 65536)
+      return fail(SA_EINVAL, "LAMBDA decode needs n_starting >= 0, L_pretrain >= 0, n_starting + L_pretrain + 1 <= 65536");
+    if (c->batch < 1 || c->h_q < 1 || c->h_kv < 1 || c->h_q % c->h_kv != 0)
+      return fail(SA_EINVAL, "need batch, h_kv >= 1 and h_q a multiple of h_kv");
+    if (c->h_q / c->h_kv > 8) return fail(SA_EUNSUPPORTED, "at most 8 query heads per kv head");
+    if (c->d != 128) return fail(SA_EUNSUPPORTED, "streaming decode supports d = 128");
+    if (c->rope != SA_ROPE_NONE && c->rope != SA_ROPE_HALF) return fail(SA_EINVAL, "unknown rope mode %d", c->rope);
+    if (c->rope == SA_ROPE_HALF && !(std::isfinite(c->rope_base) && c->rope_base > 1.0f))
+      return fail(SA_EINVAL, "rope_base must be finite and > 1");
+    if (!(std::isfinite(c->scale) && c->scale > 0.0f)) return fail(SA_EINVAL, "scale must be finite and > 0");
+    return SA_OK;
+  }
   if (c->batch < 1 || c->h_q < 1 || c->h_kv < 1 || c->h_q % c->h_kv != 0)
     return fail(SA_EINVAL, "need batch, h_kv >= 1 and h_q a multiple of h_kv");
   if (c->h_q / c->h_kv > 8) return fail(SA_EUNSUPPORTED, "at most 8 query heads per kv head");
@@ -551,7 +578,7 @@ int sa_stream_state_bytes(const sa_stream_cfg_t* cfg, size_t* bytes) {
   int r = check_stream_cfg(cfg);
   if (r != SA_OK) return r;
   if (bytes == nullptr) return fail(SA_EINVAL, "bytes is NULL");
-  *bytes = (size_t)sa::stream_layout(*cfg).total;
+  *bytes = (size_t)sa::stream_layout(stream_geometry(*cfg)).total;
   return ok();
 }
 
@@ -559,7 +586,7 @@ int sa_decode_workspace_bytes(const sa_stream_cfg_t* cfg, size_t* bytes) {
   int r = check_stream_cfg(cfg);
   if (r != SA_OK) return r;
   if (bytes == nullptr) return fail(SA_EINVAL, "bytes is NULL");
-  *bytes = (size_t)sa::stream_layout(*cfg).ws_total;
+  *bytes = (size_t)sa::stream_layout(stream_geometry(*cfg)).ws_total;
   return ok();
 }
 
@@ -567,7 +594,7 @@ int sa_stream_layout(const sa_stream_cfg_t* cfg, int64_t offsets[5]) {
   int r = check_stream_cfg(cfg);
   if (r != SA_OK) return r;
   if (offsets == nullptr) return fail(SA_EINVAL, "offsets is NULL");
-  const sa::StreamLayout L = sa::stream_layout(*cfg);
+  const sa::StreamLayout L = sa::stream_layout(stream_geometry(*cfg));
   offsets[0] = L.k;
   offsets[1] = L.v;
   offsets[2] = L.pos;
@@ -579,12 +606,13 @@ int sa_stream_layout(const sa_stream_cfg_t* cfg, int64_t offsets[5]) {
 int sparse_attn_stream_reset(const sa_stream_cfg_t* cfg, void* state, size_t state_bytes, hipStream_t stream) {
   int r = check_stream_cfg(cfg);
   if (r != SA_OK) return r;
-  const sa::StreamLayout L = sa::stream_layout(*cfg);
+  const sa_stream_cfg_t geo = stream_geometry(*cfg);
+  const sa::StreamLayout L = sa::stream_layout(geo);
   if (state == nullptr || !aligned16(state)) return fail(SA_EINVAL, "state must be a 16-byte aligned device pointer");
   if (state_bytes < (size_t)L.total)
     return fail(SA_ENOSPACE, "state too small: %zu < %lld bytes", state_bytes, (long long)L.total);
   if ((r = check_device()) != SA_OK) return r;
-  hipError_t e = sa::launch_stream_reset(*cfg, state, stream);
+  hipError_t e = sa::launch_stream_reset(geo, state, stream);
   if (e != hipSuccess) return fail(SA_EHIP, "reset launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -594,15 +622,17 @@ int sparse_attn_decode_step(const sa_stream_cfg_t* cfg, void* state, size_t stat
                             size_t ws_bytes, hipStream_t stream) {
   int r = check_stream_cfg(cfg);
   if (r != SA_OK) return r;
-  const sa::StreamLayout L = sa::stream_layout(*cfg);
+  const sa_stream_cfg_t geo = stream_geometry(*cfg);
+  const sa::StreamLayout L = sa::stream_layout(geo);
   if (state == nullptr || !aligned16(state)) return fail(SA_EINVAL, "state must be a 16-byte aligned device pointer");
   if (state_bytes < (size_t)L.total)
     return fail(SA_ENOSPACE, "state too small: %zu < %lld bytes", state_bytes, (long long)L.total);
   if (ws == nullptr || !aligned16(ws)) return fail(SA_EINVAL, "workspace must be a 16-byte aligned device pointer");
   if (ws_bytes < (size_t)L.ws_total)
     return fail(SA_ENOSPACE, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)L.ws_total);
-  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr || is_sep == nullptr)
-    return fail(SA_EINVAL, "q, k, v, is_sep and o must not be NULL");
+  if (q == nullptr || k == nullptr || v == nullptr || o == nullptr ||
+      (is_sep == nullptr && cfg->kind == SA_MASK_SEPLLM))
+    return fail(SA_EINVAL, "q, k, v, o (and is_sep for SEPLLM) must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(SA_EINVAL, "q, k, v and o must be 16-byte aligned");
   if ((r = check_device()) != SA_OK) return r;
@@ -610,7 +640,7 @@ int sparse_attn_decode_step(const sa_stream_cfg_t* cfg, void* state, size_t stat
   memset(&th, 0, sizeof(th));
   if (cfg->rope == SA_ROPE_HALF)
     for (int c = 0; c < cfg->d / 2; ++c) th.th[c] = std::pow((double)cfg->rope_base, -2.0 * c / cfg->d);
-  hipError_t e = sa::launch_decode_step(*cfg, state, q, k, v, is_sep, o, lse, ws, th, stream);
+  hipError_t e = sa::launch_decode_step(geo, state, q, k, v, is_sep, o, lse, ws, th, stream);
   if (e != hipSuccess) return fail(SA_EHIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
 }

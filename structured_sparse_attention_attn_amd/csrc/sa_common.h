@@ -124,7 +124,7 @@ struct BwdWs {
 struct StreamLayout {
   int64_t k, v, pos, flag, ctrl, total;
   int n_split;
-  int64_t ws_qrot, ws_part, ws_total;
+  int64_t ws_qrot, ws_capl, ws_part, ws_total;
 };
 
 StreamLayout stream_layout(const sa_stream_cfg_t& cfg);

@@ -39,10 +39,12 @@ struct StreamArgs {
   const u16* v;
   const unsigned char* is_sep;  // [B]
   float* qrot;               // [B, h_q, d] rotated, scaled by scale * log2(e)
+  float* capl;               // [B, h_q, a] LAMBDA: base-2 logits of the capped starting keys
   float* part;               // [B, h_q, n_split, d + 2]
   u16* o;                    // [B, h_q, d]
   float* lse;                // [B, h_q] or null
   int B, h_q, h_kv, d, a, s, w, c, P, group, rotate, n_split;
+  int lambda, L;             // LAMBDA: no Separator or Past part; starting keys capped at L
   float scale_log2;
   ThetaTable theta;
 };
@@ -158,8 +160,8 @@ __global__ __launch_bounds__(256) void stream_insert(StreamArgs p) {
       *reinterpret_cast<uint4*>(dstb + (int64_t)list_dst[r] * 256 + pc * 16) =
           *reinterpret_cast<const uint4*>(srcb + (int64_t)list_src[r] * 256 + pc * 16);
     }
-  } else if (sp.evict && tid < 32) {
-    // the evicted local token enters Past
+  } else if (sp.evict && tid < 32 && !p.lambda) {
+    // the evicted local token enters Past (LAMBDA: it is dropped)
     const int pc = tid & 15;
     char* base = tid < 16 ? K : V;
     *reinterpret_cast<uint4*>(base + (int64_t)(p.a + p.s + sp.n_past) * 256 + pc * 16) =
@@ -204,6 +206,27 @@ __global__ __launch_bounds__(256) void stream_insert(StreamArgs p) {
     qd[c0] = x1 * p.scale_log2;
     qd[c0 + half] = x2 * p.scale_log2;
   }
+  // LAMBDA: the starting keys j with t - j > L take scale <R(L) q, k_j> =
+  // scale <R(L + j) q, R(j) k_j> (keys are stored rotated at their index).
+  // One wave per starting key, one lane per rotation pair, a wave sum per head.
+  if (p.lambda && half == 64) {
+    for (int jj = wid; jj < min(p.a, sp.t); jj += 4) {
+      if (sp.t - jj <= p.L) continue;
+      const int c0 = lane;
+      float cs = 1.f, sn = 0.f;
+      if (p.rotate) angle_sincos((double)(p.L + jj), p.theta.th[c0], &cs, &sn);
+      const u16* kr = reinterpret_cast<const u16*>(K + (int64_t)jj * 256);
+      const float k1 = bf2f(kr[c0]), k2 = bf2f(kr[c0 + 64]);
+      for (int gq = 0; gq < p.group; ++gq) {
+        const int hq = g * p.group + gq;
+        const u16* qr = p.q + ((int64_t)b * p.h_q + hq) * p.d;
+        const float x1 = bf2f(qr[c0]), x2 = bf2f(qr[c0 + 64]);
+        float acc = k1 * (x1 * cs - x2 * sn) + k2 * (x2 * cs + x1 * sn);
+        for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o);
+        if (lane == 0) p.capl[((int64_t)b * p.h_q + hq) * p.a + jj] = acc * p.scale_log2;
+      }
+    }
+  }
 }
 
 // Token index, flag and counters of sequence b after the step.  Called by
@@ -230,7 +253,7 @@ __device__ inline void update_ctrl(const StreamArgs& p, int b, int* list_src, in
     head = (head + max(0, n_sep + n_new - p.s)) % p.s;
     n_sep = min(p.s, n_sep + n_new);
     n_past = 0;
-  } else if (sp.evict) {
+  } else if (sp.evict && !p.lambda) {
     if (threadIdx.x == 0) {
       pos[p.a + p.s + n_past] = pos[sp.ms];
       fl[p.a + p.s + n_past] = fl[sp.ms];
@@ -247,7 +270,7 @@ __device__ inline void update_ctrl(const StreamArgs& p, int b, int* list_src, in
       lhead = (lhead + 1) % p.w;
     }
     pos[sp.ns] = sp.t;
-    fl[sp.ns] = p.is_sep[b] != 0 ? 1 : 0;
+    fl[sp.ns] = (p.is_sep != nullptr && p.is_sep[b] != 0) ? 1 : 0;
     ct[C_T] = sp.t + 1;
     ct[C_NINIT] = n_init;
     ct[C_NSEP] = n_sep;
@@ -280,6 +303,7 @@ __device__ inline int held_slot(const StreamArgs& p, const Held& h, int v) {
 // logits; thread (slot group sg, column chunk cc) holds columns 8 cc .. +7 of
 // the values of slots 4 sg .. 4 sg + 3 for the weighted sum, reduced over the
 // 16 slot groups by shuffles within a wave and LDS across the 4 waves.
+template <bool LAM>
 __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
   __shared__ float qs[MAX_G][128];
   __shared__ float ps[MAX_G][SPLIT];
@@ -314,7 +338,7 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
     __syncthreads();
     h.n_sep = min(p.s, h.n_sep + n_new_s);
     h.n_past = 0;
-  } else if (sp.evict) {
+  } else if (sp.evict && !p.lambda) {
     h.n_past += 1;
   }
   const int nv = h.count();
@@ -356,12 +380,17 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
         kx[8 * e + 2 * f + 1] = bf2f((u16)(xs[f] >> 16));
       }
     }
+    // LAMBDA: a starting key j (its slot index) farther than L from t takes the
+    // capped logit computed by stream_insert
+    const int jslot = kok ? held_slot(p, h, v0 + r) : 0;
+    const bool capped = LAM && kok && jslot < p.a && sp.t - jslot > p.L;
     for (int gq = 0; gq < p.group; ++gq) {
       float acc = 0.f;
 #pragma unroll
       for (int e = 0; e < 32; ++e) acc = fmaf(kx[e], qs[gq][qq * 32 + e], acc);
       acc += __shfl_xor(acc, 1, 4);
       acc += __shfl_xor(acc, 2, 4);
+      if (capped) acc = p.capl[((int64_t)b * p.h_q + g * p.group + gq) * p.a + jslot];
       if (qq == 0) ps[gq][r] = kok ? acc : -__builtin_huge_valf();
     }
   }
@@ -472,7 +501,8 @@ StreamLayout stream_layout(const sa_stream_cfg_t& cfg) {
   L.total = off;
   L.n_split = (int)ceil_div(cfg.c, SPLIT);
   L.ws_qrot = 0;
-  L.ws_part = align_up((int64_t)cfg.batch * cfg.h_q * cfg.d * 4, 256);
+  L.ws_capl = align_up((int64_t)cfg.batch * cfg.h_q * cfg.d * 4, 256);
+  L.ws_part = L.ws_capl + align_up((int64_t)cfg.batch * cfg.h_q * (cfg.a > 0 ? cfg.a : 1) * 4, 256);
   L.ws_total = L.ws_part + (int64_t)cfg.batch * cfg.h_q * L.n_split * (cfg.d + 2) * 4;
   return L;
 }
@@ -503,6 +533,7 @@ hipError_t launch_decode_step(const sa_stream_cfg_t& cfg, void* state, const voi
   p.v = static_cast<const u16*>(v);
   p.is_sep = is_sep;
   p.qrot = reinterpret_cast<float*>(w + L.ws_qrot);
+  p.capl = reinterpret_cast<float*>(w + L.ws_capl);
   p.part = reinterpret_cast<float*>(w + L.ws_part);
   p.o = static_cast<u16*>(o);
   p.lse = lse;
@@ -515,13 +546,18 @@ hipError_t launch_decode_step(const sa_stream_cfg_t& cfg, void* state, const voi
   p.w = cfg.w;
   p.c = cfg.c;
   p.P = cfg.c - cfg.a - cfg.s - cfg.w;
+  p.lambda = cfg.kind == SA_MASK_LAMBDA ? 1 : 0;
+  p.L = cfg.L_pretrain;
   p.group = cfg.h_q / cfg.h_kv;
   p.rotate = cfg.rope == SA_ROPE_HALF ? 1 : 0;
   p.n_split = L.n_split;
   p.scale_log2 = cfg.scale * 1.4426950408889634f;
   p.theta = theta;
   hipLaunchKernelGGL(stream_insert, dim3((unsigned)(cfg.batch * cfg.h_kv)), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(decode_attn, dim3((unsigned)(cfg.batch * cfg.h_kv * L.n_split)), dim3(256), 0, s, p);
+  if (p.lambda)
+    hipLaunchKernelGGL(decode_attn<true>, dim3((unsigned)(cfg.batch * cfg.h_kv * L.n_split)), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(decode_attn<false>, dim3((unsigned)(cfg.batch * cfg.h_kv * L.n_split)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(decode_combine, dim3((unsigned)(cfg.batch * cfg.h_q)), dim3(128), 0, s, p);
   return hipGetLastError();
 }

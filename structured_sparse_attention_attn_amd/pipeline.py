@@ -174,12 +174,16 @@ class SegmentRunner:
 
 
 class StreamDecoder:
-    """Decode with the generation-time cache (Initial, Separator, Local, Past) for a batch
-    of sequences: one state buffer and one workspace, both device memory."""
+    """Streaming decode for a batch of sequences: one state buffer and one workspace, both
+    device memory.  kind "sepllm": the generation-time cache (Initial, Separator, Local,
+    Past) with (a, s, w, c); kind "lambda": LM-Infinite's starting span a = n_starting
+    and window L_pretrain + 1 (s, w, c unused)."""
 
-    def __init__(self, batch, h_q, h_kv, d, a, s, w, c, *, rope_base=None, scale=None,
-                 device: str = "cuda"):
-        self.cfg = stream_cfg(batch, h_q, h_kv, d, a, s, w, c, rope_base=rope_base, scale=scale)
+    def __init__(self, batch, h_q, h_kv, d, a, s=1, w=1, c=0, *, rope_base=None, scale=None,
+                 kind: str = "sepllm", L_pretrain: int = 0, device: str = "cuda"):
+        self.lam = kind == "lambda"
+        self.cfg = stream_cfg(batch, h_q, h_kv, d, a, s, w, c, rope_base=rope_base, scale=scale,
+                              kind=KINDS[kind], L_pretrain=L_pretrain)
         self.state = torch.empty(sa_stream_state_bytes(self.cfg), dtype=torch.uint8, device=device)
         self.ws = torch.empty(sa_decode_workspace_bytes(self.cfg), dtype=torch.uint8, device=device)
         self.layout = sa_stream_layout(self.cfg)
@@ -188,7 +192,7 @@ class StreamDecoder:
     def reset(self) -> None:
         sparse_attn_stream_reset(self.cfg, self.state)
 
-    def step(self, q, k, v, is_sep, o=None, lse=None):
+    def step(self, q, k, v, is_sep=None, o=None, lse=None):
         o = torch.empty_like(q) if o is None else o
         sparse_attn_decode_step(self.cfg, self.state, q, k, v, is_sep, o, self.ws, lse=lse)
         return o
@@ -196,6 +200,9 @@ class StreamDecoder:
     def held(self, b: int):
         """Token indices sequence b's cache holds (reads the state back; for inspection)."""
         c, a, s_, w = self.cfg.c, self.cfg.a, self.cfg.s, self.cfg.w
+        if self.lam:
+            s_, w = 0, self.cfg.L_pretrain + 1
+            c = a + w
         P = c - a - s_ - w
         st = self.state.cpu()
         ctrl = st[self.layout[4]:self.layout[4] + self.cfg.batch * 32].view(torch.int32).view(-1, 8)[b]

@@ -677,3 +677,39 @@ def test_workload3_topk_middle_sampled(sa):
         nk = O.pair_counts(spec)[rows] + np.minimum(kmid, np.maximum(0, rows - wl.L - wl.n_s))
         compare(to64(o[0, h][torch.from_numpy(rows).cuda()]), ro, to64(lse[0, h][torch.from_numpy(rows).cuda()]),
                 rl, "bf16", nkeys=nk)
+
+
+# LM-Infinite decode: the starting span and the window t-L .. t, starting keys capped,
+# against the oracle's Lambda attention of the new query over its t + 1 tokens.
+LAM_DECODE_CASES = [
+    dict(B=2, h_q=8, h_kv=2, n_s=4, L=32, n=200, rope=10000.0),
+    dict(B=1, h_q=2, h_kv=2, n_s=0, L=16, n=60, rope=None),
+    dict(B=1, h_q=4, h_kv=1, n_s=10, L=64, n=150, rope=500000.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(LAM_DECODE_CASES)))
+def test_lambda_decode(sa, case):
+    from structured_sparse_attention_attn_amd.pipeline import StreamDecoder
+    cfg = LAM_DECODE_CASES[case]
+    B, hq, hkv, d = cfg["B"], cfg["h_q"], cfg["h_kv"], 128
+    log(f"lambda decode {case}: {cfg}")
+    q, k, v, _ = W.make_decode_stream(B, hq, hkv, d, cfg["n"], seed=1500 + case, p_sep=0.0)
+    dec = StreamDecoder(B, hq, hkv, d, cfg["n_s"], rope_base=cfg["rope"], kind="lambda", L_pretrain=cfg["L"])
+    scale = d ** -0.5
+    group = hq // hkv
+    lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
+    for t in range(cfg["n"]):
+        o = dec.step(q[t].cuda(), k[t].cuda(), v[t].cuda(), lse=lse)
+        torch.cuda.synchronize()
+        spec = O.MaskSpec(O.LAMBDA, t + 1, t + 1, n_s=cfg["n_s"], L=cfg["L"])
+        for b in range(B):
+            if t % 5 == 0 or t == cfg["n"] - 1:
+                assert dec.held(b) == O.key_set(spec, t).tolist(), (t, b)
+            ro = np.zeros((hq, d))
+            rl = np.zeros(hq)
+            for h in range(hq):
+                oo, ll = O.attention_rows(to64(q[:t + 1, b, h]), to64(k[:t + 1, b, h // group]),
+                                          to64(v[:t + 1, b, h // group]), [t], spec, cfg["rope"], scale)
+                ro[h], rl[h] = oo[0], ll[0]
+            compare(to64(o[b]), ro, to64(lse[b]), rl, "bf16", nkeys=np.full(hq, len(O.key_set(spec, t))))
