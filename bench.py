@@ -75,9 +75,10 @@ def stage_bytes(wl, sep_np, plan_bytes):
         n_sep = int(sep_np[g0:].astype(np.int64).sum())
     rot = wl.rope_base is not None
     n_cap = min(wl.n_s, wl.n_k) if (wl.mode == "lambda" and rot) else 0
-    # the query copy (rotated and/or pre-scaled for bf16), rotated keys, the
-    # gathered separator rows (read K and V, write both) and the capped keys
-    n_qrows = 2 * wl.h_q * wl.n_q if (rot or wl.dtype == "bf16") else 0
+    # the rotated query copy (fp32 only: bf16 queries are rotated and scaled
+    # inside the fused forward), rotated keys, the gathered separator rows
+    # (read K and V, write both) and the capped keys
+    n_qrows = 2 * wl.h_q * wl.n_q if (rot and wl.dtype != "bf16") else 0
     n_krows = 2 * wl.h_kv * wl.n_k if rot else 0
     rope = esz * d * B * (n_qrows + n_krows + 3 * wl.h_kv * n_sep + wl.h_kv * n_cap)
     plan = (wl.n_k if sep_np is not None else 0) + plan_bytes
@@ -465,7 +466,7 @@ def main():
     sb = stage_bytes(wl, None if sep is None else sep.numpy(), int(host_plan["header"].total_bytes))
     stage_roofline = {}
     for name_, nbytes in sb.items():
-        if name_ in stage:
+        if name_ in stage and nbytes > 0 and stage[name_] > 0:
             gbs = nbytes / (stage[name_] * 1e-3) / 1e9
             stage_roofline[name_] = {"bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
                                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}

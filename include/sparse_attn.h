@@ -174,8 +174,9 @@ int sparse_attn_fwd(const sa_mask_t *m, const void *plan, size_t plan_bytes,
 /*
  * The two stages of sparse_attn_fwd as separate calls (same arguments, same
  * workspace), so a caller can time or schedule them apart.  sparse_attn_rope
- * writes the rotated queries and keys, the gathered separator rows and the
- * capped keys into ws; sparse_attn_attend then reads them.  Calling
+ * writes the rotated keys, the gathered separator rows and the capped keys
+ * into ws (and, for f32, the rotated queries; bf16 queries are rotated and
+ * scaled inside sparse_attn_attend); sparse_attn_attend then reads them.  Calling
  * sparse_attn_rope then sparse_attn_attend on one stream equals
  * sparse_attn_fwd.  Errors as for sparse_attn_fwd.
  */

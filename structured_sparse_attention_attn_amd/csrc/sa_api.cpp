@@ -126,7 +126,10 @@ struct WsLayout {
   int64_t total = 0;
 };
 
-WsLayout ws_layout(const sa_mask_t& m, const sa_fwd_args_t& a) {
+// The rotated query copy: fp32 forwards with RoPE read it; the bf16 forward
+// rotates and scales its queries in registers, so only the backward (which
+// reads them pre-scaled) needs it there.
+WsLayout ws_layout(const sa_mask_t& m, const sa_fwd_args_t& a, bool for_bwd = false) {
   WsLayout w;
   const int64_t esz = a.dtype == SA_BF16 ? 2 : 4;
   const int64_t row = esz * a.d;
@@ -136,7 +139,7 @@ WsLayout ws_layout(const sa_mask_t& m, const sa_fwd_args_t& a) {
     off = sa::align_up(off + bytes, 256);
     return o;
   };
-  if (a.rope == SA_ROPE_HALF || a.dtype == SA_BF16)  // bf16 always reads a scaled query copy
+  if (a.dtype == SA_BF16 ? for_bwd : a.rope == SA_ROPE_HALF)
     w.qrot = take((int64_t)a.batch * a.h_q * m.n_q * row);
   if (a.rope == SA_ROPE_HALF) w.krot = take((int64_t)a.batch * a.h_kv * m.n_k * row);
   if (m.kind == SA_MASK_SEPLLM && m.sep != nullptr) {
@@ -163,7 +166,7 @@ struct BwdLayout {
 
 BwdLayout bwd_layout(const sa_mask_t& m, const sa_fwd_args_t& a) {
   BwdLayout L;
-  L.fwd = ws_layout(m, a);
+  L.fwd = ws_layout(m, a, true);
   int64_t off = sa::align_up(L.fwd.total, 256);
   auto take = [&](int64_t bytes) {
     const int64_t o = off;

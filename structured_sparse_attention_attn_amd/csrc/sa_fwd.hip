@@ -10,11 +10,13 @@
 // compacted rows gathered by the RoPE stage.
 //
 // Work units of a tile, all folded into one fp32 online softmax (base-2, the
-// scale times log2(e) applied to the logits):
-//   1. LM-Infinite CAPPED blocks, capped pairs only: raw Q against R(-L) K;
-//   2. SepLLM gathered separator chunks of 64 rows (no mask but the count);
-//   3. the plan's blocks: unmasked when FULL, otherwise the key-set predicate
-//      (LM-Infinite CAPPED blocks exclude their capped pairs here).
+// scale times log2(e) applied to the logits).  The bf16 kernel visits:
+//   1. SepLLM gathered separator chunks of 64 rows (no mask but the count);
+//   2. the plan's blocks: unmasked when FULL, otherwise the key-set predicate
+//      (LM-Infinite CAPPED blocks exclude their capped pairs here);
+//   3. LM-Infinite CAPPED blocks, capped pairs only: raw Q against R(-L) K.
+// (The fp32 kernel visits the capped blocks first.)
+#include <cmath>
 #include <type_traits>
 
 #include "sa_common.h"
@@ -50,6 +52,11 @@ struct FwdArgs {
   float scale_log2;
   int alibi;          // ALiBi-style bias -m_h * min(i-j, L) instead of RoPE (Lambda only)
   float alibi_e;      // slope exponent E: m_h = 2^(-E (h+1) / h_q)
+  // bf16: q is the caller's raw query; the kernel rotates it at q_pos0 + i
+  // (when rot_q) and multiplies it by q_scale itself
+  int rot_q, q_pos0;
+  float q_scale;
+  double th1, th8, th16;  // base^(-2/d) and its 8th and 16th powers: theta_{c+1} = theta_c * th1
 };
 
 // Iterate the units of tile t in order; F(unit, use_raw_q) is called for each.
@@ -198,8 +205,43 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       qf[s] = __builtin_bit_cast(bf16x8, x);
     }
   };
-  if (tu.n_capu > 0) load_q(p.qraw, p.qrB, p.qrH, p.qrT);
-  else load_q(p.q, p.qsB, p.qsH, p.qsT);
+  load_q(p.q, p.qsB, p.qsH, p.qsT);
+
+  // Every unit but the capped ones reads R(pos) q * scale * log2(e), made
+  // here in registers; the capped units (visited last) pair the raw query,
+  // loaded again before them, with R(-L) k.  Lane (l32, hl) holds dims 16 s + 8 hl + e of
+  // its query, so the rotate-half partner of dim c (s < 4) is c + 64 in
+  // qf[s + 4], same lane.  theta_c / (2 pi) comes from products of powers of
+  // base^(-2/d) in fp64 (a few ulp from the direct power); the angle is
+  // reduced in fp64 to a fraction of a turn, and the hardware sine and cosine
+  // take turns.
+  auto prep_q = [&]() {
+    const float qs = p.q_scale;
+    if (p.rot_q) {
+      const double pos = (double)(p.q_pos0 + qi);
+      double th_s = (hl ? p.th8 : 1.0) * 0.15915494309189535;  // theta_{8 hl} / (2 pi)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        double th = th_s;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double rev = pos * th;
+          th *= p.th1;
+          const float f = (float)(rev - rint(rev));
+          const float cs = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
+          const float x1 = (float)qf[s][e], x2 = (float)qf[s + 4][e];
+          qf[s][e] = (__bf16)((x1 * cs - x2 * sn) * qs);
+          qf[s + 4][e] = (__bf16)((x2 * cs + x1 * sn) * qs);
+        }
+        th_s *= p.th16;
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)((float)qf[s][e] * qs);
+    }
+  };
 
   // Online softmax against a reference max m_ref per query (base-2 logits:
   // the queries and capped keys carry scale * log2(e)).  -m_ref enters the
@@ -307,11 +349,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   // some row of the wave has no finite reference yet, the fast path
   // afterwards.  Every wave runs exactly one barrier per unit, whichever loop
   // it is in.
+  // unit order: separator chunks, the plan's blocks, then the capped units
+  const int u_cap = n_units - tu.n_capu;
+  auto unit = [&](int u) { return unit_at<ALIBI>(p, tu, u < u_cap ? u + tu.n_capu : u - u_cap); };
   Unit cur;
   if (n_units > 0) {
-    cur = unit_at<ALIBI>(p, tu, 0);
+    cur = unit(0);
     issue_loads(cur, 0, 0);
   }
+  if (u_cap > 0) prep_q();
   bf16x8 pb[4];  // P(u-1), carried into step u
   int vs_prev = 2, vs_next = 1;  // V slots of units u-1 and u+1 (u % 3 = 0 at u = 0)
   auto step = [&](int u, auto full_path) {
@@ -323,7 +369,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
     if (u > 0) pv(pb, vs_prev);
     Unit nxt;
     if (u + 1 < n_units) {
-      nxt = unit_at<ALIBI>(p, tu, u + 1);
+      nxt = unit(u + 1);
       issue_loads(nxt, buf ^ 1, vs_next);
     }
     vs_prev = vs_prev == 2 ? 0 : vs_prev + 1;
@@ -430,10 +476,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       negm = f32x16{} - m_ref;
     }
 
-    // the rotated queries for the units after the capped ones: loaded once Q
-    // is no longer read by this step, and waited for with the next unit's
-    // K/V at the top of the next step
-    if (u + 1 == tu.n_capu) load_q(p.q, p.qsB, p.qsH, p.qsT);
+    // the raw queries for the capped units: loaded once Q is no longer read
+    // by this step, and waited for with the next unit's K/V at the top of the
+    // next step
+    if (u + 1 == u_cap && tu.n_capu > 0) load_q(p.q, p.qsB, p.qsH, p.qsT);
     cur = nxt;
   };
   int u = 0;
@@ -565,7 +611,7 @@ hipError_t launch_fwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   FwdArgs p;
   memset(&p, 0, sizeof(p));
   const bool rope = a.rope == SA_ROPE_HALF;
-  if (ro.qrot != nullptr) {  // rotated (bf16: also scaled) query copy
+  if (ro.qrot != nullptr) {  // fp32: the rotated query copy
     p.q = ro.qrot;
     p.qsT = a.d; p.qsH = (int64_t)m.n_q * a.d; p.qsB = p.qsH * a.h_q;
   } else {
@@ -614,6 +660,16 @@ hipError_t launch_fwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   p.scale_log2 = a.scale * LOG2E;
   p.alibi = a.rope == SA_ALIBI ? 1 : 0;
   p.alibi_e = p.alibi ? a.rope_base : 0.f;
+  if (a.dtype == SA_BF16) {
+    p.rot_q = rope ? 1 : 0;
+    p.q_pos0 = m.kind == SA_MASK_SEGMENT ? m.prefix_len : 0;
+    p.q_scale = p.scale_log2;
+    if (rope) {
+      p.th1 = std::pow((double)a.rope_base, -2.0 / a.d);
+      p.th8 = std::pow((double)a.rope_base, -16.0 / a.d);
+      p.th16 = std::pow((double)a.rope_base, -32.0 / a.d);
+    }
+  }
   const unsigned grid = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
   if (a.dtype == SA_BF16) {
     if (p.alibi)

@@ -267,11 +267,12 @@ hipError_t launch_rope(const sa_mask_t& m, const sa_plan_header_t& lay, const vo
   memset(&p, 0, sizeof(p));
   const bool rotate = a.rope == SA_ROPE_HALF;
   const bool gather = m.kind == SA_MASK_SEPLLM && m.sep != nullptr;
-  // bf16: the forward reads queries pre-multiplied by scale * log2(e) (its
-  // logits come out of the MFMA in base-2 units), so the query copy is always
-  // written; fp32 keeps the scale in the forward.
-  const bool write_q = rotate || a.dtype == SA_BF16;
-  if (!write_q && !gather) return hipSuccess;
+  // The query copy is written where the caller provides one: the fp32
+  // forward reads rotated queries (it keeps the scale itself); the bf16
+  // backward reads them rotated and pre-multiplied by scale * log2(e).  The
+  // bf16 forward prepares its queries in registers and passes no copy.
+  const bool write_q = ro.qrot != nullptr && (rotate || a.dtype == SA_BF16);
+  if (!write_q && !gather && !rotate) return hipSuccess;
   const char* pb = static_cast<const char*>(plan);
   p.q = a.q;
   p.qsB = a.q_stride[0]; p.qsH = a.q_stride[1]; p.qsT = a.q_stride[2];
@@ -309,7 +310,9 @@ hipError_t launch_rope(const sa_mask_t& m, const sa_plan_header_t& lay, const vo
   const int64_t threads = (int64_t)p.n_pos * (a.d / 16);
   const unsigned wg = (unsigned)ceil_div(threads, 256);
   p.row0 = (rotate || gather) ? 0 : a.batch * a.h_kv;
-  const unsigned chunks = (unsigned)ceil_div((int64_t)a.batch * (a.h_kv + a.h_q) - p.row0, ROPE_ROWS);
+  // rows past the key rows are query rows: only when the query copy is written
+  const int64_t rows = (int64_t)a.batch * a.h_kv + (write_q ? (int64_t)a.batch * a.h_q : 0);
+  const unsigned chunks = (unsigned)ceil_div(rows - p.row0, ROPE_ROWS);
   if (a.dtype == SA_BF16)
     hipLaunchKernelGGL(rope_qk<unsigned short>, dim3(wg, chunks), dim3(256), 0, s, p);
   else

@@ -116,9 +116,13 @@ def test_fwd_workspace_and_validation():
     m = sa.mask(sa.SA_MASK_LAMBDA, 300, 300, n_starting=10, L_pretrain=100)
     a = _args()
     ws = sa.sa_fwd_workspace_bytes(m, a)
-    # rotated q (4 heads) and k (2 heads), plus 64 capped-key rows per kv head
-    expect = 4 * 300 * 256 + 2 * 300 * 256 + 2 * 64 * 256
+    # rotated k (2 heads) plus 64 capped-key rows per kv head (bf16 queries are
+    # rotated inside the forward)
+    expect = 2 * 300 * 256 + 2 * 64 * 256
     assert ws >= expect and ws - expect < 3 * 256
+    # the backward also keeps the rotated, scaled queries (4 heads)
+    bws = sa.sa_bwd_workspace_bytes(m, a)
+    assert bws >= expect + 4 * 300 * 256
     plan_bytes = sa.sa_plan_bytes(m)
     cases = [
         (dict(dtype=5), sa.SA_EINVAL),
@@ -145,9 +149,11 @@ def test_fwd_workspace_and_validation():
                                None) == sa.SA_ENOSPACE
     assert lib.sparse_attn_fwd(ctypes.byref(m), None, plan_bytes, ctypes.byref(a), 512, ws,
                                None) == sa.SA_EINVAL
-    # the ALiBi bias: Lambda masks only; no rotated keys and no capped-key rows in the workspace
+    # the ALiBi bias: Lambda masks only; nothing rotated, so the forward needs no workspace
+    # (its queries are scaled in registers) and the backward only the scaled queries
     al = _args(rope=sa.SA_ALIBI, rope_base=8.0)
-    assert sa.sa_fwd_workspace_bytes(m, al) == 4 * 300 * 256
+    assert sa.sa_fwd_workspace_bytes(m, al) == 0
+    assert sa.sa_bwd_workspace_bytes(m, al) >= 4 * 300 * 256
     ms = sa.mask(sa.SA_MASK_SEPLLM, 300, 300, a=4, w=16)
     assert lib.sparse_attn_fwd(ctypes.byref(ms), 256, sa.sa_plan_bytes(ms), ctypes.byref(al), 512,
                                1 << 20, None) == sa.SA_EUNSUPPORTED
