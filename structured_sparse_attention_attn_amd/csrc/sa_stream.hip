@@ -14,9 +14,9 @@
 // Per step: stream_insert (one work group per (sequence, kv head): the moved
 // and compressed rows, the new key and value, the rotated queries), then
 // decode_attn (split over slots: partial softmax per 64 slots, over the held
-// ranges the step leaves) and decode_combine (the splits merged; then one
-// work group per sequence records each slot's token index and separator flag
-// and advances the counters).
+// ranges the step leaves) and decode_combine (the splits merged; its extra
+// work groups, one per sequence, record each slot's token index and
+// separator flag and advance the counters).
 #include "sa_common.h"
 
 namespace sa {
@@ -230,8 +230,11 @@ __global__ __launch_bounds__(256) void stream_insert(StreamArgs p) {
 }
 
 // Token index, flag and counters of sequence b after the step.  Called by
-// every thread of a work group (its barriers are uniform); wave 0 works.
-__device__ inline void update_ctrl(const StreamArgs& p, int b, int* list_src, int* list_dst) {
+// every thread of a work group (its barriers are uniform); wave 0 works.  On
+// compression the survivors' token indices and flags are copied straight to
+// their ring slots: the ring and the Past / evicted-local slots they come
+// from are disjoint, so no copy reads a slot another has written.
+__device__ inline void update_ctrl(const StreamArgs& p, int b) {
   const int lane = threadIdx.x & 63;
   const bool w0 = threadIdx.x < 64;
   int* ct = p.ctrl + b * 8;
@@ -241,15 +244,29 @@ __device__ inline void update_ctrl(const StreamArgs& p, int b, int* list_src, in
   int n_sep = ct[C_NSEP], head = ct[C_SEPHEAD], n_past = ct[C_NPAST];
   int n_local = ct[C_NLOCAL], lhead = ct[C_LOCALHEAD], n_init = ct[C_NINIT];
   if (sp.compress) {
-    int n_new = 0, n = 0;
-    if (w0) n = compress_list(p, b, ct, sp, lane, list_src, list_dst, &n_new);
-    __syncthreads();
-    if (w0)
-      for (int r = lane; r < n; r += 64) {
-        pos[list_dst[r]] = pos[list_src[r]];
-        fl[list_dst[r]] = fl[list_src[r]];
+    auto src_of = [&](int i) { return i < sp.n_past ? p.a + p.s + i : sp.ms; };
+    int n_new = 0;
+    if (w0) {
+      for (int i0 = 0; i0 < p.P; i0 += 64) {
+        const int i = i0 + lane;
+        n_new += __popcll(__ballot(i < p.P && fl[src_of(i)] != 0));
       }
-    __syncthreads();
+      const int first = max(0, n_new - p.s);  // appends before this one are overwritten
+      int rank0 = 0;
+      for (int i0 = 0; i0 < p.P; i0 += 64) {
+        const int i = i0 + lane;
+        const bool f = i < p.P && fl[src_of(i)] != 0;
+        const unsigned long long m = __ballot(f);
+        const int k = rank0 + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+        if (f && k >= first) {
+          const int dst = p.a + (head + n_sep + k) % p.s;
+          pos[dst] = pos[src_of(i)];
+          fl[dst] = fl[src_of(i)];
+        }
+        rank0 += __popcll(m);
+      }
+    }
+    __syncthreads();  // (only thread 0 uses the counts below; wave 0's lanes agree on n_new)
     head = (head + max(0, n_sep + n_new - p.s)) % p.s;
     n_sep = min(p.s, n_sep + n_new);
     n_past = 0;
@@ -454,27 +471,70 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
   }
 }
 
-// o = sum_i 2^(m_i - m) o_i / sum_i 2^(m_i - m) l_i over the splits; the work
-// group of each sequence's first query head then advances its counters.
-__global__ __launch_bounds__(128) void decode_combine(StreamArgs p) {
-  __shared__ int list_src[4096];
-  __shared__ int list_dst[4096];
-  const int row = blockIdx.x;  // b * h_q + hq
-  const int col = threadIdx.x;
-  const float* pr = p.part + (int64_t)row * p.n_split * (128 + 2);
-  float m = -__builtin_huge_valf();
-  for (int i = 0; i < p.n_split; ++i) m = fmaxf(m, pr[i * 130]);
-  float l = 0.f, acc = 0.f;
-  for (int i = 0; i < p.n_split; ++i) {
-    const float mi = pr[i * 130];
-    if (mi == -__builtin_huge_valf()) continue;
-    const float f = __builtin_amdgcn_exp2f(mi - m);
-    l = fmaf(pr[i * 130 + 1], f, l);
-    acc = fmaf(pr[i * 130 + 2 + col], f, acc);
+// o = sum_i 2^(m_i - m) o_i / sum_i 2^(m_i - m) l_i over the splits, one
+// work group per (sequence, query head): the split weights go to LDS, then
+// wave w sums splits w, w + 4, ... over all 128 columns (two per lane, eight
+// splits' loads in flight), and the four waves' sums are added.  Work groups
+// past the last row each advance one sequence's counters.
+constexpr int MAX_SPLIT = 1024;  // 65536 slots / SPLIT
+
+__global__ __launch_bounds__(256) void decode_combine(StreamArgs p) {
+  __shared__ float wgt[MAX_SPLIT];
+  __shared__ float red[4][128];
+  __shared__ float rm[4], rl[4];
+  const int n_rows = p.B * p.h_q;
+  if ((int)blockIdx.x >= n_rows) {
+    update_ctrl(p, blockIdx.x - n_rows);
+    return;
   }
-  p.o[(int64_t)row * 128 + col] = f2bf(acc / l);
-  if (p.lse != nullptr && col == 0) p.lse[row] = (m + __log2f(l)) * 0.6931471805599453f;
-  if (row % p.h_q == 0) update_ctrl(p, row / p.h_q, list_src, list_dst);
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int ns = p.n_split;
+  const float* pr = p.part + (int64_t)row * ns * 130;
+  float m = -__builtin_huge_valf();
+  for (int i = tid; i < ns; i += 256) m = fmaxf(m, pr[i * 130]);
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  if (lane == 0) rm[wv] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(rm[0], rm[1]), fmaxf(rm[2], rm[3]));
+  float l = 0.f;
+  for (int i = tid; i < ns; i += 256) {
+    const float mi = pr[i * 130];
+    const float f = mi == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(mi - m);
+    wgt[i] = f;
+    l = fmaf(pr[i * 130 + 1], f, l);
+  }
+  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+  if (lane == 0) rl[wv] = l;
+  __syncthreads();
+  l = rl[0] + rl[1] + rl[2] + rl[3];
+  float2 acc = make_float2(0.f, 0.f);
+  const float* col = pr + 2 + 2 * lane;
+  int i = wv;
+  for (; i + 28 < ns; i += 32) {  // eight splits per round
+    float2 x[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[u] = *reinterpret_cast<const float2*>(col + (int64_t)(i + 4 * u) * 130);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float f = wgt[i + 4 * u];
+      acc.x = fmaf(f, x[u].x, acc.x);
+      acc.y = fmaf(f, x[u].y, acc.y);
+    }
+  }
+  for (; i < ns; i += 4) {
+    const float2 x = *reinterpret_cast<const float2*>(col + (int64_t)i * 130);
+    const float f = wgt[i];
+    acc.x = fmaf(f, x.x, acc.x);
+    acc.y = fmaf(f, x.y, acc.y);
+  }
+  red[wv][2 * lane] = acc.x;
+  red[wv][2 * lane + 1] = acc.y;
+  __syncthreads();
+  if (tid < 128) {
+    const float sum = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+    p.o[(int64_t)row * 128 + tid] = f2bf(sum / l);
+    if (p.lse != nullptr && tid == 0) p.lse[row] = (m + __log2f(l)) * 0.6931471805599453f;
+  }
 }
 
 __global__ void stream_zero(int* ctrl, int n) {
@@ -558,7 +618,7 @@ hipError_t launch_decode_step(const sa_stream_cfg_t& cfg, void* state, const voi
     hipLaunchKernelGGL(decode_attn<true>, dim3((unsigned)(cfg.batch * cfg.h_kv * L.n_split)), dim3(256), 0, s, p);
   else
     hipLaunchKernelGGL(decode_attn<false>, dim3((unsigned)(cfg.batch * cfg.h_kv * L.n_split)), dim3(256), 0, s, p);
-  hipLaunchKernelGGL(decode_combine, dim3((unsigned)(cfg.batch * cfg.h_q)), dim3(128), 0, s, p);
+  hipLaunchKernelGGL(decode_combine, dim3((unsigned)(cfg.batch * cfg.h_q + cfg.batch)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
