@@ -38,12 +38,11 @@ struct MidArgs {
   float cosL[64], sinL[64];  // cos, sin of L * theta_c (rotate-half pairs); identity without RoPE
 };
 
-__device__ inline bool better(float x, int j, float y, int jy) { return x > y || (x == y && j < jy); }
+__device__ inline bool better(float x, int j, float y, int jy) { return (x > y) | ((x == y) & (j < jy)); }
 
 __global__ __launch_bounds__(256, 2) void mid_select(MidArgs p) {
   __shared__ __attribute__((aligned(16))) char K0[BLK_BYTES];
   __shared__ __attribute__((aligned(16))) char K1[BLK_BYTES];
-  __shared__ float cand[4 * 32 * 64];  // per wave: 32 candidate scores x 64 lanes
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
@@ -109,6 +108,9 @@ __global__ __launch_bounds__(256, 2) void mid_select(MidArgs p) {
   const int64_t kst = p.ksT * 2;
   const int kf = swzf(l32) ^ hl;
   const int jmax = qi - p.L - 1;  // this query's last middle key
+  const int wave_q0 = q0 + wid * 32;
+  const int wave_jmin = wave_q0 - p.L - 1;      // the wave's smallest last middle key
+  const bool wave_full = wave_q0 + 31 < p.n_q;  // every lane holds a query
 
   auto step = [&](int u, char* Kc, char* Kn) __attribute__((always_inline)) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -134,50 +136,70 @@ __global__ __launch_bounds__(256, 2) void mid_select(MidArgs p) {
       s[0] = h0 + g0;
       s[1] = h1 + g1;
     }
-    // candidates: register r of half mb is key j0 + 32 mb + 8 (r / 4) + r % 4.
-    // A bit per candidate that beats this lane's k-th best; only those are
-    // inserted, one per lane per round, their scores read back from LDS.
+    // candidates: register r of half mb is key j0 + 32 mb + 8 (r / 4) + r % 4,
+    // so register order is ascending key order.  Keys that are not middle keys
+    // of the lane's query are set to -inf (only blocks at the edges of the
+    // wave's middle range have any).  Then, while the block's largest score
+    // beats the lane's k-th best, its first (lowest-index) occurrence is
+    // inserted and removed; once the first occurrence of the maximum fails,
+    // every remaining key fails too.  All of it branch-free per lane.
     const int j0 = blk * BK + 4 * hl;
-    unsigned pass = 0;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = j0 + 32 * mb + 8 * (r >> 2) + (r & 3);
-        const bool ok = qok & (j >= p.n_s) & (j <= jmax) & (j < p.n_k);
-        pass |= (ok && better(s[mb][r], j, thr_v, thr_i)) ? (1u << (16 * mb + r)) : 0u;
-      }
-    if (__any(pass != 0)) {
-      float* my = cand + wid * (32 * 64) + lane;
+    if (!(blk * BK >= p.n_s && blk * BK + BK - 1 <= wave_jmin && blk * BK + BK <= p.n_k && wave_full)) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) my[(16 * mb + r) * 64] = s[mb][r];
-      while (__any(pass != 0)) {
-        if (pass != 0) {
-          const int rr = __builtin_ctz(pass);
-          pass &= pass - 1;
-          float x = my[rr * 64];
-          int j = j0 + 32 * (rr >> 4) + 8 * ((rr & 15) >> 2) + (rr & 3);
-          if (better(x, j, thr_v, thr_i)) {
+        for (int r = 0; r < 16; ++r) {
+          const int j = j0 + 32 * mb + 8 * (r >> 2) + (r & 3);
+          const bool ok = qok & (j >= p.n_s) & (j <= jmax) & (j < p.n_k);
+          s[mb][r] = ok ? s[mb][r] : -__builtin_huge_valf();
+        }
+    }
+    auto block_max = [&]() {
+      float mx = s[0][0];
 #pragma unroll
-            for (int e = 0; e < KMID_MAX; ++e) {
-              if (e < kk && better(x, j, bv[e], bi[e])) {
-                const float tv = bv[e];
-                const int ti = bi[e];
-                bv[e] = x;
-                bi[e] = j;
-                x = tv;
-                j = ti;
-              }
-            }
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-            for (int e = 0; e < KMID_MAX; ++e)
-              if (e == kk - 1) {
-                thr_v = bv[e];
-                thr_i = bi[e];
-              }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+      return mx;
+    };
+    float mx = block_max();
+    bool act = (mx != -__builtin_huge_valf()) & (mx >= thr_v);
+    while (__any(act)) {
+      if (act) {
+        bool found = false;
+        int jc = 0;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bool hit = !found & (s[mb][r] == mx);
+            jc = hit ? j0 + 32 * mb + 8 * (r >> 2) + (r & 3) : jc;
+            s[mb][r] = hit ? -__builtin_huge_valf() : s[mb][r];
+            found = found | hit;
           }
+        if (better(mx, jc, thr_v, thr_i)) {
+          float x = mx;
+          int j = jc;
+#pragma unroll
+          for (int e = 0; e < KMID_MAX; ++e) {
+            const bool sw = (e < kk) & better(x, j, bv[e], bi[e]);
+            const float tv = bv[e];
+            const int ti = bi[e];
+            bv[e] = sw ? x : tv;
+            bi[e] = sw ? j : ti;
+            x = sw ? tv : x;
+            j = sw ? ti : j;
+          }
+#pragma unroll
+          for (int e = 0; e < KMID_MAX; ++e)
+            if (e == kk - 1) {
+              thr_v = bv[e];
+              thr_i = bi[e];
+            }
+          mx = block_max();
+          act = (mx != -__builtin_huge_valf()) & (mx >= thr_v);
+        } else {
+          act = false;
         }
       }
     }
