@@ -118,11 +118,12 @@ __global__ __launch_bounds__(256, 2) void mid_select(MidArgs p) {
     const int blk = blk_lo + u;
     if (u + 1 < n_blk)
       dma_block(kb + (int64_t)(blk + 1) * BK * kst, kst, min(BK, p.n_k - (blk + 1) * BK), Kn, wid, lane);
-    // S^T = K q_hi^T + K q_lo^T: four independent accumulation chains
+    // S^T = K q_hi^T + K q_lo^T: both parts accumulate into one chain per
+    // 32-key half, the two halves interleaved
     f32x16 s[2];
     {
       const char* kl = Kc + l32 * 256;
-      f32x16 h0 = f32x16{}, h1 = f32x16{}, g0 = f32x16{}, g1 = f32x16{};
+      f32x16 h0 = f32x16{}, h1 = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         const int off = ((2 * ks) ^ kf) << 4;
@@ -130,11 +131,11 @@ __global__ __launch_bounds__(256, 2) void mid_select(MidArgs p) {
         const bf16x8 a1 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + 32 * 256 + off));
         h0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qh[ks], h0, 0, 0, 0);
         h1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qh[ks], h1, 0, 0, 0);
-        g0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qlo[ks], g0, 0, 0, 0);
-        g1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qlo[ks], g1, 0, 0, 0);
+        h0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qlo[ks], h0, 0, 0, 0);
+        h1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qlo[ks], h1, 0, 0, 0);
       }
-      s[0] = h0 + g0;
-      s[1] = h1 + g1;
+      s[0] = h0;
+      s[1] = h1;
     }
     // candidates: register r of half mb is key j0 + 32 mb + 8 (r / 4) + r % 4,
     // so register order is ascending key order.  Keys that are not middle keys
