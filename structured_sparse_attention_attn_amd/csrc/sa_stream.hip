@@ -298,28 +298,21 @@ __device__ inline void update_ctrl(const StreamArgs& p, int b) {
   }
 }
 
-// The held slots as one virtual range: Initial, Separator, Past, Local.
+// Held slots per part after a step.
 struct Held {
   int n_init, n_sep, n_past, n_local;
-  __device__ int count() const { return n_init + n_sep + n_past + n_local; }
 };
 
-__device__ inline int held_slot(const StreamArgs& p, const Held& h, int v) {
-  if (v < h.n_init) return v;
-  v -= h.n_init;
-  if (v < h.n_sep) return p.a + v;
-  v -= h.n_sep;
-  if (v < h.n_past) return p.a + p.s + v;
-  v -= h.n_past;
-  return p.a + p.s + p.P + v;
-}
-
 // Partial softmax of the group's queries over 64 held slots: (m, l, o) per
-// query head in base 2.  Every K and V byte of the slots is requested at the
-// start: thread (slot r, quarter qq) holds a quarter of r's key for the
-// logits; thread (slot group sg, column chunk cc) holds columns 8 cc .. +7 of
-// the values of slots 4 sg .. 4 sg + 3 for the weighted sum, reduced over the
-// 16 slot groups by shuffles within a wave and LDS across the 4 waves.
+// query head in base 2, over 64 consecutive physical slots (the held ones
+// among them).  Every K and V byte of the slots is requested first, before
+// the counters say which slots are held: thread (slot r, quarter qq) holds a
+// quarter of r's key for the logits; thread (slot group sg, column chunk cc)
+// holds columns 8 cc .. +7 of the values of slots 4 sg .. 4 sg + 3 for the
+// weighted sum, reduced over the 16 slot groups by shuffles within a wave and
+// LDS across the 4 waves.  Slots not held take no part: their logits are
+// -inf and their values are replaced by zeros (never-written slots may hold
+// any bits).
 template <bool LAM>
 __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
   __shared__ float qs[MAX_G][128];
@@ -329,6 +322,24 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int bg = blockIdx.x / p.n_split, spl = blockIdx.x % p.n_split;
   const int b = bg / p.h_kv, g = bg % p.h_kv;
+  const int v0 = spl * SPLIT;                      // first physical slot
+  const int nslot = min(SPLIT, p.c - v0);          // slots of this work group
+  const char* K = p.kc + ((int64_t)b * p.h_kv + g) * p.c * 256;
+  const char* V = p.vc + ((int64_t)b * p.h_kv + g) * p.c * 256;
+  const int r = tid >> 2, qq = tid & 3;
+  uint4 kx4[4];
+  {
+    const uint4* kp = reinterpret_cast<const uint4*>(K + (int64_t)(v0 + (r < nslot ? r : 0)) * 256 + qq * 64);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kx4[e] = kp[e];
+  }
+  const int sg = tid >> 4, cc = tid & 15;
+  uint4 vx4[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = 4 * sg + i;
+    vx4[i] = *reinterpret_cast<const uint4*>(V + (int64_t)(v0 + (rr < nslot ? rr : 0)) * 256 + cc * 16);
+  }
   // the held ranges after this step, from the counters before it (they are
   // updated by decode_combine, after every read of them in this step)
   __shared__ int n_new_s;
@@ -358,29 +369,18 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
   } else if (sp.evict && !p.lambda) {
     h.n_past += 1;
   }
-  const int nv = h.count();
-  const int v0 = spl * SPLIT;
-  const int nslot = max(0, min(SPLIT, nv - v0));
-  const char* K = p.kc + ((int64_t)b * p.h_kv + g) * p.c * 256;
-  const char* V = p.vc + ((int64_t)b * p.h_kv + g) * p.c * 256;
-  // loads
-  const int r = tid >> 2, qq = tid & 3;
-  const bool kok = r < nslot;
-  uint4 kx4[4];
-  {
-    const int slot = kok ? held_slot(p, h, v0 + r) : 0;
-    const uint4* kp = reinterpret_cast<const uint4*>(K + (int64_t)slot * 256 + qq * 64);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) kx4[e] = kok ? kp[e] : make_uint4(0, 0, 0, 0);
-  }
-  const int sg = tid >> 4, cc = tid & 15;
-  uint4 vx4[4];
+  // Initial [0, n_init), Separator [a, a + n_sep), Past [a + s, a + s + n_past),
+  // Local [a + s + P, a + s + P + n_local): the rings fill from their first slot
+  auto held = [&](int x) {
+    const int x1 = x - p.a, x2 = x1 - p.s, x3 = x2 - p.P;
+    return (x < h.n_init) | ((x1 >= 0) & (x1 < h.n_sep)) | ((x2 >= 0) & (x2 < h.n_past)) |
+           ((x3 >= 0) & (x3 < h.n_local));
+  };
+  const bool kok = (r < nslot) && held(v0 + r);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int rr = 4 * sg + i;
-    const bool ok = rr < nslot;
-    const int slot = ok ? held_slot(p, h, v0 + rr) : 0;
-    vx4[i] = ok ? *reinterpret_cast<const uint4*>(V + (int64_t)slot * 256 + cc * 16) : make_uint4(0, 0, 0, 0);
+    if (!((rr < nslot) && held(v0 + rr))) vx4[i] = make_uint4(0, 0, 0, 0);
   }
   for (int e = tid; e < p.group * 128; e += 256)
     qs[e >> 7][e & 127] = p.qrot[((int64_t)b * p.h_q + g * p.group + (e >> 7)) * 128 + (e & 127)];
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
     }
     // LAMBDA: a starting key j (its slot index) farther than L from t takes the
     // capped logit computed by stream_insert
-    const int jslot = kok ? held_slot(p, h, v0 + r) : 0;
+    const int jslot = v0 + r;
     const bool capped = LAM && kok && jslot < p.a && sp.t - jslot > p.L;
     for (int gq = 0; gq < p.group; ++gq) {
       float acc = 0.f;
@@ -417,12 +417,12 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
     const float x = ps[gq][lane];
     float m = x;
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-    const float e = (lane < nslot) ? __builtin_amdgcn_exp2f(x - m) : 0.f;
+    const float e = x == -__builtin_huge_valf() ? 0.f : __builtin_amdgcn_exp2f(x - m);
     float l = e;
     for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
     ps[gq][lane] = e;
     if (lane == 0) {
-      mrow[gq] = nslot > 0 ? m : -__builtin_huge_valf();
+      mrow[gq] = m;  // -inf when no slot of the group is held
       lrow[gq] = l;
     }
   }
