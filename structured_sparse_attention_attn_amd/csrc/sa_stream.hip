@@ -50,6 +50,11 @@ struct StreamArgs {
 };
 
 __device__ inline float bf2f(u16 x) { return __uint_as_float(((unsigned)x) << 16); }
+// element e (0..7, compile-time) of 8 packed bf16 values, widened to fp32
+__device__ inline float bf_at(const uint4& x, int e) {
+  const unsigned w = (e >> 1) == 0 ? x.x : (e >> 1) == 1 ? x.y : (e >> 1) == 2 ? x.z : x.w;
+  return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+}
 __device__ inline u16 f2bf(float f) {  // round to nearest even (finite inputs)
   const unsigned u = __float_as_uint(f);
   return (u16)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
@@ -385,18 +390,8 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
   for (int e = tid; e < p.group * 128; e += 256)
     qs[e >> 7][e & 127] = p.qrot[((int64_t)b * p.h_q + g * p.group + (e >> 7)) * 128 + (e & 127)];
   __syncthreads();
-  // logits
+  // logits (bf16 elements widened where they are used: fewer live registers)
   {
-    float kx[32];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const unsigned xs[4] = {kx4[e].x, kx4[e].y, kx4[e].z, kx4[e].w};
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        kx[8 * e + 2 * f] = bf2f((u16)(xs[f] & 0xffffu));
-        kx[8 * e + 2 * f + 1] = bf2f((u16)(xs[f] >> 16));
-      }
-    }
     // LAMBDA: a starting key j (its slot index) farther than L from t takes the
     // capped logit computed by stream_insert
     const int jslot = v0 + r;
@@ -404,7 +399,7 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
     for (int gq = 0; gq < p.group; ++gq) {
       float acc = 0.f;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) acc = fmaf(kx[e], qs[gq][qq * 32 + e], acc);
+      for (int e = 0; e < 32; ++e) acc = fmaf(bf_at(kx4[e >> 3], e & 7), qs[gq][qq * 32 + e], acc);
       acc += __shfl_xor(acc, 1, 4);
       acc += __shfl_xor(acc, 2, 4);
       if (capped) acc = p.capl[((int64_t)b * p.h_q + g * p.group + gq) * p.a + jslot];
@@ -428,16 +423,6 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
   }
   __syncthreads();
   // weighted values: this thread's 4 slots x 8 columns, then the reductions
-  float vf[4][8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const unsigned xs[4] = {vx4[i].x, vx4[i].y, vx4[i].z, vx4[i].w};
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      vf[i][2 * f] = bf2f((u16)(xs[f] & 0xffffu));
-      vf[i][2 * f + 1] = bf2f((u16)(xs[f] >> 16));
-    }
-  }
   for (int gq = 0; gq < p.group; ++gq) {
     float acc[8];
 #pragma unroll
@@ -446,7 +431,7 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
     for (int i = 0; i < 4; ++i) {
       const float pw = ps[gq][4 * sg + i];
 #pragma unroll
-      for (int c = 0; c < 8; ++c) acc[c] = fmaf(pw, vf[i][c], acc[c]);
+      for (int c = 0; c < 8; ++c) acc[c] = fmaf(pw, bf_at(vx4[i], c), acc[c]);
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
