@@ -375,16 +375,23 @@ __device__ inline int first_gathering_tile(const BwdArgs& p, int c0) {
   return lo;
 }
 
-// The item of block blk in tile t, or -1 (items are ascending by block).
+// The item of block blk in tile t, or -1.  The plan lists a tile's leading
+// blocks 0 .. lo_end-1 and then one run of consecutive blocks ending at the
+// tile's last item, so blk can only sit at index lo + blk or at
+// (hi - 1) - (last block - blk): two probes instead of a search (each search
+// step is a dependent scalar load).
 __device__ inline int find_item(const BwdArgs& p, int t, int blk) {
-  int lo = ld_uniform(p.tile_ptr + t), hi = ld_uniform(p.tile_ptr + t + 1);
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    const int it = ld_uniform(p.items + mid);
-    const int bb = it & 0xffffff;
-    if (bb == blk) return it;
-    if (bb < blk) lo = mid + 1;
-    else hi = mid;
+  const int lo = ld_uniform(p.tile_ptr + t), hi = ld_uniform(p.tile_ptr + t + 1);
+  if (hi <= lo) return -1;
+  const int last = ld_uniform(p.items + hi - 1) & 0xffffff;
+  const int iw = hi - 1 - (last - blk);
+  if (blk <= last && iw >= lo) {
+    const int it = ld_uniform(p.items + iw);
+    if ((it & 0xffffff) == blk) return it;
+  }
+  if (blk < hi - lo) {
+    const int it = ld_uniform(p.items + lo + blk);
+    if ((it & 0xffffff) == blk) return it;
   }
   return -1;
 }

@@ -169,6 +169,8 @@ __global__ __launch_bounds__(FIN_THREADS) void plan_finish(PlanArgs p) {
       const int start = carry + ex;
       p.tile_ptr[t] = start;
       int k = start;
+      // leading blocks 0 .. lo_end-1, then one run of consecutive blocks (the
+      // backward's key-major kernel finds a block's item from this layout)
       for (int b = 0; b < r.lo_end; ++b) p.items[k++] = b | (item_flags(p, r, b) << 24);
       for (int b = r.hi0; b <= r.hi1; ++b) p.items[k++] = b | (item_flags(p, r, b) << 24);
       int sc = 0;
