@@ -563,6 +563,9 @@ def test_stream_decode(sa, case):
     log(f"stream decode {case}: {cfg}")
     q, k, v, flags = W.make_decode_stream(B, hq, hkv, d, cfg["n"], seed=1300 + case, p_sep=cfg["p"])
     dec = StreamDecoder(B, hq, hkv, d, cfg["a"], cfg["s"], cfg["w"], cfg["c"], rope_base=cfg["rope"])
+    # slots never written hold NaN bit patterns: a slot that is not held must take no part
+    dec.state.fill_(0xFF)
+    dec.reset()
     scale = d ** -0.5
     group = hq // hkv
     lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
@@ -696,6 +699,8 @@ def test_lambda_decode(sa, case):
     log(f"lambda decode {case}: {cfg}")
     q, k, v, _ = W.make_decode_stream(B, hq, hkv, d, cfg["n"], seed=1500 + case, p_sep=0.0)
     dec = StreamDecoder(B, hq, hkv, d, cfg["n_s"], rope_base=cfg["rope"], kind="lambda", L_pretrain=cfg["L"])
+    dec.state.fill_(0xFF)  # NaN bit patterns in every slot not yet written
+    dec.reset()
     scale = d ** -0.5
     group = hq // hkv
     lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
