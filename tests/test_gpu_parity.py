@@ -480,6 +480,39 @@ def test_bwd_small(sa, case):
             bwd_compare(f"b{b} {name}", to64(got), ref)
 
 
+@pytest.mark.parametrize("case", [1, 3, 6])
+def test_bwd_strided(sa, case):
+    """The backward on [B, T, H, d] storage viewed as [B, H, T, d]: strided q, k, v, dout
+    and gradients written through the same strides."""
+    mode, kw, rope, alibi = BWD_SMALL[case]
+    wl = W.small(mode, seed=500 + case, rope_base=rope, alibi_exp=alibi, **kw)
+    log(f"bwd strided {case}: {mode} {kw} rope={rope} alibi={alibi}")
+    inp = W.make_small_inputs(wl)
+    strided = lambda t: t.permute(0, 2, 1, 3).contiguous().cuda().permute(0, 2, 1, 3)  # noqa: E731
+    q, k, v = (strided(inp[x]) for x in ("q", "k", "v"))
+    assert q.stride(2) != q.shape[3]
+    sep = inp.get("sep")
+    sa_obj = device_mask(wl, None if sep is None else sep.cuda())
+    sa_obj.build_plan()
+    lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
+    o = sa_obj.forward(q, k, v, o=strided(torch.zeros(tuple(q.shape), dtype=q.dtype)), lse=lse,
+                       rope_base=wl.rope_base, scale=wl.scale, alibi_exp=wl.alibi_exp)
+    dout_c = W.make_grad(tuple(q.shape), seed=900 + case)
+    dq, dk, dv = sa_obj.backward(q, k, v, o, lse, strided(dout_c), rope_base=wl.rope_base, scale=wl.scale,
+                                 alibi_exp=wl.alibi_exp, dq=strided(torch.zeros(tuple(q.shape), dtype=q.dtype)),
+                                 dk=strided(torch.zeros(tuple(k.shape), dtype=k.dtype)),
+                                 dv=strided(torch.zeros(tuple(v.shape), dtype=v.dtype)))
+    torch.cuda.synchronize()
+    assert dq.stride() == q.stride() and dk.stride() == k.stride()
+    spec = spec_of(wl, None if sep is None else sep.numpy())
+    for b in range(wl.batch):
+        rq, rk, rv = O.attention_backward(to64(inp["q"][b]), to64(inp["k"][b]), to64(inp["v"][b]),
+                                          to64(dout_c[b]), spec, wl.rope_base, wl.scale,
+                                          alibi_exp=wl.alibi_exp)
+        for name, got, ref in (("dq", dq[b], rq), ("dk", dk[b], rk), ("dv", dv[b], rv)):
+            bwd_compare(f"b{b} {name}", to64(got), ref)
+
+
 def _workload_bwd_parity(sa, cid, dq_heads, n_random, key_block, dk_kv_head, nonsep_only=False):
     """Backward at a workload's full size: dQ on sampled rows of some heads; dK, dV on one
     key block of one kv head, from every query row that sees a key of that block (the
