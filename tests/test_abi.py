@@ -221,3 +221,84 @@ def test_segment_carry_validation():
     # nothing to do (no local rows kept, no long heads): returns before any device call
     assert call(n_local=H, tail_len=0) == sa.SA_OK
 
+
+
+def _grads(**kw):
+    g = sa.sa_bwd_args_t()
+    for name in ("dout", "dq", "dk", "dv"):
+        setattr(g, name, 4096)
+        getattr(g, name + "_stride")[:] = [4 * 300 * 128, 300 * 128, 128]
+    for k, v in kw.items():
+        setattr(g, k, v)
+    return g
+
+
+def test_bwd_validation():
+    lib = sa._lib
+    m = sa.mask(sa.SA_MASK_LAMBDA, 300, 300, n_starting=10, L_pretrain=100)
+    plan_bytes = sa.sa_plan_bytes(m)
+    a = _args(lse=8192)
+    ws = sa.sa_bwd_workspace_bytes(m, a)
+
+    def call(args=a, grads=_grads(), plan=256, pb=plan_bytes, wsp=1 << 20, wsb=ws):
+        return lib.sparse_attn_bwd(ctypes.byref(m), plan, pb, ctypes.byref(args),
+                                   None if grads is None else ctypes.byref(grads), wsp, wsb, None)
+
+    assert call(args=_args()) == sa.SA_EINVAL and "lse" in sa.sa_last_error()  # no lse
+    assert call(args=_args(lse=8192, dtype=sa.SA_F32, d=64)) == sa.SA_EUNSUPPORTED
+    assert call(grads=None) == sa.SA_EINVAL
+    assert call(grads=_grads(dout=None)) == sa.SA_EINVAL
+    bad = _grads()
+    bad.dk_stride[1] = 100  # 200 bytes: not a multiple of 16
+    assert call(grads=bad) == sa.SA_EINVAL
+    assert call(plan=None) == sa.SA_EINVAL
+    assert call(pb=plan_bytes - 1) == sa.SA_ENOSPACE
+    assert call(wsb=ws - 1) == sa.SA_ENOSPACE
+    assert call(wsp=None) == sa.SA_EINVAL
+
+
+def test_stream_cfg_validation():
+    ok = sa.stream_cfg(2, 8, 2, 128, 4, 8, 16, 60, rope_base=10000.0)
+    assert sa.sa_stream_state_bytes(ok) > 0 and sa.sa_decode_workspace_bytes(ok) > 0
+    lam = sa.stream_cfg(2, 8, 2, 128, 10, rope_base=10000.0, kind=sa.SA_MASK_LAMBDA, L_pretrain=4096,
+                        s=0, w=0, c=0)
+    assert sa.sa_stream_state_bytes(lam) > 0
+    bad = [
+        (sa.stream_cfg(2, 8, 2, 128, 4, 8, 16, 28), sa.SA_EINVAL),          # c <= a + s + w
+        (sa.stream_cfg(2, 8, 2, 128, 4, 0, 16, 60), sa.SA_EINVAL),          # s = 0
+        (sa.stream_cfg(2, 8, 2, 128, 4, 8, 16, 5000), sa.SA_EUNSUPPORTED),  # c > 4096
+        (sa.stream_cfg(2, 18, 2, 128, 4, 8, 16, 60), sa.SA_EUNSUPPORTED),   # 9 query heads per kv head
+        (sa.stream_cfg(2, 8, 3, 128, 4, 8, 16, 60), sa.SA_EINVAL),          # h_q not a multiple of h_kv
+        (sa.stream_cfg(2, 8, 2, 64, 4, 8, 16, 60), sa.SA_EUNSUPPORTED),     # d = 64
+        (sa.stream_cfg(0, 8, 2, 128, 4, 8, 16, 60), sa.SA_EINVAL),          # batch 0
+        (sa.stream_cfg(2, 8, 2, 128, 4, 8, 16, 60, rope_base=0.5), sa.SA_EINVAL),
+        (sa.stream_cfg(2, 8, 2, 128, 4, 8, 16, 60, kind=7), sa.SA_EINVAL),
+        (sa.stream_cfg(2, 8, 2, 128, 10, 0, 0, 0, kind=sa.SA_MASK_LAMBDA, L_pretrain=65530), sa.SA_EINVAL),
+    ]
+    for cfg, code in bad:
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sa_stream_state_bytes(cfg)
+        assert e.value.code == code, (cfg.batch, cfg.h_q, cfg.h_kv, cfg.d, cfg.a, cfg.s, cfg.w, cfg.c)
+    # decode step: state and workspace sizes are checked before any launch
+    lib = sa._lib
+    sb, wb = sa.sa_stream_state_bytes(ok), sa.sa_decode_workspace_bytes(ok)
+    step = lambda st, sbytes, w, wbytes, is_sep=512: lib.sparse_attn_decode_step(  # noqa: E731
+        ctypes.byref(ok), st, sbytes, 256, 256, 256, is_sep, 256, None, w, wbytes, None)
+    assert step(1 << 20, sb - 1, 1 << 24, wb) == sa.SA_ENOSPACE
+    assert step(1 << 20, sb, 1 << 24, wb - 1) == sa.SA_ENOSPACE
+    assert step(None, sb, 1 << 24, wb) == sa.SA_EINVAL
+    assert step(1 << 20, sb, 1 << 24, wb, is_sep=None) == sa.SA_EINVAL  # SEPLLM needs the flags
+
+
+def test_topk_middle_validation():
+    lib = sa._lib
+    lam = sa.mask(sa.SA_MASK_LAMBDA, 300, 300, n_starting=10, L_pretrain=100)
+    sep = sa.mask(sa.SA_MASK_SEPLLM, 300, 300, a=4, w=16)
+    a = _args(lse=8192)
+    call = lambda m, args, k: lib.sparse_attn_topk_middle(ctypes.byref(m), ctypes.byref(args), k,  # noqa: E731
+                                                          1 << 20, 1 << 21, None)
+    assert call(sep, a, 4) == sa.SA_EINVAL
+    assert call(lam, _args(lse=8192, rope=sa.SA_ALIBI, rope_base=8.0), 4) == sa.SA_EUNSUPPORTED
+    assert call(lam, _args(lse=8192, dtype=sa.SA_F32, d=64), 4) == sa.SA_EUNSUPPORTED
+    assert call(lam, a, 0) == sa.SA_EINVAL and call(lam, a, 9) == sa.SA_EINVAL
+    assert call(lam, _args(), 4) == sa.SA_EINVAL  # no lse
