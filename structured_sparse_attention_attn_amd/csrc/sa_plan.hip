@@ -137,7 +137,7 @@ __device__ int item_flags(const PlanArgs& p, const TileRange& r, int b) {
 }
 
 // One workgroup: scan of the per-block separator counts, the per-tile item
-// lists (CSR) and separator counts, and the header.
+// offsets (CSR) and separator counts, and the header.
 __global__ __launch_bounds__(FIN_THREADS) void plan_finish(PlanArgs p) {
   __shared__ int wave_tot[40];
   const int tid = threadIdx.x;
@@ -166,13 +166,7 @@ __global__ __launch_bounds__(FIN_THREADS) void plan_finish(PlanArgs p) {
     }
     const int ex = block_excl_scan(cnt, wave_tot, &total);
     if (t < p.n_tiles) {
-      const int start = carry + ex;
-      p.tile_ptr[t] = start;
-      int k = start;
-      // leading blocks 0 .. lo_end-1, then one run of consecutive blocks (the
-      // backward's key-major kernel finds a block's item from this layout)
-      for (int b = 0; b < r.lo_end; ++b) p.items[k++] = b | (item_flags(p, r, b) << 24);
-      for (int b = r.hi0; b <= r.hi1; ++b) p.items[k++] = b | (item_flags(p, r, b) << 24);
+      p.tile_ptr[t] = carry + ex;  // the items themselves: plan_lists
       int sc = 0;
       if (p.kind == SA_MASK_SEPLLM) {
         const int gh = r.hi0 * BK;  // first key of the first window block
@@ -191,11 +185,30 @@ __global__ __launch_bounds__(FIN_THREADS) void plan_finish(PlanArgs p) {
   }
 }
 
-// One wave per block at or after g0: write the block's separator positions at
-// their rank (block prefix + popcount of the lower lanes' bits).
-__global__ __launch_bounds__(256) void plan_sep_compact(PlanArgs p) {
+// Two jobs in one launch, both after plan_finish:
+//  * work groups [0, n_item_wg): one wave per tile writes the tile's items,
+//    leading blocks 0 .. lo_end-1 and then one run of consecutive blocks hi0 ..
+//    hi1, a lane per item (the backward's key-major kernel finds a block's
+//    item from this layout);
+//  * the rest (SepLLM): one wave per block at or after g0 writes the block's
+//    separator positions at their rank (block prefix + popcount of the lower
+//    lanes' bits).
+__global__ __launch_bounds__(256) void plan_lists(PlanArgs p, int n_item_wg) {
   const int lane = threadIdx.x & 63;
-  const int blk = (int)((blockIdx.x * 256u + threadIdx.x) >> 6);
+  if ((int)blockIdx.x < n_item_wg) {
+    const int t = (int)((blockIdx.x * 256u + threadIdx.x) >> 6);
+    if (t >= p.n_tiles) return;
+    const TileRange r = tile_range(p, t);
+    const int start = p.tile_ptr[t];
+    const int cnt = r.lo_end + (r.hi1 - r.hi0 + 1);
+    for (int i = lane; i < cnt; i += 64) {
+      const int b = i < r.lo_end ? i : r.hi0 + (i - r.lo_end);
+      p.items[start + i] = b | (item_flags(p, r, b) << 24);
+    }
+    return;
+  }
+  if (p.sep == nullptr) return;
+  const int blk = (int)(((blockIdx.x - n_item_wg) * 256u + threadIdx.x) >> 6);
   if (blk >= p.n_blocks || blk * BK < p.g0) return;
   const unsigned long long word = p.sep_bits[blk];
   if ((word >> lane) & 1ull) {
@@ -237,11 +250,10 @@ hipError_t launch_plan(const sa_mask_t& m, const sa_plan_header_t& lay, void* pl
   hipLaunchKernelGGL(plan_finish, dim3(1), dim3(FIN_THREADS), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.sep != nullptr) {
-    hipLaunchKernelGGL(plan_sep_compact, dim3(wg), dim3(256), 0, s, p);
-    e = hipGetLastError();
-  }
-  return e;
+  const int n_item_wg = (int)ceil_div(lay.n_tiles, 4);
+  const unsigned lists_wg = (unsigned)(n_item_wg + (p.sep != nullptr ? (int)wg : 0));
+  hipLaunchKernelGGL(plan_lists, dim3(lists_wg), dim3(256), 0, s, p, n_item_wg);
+  return hipGetLastError();
 }
 
 }  // namespace sa
