@@ -2,8 +2,8 @@
 // separator rows and precompute the LM-Infinite capped keys.
 //
 // Rotary embedding: rotate-half pairs (c, c + d/2), theta_c = base^(-2c/d);
-// the angle pos * theta_c is formed and reduced modulo 2*pi in fp64, then one
-// fp32 sincos.  Positions (segmented-execution page, method / overall
+// the angle pos * theta_c is formed in fp64 and reduced to a fraction of a
+// turn, then the hardware sine and cosine.  Positions (segmented-execution page, method / overall
 // framework): keys at their index (the prefix re-indexed to 0..P-1), queries
 // at P + i in a segment and at i otherwise.  LM-Infinite page, section
 // "method": starting-span keys outside the window keep the raw key and take
@@ -55,16 +55,12 @@ __device__ inline u16 f2bf(float f) {  // round to nearest even (inputs are fini
   return (u16)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
 }
 
-// cos and sin of pos * theta: fp64 product and reduction, fp32 sincos.
-__device__ inline void angle_sincos(double pos, double th, float* c, float* s) {
-  const double TWO_PI_HI = 6.283185307179586232;     // nearest double to 2*pi
-  const double TWO_PI_LO = 2.4492935982947064e-16;   // 2*pi - TWO_PI_HI
-  const double INV_TWO_PI = 0.15915494309189535;
-  const double ang = pos * th;
-  const double kq = rint(ang * INV_TWO_PI);
-  double r = fma(-kq, TWO_PI_HI, ang);
-  r = fma(-kq, TWO_PI_LO, r);
-  sincosf((float)r, s, c);
+// cos and sin of an angle given in turns: reduced in fp64 to [-1/2, 1/2],
+// then the hardware sine and cosine (whose argument is in turns).
+__device__ inline void turn_sincos(double rev, float* c, float* s) {
+  const float f = (float)(rev - rint(rev));
+  *c = __builtin_amdgcn_cosf(f);
+  *s = __builtin_amdgcn_sinf(f);
 }
 
 // 8 consecutive elements of a row: 16 bytes (bf16) or 32 bytes (fp32).
@@ -132,12 +128,8 @@ __global__ __launch_bounds__(256) void rope_qk(RopeArgs p) {
   const int n_qrows = (p.write_q && i >= 0 && i < p.n_q) ? p.B * p.h_q : 0;
   const int r_begin = p.row0 + blockIdx.y * ROPE_ROWS;
   if (r_begin >= p.B * (p.h_kv + p.h_q)) return;
-  float cs[8], sn[8];
-  if (p.rotate) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) angle_sincos((double)pos, p.theta.th[c0 + e], &cs[e], &sn[e]);
-  }
-  // key-row extras of this position: separator rank, capped rotation
+  // key-row extras of this position: separator rank (its plan reads go out
+  // before the row loads, so waiting for them does not wait for the rows)
   bool is_sep = false;
   int64_t rank = 0;
   if (pos < p.n_k && p.gather && pos >= p.g0) {
@@ -148,12 +140,6 @@ __global__ __launch_bounds__(256) void rope_qk(RopeArgs p) {
       is_sep = true;
       rank = p.blk_sep[blk] + __popcll(word & ((r == 0) ? 0ull : (~0ull >> (64 - r))));
     }
-  }
-  const bool is_cap = p.rotate && pos < p.n_cap;
-  float ccs[8], csn[8];
-  if (is_cap) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) angle_sincos(-(double)p.L, p.theta.th[c0 + e], &ccs[e], &csn[e]);
   }
   const int hk = p.B * p.h_kv;
   Row8<T> in1[ROPE_ROWS], in2[ROPE_ROWS];
@@ -173,6 +159,27 @@ __global__ __launch_bounds__(256) void rope_qk(RopeArgs p) {
     if (src) {
       in1[rr].load(src + c0 * esz);
       in2[rr].load(src + (c0 + half) * esz);
+    }
+  }
+  // cos and sin of pos * theta_c, c = c0 .. c0+7 (and of -L * theta_c for the
+  // capped keys), after the row loads are in flight: theta_c / (2 pi) from
+  // theta_{c0} times powers of base^(-2/d) in fp64, the angle reduced in fp64
+  // to a fraction of a turn, then the hardware sine and cosine (which take
+  // turns)
+  const bool is_cap = p.rotate && pos < p.n_cap;
+  float cs[8], sn[8], ccs[8], csn[8];
+  if (p.rotate) {
+    // theta_{c0} = (base^(-16/d))^(c0/8) from table entries 8, 16, 32 (uniform
+    // loads, no per-lane memory read); th[0] = 1
+    const int e8 = c0 >> 3;
+    double t = ((e8 & 1) ? p.theta.th[8] : 1.0) * ((e8 & 2) ? p.theta.th[16] : 1.0) *
+               ((e8 & 4) ? p.theta.th[32] : 1.0) * 0.15915494309189535;
+    const double r1 = p.theta.th[1];  // base^(-2/d)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      turn_sincos((double)pos * t, &cs[e], &sn[e]);
+      if (is_cap) turn_sincos(-(double)p.L * t, &ccs[e], &csn[e]);
+      t *= r1;
     }
   }
 #pragma unroll
