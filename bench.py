@@ -289,14 +289,24 @@ def fwd_source_sha():
     return source_sha([os.path.join(csrc, f) for f in FWD_SOURCES])
 
 
-def load_traffic(workload_name):
-    """HBM bytes per launch of the fused forward from committed rocprofv3 PMC
-    counters, or None when absent or taken on a different kernel source."""
-    p = os.path.join(ROOT, "profiles", f"attend_{workload_name}_pmc.json")
+ROPE_SOURCES = ("sa_rope.hip", "sa_common.h")
+
+
+def rope_source_sha():
+    """Hash of the sources the RoPE stage is compiled from."""
+    csrc = os.path.join(ROOT, "structured_sparse_attention_attn_amd", "csrc")
+    return source_sha([os.path.join(csrc, f) for f in ROPE_SOURCES])
+
+
+def load_traffic(workload_name, stage="attend"):
+    """HBM bytes per launch of the fused forward ("attend") or of the RoPE stage
+    ("rope") from committed rocprofv3 PMC counters, or None when absent or taken
+    on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", f"{stage}_{workload_name}_pmc.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
-    if d.get("source_sha") != fwd_source_sha():
+    if d.get("source_sha") != (fwd_source_sha() if stage == "attend" else rope_source_sha()):
         return None
     return (d["fetch_kib"] * d["copy_factor_fetch"] + d["write_kib"] * d["copy_factor_write"]) * 1024.0
 
@@ -443,6 +453,17 @@ def main():
     if topk is None:
         stage.pop("topk")
 
+    def spread(vals):
+        v = np.asarray(vals, dtype=np.float64)
+        return {"median": round(float(np.median(v)), 4), "p10": round(float(np.percentile(v, 10)), 4),
+                "p90": round(float(np.percentile(v, 90)), 4)}
+
+    step_spread = {"step": spread([e[0].elapsed_time(e[4]) for e in evs]),
+                   "attend": spread([e[3].elapsed_time(e[4]) for e in evs])}
+    in_bytes = sum(t.numel() * t.element_size() for t in (q, k, v, o))
+    cache = ("warm: q, k, v and o fit in the 256 MB last-level cache" if in_bytes <= (256 << 20)
+             else "cold: q, k, v and o exceed the 256 MB last-level cache")
+
     if args.copy_calib:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -470,6 +491,8 @@ def main():
             gbs = nbytes / (stage[name_] * 1e-3) / 1e9
             stage_roofline[name_] = {"bound": "hbm", "bytes": nbytes, "achieved": round(gbs, 1),
                                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
+            if name_ == "rope":
+                stage_roofline[name_]["traffic"] = load_traffic(wl.name, "rope")
     props = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC,
@@ -494,6 +517,8 @@ def main():
         "ms_per_layer": round(stage["rope"] + stage["attend"], 4),
         "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "stages_ms": {k_: round(v_, 4) for k_, v_ in stage.items()},
+        "per_step_ms": step_spread,
+        "cache": cache,
         "roofline": roofline,
         "issued_mfma": issued,
         "stages_roofline": stage_roofline,
