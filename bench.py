@@ -49,18 +49,25 @@ def pair_count_per_head(wl, sep_np):
 
 def issued_flops(wl, host_plan):
     """MFMA work the fused forward issues: every unit of a tile is a full
-    64-key x 128-query block (both products), masked pairs included."""
+    64-key x 128-query block (both products), masked pairs included.  With
+    RoPE, a Lambda tile's capped blocks get a capped pass, and the ordinary
+    pass skips those of them farther than L from the tile's first query."""
     import numpy as np
     tp = host_plan["tile_ptr"].astype(np.int64)
-    items = host_plan["items"]
+    items = host_plan["items"].astype(np.int64)
     n_items = tp[1:] - tp[:-1]
     n_cap = np.zeros_like(n_items)
-    if wl.mode == "lambda":
+    n_skip = np.zeros_like(n_items)
+    if wl.mode == "lambda" and wl.rope_base is not None:
         capped = ((items >> 24) & 2) != 0
+        tile = np.repeat(np.arange(len(n_items), dtype=np.int64), n_items)
+        skip = capped & ((items & 0xFFFFFF) * 64 + 63 < tile * 128 - wl.L)
         cs = np.concatenate([[0], np.cumsum(capped)])
+        ks = np.concatenate([[0], np.cumsum(skip)])
         n_cap = cs[tp[1:]] - cs[tp[:-1]]
+        n_skip = ks[tp[1:]] - ks[tp[:-1]]
     n_ch = (host_plan["sep_count"].astype(np.int64) + 63) // 64 if wl.mode == "sepllm" else 0
-    units = int((n_items + n_cap + n_ch).sum())
+    units = int((n_items - n_skip + n_cap + n_ch).sum())
     return 4.0 * 64 * 128 * wl.d * units * wl.h_q * wl.batch
 
 

@@ -155,11 +155,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
   const bool qok = qi < p.n_q;
 
   TileUnits tu;
-  tu.it0 = ld_uniform(p.tile_ptr + t);
-  tu.n_items = ld_uniform(p.tile_ptr + t + 1) - tu.it0;
-  tu.n_capu = 0;
-  if (p.use_cap)
-    while (tu.n_capu < tu.n_items && ((ld_uniform(p.items + tu.it0 + tu.n_capu) >> 24) & SA_ITEM_CAPPED)) ++tu.n_capu;
+  tile_items(p, t, tu);
   tu.nsep = p.gather ? ld_uniform(p.sep_count + t) : 0;
   tu.n_ch = (tu.nsep + BK - 1) / BK;
   tu.kb = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH) * 2;
@@ -518,7 +514,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p) {
     if (it < 0) return -1;
     const int fl = it >> 24;
     if (kind == G_CAP) return (fl & SA_ITEM_CAPPED) ? MK_LCAP : -1;
-    if (p.use_cap && (fl & SA_ITEM_CAPPED)) return MK_LNORM;
+    if (p.use_cap && (fl & SA_ITEM_CAPPED)) {
+      // no pair of the ordinary pass when the block is farther than L from the whole tile
+      if (uidx * BK + BK - 1 < t * TQ - p.L) return -1;
+      return MK_LNORM;
+    }
     if (fl & SA_ITEM_FULL) return MK_NONE;
     if (p.kind == SA_MASK_SEPLLM) return MK_SEPLLM;
     if (p.kind == SA_MASK_LAMBDA) return MK_LALL;

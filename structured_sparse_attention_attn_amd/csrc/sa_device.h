@@ -150,6 +150,7 @@ __device__ inline float sum_p(const bf16x8 (&pb)[4]) {
 // Per-tile unit list: [capped items] [gathered separator chunks] [items].
 struct TileUnits {
   int it0, n_items, n_capu, n_ch, nsep;
+  int cap0;            // index of the first capped item (the ordinary pass starts at it0)
   const char* kb;      // dense keys of this (batch, kv head)
   const char* vb;
   int64_t kst, vst;
@@ -158,6 +159,27 @@ struct TileUnits {
   const char* vsb;
 };
 
+// The tile's capped items (LM-Infinite: leading blocks holding starting
+// tokens seen from farther than L) and its ordinary items.  A capped block
+// whose last key is farther than L from the tile's first query holds no pair
+// of the ordinary pass (every pair of it is a capped one), so that pass skips
+// it; such blocks form a prefix of the capped items.
+template <class A>
+__device__ inline void tile_items(const A& p, int t, TileUnits& tu) {
+  tu.it0 = ld_uniform(p.tile_ptr + t);
+  tu.n_items = ld_uniform(p.tile_ptr + t + 1) - tu.it0;
+  tu.cap0 = tu.it0;
+  tu.n_capu = 0;
+  if (p.use_cap) {
+    while (tu.n_capu < tu.n_items && ((ld_uniform(p.items + tu.it0 + tu.n_capu) >> 24) & SA_ITEM_CAPPED)) ++tu.n_capu;
+    int n_skip = 0;
+    while (n_skip < tu.n_capu && (ld_uniform(p.items + tu.it0 + n_skip) & 0xffffff) * BK + BK - 1 < t * TQ - p.L)
+      ++n_skip;
+    tu.it0 += n_skip;
+    tu.n_items -= n_skip;
+  }
+}
+
 // REV visits the plan's blocks last to first (the diagonal block first).
 template <bool REV, class A>
 __device__ inline Unit unit_at(const A& p, const TileUnits& tu, int u) {
@@ -165,7 +187,7 @@ __device__ inline Unit unit_at(const A& p, const TileUnits& tu, int u) {
   x.count = 0;
   x.sbits = 0;
   if (u < tu.n_capu) {
-    const int blk = ld_uniform(p.items + tu.it0 + u) & 0xffffff;
+    const int blk = ld_uniform(p.items + tu.cap0 + u) & 0xffffff;
     x.kbase = tu.capb + (int64_t)blk * BK * (D128 * 2);
     x.kstride = D128 * 2;
     x.kvalid = min(BK, p.n_cap - blk * BK);

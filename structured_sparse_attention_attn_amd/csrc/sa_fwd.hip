@@ -176,11 +176,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   const bool qok = qi < p.n_q;
 
   TileUnits tu;
-  tu.it0 = ld_uniform(p.tile_ptr + t);
-  tu.n_items = ld_uniform(p.tile_ptr + t + 1) - tu.it0;
-  tu.n_capu = 0;
-  if (p.use_cap)
-    while (tu.n_capu < tu.n_items && ((ld_uniform(p.items + tu.it0 + tu.n_capu) >> 24) & SA_ITEM_CAPPED)) ++tu.n_capu;
+  tile_items(p, t, tu);
   tu.nsep = p.gather ? ld_uniform(p.sep_count + t) : 0;
   tu.n_ch = (tu.nsep + BK - 1) / BK;
   tu.kb = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH) * 2;
