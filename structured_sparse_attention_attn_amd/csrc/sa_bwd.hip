@@ -155,7 +155,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
   const bool qok = qi < p.n_q;
 
   TileUnits tu;
-  tile_items(p, t, tu);
+  tile_items<!ALIBI>(p, t, tu);
   tu.nsep = p.gather ? ld_uniform(p.sep_count + t) : 0;
   tu.n_ch = (tu.nsep + BK - 1) / BK;
   tu.kb = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH) * 2;

@@ -163,14 +163,15 @@ struct TileUnits {
 // tokens seen from farther than L) and its ordinary items.  A capped block
 // whose last key is farther than L from the tile's first query holds no pair
 // of the ordinary pass (every pair of it is a capped one), so that pass skips
-// it; such blocks form a prefix of the capped items.
-template <class A>
+// it; such blocks form a prefix of the capped items.  CAP false: a kernel
+// that never has capped passes (the ALiBi bias).
+template <bool CAP, class A>
 __device__ inline void tile_items(const A& p, int t, TileUnits& tu) {
   tu.it0 = ld_uniform(p.tile_ptr + t);
   tu.n_items = ld_uniform(p.tile_ptr + t + 1) - tu.it0;
   tu.cap0 = tu.it0;
   tu.n_capu = 0;
-  if (p.use_cap) {
+  if (CAP && p.use_cap) {
     while (tu.n_capu < tu.n_items && ((ld_uniform(p.items + tu.it0 + tu.n_capu) >> 24) & SA_ITEM_CAPPED)) ++tu.n_capu;
     int n_skip = 0;
     while (n_skip < tu.n_capu && (ld_uniform(p.items + tu.it0 + n_skip) & 0xffffff) * BK + BK - 1 < t * TQ - p.L)

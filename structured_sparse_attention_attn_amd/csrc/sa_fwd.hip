@@ -176,7 +176,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   const bool qok = qi < p.n_q;
 
   TileUnits tu;
-  tile_items(p, t, tu);
+  tile_items<!ALIBI>(p, t, tu);
   tu.nsep = p.gather ? ld_uniform(p.sep_count + t) : 0;
   tu.n_ch = (tu.nsep + BK - 1) / BK;
   tu.kb = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH) * 2;
