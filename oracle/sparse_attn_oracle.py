@@ -20,7 +20,7 @@ Sources, cited by page title and section:
   the segment is shifted by P; the long-range heads' prefix is the top-k of a
   detached pool scored by the segment-end query (forward only).
 
-Readings where the pages are silent or garbled (each is listed in the design doc):
+Readings taken where the pages are silent or garbled:
 rotate-half RoPE with ``theta_c = base**(-2c/d)``; SepLLM neighbours are
 ``0 <= i-j < w`` (the query itself included); "separator before i" includes
 j = i; masked means -inf (the printed elementwise product with M is not taken
