@@ -41,12 +41,18 @@ def device_flags():
             "-munsafe-fp-atomics"]
 
 
+# Per-source code-generation options.  The backward kernels are scheduled with
+# the compiler's memory-clause strategy (measured: 32K backward about 2%
+# faster, 128K about 0.5%; the forward gains nothing from it).
+EXTRA_FLAGS = {"sa_bwd.hip": ["-mllvm", "--amdgpu-sched-strategy=max-memory-clause"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
     path = os.path.join(CSRC, src)
     cmd = [hipcc()] + common_flags()
     if src.endswith(".hip"):
-        cmd += device_flags() + ["-x", "hip"]
+        cmd += device_flags() + EXTRA_FLAGS.get(src, []) + ["-x", "hip"]
     cmd += ["-c", path, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
