@@ -110,10 +110,13 @@ typedef struct {
  *               theta_c = rope_base^(-2c/d)); or SA_ALIBI (LAMBDA masks only,
  *               else SA_EUNSUPPORTED): no rotation, and the logit of query
  *               head h gains the ALiBi-style bias -m_h * min(i-j, L_pretrain)
- *               with m_h = 2^(-E (h+1) / h_q), E = rope_base > 0 (8 is the
- *               usual value) -- the LM-Infinite page, section "method": the
- *               bias matrix of ALiBi-style models clipped at the same cap.
+ *               with m_h = 2^(-E (h+1) / h_q), E = alibi_exp -- the
+ *               LM-Infinite page, section "method": the bias matrix of
+ *               ALiBi-style models clipped at the same cap.
+ *   rope_base   SA_ROPE_HALF: the RoPE base (> 1); ignored otherwise.
  *   scale       logit scale, normally 1/sqrt(d).
+ *   alibi_exp   SA_ALIBI: the slope exponent E > 0 (8 is the usual value);
+ *               ignored otherwise.
  *   q           [batch, h_q, n_q, d] raw (unrotated) queries.
  *   k, v        [batch, h_kv, n_k, d] raw keys and values.
  *   o           [batch, h_q, n_q, d] output (written).
@@ -126,6 +129,7 @@ typedef struct {
   int32_t rope;
   float rope_base;
   float scale;
+  float alibi_exp;
   const void *q; int64_t q_stride[3];
   const void *k; int64_t k_stride[3];
   const void *v; int64_t v_stride[3];
@@ -157,6 +161,29 @@ int sparse_attn_plan(const sa_mask_t *m, void *plan, size_t plan_bytes, hipStrea
 
 /* Host only: bytes of device workspace sparse_attn_fwd needs for (m, args). */
 int sa_fwd_workspace_bytes(const sa_mask_t *m, const sa_fwd_args_t *args, size_t *bytes);
+
+/*
+ * Host only: where the RoPE stage (sparse_attn_rope / the first stage of
+ * sparse_attn_fwd) puts its results in the workspace: byte offsets from the
+ * workspace base, -1 for a section the call does not use.  Element type is
+ * args->dtype; rows are d elements, contiguous.
+ *   krot  [batch, h_kv, n_k, d]      R(pos_k(j)) k_j, rounded once (SA_ROPE_HALF)
+ *   ksep  [batch, h_kv, sep_rows, d] row r = krot row SEP[r] (SepLLM with
+ *   vsep  [batch, h_kv, sep_rows, d]   separators; vsep holds raw v), for the
+ *                                      rows some tile gathers
+ *   kcap  [batch, h_kv, cap_rows, d] row j < min(n_starting, n_k):
+ *                                    R(-L_pretrain) k_j times scale*log2(e) for
+ *                                    bf16 (times 1 for f32) (LAMBDA with RoPE)
+ *   qrot  [batch, h_q, n_q, d]       rotated queries (f32 with RoPE only)
+ * (LM-Infinite page, section "method": <R(L) q, k> = <q, R(-L) k>; SepLLM
+ * page, part 6.2: only kept keys take part.)
+ */
+typedef struct {
+  int64_t krot, ksep, vsep, kcap, qrot;
+  int64_t sep_rows, cap_rows;
+  int64_t total;
+} sa_fwd_ws_layout_t;
+int sa_fwd_workspace_layout(const sa_mask_t *m, const sa_fwd_args_t *args, sa_fwd_ws_layout_t *layout);
 
 /*
  * Sparse attention forward for every batch row and head: a RoPE stage
@@ -298,8 +325,9 @@ int sa_stream_layout(const sa_stream_cfg_t *cfg, int64_t offsets[5]);
  * which are rewritten in place to the extended attention).  sel int32 and
  * score fp32 [batch, h_q, n_q, k_mid] receive the chosen j (ascending score
  * order, -1 when a query has fewer middle tokens) and their base-2 logits.
- * 1 <= k_mid <= 8.  Errors: SA_EINVAL, SA_EUNSUPPORTED, SA_EHIP.
+ * 1 <= k_mid <= SA_TOPK_MIDDLE_MAX.  Errors: SA_EINVAL, SA_EUNSUPPORTED, SA_EHIP.
  */
+enum { SA_TOPK_MIDDLE_MAX = 64 };
 int sparse_attn_topk_middle(const sa_mask_t *m, const sa_fwd_args_t *args, int32_t k_mid,
                             int32_t *sel, float *score, hipStream_t stream);
 

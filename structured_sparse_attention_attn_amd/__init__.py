@@ -32,6 +32,7 @@ SA_MASK_SEPLLM, SA_MASK_LAMBDA, SA_MASK_SEGMENT = 0, 1, 2
 SA_F32, SA_BF16 = 0, 1
 SA_ROPE_NONE, SA_ROPE_HALF, SA_ALIBI = 0, 1, 2
 SA_TQ, SA_BK = 128, 64
+SA_TOPK_MIDDLE_MAX = 64
 SA_ITEM_FULL, SA_ITEM_CAPPED = 1, 2
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -54,10 +55,15 @@ class sa_plan_header_t(ctypes.Structure):
 
 class sa_fwd_args_t(ctypes.Structure):
     _fields_ = [("dtype", _i32), ("batch", _i32), ("h_q", _i32), ("h_kv", _i32), ("d", _i32),
-                ("rope", _i32), ("rope_base", _f32), ("scale", _f32),
+                ("rope", _i32), ("rope_base", _f32), ("scale", _f32), ("alibi_exp", _f32),
                 ("q", _vp), ("q_stride", _i64 * 3), ("k", _vp), ("k_stride", _i64 * 3),
                 ("v", _vp), ("v_stride", _i64 * 3), ("o", _vp), ("o_stride", _i64 * 3),
                 ("lse", _vp)]
+
+
+class sa_fwd_ws_layout_t(ctypes.Structure):
+    _fields_ = [("krot", _i64), ("ksep", _i64), ("vsep", _i64), ("kcap", _i64), ("qrot", _i64),
+                ("sep_rows", _i64), ("cap_rows", _i64), ("total", _i64)]
 
 
 class sa_bwd_args_t(ctypes.Structure):
@@ -79,6 +85,7 @@ _lib.sa_plan_layout.argtypes = [_MASKP, ctypes.POINTER(sa_plan_header_t)]
 _lib.sa_plan_bytes.argtypes = [_MASKP, ctypes.POINTER(_sz)]
 _lib.sparse_attn_plan.argtypes = [_MASKP, _vp, _sz, _vp]
 _lib.sa_fwd_workspace_bytes.argtypes = [_MASKP, _ARGSP, ctypes.POINTER(_sz)]
+_lib.sa_fwd_workspace_layout.argtypes = [_MASKP, _ARGSP, ctypes.POINTER(sa_fwd_ws_layout_t)]
 _lib.sparse_attn_fwd.argtypes = [_MASKP, _vp, _sz, _ARGSP, _vp, _sz, _vp]
 _lib.sparse_attn_rope.argtypes = [_MASKP, _vp, _sz, _ARGSP, _vp, _sz, _vp]
 _lib.sparse_attn_attend.argtypes = [_MASKP, _vp, _sz, _ARGSP, _vp, _sz, _vp]
@@ -102,6 +109,7 @@ for _name in ("sa_stream_state_bytes", "sa_decode_workspace_bytes", "sa_stream_l
               "sparse_attn_stream_reset", "sparse_attn_decode_step"):
     getattr(_lib, _name).restype = ctypes.c_int
 for _name in ("sa_plan_layout", "sa_plan_bytes", "sparse_attn_plan", "sa_fwd_workspace_bytes",
+              "sa_fwd_workspace_layout",
               "sparse_attn_fwd", "sparse_attn_rope", "sparse_attn_attend", "sa_topk_workspace_bytes",
               "topk_retrieve", "sparse_attn_segment_carry", "sa_bwd_workspace_bytes",
               "sparse_attn_bwd"):
@@ -157,29 +165,65 @@ def sparse_attn_plan(m: sa_mask_t, plan, stream=None) -> None:
     _check(_lib.sparse_attn_plan(ctypes.byref(m), _ptr(plan), plan.numel(), _stream(stream)))
 
 
+def _check_4d(name, t, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: device {t.device}, expected {device}")
+    if t.stride(-1) != 1:
+        raise ValueError(f"{name}: last dimension must be contiguous")
+
+
+def _check_lse(lse, shape, device):
+    import torch
+    if lse is None:
+        return
+    if tuple(lse.shape) != tuple(shape) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError(f"lse: must be a contiguous float32 tensor of shape {tuple(shape)} "
+                         f"(got {tuple(lse.shape)}, {lse.dtype})")
+    if lse.device != device:
+        raise ValueError(f"lse: device {lse.device}, expected {device}")
+
+
 def fwd_args(q, k, v, o, *, lse=None, rope_base: Optional[float] = None,
-             scale: Optional[float] = None, alibi_exp: Optional[float] = None) -> sa_fwd_args_t:
+             scale: Optional[float] = None, alibi_exp: Optional[float] = None,
+             mask: Optional[sa_mask_t] = None) -> sa_fwd_args_t:
     """sa_fwd_args_t for [B,H,T,d] tensors (last dimension contiguous).
 
     ``alibi_exp`` = E selects SA_ALIBI (slopes 2^(-E (h+1) / h_q)) instead of RoPE.
+    q and o must be [B, h_q, n_q, d], k and v [B, h_kv, n_k, d], all of one dtype and
+    device, with n_q and n_k those of ``mask`` when it is given; lse (optional) a
+    contiguous float32 [B, h_q, n_q].  The C ABI sees only pointers and strides, so
+    these are checked here (ValueError).
     """
     import torch
+    if q.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"q: dtype {q.dtype} is neither float32 nor bfloat16")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v and o must be 4-d [B, H, T, d]")
     dtype = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}[q.dtype]
-    B, h_q, _, d = q.shape
-    h_kv = k.shape[1]
+    B, h_q, n_q, d = q.shape
+    h_kv, n_k = k.shape[1], k.shape[2]
+    if mask is not None and (n_q != mask.n_q or n_k != mask.n_k):
+        raise ValueError(f"q / k token counts ({n_q}, {n_k}) differ from the mask's ({mask.n_q}, {mask.n_k})")
+    _check_4d("q", q, (B, h_q, n_q, d), q.dtype, q.device)
+    _check_4d("o", o, (B, h_q, n_q, d), q.dtype, q.device)
+    _check_4d("k", k, (B, h_kv, n_k, d), q.dtype, q.device)
+    _check_4d("v", v, (B, h_kv, n_k, d), q.dtype, q.device)
+    _check_lse(lse, (B, h_q, n_q), q.device)
     a = sa_fwd_args_t()
     a.dtype, a.batch, a.h_q, a.h_kv, a.d = dtype, B, h_q, h_kv, d
     if alibi_exp is not None:
         if rope_base:
             raise ValueError("rope_base and alibi_exp are exclusive")
-        a.rope, a.rope_base = SA_ALIBI, float(alibi_exp)
+        a.rope, a.rope_base, a.alibi_exp = SA_ALIBI, 0.0, float(alibi_exp)
     else:
         a.rope = SA_ROPE_HALF if rope_base else SA_ROPE_NONE
         a.rope_base = float(rope_base or 0.0)
     a.scale = float(scale if scale is not None else d ** -0.5)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        if t.stride(-1) != 1:
-            raise ValueError(f"{name}: last dimension must be contiguous")
         setattr(a, name, t.data_ptr())
         getattr(a, name + "_stride")[:] = list(t.stride()[:3])
     a.lse = _ptr(lse)
@@ -190,6 +234,12 @@ def sa_fwd_workspace_bytes(m: sa_mask_t, args: sa_fwd_args_t) -> int:
     out = _sz()
     _check(_lib.sa_fwd_workspace_bytes(ctypes.byref(m), ctypes.byref(args), ctypes.byref(out)))
     return out.value
+
+
+def sa_fwd_workspace_layout(m: sa_mask_t, args: sa_fwd_args_t) -> sa_fwd_ws_layout_t:
+    out = sa_fwd_ws_layout_t()
+    _check(_lib.sa_fwd_workspace_layout(ctypes.byref(m), ctypes.byref(args), ctypes.byref(out)))
+    return out
 
 
 def sparse_attn_fwd(m: sa_mask_t, plan, args: sa_fwd_args_t, ws, stream=None) -> None:
@@ -282,8 +332,17 @@ def sparse_attn_segment_carry(k, v, n_local: int, prefix_len: int, seg_len: int,
                                           ps[0], ps[1], pool_len, cap, _stream(stream)))
 
 
-def bwd_args(dout, dq, dk, dv) -> sa_bwd_args_t:
-    """sa_bwd_args_t for [B,H,T,d] tensors (last dimension contiguous)."""
+def bwd_args(dout, dq, dk, dv, *, q=None, k=None) -> sa_bwd_args_t:
+    """sa_bwd_args_t for [B,H,T,d] tensors (last dimension contiguous).
+
+    With the forward's q and k given, dout and dq must match q (shape, dtype, device)
+    and dk, dv must match k (ValueError otherwise)."""
+    if q is not None:
+        for name, t in (("dout", dout), ("dq", dq)):
+            _check_4d(name, t, tuple(q.shape), q.dtype, q.device)
+    if k is not None:
+        for name, t in (("dk", dk), ("dv", dv)):
+            _check_4d(name, t, tuple(k.shape), k.dtype, k.device)
     g = sa_bwd_args_t()
     for name, t in (("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
         if t.stride(-1) != 1:
@@ -352,7 +411,14 @@ def sparse_attn_decode_step(cfg: sa_stream_cfg_t, state, q, k, v, is_sep, o, ws,
 
 
 def sparse_attn_topk_middle(m: sa_mask_t, args: sa_fwd_args_t, k_mid: int, sel, score, stream=None) -> None:
-    """LM-Infinite top-k middle tokens on a forward's o and lse (see include/sparse_attn.h)."""
+    """LM-Infinite top-k middle tokens on a forward's o and lse (see include/sparse_attn.h).
+
+    sel (int32) and score (float32) must be contiguous [batch, h_q, n_q, k_mid]."""
+    import torch
+    shape = (args.batch, args.h_q, m.n_q, k_mid)
+    for name, t, dt in (("sel", sel, torch.int32), ("score", score, torch.float32)):
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name}: must be a contiguous {dt} tensor of shape {shape}")
     _check(_lib.sparse_attn_topk_middle(ctypes.byref(m), ctypes.byref(args), k_mid, _ptr(sel), _ptr(score),
                                         _stream(stream)))
 

@@ -105,8 +105,8 @@ int check_args(const sa_mask_t* m, const sa_fwd_args_t* a) {
     return fail(SA_EINVAL, "rope_base must be finite and > 1");
   if (a->rope == SA_ALIBI) {
     if (m->kind != SA_MASK_LAMBDA) return fail(SA_EUNSUPPORTED, "the ALiBi bias is supported with the LAMBDA mask only");
-    if (!(std::isfinite(a->rope_base) && a->rope_base > 0.0f))
-      return fail(SA_EINVAL, "ALiBi slope exponent (rope_base) must be finite and > 0");
+    if (!(std::isfinite(a->alibi_exp) && a->alibi_exp > 0.0f))
+      return fail(SA_EINVAL, "ALiBi slope exponent alibi_exp must be finite and > 0");
   }
   if (!(std::isfinite(a->scale) && a->scale > 0.0f)) return fail(SA_EINVAL, "scale must be finite and > 0");
   const int esz = a->dtype == SA_BF16 ? 2 : 4;
@@ -235,6 +235,23 @@ int sa_fwd_workspace_bytes(const sa_mask_t* m, const sa_fwd_args_t* a, size_t* b
   if (r != SA_OK) return r;
   if (a == nullptr || bytes == nullptr) return fail(SA_EINVAL, "args or bytes is NULL");
   *bytes = (size_t)ws_layout(*m, *a).total;
+  return ok();
+}
+
+int sa_fwd_workspace_layout(const sa_mask_t* m, const sa_fwd_args_t* a, sa_fwd_ws_layout_t* out) {
+  int r = check_mask(m);
+  if (r != SA_OK) return r;
+  if (a == nullptr || out == nullptr) return fail(SA_EINVAL, "args or layout is NULL");
+  if ((r = check_args(m, a)) != SA_OK) return r;
+  const WsLayout w = ws_layout(*m, *a);
+  out->krot = w.krot;
+  out->ksep = w.ksep;
+  out->vsep = w.vsep;
+  out->kcap = w.kcap;
+  out->qrot = w.qrot;
+  out->sep_rows = w.sep_rows;
+  out->cap_rows = w.cap_rows;
+  out->total = w.total;
   return ok();
 }
 
@@ -656,7 +673,8 @@ int sparse_attn_topk_middle(const sa_mask_t* m, const sa_fwd_args_t* a, int32_t 
   if (m->kind != SA_MASK_LAMBDA) return fail(SA_EINVAL, "top-k middle tokens apply to the LAMBDA mask");
   if (a->dtype != SA_BF16 || a->d != 128 || a->rope == SA_ALIBI)
     return fail(SA_EUNSUPPORTED, "top-k middle tokens: bf16, d = 128, RoPE or none");
-  if (k_mid < 1 || k_mid > 8) return fail(SA_EINVAL, "k_mid must be in [1, 8] (got %d)", k_mid);
+  if (k_mid < 1 || k_mid > SA_TOPK_MIDDLE_MAX)
+    return fail(SA_EINVAL, "k_mid must be in [1, %d] (got %d)", (int)SA_TOPK_MIDDLE_MAX, k_mid);
   if (a->lse == nullptr || sel == nullptr || score == nullptr)
     return fail(SA_EINVAL, "lse, sel and score must not be NULL");
   if ((r = check_device()) != SA_OK) return r;

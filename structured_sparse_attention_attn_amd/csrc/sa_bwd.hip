@@ -914,7 +914,7 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   p.gather = (m.kind == SA_MASK_SEPLLM && m.sep != nullptr) ? 1 : 0;
   p.scale = a.scale;
   p.alibi = alibi ? 1 : 0;
-  p.alibi_e = alibi ? a.rope_base : 0.f;
+  p.alibi_e = alibi ? a.alibi_exp : 0.f;
   p.n_sep_chunks = p.gather ? (int)(ro.sep_rows / BK) : 0;
   p.n_cap_blocks = p.use_cap ? (int)ceil_div(ro.n_cap, BK) : 0;
   // 2. dQ (query-major)

@@ -19,7 +19,10 @@
 namespace sa {
 namespace {
 
-constexpr int KMID_MAX = 8;
+// Per-lane selection lists hold up to KMAX (score, index) pairs; the launch
+// picks the smallest KMAX in {8, 16, 32, 64} that holds k.  Lists of 32 and
+// 64 pairs run one wave per SIMD (their registers).
+constexpr int KMID_LIMIT = 64;
 
 struct MidArgs {
   const char* q;   // raw queries [B, h_q, n_q, d]
@@ -40,7 +43,8 @@ struct MidArgs {
 
 __device__ inline bool better(float x, int j, float y, int jy) { return (x > y) | ((x == y) & (j < jy)); }
 
-__global__ __launch_bounds__(256, 2) void mid_select(MidArgs p) {
+template <int KMID_MAX>
+__global__ __launch_bounds__(256, KMID_MAX <= 16 ? 2 : 1) void mid_select(MidArgs p) {
   __shared__ __attribute__((aligned(16))) char K0[BLK_BYTES];
   __shared__ __attribute__((aligned(16))) char K1[BLK_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -342,7 +346,14 @@ hipError_t launch_topk_middle(const sa_mask_t& m, const sa_fwd_args_t& a, int km
     }
   }
   const unsigned grid = (unsigned)((int64_t)a.batch * a.h_q * p.n_tiles);
-  hipLaunchKernelGGL(mid_select, dim3(grid), dim3(256), 0, s, p);
+  if (kmid <= 8)
+    hipLaunchKernelGGL(mid_select<8>, dim3(grid), dim3(256), 0, s, p);
+  else if (kmid <= 16)
+    hipLaunchKernelGGL(mid_select<16>, dim3(grid), dim3(256), 0, s, p);
+  else if (kmid <= 32)
+    hipLaunchKernelGGL(mid_select<32>, dim3(grid), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(mid_select<KMID_LIMIT>, dim3(grid), dim3(256), 0, s, p);
   const int64_t threads = (int64_t)a.batch * a.h_q * m.n_q * 16;
   hipLaunchKernelGGL(mid_merge, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s, p);
   return hipGetLastError();

@@ -38,7 +38,7 @@ class SparseAttention:
 
     def args(self, q, k, v, o, lse=None, rope_base=None, scale=None, alibi_exp=None):
         return fwd_args(q, k, v, o, lse=lse, rope_base=rope_base, scale=scale,
-                        alibi_exp=alibi_exp)
+                        alibi_exp=alibi_exp, mask=self.mask)
 
     def ensure_workspace(self, args) -> None:
         need = sa_fwd_workspace_bytes(self.mask, args)
@@ -74,7 +74,7 @@ class SparseAttention:
         need = sa_bwd_workspace_bytes(self.mask, args)
         if self.bws is None or self.bws.numel() < need:
             self.bws = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
-        sparse_attn_bwd(self.mask, self.plan, args, bwd_args(dout, dq, dk, dv), self.bws)
+        sparse_attn_bwd(self.mask, self.plan, args, bwd_args(dout, dq, dk, dv, q=q, k=k), self.bws)
         return dq, dk, dv
 
 

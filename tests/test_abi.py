@@ -45,7 +45,8 @@ def test_struct_layout_matches_header(tmp_path):
 int main(void) {
   printf("sa_mask_t %zu\nsa_fwd_args_t %zu\nsa_plan_header_t %zu\n", sizeof(sa_mask_t),
          sizeof(sa_fwd_args_t), sizeof(sa_plan_header_t));
-  P(sa_mask_t, sep) P(sa_mask_t, prefix_len) P(sa_fwd_args_t, q) P(sa_fwd_args_t, k_stride)
+  P(sa_mask_t, sep) P(sa_mask_t, prefix_len) P(sa_fwd_args_t, alibi_exp) P(sa_fwd_args_t, q)
+  P(sa_fwd_args_t, k_stride)
   P(sa_fwd_args_t, o_stride) P(sa_fwd_args_t, lse) P(sa_plan_header_t, off_tile_ptr)
   P(sa_plan_header_t, total_bytes)
   return 0;
@@ -133,8 +134,8 @@ def test_fwd_workspace_and_validation():
         (dict(q=None), sa.SA_EINVAL),
         (dict(k=4100), sa.SA_EINVAL),  # misaligned
         (dict(batch=0), sa.SA_EINVAL),
-        (dict(rope=sa.SA_ALIBI, rope_base=0.0), sa.SA_EINVAL),
-        (dict(rope=sa.SA_ALIBI, rope_base=float("inf")), sa.SA_EINVAL),
+        (dict(rope=sa.SA_ALIBI, alibi_exp=0.0), sa.SA_EINVAL),
+        (dict(rope=sa.SA_ALIBI, alibi_exp=float("inf")), sa.SA_EINVAL),
     ]
     for kw, code in cases:
         assert lib.sparse_attn_fwd(ctypes.byref(m), 256, plan_bytes, ctypes.byref(_args(**kw)), 512,
@@ -151,7 +152,7 @@ def test_fwd_workspace_and_validation():
                                None) == sa.SA_EINVAL
     # the ALiBi bias: Lambda masks only; nothing rotated, so the forward needs no workspace
     # (its queries are scaled in registers) and the backward only the scaled queries
-    al = _args(rope=sa.SA_ALIBI, rope_base=8.0)
+    al = _args(rope=sa.SA_ALIBI, alibi_exp=8.0)
     assert sa.sa_fwd_workspace_bytes(m, al) == 0
     assert sa.sa_bwd_workspace_bytes(m, al) >= 4 * 300 * 256
     ms = sa.mask(sa.SA_MASK_SEPLLM, 300, 300, a=4, w=16)
@@ -298,7 +299,48 @@ def test_topk_middle_validation():
     call = lambda m, args, k: lib.sparse_attn_topk_middle(ctypes.byref(m), ctypes.byref(args), k,  # noqa: E731
                                                           1 << 20, 1 << 21, None)
     assert call(sep, a, 4) == sa.SA_EINVAL
-    assert call(lam, _args(lse=8192, rope=sa.SA_ALIBI, rope_base=8.0), 4) == sa.SA_EUNSUPPORTED
+    assert call(lam, _args(lse=8192, rope=sa.SA_ALIBI, alibi_exp=8.0), 4) == sa.SA_EUNSUPPORTED
     assert call(lam, _args(lse=8192, dtype=sa.SA_F32, d=64), 4) == sa.SA_EUNSUPPORTED
-    assert call(lam, a, 0) == sa.SA_EINVAL and call(lam, a, 9) == sa.SA_EINVAL
+    assert call(lam, a, 0) == sa.SA_EINVAL and call(lam, a, sa.SA_TOPK_MIDDLE_MAX + 1) == sa.SA_EINVAL
     assert call(lam, _args(), 4) == sa.SA_EINVAL  # no lse
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The ctypes binding checks what the C ABI cannot see (it receives pointers and strides
+    only): shapes against the mask and each other, one dtype and device, the lse buffer, the
+    gradient buffers, and the top-k middle-token outputs.  CPU tensors: nothing is launched."""
+    import torch
+    m = sa.mask(sa.SA_MASK_LAMBDA, 300, 300, n_starting=10, L_pretrain=100)
+    bf = torch.bfloat16
+    q = torch.zeros((1, 4, 300, 128), dtype=bf)
+    k = torch.zeros((1, 2, 300, 128), dtype=bf)
+    lse = torch.zeros((1, 4, 300), dtype=torch.float32)
+    sa.fwd_args(q, k, k, q.clone(), lse=lse, mask=m)  # accepted
+    bad = [
+        dict(k=torch.zeros((1, 2, 299, 128), dtype=bf)),                 # n_k differs from the mask
+        dict(q=torch.zeros((1, 4, 299, 128), dtype=bf)),                 # n_q differs from the mask
+        dict(v=torch.zeros((1, 2, 300, 128), dtype=torch.float32)),      # dtype differs
+        dict(o=torch.zeros((1, 3, 300, 128), dtype=bf)),                 # o not shaped like q
+        dict(v=torch.zeros((1, 2, 300, 64), dtype=bf)),                  # d differs
+        dict(lse=torch.zeros((1, 4, 300), dtype=bf)),                    # lse not float32
+        dict(lse=torch.zeros((1, 4, 299), dtype=torch.float32)),         # lse too short
+        dict(lse=torch.zeros((1, 300, 4), dtype=torch.float32).transpose(1, 2)),  # not contiguous
+        dict(q=torch.zeros((1, 4, 300, 128), dtype=torch.float16)),      # unsupported dtype
+    ]
+    for kw in bad:
+        t = dict(q=q, k=k, v=k, o=q.clone(), lse=lse)
+        t.update(kw)
+        with pytest.raises(ValueError):
+            sa.fwd_args(t["q"], t["k"], t["v"], t["o"], lse=t["lse"], mask=m)
+    # gradient buffers shaped like q (dout, dq) and k (dk, dv)
+    sa.bwd_args(q, q, k, k, q=q, k=k)
+    for args in ((q[:, :3], q, k, k), (q, q, k[:, :1], k), (q, q, k, k.float())):
+        with pytest.raises(ValueError):
+            sa.bwd_args(*args, q=q, k=k)
+    # top-k middle tokens: sel int32 and score float32 [B, h_q, n_q, k_mid], contiguous
+    a = sa.fwd_args(q, k, k, q.clone(), lse=lse, mask=m)
+    for sel, score in ((torch.zeros((1, 4, 300, 7), dtype=torch.int32), torch.zeros((1, 4, 300, 8))),
+                       (torch.zeros((1, 4, 300, 8), dtype=torch.int64), torch.zeros((1, 4, 300, 8))),
+                       (torch.zeros((1, 4, 300, 8), dtype=torch.int32), torch.zeros((1, 4, 300, 8), dtype=bf))):
+        with pytest.raises(ValueError):
+            sa.sparse_attn_topk_middle(m, a, 8, sel, score)
