@@ -245,6 +245,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   // already shifted; the reference is raised only when a row's running sum
   // of one unit passes 2^10 (or while some row has no finite reference yet),
   // which keeps every p <= ~2^10 and the shift exact in the final O and LSE.
+  // A unit whose logits exceed the reference by 64 base-2 units or more is
+  // computed again and taken with its exact row maximum, so no weight
+  // overflows whatever the logit range (any finite input).
   bool has_ref = false;
   float m_ref = 0.f, l_run = 0.f;
   f32x16 negm = f32x16{};
@@ -434,6 +437,56 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) pm = fmaxf(pm, s[mb][r]);
         pm = swap_halves_max(pm);
+        if (__any(!(pm < 0x1p64f))) {
+          // Some logit lies 64 or more base-2 units above its row's
+          // reference: its weight may have overflowed to +inf (from 128 units
+          // up) and 1/pm would leave the normal range.  The unit's logits are
+          // computed again from its K block, still in LDS (the slot is
+          // refilled only after the next step's barrier), and the unit takes
+          // the exact-max update: the reference rises to the unit's row
+          // maximum and every weight is <= 1.
+          {
+            const char* kl = Kb + l32 * 256;
+            f32x16 c0 = negm, c1 = negm;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+              const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + (((2 * ks) ^ kf) << 4)));
+              const bf16x8 a1 =
+                  __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + 32 * 256 + (((2 * ks) ^ kf) << 4)));
+              c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], c0, 0, 0, 0);
+              c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], c1, 0, 0, 0);
+            }
+            s[0] = c0;
+            s[1] = c1;
+          }
+          switch (cur.mk) {
+            case MK_NONE: break;
+            case MK_COUNT: apply_mask<MK_COUNT>(p, cur, qi, hl, s); break;
+            case MK_SEPLLM: apply_mask<MK_SEPLLM>(p, cur, qi, hl, s); break;
+            case MK_LALL: apply_mask<MK_LALL>(p, cur, qi, hl, s); break;
+            case MK_LNORM: apply_mask<MK_LNORM>(p, cur, qi, hl, s); break;
+            case MK_LCAP: apply_mask<MK_LCAP>(p, cur, qi, hl, s); break;
+            default: apply_mask<MK_SEG>(p, cur, qi, hl, s); break;
+          }
+          if constexpr (ALIBI) add_alibi(cur, qi, hl, m2, Lf, s);
+          float mx = NEG_INF;
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+          mx = fmaxf(swap_halves_max(mx), 0.f);  // relative to m_ref; every row has a reference here
+          const float alpha = __builtin_amdgcn_exp2f(-mx);
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r] - mx);
+#pragma unroll
+          for (int dm = 0; dm < 4; ++dm) acc[dm] *= alpha;
+          l_run *= alpha;
+          m_ref += mx;
+          negm = f32x16{} - m_ref;
+          pm = 1.f;  // the division below is not needed
+        }
         if (pm > 1.f) {
           const float f = 1.f / pm;
 #pragma unroll
@@ -655,7 +708,7 @@ hipError_t launch_fwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   p.gather = (m.kind == SA_MASK_SEPLLM && m.sep != nullptr) ? 1 : 0;
   p.scale_log2 = a.scale * LOG2E;
   p.alibi = a.rope == SA_ALIBI ? 1 : 0;
-  p.alibi_e = p.alibi ? a.rope_base : 0.f;
+  p.alibi_e = p.alibi ? a.alibi_exp : 0.f;
   if (a.dtype == SA_BF16) {
     p.rot_q = rope ? 1 : 0;
     p.q_pos0 = m.kind == SA_MASK_SEGMENT ? m.prefix_len : 0;
