@@ -55,7 +55,7 @@ __all__ = [
     "attention_rows", "attention_fast", "attention", "plan", "plan_items_of_tile",
     "topk_scores", "topk_select", "pair_counts", "pair_count_total", "q0_closed_form",
     "alibi_slope", "q0_alibi_closed_form", "segmented_run", "attention_grad_rows",
-    "attention_backward", "StreamCache", "stream_cache_tokens", "decode_attention",
+    "attention_backward", "attention_grad_keys_fast", "StreamCache", "stream_cache_tokens", "decode_attention",
     "middle_scores", "attention_topk_middle",
 ]
 
@@ -591,6 +591,77 @@ def attention_grad_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, dO: np.ndar
         np.add.at(dk, A, scale * ds[:, None] * qr)
         np.add.at(dv, A, p[:, None] * dO[i][None, :])
     return dq, dk, dv
+
+
+def attention_grad_keys_fast(q: np.ndarray, k: np.ndarray, v: np.ndarray, dO: np.ndarray,
+                             spec: MaskSpec, rope_base: Optional[float], scale: float,
+                             keys: Sequence[int], rows: Sequence[int],
+                             alibi: Optional[float] = None):
+    """dk, dv of the listed keys summed over the listed query rows, one head: the same
+    gradients as :func:`attention_grad_rows`, computed tile-wise like
+    :func:`attention_fast` (absolute rotations, one dense masked product per block of
+    up to 128 rows).
+
+    With qr_i = R(pos_q(i)) q_i and kr_j = R(pos_k(j)) k_j the logit is
+    s_ij = scale <qr_i, kr_j>, so ds/dk_j = scale R(-pos_k(j)) qr_i; a capped
+    LM-Infinite pair has s_ij = scale <R(L) q_i, k_j> and ds/dk_j = scale R(L) q_i;
+    with the ALiBi bias (no rotation) ds/dk_j = scale q_i.  Per row: p = softmax(s),
+    o = p V, D = <dO_i, o>, ds_j = p_j (<dO_i, v_j> - D); dk_j += ds_j ds/dk_j and
+    dv_j += p_j dO_i.  Returns dk, dv [len(keys), d].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dO = np.asarray(dO, dtype=np.float64)
+    keys = np.asarray(keys, dtype=np.int64)
+    rows = np.asarray(rows, dtype=np.int64)
+    d = q.shape[1]
+    theta = rope_theta(d, rope_base) if rope_base else None
+    dk = np.zeros((len(keys), d))
+    dv = np.zeros((len(keys), v.shape[1]))
+    for s0 in range(0, len(rows), TQ):
+        R = rows[s0:s0 + TQ]
+        M = mask_rows(spec, R)
+        U = np.flatnonzero(M.any(axis=0))
+        Mu = M[:, U]
+        C = np.zeros(Mu.shape, dtype=bool)
+        if theta is not None:
+            qr = rotate(q[R], pos_q(spec, R).astype(np.float64)[:, None] * theta[None, :])
+            kr = rotate(k[U], pos_k(spec, U).astype(np.float64)[:, None] * theta[None, :])
+            S = qr @ kr.T
+            if spec.mode == LAMBDA:
+                C = capped(spec, R[:, None], U[None, :])
+                qcap = rotate(q[R], float(spec.L) * theta[None, :])
+                S = np.where(C, qcap @ k[U].T, S)
+        else:
+            qr = q[R]
+            S = qr @ k[U].T
+        S = S * scale
+        if alibi is not None:
+            dist = pos_q(spec, R)[:, None] - pos_k(spec, U)[None, :]
+            if spec.mode == LAMBDA:
+                dist = np.minimum(dist, spec.L)
+            S = S - alibi * dist.astype(np.float64)
+        S = np.where(Mu, S, -np.inf)
+        P = np.exp(S - S.max(axis=1, keepdims=True))
+        P = P / P.sum(axis=1, keepdims=True)
+        Oo = P @ v[U]
+        D = np.einsum("rd,rd->r", dO[R], Oo)
+        dS = P * (dO[R] @ v[U].T - D[:, None])
+        pos_in_u = np.searchsorted(U, keys)
+        present = (pos_in_u < len(U)) & (U[np.minimum(pos_in_u, len(U) - 1)] == keys)
+        kk = np.flatnonzero(present)
+        cols = pos_in_u[kk]
+        dv[kk] += P[:, cols].T @ dO[R]
+        dsn = np.where(C[:, cols], 0.0, dS[:, cols])
+        dsc = np.where(C[:, cols], dS[:, cols], 0.0)
+        g = scale * (dsn.T @ qr)  # sum_i ds_ij qr_i, in the rotated frame of key j
+        if theta is not None:
+            g = rotate(g, -pos_k(spec, keys[kk]).astype(np.float64)[:, None] * theta[None, :])
+            if C.any():
+                g = g + scale * (dsc.T @ rotate(q[R], float(spec.L) * theta[None, :]))
+        dk[kk] += g
+    return dk, dv
 
 
 def attention_backward(Q, K, V, dO, spec: MaskSpec, rope_base: Optional[float], scale: float,

@@ -13,8 +13,9 @@ import torch
 
 import oracle as O
 import workloads as W
-from _helpers import (compare, device_mask, effective_keys, log, oracle_rows, row_counts,
-                      sample_rows, spec_of, to64)
+from _helpers import (compare, device_mask, log, logit_bound, oracle_rows, sample_rows, spec_of,
+                      to64)
+from _softmax_model import replay, spike_queries
 
 pytestmark = pytest.mark.gpu
 
@@ -73,12 +74,37 @@ def test_plan_bitexact_random(sa):
         _plan_compare(sa, wl, sep)
 
 
-def _run_small(sa, wl, *, strided=False, q_zero=False, check_canary=False):
+def _run_small(sa, wl, *, strided=False, q_zero=False, check_canary=False, qmul=1.0, vmul=1.0,
+               spike=None, expect=()):
+    """Runs one small case through the C ABI and compares it with the oracle in full.
+
+    qmul / vmul scale q and v (powers of 2: exact in bf16); spike lists rows whose query is
+    replaced by one aimed at a single visible key with a logit of 150 natural units
+    (spike_queries).  expect names flags of the CPU replay of the kernel's softmax update
+    rule that these inputs must raise (e.g. "rescale", "recompute"), so the test is known to
+    reach those branches.  With qmul or spike the LSE bar widens with the logit magnitude:
+    2e-2 + 2^-8 * logit_bound (the bf16 rounding of the rotated q and k)."""
     inp = W.make_small_inputs(wl)
     q, k, v = inp["q"], inp["k"], inp["v"]
     if q_zero:
         q = torch.zeros_like(q)
     sep = inp.get("sep")
+    if qmul != 1.0:
+        q = (q.float() * qmul).to(q.dtype)
+    if vmul != 1.0:
+        v = (v.float() * vmul).to(v.dtype)
+    slope_of = (lambda h: O.alibi_slope(h, wl.h_q, wl.alibi_exp)) if wl.alibi_exp else None
+    if spike is not None:
+        spec0 = spec_of(wl, None if sep is None else sep.numpy())
+        q = torch.from_numpy(spike_queries(to64(q), to64(k), spec0, spike, 150.0, wl.scale,
+                                           rope_base=wl.rope_base, slope=slope_of, h_q=wl.h_q,
+                                           h_kv=wl.h_kv)).to(q.dtype)
+    if expect:
+        spec0 = spec_of(wl, None if sep is None else sep.numpy())
+        flags, _ = replay(to64(q[0, 0]), to64(k[0, 0]), spec0, wl.rope_base, wl.scale,
+                          slope=slope_of(0) if slope_of else None)
+        for f in expect:
+            assert flags[f], f"the inputs do not reach the '{f}' branch"
     dev = "cuda"
     if strided:
         # [B,T,H,d] storage viewed as [B,H,T,d]
@@ -103,12 +129,11 @@ def _run_small(sa, wl, *, strided=False, q_zero=False, check_canary=False):
     for b in range(wl.batch):
         Q, K, V = to64(q[b]), to64(k[b]), to64(v[b])
         ref_o, ref_l = O.attention(Q, K, V, spec, wl.rope_base, wl.scale, alibi_exp=wl.alibi_exp)
-        nkeys = cnt[None, :]
-        if wl.alibi_exp is not None:
-            _, l2 = oracle_rows(Q, K, V, spec, None, 2 * wl.scale, range(wl.h_q), range(wl.n_q),
-                                slope_of=lambda h: 2 * O.alibi_slope(h, wl.h_q, wl.alibi_exp))
-            nkeys = effective_keys(ref_l, l2)
-        compare(to64(o[b]), ref_o, to64(lse[b]), ref_l, wl.dtype, nkeys=nkeys)
+        lse_tol = None
+        if qmul != 1.0 or spike is not None:
+            lse_tol = 2e-2 + 2.0 ** -8 * logit_bound(Q, K, spec, wl.scale, np.arange(wl.n_q))
+        assert np.isfinite(to64(o[b])).all() and np.isfinite(to64(lse[b])).all()
+        compare(to64(o[b]), ref_o, to64(lse[b]), ref_l, wl.dtype, lse_tol=lse_tol)
         if q_zero and wl.alibi_exp is None:
             np.testing.assert_allclose(to64(lse[b]), np.broadcast_to(np.log(cnt), ref_l.shape),
                                        rtol=0, atol=2e-6)
@@ -172,6 +197,123 @@ def test_q_zero_counts(sa, mode):
     _run_small(sa, wl, q_zero=True)
 
 
+def _ulp_bf16(x):
+    """One bf16 ulp at |x| (8 significant bits)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.ldexp(1.0, (np.floor(np.log2(ax)) - 7).astype(np.int64))
+
+
+def _check_rotated(got, x, angle, factor, what):
+    """got (bf16 rows) against the fp64 rotation of x by angle, times factor: within one bf16
+    ulp of the exact value (the one rounding to bf16 takes half), plus 2^-18 of the pair's
+    magnitude for the fp32 rotation and the hardware sine/cosine when the result cancels."""
+    ref = O.rotate(x, angle) * factor
+    h = x.shape[-1] // 2
+    mag = (np.abs(x[..., :h]) + np.abs(x[..., h:])) * abs(factor)
+    mag = np.concatenate([mag, mag], axis=-1)
+    err = np.abs(got - ref)
+    bound = _ulp_bf16(ref) + 2.0 ** -18 * mag
+    bad = err > bound
+    assert not bad.any(), (what, int(bad.sum()), float(err[bad].max()))
+
+
+ROPE_CASES = [
+    # (mode, kwargs, rope_base): positions up to 131071 with base 500000 (workload 5's keys,
+    # one kv head), the 32K Lambda capped keys, a segment with a 1024-row prefix
+    (W.SEPLLM, dict(m=131072, a=4, w=1024, p_sep=0.06, h_q=4, h_kv=1), 500000.0),
+    (W.LAMBDA, dict(m=32768, n_s=10, L=4096, h_q=1, h_kv=1), 10000.0),
+    (W.SEGMENT, dict(m=4096, P=1024, h_q=2, h_kv=2), 10000.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(ROPE_CASES)))
+def test_rope_stage_direct(sa, case):
+    """The RoPE stage alone (sparse_attn_rope), read back from the workspace sections the C
+    ABI reports: rotated keys R(pos_k(j)) k_j (LM-Infinite page, section "method", and the
+    segmented-execution page: positions 0..P-1 for the prefix), the capped keys
+    R(-L) k_j * scale * log2(e) for j < n_starting, and the gathered separator rows, byte
+    for byte the rotated key rows and raw value rows at SEP[r] (SepLLM page, part 6.2)."""
+    mode, kw, base = ROPE_CASES[case]
+    wl = W.small(mode, seed=600 + case, rope_base=base, **kw)
+    log(f"rope stage {case}: n_k={wl.n_k}")
+    inp = W.make_small_inputs(wl)
+    sep = inp.get("sep")
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    sa_obj = device_mask(wl, None if sep is None else sep.cuda())
+    sa_obj.build_plan()
+    o = torch.empty_like(q)
+    args = sa_obj.args(q, k, v, o, rope_base=base, scale=wl.scale)
+    sa_obj.ensure_workspace(args)
+    sa.sparse_attn_rope(sa_obj.mask, sa_obj.plan, args, sa_obj.ws)
+    torch.cuda.synchronize()
+    lay = sa.sa_fwd_workspace_layout(sa_obj.mask, args)
+    ws = sa_obj.ws
+    B, hkv, nk, d = wl.batch, wl.h_kv, wl.n_k, wl.d
+
+    def section(off, rows):
+        n = B * hkv * rows * d * 2
+        return ws[off:off + n].view(torch.bfloat16).view(B, hkv, rows, d)
+
+    spec = spec_of(wl, None if sep is None else sep.numpy())
+    theta = O.rope_theta(d, base)
+    krot = section(lay.krot, nk)
+    pos = O.pos_k(spec, np.arange(nk)).astype(np.float64)
+    for g in range(hkv):
+        _check_rotated(to64(krot[0, g]), to64(k[0, g]), pos[:, None] * theta[None, :], 1.0, "krot")
+    if mode == W.LAMBDA:
+        assert lay.kcap >= 0 and lay.cap_rows >= wl.n_s
+        kcap = section(lay.kcap, lay.cap_rows)
+        fac = wl.scale / math.log(2.0)
+        for g in range(hkv):
+            _check_rotated(to64(kcap[0, g, :wl.n_s]), to64(k[0, g, :wl.n_s]),
+                           np.full((wl.n_s, d // 2), -float(wl.L)) * theta[None, :], fac, "kcap")
+    if mode == W.SEPLLM:
+        pl = O.plan(spec)
+        n_used = int(pl["sep_count"].max())
+        assert n_used > 1000
+        rows = torch.from_numpy(pl["sep_idx"][:n_used].astype(np.int64)).cuda()
+        ksep = section(lay.ksep, lay.sep_rows)
+        vsep = section(lay.vsep, lay.sep_rows)
+        for g in range(hkv):
+            assert torch.equal(ksep[0, g, :n_used], krot[0, g][rows])
+            assert torch.equal(vsep[0, g, :n_used], v[0, g][rows])
+
+
+# Inputs with a wide logit range (the bf16 forward's online softmax against a stale
+# per-row reference; SepLLM page part 6.1, LM-Infinite page section "method").
+WIDE = [
+    (W.SEPLLM, dict(m=700, a=4, w=64, p_sep=0.1, h_q=4, h_kv=2), 10000.0, None),
+    (W.LAMBDA, dict(m=900, n_s=10, L=100), 10000.0, None),
+    (W.SEGMENT, dict(m=600, P=200), 10000.0, None),
+    (W.LAMBDA, dict(m=900, n_s=10, L=300, h_q=4, h_kv=2), None, 8.0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(WIDE)))
+def test_fwd_wide_logits(sa, case):
+    """Queries scaled by 4 (logit std about 4 natural units) and values by 1/4: rows whose
+    later units exceed their reference by more than 2^10 in weight take the rescale."""
+    mode, kw, rope, alibi = WIDE[case]
+    wl = W.small(mode, seed=520 + case, rope_base=rope, alibi_exp=alibi, **kw)
+    log(f"wide logits {case}")
+    _run_small(sa, wl, check_canary=True, qmul=4.0, vmul=0.25, expect=("rescale",))
+
+
+@pytest.mark.parametrize("case", range(len(WIDE)))
+def test_fwd_logit_spike(sa, case):
+    """Every 7th row of the second half aims its query at one key with a logit of 150 natural
+    units, visited after the keys that set the row's reference: the capped starting key
+    (Lambda with RoPE, visited last), the diagonal key after the gathered separators (SepLLM)
+    or the prefix (segment), the first key under the clipped ALiBi bias (visited last).  The
+    weight against the stale reference would overflow (2^(s - m_ref) with s - m_ref >= 128):
+    the kernel computes that unit again with its exact row maximum."""
+    mode, kw, rope, alibi = WIDE[case]
+    wl = W.small(mode, seed=540 + case, rope_base=rope, alibi_exp=alibi, **kw)
+    log(f"logit spike {case}")
+    _run_small(sa, wl, check_canary=True, spike=list(range(wl.n_q // 2, wl.n_q, 7)),
+               expect=("recompute", "overflow"))
+
+
 def test_determinism(sa):
     wl = W.small(W.SEPLLM, seed=11, m=1000, a=4, w=128, p_sep=0.1, h_q=4, h_kv=2)
     o1, l1 = _run_small(sa, wl)
@@ -196,7 +338,6 @@ def _workload_parity(sa, cid, heads, n_random):
     rows = np.arange(wl.n_q) if n_random is None else sample_rows(wl.n_q, n_random, cid)
     group = wl.h_q // wl.h_kv
     kv_heads = sorted(set(h // group for h in heads))
-    nkeys = row_counts(spec, rows)
     K = {g: to64(inp["k"][0, g]) for g in kv_heads}
     V = {g: to64(inp["v"][0, g]) for g in kv_heads}
     for h in heads:
@@ -207,12 +348,7 @@ def _workload_parity(sa, cid, heads, n_random):
                                    [0], rows, slope_of=lambda _h: slope)
         got_o = to64(o[0, h][torch.from_numpy(rows).cuda()])
         got_l = to64(lse[0, h][torch.from_numpy(rows).cuda()])
-        nk = nkeys
-        if slope is not None:
-            _, l2 = oracle_rows(Qh[None], K[g][None], V[g][None], spec, None, 2 * wl.scale, [0],
-                                rows, slope_of=lambda _h: 2 * slope)
-            nk = effective_keys(ref_l[0], l2[0])
-        stats = compare(got_o, ref_o[0], got_l, ref_l[0], wl.dtype, nkeys=nk)
+        stats = compare(got_o, ref_o[0], got_l, ref_l[0], wl.dtype)
         log(f"workload {cid} head {h}: max-abs {stats[0]:.2e} mean-abs {stats[1]:.2e} lse {stats[2]:.2e}")
 
 
@@ -304,7 +440,6 @@ def test_workload4_segment_with_topk(sa):
         np.testing.assert_array_equal(score[hh].cpu().numpy(), s[ri])
         ref_idx.append(ri)
     rows = sample_rows(S, 128, 4)
-    nkeys = row_counts(spec, rows)
     for h in [0, 23, 24, 31]:
         if h < wl.n_local:
             Kh = np.concatenate([to64(inp["k_tail"][0, h]), to64(inp["k_seg"][0, h])])
@@ -316,8 +451,7 @@ def test_workload4_segment_with_topk(sa):
         ref_o, ref_l = oracle_rows(to64(inp["q"][0, h])[None], Kh[None], Vh[None], spec,
                                    wl.rope_base, wl.scale, [0], rows)
         rr = torch.from_numpy(rows).cuda()
-        stats = compare(to64(o[0, h][rr]), ref_o[0], to64(lse[0, h][rr]), ref_l[0], wl.dtype,
-                        nkeys=nkeys)
+        stats = compare(to64(o[0, h][rr]), ref_o[0], to64(lse[0, h][rr]), ref_l[0], wl.dtype)
         log(f"workload 4 head {h}: max-abs {stats[0]:.2e} mean-abs {stats[1]:.2e} lse {stats[2]:.2e}")
 
 
@@ -404,7 +538,7 @@ def test_segment_runner_vs_oracle(sa, dtype, S, M, N):
     for i in range(N):
         o_g, l_g, P, idx_g = got[i]
         assert P == ref[i]["P"]
-        compare(o_g, ref[i]["O"], l_g, ref[i]["LSE"], dtype, nkeys=(P + np.arange(S) + 1)[None, :])
+        compare(o_g, ref[i]["O"], l_g, ref[i]["LSE"], dtype)
         if i + 1 < N:
             np.testing.assert_array_equal(idx_g, ref[i + 1]["idx"])
     # the final state is a byte copy of the history
@@ -513,7 +647,7 @@ def test_bwd_strided(sa, case):
             bwd_compare(f"b{b} {name}", to64(got), ref)
 
 
-def _workload_bwd_parity(sa, cid, dq_heads, n_random, key_block, dk_kv_head, nonsep_only=False):
+def _workload_bwd_parity(sa, cid, dq_heads, n_random, key_block, dk_kv_head, expect_sep=False):
     """Backward at a workload's full size: dQ on sampled rows of some heads; dK, dV on one
     key block of one kv head, from every query row that sees a key of that block (the
     oracle sums those rows' contributions, over the kv head's whole GQA group)."""
@@ -544,8 +678,10 @@ def _workload_bwd_parity(sa, cid, dq_heads, n_random, key_block, dk_kv_head, non
         bwd_compare(f"w{cid} dq h{h}", to64(dq[0, h][torch.from_numpy(rows).cuda()]), rq)
     keys = np.arange(64 * key_block, min(wl.n_k, 64 * key_block + 64))
     sel = np.ones(len(keys), dtype=bool)
-    if nonsep_only:  # separators are read by every later query: only the other keys are checked
-        sel = sep.numpy()[keys] == 0
+    if expect_sep:
+        n_sep_blk = int(sep.numpy()[keys].sum())
+        assert n_sep_blk > 0
+        log(f"workload {cid} backward: block {key_block} holds {n_sep_blk} separators")
     cand = np.arange(max(0, keys[0] - wl.P), wl.n_q)
     seen = O.visible(spec, cand[:, None], keys[sel][None, :]).any(axis=1)
     qrows = cand[seen]
@@ -554,10 +690,10 @@ def _workload_bwd_parity(sa, cid, dq_heads, n_random, key_block, dk_kv_head, non
     rv = np.zeros((len(keys), wl.d))
     Kg, Vg = to64(inp["k"][0, dk_kv_head]), to64(inp["v"][0, dk_kv_head])
     for h in range(dk_kv_head * group, (dk_kv_head + 1) * group):
-        _, dkc, dvc = O.attention_grad_rows(to64(inp["q"][0, h]), Kg, Vg, to64(dout[0, h]), qrows, spec,
-                                            wl.rope_base, wl.scale, slope(h))
-        rk += dkc[keys]
-        rv += dvc[keys]
+        dkc, dvc = O.attention_grad_keys_fast(to64(inp["q"][0, h]), Kg, Vg, to64(dout[0, h]), spec,
+                                              wl.rope_base, wl.scale, keys, qrows, slope(h))
+        rk += dkc
+        rv += dvc
     gk = to64(dk[0, dk_kv_head, torch.from_numpy(keys).cuda()])
     gv = to64(dv[0, dk_kv_head, torch.from_numpy(keys).cuda()])
     bwd_compare(f"w{cid} dk g{dk_kv_head} blk{key_block}", gk[sel], rk[sel])
@@ -570,8 +706,12 @@ def test_workload3_backward_sampled(sa):
 
 
 def test_workload5_backward_sampled(sa):
-    _workload_bwd_parity(sa, 5, dq_heads=[31], n_random=32, key_block=2040, dk_kv_head=7,
-                         nonsep_only=True)
+    # block 2020 (keys 129280..129343) holds separators read by every later query: through
+    # the window blocks by the queries within w = 1024 and through the gathered separator
+    # chunks by the ~700 queries after that; their dK, dV sum over all those rows of the
+    # kv head's 4 query heads (the gathered path's scatter back to the key rows)
+    _workload_bwd_parity(sa, 5, dq_heads=[31], n_random=32, key_block=2020, dk_kv_head=7,
+                         expect_sep=True)
 
 
 def test_workload6_backward_sampled(sa):
@@ -616,7 +756,7 @@ def test_stream_decode(sa, case):
             for h in range(hq):
                 ro[h], rl[h] = O.decode_attention(to64(q[t, b, h]), to64(k[:t + 1, b, h // group]),
                                                   to64(v[:t + 1, b, h // group]), t, toks, cfg["rope"], scale)
-            errs.append(compare(to64(o[b]), ro, to64(lse[b]), rl, "bf16", nkeys=np.full(hq, len(toks))))
+            errs.append(compare(to64(o[b]), ro, to64(lse[b]), rl, "bf16"))
     log(f"  max-abs {max(e[0] for e in errs):.3e}, lse {max(e[2] for e in errs):.3e}")
 
 
@@ -631,6 +771,16 @@ MID_CASES = [
     (dict(m=200, n_s=10, L=250), 4, 10000.0),
     (dict(m=600, n_s=70, L=130, batch=2), 5, 500000.0),
 ]
+
+
+def _check_mid_sel(row, i, wl):
+    """One query's selection: the chosen indices first, then -1; chosen indices distinct and
+    middle tokens of query i, n_starting <= j < i - L (LM-Infinite page, section "method")."""
+    n = int((row >= 0).sum())
+    assert (row[:n] >= 0).all() and (row[n:] == -1).all(), (i, row)
+    g = row[:n].tolist()
+    assert len(set(g)) == n, (i, row)
+    assert all(wl.n_s <= j < i - wl.L for j in g), (i, row)
 
 
 @pytest.mark.parametrize("case", range(len(MID_CASES)))
@@ -659,6 +809,7 @@ def test_topk_middle(sa, case):
                 jm, sm = O.middle_scores(Q, K, spec, i, wl.rope_base, wl.scale)
                 g = gsel[i][gsel[i] >= 0]
                 assert len(g) == min(kmid, len(jm)), (i, g)
+                _check_mid_sel(gsel[i], i, wl)
                 if not len(jm):
                     continue
                 sc = dict(zip(jm.tolist(), sm.tolist()))
@@ -670,8 +821,7 @@ def test_topk_middle(sa, case):
                 for jj in diff:
                     assert abs(sc[jj] - kth) <= eps, (i, jj, sc[jj], kth)
                 n_near += len(diff) > 0
-            compare(to64(o[b, h]), ro, to64(lse[b, h]), rl, "bf16",
-                    nkeys=O.pair_counts(spec) + np.minimum(kmid, np.maximum(0, np.arange(wl.n_q) - wl.L - wl.n_s)))
+            compare(to64(o[b, h]), ro, to64(lse[b, h]), rl, "bf16")
     log(f"  queries with a near-tie swap: {n_near}")
 
 
@@ -701,6 +851,7 @@ def test_workload3_topk_middle_sampled(sa):
             jm, sm = O.middle_scores(Q, K, spec, int(i), wl.rope_base, wl.scale)
             g = gsel[i][gsel[i] >= 0]
             assert len(g) == min(kmid, len(jm))
+            _check_mid_sel(gsel[i], int(i), wl)
             if not len(jm):
                 continue
             sc = dict(zip(jm.tolist(), sm.tolist()))
@@ -710,9 +861,8 @@ def test_workload3_topk_middle_sampled(sa):
                 assert abs(gs - sc[int(jj)]) <= eps
             for jj in set(g.tolist()) ^ set(rsel[r].tolist()):
                 assert abs(sc[jj] - kth) <= eps
-        nk = O.pair_counts(spec)[rows] + np.minimum(kmid, np.maximum(0, rows - wl.L - wl.n_s))
         compare(to64(o[0, h][torch.from_numpy(rows).cuda()]), ro, to64(lse[0, h][torch.from_numpy(rows).cuda()]),
-                rl, "bf16", nkeys=nk)
+                rl, "bf16")
 
 
 # LM-Infinite decode: the starting span and the window t-L .. t, starting keys capped,
@@ -750,4 +900,83 @@ def test_lambda_decode(sa, case):
                 oo, ll = O.attention_rows(to64(q[:t + 1, b, h]), to64(k[:t + 1, b, h // group]),
                                           to64(v[:t + 1, b, h // group]), [t], spec, cfg["rope"], scale)
                 ro[h], rl[h] = oo[0], ll[0]
-            compare(to64(o[b]), ro, to64(lse[b]), rl, "bf16", nkeys=np.full(hq, len(O.key_set(spec, t))))
+            compare(to64(o[b]), ro, to64(lse[b]), rl, "bf16")
+
+
+# Repeat runs and guard canaries beyond the forward: the backward, the top-k middle tokens
+# and the streaming decode write only their outputs and give the same bits every time.
+def _guarded(shape, dtype, fill=7.0, guard=4096):
+    n = int(np.prod(shape))
+    store = torch.full((guard * 2 + n,), fill, dtype=dtype, device="cuda")
+    return store, store[guard:guard + n].view(shape)
+
+
+def _guards_intact(store, fill=7.0, guard=4096):
+    return bool(torch.all(store[:guard] == fill)) and bool(torch.all(store[-guard:] == fill))
+
+
+def test_bwd_repeat_and_canary(sa):
+    mode, kw, rope, alibi = BWD_SMALL[1]
+    wl = W.small(mode, seed=800, rope_base=rope, alibi_exp=alibi, **kw)
+    inp = W.make_small_inputs(wl)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    sep = inp.get("sep")
+    sa_obj = device_mask(wl, None if sep is None else sep.cuda())
+    sa_obj.build_plan()
+    lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
+    o = sa_obj.forward(q, k, v, lse=lse, rope_base=rope, scale=wl.scale)
+    dout = W.make_grad(tuple(q.shape), seed=801).cuda()
+    outs = []
+    for rep in range(2):
+        sq, dq = _guarded(tuple(q.shape), q.dtype)
+        sk, dk = _guarded(tuple(k.shape), k.dtype)
+        sv, dv = _guarded(tuple(v.shape), v.dtype)
+        sa_obj.backward(q, k, v, o, lse, dout, rope_base=rope, scale=wl.scale, dq=dq, dk=dk, dv=dv)
+        torch.cuda.synchronize()
+        assert _guards_intact(sq) and _guards_intact(sk) and _guards_intact(sv), rep
+        outs.append((dq.clone(), dk.clone(), dv.clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
+def test_topk_middle_repeat_and_canary(sa):
+    kw, kmid, rope = MID_CASES[4]
+    wl = W.small(W.LAMBDA, seed=810, rope_base=rope, **kw)
+    inp = W.make_small_inputs(wl)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    sa_obj = device_mask(wl)
+    sa_obj.build_plan()
+    outs = []
+    shp = (wl.batch, wl.h_q, wl.n_q, kmid)
+    for rep in range(2):
+        so, o = _guarded(tuple(q.shape), q.dtype)
+        sl, lse = _guarded((wl.batch, wl.h_q, wl.n_q), torch.float32)
+        sa_obj.forward(q, k, v, o=o, lse=lse, rope_base=rope, scale=wl.scale)
+        ss, sel = _guarded(shp, torch.int32, fill=7)
+        sc, score = _guarded(shp, torch.float32)
+        sa.sparse_attn_topk_middle(sa_obj.mask, sa_obj.args(q, k, v, o, lse, rope, wl.scale), kmid, sel, score)
+        torch.cuda.synchronize()
+        assert all(_guards_intact(x) for x in (so, sl, sc)) and _guards_intact(ss, fill=7), rep
+        outs.append((o.clone(), lse.clone(), sel.clone(), score.clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("kind", ["sepllm", "lambda"])
+def test_decode_repeat_and_canary(sa, kind):
+    from structured_sparse_attention_attn_amd.pipeline import StreamDecoder
+    B, hq, hkv, d, n = 2, 8, 2, 128, 200
+    q, k, v, flags = W.make_decode_stream(B, hq, hkv, d, n, 820, 0.2)
+    decs = [StreamDecoder(B, hq, hkv, d, 4, 8, 16, 60, rope_base=10000.0, kind=kind, L_pretrain=50)
+            for _ in range(2)]
+    for t in range(n):
+        res = []
+        for dec in decs:
+            so, o = _guarded((B, hq, d), torch.bfloat16)
+            sl, lse = _guarded((B, hq), torch.float32)
+            dec.step(q[t].cuda(), k[t].cuda(), v[t].cuda(), flags[t].cuda(), o=o, lse=lse)
+            res.append((so, sl, o, lse))
+        torch.cuda.synchronize()
+        for so, sl, _, _ in res:
+            assert _guards_intact(so) and _guards_intact(sl), t
+        assert torch.equal(res[0][2], res[1][2]) and torch.equal(res[0][3], res[1][3]), t

@@ -817,3 +817,39 @@ def test_topk_middle_selection_brute_force():
     o1, l1 = O.attention_rows(q, k, v, range(m), spec, 10000.0, 0.3)
     np.testing.assert_allclose(o0, o1, rtol=0, atol=1e-12)
     np.testing.assert_allclose(l0, l1, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("case", ["sepllm", "lambda_capped", "alibi_capped", "segment", "sepllm_norope"])
+def test_grad_keys_fast_equals_definition_mode(case):
+    # the tile-wise gradient of chosen keys (absolute rotations, capped pairs through the
+    # page's realisation <R(L) q, k>) against the per-row definition mode, itself pinned by
+    # torch.autograd and central differences above; every key and its rows, and a subset of
+    # keys over a subset of rows that spans several tiles
+    d, m, base = 16, 300, 500.0
+    scale = 1.0 / math.sqrt(d)
+    P = 40 if case == "segment" else 0
+    n_k = m + P
+    rope, slope = base, None
+    if case.startswith("sepllm"):
+        flags = (RNG.random(n_k) < 0.15).astype(np.uint8)
+        spec = O.MaskSpec(O.SEPLLM, m, n_k, a=3, w=20, sep=flags)
+        if case == "sepllm_norope":
+            rope = None
+    elif case == "segment":
+        spec = O.MaskSpec(O.SEGMENT, m, n_k, P=P)
+    else:
+        spec = O.MaskSpec(O.LAMBDA, m, n_k, n_s=6, L=25)
+        if case == "alibi_capped":
+            rope, slope = None, 0.2
+    q, do = (RNG.standard_normal((m, d)) for _ in range(2))
+    k, v = (RNG.standard_normal((n_k, d)) for _ in range(2))
+    _, rk, rv = O.attention_grad_rows(q, k, v, do, range(m), spec, rope, scale, slope)
+    fk, fv = O.attention_grad_keys_fast(q, k, v, do, spec, rope, scale, np.arange(n_k), np.arange(m), slope)
+    np.testing.assert_allclose(fk, rk, rtol=0, atol=1e-12 * max(1.0, np.abs(rk).max()))
+    np.testing.assert_allclose(fv, rv, rtol=0, atol=1e-12 * max(1.0, np.abs(rv).max()))
+    keys = np.array([0, 2, 5, 64, 65, 130, n_k - 1])
+    rows = np.arange(100, m)
+    _, rk2, rv2 = O.attention_grad_rows(q, k, v, do, rows, spec, rope, scale, slope)
+    fk2, fv2 = O.attention_grad_keys_fast(q, k, v, do, spec, rope, scale, keys, rows, slope)
+    np.testing.assert_allclose(fk2, rk2[keys], rtol=0, atol=1e-12 * max(1.0, np.abs(rk2).max()))
+    np.testing.assert_allclose(fv2, rv2[keys], rtol=0, atol=1e-12 * max(1.0, np.abs(rv2).max()))
