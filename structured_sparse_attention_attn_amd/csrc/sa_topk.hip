@@ -2,16 +2,15 @@
 // design 3: before the next segment the segment-end query selects R keys of a
 // detached read-only pool for the long-range heads).
 //
-// 1. topk_score: one thread per pool key, s_j = fp64 fma chain over c = 0..d-1
+// 1. topk_score: s_j = fp64 fma chain over c = 0..d-1 for every pool key
 //    (each bf16/fp32 product is exact in fp64, so the chain equals plain
 //    multiply-then-add in the same order); stored as an order-preserving
-//    64-bit key (+0 and -0 share one key).
-// 2. topk_select: one work group per head; radix select (a 12-bit digit over
-//    all keys, the rest over the keys sharing that prefix, in LDS when they
-//    fit) finds the k-th largest key T; then each thread takes a contiguous run of
-//    keys and one block scan gives every selected index its output slot, so
-//    idx comes out in ascending pool order with ties at T taken from the
-//    lowest indices.
+//    64-bit key (+0 and -0 share one key).  Rows reach LDS by coalesced loads.
+// 2. topk_select: one work group per head, its keys held in registers; radix
+//    select of the k-th largest key T by 12-bit digits, stopping as soon as
+//    the threshold bin holds exactly the keys still wanted; one block scan
+//    then gives every selected index its output slot, so idx comes out in
+//    ascending pool order with ties at T taken from the lowest indices.
 // 3. topk_gather: copies the selected pool K/V rows into the prefix rows.
 #include "sa_common.h"
 
@@ -42,23 +41,49 @@ __device__ inline double elem<float>(const float* p, int c) {
   return (double)p[c];
 }
 
-// Thread = one pool key: its row in 16-byte pieces (rows are 16-byte
-// aligned), the fp64 chain in c order.
-template <typename T>
+// One work group scores ROWS = 256 consecutive pool keys of one head.  The
+// rows are staged in LDS with coalesced 16-byte loads (a row's chunks come
+// from consecutive lanes; rows padded by 16 bytes, so each thread's later
+// reads of its own row are bank-conflict free), then thread t runs the fp64
+// chain of key t in c order and stores its order-preserving key.
+constexpr int SCORE_ROWS = 256;
+
+template <typename T, int D>
 __global__ __launch_bounds__(256) void topk_score(const T* q, int64_t q_hs, const T* pool,
-                                                  int64_t p_hs, int64_t p_rs, int n, int d,
+                                                  int64_t p_hs, int64_t p_rs, int n,
                                                   unsigned long long* keys) {
-  __shared__ double qs[128];
+  constexpr int ROW = D * (int)sizeof(T);  // bytes per row
+  constexpr int CPR = ROW / 16;            // 16-byte chunks per row
+  constexpr int PITCH = ROW + 16;
+  __shared__ double qs[D];
+  __shared__ __attribute__((aligned(16))) char rows[SCORE_ROWS * PITCH];
   const int h = blockIdx.y;
-  if (threadIdx.x < d) qs[threadIdx.x] = elem<T>(q + h * q_hs, threadIdx.x);
+  const int t = threadIdx.x;
+  const int j0 = blockIdx.x * SCORE_ROWS;
+  if (t < D) qs[t] = elem<T>(q + h * q_hs, t);
+  const char* base = reinterpret_cast<const char*>(pool + h * p_hs);
+  const int64_t rs = p_rs * (int64_t)sizeof(T);
+  uint4 x[CPR];
+#pragma unroll
+  for (int i = 0; i < CPR; ++i) {
+    const int f = t + 256 * i;  // chunk f % CPR of row f / CPR
+    const int r = min(j0 + f / CPR, n - 1);
+    x[i] = *reinterpret_cast<const uint4*>(base + (int64_t)r * rs + (f % CPR) * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < CPR; ++i) {
+    const int f = t + 256 * i;
+    *reinterpret_cast<uint4*>(rows + (f / CPR) * PITCH + (f % CPR) * 16) = x[i];
+  }
   __syncthreads();
-  const int j = blockIdx.x * 256 + threadIdx.x;
+  const int j = j0 + t;
   if (j >= n) return;
-  const T* row = pool + h * p_hs + (int64_t)j * p_rs;
-  constexpr int PER = 16 / sizeof(T);
+  const char* row = rows + t * PITCH;
+  constexpr int PER = 16 / (int)sizeof(T);
   double acc = 0.0;
-  for (int c0 = 0; c0 < d; c0 += PER) {
-    const uint4 w = *reinterpret_cast<const uint4*>(row + c0);
+#pragma unroll
+  for (int c0 = 0; c0 < D; c0 += PER) {
+    const uint4 w = *reinterpret_cast<const uint4*>(row + c0 * (int)sizeof(T));
     const T* e = reinterpret_cast<const T*>(&w);
 #pragma unroll
     for (int c = 0; c < PER; ++c) acc = fma(qs[c0 + c], elem<T>(e, c), acc);
@@ -95,113 +120,114 @@ __device__ int block_excl_scan(int v, int* wave_tot, int* total) {
   return r;
 }
 
-constexpr int SEL_CAND = 4096;  // candidates kept in LDS after the first digit
+// One work group per head.  Thread t owns the contiguous run of keys
+// [t*per, t*per + per), held in registers when per <= KPT (RESIDENT), read
+// again from memory on every pass otherwise.  Radix select of the k-th
+// largest key, 12-bit digits from the top (bits 63..52, 51..40, ..., 15..4,
+// then 3..0): a digit's histogram counts the keys that match the prefix
+// chosen so far; the bin holding the remaining-th largest extends the
+// prefix.  The search stops early once that bin holds exactly the keys still
+// wanted (all of them are taken).  Then one pass marks each selected key --
+// a prefix above the chosen one, or equal to it (all of them, or the lowest
+// indices when the full 64-bit key ties) -- and a block scan gives every
+// selected index its output slot in ascending pool order.
+constexpr int KPT = 32;
 
+template <bool RESIDENT>
 __global__ __launch_bounds__(SEL_THREADS) void topk_select(const unsigned long long* keys_all,
                                                            int n, int k, int32_t* idx_all,
                                                            double* score_all) {
   __shared__ int hist[4096];
-  __shared__ unsigned long long cand[SEL_CAND];
   __shared__ int wave_tot[40];
   __shared__ unsigned long long sh_prefix;
-  __shared__ int sh_remaining, sh_ncand;
+  __shared__ int sh_remaining, sh_count;
   const int tid = threadIdx.x;
   const int h = blockIdx.x;
   const unsigned long long* keys = keys_all + (int64_t)h * n;
-  // Radix select of the k-th largest key, most significant digit first: a
-  // 12-bit digit over all keys, then 8-bit digits (a 4-bit one last).  After
-  // the first digit the keys sharing the selected prefix are copied to LDS
-  // when they fit, and the remaining digits run there.
+  const int per = (n + SEL_THREADS - 1) / SEL_THREADS;
+  const int j0 = min(n, tid * per), j1 = min(n, j0 + per);
+  const int cnt = j1 - j0;
+  unsigned long long kr[RESIDENT ? KPT : 1];
+  if constexpr (RESIDENT) {
+#pragma unroll
+    for (int e = 0; e < KPT; ++e) kr[e] = e < cnt ? keys[j0 + e] : 0ull;
+  }
+  // f(key, position in the run) over this thread's keys, in index order
+  auto for_keys = [&](auto&& f) {
+    if constexpr (RESIDENT) {
+#pragma unroll
+      for (int e = 0; e < KPT; ++e)
+        if (e < cnt) f(kr[e], e);
+    } else {
+      for (int e = 0; e < cnt; ++e) f(keys[j0 + e], e);
+    }
+  };
   unsigned long long prefix = 0, pmask = 0;
-  int remaining = k;  // how many of the largest keys with this prefix are still wanted
-  // one digit: histogram of (key >> shift) & (nb-1) over the keys matching the
-  // prefix, then the bin holding the remaining-th largest
-  auto digit = [&](auto&& for_keys, int shift, int nb) {
-    for (int b = tid; b < nb; b += SEL_THREADS) hist[b] = 0;
+  int remaining = k;  // keys with this prefix still to take
+  bool all_eq = false;  // every key matching the prefix is taken
+  for (int shift = 52; shift >= 0 && !all_eq; shift = shift >= 12 ? shift - 12 : (shift > 0 ? 0 : -1)) {
+    const int bits = shift >= 4 ? 12 : 4;  // the last digit is bits 3..0
+    const int nb = 1 << bits;
+    for (int b = tid; b < 4096; b += SEL_THREADS) hist[b] = 0;
     __syncthreads();
-    for_keys([&](unsigned long long key) {
+    for_keys([&](unsigned long long key, int) {
       if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nb - 1)], 1);
     });
     __syncthreads();
-    // thread t owns bins t*per .. t*per+per-1; counts above a thread's bins
-    // come from an exclusive scan of the per-thread sums
-    const int per = nb / SEL_THREADS > 0 ? nb / SEL_THREADS : 1;
-    const int b0 = tid * per;
+    // thread t owns bins 4t .. 4t+3 (the first nb of them exist)
+    const int b0 = 4 * tid;
     int mine = 0;
     if (b0 < nb)
-      for (int e = 0; e < per; ++e) mine += hist[b0 + e];
+      for (int e = 0; e < 4; ++e) mine += hist[b0 + e];
     int tot;
     const int below = block_excl_scan(mine, wave_tot, &tot);
-    const int above = tot - below - mine;  // keys in bins above this thread's
+    const int above = tot - below - mine;  // keys in higher bins
     if (b0 < nb && above < remaining && remaining <= above + mine) {
       int acc = above, sel = b0;
-      for (int e = per - 1; e >= 0; --e) {
+      for (int e = 3; e >= 0; --e) {
         if (acc + hist[b0 + e] >= remaining) { sel = b0 + e; break; }
         acc += hist[b0 + e];
       }
       sh_prefix = prefix | ((unsigned long long)sel << shift);
       sh_remaining = remaining - acc;
+      sh_count = hist[sel];
     }
     __syncthreads();
     prefix = sh_prefix;
     remaining = sh_remaining;
+    all_eq = sh_count == remaining;
     pmask |= (unsigned long long)(nb - 1) << shift;
     __syncthreads();
-  };
-  auto global_keys = [&](auto&& f) {
-    for (int j = tid; j < n; j += SEL_THREADS) f(keys[j]);
-  };
-  digit(global_keys, 52, 4096);
-  if (tid == 0) sh_ncand = 0;
-  __syncthreads();
-  const int n_match = hist[(int)((prefix >> 52) & 4095)];
-  if (n_match <= SEL_CAND) {
-    for (int j = tid; j < n; j += SEL_THREADS) {
-      const unsigned long long key = keys[j];
-      if ((key & pmask) == prefix) cand[atomicAdd(&sh_ncand, 1)] = key;
-    }
-    __syncthreads();
-    const int nc = sh_ncand;
-    auto lds_keys = [&](auto&& f) {
-      for (int j = tid; j < nc; j += SEL_THREADS) f(cand[j]);
-    };
-    for (int shift = 44; shift >= 4; shift -= 8) digit(lds_keys, shift, 256);
-    digit(lds_keys, 0, 16);
-  } else {
-    for (int shift = 44; shift >= 4; shift -= 8) digit(global_keys, shift, 256);
-    digit(global_keys, 0, 16);
   }
-  const unsigned long long T = prefix;
-  const int need = remaining;  // keys equal to T to take, lowest indices first
-  // contiguous run per thread
-  const int per = (n + SEL_THREADS - 1) / SEL_THREADS;
-  const int j0 = min(n, tid * per), j1 = min(n, j0 + per);
+  // selected: prefix above the chosen one, or equal to it (every such key
+  // when all_eq, else the lowest `remaining` indices: the full key ties)
   int gt = 0, eq = 0;
-  for (int j = j0; j < j1; ++j) {
-    const unsigned long long key = keys[j];
-    gt += key > T;
-    eq += key == T;
-  }
+  for_keys([&](unsigned long long key, int) {
+    const unsigned long long m = key & pmask;
+    gt += m > prefix;
+    eq += m == prefix;
+  });
   int tot;
   const int gt_pre = block_excl_scan(gt, wave_tot, &tot);
   const int eq_pre = block_excl_scan(eq, wave_tot, &tot);
+  const int need = all_eq ? 0x7fffffff : remaining;
   int pos = gt_pre + min(eq_pre, need);
   int eq_seen = eq_pre;
   int32_t* idx = idx_all + (int64_t)h * k;
   double* score = score_all ? score_all + (int64_t)h * k : nullptr;
-  for (int j = j0; j < j1; ++j) {
-    const unsigned long long key = keys[j];
-    bool take = key > T;
-    if (key == T) {
+  for_keys([&](unsigned long long key, int e) {
+    const unsigned long long m = key & pmask;
+    bool take = m > prefix;
+    if (m == prefix) {
       take = eq_seen < need;
       ++eq_seen;
     }
     if (take) {
-      idx[pos] = j;
+      idx[pos] = j0 + e;
       if (score) score[pos] = key_value(key);
       ++pos;
     }
-  }
+  });
 }
 
 // Thread = (prefix row r, 16-byte chunk): copy the pool row idx[h, r].
@@ -232,18 +258,29 @@ hipError_t launch_topk(int dtype, int n_heads, int pool_len, int d, int k, const
                        int64_t p_rs, int32_t* idx, double* score, void* pref_k, void* pref_v,
                        int64_t r_hs, int64_t r_rs, void* ws, hipStream_t s) {
   unsigned long long* keys = static_cast<unsigned long long*>(ws);
-  const dim3 g1((unsigned)ceil_div(pool_len, 256), (unsigned)n_heads);
-  if (dtype == SA_BF16)
-    hipLaunchKernelGGL(topk_score<unsigned short>, g1, dim3(256), 0, s,
-                       static_cast<const unsigned short*>(q), q_hs,
-                       static_cast<const unsigned short*>(pool_k), p_hs, p_rs, pool_len, d, keys);
+  const dim3 g1((unsigned)ceil_div(pool_len, SCORE_ROWS), (unsigned)n_heads);
+  const dim3 b1(256);
+  typedef unsigned short u16;
+  if (dtype == SA_BF16 && d == 128)
+    hipLaunchKernelGGL((topk_score<u16, 128>), g1, b1, 0, s, static_cast<const u16*>(q), q_hs,
+                       static_cast<const u16*>(pool_k), p_hs, p_rs, pool_len, keys);
+  else if (dtype == SA_BF16)
+    hipLaunchKernelGGL((topk_score<u16, 64>), g1, b1, 0, s, static_cast<const u16*>(q), q_hs,
+                       static_cast<const u16*>(pool_k), p_hs, p_rs, pool_len, keys);
+  else if (d == 128)
+    hipLaunchKernelGGL((topk_score<float, 128>), g1, b1, 0, s, static_cast<const float*>(q), q_hs,
+                       static_cast<const float*>(pool_k), p_hs, p_rs, pool_len, keys);
   else
-    hipLaunchKernelGGL(topk_score<float>, g1, dim3(256), 0, s, static_cast<const float*>(q), q_hs,
-                       static_cast<const float*>(pool_k), p_hs, p_rs, pool_len, d, keys);
+    hipLaunchKernelGGL((topk_score<float, 64>), g1, b1, 0, s, static_cast<const float*>(q), q_hs,
+                       static_cast<const float*>(pool_k), p_hs, p_rs, pool_len, keys);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(topk_select, dim3(n_heads), dim3(SEL_THREADS), 0, s, keys, pool_len, k, idx,
-                     score);
+  if (ceil_div(pool_len, SEL_THREADS) <= KPT)
+    hipLaunchKernelGGL(topk_select<true>, dim3(n_heads), dim3(SEL_THREADS), 0, s, keys, pool_len, k,
+                       idx, score);
+  else
+    hipLaunchKernelGGL(topk_select<false>, dim3(n_heads), dim3(SEL_THREADS), 0, s, keys, pool_len, k,
+                       idx, score);
   e = hipGetLastError();
   if (e != hipSuccess || pool_v == nullptr) return e;
   const int esz = dtype == SA_BF16 ? 2 : 4;
