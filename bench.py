@@ -318,89 +318,109 @@ def load_traffic(workload_name, stage="attend"):
     return (d["fetch_kib"] * d["copy_factor_fetch"] + d["write_kib"] * d["copy_factor_write"]) * 1024.0
 
 
-def cpu_baseline(wl, inp, budget_s):
-    """The fp64 oracle (as it stands) on a bounded sample of the workload."""
+_CPU = {}
+
+
+def _cpu_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+        _CPU["limit"] = threadpool_limits(1)  # one thread per process: the pool spreads the work
+    except Exception:  # pragma: no cover
+        pass
+
+
+def _cpu_tile(task):
+    """One (head, query tile) of the oracle's fast mode; skipped once the deadline passed."""
     import numpy as np
 
     import oracle as O
+    h, t = task
+    if time.time() > _CPU["deadline"]:
+        return 0, 0
+    wl, spec, Q, K, V = _CPU["wl"], _CPU["spec"], _CPU["q"], _CPU["k"], _CPU["v"]
+    g = h // (wl.h_q // wl.h_kv)
+    rows = np.arange(128 * t, min(wl.n_q, 128 * t + 128))
+    slope = None if wl.alibi_exp is None else O.alibi_slope(h, wl.h_q, wl.alibi_exp)
+    O.attention_fast(Q[h].astype(np.float64), K[g].astype(np.float64), V[g].astype(np.float64), spec,
+                     wl.rope_base, wl.scale, [rows], alibi=slope)
+    return int(O.mask_rows(spec, rows).sum()), 1
+
+
+def cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([x.get("num_threads", 1) for x in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:  # pragma: no cover
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, inp, budget_s):
+    """The fp64 oracle (as it stands) on a bounded sample of the workload: its fast mode
+    over (head, query tile) tasks, last tiles first (the ones with the most keys), in a
+    process pool of one single-threaded worker per core this process may run on, for
+    about budget_s seconds of wall time.  Run before the GPU is touched."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    import oracle as O
+    cores = len(os.sched_getaffinity(0))
     sep = inp.get("sep")
     spec = O.MaskSpec(wl.mode, wl.n_q, wl.n_k, a=wl.a, w=wl.w,
                       sep=None if sep is None else sep.numpy(), n_s=wl.n_s, L=wl.L, P=wl.P)
     if wl.mode == "segment":
-        k = np.concatenate([inp["k_tail"][0, 0].double().numpy(), inp["k_seg"][0, 0].double().numpy()])
-        v = np.concatenate([inp["v_tail"][0, 0].double().numpy(), inp["v_seg"][0, 0].double().numpy()])
+        k = np.concatenate([inp["k_tail"][0, :1].float().numpy(), inp["k_seg"][0, :1].float().numpy()], axis=1)
+        v = np.concatenate([inp["v_tail"][0, :1].float().numpy(), inp["v_seg"][0, :1].float().numpy()], axis=1)
+        q = inp["q"][0, :1].float().numpy()
+        heads = [0]
     else:
-        k = inp["k"][0, 0].double().numpy()
-        v = inp["v"][0, 0].double().numpy()
-    q = inp["q"][0, 0].double().numpy()
-    slope = None if wl.alibi_exp is None else O.alibi_slope(0, wl.h_q, wl.alibi_exp)
+        q, k, v = (inp[x][0].float().numpy() for x in ("q", "k", "v"))
+        heads = list(range(wl.h_q))
     n_tiles = -(-wl.n_q // 128)
-    # tiles from the last one backwards: the ones with the most keys
-    pairs = 0
-    done = 0
-    t0 = time.perf_counter()
-    for t in range(n_tiles - 1, -1, -1):
-        rows = np.arange(128 * t, min(wl.n_q, 128 * t + 128))
-        O.attention_fast(q, k, v, spec, wl.rope_base, wl.scale, [rows], alibi=slope)
-        pairs += int(O.mask_rows(spec, rows).sum())
-        done += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": 4.0 * wl.d * pairs / el / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"head 0, last {done} of {n_tiles} query tiles (128 rows each), fast mode fp64, "
-                      f"{el:.1f} s; rate scaled to effective FLOPs of the sampled rows"}
+    tasks = [(h, t) for t in range(n_tiles - 1, -1, -1) for h in heads]
+    _CPU.update(wl=wl if wl.mode != "segment" else dataclass_replace(wl, h_q=1, h_kv=1),
+                spec=spec, q=q, k=k, v=v)
+    t0 = time.time()
+    _CPU["deadline"] = t0 + budget_s
+    pairs = done = 0
+    with mp.get_context("fork").Pool(cores, initializer=_cpu_worker_init) as pool:
+        for pr, n in pool.imap_unordered(_cpu_tile, tasks, chunksize=1):
+            pairs += pr
+            done += n
+            if time.time() > _CPU["deadline"]:
+                break
+        pool.terminate()
+    el = time.time() - t0
+    return {"value": 4.0 * wl.d * pairs / el / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"{done} (head, 128-row query tile) tasks of {len(tasks)}, last tiles first, "
+                      f"fast mode fp64, {cores} single-threaded processes, {el:.1f} s wall; rate scaled "
+                      f"to the effective FLOPs of the sampled rows"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, help="1..6 (default: the 32K Lambda layer)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
-    ap.add_argument("--no-gemm-ceiling", action="store_true",
-                    help="skip the dense bf16 GEMM reference measurement")
-    ap.add_argument("--backward", type=int, default=0,
-                    help="also time the backward over this many steps (0: skip)")
-    ap.add_argument("--topk-middle", type=int, default=0,
-                    help="Lambda workloads: also time the top-k middle tokens with this k (0: skip)")
-    ap.add_argument("--decode", type=int, default=0,
-                    help="also time this many streaming decode steps (0: skip)")
-    ap.add_argument("--segments", type=int, default=8,
-                    help="segment workload: also run this many consecutive segments (0: skip)")
-    ap.add_argument("--copy-calib", action="store_true",
-                    help="also run a plain 256 MiB device copy (scale for PMC byte counters)")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(heads or query tiles would shard with no or one exchange step)", file=sys.stderr)
-        sys.exit(2)
+def dataclass_replace(obj, **kw):
+    import dataclasses
+    return dataclasses.replace(obj, **kw)
 
+
+def measure_layer(wl, inp, steps, warmup, torch):
+    """Times `steps` passes of the hot path on one workload (inputs moved to HBM first):
+    plan, RoPE stage and fused forward (plus top-k retrieval for the segment workload),
+    each bracketed by HIP events on the launch stream.  Returns the layer's figures and
+    the objects the optional extra measurements reuse."""
     import numpy as np
-    import torch
 
-    import workloads as W
     from structured_sparse_attention_attn_amd import (fwd_args, plan_to_host, sparse_attn_attend,
                                                       sparse_attn_plan, sparse_attn_rope)
     from structured_sparse_attention_attn_amd.pipeline import SparseAttention, TopK
 
-    wl = W.WORKLOADS[args.workload]
     dev = "cuda"
-    torch.cuda.set_device(0)
-    inp = W.make_inputs(wl)
     sep = inp.get("sep")
     stream = torch.cuda.current_stream()
-
     topk = None
+    run_topk = None
     if wl.mode == "segment":
         S, P, H, d = wl.n_q, wl.P, wl.h_q, wl.d
         nl = wl.n_local
@@ -426,13 +446,13 @@ def main():
     o = torch.empty_like(q)
     lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device=dev)
     fa = fwd_args(q, k, v, o, lse=lse, rope_base=wl.rope_base, scale=wl.scale,
-                  alibi_exp=wl.alibi_exp)
+                  alibi_exp=wl.alibi_exp, mask=sa.mask)
     sa.ensure_workspace(fa)
     torch.cuda.synchronize()
 
     def step(ev):
         ev[0].record(stream)
-        if topk is not None:
+        if run_topk is not None:
             run_topk()
         ev[1].record(stream)
         sparse_attn_plan(sa.mask, sa.plan)
@@ -443,10 +463,10 @@ def main():
         ev[4].record(stream)
 
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(5)]  # noqa: E731
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step(mk())
     torch.cuda.synchronize()
-    evs = [mk() for _ in range(args.steps)]
+    evs = [mk() for _ in range(steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
@@ -454,38 +474,29 @@ def main():
         step(e)
     t_end.record(stream)
     torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ms_step = t_start.elapsed_time(t_end) / steps
     stage = {name: float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
              for i, name in enumerate(["topk", "plan", "rope", "attend"])}
-    if topk is None:
+    if run_topk is None:
         stage.pop("topk")
 
     def spread(vals):
-        v = np.asarray(vals, dtype=np.float64)
-        return {"median": round(float(np.median(v)), 4), "p10": round(float(np.percentile(v, 10)), 4),
-                "p90": round(float(np.percentile(v, 90)), 4)}
+        x = np.asarray(vals, dtype=np.float64)
+        return {"median": round(float(np.median(x)), 4), "p10": round(float(np.percentile(x, 10)), 4),
+                "p90": round(float(np.percentile(x, 90)), 4)}
 
     step_spread = {"step": spread([e[0].elapsed_time(e[4]) for e in evs]),
                    "attend": spread([e[3].elapsed_time(e[4]) for e in evs])}
     in_bytes = sum(t.numel() * t.element_size() for t in (q, k, v, o))
     cache = ("warm: q, k, v and o fit in the 256 MB last-level cache" if in_bytes <= (256 << 20)
              else "cold: q, k, v and o exceed the 256 MB last-level cache")
-
-    if args.copy_calib:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-
     pairs_head = pair_count_per_head(wl, None if sep is None else sep.numpy())
     flops = 4.0 * wl.d * pairs_head * wl.h_q * wl.batch
     value = flops / (ms_step * 1e-3) / 1e12
     attend_tflops = flops / (stage["attend"] * 1e-3) / 1e12
-    traffic = load_traffic(wl.name)
     roofline = {"bound": "mfma", "achieved": round(attend_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(attend_tflops / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic}
+                "traffic": load_traffic(wl.name)}
     host_plan = plan_to_host(sa.mask, sa.plan)
     iflops = issued_flops(wl, host_plan)
     issued = {"flops_per_launch": iflops, "ratio_to_effective": round(iflops / flops, 4),
@@ -500,37 +511,95 @@ def main():
                                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4)}
             if name_ == "rope":
                 stage_roofline[name_]["traffic"] = load_traffic(wl.name, "rope")
+    res = {
+        "value": value, "ms_step": ms_step, "flops": flops, "pairs_head": pairs_head,
+        "ms_per_layer": round(stage["rope"] + stage["attend"], 4),
+        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "stages_ms": {k_: round(v_, 4) for k_, v_ in stage.items()},
+        "per_step_ms": step_spread, "cache": cache, "roofline": roofline, "issued_mfma": issued,
+        "stages_roofline": stage_roofline,
+    }
+    ctx = dict(sa=sa, q=q, k=k, v=v, o=o, lse=lse)
+    return res, ctx
+
+
+def config_of(wl, pairs_head):
+    return {"workload": wl.name, "mode": wl.mode, "batch": wl.batch, "h_q": wl.h_q,
+            "h_kv": wl.h_kv, "head_dim": wl.d, "n_q": wl.n_q, "n_k": wl.n_k,
+            "a": wl.a, "w": wl.w, "p_sep": wl.p_sep, "n_starting": wl.n_s,
+            "L_pretrain": wl.L, "prefix_len": wl.P, "rope_base": wl.rope_base,
+            "alibi_exp": wl.alibi_exp, "pairs_per_head": pairs_head}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="1..6 (default: the 32K Lambda layer)")
+    ap.add_argument("--no-128k", action="store_true",
+                    help="with the default workload, skip the 128K GQA SepLLM layer's sub-object")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--no-gemm-ceiling", action="store_true",
+                    help="skip the dense bf16 GEMM reference measurement")
+    ap.add_argument("--backward", type=int, default=0,
+                    help="also time the backward over this many steps (0: skip)")
+    ap.add_argument("--topk-middle", type=int, default=0,
+                    help="Lambda workloads: also time the top-k middle tokens with this k (0: skip)")
+    ap.add_argument("--decode", type=int, default=0,
+                    help="also time this many streaming decode steps (0: skip)")
+    ap.add_argument("--segments", type=int, default=8,
+                    help="segment workload: also run this many consecutive segments (0: skip)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run a plain 256 MiB device copy (scale for PMC byte counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(heads or query tiles would shard with no or one exchange step)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+
+    wl = W.WORKLOADS[args.workload]
+    inp = W.make_inputs(wl)
+    # the oracle sample runs first, on the host cores, before the GPU is touched
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl, inp, args.cpu_budget_s)
+
+    torch.cuda.set_device(0)
+    res, ctx = measure_layer(wl, inp, args.steps, args.warmup, torch)
+    if args.copy_calib:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
     props = torch.cuda.get_device_properties(0)
     out = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": round(res["value"], 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "ms_per_step": round(res["ms_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16" if wl.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded N(0,1) Q/K/V" + (", Bernoulli separator flags" if sep is not None else "")
+        "data": "synthetic (seeded N(0,1) Q/K/V" + (", Bernoulli separator flags" if "sep" in inp else "")
                 + ", resident in HBM)",
-        "config": {"workload": wl.name, "mode": wl.mode, "batch": wl.batch, "h_q": wl.h_q,
-                   "h_kv": wl.h_kv, "head_dim": wl.d, "n_q": wl.n_q, "n_k": wl.n_k,
-                   "a": wl.a, "w": wl.w, "p_sep": wl.p_sep, "n_starting": wl.n_s,
-                   "L_pretrain": wl.L, "prefix_len": wl.P, "rope_base": wl.rope_base,
-                   "alibi_exp": wl.alibi_exp,
-                   "pairs_per_head": pairs_head},
-        "ms_per_layer": round(stage["rope"] + stage["attend"], 4),
-        "pct_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
-        "stages_ms": {k_: round(v_, 4) for k_, v_ in stage.items()},
-        "per_step_ms": step_spread,
-        "cache": cache,
-        "roofline": roofline,
-        "issued_mfma": issued,
-        "stages_roofline": stage_roofline,
-        "device": {"name": props.name, "cus": props.multi_processor_count},
+        "config": config_of(wl, res["pairs_head"]),
     }
+    for key in ("ms_per_layer", "pct_bf16_peak", "stages_ms", "per_step_ms", "cache", "roofline",
+                "issued_mfma", "stages_roofline"):
+        out[key] = res[key]
+    out["device"] = {"name": props.name, "cus": props.multi_processor_count}
+    sa, q, k, v, o, lse = (ctx[x] for x in ("sa", "q", "k", "v", "o", "lse"))
+    flops = res["flops"]
     if args.backward > 0 and wl.dtype == "bf16":
         import structured_sparse_attention_attn_amd as sa_mod
         bms, bws = backward_timing(sa_mod, sa, q, k, v, o, lse, wl, args.backward, torch)
@@ -547,10 +616,22 @@ def main():
         out["decode_lambda"] = lambda_decode_timing(args.decode, torch)
     if wl.mode == "segment" and args.segments > 0:
         out["multi_segment"] = multi_segment(wl, inp, args.segments, torch)
+    del ctx, sa, q, k, v, o, lse
+    if args.workload == 3 and not args.no_128k:
+        # the second configuration the 50%-of-peak target names: 128K GQA SepLLM layer
+        wl5 = W.WORKLOADS[5]
+        inp5 = W.make_inputs(wl5)
+        r5, _ = measure_layer(wl5, inp5, max(3, args.steps // 4), max(1, args.warmup), torch)
+        out["w128k"] = {"config": config_of(wl5, r5["pairs_head"]), "steps": max(3, args.steps // 4),
+                        "effective_tflops": round(r5["value"], 3), "ms_per_step": round(r5["ms_step"], 4)}
+        for key in ("ms_per_layer", "pct_bf16_peak", "stages_ms", "per_step_ms", "cache", "roofline",
+                    "issued_mfma", "stages_roofline"):
+            out["w128k"][key] = r5[key]
+        del inp5
     if not args.no_gemm_ceiling:
         out["gemm_ceiling_tflops"] = round(gemm_ceiling_tflops(torch), 1)
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, args.cpu_budget_s)
+    if cpu is not None:
+        out["cpu_baseline"] = cpu
     print(json.dumps(out), flush=True)
 
 
