@@ -308,6 +308,23 @@ int sparse_attn_decode_step(const sa_stream_cfg_t *cfg, void *state, size_t stat
                             void *o, float *lse, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /*
+ * The same decode step with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  The per-step scratch (rotated queries,
+ * capped logits, per-split partial sums: sa_decode_workspace_bytes) lives in a
+ * static array of SA_DECODE_STATIC_SCRATCH_BYTES in each GPU's memory, held by
+ * the library until the process ends; the call allocates nothing.  A
+ * configuration needing more scratch than that returns SA_ENOSPACE.  Every
+ * call on one GPU shares that GPU's array: calls that overlap in time on one
+ * GPU (other streams, other threads) race and must be ordered by the caller.
+ * Arguments, results and errors are those of sparse_attn_decode_step.
+ */
+enum { SA_DECODE_STATIC_SCRATCH_BYTES = 32 << 20 };
+int sparse_attn_decode_step_static(const sa_stream_cfg_t *cfg, void *state, size_t state_bytes,
+                                   const void *q, const void *k, const void *v, const uint8_t *is_sep,
+                                   void *o, float *lse, hipStream_t stream);
+
+/*
  * Host only: the state layout (byte offsets of the K rows, V rows, per-slot
  * token index int32 [batch, c], per-slot flag uint8 [batch, c] and the
  * per-sequence counters int32 [batch, 8]: t, n_init, n_sep, sep_head, n_past,

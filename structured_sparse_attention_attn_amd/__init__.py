@@ -33,6 +33,7 @@ SA_F32, SA_BF16 = 0, 1
 SA_ROPE_NONE, SA_ROPE_HALF, SA_ALIBI = 0, 1, 2
 SA_TQ, SA_BK = 128, 64
 SA_TOPK_MIDDLE_MAX = 64
+SA_DECODE_STATIC_SCRATCH_BYTES = 32 << 20
 SA_ITEM_FULL, SA_ITEM_CAPPED = 1, 2
 
 _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -103,10 +104,11 @@ _lib.sa_decode_workspace_bytes.argtypes = [_CFGP, ctypes.POINTER(_sz)]
 _lib.sa_stream_layout.argtypes = [_CFGP, ctypes.POINTER(_i64)]
 _lib.sparse_attn_stream_reset.argtypes = [_CFGP, _vp, _sz, _vp]
 _lib.sparse_attn_decode_step.argtypes = [_CFGP, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.sparse_attn_decode_step_static.argtypes = [_CFGP, _vp, _sz, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 _lib.sparse_attn_topk_middle.argtypes = [_MASKP, _ARGSP, _i32, _vp, _vp, _vp]
 _lib.sparse_attn_topk_middle.restype = ctypes.c_int
 for _name in ("sa_stream_state_bytes", "sa_decode_workspace_bytes", "sa_stream_layout",
-              "sparse_attn_stream_reset", "sparse_attn_decode_step"):
+              "sparse_attn_stream_reset", "sparse_attn_decode_step", "sparse_attn_decode_step_static"):
     getattr(_lib, _name).restype = ctypes.c_int
 for _name in ("sa_plan_layout", "sa_plan_bytes", "sparse_attn_plan", "sa_fwd_workspace_bytes",
               "sa_fwd_workspace_layout",
@@ -408,6 +410,18 @@ def sparse_attn_decode_step(cfg: sa_stream_cfg_t, state, q, k, v, is_sep, o, ws,
     _check(_lib.sparse_attn_decode_step(ctypes.byref(cfg), _ptr(state), state.numel(), _ptr(q), _ptr(k),
                                         _ptr(v), _ptr(is_sep), _ptr(o), _ptr(lse), _ptr(ws),
                                         ws.numel(), _stream(stream)))
+
+
+def sparse_attn_decode_step_static(cfg: sa_stream_cfg_t, state, q, k, v, is_sep, o, lse=None,
+                                   stream=None) -> None:
+    """The decode step with the library's static scratch instead of a workspace (see
+    include/sparse_attn.h): it allocates nothing."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    _check(_lib.sparse_attn_decode_step_static(ctypes.byref(cfg), _ptr(state), state.numel(), _ptr(q),
+                                               _ptr(k), _ptr(v), _ptr(is_sep), _ptr(o), _ptr(lse),
+                                               _stream(stream)))
 
 
 def sparse_attn_topk_middle(m: sa_mask_t, args: sa_fwd_args_t, k_mid: int, sel, score, stream=None) -> None:

@@ -637,32 +637,72 @@ int sparse_attn_stream_reset(const sa_stream_cfg_t* cfg, void* state, size_t sta
   return ok();
 }
 
-int sparse_attn_decode_step(const sa_stream_cfg_t* cfg, void* state, size_t state_bytes, const void* q,
-                            const void* k, const void* v, const uint8_t* is_sep, void* o, float* lse, void* ws,
-                            size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the two decode-step entry points (everything but the
+// workspace).
+int check_decode(const sa_stream_cfg_t* cfg, const void* state, size_t state_bytes, const void* q,
+                 const void* k, const void* v, const uint8_t* is_sep, const void* o) {
   int r = check_stream_cfg(cfg);
   if (r != SA_OK) return r;
-  const sa_stream_cfg_t geo = stream_geometry(*cfg);
-  const sa::StreamLayout L = sa::stream_layout(geo);
+  const sa::StreamLayout L = sa::stream_layout(stream_geometry(*cfg));
   if (state == nullptr || !aligned16(state)) return fail(SA_EINVAL, "state must be a 16-byte aligned device pointer");
   if (state_bytes < (size_t)L.total)
     return fail(SA_ENOSPACE, "state too small: %zu < %lld bytes", state_bytes, (long long)L.total);
-  if (ws == nullptr || !aligned16(ws)) return fail(SA_EINVAL, "workspace must be a 16-byte aligned device pointer");
-  if (ws_bytes < (size_t)L.ws_total)
-    return fail(SA_ENOSPACE, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)L.ws_total);
   if (q == nullptr || k == nullptr || v == nullptr || o == nullptr ||
       (is_sep == nullptr && cfg->kind == SA_MASK_SEPLLM))
     return fail(SA_EINVAL, "q, k, v, o (and is_sep for SEPLLM) must not be NULL");
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(SA_EINVAL, "q, k, v and o must be 16-byte aligned");
-  if ((r = check_device()) != SA_OK) return r;
+  return SA_OK;
+}
+
+int launch_decode(const sa_stream_cfg_t* cfg, void* state, const void* q, const void* k, const void* v,
+                  const uint8_t* is_sep, void* o, float* lse, void* ws, hipStream_t stream) {
   sa::ThetaTable th;
   memset(&th, 0, sizeof(th));
   if (cfg->rope == SA_ROPE_HALF)
     for (int c = 0; c < cfg->d / 2; ++c) th.th[c] = std::pow((double)cfg->rope_base, -2.0 * c / cfg->d);
-  hipError_t e = sa::launch_decode_step(geo, state, q, k, v, is_sep, o, lse, ws, th, stream);
+  hipError_t e = sa::launch_decode_step(stream_geometry(*cfg), state, q, k, v, is_sep, o, lse, ws, th, stream);
   if (e != hipSuccess) return fail(SA_EHIP, "decode launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int sparse_attn_decode_step(const sa_stream_cfg_t* cfg, void* state, size_t state_bytes, const void* q,
+                            const void* k, const void* v, const uint8_t* is_sep, void* o, float* lse, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  int r = check_decode(cfg, state, state_bytes, q, k, v, is_sep, o);
+  if (r != SA_OK) return r;
+  const sa::StreamLayout L = sa::stream_layout(stream_geometry(*cfg));
+  if (ws == nullptr || !aligned16(ws)) return fail(SA_EINVAL, "workspace must be a 16-byte aligned device pointer");
+  if (ws_bytes < (size_t)L.ws_total)
+    return fail(SA_ENOSPACE, "workspace too small: %zu < %lld bytes", ws_bytes, (long long)L.ws_total);
+  if ((r = check_device()) != SA_OK) return r;
+  return launch_decode(cfg, state, q, k, v, is_sep, o, lse, ws, stream);
+}
+
+int sparse_attn_decode_step_static(const sa_stream_cfg_t* cfg, void* state, size_t state_bytes, const void* q,
+                                   const void* k, const void* v, const uint8_t* is_sep, void* o, float* lse,
+                                   hipStream_t stream) {
+  int r = check_decode(cfg, state, state_bytes, q, k, v, is_sep, o);
+  if (r != SA_OK) return r;
+  const sa::StreamLayout L = sa::stream_layout(stream_geometry(*cfg));
+  if (L.ws_total > (int64_t)SA_DECODE_STATIC_SCRATCH_BYTES)
+    return fail(SA_ENOSPACE,
+                "the step needs %lld bytes of scratch, more than the library's static %d bytes "
+                "(use sparse_attn_decode_step with a workspace)",
+                (long long)L.ws_total, (int)SA_DECODE_STATIC_SCRATCH_BYTES);
+  if ((r = check_device()) != SA_OK) return r;
+  void* ws = nullptr;
+  hipError_t e = sa::decode_static_scratch(&ws);
+  if (e != hipSuccess) return fail(SA_EHIP, "static scratch lookup: %s", hipGetErrorString(e));
+  return launch_decode(cfg, state, q, k, v, is_sep, o, lse, ws, stream);
 }
 
 int sparse_attn_topk_middle(const sa_mask_t* m, const sa_fwd_args_t* a, int32_t k_mid, int32_t* sel,

@@ -133,6 +133,10 @@ hipError_t launch_decode_step(const sa_stream_cfg_t& cfg, void* state, const voi
                               const void* v, const uint8_t* is_sep, void* o, float* lse, void* ws,
                               const ThetaTable& theta, hipStream_t s);
 
+// The no-allocation decode step's scratch array on the current device (its
+// device address, looked up once per device).
+hipError_t decode_static_scratch(void** out);
+
 hipError_t launch_topk_middle(const sa_mask_t& m, const sa_fwd_args_t& a, int kmid, int32_t* sel, float* score,
                               hipStream_t s);
 

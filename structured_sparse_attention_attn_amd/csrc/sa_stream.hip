@@ -17,6 +17,8 @@
 // ranges the step leaves) and decode_combine (the splits merged; its extra
 // work groups, one per sequence, record each slot's token index and
 // separator flag and advance the counters).
+#include <atomic>
+
 #include "sa_common.h"
 
 namespace sa {
@@ -605,6 +607,34 @@ hipError_t launch_decode_step(const sa_stream_cfg_t& cfg, void* state, const voi
     hipLaunchKernelGGL(decode_attn<false>, dim3((unsigned)(cfg.batch * cfg.h_kv * L.n_split)), dim3(256), 0, s, p);
   hipLaunchKernelGGL(decode_combine, dim3((unsigned)(cfg.batch * cfg.h_q + cfg.batch)), dim3(256), 0, s, p);
   return hipGetLastError();
+}
+
+// Per-step scratch of the no-allocation decode step: one array in each GPU's
+// memory, held until the process ends.  Host code never passes the array's
+// name to a kernel; it uses the device address hipGetSymbolAddress returns,
+// looked up once per device (with that device current) and kept.  Every
+// value a step reads from it is written earlier in the same step (rotated
+// queries, capped logits, per-split partial sums), so nothing is cleared.
+static __device__ __align__(256) char scratch[SA_DECODE_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDev = 64;
+std::atomic<void*> g_scratch[kMaxScratchDev];
+}  // namespace
+
+hipError_t decode_static_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDev) return hipErrorInvalidDevice;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (ptr == nullptr) {
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return hipSuccess;
 }
 
 }  // namespace sa
