@@ -770,6 +770,9 @@ MID_CASES = [
     (dict(m=300, n_s=10, L=0), 1, None),
     (dict(m=200, n_s=10, L=250), 4, 10000.0),
     (dict(m=600, n_s=70, L=130, batch=2), 5, 500000.0),
+    # lists beyond 8 entries (16- and 64-entry selection lists)
+    (dict(m=700, n_s=10, L=100, h_q=4, h_kv=2), 16, 10000.0),
+    (dict(m=500, n_s=4, L=64), 40, 10000.0),
 ]
 
 
