@@ -62,6 +62,17 @@ enum { SA_ITEM_FULL = 1, SA_ITEM_CAPPED = 2 };
  *   n_starting  LAMBDA: starting span >= 0.
  *   L_pretrain  LAMBDA: window i-j <= L_pretrain and distance cap, >= 0.
  *   prefix_len  SEGMENT: P >= 0.
+ *   sep_max     SEPLLM: 0, or the caller's upper bound on the separators the
+ *               plan lists (the nonzero entries of sep at positions
+ *               j >= g0 = 64*ceil(a/64); a bound on all nonzero entries of
+ *               sep serves).  It sizes the plan's sep_idx section and the
+ *               gathered separator rows of the workspaces (sep_rows =
+ *               64*ceil(min(sep_max, n_k)/64)) instead of n_k.  A mask that
+ *               breaks the bound is detected on the device: the plan keeps
+ *               the first sep_max separators and records the true count,
+ *               sa_plan_status reports SA_ENOSPACE, and the forward writes
+ *               NaN to every output row and log-sum-exp of such a plan.
+ *               0 = no bound.  Must be >= 0.
  * Fields that do not belong to `kind` are ignored.
  */
 typedef struct {
@@ -71,6 +82,7 @@ typedef struct {
   const uint8_t *sep;
   int32_t n_starting, L_pretrain;
   int32_t prefix_len;
+  int32_t sep_max;
 } sa_mask_t;
 
 /*
@@ -84,6 +96,8 @@ typedef struct {
  *   sep_count int32 [n_tiles]     separators gathered by tile t: those in
  *                                 [g0, 64*floor(max(0,q0-w+1)/64)), g0 = 64*ceil(a/64)
  *   sep_idx   int32 [cap_sep]     ascending positions j >= g0 with sep[j] != 0
+ *                                 (cap_sep = n_k, or min(sep_max, n_k); the first
+ *                                 cap_sep of them when n_sep exceeds it)
  *   sep_bits  uint64 [n_blocks]   bit r of word b = (sep[64b+r] != 0)
  *   blk_sep   int32 [n_blocks+1]  separators (j >= g0) before block b
  * LAMBDA and SEGMENT plans have sep_count, sep_bits and blk_sep all zero.
@@ -93,7 +107,7 @@ typedef struct {
   int32_t version;       /* 1 */
   int32_t kind, tq, bk, n_q, n_k, n_tiles, n_blocks;
   int32_t n_items;       /* written by the device */
-  int32_t n_sep;         /* written by the device */
+  int32_t n_sep;         /* written by the device: separators at j >= g0 */
   int32_t g0, cap_items, cap_sep, max_items_per_tile, reserved;
   int64_t off_tile_ptr, off_items, off_sep_count, off_sep_idx, off_sep_bits, off_blk_sep;
   int64_t total_bytes;
@@ -158,6 +172,16 @@ int sa_plan_bytes(const sa_mask_t *m, size_t *bytes);
  * plan), SA_ENOSPACE (plan_bytes too small), SA_EHIP.
  */
 int sparse_attn_plan(const sa_mask_t *m, void *plan, size_t plan_bytes, hipStream_t stream);
+
+/*
+ * Waits for `stream` (the plan must have been built on it) and copies the
+ * plan's header to *out (may be NULL).  Returns SA_ENOSPACE when the mask
+ * held more separators than the plan could list (n_sep > cap_sep: the
+ * caller's sep_max was too small; rebuild with a larger bound), SA_EINVAL
+ * for a NULL or short plan or a header that is not a plan's, SA_EHIP on a
+ * HIP error, else SA_OK.
+ */
+int sa_plan_status(const void *plan, size_t plan_bytes, hipStream_t stream, sa_plan_header_t *out);
 
 /* Host only: bytes of device workspace sparse_attn_fwd needs for (m, args). */
 int sa_fwd_workspace_bytes(const sa_mask_t *m, const sa_fwd_args_t *args, size_t *bytes);

@@ -41,7 +41,8 @@ _i32, _i64, _f32, _vp, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, cty
 
 class sa_mask_t(ctypes.Structure):
     _fields_ = [("kind", _i32), ("n_q", _i32), ("n_k", _i32), ("a", _i32), ("w", _i32),
-                ("sep", _vp), ("n_starting", _i32), ("L_pretrain", _i32), ("prefix_len", _i32)]
+                ("sep", _vp), ("n_starting", _i32), ("L_pretrain", _i32), ("prefix_len", _i32),
+                ("sep_max", _i32)]
 
 
 class sa_plan_header_t(ctypes.Structure):
@@ -85,6 +86,7 @@ _lib.sa_last_error.argtypes = []
 _lib.sa_plan_layout.argtypes = [_MASKP, ctypes.POINTER(sa_plan_header_t)]
 _lib.sa_plan_bytes.argtypes = [_MASKP, ctypes.POINTER(_sz)]
 _lib.sparse_attn_plan.argtypes = [_MASKP, _vp, _sz, _vp]
+_lib.sa_plan_status.argtypes = [_vp, _sz, _vp, ctypes.POINTER(sa_plan_header_t)]
 _lib.sa_fwd_workspace_bytes.argtypes = [_MASKP, _ARGSP, ctypes.POINTER(_sz)]
 _lib.sa_fwd_workspace_layout.argtypes = [_MASKP, _ARGSP, ctypes.POINTER(sa_fwd_ws_layout_t)]
 _lib.sparse_attn_fwd.argtypes = [_MASKP, _vp, _sz, _ARGSP, _vp, _sz, _vp]
@@ -110,7 +112,7 @@ _lib.sparse_attn_topk_middle.restype = ctypes.c_int
 for _name in ("sa_stream_state_bytes", "sa_decode_workspace_bytes", "sa_stream_layout",
               "sparse_attn_stream_reset", "sparse_attn_decode_step", "sparse_attn_decode_step_static"):
     getattr(_lib, _name).restype = ctypes.c_int
-for _name in ("sa_plan_layout", "sa_plan_bytes", "sparse_attn_plan", "sa_fwd_workspace_bytes",
+for _name in ("sa_plan_layout", "sa_plan_bytes", "sparse_attn_plan", "sa_plan_status", "sa_fwd_workspace_bytes",
               "sa_fwd_workspace_layout",
               "sparse_attn_fwd", "sparse_attn_rope", "sparse_attn_attend", "sa_topk_workspace_bytes",
               "topk_retrieve", "sparse_attn_segment_carry", "sa_bwd_workspace_bytes",
@@ -145,9 +147,10 @@ def _stream(stream) -> Optional[int]:
 
 
 def mask(kind: int, n_q: int, n_k: int, *, a: int = 0, w: int = 1, sep=None, n_starting: int = 0,
-         L_pretrain: int = 0, prefix_len: int = 0) -> sa_mask_t:
-    """Build an sa_mask_t; `sep` is a device uint8 tensor [n_k] (kept alive by the caller)."""
-    return sa_mask_t(kind, n_q, n_k, a, w, _ptr(sep), n_starting, L_pretrain, prefix_len)
+         L_pretrain: int = 0, prefix_len: int = 0, sep_max: int = 0) -> sa_mask_t:
+    """Build an sa_mask_t; `sep` is a device uint8 tensor [n_k] (kept alive by the caller);
+    `sep_max` > 0 bounds the separators the plan lists (0 = no bound)."""
+    return sa_mask_t(kind, n_q, n_k, a, w, _ptr(sep), n_starting, L_pretrain, prefix_len, sep_max)
 
 
 def sa_plan_layout(m: sa_mask_t) -> sa_plan_header_t:
@@ -165,6 +168,14 @@ def sa_plan_bytes(m: sa_mask_t) -> int:
 def sparse_attn_plan(m: sa_mask_t, plan, stream=None) -> None:
     """Enqueue the plan kernels for mask m into the uint8 device tensor `plan`."""
     _check(_lib.sparse_attn_plan(ctypes.byref(m), _ptr(plan), plan.numel(), _stream(stream)))
+
+
+def sa_plan_status(plan, stream=None) -> sa_plan_header_t:
+    """Wait for the plan's stream and return its header; raises SparseAttnError (SA_ENOSPACE)
+    when the mask held more separators than the plan's sep_max bound lets it list."""
+    out = sa_plan_header_t()
+    _check(_lib.sa_plan_status(_ptr(plan), plan.numel(), _stream(stream), ctypes.byref(out)))
+    return out
 
 
 def _check_4d(name, t, shape, dtype, device):
@@ -305,7 +316,7 @@ def plan_to_host(m: sa_mask_t, plan) -> dict:
         "tile_ptr": sec(lay.off_tile_ptr, lay.n_tiles + 1, np.int32),
         "items": sec(lay.off_items, hdr.n_items, np.int32),
         "sep_count": sec(lay.off_sep_count, lay.n_tiles, np.int32),
-        "sep_idx": sec(lay.off_sep_idx, hdr.n_sep, np.int32),
+        "sep_idx": sec(lay.off_sep_idx, min(hdr.n_sep, lay.cap_sep), np.int32),
         "sep_bits": sec(lay.off_sep_bits, lay.n_blocks, np.uint64),
         "blk_sep": sec(lay.off_blk_sep, lay.n_blocks + 1, np.int32),
     }

@@ -59,6 +59,7 @@ int check_mask(const sa_mask_t* m) {
       if (m->n_q != m->n_k) return fail(SA_EINVAL, "SEPLLM needs n_q == n_k (got %d, %d)", m->n_q, m->n_k);
       if (m->a < 0) return fail(SA_EINVAL, "SEPLLM initial count a must be >= 0 (got %d)", m->a);
       if (m->w < 1) return fail(SA_EINVAL, "SEPLLM neighbour count w must be >= 1 (got %d)", m->w);
+      if (m->sep_max < 0) return fail(SA_EINVAL, "SEPLLM separator bound sep_max must be >= 0 (got %d)", m->sep_max);
       break;
     case SA_MASK_LAMBDA:
       if (m->n_q != m->n_k) return fail(SA_EINVAL, "LAMBDA needs n_q == n_k (got %d, %d)", m->n_q, m->n_k);
@@ -143,7 +144,7 @@ WsLayout ws_layout(const sa_mask_t& m, const sa_fwd_args_t& a, bool for_bwd = fa
     w.qrot = take((int64_t)a.batch * a.h_q * m.n_q * row);
   if (a.rope == SA_ROPE_HALF) w.krot = take((int64_t)a.batch * a.h_kv * m.n_k * row);
   if (m.kind == SA_MASK_SEPLLM && m.sep != nullptr) {
-    w.sep_rows = sa::align_up(m.n_k, sa::BK);
+    w.sep_rows = sa::align_up(sa::plan_layout(m).cap_sep, sa::BK);
     w.ksep = take((int64_t)a.batch * a.h_kv * w.sep_rows * row);
     w.vsep = take((int64_t)a.batch * a.h_kv * w.sep_rows * row);
   }
@@ -227,6 +228,25 @@ int sparse_attn_plan(const sa_mask_t* m, void* plan, size_t plan_bytes, hipStrea
   if ((r = check_device()) != SA_OK) return r;
   hipError_t e = sa::launch_plan(*m, lay, plan, stream);
   if (e != hipSuccess) return fail(SA_EHIP, "plan launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int sa_plan_status(const void* plan, size_t plan_bytes, hipStream_t stream, sa_plan_header_t* out) {
+  if (plan == nullptr) return fail(SA_EINVAL, "plan is NULL");
+  if (plan_bytes < sizeof(sa_plan_header_t)) return fail(SA_EINVAL, "plan buffer too small for a header");
+  int r;
+  if ((r = check_device()) != SA_OK) return r;
+  hipError_t e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(SA_EHIP, "hipStreamSynchronize: %s", hipGetErrorString(e));
+  sa_plan_header_t h;
+  e = hipMemcpy(&h, plan, sizeof(h), hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(SA_EHIP, "hipMemcpy of the plan header: %s", hipGetErrorString(e));
+  if (h.magic != 0x31504153u || h.version != 1 || h.total_bytes > (int64_t)plan_bytes)
+    return fail(SA_EINVAL, "the buffer does not hold a complete plan");
+  if (out != nullptr) *out = h;
+  if (h.n_sep > h.cap_sep)
+    return fail(SA_ENOSPACE, "the mask has %d separators at j >= %d, the plan lists at most %d (sep_max)", h.n_sep,
+                h.g0, h.cap_sep);
   return ok();
 }
 

@@ -432,7 +432,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p) {
   else if (gi < n_sep_pairs + n_cap_pairs) { kind = G_CAP; pi = gi - n_sep_pairs; }
   else { kind = G_DENSE; pi = gi - n_sep_pairs - n_cap_pairs; }
 
-  const int n_sep_all = kind == G_SEP ? ld_uniform(p.n_sep) : 0;
+  // (clamped to the gathered rows: a mask past the plan's sep_max bound)
+  const int n_sep_all = kind == G_SEP ? min(ld_uniform(p.n_sep), (int)p.sep_rows) : 0;
   if (kind == G_SEP && pi * 2 * BK >= n_sep_all) return;
   KeyUnit U0, U1;
 #pragma unroll
@@ -780,8 +781,8 @@ __global__ __launch_bounds__(256) void bwd_finish(FinishArgs p) {
   if (p.sep != nullptr && i >= p.g0) {
     const int blk = i / BK, r = i - blk * BK;
     const unsigned long long word = p.sep_bits[blk];
-    if ((word >> r) & 1ull) {
-      const int64_t rank = p.blk_sep[blk] + __popcll(word & ((r == 0) ? 0ull : (~0ull >> (64 - r))));
+    const int64_t rank = p.blk_sep[blk] + __popcll(word & ((r == 0) ? 0ull : (~0ull >> (64 - r))));
+    if (((word >> r) & 1ull) && rank < p.sep_rows) {  // rows past a broken sep_max bound: none
       const float* sr = p.sep + (bh * p.sep_rows + rank) * p.d;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {

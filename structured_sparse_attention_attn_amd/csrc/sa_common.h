@@ -41,7 +41,8 @@ inline sa_plan_header_t plan_layout(const sa_mask_t& m) {
   if (per_tile > h.n_blocks) per_tile = h.n_blocks;
   h.max_items_per_tile = (int32_t)per_tile;
   h.cap_items = (int32_t)(per_tile * h.n_tiles);
-  h.cap_sep = (m.kind == SA_MASK_SEPLLM) ? m.n_k : 0;
+  h.cap_sep = 0;
+  if (m.kind == SA_MASK_SEPLLM) h.cap_sep = (m.sep_max > 0 && m.sep_max < m.n_k) ? m.sep_max : m.n_k;
   int64_t off = 256;  // header
   h.off_tile_ptr = off;  off = align_up(off + 4 * (int64_t)(h.n_tiles + 1), 256);
   h.off_items = off;     off = align_up(off + 4 * (int64_t)h.cap_items, 256);

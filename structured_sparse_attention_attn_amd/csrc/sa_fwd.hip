@@ -46,6 +46,8 @@ struct FwdArgs {
   const int* items;
   const int* sep_count;
   const unsigned long long* sep_bits;
+  const int* n_sep;   // the plan header's separator count (j >= g0)
+  int cap_sep;        // separators the plan lists at most
   int kind, B, h_q, h_kv, n_q, n_k, n_tiles, group;
   int a, w, n_s, L, P, n_cap;
   int use_cap, gather;
@@ -58,6 +60,13 @@ struct FwdArgs {
   float q_scale;
   double th1, th8, th16;  // base^(-2/d) and its 8th and 16th powers: theta_{c+1} = theta_c * th1
 };
+
+// A plan whose mask held more separators than its sep_idx section lists:
+// every count it hands out is clamped, so the kernels stay in bounds, and the
+// outputs are poisoned (NaN) instead of silently missing keys.
+__device__ inline bool plan_overflowed(const FwdArgs& p) {
+  return p.gather && ld_uniform(p.n_sep) > p.cap_sep;
+}
 
 // Iterate the units of tile t in order; F(unit, use_raw_q) is called for each.
 // row_bytes: bytes of one row of the compact arrays (d * element size).
@@ -539,7 +548,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   // --- epilogue ---
   const float l_tot = swap_halves_sum(l_run);
   if (qok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const bool bad = plan_overflowed(p);
+    const float inv = bad ? __builtin_nanf("") : (l_tot > 0.f ? 1.f / l_tot : 0.f);
     char* orow = static_cast<char*>(p.o) + (b * p.osB + hq * p.osH + (int64_t)qi * p.osT) * 2;
 #pragma unroll
     for (int dm = 0; dm < 4; ++dm) {
@@ -557,7 +567,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       }
     }
     if (p.lse != nullptr && hl == 0)
-      p.lse[((int64_t)b * p.h_q + hq) * p.n_q + qi] = (m_ref + __log2f(l_tot)) * LN2;
+      p.lse[((int64_t)b * p.h_q + hq) * p.n_q + qi] = bad ? __builtin_nanf("") : (m_ref + __log2f(l_tot)) * LN2;
   }
 }
 
@@ -642,13 +652,15 @@ __global__ __launch_bounds__(128) void fwd_f32(FwdArgs p) {
   for_each_unit(p, b, kvh, t, 4, (int64_t)D * 4, unit);
 
   if (qok) {
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const bool bad = plan_overflowed(p);
+    const float inv = bad ? __builtin_nanf("") : (l_run > 0.f ? 1.f / l_run : 0.f);
     float* orow = static_cast<float*>(p.o) + (b * p.osB + hq * p.osH + (int64_t)qi * p.osT);
 #pragma unroll
     for (int c = 0; c < D; c += 4)
       *reinterpret_cast<float4*>(orow + c) =
           make_float4(acc[c] * inv, acc[c + 1] * inv, acc[c + 2] * inv, acc[c + 3] * inv);
-    if (p.lse != nullptr) p.lse[((int64_t)b * p.h_q + hq) * p.n_q + qi] = (m_run + log2f(l_run)) * LN2;
+    if (p.lse != nullptr)
+      p.lse[((int64_t)b * p.h_q + hq) * p.n_q + qi] = bad ? __builtin_nanf("") : (m_run + log2f(l_run)) * LN2;
   }
 }
 
@@ -690,6 +702,8 @@ hipError_t launch_fwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   p.items = reinterpret_cast<const int*>(pb + lay.off_items);
   p.sep_count = reinterpret_cast<const int*>(pb + lay.off_sep_count);
   p.sep_bits = reinterpret_cast<const unsigned long long*>(pb + lay.off_sep_bits);
+  p.n_sep = reinterpret_cast<const int*>(pb + offsetof(sa_plan_header_t, n_sep));
+  p.cap_sep = lay.cap_sep;
   p.kind = m.kind;
   p.B = a.batch;
   p.h_q = a.h_q;

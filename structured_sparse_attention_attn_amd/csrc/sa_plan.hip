@@ -170,7 +170,7 @@ __global__ __launch_bounds__(FIN_THREADS) void plan_finish(PlanArgs p) {
       int sc = 0;
       if (p.kind == SA_MASK_SEPLLM) {
         const int gh = r.hi0 * BK;  // first key of the first window block
-        if (gh > p.g0) sc = p.blk_sep[r.hi0];
+        if (gh > p.g0) sc = min(p.blk_sep[r.hi0], p.lay.cap_sep);  // a broken sep_max bound: clamped
       }
       p.sep_count[t] = sc;
     }
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void plan_lists(PlanArgs p, int n_item_wg) {
   const unsigned long long word = p.sep_bits[blk];
   if ((word >> lane) & 1ull) {
     const int rank = p.blk_sep[blk] + __popcll(word & low_bits(lane));
-    p.sep_idx[rank] = blk * BK + lane;
+    if (rank < p.lay.cap_sep) p.sep_idx[rank] = blk * BK + lane;
   }
 }
 

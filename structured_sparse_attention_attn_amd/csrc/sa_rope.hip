@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void rope_qk(RopeArgs p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) { y1[e] = x1[e]; y2[e] = x2[e]; }
       }
-      if (is_sep) {
+      if (is_sep && rank < p.sep_rows) {  // rows past a broken sep_max bound are dropped
         const int64_t srow = ((int64_t)b * p.h_kv + h) * p.sep_rows + rank;
         char* kd = static_cast<char*>(p.ksep) + srow * p.d * esz;
         Row8<T> o1, o2;

@@ -12,7 +12,7 @@ import torch
 from . import (SA_MASK_LAMBDA, SA_MASK_SEGMENT, SA_MASK_SEPLLM, bwd_args, fwd_args, mask,
                sa_bwd_workspace_bytes, sa_decode_workspace_bytes, sa_fwd_workspace_bytes,
                sa_plan_bytes, sa_stream_layout, sa_stream_state_bytes, sa_topk_workspace_bytes,
-               sparse_attn_bwd, sparse_attn_decode_step, sparse_attn_fwd, sparse_attn_plan,
+               sa_plan_status, sparse_attn_bwd, sparse_attn_decode_step, sparse_attn_fwd, sparse_attn_plan,
                sparse_attn_segment_carry, sparse_attn_stream_reset, sparse_attn_topk_middle, stream_cfg,
                topk_retrieve)
 
@@ -24,17 +24,20 @@ class SparseAttention:
 
     def __init__(self, kind: str, n_q: int, n_k: int, *, a: int = 0, w: int = 1, sep=None,
                  n_starting: int = 0, L_pretrain: int = 0, prefix_len: int = 0,
-                 device: str = "cuda"):
+                 sep_max: int = 0, device: str = "cuda"):
         self.sep = sep  # keeps the device flags alive while the mask points at them
         self.mask = mask(KINDS[kind], n_q, n_k, a=a, w=w, sep=sep, n_starting=n_starting,
-                         L_pretrain=L_pretrain, prefix_len=prefix_len)
+                         L_pretrain=L_pretrain, prefix_len=prefix_len, sep_max=sep_max)
         self.plan = torch.empty(sa_plan_bytes(self.mask), dtype=torch.uint8, device=device)
         self.ws: Optional[torch.Tensor] = None
         self.bws: Optional[torch.Tensor] = None
         self.device = device
 
-    def build_plan(self) -> None:
+    def build_plan(self, check: bool = False) -> None:
+        """Enqueue the plan; with `check`, wait for it and raise if the mask broke sep_max."""
         sparse_attn_plan(self.mask, self.plan)
+        if check:
+            sa_plan_status(self.plan)
 
     def args(self, q, k, v, o, lse=None, rope_base=None, scale=None, alibi_exp=None):
         return fwd_args(q, k, v, o, lse=lse, rope_base=rope_base, scale=scale,

@@ -13,10 +13,10 @@ def spec_of(wl, sep_np=None):
                       P=wl.P)
 
 
-def device_mask(wl, sep=None):
+def device_mask(wl, sep=None, sep_max=0):
     from structured_sparse_attention_attn_amd.pipeline import SparseAttention
     return SparseAttention(wl.mode, wl.n_q, wl.n_k, a=wl.a, w=wl.w, sep=sep, n_starting=wl.n_s,
-                           L_pretrain=wl.L, prefix_len=wl.P)
+                           L_pretrain=wl.L, prefix_len=wl.P, sep_max=sep_max)
 
 
 def sample_rows(n_q, n_random, seed):

@@ -88,6 +88,7 @@ def test_plan_layout_and_validation():
         sa.mask(sa.SA_MASK_SEGMENT, 100, 150, prefix_len=49),
         sa.mask(7, 100, 100),
         sa.mask(sa.SA_MASK_LAMBDA, 0, 0),
+        sa.mask(sa.SA_MASK_SEPLLM, 100, 100, a=4, w=3, sep_max=-1),
     ]
     for b in bad:
         with pytest.raises(sa.SparseAttnError) as e:
@@ -98,6 +99,37 @@ def test_plan_layout_and_validation():
     assert lib.sparse_attn_plan(ctypes.byref(m), None, 1 << 30, None) == sa.SA_EINVAL
     assert lib.sparse_attn_plan(ctypes.byref(m), 256, 1024, None) == sa.SA_ENOSPACE
     assert "too small" in sa.sa_last_error()
+    # plan status: NULL or header-less buffers are refused before any device call
+    assert lib.sa_plan_status(None, 1 << 20, None, None) == sa.SA_EINVAL
+    assert lib.sa_plan_status(256, 16, None, None) == sa.SA_EINVAL
+
+
+def test_sep_max_bounds_plan_and_workspace():
+    """A caller bound on the separators sizes the plan's sep_idx section and the gathered
+    separator rows of the forward and backward workspaces instead of n_k."""
+    n = 131072
+    sep = 1 << 20  # any non-NULL device address: layouts never dereference it
+    free = sa.mask(sa.SA_MASK_SEPLLM, n, n, a=4, w=1024)
+    free.sep = sep
+    lay0 = sa.sa_plan_layout(free)
+    assert lay0.cap_sep == n
+    args = _args()
+    w0 = sa.sa_fwd_workspace_layout(free, args)
+    assert w0.sep_rows == n
+    for bound, rows in ((8000, 8000), (8001, 8064), (1, 64), (n + 5, n)):
+        m = sa.mask(sa.SA_MASK_SEPLLM, n, n, a=4, w=1024, sep_max=bound)
+        m.sep = sep
+        lay = sa.sa_plan_layout(m)
+        assert lay.cap_sep == min(bound, n)
+        assert lay.total_bytes < lay0.total_bytes or bound >= n
+        w = sa.sa_fwd_workspace_layout(m, args)
+        assert w.sep_rows == rows
+        assert w.vsep - w.ksep == w.sep_rows * 128 * 2 * args.h_kv
+        assert (w.total < w0.total) == (bound < n)
+        assert sa.sa_bwd_workspace_bytes(m, args) <= sa.sa_bwd_workspace_bytes(free, args)
+    # other kinds ignore the field
+    lam = sa.mask(sa.SA_MASK_LAMBDA, n, n, n_starting=10, L_pretrain=4096, sep_max=-3)
+    assert sa.sa_plan_layout(lam).cap_sep == 0
 
 
 def _args(**kw):

@@ -647,6 +647,54 @@ def test_bwd_strided(sa, case):
             bwd_compare(f"b{b} {name}", to64(got), ref)
 
 
+def test_sep_max_bound(sa):
+    """A caller bound on the separator count (sep_max): with the exact count the plan, the
+    forward and the backward are bit-identical to the unbounded ones (and the forward matches
+    the oracle); one below it, sa_plan_status reports SA_ENOSPACE, every kernel stays inside
+    its buffers (guard bytes after the exactly sized workspace), and O, the LSE and dQ come
+    out NaN instead of silently missing keys."""
+    wl = W.small(W.SEPLLM, seed=777, m=1000, a=4, w=64, p_sep=0.2, h_q=4, h_kv=2)
+    inp = W.make_small_inputs(wl)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    sep = inp["sep"]
+    g0 = 64 * math.ceil(wl.a / 64)
+    n_sep = int(sep[g0:].sum())
+    log(f"sep_max bound: {n_sep} separators at j >= {g0}")
+    assert n_sep > 100
+    dout = W.make_grad(tuple(q.shape), seed=778).cuda()
+    runs = {}
+    for name, bound in (("free", 0), ("exact", n_sep), ("short", n_sep - 5)):
+        sa_obj = device_mask(wl, sep.cuda(), sep_max=bound)
+        sa_obj.build_plan()
+        if name == "short":
+            with pytest.raises(sa.SparseAttnError) as e:
+                sa.sa_plan_status(sa_obj.plan)
+            assert e.value.code == sa.SA_ENOSPACE
+        else:
+            hdr = sa.sa_plan_status(sa_obj.plan)
+            assert hdr.n_sep == n_sep and hdr.cap_sep == (n_sep if bound else wl.n_k)
+        args0 = sa_obj.args(q, k, v, torch.empty_like(q))
+        need = sa.sa_fwd_workspace_bytes(sa_obj.mask, args0)
+        guard = 1 << 16
+        store = torch.full((need + guard,), 0xA5, dtype=torch.uint8, device="cuda")
+        sa_obj.ws = store[:need]
+        lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
+        o = sa_obj.forward(q, k, v, lse=lse, rope_base=wl.rope_base, scale=wl.scale)
+        grads = sa_obj.backward(q, k, v, o, lse, dout, rope_base=wl.rope_base, scale=wl.scale)
+        torch.cuda.synchronize()
+        assert torch.all(store[need:] == 0xA5), f"{name}: workspace guard overwritten"
+        runs[name] = (o, lse) + tuple(grads)
+    for a_, b_ in zip(runs["free"], runs["exact"]):
+        assert torch.equal(a_, b_)
+    o, lse = runs["exact"][:2]
+    spec = spec_of(wl, sep.numpy())
+    ref_o, ref_l = O.attention(to64(inp["q"][0]), to64(inp["k"][0]), to64(inp["v"][0]), spec,
+                               wl.rope_base, wl.scale)
+    compare(to64(o[0]), ref_o, to64(lse[0]), ref_l, wl.dtype)
+    o, lse, dq = runs["short"][:3]
+    assert torch.isnan(o).all() and torch.isnan(lse).all() and torch.isnan(dq).all()
+
+
 def _workload_bwd_parity(sa, cid, dq_heads, n_random, key_block, dk_kv_head, expect_sep=False):
     """Backward at a workload's full size: dQ on sampled rows of some heads; dK, dV on one
     key block of one kv head, from every query row that sees a key of that block (the
