@@ -265,7 +265,9 @@ int sa_bwd_workspace_bytes(const sa_mask_t *m, const sa_fwd_args_t *args, size_t
  * a key-major dK/dV kernel (one work group per 64-key group: dense block,
  * gathered separator chunk or capped block; every sum in a fixed order, no
  * atomics) and a per-row finishing kernel (inverse rotations, separator and
- * capped contributions).  bf16 with d = 128 only (else SA_EUNSUPPORTED).
+ * capped contributions).  bf16 with d = 128 (MFMA kernels), or f32 with
+ * d = 64 or 128 (vector-ALU kernels, every product and sum in fp32; same
+ * sections, same order of the key-major sums); else SA_EUNSUPPORTED.
  * ws: ws_bytes >= sa_bwd_workspace_bytes; scratch.  Errors: SA_EINVAL,
  * SA_EUNSUPPORTED, SA_ENOSPACE, SA_EHIP.
  */

@@ -354,15 +354,16 @@ int sparse_attn_bwd(const sa_mask_t* m, const void* plan, size_t plan_bytes, con
   int r = check_mask(m);
   if (r != SA_OK) return r;
   if ((r = check_args(m, a)) != SA_OK) return r;
-  if (a->dtype != SA_BF16 || a->d != 128)
-    return fail(SA_EUNSUPPORTED, "the backward supports bf16 with d = 128");
+  if (a->dtype == SA_BF16 && a->d != 128)
+    return fail(SA_EUNSUPPORTED, "the bf16 backward supports d = 128");
   if (a->lse == nullptr) return fail(SA_EINVAL, "the backward needs the forward's lse");
   if (!aligned16(a->lse)) return fail(SA_EINVAL, "lse must be 16-byte aligned");
   if (g == nullptr) return fail(SA_EINVAL, "grads is NULL");
-  if ((r = check_tensor("dout", g->dout, g->dout_stride, 2)) != SA_OK) return r;
-  if ((r = check_tensor("dq", g->dq, g->dq_stride, 2)) != SA_OK) return r;
-  if ((r = check_tensor("dk", g->dk, g->dk_stride, 2)) != SA_OK) return r;
-  if ((r = check_tensor("dv", g->dv, g->dv_stride, 2)) != SA_OK) return r;
+  const int esz = a->dtype == SA_BF16 ? 2 : 4;
+  if ((r = check_tensor("dout", g->dout, g->dout_stride, esz)) != SA_OK) return r;
+  if ((r = check_tensor("dq", g->dq, g->dq_stride, esz)) != SA_OK) return r;
+  if ((r = check_tensor("dk", g->dk, g->dk_stride, esz)) != SA_OK) return r;
+  if ((r = check_tensor("dv", g->dv, g->dv_stride, esz)) != SA_OK) return r;
   if (plan == nullptr) return fail(SA_EINVAL, "plan is NULL");
   const sa_plan_header_t lay = sa::plan_layout(*m);
   if (plan_bytes < (size_t)lay.total_bytes)

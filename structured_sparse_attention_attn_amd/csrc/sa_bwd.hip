@@ -27,6 +27,10 @@
 //                  loads in flight while the current one computes: S = Q K^T,
 //                  P, dP = dO V^T, dS, then dV^T += dO^T P and
 //                  dK^T += Q^T dS (transpose reads of the query-side tiles).
+//   bwd_dq_f32, bwd_dkdv_f32
+//                  fp32: the same two sums on the vector ALU (query-major
+//                  per tile; key-major per 64-key unit), a thread per
+//                  32-element slice of a row.
 //   bwd_finish     per row: the inverse rotations, the separator and capped
 //                  contributions, the output dtype.
 #include <type_traits>
@@ -78,8 +82,9 @@ struct BwdArgs {
 };
 
 // ---------------------------------------------------------------------------
-// D_i = <dO_i, O_i>: 16 consecutive lanes per row, one 16-byte piece each,
-// then a butterfly sum over the 16 lanes.
+// D_i = <dO_i, O_i>: d * esz / 16 consecutive lanes per row (16 for bf16
+// d = 128, 32 for fp32), one 16-byte piece each, then a butterfly sum over
+// those lanes.
 // ---------------------------------------------------------------------------
 
 struct RowDotArgs {
@@ -95,7 +100,7 @@ __device__ inline float bf_lo(unsigned x) { return __uint_as_float(x << 16); }
 __device__ inline float bf_hi(unsigned x) { return __uint_as_float(x & 0xffff0000u); }
 
 __global__ __launch_bounds__(256) void bwd_rowdot(RowDotArgs p) {
-  const int pieces = p.d * p.esz / 16;  // 16 for bf16 d = 128
+  const int pieces = p.d * p.esz / 16;  // 16 for bf16 d = 128, 32 for fp32
   const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t row = g / pieces;
   const int pc = (int)(g % pieces);
@@ -108,13 +113,18 @@ __global__ __launch_bounds__(256) void bwd_rowdot(RowDotArgs p) {
     const uint4 x = *reinterpret_cast<const uint4*>(p.dout + (b * p.dsB + h * p.dsH + (int64_t)i * p.dsT) * p.esz + pc * 16);
     const uint4 y = *reinterpret_cast<const uint4*>(p.o + (b * p.osB + h * p.osH + (int64_t)i * p.osT) * p.esz + pc * 16);
     const unsigned xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+    if (p.esz == 2) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(bf_lo(xs[e]), bf_lo(ys[e]), acc);
-      acc = fmaf(bf_hi(xs[e]), bf_hi(ys[e]), acc);
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf(bf_lo(xs[e]), bf_lo(ys[e]), acc);
+        acc = fmaf(bf_hi(xs[e]), bf_hi(ys[e]), acc);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = fmaf(__uint_as_float(xs[e]), __uint_as_float(ys[e]), acc);
     }
   }
-  for (int m = 1; m < pieces; m <<= 1) acc += __shfl_xor(acc, m, 16);
+  for (int m = 1; m < pieces; m <<= 1) acc += __shfl_xor(acc, m, pieces);  // a row's pieces: aligned lanes
   if (row < rows && pc == 0) p.D[row] = acc;
 }
 
@@ -718,6 +728,299 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p) {
 }
 
 // ===========================================================================
+// fp32 (no bf16 rounding anywhere): every product and sum in fp32, on the
+// vector ALU.  The same sums as above, the same accumulator sections and the
+// same finishing kernel (dk_acc holds sum dS q~ unscaled here, the finish
+// multiplies by scale instead of ln 2).  A thread owns a 32-element slice of
+// its row; a dot product is the slice's fma chain plus a butterfly over the
+// row's D/32 lanes (adjacent lanes, so every lane gets the same sum).
+// ===========================================================================
+
+constexpr int F32_SLICE = 32;
+
+template <int TPR>
+__device__ inline float row_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < TPR; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// Loads a 32-element fp32 slice (zeros when !ok).
+__device__ inline void load_slice(const float* src, bool ok, float (&x)[F32_SLICE]) {
+#pragma unroll
+  for (int c = 0; c < F32_SLICE; c += 4) {
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (ok) v = *reinterpret_cast<const float4*>(src + c);
+    x[c] = v.x; x[c + 1] = v.y; x[c + 2] = v.z; x[c + 3] = v.w;
+  }
+}
+
+// dQ: one work group per (batch, query head, 128-query tile), the forward's
+// units in the forward's order; thread = (query, slice).
+//   dq_acc_i = scale sum dS_ij k~_j        dq_cap_i = scale sum dS_ij R(-L) k_j
+template <int D>
+__global__ __launch_bounds__(TQ * D / F32_SLICE) void bwd_dq_f32(BwdArgs p) {
+  constexpr int TPR = D / F32_SLICE, NT = TQ * TPR;
+  __shared__ __attribute__((aligned(16))) float Ks[BK][D];
+  __shared__ __attribute__((aligned(16))) float Vs[BK][D];
+  const int tid = threadIdx.x;
+  const int c0 = (tid % TPR) * F32_SLICE;
+  int b, kvh, t, hq;
+  map_unit(p, b, kvh, t, hq);
+  const int qi = t * TQ + tid / TPR;
+  const bool qok = qi < p.n_q;
+  const int64_t row = ((int64_t)b * p.h_q + hq) * p.n_q + (qok ? qi : 0);
+  float q[F32_SLICE], g[F32_SLICE], dq[F32_SLICE], dqc[F32_SLICE];
+  load_slice(static_cast<const float*>(p.dout) + b * p.dsB + hq * p.dsH + (int64_t)qi * p.dsT + c0, qok, g);
+  auto load_q = [&](bool raw) {
+    const float* src = raw ? static_cast<const float*>(p.qraw) + b * p.qrB + hq * p.qrH + (int64_t)qi * p.qrT
+                           : static_cast<const float*>(p.q) + b * p.qsB + hq * p.qsH + (int64_t)qi * p.qsT;
+    load_slice(src + c0, qok, q);
+  };
+  load_q(false);
+  bool q_is_raw = false;
+#pragma unroll
+  for (int c = 0; c < F32_SLICE; ++c) { dq[c] = 0.f; dqc[c] = 0.f; }
+  const float lse2 = qok ? p.lse[row] * LOG2E : 0.f;
+  const float Di = qok ? p.Dv[row] : 0.f;
+  const float sl2 = p.scale * LOG2E;
+  const float m2 = p.alibi ? alibi_slope_log2(p, hq) : 0.f;
+  const float Lf = (float)p.L;
+
+  auto unit = [&](const Unit& u, bool raw_q) {
+    if (raw_q != q_is_raw) {
+      load_q(raw_q);
+      q_is_raw = raw_q;
+    }
+    constexpr int CH = D / 4;
+    for (int x = tid; x < BK * CH; x += NT) {
+      const int r = x / CH, ch = x % CH;
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      if (r < u.kvalid) kv = *reinterpret_cast<const float4*>(u.kbase + r * u.kstride + ch * 16);
+      if (r < u.vvalid) vv = *reinterpret_cast<const float4*>(u.vbase + r * u.vstride + ch * 16);
+      *reinterpret_cast<float4*>(&Ks[r][ch * 4]) = kv;
+      *reinterpret_cast<float4*>(&Vs[r][ch * 4]) = vv;
+    }
+    __syncthreads();
+    for (int r = 0; r < BK; ++r) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int c = 0; c < F32_SLICE; ++c) {
+        s = fmaf(q[c], Ks[r][c0 + c], s);
+        dp = fmaf(g[c], Vs[r][c0 + c], dp);
+      }
+      s = row_sum<TPR>(s);
+      dp = row_sum<TPR>(dp);
+      float x = s * sl2;
+      if (p.alibi) x = fmaf(-m2, fminf((float)(qi - u.key0 - r), Lf), x);
+      const bool vis = qok && r < u.kvalid && (u.mk == MK_NONE || visible(p, u, qi, r));
+      const float pr = vis ? exp2f(x - lse2) : 0.f;
+      const float ds = pr * (dp - Di);
+      if (raw_q) {
+#pragma unroll
+        for (int c = 0; c < F32_SLICE; ++c) dqc[c] = fmaf(ds, Ks[r][c0 + c], dqc[c]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < F32_SLICE; ++c) dq[c] = fmaf(ds, Ks[r][c0 + c], dq[c]);
+      }
+    }
+    __syncthreads();
+  };
+  for_each_unit(p, b, kvh, t, 4, (int64_t)D * 4, unit);
+  if (qok) {
+    float* o = p.dq_acc + row * D + c0;
+#pragma unroll
+    for (int c = 0; c < F32_SLICE; c += 4)
+      *reinterpret_cast<float4*>(o + c) =
+          make_float4(dq[c] * p.scale, dq[c + 1] * p.scale, dq[c + 2] * p.scale, dq[c + 3] * p.scale);
+    if (p.use_cap) {
+      float* oc = p.dq_cap + row * D + c0;
+#pragma unroll
+      for (int c = 0; c < F32_SLICE; c += 4)
+        *reinterpret_cast<float4*>(oc + c) =
+            make_float4(dqc[c] * p.scale, dqc[c + 1] * p.scale, dqc[c + 2] * p.scale, dqc[c + 3] * p.scale);
+    }
+  }
+}
+
+// dK, dV: key-major, one work group per (batch, kv head, 64-key unit: a
+// gathered separator chunk, a capped block or a dense block); thread =
+// (key, slice).  It walks the tiles that read the unit in order, every query
+// head of the group, 32 queries at a time staged in LDS:
+//   dk_j += dS_ij q_i (q~, or the raw q for capped pairs)   dv_j += P_ij dO_i
+template <int D>
+__global__ __launch_bounds__(BK * D / F32_SLICE) void bwd_dkdv_f32(BwdArgs p) {
+  constexpr int TPR = D / F32_SLICE, NT = BK * TPR, QC = 32;
+  __shared__ __attribute__((aligned(16))) float Qs[QC][D];
+  __shared__ __attribute__((aligned(16))) float Gs[QC][D];
+  __shared__ float Ls[QC], Ds[QC];
+  const int tid = threadIdx.x;
+  const int kk = tid / TPR, c0 = (tid % TPR) * F32_SLICE;
+  const int BH = p.B * p.h_kv;
+  const int bh = blockIdx.x % BH;
+  const int gi = blockIdx.x / BH;
+  const int b = bh / p.h_kv, kvh = bh % p.h_kv;
+  int kind, idx;
+  if (gi < p.n_sep_chunks) { kind = G_SEP; idx = gi; }
+  else if (gi < p.n_sep_chunks + p.n_cap_blocks) { kind = G_CAP; idx = gi - p.n_sep_chunks; }
+  else { kind = G_DENSE; idx = gi - p.n_sep_chunks - p.n_cap_blocks; }
+  // (clamped to the gathered rows: a mask past the plan's sep_max bound)
+  const int n_sep_all = kind == G_SEP ? min(ld_uniform(p.n_sep), (int)p.sep_rows) : 0;
+  if (kind == G_SEP && idx * BK >= n_sep_all) return;
+
+  const int64_t rowb = (int64_t)D * 4;
+  const char* kbase;
+  const char* vbase;
+  int64_t kstr, vstr;
+  int valid, key0 = idx * BK;
+  float *dk_out, *dv_out;
+  if (kind == G_SEP) {
+    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.sep_rows + (int64_t)idx * BK;
+    kbase = static_cast<const char*>(p.ksep) + ho * rowb;
+    vbase = static_cast<const char*>(p.vsep) + ho * rowb;
+    kstr = vstr = rowb;
+    valid = min(BK, n_sep_all - idx * BK);
+    dk_out = p.dksep + ho * D;
+    dv_out = p.dvsep + ho * D;
+    key0 = 0;
+  } else if (kind == G_CAP) {
+    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.cap_rows + (int64_t)idx * BK;
+    kbase = static_cast<const char*>(p.kcap) + ho * rowb;
+    kstr = rowb;
+    vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)key0 * p.vsT) * 4;
+    vstr = p.vsT * 4;
+    valid = min(BK, p.n_cap - key0);
+    dk_out = p.dkcap + ho * D;
+    dv_out = p.dvcap + ho * D;
+  } else {
+    kbase = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH + (int64_t)key0 * p.ksT) * 4;
+    vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)key0 * p.vsT) * 4;
+    kstr = p.ksT * 4;
+    vstr = p.vsT * 4;
+    valid = min(BK, p.n_k - key0);
+    const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.n_k + key0;
+    dk_out = p.dk_acc + ho * D;
+    dv_out = p.dv_acc + ho * D;
+  }
+  const bool kok = kk < valid;
+  float kx[F32_SLICE], vx[F32_SLICE], dk[F32_SLICE], dv[F32_SLICE];
+  load_slice(reinterpret_cast<const float*>(kbase + kk * kstr) + c0, kok, kx);
+  load_slice(reinterpret_cast<const float*>(vbase + kk * vstr) + c0, kok, vx);
+#pragma unroll
+  for (int c = 0; c < F32_SLICE; ++c) { dk[c] = 0.f; dv[c] = 0.f; }
+  const int j = key0 + kk;
+  const bool q_raw = kind == G_CAP;
+  const float* qsrc = static_cast<const float*>(q_raw ? p.qraw : p.q);
+  const int64_t qB = q_raw ? p.qrB : p.qsB, qH = q_raw ? p.qrH : p.qsH, qT = q_raw ? p.qrT : p.qsT;
+  const float sl2 = p.scale * LOG2E;
+  const float Lf = (float)p.L;
+
+  // the unit as one tile reads it (mk < 0: not read)
+  auto unit_of = [&](int t) -> Unit {
+    Unit u;
+    u.key0 = key0;
+    u.count = 0;
+    u.sbits = 0;
+    u.mk = -1;
+    if (kind == G_SEP) {
+      u.count = ld_uniform(p.sep_count + t) - idx * BK;
+      if (u.count > 0) u.mk = MK_COUNT;
+      return u;
+    }
+    const int it = find_item(p, t, idx);
+    if (it < 0) return u;
+    const int fl = it >> 24;
+    if (kind == G_CAP) {
+      if (fl & SA_ITEM_CAPPED) u.mk = MK_LCAP;
+    } else if (p.use_cap && (fl & SA_ITEM_CAPPED)) {
+      u.mk = MK_LNORM;
+    } else if (fl & SA_ITEM_FULL) {
+      u.mk = MK_NONE;
+    } else if (p.kind == SA_MASK_SEPLLM) {
+      u.mk = MK_SEPLLM;
+      u.sbits = ld_uniform(p.sep_bits + idx);
+    } else if (p.kind == SA_MASK_LAMBDA) {
+      u.mk = MK_LALL;
+    } else {
+      u.mk = MK_SEG;
+    }
+    return u;
+  };
+  // Tiles reading the unit: separator chunk c from the first tile gathering
+  // more than 64 c rows to the last (the counts never decrease); a dense
+  // block from the tile holding its first key while the tiles list it
+  // (consecutive); a capped block: every tile, each checked.
+  int t = 0;
+  if (kind == G_SEP) t = first_gathering_tile(p, idx * BK);
+  else if (kind == G_DENSE) t = max(0, key0 - (p.kind == SA_MASK_SEGMENT ? p.P : 0)) / TQ;
+  for (; t < p.n_tiles; ++t) {
+    const Unit u = unit_of(t);
+    if (u.mk < 0) {
+      if (kind == G_DENSE) break;
+      continue;
+    }
+    for (int gq = 0; gq < p.group; ++gq) {
+      const int hq = kvh * p.group + gq;
+      const float m2 = p.alibi ? alibi_slope_log2(p, hq) : 0.f;
+      const int q_end = min(p.n_q, (t + 1) * TQ);
+      for (int qc0 = t * TQ; qc0 < q_end; qc0 += QC) {
+        constexpr int CH = D / 4;
+        for (int x = tid; x < QC * CH; x += NT) {
+          const int r = x / CH, ch = x % CH;
+          const int i = qc0 + r;
+          float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), gv = qv;
+          if (i < q_end) {
+            qv = *reinterpret_cast<const float4*>(qsrc + b * qB + hq * qH + (int64_t)i * qT + ch * 4);
+            gv = *reinterpret_cast<const float4*>(static_cast<const float*>(p.dout) + b * p.dsB + hq * p.dsH +
+                                                  (int64_t)i * p.dsT + ch * 4);
+          }
+          *reinterpret_cast<float4*>(&Qs[r][ch * 4]) = qv;
+          *reinterpret_cast<float4*>(&Gs[r][ch * 4]) = gv;
+        }
+        if (tid < QC) {
+          const int i = qc0 + tid;
+          const int64_t ri = ((int64_t)b * p.h_q + hq) * p.n_q + i;
+          Ls[tid] = i < q_end ? p.lse[ri] * LOG2E : 0.f;
+          Ds[tid] = i < q_end ? p.Dv[ri] : 0.f;
+        }
+        __syncthreads();
+        for (int r = 0; r < QC; ++r) {
+          const int i = qc0 + r;
+          float s = 0.f, dp = 0.f;
+#pragma unroll
+          for (int c = 0; c < F32_SLICE; ++c) {
+            s = fmaf(kx[c], Qs[r][c0 + c], s);
+            dp = fmaf(vx[c], Gs[r][c0 + c], dp);
+          }
+          s = row_sum<TPR>(s);
+          dp = row_sum<TPR>(dp);
+          float x = s * sl2;
+          if (p.alibi) x = fmaf(-m2, fminf((float)(i - j), Lf), x);
+          const bool vis = kok && i < q_end && (u.mk == MK_NONE || visible(p, u, i, kk));
+          const float pr = vis ? exp2f(x - Ls[r]) : 0.f;
+          const float ds = pr * (dp - Ds[r]);
+#pragma unroll
+          for (int c = 0; c < F32_SLICE; ++c) {
+            dk[c] = fmaf(ds, Qs[r][c0 + c], dk[c]);
+            dv[c] = fmaf(pr, Gs[r][c0 + c], dv[c]);
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
+  if (kok) {
+    float* ko = dk_out + (int64_t)kk * D + c0;
+    float* vo = dv_out + (int64_t)kk * D + c0;
+#pragma unroll
+    for (int c = 0; c < F32_SLICE; c += 4) {
+      *reinterpret_cast<float4*>(ko + c) = make_float4(dk[c], dk[c + 1], dk[c + 2], dk[c + 3]);
+      *reinterpret_cast<float4*>(vo + c) = make_float4(dv[c], dv[c + 1], dv[c + 2], dv[c + 3]);
+    }
+  }
+}
+
+// ===========================================================================
 // Finish: per row, the inverse rotation of the rotated-frame sums, the
 // separator and capped contributions, the output dtype.
 //   dq_i = R(-pos_q(i)) dq_acc_i + dq_cap_i
@@ -864,6 +1167,8 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   const bool rope = a.rope == SA_ROPE_HALF;
   const bool alibi = a.rope == SA_ALIBI;
   const int64_t rows_q = (int64_t)a.batch * a.h_q * m.n_q;
+  const bool f32 = a.dtype == SA_F32;
+  const int esz = f32 ? 4 : 2;
   // 1. D = rowsum(dO * O)
   {
     RowDotArgs r;
@@ -872,14 +1177,19 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
     r.o = static_cast<const char*>(a.o);
     r.osB = a.o_stride[0]; r.osH = a.o_stride[1]; r.osT = a.o_stride[2];
     r.D = w.D;
-    r.B = a.batch; r.h = a.h_q; r.n = m.n_q; r.d = a.d; r.esz = 2;
-    const int64_t threads = rows_q * (a.d * 2 / 16);
+    r.B = a.batch; r.h = a.h_q; r.n = m.n_q; r.d = a.d; r.esz = esz;
+    const int64_t threads = rows_q * (a.d * esz / 16);
     hipLaunchKernelGGL(bwd_rowdot, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s, r);
   }
   BwdArgs p;
   memset(&p, 0, sizeof(p));
-  p.q = ro.qrot;
-  p.qsT = a.d; p.qsH = (int64_t)m.n_q * a.d; p.qsB = p.qsH * a.h_q;
+  if (ro.qrot != nullptr) {  // the rotated (bf16: and pre-scaled) query copy
+    p.q = ro.qrot;
+    p.qsT = a.d; p.qsH = (int64_t)m.n_q * a.d; p.qsB = p.qsH * a.h_q;
+  } else {                   // fp32 without rotation: the caller's queries
+    p.q = a.q;
+    p.qsB = a.q_stride[0]; p.qsH = a.q_stride[1]; p.qsT = a.q_stride[2];
+  }
   p.qraw = a.q;
   p.qrB = a.q_stride[0]; p.qrH = a.q_stride[1]; p.qrT = a.q_stride[2];
   if (rope) {
@@ -918,14 +1228,26 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   p.alibi_e = alibi ? a.alibi_exp : 0.f;
   p.n_sep_chunks = p.gather ? (int)(ro.sep_rows / BK) : 0;
   p.n_cap_blocks = p.use_cap ? (int)ceil_div(ro.n_cap, BK) : 0;
+  if (f32) {
+    const unsigned gq = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
+    const int64_t units = (int64_t)p.n_sep_chunks + p.n_cap_blocks + lay.n_blocks;
+    const unsigned gk = (unsigned)(units * a.batch * a.h_kv);
+    if (a.d == 64) {
+      hipLaunchKernelGGL(bwd_dq_f32<64>, dim3(gq), dim3(TQ * 64 / F32_SLICE), 0, s, p);
+      hipLaunchKernelGGL(bwd_dkdv_f32<64>, dim3(gk), dim3(BK * 64 / F32_SLICE), 0, s, p);
+    } else {
+      hipLaunchKernelGGL(bwd_dq_f32<128>, dim3(gq), dim3(TQ * 128 / F32_SLICE), 0, s, p);
+      hipLaunchKernelGGL(bwd_dkdv_f32<128>, dim3(gk), dim3(BK * 128 / F32_SLICE), 0, s, p);
+    }
+  }
   // 2. dQ (query-major)
-  {
+  if (!f32) {
     const unsigned grid = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
     if (alibi) hipLaunchKernelGGL(bwd_dq_bf16<true>, dim3(grid), dim3(256), 0, s, p);
     else hipLaunchKernelGGL(bwd_dq_bf16<false>, dim3(grid), dim3(256), 0, s, p);
   }
   // 3. dK, dV (key-major): separator chunks, then capped blocks, then dense blocks
-  {
+  if (!f32) {
     const int64_t groups = (int64_t)(p.n_sep_chunks + 1) / 2 + (p.n_cap_blocks + 1) / 2 + (lay.n_blocks + 1) / 2;
     const unsigned grid = (unsigned)(groups * a.batch * a.h_kv);
     if (alibi) hipLaunchKernelGGL(bwd_dkdv_bf16<true>, dim3(grid), dim3(512), 0, s, p);
@@ -937,7 +1259,7 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
     memset(&f, 0, sizeof(f));
     f.which = which;
     f.d = a.d;
-    f.esz = 2;
+    f.esz = esz;
     f.L = m.L_pretrain;
     f.theta = theta;
     f.sep_bits = p.sep_bits;
@@ -969,7 +1291,8 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
       f.osB = st[0]; f.osH = st[1]; f.osT = st[2];
       f.rotate = which == 1 && rope;
       f.pos0 = 0;
-      f.acc_scale = which == 1 ? LN2 : 1.f;
+      // dk_acc: sum dS q~ pre-scaled by scale * log2(e) (bf16), unscaled (fp32)
+      f.acc_scale = which == 1 ? (f32 ? a.scale : LN2) : 1.f;
       f.cap_scale = which == 1 ? a.scale : 1.f;
     }
     const int64_t threads = (int64_t)f.B * f.h * f.n * (a.d / 16);

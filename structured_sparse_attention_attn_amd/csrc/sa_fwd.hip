@@ -68,90 +68,6 @@ __device__ inline bool plan_overflowed(const FwdArgs& p) {
   return p.gather && ld_uniform(p.n_sep) > p.cap_sep;
 }
 
-// Iterate the units of tile t in order; F(unit, use_raw_q) is called for each.
-// row_bytes: bytes of one row of the compact arrays (d * element size).
-template <class F>
-__device__ inline void for_each_unit(const FwdArgs& p, int b, int kvh, int t, int esz,
-                                     int64_t row_bytes, F&& f) {
-  const int it0 = p.tile_ptr[t], it1 = p.tile_ptr[t + 1];
-  const char* kb = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH) * esz;
-  const char* vb = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH) * esz;
-  const int64_t kst = p.ksT * esz, vst = p.vsT * esz;
-  // 1. capped pairs (LM-Infinite with RoPE): raw queries against R(-L) K
-  if (p.use_cap) {
-    const char* cb = static_cast<const char*>(p.kcap) +
-                     ((int64_t)b * p.h_kv + kvh) * p.cap_rows * row_bytes;
-    for (int it = it0; it < it1; ++it) {
-      const int item = p.items[it];
-      if (!((item >> 24) & SA_ITEM_CAPPED)) continue;
-      const int blk = item & 0xffffff;
-      Unit u;
-      u.kbase = cb + (int64_t)blk * BK * row_bytes;
-      u.kstride = row_bytes;
-      u.kvalid = min(BK, p.n_cap - blk * BK);
-      u.vbase = vb + (int64_t)blk * BK * vst;
-      u.vstride = vst;
-      u.vvalid = min(BK, p.n_k - blk * BK);
-      u.key0 = blk * BK;
-      u.mk = MK_LCAP;
-      u.count = 0;
-      u.sbits = 0;
-      f(u, true);
-    }
-  }
-  // 2. gathered separators: every row precedes the tile and lies outside all
-  //    of its windows, so only the count masks
-  if (p.gather) {
-    const int nsep = p.sep_count[t];
-    const int64_t hb = ((int64_t)b * p.h_kv + kvh) * p.sep_rows * row_bytes;
-    const char* ksb = static_cast<const char*>(p.ksep) + hb;
-    const char* vsb = static_cast<const char*>(p.vsep) + hb;
-    for (int c0 = 0; c0 < nsep; c0 += BK) {
-      Unit u;
-      u.kbase = ksb + (int64_t)c0 * row_bytes;
-      u.kstride = row_bytes;
-      u.kvalid = min(BK, nsep - c0);
-      u.vbase = vsb + (int64_t)c0 * row_bytes;
-      u.vstride = row_bytes;
-      u.vvalid = u.kvalid;
-      u.key0 = 0;
-      u.mk = u.kvalid == BK ? MK_NONE : MK_COUNT;
-      u.count = u.kvalid;
-      u.sbits = 0;
-      f(u, false);
-    }
-  }
-  // 3. the plan's blocks
-  for (int it = it0; it < it1; ++it) {
-    const int item = p.items[it];
-    const int blk = item & 0xffffff;
-    const int fl = item >> 24;
-    Unit u;
-    u.kbase = kb + (int64_t)blk * BK * kst;
-    u.kstride = kst;
-    u.kvalid = min(BK, p.n_k - blk * BK);
-    u.vbase = vb + (int64_t)blk * BK * vst;
-    u.vstride = vst;
-    u.vvalid = u.kvalid;
-    u.key0 = blk * BK;
-    u.count = 0;
-    u.sbits = 0;
-    if (p.use_cap && (fl & SA_ITEM_CAPPED)) {
-      u.mk = MK_LNORM;
-    } else if (fl & SA_ITEM_FULL) {
-      u.mk = MK_NONE;
-    } else if (p.kind == SA_MASK_SEPLLM) {
-      u.mk = MK_SEPLLM;
-      u.sbits = p.sep_bits[blk];
-    } else if (p.kind == SA_MASK_LAMBDA) {
-      u.mk = MK_LALL;
-    } else {
-      u.mk = MK_SEG;
-    }
-    f(u, false);
-  }
-}
-
 // ===========================================================================
 // bf16, d = 128: MFMA 32x32x16.  4 waves x 32 queries = one 128-query tile.
 // S^T = K Q^T (keys as rows) so every lane owns one query's logits and the

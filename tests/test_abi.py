@@ -278,7 +278,14 @@ def test_bwd_validation():
                                    None if grads is None else ctypes.byref(grads), wsp, wsb, None)
 
     assert call(args=_args()) == sa.SA_EINVAL and "lse" in sa.sa_last_error()  # no lse
-    assert call(args=_args(lse=8192, dtype=sa.SA_F32, d=64)) == sa.SA_EUNSUPPORTED
+    assert call(args=_args(lse=8192, d=64)) == sa.SA_EUNSUPPORTED  # bf16 needs d = 128
+    # fp32 gradients: 16-byte rows checked with 4-byte elements (a 4-element row stride is 16 bytes
+    # in fp32 but only 8 in bf16)
+    g4 = _grads()
+    g4.dq_stride[2] = 4
+    assert call(args=_args(lse=8192, dtype=sa.SA_F32, d=64), grads=g4, wsp=None) == sa.SA_EINVAL
+    assert "workspace" in sa.sa_last_error()
+    assert call(grads=g4) == sa.SA_EINVAL and "dq" in sa.sa_last_error()
     assert call(grads=None) == sa.SA_EINVAL
     assert call(grads=_grads(dout=None)) == sa.SA_EINVAL
     bad = _grads()

@@ -647,6 +647,72 @@ def test_bwd_strided(sa, case):
             bwd_compare(f"b{b} {name}", to64(got), ref)
 
 
+# fp32 backward: every product and sum in fp32 on both passes; the oracle in fp64.
+BWD_F32 = [
+    (W.SEPLLM, dict(m=700, a=4, w=64, p_sep=0.1, d=64), None, None),
+    (W.SEPLLM, dict(m=500, a=70, w=100, p_sep=0.2, h_q=4, h_kv=2, batch=2), 10000.0, None),
+    (W.LAMBDA, dict(m=900, n_s=10, L=300), 10000.0, None),
+    (W.LAMBDA, dict(m=600, n_s=100, L=64, h_q=4, h_kv=1, d=64), 10000.0, None),
+    (W.LAMBDA, dict(m=700, n_s=10, L=100), None, 8.0),
+    (W.SEGMENT, dict(m=129, P=1, h_q=4, h_kv=2), 10000.0, None),
+    (W.SEGMENT, dict(m=300, P=200, d=64), 10000.0, None),
+    (W.SEPLLM, dict(m=1, a=4, w=64, p_sep=0.5), 10000.0, None),
+]
+
+
+def f32_grad_compare(name, got, ref):
+    """fp32 gradient bar: max-abs <= 1e-5 * max(1, max|ref|), the fp32 forward's 1e-5 read
+    relative to the gradient's own scale (the sums hold up to a few hundred terms of
+    relative rounding 2^-24 each, and P carries the forward's LSE error of ~1e-6)."""
+    err = np.abs(got - ref)
+    rmx = float(np.abs(ref).max()) if ref.size else 0.0
+    log(f"  {name}: max-abs {err.max():.3e} | ref max {rmx:.3e}")
+    assert np.isfinite(got).all(), name
+    assert err.max() <= 1e-5 * max(1.0, rmx), (name, float(err.max()), rmx)
+
+
+def _bwd_f32_case(sa, wl, seed):
+    inp = W.make_small_inputs(wl)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    assert q.dtype == torch.float32
+    sep = inp.get("sep")
+    sa_obj = device_mask(wl, None if sep is None else sep.cuda())
+    sa_obj.build_plan()
+    lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
+    o = sa_obj.forward(q, k, v, lse=lse, rope_base=wl.rope_base, scale=wl.scale, alibi_exp=wl.alibi_exp)
+    dout = W.make_grad(tuple(q.shape), seed=seed, dtype=torch.float32).cuda()
+    dq, dk, dv = sa_obj.backward(q, k, v, o, lse, dout, rope_base=wl.rope_base, scale=wl.scale,
+                                 alibi_exp=wl.alibi_exp)
+    torch.cuda.synchronize()
+    spec = spec_of(wl, None if sep is None else sep.numpy())
+    for b in range(wl.batch):
+        rq, rk, rv = O.attention_backward(to64(inp["q"][b]), to64(inp["k"][b]), to64(inp["v"][b]),
+                                          to64(dout[b]), spec, wl.rope_base, wl.scale,
+                                          alibi_exp=wl.alibi_exp)
+        for name, got, ref in (("dq", dq[b], rq), ("dk", dk[b], rk), ("dv", dv[b], rv)):
+            f32_grad_compare(f"b{b} {name}", to64(got), ref)
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("case", range(len(BWD_F32)))
+def test_bwd_f32_small(sa, case):
+    mode, kw, rope, alibi = BWD_F32[case]
+    wl = W.small(mode, seed=600 + case, dtype="f32", rope_base=rope, alibi_exp=alibi, **kw)
+    log(f"bwd f32 {case}: {mode} {kw} rope={rope} alibi={alibi}")
+    _bwd_f32_case(sa, wl, 950 + case)
+
+
+def test_workload1_backward(sa):
+    """The tiny fp32 SepLLM configuration (2 heads, d = 64, m = 512, no RoPE): every gradient
+    row against the oracle, and a second run bit-identical (fixed summation order)."""
+    wl = W.WORKLOADS[1]
+    log("workload 1 backward")
+    first = _bwd_f32_case(sa, wl, 1001)
+    again = _bwd_f32_case(sa, wl, 1001)
+    for a_, b_ in zip(first, again):
+        assert torch.equal(a_, b_)
+
+
 def test_sep_max_bound(sa):
     """A caller bound on the separator count (sep_max): with the exact count the plan, the
     forward and the backward are bit-identical to the unbounded ones (and the forward matches
