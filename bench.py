@@ -536,7 +536,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=3, help="1..6 (default: the 32K Lambda layer)")
+    ap.add_argument("--workload", type=int, default=3, help="1..7 (default: the 32K Lambda layer)")
     ap.add_argument("--no-128k", action="store_true",
                     help="with the default workload, skip the 128K GQA SepLLM layer's sub-object")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -118,7 +118,7 @@ typedef struct {
  * dimension contiguous; *_stride give the element strides of the batch, head
  * and token dimensions.
  *   dtype       SA_F32 or SA_BF16 for q, k, v and o.
- *   d           head dimension: 128 (bf16 and f32) or 64 (f32).
+ *   d           head dimension: 64 or 128 (bf16 and f32).
  *   h_q, h_kv   h_q % h_kv == 0; query head h reads kv head h / (h_q/h_kv).
  *   rope        position encoding: SA_ROPE_NONE; SA_ROPE_HALF (rotate-half RoPE,
  *               theta_c = rope_base^(-2c/d)); or SA_ALIBI (LAMBDA masks only,
@@ -265,9 +265,10 @@ int sa_bwd_workspace_bytes(const sa_mask_t *m, const sa_fwd_args_t *args, size_t
  * a key-major dK/dV kernel (one work group per 64-key group: dense block,
  * gathered separator chunk or capped block; every sum in a fixed order, no
  * atomics) and a per-row finishing kernel (inverse rotations, separator and
- * capped contributions).  bf16 with d = 128 (MFMA kernels), or f32 with
- * d = 64 or 128 (vector-ALU kernels, every product and sum in fp32; same
- * sections, same order of the key-major sums); else SA_EUNSUPPORTED.
+ * capped contributions).  bf16 with d = 128 runs on MFMA kernels; f32 with
+ * d = 64 or 128 and bf16 with d = 64 on vector-ALU kernels (bf16 rows
+ * widened, every product and sum in fp32; same sections, same order of the
+ * key-major sums).
  * ws: ws_bytes >= sa_bwd_workspace_bytes; scratch.  Errors: SA_EINVAL,
  * SA_EUNSUPPORTED, SA_ENOSPACE, SA_EHIP.
  */

@@ -91,10 +91,7 @@ int check_tensor(const char* name, const void* p, const int64_t st[3], int esz) 
 int check_args(const sa_mask_t* m, const sa_fwd_args_t* a) {
   if (a == nullptr) return fail(SA_EINVAL, "args is NULL");
   if (a->dtype != SA_F32 && a->dtype != SA_BF16) return fail(SA_EINVAL, "unknown dtype %d", a->dtype);
-  if (a->dtype == SA_BF16 && a->d != 128)
-    return fail(SA_EUNSUPPORTED, "bf16 supports d = 128 (got %d)", a->d);
-  if (a->dtype == SA_F32 && a->d != 64 && a->d != 128)
-    return fail(SA_EUNSUPPORTED, "f32 supports d = 64 or 128 (got %d)", a->d);
+  if (a->d != 64 && a->d != 128) return fail(SA_EUNSUPPORTED, "d must be 64 or 128 (got %d)", a->d);
   if (a->batch < 1 || a->h_q < 1 || a->h_kv < 1)
     return fail(SA_EINVAL, "batch, h_q and h_kv must be >= 1");
   if (a->h_q % a->h_kv != 0) return fail(SA_EINVAL, "h_q (%d) must be a multiple of h_kv (%d)", a->h_q, a->h_kv);
@@ -354,8 +351,6 @@ int sparse_attn_bwd(const sa_mask_t* m, const void* plan, size_t plan_bytes, con
   int r = check_mask(m);
   if (r != SA_OK) return r;
   if ((r = check_args(m, a)) != SA_OK) return r;
-  if (a->dtype == SA_BF16 && a->d != 128)
-    return fail(SA_EUNSUPPORTED, "the bf16 backward supports d = 128");
   if (a->lse == nullptr) return fail(SA_EINVAL, "the backward needs the forward's lse");
   if (!aligned16(a->lse)) return fail(SA_EINVAL, "lse must be 16-byte aligned");
   if (g == nullptr) return fail(SA_EINVAL, "grads is NULL");

@@ -27,10 +27,10 @@
 //                  loads in flight while the current one computes: S = Q K^T,
 //                  P, dP = dO V^T, dS, then dV^T += dO^T P and
 //                  dK^T += Q^T dS (transpose reads of the query-side tiles).
-//   bwd_dq_f32, bwd_dkdv_f32
-//                  fp32: the same two sums on the vector ALU (query-major
-//                  per tile; key-major per 64-key unit), a thread per
-//                  32-element slice of a row.
+//   bwd_dq_valu, bwd_dkdv_valu
+//                  fp32, and bf16 with d = 64: the same two sums on the
+//                  vector ALU in fp32 (query-major per tile; key-major per
+//                  64-key unit), a thread per 32-element slice of a row.
 //   bwd_finish     per row: the inverse rotations, the separator and capped
 //                  contributions, the output dtype.
 #include <type_traits>
@@ -728,12 +728,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p) {
 }
 
 // ===========================================================================
-// fp32 (no bf16 rounding anywhere): every product and sum in fp32, on the
-// vector ALU.  The same sums as above, the same accumulator sections and the
-// same finishing kernel (dk_acc holds sum dS q~ unscaled here, the finish
-// multiplies by scale instead of ln 2).  A thread owns a 32-element slice of
-// its row; a dot product is the slice's fma chain plus a butterfly over the
-// row's D/32 lanes (adjacent lanes, so every lane gets the same sum).
+// Vector-ALU backward: fp32 (no bf16 rounding anywhere), and bf16 with
+// d = 64 (bf16 rows read and widened, every product and sum in fp32).  The
+// same sums as above, the same accumulator sections and the same finishing
+// kernel.  The query copy and the capped keys carry scale * log2(e) for bf16
+// (the RoPE stage's convention) and nothing for fp32, which decides the
+// factor of the logits (1 or scale * log2(e)), of dq_cap (ln 2 or scale) and
+// of dk_acc in the finish (ln 2 or scale).  A thread owns a 32-element slice
+// of its row; a dot product is the slice's fma chain plus a butterfly over
+// the row's D/32 lanes (adjacent lanes, so every lane gets the same sum).
 // ===========================================================================
 
 constexpr int F32_SLICE = 32;
@@ -745,21 +748,60 @@ __device__ inline float row_sum(float x) {
   return x;
 }
 
-// Loads a 32-element fp32 slice (zeros when !ok).
-__device__ inline void load_slice(const float* src, bool ok, float (&x)[F32_SLICE]) {
+// One 16-byte piece of a row (4 fp32 or 8 bf16 elements) widened to fp32.
+template <class T>
+__device__ inline void load_piece(const T* src, float* x) {
+  const uint4 v = *reinterpret_cast<const uint4*>(src);
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (sizeof(T) == 4) {
 #pragma unroll
-  for (int c = 0; c < F32_SLICE; c += 4) {
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (ok) v = *reinterpret_cast<const float4*>(src + c);
-    x[c] = v.x; x[c + 1] = v.y; x[c + 2] = v.z; x[c + 3] = v.w;
+    for (int e = 0; e < 4; ++e) x[e] = __uint_as_float(w[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[2 * e] = bf_lo(w[e]);
+      x[2 * e + 1] = bf_hi(w[e]);
+    }
+  }
+}
+
+// Loads a 32-element slice (zeros when !ok).
+template <class T>
+__device__ inline void load_slice(const T* src, bool ok, float (&x)[F32_SLICE]) {
+  constexpr int EP = 16 / (int)sizeof(T);
+#pragma unroll
+  for (int c = 0; c < F32_SLICE; c += EP) {
+    if (ok) load_piece(src + c, x + c);
+    else
+#pragma unroll
+      for (int e = 0; e < EP; ++e) x[c + e] = 0.f;
+  }
+}
+
+// Stages `rows` rows (row r at base + r * stride bytes) of a D-element T row
+// into an fp32 LDS array [nrows][D], zeros past `valid`.
+template <class T, int D, int NT>
+__device__ inline void stage_rows(float (*dst)[D], int nrows, const char* base, int64_t stride, int valid, int tid) {
+  constexpr int EP = 16 / (int)sizeof(T), CH = D / EP;
+  for (int x = tid; x < nrows * CH; x += NT) {
+    const int r = x / CH, ch = x % CH;
+    float v[EP];
+    if (r < valid) load_piece(reinterpret_cast<const T*>(base + r * stride) + ch * EP, v);
+    else
+#pragma unroll
+      for (int e = 0; e < EP; ++e) v[e] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EP; ++e) dst[r][ch * EP + e] = v[e];
   }
 }
 
 // dQ: one work group per (batch, query head, 128-query tile), the forward's
 // units in the forward's order; thread = (query, slice).
 //   dq_acc_i = scale sum dS_ij k~_j        dq_cap_i = scale sum dS_ij R(-L) k_j
-template <int D>
-__global__ __launch_bounds__(TQ * D / F32_SLICE) void bwd_dq_f32(BwdArgs p) {
+template <class T, int D>
+__global__ __launch_bounds__(TQ * D / F32_SLICE) void bwd_dq_valu(BwdArgs p) {
+  constexpr int ESZ = (int)sizeof(T);
+  constexpr bool F32 = ESZ == 4;
   constexpr int TPR = D / F32_SLICE, NT = TQ * TPR;
   __shared__ __attribute__((aligned(16))) float Ks[BK][D];
   __shared__ __attribute__((aligned(16))) float Vs[BK][D];
@@ -771,10 +813,10 @@ __global__ __launch_bounds__(TQ * D / F32_SLICE) void bwd_dq_f32(BwdArgs p) {
   const bool qok = qi < p.n_q;
   const int64_t row = ((int64_t)b * p.h_q + hq) * p.n_q + (qok ? qi : 0);
   float q[F32_SLICE], g[F32_SLICE], dq[F32_SLICE], dqc[F32_SLICE];
-  load_slice(static_cast<const float*>(p.dout) + b * p.dsB + hq * p.dsH + (int64_t)qi * p.dsT + c0, qok, g);
+  load_slice(static_cast<const T*>(p.dout) + b * p.dsB + hq * p.dsH + (int64_t)qi * p.dsT + c0, qok, g);
   auto load_q = [&](bool raw) {
-    const float* src = raw ? static_cast<const float*>(p.qraw) + b * p.qrB + hq * p.qrH + (int64_t)qi * p.qrT
-                           : static_cast<const float*>(p.q) + b * p.qsB + hq * p.qsH + (int64_t)qi * p.qsT;
+    const T* src = raw ? static_cast<const T*>(p.qraw) + b * p.qrB + hq * p.qrH + (int64_t)qi * p.qrT
+                       : static_cast<const T*>(p.q) + b * p.qsB + hq * p.qsH + (int64_t)qi * p.qsT;
     load_slice(src + c0, qok, q);
   };
   load_q(false);
@@ -783,7 +825,7 @@ __global__ __launch_bounds__(TQ * D / F32_SLICE) void bwd_dq_f32(BwdArgs p) {
   for (int c = 0; c < F32_SLICE; ++c) { dq[c] = 0.f; dqc[c] = 0.f; }
   const float lse2 = qok ? p.lse[row] * LOG2E : 0.f;
   const float Di = qok ? p.Dv[row] : 0.f;
-  const float sl2 = p.scale * LOG2E;
+  const float sl2 = F32 ? p.scale * LOG2E : 1.f;
   const float m2 = p.alibi ? alibi_slope_log2(p, hq) : 0.f;
   const float Lf = (float)p.L;
 
@@ -792,15 +834,8 @@ __global__ __launch_bounds__(TQ * D / F32_SLICE) void bwd_dq_f32(BwdArgs p) {
       load_q(raw_q);
       q_is_raw = raw_q;
     }
-    constexpr int CH = D / 4;
-    for (int x = tid; x < BK * CH; x += NT) {
-      const int r = x / CH, ch = x % CH;
-      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
-      if (r < u.kvalid) kv = *reinterpret_cast<const float4*>(u.kbase + r * u.kstride + ch * 16);
-      if (r < u.vvalid) vv = *reinterpret_cast<const float4*>(u.vbase + r * u.vstride + ch * 16);
-      *reinterpret_cast<float4*>(&Ks[r][ch * 4]) = kv;
-      *reinterpret_cast<float4*>(&Vs[r][ch * 4]) = vv;
-    }
+    stage_rows<T, D, NT>(Ks, BK, u.kbase, u.kstride, u.kvalid, tid);
+    stage_rows<T, D, NT>(Vs, BK, u.vbase, u.vstride, u.vvalid, tid);
     __syncthreads();
     for (int r = 0; r < BK; ++r) {
       float s = 0.f, dp = 0.f;
@@ -826,7 +861,9 @@ __global__ __launch_bounds__(TQ * D / F32_SLICE) void bwd_dq_f32(BwdArgs p) {
     }
     __syncthreads();
   };
-  for_each_unit(p, b, kvh, t, 4, (int64_t)D * 4, unit);
+  for_each_unit(p, b, kvh, t, ESZ, (int64_t)D * ESZ, unit);
+  // dq_cap = scale sum dS R(-L) k: the capped keys carry scale * log2(e) for bf16
+  const float cap_mul = F32 ? p.scale : LN2;
   if (qok) {
     float* o = p.dq_acc + row * D + c0;
 #pragma unroll
@@ -838,7 +875,7 @@ __global__ __launch_bounds__(TQ * D / F32_SLICE) void bwd_dq_f32(BwdArgs p) {
 #pragma unroll
       for (int c = 0; c < F32_SLICE; c += 4)
         *reinterpret_cast<float4*>(oc + c) =
-            make_float4(dqc[c] * p.scale, dqc[c + 1] * p.scale, dqc[c + 2] * p.scale, dqc[c + 3] * p.scale);
+            make_float4(dqc[c] * cap_mul, dqc[c + 1] * cap_mul, dqc[c + 2] * cap_mul, dqc[c + 3] * cap_mul);
     }
   }
 }
@@ -848,8 +885,10 @@ __global__ __launch_bounds__(TQ * D / F32_SLICE) void bwd_dq_f32(BwdArgs p) {
 // (key, slice).  It walks the tiles that read the unit in order, every query
 // head of the group, 32 queries at a time staged in LDS:
 //   dk_j += dS_ij q_i (q~, or the raw q for capped pairs)   dv_j += P_ij dO_i
-template <int D>
-__global__ __launch_bounds__(BK * D / F32_SLICE) void bwd_dkdv_f32(BwdArgs p) {
+template <class T, int D>
+__global__ __launch_bounds__(BK * D / F32_SLICE) void bwd_dkdv_valu(BwdArgs p) {
+  constexpr int ESZ = (int)sizeof(T);
+  constexpr bool F32 = ESZ == 4;
   constexpr int TPR = D / F32_SLICE, NT = BK * TPR, QC = 32;
   __shared__ __attribute__((aligned(16))) float Qs[QC][D];
   __shared__ __attribute__((aligned(16))) float Gs[QC][D];
@@ -868,7 +907,7 @@ __global__ __launch_bounds__(BK * D / F32_SLICE) void bwd_dkdv_f32(BwdArgs p) {
   const int n_sep_all = kind == G_SEP ? min(ld_uniform(p.n_sep), (int)p.sep_rows) : 0;
   if (kind == G_SEP && idx * BK >= n_sep_all) return;
 
-  const int64_t rowb = (int64_t)D * 4;
+  const int64_t rowb = (int64_t)D * ESZ;
   const char* kbase;
   const char* vbase;
   int64_t kstr, vstr;
@@ -887,16 +926,16 @@ __global__ __launch_bounds__(BK * D / F32_SLICE) void bwd_dkdv_f32(BwdArgs p) {
     const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.cap_rows + (int64_t)idx * BK;
     kbase = static_cast<const char*>(p.kcap) + ho * rowb;
     kstr = rowb;
-    vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)key0 * p.vsT) * 4;
-    vstr = p.vsT * 4;
+    vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)key0 * p.vsT) * ESZ;
+    vstr = p.vsT * ESZ;
     valid = min(BK, p.n_cap - key0);
     dk_out = p.dkcap + ho * D;
     dv_out = p.dvcap + ho * D;
   } else {
-    kbase = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH + (int64_t)key0 * p.ksT) * 4;
-    vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)key0 * p.vsT) * 4;
-    kstr = p.ksT * 4;
-    vstr = p.vsT * 4;
+    kbase = static_cast<const char*>(p.k) + (b * p.ksB + kvh * p.ksH + (int64_t)key0 * p.ksT) * ESZ;
+    vbase = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH + (int64_t)key0 * p.vsT) * ESZ;
+    kstr = p.ksT * ESZ;
+    vstr = p.vsT * ESZ;
     valid = min(BK, p.n_k - key0);
     const int64_t ho = ((int64_t)b * p.h_kv + kvh) * p.n_k + key0;
     dk_out = p.dk_acc + ho * D;
@@ -904,15 +943,15 @@ __global__ __launch_bounds__(BK * D / F32_SLICE) void bwd_dkdv_f32(BwdArgs p) {
   }
   const bool kok = kk < valid;
   float kx[F32_SLICE], vx[F32_SLICE], dk[F32_SLICE], dv[F32_SLICE];
-  load_slice(reinterpret_cast<const float*>(kbase + kk * kstr) + c0, kok, kx);
-  load_slice(reinterpret_cast<const float*>(vbase + kk * vstr) + c0, kok, vx);
+  load_slice(reinterpret_cast<const T*>(kbase + kk * kstr) + c0, kok, kx);
+  load_slice(reinterpret_cast<const T*>(vbase + kk * vstr) + c0, kok, vx);
 #pragma unroll
   for (int c = 0; c < F32_SLICE; ++c) { dk[c] = 0.f; dv[c] = 0.f; }
   const int j = key0 + kk;
   const bool q_raw = kind == G_CAP;
-  const float* qsrc = static_cast<const float*>(q_raw ? p.qraw : p.q);
+  const char* qsrc = static_cast<const char*>(q_raw ? p.qraw : p.q);
   const int64_t qB = q_raw ? p.qrB : p.qsB, qH = q_raw ? p.qrH : p.qsH, qT = q_raw ? p.qrT : p.qsT;
-  const float sl2 = p.scale * LOG2E;
+  const float sl2 = F32 ? p.scale * LOG2E : 1.f;
   const float Lf = (float)p.L;
 
   // the unit as one tile reads it (mk < 0: not read)
@@ -964,19 +1003,11 @@ __global__ __launch_bounds__(BK * D / F32_SLICE) void bwd_dkdv_f32(BwdArgs p) {
       const float m2 = p.alibi ? alibi_slope_log2(p, hq) : 0.f;
       const int q_end = min(p.n_q, (t + 1) * TQ);
       for (int qc0 = t * TQ; qc0 < q_end; qc0 += QC) {
-        constexpr int CH = D / 4;
-        for (int x = tid; x < QC * CH; x += NT) {
-          const int r = x / CH, ch = x % CH;
-          const int i = qc0 + r;
-          float4 qv = make_float4(0.f, 0.f, 0.f, 0.f), gv = qv;
-          if (i < q_end) {
-            qv = *reinterpret_cast<const float4*>(qsrc + b * qB + hq * qH + (int64_t)i * qT + ch * 4);
-            gv = *reinterpret_cast<const float4*>(static_cast<const float*>(p.dout) + b * p.dsB + hq * p.dsH +
-                                                  (int64_t)i * p.dsT + ch * 4);
-          }
-          *reinterpret_cast<float4*>(&Qs[r][ch * 4]) = qv;
-          *reinterpret_cast<float4*>(&Gs[r][ch * 4]) = gv;
-        }
+        const int qv = q_end - qc0;
+        stage_rows<T, D, NT>(Qs, QC, qsrc + (b * qB + hq * qH + (int64_t)qc0 * qT) * ESZ, qT * ESZ, qv, tid);
+        stage_rows<T, D, NT>(Gs, QC,
+                             static_cast<const char*>(p.dout) + (b * p.dsB + hq * p.dsH + (int64_t)qc0 * p.dsT) * ESZ,
+                             p.dsT * ESZ, qv, tid);
         if (tid < QC) {
           const int i = qc0 + tid;
           const int64_t ri = ((int64_t)b * p.h_q + hq) * p.n_q + i;
@@ -1228,26 +1259,30 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   p.alibi_e = alibi ? a.alibi_exp : 0.f;
   p.n_sep_chunks = p.gather ? (int)(ro.sep_rows / BK) : 0;
   p.n_cap_blocks = p.use_cap ? (int)ceil_div(ro.n_cap, BK) : 0;
-  if (f32) {
+  const bool valu = f32 || a.d != 128;  // the MFMA kernels are bf16 with d = 128
+  if (valu) {
     const unsigned gq = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
     const int64_t units = (int64_t)p.n_sep_chunks + p.n_cap_blocks + lay.n_blocks;
     const unsigned gk = (unsigned)(units * a.batch * a.h_kv);
-    if (a.d == 64) {
-      hipLaunchKernelGGL(bwd_dq_f32<64>, dim3(gq), dim3(TQ * 64 / F32_SLICE), 0, s, p);
-      hipLaunchKernelGGL(bwd_dkdv_f32<64>, dim3(gk), dim3(BK * 64 / F32_SLICE), 0, s, p);
+    if (f32 && a.d == 64) {
+      hipLaunchKernelGGL((bwd_dq_valu<float, 64>), dim3(gq), dim3(TQ * 64 / F32_SLICE), 0, s, p);
+      hipLaunchKernelGGL((bwd_dkdv_valu<float, 64>), dim3(gk), dim3(BK * 64 / F32_SLICE), 0, s, p);
+    } else if (f32) {
+      hipLaunchKernelGGL((bwd_dq_valu<float, 128>), dim3(gq), dim3(TQ * 128 / F32_SLICE), 0, s, p);
+      hipLaunchKernelGGL((bwd_dkdv_valu<float, 128>), dim3(gk), dim3(BK * 128 / F32_SLICE), 0, s, p);
     } else {
-      hipLaunchKernelGGL(bwd_dq_f32<128>, dim3(gq), dim3(TQ * 128 / F32_SLICE), 0, s, p);
-      hipLaunchKernelGGL(bwd_dkdv_f32<128>, dim3(gk), dim3(BK * 128 / F32_SLICE), 0, s, p);
+      hipLaunchKernelGGL((bwd_dq_valu<__bf16, 64>), dim3(gq), dim3(TQ * 64 / F32_SLICE), 0, s, p);
+      hipLaunchKernelGGL((bwd_dkdv_valu<__bf16, 64>), dim3(gk), dim3(BK * 64 / F32_SLICE), 0, s, p);
     }
   }
   // 2. dQ (query-major)
-  if (!f32) {
+  if (!valu) {
     const unsigned grid = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
     if (alibi) hipLaunchKernelGGL(bwd_dq_bf16<true>, dim3(grid), dim3(256), 0, s, p);
     else hipLaunchKernelGGL(bwd_dq_bf16<false>, dim3(grid), dim3(256), 0, s, p);
   }
   // 3. dK, dV (key-major): separator chunks, then capped blocks, then dense blocks
-  if (!f32) {
+  if (!valu) {
     const int64_t groups = (int64_t)(p.n_sep_chunks + 1) / 2 + (p.n_cap_blocks + 1) / 2 + (lay.n_blocks + 1) / 2;
     const unsigned grid = (unsigned)(groups * a.batch * a.h_kv);
     if (alibi) hipLaunchKernelGGL(bwd_dkdv_bf16<true>, dim3(grid), dim3(512), 0, s, p);

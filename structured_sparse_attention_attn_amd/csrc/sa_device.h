@@ -179,6 +179,16 @@ constexpr int BLK_BYTES = BK * 256;        // one 64 x 128 bf16 block
 // the 8 rows x 64 bytes of one V^T transpose read cover every bank twice.
 __device__ inline int swzf(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 
+// The swizzle of a block with D-element bf16 rows: 256-byte rows (D = 128)
+// use swzf; 128-byte rows (D = 64, 8 chunks) use chunk c ^ ((r >> 1) & 7),
+// so 16 consecutive rows (two per 256-byte bank line) put one logical chunk
+// in 16 distinct bank groups.
+template <int D>
+__device__ inline int swz(int r) {
+  if constexpr (D == 128) return swzf(r);
+  else return (r >> 1) & 7;
+}
+
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ inline uint4 ld16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -266,15 +276,16 @@ __device__ inline void tile_items(const A& p, int t, TileUnits& tu) {
 }
 
 // REV visits the plan's blocks last to first (the diagonal block first).
-template <bool REV, class A>
+// ROWB: bytes per row of the compact arrays (capped keys, gathered rows).
+template <bool REV, int ROWB = D128 * 2, class A>
 __device__ inline Unit unit_at(const A& p, const TileUnits& tu, int u) {
   Unit x;
   x.count = 0;
   x.sbits = 0;
   if (u < tu.n_capu) {
     const int blk = ld_uniform(p.items + tu.cap0 + u) & 0xffffff;
-    x.kbase = tu.capb + (int64_t)blk * BK * (D128 * 2);
-    x.kstride = D128 * 2;
+    x.kbase = tu.capb + (int64_t)blk * BK * ROWB;
+    x.kstride = ROWB;
     x.kvalid = min(BK, p.n_cap - blk * BK);
     x.vbase = tu.vb + (int64_t)blk * BK * tu.vst;
     x.vstride = tu.vst;
@@ -286,10 +297,10 @@ __device__ inline Unit unit_at(const A& p, const TileUnits& tu, int u) {
   u -= tu.n_capu;
   if (u < tu.n_ch) {
     const int c0 = u * BK;
-    x.kbase = tu.ksb + (int64_t)c0 * (D128 * 2);
-    x.kstride = D128 * 2;
-    x.vbase = tu.vsb + (int64_t)c0 * (D128 * 2);
-    x.vstride = D128 * 2;
+    x.kbase = tu.ksb + (int64_t)c0 * ROWB;
+    x.kstride = ROWB;
+    x.vbase = tu.vsb + (int64_t)c0 * ROWB;
+    x.vstride = ROWB;
     x.kvalid = x.vvalid = min(BK, tu.nsep - c0);
     x.key0 = 0;
     x.count = x.kvalid;

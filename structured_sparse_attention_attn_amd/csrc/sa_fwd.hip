@@ -69,7 +69,7 @@ __device__ inline bool plan_overflowed(const FwdArgs& p) {
 }
 
 // ===========================================================================
-// bf16, d = 128: MFMA 32x32x16.  4 waves x 32 queries = one 128-query tile.
+// bf16, d = 128 or 64: MFMA 32x32x16.  4 waves x 32 queries = one 128-query tile.
 // S^T = K Q^T (keys as rows) so every lane owns one query's logits and the
 // row max / row sum stay in the lane (plus one swap between the two 32-lane
 // halves); then O^T += V^T P^T, the key order inside each 16-key step permuted
@@ -87,10 +87,19 @@ __device__ inline bool plan_overflowed(const FwdArgs& p) {
 // from the diagonal down, so a row's first reference already includes its
 // largest bias (0 at j = i): every later logit is at most the query-key spread
 // above it, and the reference stays the size of a query-key logit.
-template <bool ALIBI>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
+template <int D, bool ALIBI>
+__global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16(FwdArgs p) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  constexpr int ROWB = D * 2;         // bytes per row
+  constexpr int BLKB = BK * ROWB;     // one 64-row block
+  constexpr int NKS = D / 16;         // k-steps of the QK product
+  constexpr int NDM = D / 32;         // 32-row d blocks of O^T
+  constexpr int LPR = ROWB / 16;      // lanes per row of one global->LDS load (16-byte pieces)
+  constexpr int RPI = 64 / LPR;       // rows per load instruction (1 KB)
+  constexpr int NJ = BLKB / 4096;     // load instructions per block and wave
+  constexpr int XSH = D == 128 ? 4 : 6;  // byte shift of instruction j's swizzle change
   // K blocks double-buffered, V blocks triple-buffered: [K0 K1 V0 V1 V2]
-  __shared__ __attribute__((aligned(16))) char smem[5 * BLK_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[5 * BLKB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int l32 = lane & 31, hl = lane >> 5;
@@ -108,19 +117,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   tu.vb = static_cast<const char*>(p.v) + (b * p.vsB + kvh * p.vsH) * 2;
   tu.kst = p.ksT * 2;
   tu.vst = p.vsT * 2;
-  tu.capb = static_cast<const char*>(p.kcap) + ((int64_t)b * p.h_kv + kvh) * p.cap_rows * (D128 * 2);
-  const int64_t sep_off = ((int64_t)b * p.h_kv + kvh) * p.sep_rows * (D128 * 2);
+  tu.capb = static_cast<const char*>(p.kcap) + ((int64_t)b * p.h_kv + kvh) * p.cap_rows * ROWB;
+  const int64_t sep_off = ((int64_t)b * p.h_kv + kvh) * p.sep_rows * ROWB;
   tu.ksb = static_cast<const char*>(p.ksep) + sep_off;
   tu.vsb = static_cast<const char*>(p.vsep) + sep_off;
   const int n_units = tu.n_capu + tu.n_ch + tu.n_items;
   const float m2 = ALIBI ? alibi_slope_log2(p, hq) : 0.f;
   const float Lf = (float)p.L;
 
-  bf16x8 qf[8];
+  bf16x8 qf[NKS];
   auto load_q = [&](const void* base, int64_t sB, int64_t sH, int64_t sT) {
     const char* row = static_cast<const char*>(base) + (b * sB + hq * sH + (int64_t)qi * sT) * 2;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+    for (int s = 0; s < NKS; ++s) {
       uint4 x = make_uint4(0, 0, 0, 0);
       if (qok) x = ld16(row + (16 * s + 8 * hl) * 2);
       qf[s] = __builtin_bit_cast(bf16x8, x);
@@ -131,8 +140,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   // Every unit but the capped ones reads R(pos) q * scale * log2(e), made
   // here in registers; the capped units (visited last) pair the raw query,
   // loaded again before them, with R(-L) k.  Lane (l32, hl) holds dims 16 s + 8 hl + e of
-  // its query, so the rotate-half partner of dim c (s < 4) is c + 64 in
-  // qf[s + 4], same lane.  theta_c / (2 pi) comes from products of powers of
+  // its query, so the rotate-half partner of dim c (s < D/32) is c + D/2 in
+  // qf[s + D/32], same lane.  theta_c / (2 pi) comes from products of powers of
   // base^(-2/d) in fp64 (a few ulp from the direct power); the angle is
   // reduced in fp64 to a fraction of a turn, and the hardware sine and cosine
   // take turns.
@@ -142,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       const double pos = (double)(p.q_pos0 + qi);
       double th_s = (hl ? p.th8 : 1.0) * 0.15915494309189535;  // theta_{8 hl} / (2 pi)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < NKS / 2; ++s) {
         double th = th_s;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -150,15 +159,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
           th *= p.th1;
           const float f = (float)(rev - rint(rev));
           const float cs = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
-          const float x1 = (float)qf[s][e], x2 = (float)qf[s + 4][e];
+          const float x1 = (float)qf[s][e], x2 = (float)qf[s + NKS / 2][e];
           qf[s][e] = (__bf16)((x1 * cs - x2 * sn) * qs);
-          qf[s + 4][e] = (__bf16)((x2 * cs + x1 * sn) * qs);
+          qf[s + NKS / 2][e] = (__bf16)((x2 * cs + x1 * sn) * qs);
         }
         th_s *= p.th16;
       }
     } else {
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
+      for (int s = 0; s < NKS; ++s)
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[s][e] = (__bf16)((float)qf[s][e] * qs);
     }
@@ -176,32 +185,34 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   bool has_ref = false;
   float m_ref = 0.f, l_run = 0.f;
   f32x16 negm = f32x16{};
-  f32x16 acc[4];
+  f32x16 acc[NDM];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < NDM; ++i) acc[i] = f32x16{};
 
-  // global -> LDS without register staging: one instruction moves rows
-  // 4i .. 4i+3 (lane l -> row 4i + l/16, stored chunk l%16); the lane fetches
-  // the logical chunk that the row's swizzle puts in that slot, which is
-  // lchunk ^ (i & 3) for a per-lane lchunk.  Rows past the unit's valid count
-  // repeat its last valid row: finite values whose logits are masked out.
-  const int lrow = lane >> 4;
-  const int lchunk = (lane & 15) ^ (lrow << 2);
-  // this lane's row (bits 8+) and logical chunk (bits 4..7) for j = 0; the
-  // j-th instruction's offset is lofs ^ (j << 4) + j * 1024.  The offsets are
+  // global -> LDS without register staging: one instruction moves RPI rows
+  // (lane l -> row RPI i + l / LPR, stored chunk l % LPR); the lane fetches
+  // the logical chunk that the row's swizzle puts in that slot, lchunk for the
+  // wave's first instruction and lchunk ^ (j << (XSH - 4)) for its j-th (the
+  // rows of instruction j differ from those of the first only in the swizzle
+  // bits that j sets).  Rows past the unit's valid count repeat its last valid
+  // row: finite values whose logits are masked out.
+  const int lrow = lane / LPR;
+  const int lchunk = (lane % LPR) ^ swz<D>(16 * wid + lrow);
+  // this lane's row and logical chunk (bits 4+) for j = 0; the j-th
+  // instruction's offset is lofs ^ (j << XSH) + j * 1024.  The offsets are
   // recomputed from lofs at each use (a 32-bit offset next to a uniform base
   // address, so each load is one instruction with no address arithmetic).
-  const uint32_t lofs = (uint32_t)((16 * wid + lrow) * 256 + (lchunk << 4));
+  const uint32_t lofs = (uint32_t)((16 * wid + lrow) * ROWB + (lchunk << 4));
   auto issue_loads = [&](const Unit& u, int kslot, int vslot) {
-    char* Kb = smem + kslot * BLK_BYTES;
-    char* Vb = smem + (2 + vslot) * BLK_BYTES;
+    char* Kb = smem + kslot * BLKB;
+    char* Vb = smem + (2 + vslot) * BLKB;
     uint32_t lo = lofs;
     __asm__ volatile("" : "+v"(lo));
-    if (u.kvalid == BK && u.vvalid == BK && u.kstride == 256 && u.vstride == 256) {
+    if (u.kvalid == BK && u.vvalid == BK && u.kstride == ROWB && u.vstride == ROWB) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = wid * 4 + j;
-        const uint32_t o = lo ^ (uint32_t)(j << 4);
+      for (int j = 0; j < NJ; ++j) {
+        const int i = wid * NJ + j;
+        const uint32_t o = lo ^ (uint32_t)(j << XSH);
         const char* kj = u.kbase + j * 1024;
         const char* vj = u.vbase + j * 1024;
         __asm__ volatile("" : "+s"(kj), "+s"(vj));  // uniform bases: one scalar add each
@@ -212,14 +223,14 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       }
       return;
     }
-    const int r0 = (int)(lo >> 8);
-    const uint32_t c0 = lo & 0xF0u;
+    const int r0 = (int)(lo / ROWB);
+    const uint32_t c0 = lo & (uint32_t)(ROWB - 16);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = wid * 4 + j;  // rows 4i .. 4i+3
-      const uint32_t ch = c0 ^ (uint32_t)(j << 4);
-      const int kr = min(r0 + 4 * j, u.kvalid - 1);
-      const int vr = min(r0 + 4 * j, u.vvalid - 1);
+    for (int j = 0; j < NJ; ++j) {
+      const int i = wid * NJ + j;  // rows RPI i .. RPI i + RPI - 1
+      const uint32_t ch = c0 ^ (uint32_t)(j << XSH);
+      const int kr = min(r0 + RPI * j, u.kvalid - 1);
+      const int vr = min(r0 + RPI * j, u.vvalid - 1);
       __builtin_amdgcn_global_load_lds((const void*)(u.kbase + (int64_t)kr * u.kstride + ch),
                                        (__attribute__((address_space(3))) void*)(Kb + i * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const void*)(u.vbase + (int64_t)vr * u.vstride + ch),
@@ -234,31 +245,31 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   // kA + i/4 (+8 for the upper half of the k-step), columns
   // 32 dm + 16 (g & 1) + 4 (i & 3) .. +3, with kA = 32 (kst/2) + 16 (kst%2) + 4 hl,
   // so row & 15 is 4 hl + i/4 (+8).
-  const int kf = swzf(l32) ^ hl;
+  const int kf = swz<D>(l32) ^ hl;
   const int vrow = 4 * hl + ((lane & 15) >> 2);
-  const int vf0 = swzf(vrow), vf1 = swzf(vrow + 8);
+  const int vf0 = swz<D>(vrow), vf1 = swz<D>(vrow + 8);
   const int vcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int vcb = vcol >> 3;  // chunk of the column within its 32-column group
 
   // O^T += V^T P^T for the unit whose weights are in pb and whose V block is
   // in slot vslot: V^T fragments two MFMAs ahead
   auto pv = [&](const bf16x8 (&pb)[4], int vslot) {
-    const char* vl = smem + (2 + vslot) * BLK_BYTES + vrow * 256 + ((vcol & 7) << 1);
+    const char* vl = smem + (2 + vslot) * BLKB + vrow * ROWB + ((vcol & 7) << 1);
     auto vfrag = [&](int kst, int dm) {
-      const char* a0 = vl + (32 * (kst >> 1) + 16 * (kst & 1)) * 256 + (((4 * dm + vcb) ^ vf0) << 4);
-      const char* a1 = vl + (32 * (kst >> 1) + 16 * (kst & 1) + 8) * 256 + (((4 * dm + vcb) ^ vf1) << 4);
+      const char* a0 = vl + (32 * (kst >> 1) + 16 * (kst & 1)) * ROWB + (((4 * dm + vcb) ^ vf0) << 4);
+      const char* a1 = vl + (32 * (kst >> 1) + 16 * (kst & 1) + 8) * ROWB + (((4 * dm + vcb) ^ vf1) << 4);
       const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a0));
       const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(a1));
       return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     };
     bf16x8 va[3];
     va[0] = vfrag(0, 0);
-    va[1] = vfrag(0, 1);
+    va[1] = vfrag(1 / NDM, 1 % NDM);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kst = i >> 2, dm = i & 3;
-      if (i + 2 < 16) va[(i + 2) % 3] = vfrag((i + 2) >> 2, (i + 2) & 3);
+    for (int i = 0; i < 4 * NDM; ++i) {
+      const int kst = i / NDM, dm = i % NDM;
+      if (i + 2 < 4 * NDM) va[(i + 2) % 3] = vfrag((i + 2) / NDM, (i + 2) % NDM);
       acc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], pb[kst], acc[dm], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -275,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
   // it is in.
   // unit order: separator chunks, the plan's blocks, then the capped units
   const int u_cap = n_units - tu.n_capu;
-  auto unit = [&](int u) { return unit_at<ALIBI>(p, tu, u < u_cap ? u + tu.n_capu : u - u_cap); };
+  auto unit = [&](int u) { return unit_at<ALIBI, ROWB>(p, tu, u < u_cap ? u + tu.n_capu : u - u_cap); };
   Unit cur;
   if (n_units > 0) {
     cur = unit(0);
@@ -298,15 +309,15 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
     }
     vs_prev = vs_prev == 2 ? 0 : vs_prev + 1;
     vs_next = vs_next == 2 ? 0 : vs_next + 1;
-    const char* Kb = smem + buf * BLK_BYTES;
+    const char* Kb = smem + buf * BLKB;
 
     // --- S^T = K Q^T - m_ref: both 32-key halves interleaved, K fragments
     //     read two k-steps ahead of their MFMAs ---
     f32x16 s[2];
     {
-      const char* kl = Kb + l32 * 256;
+      const char* kl = Kb + l32 * ROWB;
       auto kfrag = [&](int mb, int ks) {
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + mb * 32 * 256 + (((2 * ks) ^ kf) << 4)));
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + mb * 32 * ROWB + (((2 * ks) ^ kf) << 4)));
       };
       bf16x8 a0[3], a1[3];
       a0[0] = kfrag(0, 0);
@@ -321,8 +332,8 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
       f32x16 c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[0], qf[0], negm, 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ks = 1; ks < 8; ++ks) {
-        if (ks + 2 < 8) {
+      for (int ks = 1; ks < NKS; ++ks) {
+        if (ks + 2 < NKS) {
           a0[(ks + 2) % 3] = kfrag(0, ks + 2);
           a1[(ks + 2) % 3] = kfrag(1, ks + 2);
         }
@@ -371,13 +382,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
           // the exact-max update: the reference rises to the unit's row
           // maximum and every weight is <= 1.
           {
-            const char* kl = Kb + l32 * 256;
+            const char* kl = Kb + l32 * ROWB;
             f32x16 c0 = negm, c1 = negm;
 #pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
+            for (int ks = 0; ks < NKS; ++ks) {
               const bf16x8 a0 = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + (((2 * ks) ^ kf) << 4)));
               const bf16x8 a1 =
-                  __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + 32 * 256 + (((2 * ks) ^ kf) << 4)));
+                  __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + 32 * ROWB + (((2 * ks) ^ kf) << 4)));
               c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0, qf[ks], c0, 0, 0, 0);
               c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1, qf[ks], c1, 0, 0, 0);
             }
@@ -406,7 +417,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r] - mx);
 #pragma unroll
-          for (int dm = 0; dm < 4; ++dm) acc[dm] *= alpha;
+          for (int dm = 0; dm < NDM; ++dm) acc[dm] *= alpha;
           l_run *= alpha;
           m_ref += mx;
           negm = f32x16{} - m_ref;
@@ -417,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
 #pragma unroll
           for (int mb = 0; mb < 2; ++mb) s[mb] *= f;
 #pragma unroll
-          for (int dm = 0; dm < 4; ++dm) acc[dm] *= f;
+          for (int dm = 0; dm < NDM; ++dm) acc[dm] *= f;
           l_run *= f;
           m_ref += __log2f(pm);
           negm = f32x16{} - m_ref;
@@ -443,7 +454,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
         for (int r = 0; r < 16; ++r) s[mb][r] = __builtin_amdgcn_exp2f(s[mb][r] - delta);
       pack_p(s, pb);
 #pragma unroll
-      for (int dm = 0; dm < 4; ++dm) acc[dm] *= alpha;
+      for (int dm = 0; dm < NDM; ++dm) acc[dm] *= alpha;
       l_run = l_run * alpha + sum_p(pb);
       m_ref += delta;
       has_ref = has_ref || mx != NEG_INF;
@@ -468,7 +479,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_d128(FwdArgs p) {
     const float inv = bad ? __builtin_nanf("") : (l_tot > 0.f ? 1.f / l_tot : 0.f);
     char* orow = static_cast<char*>(p.o) + (b * p.osB + hq * p.osH + (int64_t)qi * p.osT) * 2;
 #pragma unroll
-    for (int dm = 0; dm < 4; ++dm) {
+    for (int dm = 0; dm < NDM; ++dm) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * dm + 8 * g + 4 * hl;
@@ -650,11 +661,16 @@ hipError_t launch_fwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
     }
   }
   const unsigned grid = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
-  if (a.dtype == SA_BF16) {
+  if (a.dtype == SA_BF16 && a.d == 128) {
     if (p.alibi)
-      hipLaunchKernelGGL(fwd_bf16_d128<true>, dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((fwd_bf16<128, true>), dim3(grid), dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL(fwd_bf16_d128<false>, dim3(grid), dim3(256), 0, s, p);
+      hipLaunchKernelGGL((fwd_bf16<128, false>), dim3(grid), dim3(256), 0, s, p);
+  } else if (a.dtype == SA_BF16) {
+    if (p.alibi)
+      hipLaunchKernelGGL((fwd_bf16<64, true>), dim3(grid), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((fwd_bf16<64, false>), dim3(grid), dim3(256), 0, s, p);
   } else if (a.d == 64) {
     hipLaunchKernelGGL(fwd_f32<64>, dim3(grid), dim3(128), 0, s, p);
   } else {

@@ -159,7 +159,7 @@ def test_fwd_workspace_and_validation():
     plan_bytes = sa.sa_plan_bytes(m)
     cases = [
         (dict(dtype=5), sa.SA_EINVAL),
-        (dict(d=64), sa.SA_EUNSUPPORTED),
+        (dict(d=96), sa.SA_EUNSUPPORTED),
         (dict(h_q=3), sa.SA_EINVAL),
         (dict(rope=9), sa.SA_EINVAL),
         (dict(rope_base=0.5), sa.SA_EINVAL),
@@ -278,7 +278,7 @@ def test_bwd_validation():
                                    None if grads is None else ctypes.byref(grads), wsp, wsb, None)
 
     assert call(args=_args()) == sa.SA_EINVAL and "lse" in sa.sa_last_error()  # no lse
-    assert call(args=_args(lse=8192, d=64)) == sa.SA_EUNSUPPORTED  # bf16 needs d = 128
+    assert call(args=_args(lse=8192, d=96)) == sa.SA_EUNSUPPORTED  # d is 64 or 128
     # fp32 gradients: 16-byte rows checked with 4-byte elements (a 4-element row stride is 16 bytes
     # in fp32 but only 8 in bf16)
     g4 = _grads()

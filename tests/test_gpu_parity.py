@@ -181,6 +181,27 @@ def test_fwd_small(sa, case, dtype):
         _run_small(sa, wl, check_canary=True)
 
 
+@pytest.mark.parametrize("case", range(len(SMALL)))
+def test_fwd_small_bf16_d64(sa, case):
+    """bf16 with 64-element heads (the Pythia-class shape): the same cases as above."""
+    mode, kw = SMALL[case]
+    for rope in (10000.0, None):
+        wl = W.small(mode, seed=700 + case, dtype="bf16", d=64, rope_base=rope, **kw)
+        log(f"small d64 {case} rope={rope}")
+        _run_small(sa, wl, check_canary=True)
+
+
+def test_fwd_bf16_d64_strided_and_alibi(sa):
+    wl = W.small(W.SEPLLM, seed=730, d=64, m=700, a=70, w=100, p_sep=0.2, h_q=4, h_kv=2)
+    _run_small(sa, wl, strided=True)
+    for i, kw in enumerate(ALIBI_SMALL):
+        wl = W.small(W.LAMBDA, seed=740 + i, d=64, rope_base=None, **kw)
+        log(f"alibi d64 {i}")
+        _run_small(sa, wl, check_canary=True)
+    wl = W.small(W.LAMBDA, seed=760, d=64, m=640, n_s=10, L=100, rope_base=None, alibi_exp=8.0)
+    _run_small(sa, wl, q_zero=True)
+
+
 def test_fwd_f32_d128_and_strided(sa):
     wl = W.small(W.SEPLLM, seed=5, dtype="f32", d=128, m=300, a=4, w=50, p_sep=0.1)
     _run_small(sa, wl)
@@ -289,18 +310,20 @@ WIDE = [
 ]
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("case", range(len(WIDE)))
-def test_fwd_wide_logits(sa, case):
+def test_fwd_wide_logits(sa, case, d):
     """Queries scaled by 4 (logit std about 4 natural units) and values by 1/4: rows whose
     later units exceed their reference by more than 2^10 in weight take the rescale."""
     mode, kw, rope, alibi = WIDE[case]
-    wl = W.small(mode, seed=520 + case, rope_base=rope, alibi_exp=alibi, **kw)
+    wl = W.small(mode, seed=520 + case, rope_base=rope, alibi_exp=alibi, d=d, **kw)
     log(f"wide logits {case}")
     _run_small(sa, wl, check_canary=True, qmul=4.0, vmul=0.25, expect=("rescale",))
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("case", range(len(WIDE)))
-def test_fwd_logit_spike(sa, case):
+def test_fwd_logit_spike(sa, case, d):
     """Every 7th row of the second half aims its query at one key with a logit of 150 natural
     units, visited after the keys that set the row's reference: the capped starting key
     (Lambda with RoPE, visited last), the diagonal key after the gathered separators (SepLLM)
@@ -308,7 +331,7 @@ def test_fwd_logit_spike(sa, case):
     weight against the stale reference would overflow (2^(s - m_ref) with s - m_ref >= 128):
     the kernel computes that unit again with its exact row maximum."""
     mode, kw, rope, alibi = WIDE[case]
-    wl = W.small(mode, seed=540 + case, rope_base=rope, alibi_exp=alibi, **kw)
+    wl = W.small(mode, seed=540 + case, rope_base=rope, alibi_exp=alibi, d=d, **kw)
     log(f"logit spike {case}")
     _run_small(sa, wl, check_canary=True, spike=list(range(wl.n_q // 2, wl.n_q, 7)),
                expect=("recompute", "overflow"))
@@ -354,6 +377,11 @@ def _workload_parity(sa, cid, heads, n_random):
 
 def test_workload1_full(sa):
     _workload_parity(sa, 1, heads=[0, 1], n_random=None)
+
+
+def test_workload7_sampled(sa):
+    """The Pythia-class 4K SepLLM layer (12 heads of 64, batch 8): batch row 0, three heads."""
+    _workload_parity(sa, 7, heads=[0, 5, 11], n_random=300)
 
 
 def test_workload2_full_rows(sa):
@@ -602,6 +630,32 @@ def test_bwd_small(sa, case):
     lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
     o = sa_obj.forward(q, k, v, lse=lse, rope_base=wl.rope_base, scale=wl.scale, alibi_exp=wl.alibi_exp)
     dout = W.make_grad(tuple(q.shape), seed=900 + case).cuda()
+    dq, dk, dv = sa_obj.backward(q, k, v, o, lse, dout, rope_base=wl.rope_base, scale=wl.scale,
+                                 alibi_exp=wl.alibi_exp)
+    torch.cuda.synchronize()
+    spec = spec_of(wl, None if sep is None else sep.numpy())
+    for b in range(wl.batch):
+        rq, rk, rv = O.attention_backward(to64(inp["q"][b]), to64(inp["k"][b]), to64(inp["v"][b]),
+                                          to64(dout[b]), spec, wl.rope_base, wl.scale,
+                                          alibi_exp=wl.alibi_exp)
+        for name, got, ref in (("dq", dq[b], rq), ("dk", dk[b], rk), ("dv", dv[b], rv)):
+            bwd_compare(f"b{b} {name}", to64(got), ref)
+
+
+@pytest.mark.parametrize("case", range(len(BWD_SMALL)))
+def test_bwd_small_bf16_d64(sa, case):
+    """bf16 with 64-element heads: the vector-ALU backward (bf16 rows, fp32 sums)."""
+    mode, kw, rope, alibi = BWD_SMALL[case]
+    wl = W.small(mode, seed=800 + case, d=64, rope_base=rope, alibi_exp=alibi, **kw)
+    log(f"bwd d64 {case}: {mode} {kw} rope={rope} alibi={alibi}")
+    inp = W.make_small_inputs(wl)
+    q, k, v = (inp[x].cuda() for x in ("q", "k", "v"))
+    sep = inp.get("sep")
+    sa_obj = device_mask(wl, None if sep is None else sep.cuda())
+    sa_obj.build_plan()
+    lse = torch.empty((wl.batch, wl.h_q, wl.n_q), dtype=torch.float32, device="cuda")
+    o = sa_obj.forward(q, k, v, lse=lse, rope_base=wl.rope_base, scale=wl.scale, alibi_exp=wl.alibi_exp)
+    dout = W.make_grad(tuple(q.shape), seed=980 + case).cuda()
     dq, dk, dv = sa_obj.backward(q, k, v, o, lse, dout, rope_base=wl.rope_base, scale=wl.scale,
                                  alibi_exp=wl.alibi_exp)
     torch.cuda.synchronize()

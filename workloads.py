@@ -72,6 +72,10 @@ WORKLOADS: Dict[int, Workload] = {
     # Lambda mask with its bias clipped at L_pretrain
     6: Workload(6, "lminfinite_alibi_lambda_32k", LAMBDA, "bf16", 1, 32, 32, 128, 32768, 32768,
                 n_s=10, L=2048, alibi_exp=8.0, seed=6000),
+    # a Pythia-160M-shaped layer (12 heads, head_dim 64) under the SepLLM training mask with
+    # n = 64 neighbours, a batch of 8 sequences of 4096 tokens; RoPE over every dimension
+    7: Workload(7, "sepllm_pythia_4k_d64", SEPLLM, "bf16", 8, 12, 12, 64, 4096, 4096,
+                a=4, w=64, p_sep=0.08, rope_base=10000.0, seed=7000),
 }
 
 
