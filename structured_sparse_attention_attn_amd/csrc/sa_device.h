@@ -245,6 +245,7 @@ __device__ inline float sum_p(const bf16x8 (&pb)[4]) {
 struct TileUnits {
   int it0, n_items, n_capu, n_ch, nsep;
   int cap0;            // index of the first capped item (the ordinary pass starts at it0)
+  int rot;             // the ordinary items are visited from item rot on, wrapping (0: in order)
   const char* kb;      // dense keys of this (batch, kv head)
   const char* vb;
   int64_t kst, vst;
@@ -265,6 +266,7 @@ __device__ inline void tile_items(const A& p, int t, TileUnits& tu) {
   tu.n_items = ld_uniform(p.tile_ptr + t + 1) - tu.it0;
   tu.cap0 = tu.it0;
   tu.n_capu = 0;
+  tu.rot = 0;
   if (CAP && p.use_cap) {
     while (tu.n_capu < tu.n_items && ((ld_uniform(p.items + tu.it0 + tu.n_capu) >> 24) & SA_ITEM_CAPPED)) ++tu.n_capu;
     int n_skip = 0;
@@ -275,7 +277,8 @@ __device__ inline void tile_items(const A& p, int t, TileUnits& tu) {
   }
 }
 
-// REV visits the plan's blocks last to first (the diagonal block first).
+// REV visits the plan's blocks last to first (the diagonal block first);
+// otherwise from item tu.rot on, wrapping around.
 // ROWB: bytes per row of the compact arrays (capped keys, gathered rows).
 template <bool REV, int ROWB = D128 * 2, class A>
 __device__ inline Unit unit_at(const A& p, const TileUnits& tu, int u) {
@@ -308,7 +311,9 @@ __device__ inline Unit unit_at(const A& p, const TileUnits& tu, int u) {
     return x;
   }
   u -= tu.n_ch;
-  const int item = ld_uniform(p.items + tu.it0 + (REV ? tu.n_items - 1 - u : u));
+  int k = u + tu.rot;
+  if (k >= tu.n_items) k -= tu.n_items;
+  const int item = ld_uniform(p.items + tu.it0 + (REV ? tu.n_items - 1 - u : k));
   const int blk = item & 0xffffff;
   const int fl = item >> 24;
   x.kbase = tu.kb + (int64_t)blk * BK * tu.kst;

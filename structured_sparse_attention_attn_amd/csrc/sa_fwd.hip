@@ -122,6 +122,19 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16(FwdArgs p) {
   tu.ksb = static_cast<const char*>(p.ksep) + sep_off;
   tu.vsb = static_cast<const char*>(p.vsep) + sep_off;
   const int n_units = tu.n_capu + tu.n_ch + tu.n_items;
+  // Phase-aligned walk over the plan's blocks (not for ALiBi, which needs the
+  // diagonal first): the run of consecutive window blocks that ends at the
+  // tile's last item is entered so that the block visited at step s of the
+  // work group has index = s (mod n_items).  Neighbouring tiles of a head hold
+  // the same number of items and run at the same time on one XCD, so they read
+  // each window block within a few steps of one another, while it is in that
+  // XCD's L2, instead of two steps later per tile (which cycles a working set
+  // larger than the L2).
+  if (!ALIBI && tu.n_items > 1) {
+    const int b_last = ld_uniform(p.items + tu.it0 + tu.n_items - 1) & 0xffffff;
+    const int m = tu.n_items;
+    tu.rot = (2 * m - 1 - b_last % m + tu.n_ch % m) % m;  // block of step n_ch + u = n_ch + u (mod m)
+  }
   const float m2 = ALIBI ? alibi_slope_log2(p, hq) : 0.f;
   const float Lf = (float)p.L;
 
