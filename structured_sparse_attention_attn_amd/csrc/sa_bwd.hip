@@ -177,6 +177,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
   tu.ksb = static_cast<const char*>(p.ksep) + sep_off;
   tu.vsb = static_cast<const char*>(p.vsep) + sep_off;
   const int n_units = tu.n_capu + tu.n_ch + tu.n_items;
+  // the forward's phase-aligned walk over the window blocks (this kernel
+  // visits the capped units first): neighbouring tiles read a block together
+  if (!ALIBI && tu.n_items > 1) {
+    const int b_last = ld_uniform(p.items + tu.it0 + tu.n_items - 1) & 0xffffff;
+    const int m = tu.n_items;
+    tu.rot = (2 * m - 1 - b_last % m + (tu.n_capu + tu.n_ch) % m) % m;
+  }
   const float m2 = ALIBI ? alibi_slope_log2(p, hq) : 0.f;
   const float Lf = (float)p.L;
 
