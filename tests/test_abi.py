@@ -195,7 +195,7 @@ def test_fwd_workspace_and_validation():
 
 def test_topk_validation():
     lib = sa._lib
-    assert sa.sa_topk_workspace_bytes(8, 32768) == 8 * 32768 * 8
+    assert sa.sa_topk_workspace_bytes(8, 32768) == 8 * 32768 * (8 + 2)  # order keys + buckets
     args = [sa.SA_BF16, 8, 32768, 128, 1024, 256, 128, 512, None, 32768 * 128, 128, 768, None,
             None, None, 0, 0, 1024, 8 * 32768 * 8, None]
     for pos, val, code in [(4, 0, sa.SA_EINVAL), (4, 32769, sa.SA_EINVAL), (3, 96, sa.SA_EUNSUPPORTED),

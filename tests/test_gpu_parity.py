@@ -514,7 +514,8 @@ def test_topk_narrow_scores(sa, dtype):
 def test_topk_bitexact(sa, dtype):
     from structured_sparse_attention_attn_amd.pipeline import TopK
     for n_heads, pool_len, d, ks, seed in [(8, 32768, 128, (1, 1024, 32768), 1), (3, 1000, 64, (1, 7, 999, 1000), 2),
-                                           (2, 5000, 128, (100,), 3)]:
+                                           (2, 5000, 128, (100,), 3), (2, 40000, 128, (1, 333, 40000), 4),
+                                           (1, 70000, 64, (4096,), 5)]:
         q, kp, vp = W.make_pool_inputs(n_heads, pool_len, d, seed, dtype)
         if seed == 3:
             kp = (kp * 2).round() / 2  # coarse values: many exactly tied scores
