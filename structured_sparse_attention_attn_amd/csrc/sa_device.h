@@ -193,6 +193,14 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 __device__ inline uint4 ld16(const char* p) { return *reinterpret_cast<const uint4*>(p); }
 
+// A 16-byte load of data read once (queries): non-temporal, so it does not
+// push out of L2 the key and value rows that other work groups read again.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ inline uint4 ld16_once(const char* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // Loads of plan data that no kernel of this launch writes, through the scalar
 // data cache (uniform addresses, results in scalar registers).
 template <class T>
@@ -246,6 +254,7 @@ struct TileUnits {
   int it0, n_items, n_capu, n_ch, nsep;
   int cap0;            // index of the first capped item (the ordinary pass starts at it0)
   int rot;             // the ordinary items are visited from item rot on, wrapping (0: in order)
+  int chrev;           // the separator chunks are visited last to first
   const char* kb;      // dense keys of this (batch, kv head)
   const char* vb;
   int64_t kst, vst;
@@ -267,6 +276,7 @@ __device__ inline void tile_items(const A& p, int t, TileUnits& tu) {
   tu.cap0 = tu.it0;
   tu.n_capu = 0;
   tu.rot = 0;
+  tu.chrev = 0;
   if (CAP && p.use_cap) {
     while (tu.n_capu < tu.n_items && ((ld_uniform(p.items + tu.it0 + tu.n_capu) >> 24) & SA_ITEM_CAPPED)) ++tu.n_capu;
     int n_skip = 0;
@@ -299,7 +309,7 @@ __device__ inline Unit unit_at(const A& p, const TileUnits& tu, int u) {
   }
   u -= tu.n_capu;
   if (u < tu.n_ch) {
-    const int c0 = u * BK;
+    const int c0 = (tu.chrev ? tu.n_ch - 1 - u : u) * BK;
     x.kbase = tu.ksb + (int64_t)c0 * ROWB;
     x.kstride = ROWB;
     x.vbase = tu.vsb + (int64_t)c0 * ROWB;

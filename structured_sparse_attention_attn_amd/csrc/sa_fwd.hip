@@ -135,6 +135,12 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16(FwdArgs p) {
     const int m = tu.n_items;
     tu.rot = (2 * m - 1 - b_last % m + tu.n_ch % m) % m;  // block of step n_ch + u = n_ch + u (mod m)
   }
+  // Gathered separator chunks: every tile of a head reads the same rows, up
+  // to its own count.  The work groups an XCD runs at one time (about 64 of
+  // them: its 32 CUs, two each) read them together; the next such group of
+  // work groups walks them the other way, starting on the rows the previous
+  // one read last, which are the ones still in the XCD's L2.
+  tu.chrev = ((blockIdx.x >> 3) >> 6) & 1;
   const float m2 = ALIBI ? alibi_slope_log2(p, hq) : 0.f;
   const float Lf = (float)p.L;
 
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16(FwdArgs p) {
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
       uint4 x = make_uint4(0, 0, 0, 0);
-      if (qok) x = ld16(row + (16 * s + 8 * hl) * 2);
+      if (qok) x = ld16_once(row + (16 * s + 8 * hl) * 2);
       qf[s] = __builtin_bit_cast(bf16x8, x);
     }
   };
