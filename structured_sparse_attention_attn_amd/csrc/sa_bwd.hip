@@ -193,7 +193,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
       uint4 x = make_uint4(0, 0, 0, 0);
-      if (qok) x = ld16(row + (16 * s + 8 * hl) * 2);
+      if (qok) x = ld16_once(row + (16 * s + 8 * hl) * 2);  // read once per tile
       f[s] = __builtin_bit_cast(bf16x8, x);
     }
   };
@@ -409,6 +409,25 @@ __device__ inline int find_item(const BwdArgs& p, int t, int blk) {
   return -1;
 }
 
+// find_item for a per-lane tile (plain loads).
+__device__ inline int find_item_lane(const BwdArgs& p, int t, int blk) {
+  const int lo = p.tile_ptr[t], hi = p.tile_ptr[t + 1];
+  if (hi <= lo) return -1;
+  const int last = p.items[hi - 1] & 0xffffff;
+  const int iw = hi - 1 - (last - blk);
+  if (blk <= last && iw >= lo) {
+    const int it = p.items[iw];
+    if ((it & 0xffffff) == blk) return it;
+  }
+  if (blk < hi - lo) {
+    const int it = p.items[lo + blk];
+    if ((it & 0xffffff) == blk) return it;
+  }
+  return -1;
+}
+
+constexpr int TINFO_CAP = 2048;  // tiles the key-major kernel tabulates per group
+
 // One 64-row unit of a 128-key group (dense block, separator chunk or capped block).
 struct KeyUnit {
   const char* kbase;
@@ -433,6 +452,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p) {
   __shared__ __attribute__((aligned(16))) char Db1[BLK_BYTES];
   __shared__ __attribute__((aligned(16))) float LD0[2][64];
   __shared__ __attribute__((aligned(16))) float LD1[2][64];
+  // how each tile from t0 on reads the group (see unit_mk; built once below)
+  __shared__ int tinfo[TINFO_CAP];
+  __shared__ int tinfo_end;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
@@ -548,9 +570,71 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p) {
     int t, gq, ch;
     int mk0, mk1, cnt0, cnt1;
   };
+
+  int t0;
+  if (kind == G_SEP) t0 = first_gathering_tile(p, pi * 2 * BK);
+  else t0 = max(0, U0.key0 - (p.kind == SA_MASK_SEGMENT ? p.P : 0)) / TQ;
+
+  // The tiles from t0 on, evaluated once by all threads (each a few tiles,
+  // every plan read a plain per-lane load) into tinfo: the walk below then
+  // reads LDS instead of a chain of dependent scalar loads per tile.  A dense
+  // block's readers are consecutive: the first tile that reads neither unit
+  // ends the walk.  More than TINFO_CAP tiles: the scalar walk.
+  const bool use_tab = p.n_tiles - t0 <= TINFO_CAP;
+  if (use_tab) {
+    if (tid == 0) tinfo_end = p.n_tiles;
+    __syncthreads();
+    for (int t = t0 + tid; t < p.n_tiles; t += 512) {
+      int mk[2], cnt[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        const KeyUnit& u = x ? U1 : U0;
+        mk[x] = -1;
+        cnt[x] = 0;
+        if (u.valid <= 0) continue;
+        if (kind == G_SEP) {
+          cnt[x] = max(0, min(BK, p.sep_count[t] - u.idx * BK));
+          mk[x] = cnt[x] > 0 ? MK_COUNT : -1;
+          continue;
+        }
+        const int it = find_item_lane(p, t, u.idx);
+        if (it < 0) continue;
+        const int fl = it >> 24;
+        if (kind == G_CAP) {
+          mk[x] = (fl & SA_ITEM_CAPPED) ? MK_LCAP : -1;
+        } else if (p.use_cap && (fl & SA_ITEM_CAPPED)) {
+          mk[x] = (u.idx * BK + BK - 1 < t * TQ - p.L) ? -1 : MK_LNORM;
+        } else if (fl & SA_ITEM_FULL) {
+          mk[x] = MK_NONE;
+        } else {
+          mk[x] = p.kind == SA_MASK_SEPLLM ? MK_SEPLLM : (p.kind == SA_MASK_LAMBDA ? MK_LALL : MK_SEG);
+        }
+      }
+      tinfo[t - t0] = (mk[0] & 0xF) | ((mk[1] & 0xF) << 4) | (cnt[0] << 8) | (cnt[1] << 16);
+      if (kind == G_DENSE && mk[0] < 0 && mk[1] < 0) atomicMin(&tinfo_end, t);
+    }
+    __syncthreads();
+  }
+  const int t_end = use_tab ? tinfo_end : p.n_tiles;
+
   // first tile at or after t that reads the group (t = n_tiles when none)
   auto tile_from = [&](int t) -> Cur {
     Cur c{p.n_tiles, 0, 0, -1, -1, 0, 0};
+    if (use_tab) {
+      for (; t < t_end; ++t) {
+        const int v = __builtin_amdgcn_readfirstlane(tinfo[t - t0]);
+        const int m0 = (v & 0xF) == 0xF ? -1 : (v & 0xF), m1 = ((v >> 4) & 0xF) == 0xF ? -1 : ((v >> 4) & 0xF);
+        if (m0 >= 0 || m1 >= 0) {
+          c.t = t;
+          c.mk0 = m0;
+          c.mk1 = m1;
+          c.cnt0 = (v >> 8) & 0xFF;
+          c.cnt1 = (v >> 16) & 0xFF;
+          return c;
+        }
+      }
+      return c;
+    }
     for (; t < p.n_tiles; ++t) {
       int c0, c1;
       const int m0 = unit_mk(0, t, c0), m1 = unit_mk(1, t, c1);
@@ -566,10 +650,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p) {
     }
     return c;
   };
-
-  int t0;
-  if (kind == G_SEP) t0 = first_gathering_tile(p, pi * 2 * BK);
-  else t0 = max(0, U0.key0 - (p.kind == SA_MASK_SEGMENT ? p.P : 0)) / TQ;
 
   auto advance = [&](Cur c) -> Cur {
     ++c.ch;
