@@ -18,8 +18,6 @@
 //    ascending pool order with ties at T taken from the lowest indices.
 // 3. topk_gather: the selected keys' scores, and copies of the selected pool
 //    K/V rows into the prefix rows.
-#include <type_traits>
-
 #include "sa_common.h"
 
 namespace sa {
@@ -163,7 +161,7 @@ __device__ int block_excl_scan(int v, int* wave_tot, int* total) {
 // e, wave w holds indices 1024 e + 64 w + lane), then thread t counts the 32
 // bits of indices 32 t .. 32 t + 31 and one block scan gives every set bit its
 // slot.
-constexpr int KPT = 32;          // rounds per batch (and keys per thread when RESIDENT)
+constexpr int KPT = 32;          // rounds of 1024 indices per batch (32768 indices)
 constexpr int CAND_CAP = 2048;   // the exact ranking handles at most this many keys
 constexpr int NWAVE = SEL_THREADS / 64;
 // staged-bucket values past every bucket: a key of the threshold bucket once ranked
@@ -180,7 +178,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select(const unsigned long l
   __shared__ int sh_remaining, sh_count, sh_tidx, sh_bsel;
   __shared__ unsigned long long ckey[CAND_CAP];
   __shared__ int cidx[CAND_CAP];
-  __shared__ unsigned short sb[RESIDENT ? KPT * SEL_THREADS : 1];
+  __shared__ __attribute__((aligned(16))) unsigned short sb[RESIDENT ? KPT * SEL_THREADS : 1];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int h = blockIdx.x;
   const unsigned long long* keys = keys_all + (int64_t)h * n;
@@ -338,7 +336,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select(const unsigned long l
   // Slots in index order for the indices whose flag(e, j) holds: f(j, slot)
   // for each (flag is evaluated with j clamped to n - 1 past the end and then
   // discarded).
-  auto ordered = [&](auto res, auto&& flag, auto&& f) {
+  auto ordered = [&](auto&& flag, auto&& f) {
     int carry = 0;
     for (int j0 = 0; j0 < n; j0 += KPT * SEL_THREADS) {
       {
@@ -370,7 +368,7 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select(const unsigned long l
     if (tid == 0) sh_tidx = n;
     __syncthreads();
     const int rem = remaining;
-    ordered(std::false_type{}, [&](int, int j) { return (keys[j] & pmask) == prefix; },
+    ordered([&](int, int j) { return (keys[j] & pmask) == prefix; },
             [&](int j, int slot) {
               if (slot == rem - 1) sh_tidx = j;
             });
@@ -382,7 +380,6 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select(const unsigned long l
   auto emit = [&](int j, int slot) { idx[slot] = j; };  // scores: written by topk_gather
   if (fast) {
     ordered(
-        std::false_type{},
         [&](int e, int j) {
           const int b = bucket_at(e, j);
           if constexpr (RESIDENT) return b == MARK_TAKEN || (b < NBUCKET && b > bsel);
@@ -393,7 +390,6 @@ __global__ __launch_bounds__(SEL_THREADS) void topk_select(const unsigned long l
         emit);
   } else {
     ordered(
-        std::false_type{},
         [&](int, int j) {
           const unsigned long long m = keys[j] & pmask;
           return m > prefix || (m == prefix && j <= t_idx);
