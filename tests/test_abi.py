@@ -195,9 +195,13 @@ def test_fwd_workspace_and_validation():
 
 def test_topk_validation():
     lib = sa._lib
-    assert sa.sa_topk_workspace_bytes(8, 32768) == 8 * 32768 * (8 + 2)  # order keys + buckets
+    # 256-byte alignment slack, order keys, buckets, maxima of 16 buckets
+    ws = 256 + 8 * 32768 * 8 + 8 * 32768 * 2 + 8 * 2048 * 2
+    assert sa.sa_topk_workspace_bytes(8, 32768) == ws
+    # rows padded to 64 entries per head, each section to 256 bytes
+    assert sa.sa_topk_workspace_bytes(3, 100) == 256 + 3 * 128 * 8 + 3 * 128 * 2 + 256
     args = [sa.SA_BF16, 8, 32768, 128, 1024, 256, 128, 512, None, 32768 * 128, 128, 768, None,
-            None, None, 0, 0, 1024, 8 * 32768 * 8, None]
+            None, None, 0, 0, 1024, ws, None]
     for pos, val, code in [(4, 0, sa.SA_EINVAL), (4, 32769, sa.SA_EINVAL), (3, 96, sa.SA_EUNSUPPORTED),
                            (0, 3, sa.SA_EINVAL), (18, 100, sa.SA_ENOSPACE), (5, None, sa.SA_EINVAL)]:
         a = list(args)
