@@ -538,6 +538,39 @@ def test_topk_bitexact(sa, dtype):
                 assert torch.equal(pv[h].cpu(), vp[h][torch.from_numpy(ri).long()])
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_topk_shapes(sa, dtype):
+    """Shapes at the edges of the selection's work split: a pool of 33 keys
+    (3 groups of 16; k below, at and above the group count), 300 heads (one
+    work group each), k equal to the group count and one more (the lower
+    bound from the group maxima used, then not), one key past a single pass
+    over the head's buckets, and a pool length that is not a multiple of 8."""
+    from structured_sparse_attention_attn_amd.pipeline import TopK
+    for n_heads, pool_len, d, ks, seed in [(1, 33, 64, (1, 2, 3, 33), 21), (300, 100, 64, (7,), 22),
+                                           (2, 2048, 128, (128, 129), 23), (2, 32769, 128, (1000,), 24),
+                                           (4, 4100, 128, (2050,), 25)]:
+        log(f"topk shapes {dtype}: heads {n_heads} pool {pool_len} d {d} k {ks}")
+        q, kp, vp = W.make_pool_inputs(n_heads, pool_len, d, seed, dtype)
+        qd, kd, vd = q.cuda(), kp.cuda(), vp.cuda()
+        topk = TopK(n_heads, pool_len)
+        for k in ks:
+            idx = torch.empty((n_heads, k), dtype=torch.int32, device="cuda")
+            score = torch.empty((n_heads, k), dtype=torch.float64, device="cuda")
+            pk = torch.zeros((n_heads, k, d), dtype=dtype, device="cuda")
+            pv = torch.zeros_like(pk)
+            topk(qd, kd, k, idx, score=score, pool_v=vd, pref_k=pk, pref_v=pv)
+            torch.cuda.synchronize()
+            got_i, got_s = idx.cpu().numpy(), score.cpu().numpy()
+            for h in range(n_heads):
+                s_ = O.topk_scores(q[h].double().numpy(), kp[h].double().numpy())
+                ri = O.topk_select(s_, k)
+                np.testing.assert_array_equal(got_i[h], ri)
+                np.testing.assert_array_equal(got_s[h], s_[ri])
+            sel = torch.from_numpy(got_i).long()
+            assert torch.equal(pk.cpu(), torch.gather(kp, 1, sel[:, :, None].expand(-1, -1, d)))
+            assert torch.equal(pv.cpu(), torch.gather(vp, 1, sel[:, :, None].expand(-1, -1, d)))
+
+
 # Several segments end to end: forward, tail carry, pool append, retrieval by the
 # segment-end query (segmented-execution page, overall framework), against the oracle's
 # segment recurrence.
