@@ -312,8 +312,8 @@ struct Held {
 
 // Partial softmax of the group's queries over 64 held slots: (m, l, o) per
 // query head in base 2, over 64 consecutive physical slots (the held ones
-// among them).  Every K and V byte of the slots is requested first, before
-// the counters say which slots are held: thread (slot r, quarter qq) holds a
+// among them).  Every K and V byte of the slots, and the group's queries, are
+// requested first, before the counters say which slots are held: thread (slot r, quarter qq) holds a
 // quarter of r's key for the logits; thread (slot group sg, column chunk cc)
 // holds columns 8 cc .. +7 of the values of slots 4 sg .. 4 sg + 3 for the
 // weighted sum, reduced over the 16 slot groups by shuffles within a wave and
@@ -346,6 +346,14 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
   for (int i = 0; i < 4; ++i) {
     const int rr = 4 * sg + i;
     vx4[i] = *reinterpret_cast<const uint4*>(V + (int64_t)(v0 + (rr < nslot ? rr : 0)) * 256 + cc * 16);
+  }
+  // the group's rotated queries (up to MAX_G * 128 floats: 4 per thread),
+  // requested with the rows
+  float qv[MAX_G * 128 / 256];
+#pragma unroll
+  for (int i = 0; i < MAX_G * 128 / 256; ++i) {
+    const int e = tid + 256 * i;
+    qv[i] = e < p.group * 128 ? p.qrot[((int64_t)b * p.h_q + g * p.group + (e >> 7)) * 128 + (e & 127)] : 0.f;
   }
   // the held ranges after this step, from the counters before it (they are
   // updated by decode_combine, after every read of them in this step)
@@ -389,8 +397,11 @@ __global__ __launch_bounds__(256) void decode_attn(StreamArgs p) {
     const int rr = 4 * sg + i;
     if (!((rr < nslot) && held(v0 + rr))) vx4[i] = make_uint4(0, 0, 0, 0);
   }
-  for (int e = tid; e < p.group * 128; e += 256)
-    qs[e >> 7][e & 127] = p.qrot[((int64_t)b * p.h_q + g * p.group + (e >> 7)) * 128 + (e & 127)];
+#pragma unroll
+  for (int i = 0; i < MAX_G * 128 / 256; ++i) {
+    const int e = tid + 256 * i;
+    if (e < p.group * 128) qs[e >> 7][e & 127] = qv[i];
+  }
   __syncthreads();
   // logits (bf16 elements widened where they are used: fewer live registers)
   {
