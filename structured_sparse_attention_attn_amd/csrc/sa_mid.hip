@@ -47,6 +47,7 @@ template <int KMID_MAX>
 __global__ __launch_bounds__(256, KMID_MAX <= 16 ? 2 : 1) void mid_select(MidArgs p) {
   __shared__ __attribute__((aligned(16))) char K0[BLK_BYTES];
   __shared__ __attribute__((aligned(16))) char K1[BLK_BYTES];
+  __shared__ float scr[32 * 256];  // a block's scores, thread t's in column t
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
@@ -98,15 +99,19 @@ __global__ __launch_bounds__(256, KMID_MAX <= 16 ? 2 : 1) void mid_select(MidArg
   const int blk_hi = j_hi >= p.n_s ? j_hi / BK : blk_lo - 1;
   const int n_blk = blk_hi - blk_lo + 1;
 
+  // The lane's list, best first: its last kk slots hold the selection; the
+  // KMID_MAX - kk slots before them hold sentinels (+inf, index -1) that
+  // nothing displaces, so the kk-th best is always the last slot.
+  const int kk = p.kmid;
+  const int pad = KMID_MAX - kk;
   float bv[KMID_MAX];
   int bi[KMID_MAX];
 #pragma unroll
   for (int e = 0; e < KMID_MAX; ++e) {
-    bv[e] = -__builtin_huge_valf();
-    bi[e] = 0x7fffffff;
+    bv[e] = e < pad ? __builtin_huge_valf() : -__builtin_huge_valf();
+    bi[e] = e < pad ? -1 : 0x7fffffff;
   }
-  const int kk = p.kmid;
-  float thr_v = -__builtin_huge_valf();  // the kk-th best so far
+  float thr_v = -__builtin_huge_valf();  // the kk-th best so far (the last slot)
   int thr_i = 0x7fffffff;
   const char* kb = p.k + (b * p.ksB + kvh * p.ksH) * 2;
   const int64_t kst = p.ksT * 2;
@@ -144,10 +149,12 @@ __global__ __launch_bounds__(256, KMID_MAX <= 16 ? 2 : 1) void mid_select(MidArg
     // candidates: register r of half mb is key j0 + 32 mb + 8 (r / 4) + r % 4,
     // so register order is ascending key order.  Keys that are not middle keys
     // of the lane's query are set to -inf (only blocks at the edges of the
-    // wave's middle range have any).  Then, while the block's largest score
-    // beats the lane's k-th best, its first (lowest-index) occurrence is
-    // inserted and removed; once the first occurrence of the maximum fails,
-    // every remaining key fails too.  All of it branch-free per lane.
+    // wave's middle range have any).  The scores go to the lane's column of
+    // LDS and the lane marks those at or above its k-th best (bit 16 mb + r);
+    // the marked ones are then taken in ascending key order, each read back
+    // from LDS and inserted while it still beats the (rising) k-th best.  A
+    // score below the k-th best at the block's start can never enter, so the
+    // lists end as if every key had been offered in turn.
     const int j0 = blk * BK + 4 * hl;
     if (!(blk * BK >= p.n_s && blk * BK + BK - 1 <= wave_jmin && blk * BK + BK <= p.n_k && wave_full)) {
 #pragma unroll
@@ -159,35 +166,26 @@ __global__ __launch_bounds__(256, KMID_MAX <= 16 ? 2 : 1) void mid_select(MidArg
           s[mb][r] = ok ? s[mb][r] : -__builtin_huge_valf();
         }
     }
-    auto block_max = [&]() {
-      float mx = s[0][0];
+    unsigned hitm = 0u;
+    const float lo = fmaxf(thr_v, -__FLT_MAX__);  // (excludes -inf while the list is not full)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
-      return mx;
-    };
-    float mx = block_max();
-    bool act = (mx != -__builtin_huge_valf()) & (mx >= thr_v);
-    while (__any(act)) {
-      if (act) {
-        bool found = false;
-        int jc = 0;
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bool hit = !found & (s[mb][r] == mx);
-            jc = hit ? j0 + 32 * mb + 8 * (r >> 2) + (r & 3) : jc;
-            s[mb][r] = hit ? -__builtin_huge_valf() : s[mb][r];
-            found = found | hit;
-          }
-        if (better(mx, jc, thr_v, thr_i)) {
-          float x = mx;
-          int j = jc;
+      for (int r = 0; r < 16; ++r) {
+        const float x = s[mb][r];
+        scr[(16 * mb + r) * 256 + tid] = x;
+        hitm |= x >= lo ? (1u << (16 * mb + r)) : 0u;
+      }
+    while (__any(hitm != 0u)) {
+      if (hitm != 0u) {
+        const int bit = __ffs(hitm) - 1;
+        hitm &= hitm - 1u;
+        float x = scr[bit * 256 + tid];
+        int j = j0 + 32 * (bit >> 4) + 8 * ((bit & 15) >> 2) + (bit & 3);
+        if (better(x, j, thr_v, thr_i)) {
 #pragma unroll
           for (int e = 0; e < KMID_MAX; ++e) {
-            const bool sw = (e < kk) & better(x, j, bv[e], bi[e]);
+            const bool sw = better(x, j, bv[e], bi[e]);
             const float tv = bv[e];
             const int ti = bi[e];
             bv[e] = sw ? x : tv;
@@ -195,16 +193,8 @@ __global__ __launch_bounds__(256, KMID_MAX <= 16 ? 2 : 1) void mid_select(MidArg
             x = sw ? tv : x;
             j = sw ? ti : j;
           }
-#pragma unroll
-          for (int e = 0; e < KMID_MAX; ++e)
-            if (e == kk - 1) {
-              thr_v = bv[e];
-              thr_i = bi[e];
-            }
-          mx = block_max();
-          act = (mx != -__builtin_huge_valf()) & (mx >= thr_v);
-        } else {
-          act = false;
+          thr_v = bv[KMID_MAX - 1];
+          thr_i = bi[KMID_MAX - 1];
         }
       }
     }
@@ -223,10 +213,10 @@ __global__ __launch_bounds__(256, KMID_MAX <= 16 ? 2 : 1) void mid_select(MidArg
   for (int e2 = 0; e2 < KMID_MAX; ++e2) {
     float x = __shfl_xor(bv[e2], 32);
     int j = __shfl_xor(bi[e2], 32);
-    if (hl == 0 && e2 < kk && x != -__builtin_huge_valf()) {
+    if (hl == 0 && e2 >= pad && x != -__builtin_huge_valf()) {
 #pragma unroll
       for (int e = 0; e < KMID_MAX; ++e) {
-        if (e < kk && better(x, j, bv[e], bi[e])) {
+        if (better(x, j, bv[e], bi[e])) {
           const float tv = bv[e];
           const int ti = bi[e];
           bv[e] = x;
@@ -241,10 +231,10 @@ __global__ __launch_bounds__(256, KMID_MAX <= 16 ? 2 : 1) void mid_select(MidArg
     const int64_t rowi = ((int64_t)b * p.h_q + hq) * p.n_q + qi;
 #pragma unroll
     for (int e = 0; e < KMID_MAX; ++e) {
-      if (e < kk) {
+      if (e >= pad) {
         const bool has = bv[e] != -__builtin_huge_valf();
-        p.sel[rowi * kk + e] = has ? bi[e] : -1;
-        p.score[rowi * kk + e] = bv[e];
+        p.sel[rowi * kk + e - pad] = has ? bi[e] : -1;
+        p.score[rowi * kk + e - pad] = bv[e];
       }
     }
   }
