@@ -1167,6 +1167,34 @@ def test_topk_middle_repeat_and_canary(sa):
         assert torch.equal(a, b)
 
 
+def test_topk_repeat_and_canary(sa):
+    """topk_retrieve twice on a workspace refilled with arbitrary bytes in
+    between: the same indices, scores and copied rows bit for bit, and no write
+    outside idx, score or the prefix rows (guard regions around each)."""
+    from structured_sparse_attention_attn_amd.pipeline import TopK
+    H, n, d, k = 4, 4100, 128, 1500
+    q, kp, vp = W.make_pool_inputs(H, n, d, 830, torch.bfloat16)
+    qd, kd, vd = q.cuda(), kp.cuda(), vp.cuda()
+    topk = TopK(H, n)
+    g = torch.Generator(device="cuda").manual_seed(831)
+    outs = []
+    for rep in range(2):
+        topk.ws.copy_(torch.randint(0, 256, topk.ws.shape, generator=g, device="cuda", dtype=torch.int32)
+                      .to(torch.uint8))
+        si, idx = _guarded((H, k), torch.int32, fill=7)
+        ss, score = _guarded((H, k), torch.float64)
+        sk, pk = _guarded((H, k, d), torch.bfloat16)
+        sv, pv = _guarded((H, k, d), torch.bfloat16)
+        topk(qd, kd, k, idx, score=score, pool_v=vd, pref_k=pk, pref_v=pv)
+        torch.cuda.synchronize()
+        assert _guards_intact(si, fill=7) and all(_guards_intact(x) for x in (ss, sk, sv)), rep
+        outs.append((idx.clone(), score.clone(), pk.clone(), pv.clone()))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b)
+    ri = O.topk_select(O.topk_scores(q[1].double().numpy(), kp[1].double().numpy()), k)
+    np.testing.assert_array_equal(outs[0][0][1].cpu().numpy(), ri)
+
+
 @pytest.mark.parametrize("kind", ["sepllm", "lambda"])
 def test_decode_repeat_and_canary(sa, kind):
     from structured_sparse_attention_attn_amd.pipeline import StreamDecoder
