@@ -544,11 +544,13 @@ def test_topk_shapes(sa, dtype):
     (3 groups of 16; k below, at and above the group count), 300 heads (one
     work group each), k equal to the group count and one more (the lower
     bound from the group maxima used, then not), one key past a single pass
-    over the head's buckets, and a pool length that is not a multiple of 8."""
+    over the head's buckets, a pool length that is not a multiple of 8, and a
+    bound so low that the list of keys above it overflows (k = 2000 of 2048
+    group maxima)."""
     from structured_sparse_attention_attn_amd.pipeline import TopK
     for n_heads, pool_len, d, ks, seed in [(1, 33, 64, (1, 2, 3, 33), 21), (300, 100, 64, (7,), 22),
                                            (2, 2048, 128, (128, 129), 23), (2, 32769, 128, (1000,), 24),
-                                           (4, 4100, 128, (2050,), 25)]:
+                                           (4, 4100, 128, (2050,), 25), (2, 32768, 128, (2000,), 26)]:
         log(f"topk shapes {dtype}: heads {n_heads} pool {pool_len} d {d} k {ks}")
         q, kp, vp = W.make_pool_inputs(n_heads, pool_len, d, seed, dtype)
         qd, kd, vd = q.cuda(), kp.cuda(), vp.cuda()
