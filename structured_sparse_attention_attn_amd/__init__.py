@@ -287,12 +287,43 @@ def topk_retrieve(q_score, pool_k, k: int, idx, ws, *, score=None, pool_v=None, 
     """Top-k pool rows per head (see include/sparse_attn.h).
 
     q_score [n_heads, d] (row stride free, d contiguous); pool_k / pool_v
-    [n_heads, pool_len, d]; idx int32 [n_heads, k]; score float64 [n_heads, k]
-    or None; pref_k / pref_v [n_heads, >=k, d] views receiving the rows.
+    [n_heads, pool_len, d] with equal strides; idx int32 [n_heads, k]; score
+    float64 [n_heads, k] or None; pref_k / pref_v [n_heads, >=k, d] views with
+    equal strides receiving the rows.  Shapes, dtypes, devices and those
+    strides are checked here (ValueError); the C ABI checks the rest.
     """
     import torch
+    if pool_k.dim() != 3 or pool_k.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("pool_k: must be a float32 or bfloat16 tensor [n_heads, pool_len, d]")
     dtype = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}[pool_k.dtype]
     n_heads, pool_len, d = pool_k.shape
+    dev = pool_k.device
+    if pool_k.stride(-1) != 1:
+        raise ValueError("pool_k: last dimension must be contiguous")
+    if q_score.dim() != 2 or tuple(q_score.shape) != (n_heads, d) or q_score.dtype != pool_k.dtype \
+            or q_score.stride(-1) != 1:
+        raise ValueError(f"q_score: must be a {pool_k.dtype} tensor [{n_heads}, {d}] with contiguous rows")
+    outs = [("idx", idx, torch.int32)] + ([("score", score, torch.float64)] if score is not None else [])
+    for name, t, dt in outs:
+        if tuple(t.shape) != (n_heads, k) or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name}: must be a contiguous {dt} tensor of shape {(n_heads, k)}")
+    if pool_v is not None:
+        if tuple(pool_v.shape) != tuple(pool_k.shape) or pool_v.dtype != pool_k.dtype \
+                or pool_v.stride() != pool_k.stride():
+            raise ValueError("pool_v: must match pool_k in shape, dtype and strides")
+        if pref_k is None or pref_v is None:
+            raise ValueError("pref_k and pref_v are required with pool_v")
+        for name, t in (("pref_k", pref_k), ("pref_v", pref_v)):
+            if t.dim() != 3 or t.shape[0] != n_heads or t.shape[1] < k or t.shape[2] != d \
+                    or t.dtype != pool_k.dtype or t.stride(-1) != 1:
+                raise ValueError(f"{name}: must be a {pool_k.dtype} tensor [{n_heads}, >= {k}, {d}] "
+                                 "with contiguous rows")
+        if pref_v.stride() != pref_k.stride():
+            raise ValueError("pref_v: must have pref_k's strides")
+    for name, t in (("q_score", q_score), ("idx", idx), ("score", score), ("pool_v", pool_v),
+                    ("pref_k", pref_k), ("pref_v", pref_v), ("ws", ws)):
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name}: device {t.device}, expected {dev}")
     prs = pref_k.stride() if pref_k is not None else (0, 0, 1)
     _check(_lib.topk_retrieve(dtype, n_heads, pool_len, d, k, _ptr(q_score), q_score.stride(0),
                               _ptr(pool_k), _ptr(pool_v), pool_k.stride(0), pool_k.stride(1),

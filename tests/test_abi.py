@@ -213,6 +213,43 @@ def test_topk_validation():
     assert lib.topk_retrieve(*a) == sa.SA_EINVAL
 
 
+def test_topk_binding_rejects_mismatched_tensors():
+    # checked in the binding before the C call (CPU tensors: no device is touched)
+    import torch
+    H, n, d, k = 3, 500, 64, 10
+    bf = torch.bfloat16
+    pk, pv = torch.zeros(H, n, d, dtype=bf), torch.zeros(H, n, d, dtype=bf)
+    q = torch.zeros(H, d, dtype=bf)
+    idx, score = torch.zeros(H, k, dtype=torch.int32), torch.zeros(H, k, dtype=torch.float64)
+    rk, rv = torch.zeros(H, k, d, dtype=bf), torch.zeros(H, k, d, dtype=bf)
+    ws = torch.zeros(sa.sa_topk_workspace_bytes(H, n), dtype=torch.uint8)
+    good = dict(score=score, pool_v=pv, pref_k=rk, pref_v=rv)
+
+    def call(q_=q, pk_=pk, idx_=idx, **kw):
+        args = dict(good)
+        args.update(kw)
+        sa.topk_retrieve(q_, pk_, k, idx_, ws, **args)
+
+    bad = [
+        dict(pk_=torch.zeros(H, n, d, dtype=torch.float16)),          # dtype
+        dict(pk_=torch.zeros(n, d, dtype=bf)),                        # rank
+        dict(q_=torch.zeros(H + 1, d, dtype=bf)),                     # query rows
+        dict(q_=torch.zeros(H, d, dtype=torch.float32)),              # query dtype
+        dict(idx_=torch.zeros(H, k - 1, dtype=torch.int32)),          # short idx
+        dict(idx_=torch.zeros(H, k, dtype=torch.int64)),              # idx dtype
+        dict(idx_=torch.zeros(k, H, dtype=torch.int32).t()),          # not contiguous
+        dict(score=torch.zeros(H, k, dtype=torch.float32)),           # score dtype
+        dict(pool_v=torch.zeros(H, n + 1, d, dtype=bf)),              # pool_v shape
+        dict(pool_v=torch.zeros(H, d, n, dtype=bf).transpose(1, 2)),  # pool_v strides
+        dict(pref_k=None),                                            # rows without a destination
+        dict(pref_k=torch.zeros(H, k - 1, d, dtype=bf)),              # too few prefix rows
+        dict(pref_v=torch.zeros(H, k + 5, d, dtype=bf)),              # pref_v strides differ
+    ]
+    for case in bad:
+        with pytest.raises(ValueError):
+            call(**case)
+
+
 def test_import_fails_loudly_without_library(tmp_path):
     # a copy of the binding next to no library must refuse to import
     pkg = tmp_path / "sa_copy"
