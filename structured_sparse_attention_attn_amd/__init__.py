@@ -139,6 +139,10 @@ def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 def _stream(stream) -> Optional[int]:
     if stream is not None:
         return stream
@@ -167,14 +171,14 @@ def sa_plan_bytes(m: sa_mask_t) -> int:
 
 def sparse_attn_plan(m: sa_mask_t, plan, stream=None) -> None:
     """Enqueue the plan kernels for mask m into the uint8 device tensor `plan`."""
-    _check(_lib.sparse_attn_plan(ctypes.byref(m), _ptr(plan), plan.numel(), _stream(stream)))
+    _check(_lib.sparse_attn_plan(ctypes.byref(m), _ptr(plan), _nbytes(plan), _stream(stream)))
 
 
 def sa_plan_status(plan, stream=None) -> sa_plan_header_t:
     """Wait for the plan's stream and return its header; raises SparseAttnError (SA_ENOSPACE)
     when the mask held more separators than the plan's sep_max bound lets it list."""
     out = sa_plan_header_t()
-    _check(_lib.sa_plan_status(_ptr(plan), plan.numel(), _stream(stream), ctypes.byref(out)))
+    _check(_lib.sa_plan_status(_ptr(plan), _nbytes(plan), _stream(stream), ctypes.byref(out)))
     return out
 
 
@@ -257,22 +261,22 @@ def sa_fwd_workspace_layout(m: sa_mask_t, args: sa_fwd_args_t) -> sa_fwd_ws_layo
 
 def sparse_attn_fwd(m: sa_mask_t, plan, args: sa_fwd_args_t, ws, stream=None) -> None:
     """Enqueue the RoPE stage and the fused forward (see include/sparse_attn.h)."""
-    _check(_lib.sparse_attn_fwd(ctypes.byref(m), _ptr(plan), plan.numel(), ctypes.byref(args),
-                                _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+    _check(_lib.sparse_attn_fwd(ctypes.byref(m), _ptr(plan), _nbytes(plan), ctypes.byref(args),
+                                _ptr(ws), _nbytes(ws),
                                 _stream(stream)))
 
 
 def sparse_attn_rope(m: sa_mask_t, plan, args: sa_fwd_args_t, ws, stream=None) -> None:
     """Enqueue only the RoPE stage of sparse_attn_fwd."""
-    _check(_lib.sparse_attn_rope(ctypes.byref(m), _ptr(plan), plan.numel(), ctypes.byref(args),
-                                 _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+    _check(_lib.sparse_attn_rope(ctypes.byref(m), _ptr(plan), _nbytes(plan), ctypes.byref(args),
+                                 _ptr(ws), _nbytes(ws),
                                  _stream(stream)))
 
 
 def sparse_attn_attend(m: sa_mask_t, plan, args: sa_fwd_args_t, ws, stream=None) -> None:
     """Enqueue only the fused forward of sparse_attn_fwd (after sparse_attn_rope)."""
-    _check(_lib.sparse_attn_attend(ctypes.byref(m), _ptr(plan), plan.numel(), ctypes.byref(args),
-                                   _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+    _check(_lib.sparse_attn_attend(ctypes.byref(m), _ptr(plan), _nbytes(plan), ctypes.byref(args),
+                                   _ptr(ws), _nbytes(ws),
                                    _stream(stream)))
 
 
@@ -328,7 +332,7 @@ def topk_retrieve(q_score, pool_k, k: int, idx, ws, *, score=None, pool_v=None, 
     _check(_lib.topk_retrieve(dtype, n_heads, pool_len, d, k, _ptr(q_score), q_score.stride(0),
                               _ptr(pool_k), _ptr(pool_v), pool_k.stride(0), pool_k.stride(1),
                               _ptr(idx), _ptr(score), _ptr(pref_k), _ptr(pref_v), prs[0], prs[1],
-                              _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+                              _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def plan_to_host(m: sa_mask_t, plan) -> dict:
@@ -405,9 +409,9 @@ def sa_bwd_workspace_bytes(m: sa_mask_t, args: sa_fwd_args_t) -> int:
 def sparse_attn_bwd(m: sa_mask_t, plan, args: sa_fwd_args_t, grads: sa_bwd_args_t, ws,
                     stream=None) -> None:
     """Enqueue the backward (see include/sparse_attn.h)."""
-    _check(_lib.sparse_attn_bwd(ctypes.byref(m), _ptr(plan), plan.numel(), ctypes.byref(args),
+    _check(_lib.sparse_attn_bwd(ctypes.byref(m), _ptr(plan), _nbytes(plan), ctypes.byref(args),
                                 ctypes.byref(grads), _ptr(ws),
-                                0 if ws is None else ws.numel() * ws.element_size(),
+                                _nbytes(ws),
                                 _stream(stream)))
 
 
@@ -440,30 +444,48 @@ def sa_stream_layout(cfg: sa_stream_cfg_t):
 
 
 def sparse_attn_stream_reset(cfg: sa_stream_cfg_t, state, stream=None) -> None:
-    _check(_lib.sparse_attn_stream_reset(ctypes.byref(cfg), _ptr(state), state.numel(), _stream(stream)))
+    _check(_lib.sparse_attn_stream_reset(ctypes.byref(cfg), _ptr(state), _nbytes(state), _stream(stream)))
+
+
+def _check_decode(cfg: sa_stream_cfg_t, state, q, k, v, is_sep, o, lse, ws=None) -> None:
+    """The decode step's tensors against its configuration: q, o bf16 [B, h_q, d];
+    k, v bf16 [B, h_kv, d]; is_sep uint8 [B] (None allowed for the LM-Infinite
+    cache; the C ABI requires it for SepLLM); lse fp32 [B, h_q] or None; all
+    contiguous and on the state's device (ValueError otherwise)."""
+    import torch
+    B, hq, hkv, d = cfg.batch, cfg.h_q, cfg.h_kv, cfg.d
+    want = [("q", q, (B, hq, d), torch.bfloat16), ("k", k, (B, hkv, d), torch.bfloat16),
+            ("v", v, (B, hkv, d), torch.bfloat16), ("o", o, (B, hq, d), torch.bfloat16)]
+    if is_sep is not None:
+        want.append(("is_sep", is_sep, (B,), torch.uint8))
+    if lse is not None:
+        want.append(("lse", lse, (B, hq), torch.float32))
+    for name, t, shape, dt in want:
+        if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name}: must be a contiguous {dt} tensor of shape {shape} "
+                             f"(got {tuple(t.shape)}, {t.dtype})")
+    for name, t in [(w[0], w[1]) for w in want] + [("ws", ws)]:
+        if t is not None and t.device != state.device:
+            raise ValueError(f"{name}: device {t.device}, expected {state.device}")
 
 
 def sparse_attn_decode_step(cfg: sa_stream_cfg_t, state, q, k, v, is_sep, o, ws, lse=None,
                             stream=None) -> None:
     """One decode step (see include/sparse_attn.h): q [B,h_q,d], k, v [B,h_kv,d], is_sep uint8 [B]."""
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    _check(_lib.sparse_attn_decode_step(ctypes.byref(cfg), _ptr(state), state.numel(), _ptr(q), _ptr(k),
-                                        _ptr(v), _ptr(is_sep), _ptr(o), _ptr(lse), _ptr(ws),
-                                        ws.numel(), _stream(stream)))
+    _check_decode(cfg, state, q, k, v, is_sep, o, lse, ws)
+    _check(_lib.sparse_attn_decode_step(ctypes.byref(cfg), _ptr(state), _nbytes(state),
+                                        _ptr(q), _ptr(k), _ptr(v), _ptr(is_sep), _ptr(o), _ptr(lse),
+                                        _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def sparse_attn_decode_step_static(cfg: sa_stream_cfg_t, state, q, k, v, is_sep, o, lse=None,
                                    stream=None) -> None:
     """The decode step with the library's static scratch instead of a workspace (see
     include/sparse_attn.h): it allocates nothing."""
-    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    _check(_lib.sparse_attn_decode_step_static(ctypes.byref(cfg), _ptr(state), state.numel(), _ptr(q),
-                                               _ptr(k), _ptr(v), _ptr(is_sep), _ptr(o), _ptr(lse),
-                                               _stream(stream)))
+    _check_decode(cfg, state, q, k, v, is_sep, o, lse)
+    _check(_lib.sparse_attn_decode_step_static(ctypes.byref(cfg), _ptr(state),
+                                               _nbytes(state), _ptr(q), _ptr(k),
+                                               _ptr(v), _ptr(is_sep), _ptr(o), _ptr(lse), _stream(stream)))
 
 
 def sparse_attn_topk_middle(m: sa_mask_t, args: sa_fwd_args_t, k_mid: int, sel, score, stream=None) -> None:

@@ -250,6 +250,31 @@ def test_topk_binding_rejects_mismatched_tensors():
             call(**case)
 
 
+def test_decode_binding_rejects_mismatched_tensors():
+    # checked in the binding before the C call (CPU tensors: no device is touched)
+    import torch
+    B, hq, hkv, d = 2, 8, 2, 128
+    cfg = sa.stream_cfg(B, hq, hkv, d, 4, 8, 16, 60, rope_base=10000.0)
+    state = torch.zeros(64, dtype=torch.uint8)
+    bf = torch.bfloat16
+    good = dict(q=torch.zeros(B, hq, d, dtype=bf), k=torch.zeros(B, hkv, d, dtype=bf),
+                v=torch.zeros(B, hkv, d, dtype=bf), is_sep=torch.zeros(B, dtype=torch.uint8),
+                o=torch.zeros(B, hq, d, dtype=bf), lse=torch.zeros(B, hq))
+    bad = [dict(q=torch.zeros(B, hq + 1, d, dtype=bf)), dict(q=torch.zeros(B, hq, d)),
+           dict(k=torch.zeros(B, hq, d, dtype=bf)), dict(v=torch.zeros(B, hkv, d, dtype=torch.float16)),
+           dict(is_sep=torch.zeros(B, dtype=torch.int32)), dict(o=torch.zeros(B, d, hq, dtype=bf).transpose(1, 2)),
+           dict(lse=torch.zeros(B, hq, dtype=torch.float64)), dict(lse=torch.zeros(B + 1, hq))]
+    for case in bad:
+        t = dict(good)
+        t.update(case)
+        with pytest.raises(ValueError):
+            sa.sparse_attn_decode_step(cfg, state, t["q"], t["k"], t["v"], t["is_sep"], t["o"], state,
+                                       lse=t["lse"])
+        with pytest.raises(ValueError):
+            sa.sparse_attn_decode_step_static(cfg, state, t["q"], t["k"], t["v"], t["is_sep"], t["o"],
+                                              lse=t["lse"])
+
+
 def test_import_fails_loudly_without_library(tmp_path):
     # a copy of the binding next to no library must refuse to import
     pkg = tmp_path / "sa_copy"

@@ -75,6 +75,7 @@ def test_static_decode_rejects_oversized_config(sa):
     state = torch.empty(sa.sa_stream_state_bytes(cfg), dtype=torch.uint8, device="cuda")
     x = torch.zeros((64, 32, 128), dtype=torch.bfloat16, device="cuda")
     kv = torch.zeros((64, 8, 128), dtype=torch.bfloat16, device="cuda")
+    is_sep = torch.zeros(64, dtype=torch.uint8, device="cuda")
     with pytest.raises(sa.SparseAttnError) as e:
-        sa.sparse_attn_decode_step_static(cfg, state, x, kv, kv, None, x)
+        sa.sparse_attn_decode_step_static(cfg, state, x, kv, kv, is_sep, x)
     assert e.value.code == sa.SA_ENOSPACE
