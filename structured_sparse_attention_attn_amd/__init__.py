@@ -365,8 +365,23 @@ def sparse_attn_segment_carry(k, v, n_local: int, prefix_len: int, seg_len: int,
     pool_k / pool_v [n_heads - n_local, pool_cap, d] or None (d contiguous everywhere).
     """
     import torch
+    if k.dim() != 3 or k.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("k: must be a float32 or bfloat16 tensor [n_heads, prefix_len + seg_len, d]")
     dtype = {torch.float32: SA_F32, torch.bfloat16: SA_BF16}[k.dtype]
-    n_heads, _, d = k.shape
+    n_heads, rows, d = k.shape
+    if rows < prefix_len + seg_len:
+        raise ValueError(f"k, v: {rows} rows per head, the segment needs {prefix_len + seg_len}")
+    keep = min(tail_len, prefix_len + seg_len)
+    n_long = n_heads - n_local
+    for name, t, h, r in (("v", v, n_heads, rows), ("tail_k", tail_k, n_local, keep),
+                          ("tail_v", tail_v, n_local, keep), ("pool_k", pool_k, n_long, None),
+                          ("pool_v", pool_v, n_long, None)):
+        if t is None:
+            continue
+        if t.dim() != 3 or t.shape[0] != h or t.shape[2] != d or (r is not None and t.shape[1] < r) \
+                or t.dtype != k.dtype or t.device != k.device:
+            raise ValueError(f"{name}: must be a {k.dtype} tensor [{h}, >= {r or 1}, {d}] on {k.device} "
+                             f"(got {tuple(t.shape)}, {t.dtype}, {t.device})")
     for a, b in ((k, v), (tail_k, tail_v), (pool_k, pool_v)):
         if a is not None and (b is None or a.stride() != b.stride() or a.stride(-1) != 1):
             raise ValueError("k/v, tail_k/tail_v and pool_k/pool_v pairs need equal strides, "

@@ -275,6 +275,29 @@ def test_decode_binding_rejects_mismatched_tensors():
                                               lse=t["lse"])
 
 
+def test_carry_binding_rejects_mismatched_tensors():
+    # checked in the binding before the C call (CPU tensors: no device is touched)
+    import torch
+    H, nl, P, S, M, cap, d = 4, 2, 16, 32, 16, 128, 64
+    bf = torch.bfloat16
+    good = dict(k=torch.zeros(H, P + S, d, dtype=bf), v=torch.zeros(H, P + S, d, dtype=bf),
+                tail_k=torch.zeros(nl, M, d, dtype=bf), tail_v=torch.zeros(nl, M, d, dtype=bf),
+                pool_k=torch.zeros(H - nl, cap, d, dtype=bf), pool_v=torch.zeros(H - nl, cap, d, dtype=bf))
+    bad = [dict(k=torch.zeros(H, P + S - 1, d, dtype=bf), v=torch.zeros(H, P + S - 1, d, dtype=bf)),
+           dict(v=torch.zeros(H, P + S, d)),
+           dict(tail_k=torch.zeros(nl, M - 1, d, dtype=bf), tail_v=torch.zeros(nl, M - 1, d, dtype=bf)),
+           dict(tail_k=torch.zeros(nl + 1, M, d, dtype=bf), tail_v=torch.zeros(nl + 1, M, d, dtype=bf)),
+           dict(pool_k=torch.zeros(H - nl, cap, d + 8, dtype=bf), pool_v=torch.zeros(H - nl, cap, d + 8, dtype=bf)),
+           dict(pool_v=torch.zeros(H - nl, cap, d, dtype=torch.float16)),
+           dict(pool_v=torch.zeros(H - nl, d, cap, dtype=bf).transpose(1, 2))]
+    for case in bad:
+        t = dict(good)
+        t.update(case)
+        with pytest.raises(ValueError):
+            sa.sparse_attn_segment_carry(t["k"], t["v"], nl, P, S, M, t["tail_k"], t["tail_v"], t["pool_k"],
+                                         t["pool_v"], 0)
+
+
 def test_import_fails_loudly_without_library(tmp_path):
     # a copy of the binding next to no library must refuse to import
     pkg = tmp_path / "sa_copy"
