@@ -1197,6 +1197,26 @@ def test_topk_repeat_and_canary(sa):
     np.testing.assert_array_equal(outs[0][0][1].cpu().numpy(), ri)
 
 
+def test_topk_workspace_offset(sa):
+    """The C ABI asks only 8-byte alignment of the top-k workspace; the
+    launcher rounds up to its sections' 256-byte boundaries inside it."""
+    H, n, d, k = 2, 3000, 64, 77
+    q, kp, vp = W.make_pool_inputs(H, n, d, 840, torch.float32)
+    need = sa.sa_topk_workspace_bytes(H, n)
+    buf = torch.zeros(need + 8, dtype=torch.uint8, device="cuda")
+    ws = buf[8:]  # 8 bytes past a 256-byte boundary
+    assert ws.data_ptr() % 256 == 8
+    idx = torch.empty((H, k), dtype=torch.int32, device="cuda")
+    score = torch.empty((H, k), dtype=torch.float64, device="cuda")
+    sa.topk_retrieve(q.cuda(), kp.cuda(), k, idx, ws, score=score)
+    torch.cuda.synchronize()
+    for h in range(H):
+        s_ = O.topk_scores(q[h].double().numpy(), kp[h].double().numpy())
+        ri = O.topk_select(s_, k)
+        np.testing.assert_array_equal(idx[h].cpu().numpy(), ri)
+        np.testing.assert_array_equal(score[h].cpu().numpy(), s_[ri])
+
+
 @pytest.mark.parametrize("kind", ["sepllm", "lambda"])
 def test_decode_repeat_and_canary(sa, kind):
     from structured_sparse_attention_attn_amd.pipeline import StreamDecoder
