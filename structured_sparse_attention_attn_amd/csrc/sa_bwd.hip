@@ -32,7 +32,12 @@
 //                  vector ALU in fp32 (query-major per tile; key-major per
 //                  64-key unit), a thread per 32-element slice of a row.
 //   bwd_finish     per row: the inverse rotations, the separator and capped
-//                  contributions, the output dtype.
+//                  contributions, the output dtype.  After the MFMA kernels
+//                  only the dk, dv rows with a separator or capped
+//                  contribution are left to it: those kernels write every
+//                  other row in its final form (inverse rotation and bf16 in
+//                  their epilogues), so the fp32 sums of those rows never go
+//                  through memory.
 #include <type_traits>
 
 #include "sa_common.h"
@@ -79,7 +84,92 @@ struct BwdArgs {
   int alibi;
   float alibi_e;
   int n_sep_chunks, n_cap_blocks;  // group counts of the key-major kernel
+  // bf16 MFMA kernels: the final gradients are written in place by the
+  // kernel that owns the row (every dq row; every dk, dv row that takes no
+  // separator or capped contribution), and the finishing pass handles only
+  // the rows that do
+  int fuse;
+  int rot;             // rotary frame on (inverse rotations in the epilogues)
+  int q_pos0;          // position of query 0 (the prefix length of a segment)
+  void* dq_out;
+  int64_t dqB, dqH, dqT;
+  void* dk_out;
+  int64_t dkB, dkH, dkT;
+  void* dv_out;
+  int64_t dvB, dvH, dvT;
+  const int* blk_sep;  // separators (j >= g0) before each key block
+  int g0;
+  double th1, th4, th8;  // theta_1 = base^(-2/d) and its 4th and 8th powers (theta_c = theta_1^c)
 };
+
+// True when key row j takes a contribution from outside its dense key group:
+// a gathered separator (j >= g0, marked, within the gathered rows) or an
+// LM-Infinite capped key (j < n_cap, n_cap = 0 without capped pairs).  The
+// key-major kernel and the finishing pass decide it with this one test.
+__device__ inline bool key_row_special(const unsigned long long* sep_bits, const int* blk_sep, int g0,
+                                       int64_t sep_rows, bool has_sep, int n_cap, int j) {
+  if (j < n_cap) return true;
+  if (has_sep && j >= g0) {
+    const int blk = j / BK, r = j - blk * BK;
+    const unsigned long long word = sep_bits[blk];
+    if ((word >> r) & 1ull) {
+      const int64_t rank = blk_sep[blk] + __popcll(word & ((r == 0) ? 0ull : (~0ull >> (64 - r))));
+      return rank < sep_rows;
+    }
+  }
+  return false;
+}
+
+// cos and sin of pos * theta with tt = theta / (2 pi): the angle reduced in
+// fp64 to a fraction of a turn, the hardware cosine and sine taking turns.
+__device__ inline void turn_sc(double pos, double tt, float& c, float& s) {
+  const double rev = pos * tt;
+  const float f = (float)(rev - rint(rev));
+  c = __builtin_amdgcn_cosf(f);
+  s = __builtin_amdgcn_sinf(f);
+}
+
+// Rotates a lane's d = 128 accumulator pairs (dim c, c + 64) by pos * theta_c
+// and multiplies them by f.  Lane half hl holds dims 32 dm + 8 g + 4 hl + e in
+// register 4 g + e of acc[dm], so the partner of dm < 2 is dm + 2 in the same
+// register.  theta_c / (2 pi) comes from products of powers of theta_1 in fp64
+// (a few ulp from the direct power).
+__device__ inline void rotate_acc128(const BwdArgs& p, int hl, double pos, float f, f32x16 (&acc)[4]) {
+  double tk = (hl ? p.th4 : 1.0) * 0.15915494309189535;  // theta_{4 hl} / (2 pi)
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {  // dims 8 k + 4 hl + e: dm = k / 4, g = k % 4
+    const int dm = k >> 2, g = k & 3;
+    double tt = tk;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float c, s;
+      turn_sc(pos, tt, c, s);
+      tt *= p.th1;
+      const float x1 = acc[dm][4 * g + e], x2 = acc[dm + 2][4 * g + e];
+      acc[dm][4 * g + e] = (x1 * c - x2 * s) * f;
+      acc[dm + 2][4 * g + e] = (x2 * c + x1 * s) * f;
+    }
+    tk *= p.th8;
+    __builtin_amdgcn_sched_barrier(0);  // one group at a time: few live temporaries
+  }
+}
+
+// Writes a lane's d = 128 row (layout as in rotate_acc128) as bf16, rounded
+// to nearest even.
+__device__ inline void store_row_bf16(char* row, int hl, const f32x16 (&acc)[4]) {
+#pragma unroll
+  for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d0 = 32 * dm + 8 * g + 4 * hl;
+      const f32x2 x01 = {acc[dm][4 * g], acc[dm][4 * g + 1]};
+      const f32x2 x23 = {acc[dm][4 * g + 2], acc[dm][4 * g + 3]};
+      uint2 w;
+      w.x = __builtin_bit_cast(unsigned, __builtin_convertvector(x01, bf16x2));
+      w.y = __builtin_bit_cast(unsigned, __builtin_convertvector(x23, bf16x2));
+      *reinterpret_cast<uint2*>(row + d0 * 2) = w;
+    }
+}
 
 // ---------------------------------------------------------------------------
 // D_i = <dO_i, O_i>: d * esz / 16 consecutive lanes per row (16 for bf16
@@ -324,6 +414,38 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
   }
   if (u < n_units) step(u, K0, V0, K1, V1);
 
+  if (p.fuse) {
+    // the final row: dq = scale R(-pos) sum + the capped part, which this
+    // lane stored to dq_cap (raw frame, times ln 2) when the capped units
+    // ended (only capped units: that part is still in acc), bf16
+    if (!qok) return;
+    if (p.use_cap && tu.n_capu == n_units && n_units > 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] *= LN2;
+    } else {
+      if (p.rot) {
+        rotate_acc128(p, hl, -(double)(p.q_pos0 + qi), p.scale, acc);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] *= p.scale;
+      }
+      if (p.use_cap && tu.n_capu > 0) {
+        const float* cr = p.dq_cap + rowi * D128;
+#pragma unroll
+        for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const float4 x = *reinterpret_cast<const float4*>(cr + 32 * dm + 8 * g + 4 * hl);
+            acc[dm][4 * g] += x.x;
+            acc[dm][4 * g + 1] += x.y;
+            acc[dm][4 * g + 2] += x.z;
+            acc[dm][4 * g + 3] += x.w;
+          }
+      }
+    }
+    store_row_bf16(static_cast<char*>(p.dq_out) + (b * p.dqB + hq * p.dqH + (int64_t)qi * p.dqT) * 2, hl, acc);
+    return;
+  }
   if (p.use_cap) {
     if (tu.n_capu == n_units && n_units > 0) {
       store_acc(p.dq_cap, LN2);
@@ -791,26 +913,39 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p) {
   }
   __syncthreads();
   if (qw == 0 && kslot64 < mu.valid) {
-    float* krow = mu.dk_out + (int64_t)kslot64 * D128;
-    float* vrow_o = mu.dv_out + (int64_t)kslot64 * D128;
 #pragma unroll
     for (int dm = 0; dm < 4; ++dm)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dm + 8 * g + 4 * hl;
-        const int r0 = dm * 16 + 4 * g;
-        float4 kx, vx;
-        kx.x = dka[dm][4 * g] + redk[(r0) * 64 + lane];
-        kx.y = dka[dm][4 * g + 1] + redk[(r0 + 1) * 64 + lane];
-        kx.z = dka[dm][4 * g + 2] + redk[(r0 + 2) * 64 + lane];
-        kx.w = dka[dm][4 * g + 3] + redk[(r0 + 3) * 64 + lane];
-        vx.x = dva[dm][4 * g] + redv[(r0) * 64 + lane];
-        vx.y = dva[dm][4 * g + 1] + redv[(r0 + 1) * 64 + lane];
-        vx.z = dva[dm][4 * g + 2] + redv[(r0 + 2) * 64 + lane];
-        vx.w = dva[dm][4 * g + 3] + redv[(r0 + 3) * 64 + lane];
-        *reinterpret_cast<float4*>(krow + d0) = kx;
-        *reinterpret_cast<float4*>(vrow_o + d0) = vx;
+      for (int r = 0; r < 16; ++r) {
+        dka[dm][r] += redk[(dm * 16 + r) * 64 + lane];
+        dva[dm][r] += redv[(dm * 16 + r) * 64 + lane];
       }
+    if (p.fuse && kind == G_DENSE &&
+        !key_row_special(p.sep_bits, p.blk_sep, p.g0, p.sep_rows, p.gather != 0, p.use_cap ? p.n_cap : 0, j)) {
+      // no contribution from another group: the final rows, dv = sum and
+      // dk = R(-j) ln 2 sum (the queries carry scale * log2(e)), bf16
+      store_row_bf16(static_cast<char*>(p.dv_out) + (b * p.dvB + kvh * p.dvH + (int64_t)j * p.dvT) * 2, hl, dva);
+      if (p.rot) {
+        rotate_acc128(p, hl, -(double)j, LN2, dka);
+      } else {
+#pragma unroll
+        for (int dm = 0; dm < 4; ++dm) dka[dm] *= LN2;
+      }
+      store_row_bf16(static_cast<char*>(p.dk_out) + (b * p.dkB + kvh * p.dkH + (int64_t)j * p.dkT) * 2, hl, dka);
+    } else {
+      float* krow = mu.dk_out + (int64_t)kslot64 * D128;
+      float* vrow_o = mu.dv_out + (int64_t)kslot64 * D128;
+#pragma unroll
+      for (int dm = 0; dm < 4; ++dm)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = 32 * dm + 8 * g + 4 * hl;
+          *reinterpret_cast<float4*>(krow + d0) =
+              make_float4(dka[dm][4 * g], dka[dm][4 * g + 1], dka[dm][4 * g + 2], dka[dm][4 * g + 3]);
+          *reinterpret_cast<float4*>(vrow_o + d0) =
+              make_float4(dva[dm][4 * g], dva[dm][4 * g + 1], dva[dm][4 * g + 2], dva[dm][4 * g + 3]);
+        }
+    }
   }
 }
 
@@ -1163,6 +1298,8 @@ struct FinishArgs {
   const unsigned long long* sep_bits;
   const int* blk_sep;
   int g0;
+  int special_only;      // dk, dv: only rows with a separator or capped contribution
+  int scan_n;            // rows visited per head: n, or the leading n_cap
   ThetaTable theta;
 };
 
@@ -1185,13 +1322,17 @@ __device__ inline unsigned short to_bf16(float f) {  // round to nearest even (f
 __global__ __launch_bounds__(256) void bwd_finish(FinishArgs p) {
   const int tpr = p.d / 16;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / tpr;
-  if (row >= (int64_t)p.B * p.h * p.n) return;
+  const int64_t vis = gid / tpr;
+  if (vis >= (int64_t)p.B * p.h * p.scan_n) return;
   const int c0 = (int)(gid % tpr) * 8;
   const int half = p.d / 2;
-  const int i = (int)(row % p.n);
-  const int64_t bh = row / p.n;
+  const int i = (int)(vis % p.scan_n);
+  const int64_t bh = vis / p.scan_n;
+  const int64_t row = bh * p.n + i;
   const int h = (int)(bh % p.h), b = (int)(bh / p.h);
+  if (p.special_only &&
+      !key_row_special(p.sep_bits, p.blk_sep, p.g0, p.sep_rows, p.sep != nullptr, p.cap != nullptr ? p.n_cap : 0, i))
+    return;
   const float* a = p.acc + row * p.d;
   float x1[8], x2[8];
 #pragma unroll
@@ -1347,6 +1488,23 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   p.n_sep_chunks = p.gather ? (int)(ro.sep_rows / BK) : 0;
   p.n_cap_blocks = p.use_cap ? (int)ceil_div(ro.n_cap, BK) : 0;
   const bool valu = f32 || a.d != 128;  // the MFMA kernels are bf16 with d = 128
+  // the MFMA kernels write the final rows themselves (see BwdArgs::fuse)
+  p.fuse = valu ? 0 : 1;
+  p.rot = rope ? 1 : 0;
+  p.q_pos0 = m.kind == SA_MASK_SEGMENT ? m.prefix_len : 0;
+  p.dq_out = g.dq;
+  p.dqB = g.dq_stride[0]; p.dqH = g.dq_stride[1]; p.dqT = g.dq_stride[2];
+  p.dk_out = g.dk;
+  p.dkB = g.dk_stride[0]; p.dkH = g.dk_stride[1]; p.dkT = g.dk_stride[2];
+  p.dv_out = g.dv;
+  p.dvB = g.dv_stride[0]; p.dvH = g.dv_stride[1]; p.dvT = g.dv_stride[2];
+  p.blk_sep = reinterpret_cast<const int*>(pb + lay.off_blk_sep);
+  p.g0 = lay.g0;
+  if (rope) {
+    p.th1 = theta.th[1];
+    p.th4 = theta.th[4];
+    p.th8 = theta.th[8];
+  }
   if (valu) {
     const unsigned gq = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
     const int64_t units = (int64_t)p.n_sep_chunks + p.n_cap_blocks + lay.n_blocks;
@@ -1375,8 +1533,10 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
     if (alibi) hipLaunchKernelGGL(bwd_dkdv_bf16<true>, dim3(grid), dim3(512), 0, s, p);
     else hipLaunchKernelGGL(bwd_dkdv_bf16<false>, dim3(grid), dim3(512), 0, s, p);
   }
-  // 4. finish: dq, dk, dv
+  // 4. finish: dq, dk, dv (after the MFMA kernels: only the dk, dv rows with
+  // a separator or capped contribution)
   for (int which = 0; which < 3; ++which) {
+    if (p.fuse && (which == 0 || (!p.gather && !p.use_cap))) continue;
     FinishArgs f;
     memset(&f, 0, sizeof(f));
     f.which = which;
@@ -1417,7 +1577,11 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
       f.acc_scale = which == 1 ? (f32 ? a.scale : LN2) : 1.f;
       f.cap_scale = which == 1 ? a.scale : 1.f;
     }
-    const int64_t threads = (int64_t)f.B * f.h * f.n * (a.d / 16);
+    f.special_only = p.fuse;
+    f.scan_n = f.n;
+    if (p.fuse && !p.gather) f.scan_n = (int)std::min<int64_t>(ro.n_cap, f.n);  // only capped rows
+    const int64_t threads = (int64_t)f.B * f.h * f.scan_n * (a.d / 16);
+    if (threads == 0) continue;
     hipLaunchKernelGGL(bwd_finish, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s, f);
   }
   return hipGetLastError();
