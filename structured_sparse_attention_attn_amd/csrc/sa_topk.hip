@@ -355,8 +355,8 @@ __global__ __launch_bounds__(PICK_THREADS) void topk_pick(PickArgs a) {
     find_bin(k, true);
     low = sh_bin;
   }
-  // 2. the keys in buckets >= low: listed in index order (up to LIST_CAP),
-  //    then their buckets counted
+  // 2. the keys in buckets >= low: listed (up to LIST_CAP) with their
+  //    buckets, and every one of them counted in the histogram
   const unsigned low2 = (unsigned)low * 0x10001u;
   int n_list = 0;
   for (int base = 0; base < n; base += BR * 8 * PICK_THREADS) {
@@ -375,43 +375,26 @@ __global__ __launch_bounds__(PICK_THREADS) void topk_pick(PickArgs a) {
     }
     int tot;
     int pos = n_list + scan(__popc(hit), &tot);
-    for (; hit != 0u; hit &= hit - 1u) {
-      const int e = __ffs(hit) - 1;
-      if (pos < LIST_CAP) lj[pos] = base + 8 * (tid + PICK_THREADS * (e >> 3)) + (e & 7);
-      ++pos;
+#pragma unroll
+    for (int r = 0; r < BR; ++r) {
+      const unsigned w[4] = {bv[r].x, bv[r].y, bv[r].z, bv[r].w};
+      for (unsigned hr = (hit >> (8 * r)) & 0xFFu; hr != 0u; hr &= hr - 1u) {
+        const int e = __ffs(hr) - 1;  // element e of piece r
+        const unsigned wq = e < 2 ? w[0] : e < 4 ? w[1] : e < 6 ? w[2] : w[3];
+        const int bkt = (int)((wq >> (16 * (e & 1))) & 0xFFFFu);
+        atomicAdd(&hist[hbin(bkt)], 1);
+        if (pos < LIST_CAP) {
+          lj[pos] = base + 8 * (tid + PICK_THREADS * r) + e;
+          lb[pos] = (unsigned short)bkt;
+        }
+        ++pos;
+      }
     }
     n_list += tot;
   }
   __syncthreads();
   const bool listed = n_list <= LIST_CAP;
   constexpr int LPT = LIST_CAP / PICK_THREADS;
-  unsigned long long kv[LPT];  // keys of this thread's list entries
-  if (listed) {
-    int bb[LPT];
-#pragma unroll
-    for (int r = 0; r < LPT; ++r) {
-      const int i = tid + PICK_THREADS * r;
-      const int j = i < n_list ? lj[i] : 0;
-      kv[r] = keys[j];
-      bb[r] = bks[j];
-    }
-#pragma unroll
-    for (int r = 0; r < LPT; ++r) {
-      const int i = tid + PICK_THREADS * r;
-      if (i < n_list) {
-        atomicAdd(&hist[hbin(bb[r])], 1);
-        lb[i] = (unsigned short)bb[r];
-      }
-    }
-  } else {
-    visit([&](int j0, const unsigned* w, const unsigned* vm) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        for (unsigned m = ge2(w[q], low2) & vm[q]; m != 0u; m &= m - 1u)
-          atomicAdd(&hist[hbin((int)((w[q] >> (16 * ((__ffs(m) - 1) >> 4))) & 0xFFFFu))], 1);
-    });
-  }
-  __syncthreads();
   find_bin(k, false);
   int bsel = sh_bin;
   const int need = sh_need, cnt = sh_cnt;
@@ -430,7 +413,7 @@ __global__ __launch_bounds__(PICK_THREADS) void topk_pick(PickArgs a) {
           if (b == bsel) {
             const int c = atomicAdd(&sh_count, 1);
             cidx[c] = j;
-            ckey[c] = kv[r];
+            ckey[c] = keys[j];
           }
         }
       }
