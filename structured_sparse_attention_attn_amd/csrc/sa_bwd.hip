@@ -84,18 +84,21 @@ struct BwdArgs {
   int alibi;
   float alibi_e;
   int n_sep_chunks, n_cap_blocks;  // group counts of the key-major kernel
-  // bf16 MFMA kernels: the final gradients are written in place by the
-  // kernel that owns the row (every dq row; every dk, dv row that takes no
-  // separator or capped contribution), and the finishing pass handles only
-  // the rows that do
-  int fuse;
+};
+
+// The bf16 MFMA kernels' outputs: the final gradients are written in place by
+// the kernel that owns the row (every dq row; every dk, dv row that takes no
+// separator or capped contribution), and the finishing pass handles only the
+// rows that do.  (A separate argument: the vector-ALU kernels keep BwdArgs
+// alone, whose size steers their register allocation.)
+struct BwdOut {
   int rot;             // rotary frame on (inverse rotations in the epilogues)
   int q_pos0;          // position of query 0 (the prefix length of a segment)
-  void* dq_out;
+  void* dq;
   int64_t dqB, dqH, dqT;
-  void* dk_out;
+  void* dk;
   int64_t dkB, dkH, dkT;
-  void* dv_out;
+  void* dv;
   int64_t dvB, dvH, dvT;
   const int* blk_sep;  // separators (j >= g0) before each key block
   int g0;
@@ -134,7 +137,7 @@ __device__ inline void turn_sc(double pos, double tt, float& c, float& s) {
 // register 4 g + e of acc[dm], so the partner of dm < 2 is dm + 2 in the same
 // register.  theta_c / (2 pi) comes from products of powers of theta_1 in fp64
 // (a few ulp from the direct power).
-__device__ inline void rotate_acc128(const BwdArgs& p, int hl, double pos, float f, f32x16 (&acc)[4]) {
+__device__ inline void rotate_acc128(const BwdOut& p, int hl, double pos, float f, f32x16 (&acc)[4]) {
   double tk = (hl ? p.th4 : 1.0) * 0.15915494309189535;  // theta_{4 hl} / (2 pi)
 #pragma unroll
   for (int k = 0; k < 8; ++k) {  // dims 8 k + 4 hl + e: dm = k / 4, g = k % 4
@@ -239,7 +242,7 @@ __device__ inline void pack_tile(const f32x16& s, bf16x8 (&pb)[2]) {
 // ===========================================================================
 
 template <bool ALIBI>
-__global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
+__global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p, BwdOut fo) {
   // K and V of the current unit and of the next one (separate arrays, so a
   // read of one slot never waits for the loads into the other)
   __shared__ __attribute__((aligned(16))) char K0[BLK_BYTES];
@@ -414,7 +417,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
   }
   if (u < n_units) step(u, K0, V0, K1, V1);
 
-  if (p.fuse) {
+  {
     // the final row: dq = scale R(-pos) sum + the capped part, which this
     // lane stored to dq_cap (raw frame, times ln 2) when the capped units
     // ended (only capped units: that part is still in acc), bf16
@@ -423,8 +426,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] *= LN2;
     } else {
-      if (p.rot) {
-        rotate_acc128(p, hl, -(double)(p.q_pos0 + qi), p.scale, acc);
+      if (fo.rot) {
+        rotate_acc128(fo, hl, -(double)(fo.q_pos0 + qi), p.scale, acc);
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] *= p.scale;
@@ -443,24 +446,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_bf16(BwdArgs p) {
           }
       }
     }
-    store_row_bf16(static_cast<char*>(p.dq_out) + (b * p.dqB + hq * p.dqH + (int64_t)qi * p.dqT) * 2, hl, acc);
-    return;
+    store_row_bf16(static_cast<char*>(fo.dq) + (b * fo.dqB + hq * fo.dqH + (int64_t)qi * fo.dqT) * 2, hl, acc);
   }
-  if (p.use_cap) {
-    if (tu.n_capu == n_units && n_units > 0) {
-      store_acc(p.dq_cap, LN2);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
-    } else if (tu.n_capu == 0) {
-      f32x16 keep[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { keep[i] = acc[i]; acc[i] = f32x16{}; }
-      store_acc(p.dq_cap, 0.f);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = keep[i];
-    }
-  }
-  store_acc(p.dq_acc, p.scale);
 }
 
 // ===========================================================================
@@ -563,7 +550,7 @@ struct KeyUnit {
 };
 
 template <bool ALIBI>
-__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p, BwdOut fo) {
   // the group's 128 keys and values; two buffers of (64 queries, their dO rows,
   // their lse * log2(e) and D), one filled while the other is read
   __shared__ __attribute__((aligned(16))) char Kg[2 * BLK_BYTES];
@@ -920,18 +907,18 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p) {
         dka[dm][r] += redk[(dm * 16 + r) * 64 + lane];
         dva[dm][r] += redv[(dm * 16 + r) * 64 + lane];
       }
-    if (p.fuse && kind == G_DENSE &&
-        !key_row_special(p.sep_bits, p.blk_sep, p.g0, p.sep_rows, p.gather != 0, p.use_cap ? p.n_cap : 0, j)) {
+    if (kind == G_DENSE &&
+        !key_row_special(p.sep_bits, fo.blk_sep, fo.g0, p.sep_rows, p.gather != 0, p.use_cap ? p.n_cap : 0, j)) {
       // no contribution from another group: the final rows, dv = sum and
       // dk = R(-j) ln 2 sum (the queries carry scale * log2(e)), bf16
-      store_row_bf16(static_cast<char*>(p.dv_out) + (b * p.dvB + kvh * p.dvH + (int64_t)j * p.dvT) * 2, hl, dva);
-      if (p.rot) {
-        rotate_acc128(p, hl, -(double)j, LN2, dka);
+      store_row_bf16(static_cast<char*>(fo.dv) + (b * fo.dvB + kvh * fo.dvH + (int64_t)j * fo.dvT) * 2, hl, dva);
+      if (fo.rot) {
+        rotate_acc128(fo, hl, -(double)j, LN2, dka);
       } else {
 #pragma unroll
         for (int dm = 0; dm < 4; ++dm) dka[dm] *= LN2;
       }
-      store_row_bf16(static_cast<char*>(p.dk_out) + (b * p.dkB + kvh * p.dkH + (int64_t)j * p.dkT) * 2, hl, dka);
+      store_row_bf16(static_cast<char*>(fo.dk) + (b * fo.dkB + kvh * fo.dkH + (int64_t)j * fo.dkT) * 2, hl, dka);
     } else {
       float* krow = mu.dk_out + (int64_t)kslot64 * D128;
       float* vrow_o = mu.dv_out + (int64_t)kslot64 * D128;
@@ -1488,22 +1475,24 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   p.n_sep_chunks = p.gather ? (int)(ro.sep_rows / BK) : 0;
   p.n_cap_blocks = p.use_cap ? (int)ceil_div(ro.n_cap, BK) : 0;
   const bool valu = f32 || a.d != 128;  // the MFMA kernels are bf16 with d = 128
-  // the MFMA kernels write the final rows themselves (see BwdArgs::fuse)
-  p.fuse = valu ? 0 : 1;
-  p.rot = rope ? 1 : 0;
-  p.q_pos0 = m.kind == SA_MASK_SEGMENT ? m.prefix_len : 0;
-  p.dq_out = g.dq;
-  p.dqB = g.dq_stride[0]; p.dqH = g.dq_stride[1]; p.dqT = g.dq_stride[2];
-  p.dk_out = g.dk;
-  p.dkB = g.dk_stride[0]; p.dkH = g.dk_stride[1]; p.dkT = g.dk_stride[2];
-  p.dv_out = g.dv;
-  p.dvB = g.dv_stride[0]; p.dvH = g.dv_stride[1]; p.dvT = g.dv_stride[2];
-  p.blk_sep = reinterpret_cast<const int*>(pb + lay.off_blk_sep);
-  p.g0 = lay.g0;
+  // the MFMA kernels write the final rows themselves (see BwdOut)
+  const bool fuse = !valu;
+  BwdOut fo;
+  memset(&fo, 0, sizeof(fo));
+  fo.rot = rope ? 1 : 0;
+  fo.q_pos0 = m.kind == SA_MASK_SEGMENT ? m.prefix_len : 0;
+  fo.dq = g.dq;
+  fo.dqB = g.dq_stride[0]; fo.dqH = g.dq_stride[1]; fo.dqT = g.dq_stride[2];
+  fo.dk = g.dk;
+  fo.dkB = g.dk_stride[0]; fo.dkH = g.dk_stride[1]; fo.dkT = g.dk_stride[2];
+  fo.dv = g.dv;
+  fo.dvB = g.dv_stride[0]; fo.dvH = g.dv_stride[1]; fo.dvT = g.dv_stride[2];
+  fo.blk_sep = reinterpret_cast<const int*>(pb + lay.off_blk_sep);
+  fo.g0 = lay.g0;
   if (rope) {
-    p.th1 = theta.th[1];
-    p.th4 = theta.th[4];
-    p.th8 = theta.th[8];
+    fo.th1 = theta.th[1];
+    fo.th4 = theta.th[4];
+    fo.th8 = theta.th[8];
   }
   if (valu) {
     const unsigned gq = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
@@ -1523,20 +1512,20 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
   // 2. dQ (query-major)
   if (!valu) {
     const unsigned grid = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
-    if (alibi) hipLaunchKernelGGL(bwd_dq_bf16<true>, dim3(grid), dim3(256), 0, s, p);
-    else hipLaunchKernelGGL(bwd_dq_bf16<false>, dim3(grid), dim3(256), 0, s, p);
+    if (alibi) hipLaunchKernelGGL(bwd_dq_bf16<true>, dim3(grid), dim3(256), 0, s, p, fo);
+    else hipLaunchKernelGGL(bwd_dq_bf16<false>, dim3(grid), dim3(256), 0, s, p, fo);
   }
   // 3. dK, dV (key-major): separator chunks, then capped blocks, then dense blocks
   if (!valu) {
     const int64_t groups = (int64_t)(p.n_sep_chunks + 1) / 2 + (p.n_cap_blocks + 1) / 2 + (lay.n_blocks + 1) / 2;
     const unsigned grid = (unsigned)(groups * a.batch * a.h_kv);
-    if (alibi) hipLaunchKernelGGL(bwd_dkdv_bf16<true>, dim3(grid), dim3(512), 0, s, p);
-    else hipLaunchKernelGGL(bwd_dkdv_bf16<false>, dim3(grid), dim3(512), 0, s, p);
+    if (alibi) hipLaunchKernelGGL(bwd_dkdv_bf16<true>, dim3(grid), dim3(512), 0, s, p, fo);
+    else hipLaunchKernelGGL(bwd_dkdv_bf16<false>, dim3(grid), dim3(512), 0, s, p, fo);
   }
   // 4. finish: dq, dk, dv (after the MFMA kernels: only the dk, dv rows with
   // a separator or capped contribution)
   for (int which = 0; which < 3; ++which) {
-    if (p.fuse && (which == 0 || (!p.gather && !p.use_cap))) continue;
+    if (fuse && (which == 0 || (!p.gather && !p.use_cap))) continue;
     FinishArgs f;
     memset(&f, 0, sizeof(f));
     f.which = which;
@@ -1577,9 +1566,9 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
       f.acc_scale = which == 1 ? (f32 ? a.scale : LN2) : 1.f;
       f.cap_scale = which == 1 ? a.scale : 1.f;
     }
-    f.special_only = p.fuse;
+    f.special_only = fuse ? 1 : 0;
     f.scan_n = f.n;
-    if (p.fuse && !p.gather) f.scan_n = (int)std::min<int64_t>(ro.n_cap, f.n);  // only capped rows
+    if (fuse && !p.gather) f.scan_n = (int)std::min<int64_t>(ro.n_cap, f.n);  // only capped rows
     const int64_t threads = (int64_t)f.B * f.h * f.scan_n * (a.d / 16);
     if (threads == 0) continue;
     hipLaunchKernelGGL(bwd_finish, dim3((unsigned)ceil_div(threads, 256)), dim3(256), 0, s, f);
