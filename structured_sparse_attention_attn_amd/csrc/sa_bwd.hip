@@ -760,11 +760,44 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p, BwdOut fo) {
     return c;
   };
 
+  // A gathered separator chunk is read by every tile from t0 on.  Those
+  // groups walk their tiles last to first: the separator groups of a kv head
+  // that run together on one XCD all start at the last tile, so they read
+  // each tile's Q and dO rows at about the same time, while the rows are in
+  // that XCD's L2 (walking first to last, each would stream its own range).
+  const bool back = kind == G_SEP;
+  // last tile at or before t that reads the group (t = n_tiles when none)
+  auto tile_back = [&](int t) -> Cur {
+    Cur c{p.n_tiles, 0, 0, -1, -1, 0, 0};
+    for (; t >= t0; --t) {
+      int m0, m1, c0, c1;
+      if (use_tab) {
+        const int v = __builtin_amdgcn_readfirstlane(tinfo[t - t0]);
+        m0 = (v & 0xF) == 0xF ? -1 : (v & 0xF);
+        m1 = ((v >> 4) & 0xF) == 0xF ? -1 : ((v >> 4) & 0xF);
+        c0 = (v >> 8) & 0xFF;
+        c1 = (v >> 16) & 0xFF;
+      } else {
+        m0 = unit_mk(0, t, c0);
+        m1 = unit_mk(1, t, c1);
+      }
+      if (m0 >= 0 || m1 >= 0) {
+        c.t = t;
+        c.mk0 = m0;
+        c.mk1 = m1;
+        c.cnt0 = c0;
+        c.cnt1 = c1;
+        return c;
+      }
+    }
+    return c;
+  };
+
   auto advance = [&](Cur c) -> Cur {
     ++c.ch;
     if (c.ch == 2 || c.t * TQ + 64 * c.ch >= p.n_q) {
       c.ch = 0;
-      if (++c.gq == p.group) return tile_from(c.t + 1);
+      if (++c.gq == p.group) return back ? tile_back(c.t - 1) : tile_from(c.t + 1);
     }
     return c;
   };
@@ -861,7 +894,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p, BwdOut fo) {
 
   // chunk loop: wait for chunk c and for every read of the other buffers, start
   // chunk c+1 into them, compute chunk c
-  Cur cur = tile_from(t0);
+  Cur cur = back ? tile_back(p.n_tiles - 1) : tile_from(t0);
   if (cur.t < p.n_tiles) issue(cur, Qb0, Db0, LD0);
   while (cur.t < p.n_tiles) {
     {
