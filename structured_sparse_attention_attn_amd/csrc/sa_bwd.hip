@@ -103,6 +103,7 @@ struct BwdOut {
   const int* blk_sep;  // separators (j >= g0) before each key block
   int g0;
   double th1, th4, th8;  // theta_1 = base^(-2/d) and its 4th and 8th powers (theta_c = theta_1^c)
+  int n_lead;          // leading dense key groups read by every tile (dispatched first)
 };
 
 // True when key row j takes a contribution from outside its dense key group:
@@ -575,9 +576,14 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p, BwdOut fo) {
   const int b = bh / p.h_kv, kvh = bh % p.h_kv;
   const int n_sep_pairs = (p.n_sep_chunks + 1) / 2, n_cap_pairs = (p.n_cap_blocks + 1) / 2;
 
+  // Grid order, longest walks first: the dense groups that every tile reads
+  // (SepLLM's initial tokens; LM-Infinite's starting tokens when no pass caps
+  // them), the gathered-separator chunks, the capped blocks, the other dense
+  // groups.
   int kind, pi;
-  if (gi < n_sep_pairs) { kind = G_SEP; pi = gi; }
-  else if (gi < n_sep_pairs + n_cap_pairs) { kind = G_CAP; pi = gi - n_sep_pairs; }
+  if (gi < fo.n_lead) { kind = G_DENSE; pi = gi; }
+  else if (gi - fo.n_lead < n_sep_pairs) { kind = G_SEP; pi = gi - fo.n_lead; }
+  else if (gi - fo.n_lead < n_sep_pairs + n_cap_pairs) { kind = G_CAP; pi = gi - fo.n_lead - n_sep_pairs; }
   else { kind = G_DENSE; pi = gi - n_sep_pairs - n_cap_pairs; }
 
   // (clamped to the gathered rows: a mask past the plan's sep_max bound)
@@ -760,12 +766,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p, BwdOut fo) {
     return c;
   };
 
-  // A gathered separator chunk is read by every tile from t0 on.  Those
-  // groups walk their tiles last to first: the separator groups of a kv head
-  // that run together on one XCD all start at the last tile, so they read
-  // each tile's Q and dO rows at about the same time, while the rows are in
-  // that XCD's L2 (walking first to last, each would stream its own range).
-  const bool back = kind == G_SEP;
+  // A gathered separator chunk is read by every tile from t0 on, a leading
+  // dense group by every tile.  With separator groups present, those groups
+  // walk their tiles last to first: the ones of a kv head that run together
+  // on one XCD all start at the last tile, so they read each tile's Q and dO
+  // rows at about the same time, while the rows are in that XCD's L2
+  // (walking first to last, each would stream its own range).  Without them
+  // a leading group walks first to last, in step with the dense groups that
+  // follow it, which read the first tiles too.
+  const bool back = kind == G_SEP || (kind == G_DENSE && pi < fo.n_lead && p.gather);
   // last tile at or before t that reads the group (t = n_tiles when none)
   auto tile_back = [&](int t) -> Cur {
     Cur c{p.n_tiles, 0, 0, -1, -1, 0, 0};
@@ -1526,6 +1535,15 @@ hipError_t launch_bwd(const sa_mask_t& m, const sa_plan_header_t& lay, const voi
     fo.th1 = theta.th[1];
     fo.th4 = theta.th[4];
     fo.th8 = theta.th[8];
+  }
+  {
+    // dense key groups (128 keys) that every tile reads: SepLLM's initial
+    // tokens, LM-Infinite's starting tokens when no capped pass takes them
+    int lead_keys = 0;
+    if (m.kind == SA_MASK_SEPLLM) lead_keys = m.a;
+    else if (m.kind == SA_MASK_LAMBDA && !p.use_cap) lead_keys = m.n_starting;
+    const int n_groups = (int)((lay.n_blocks + 1) / 2);
+    fo.n_lead = std::min(n_groups, (int)ceil_div(std::min(lead_keys, m.n_k), 2 * BK));
   }
   if (valu) {
     const unsigned gq = (unsigned)((int64_t)a.batch * a.h_q * lay.n_tiles);
