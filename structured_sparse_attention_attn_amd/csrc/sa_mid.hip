@@ -51,13 +51,14 @@ __global__ __launch_bounds__(256, KMID_MAX <= 16 ? 2 : 1) void mid_select(MidArg
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hl = lane >> 5;
-  // work group -> (batch, query head, tile), tiles from the last (most middle keys)
-  const int U = p.B * p.h_q * p.n_tiles;
+  // work group -> (batch, query head, tile): tiles from the last (most middle
+  // keys) over all heads at once, so the longest tiles of every head start
+  // first and the shortest ones fill the end of the launch
+  const int BH = p.B * p.h_q;
   const int g = blockIdx.x;
-  const int t = p.n_tiles - 1 - g % p.n_tiles;
-  const int bh = g / p.n_tiles;
+  const int t = p.n_tiles - 1 - g / BH;
+  const int bh = g % BH;
   const int hq = bh % p.h_q, b = bh / p.h_q;
-  (void)U;
   const int kvh = hq / p.group;
   const int q0 = t * TQ;
   const int qi = q0 + wid * 32 + l32;
