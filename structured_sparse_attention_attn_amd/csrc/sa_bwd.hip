@@ -901,6 +901,11 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p, BwdOut fo) {
     }
   };
 
+  // The two waves on a SIMD (wave w and w + 4: the same keys, the two query
+  // halves) would run the same phases at the same time; the first half's
+  // wave issues first, so it runs ahead and its softmax meets the other's
+  // products.
+  if (qw == 0) __builtin_amdgcn_s_setprio(2);
   // chunk loop: wait for chunk c and for every read of the other buffers, start
   // chunk c+1 into them, compute chunk c
   Cur cur = back ? tile_back(p.n_tiles - 1) : tile_from(t0);
