@@ -143,13 +143,22 @@ __global__ __launch_bounds__(FIN_THREADS) void plan_finish(PlanArgs p) {
   const int tid = threadIdx.x;
   int total;
   // 1. blk_sep: exclusive prefix of the per-block counts, plus the grand total
+  //    (no separator flags: plan_sep_blocks did not run, every bit and count
+  //    is zero)
   int carry = 0;
-  for (int base = 0; base < p.n_blocks; base += FIN_THREADS) {
-    const int b = base + tid;
-    const int v = b < p.n_blocks ? p.blk_sep[b] : 0;
-    const int ex = block_excl_scan(v, wave_tot, &total);
-    if (b < p.n_blocks) p.blk_sep[b] = carry + ex;
-    carry += total;
+  if (p.sep == nullptr) {
+    for (int b = tid; b < p.n_blocks; b += FIN_THREADS) {
+      p.sep_bits[b] = 0ull;
+      p.blk_sep[b] = 0;
+    }
+  } else {
+    for (int base = 0; base < p.n_blocks; base += FIN_THREADS) {
+      const int b = base + tid;
+      const int v = b < p.n_blocks ? p.blk_sep[b] : 0;
+      const int ex = block_excl_scan(v, wave_tot, &total);
+      if (b < p.n_blocks) p.blk_sep[b] = carry + ex;
+      carry += total;
+    }
   }
   const int n_sep = carry;
   if (tid == 0) p.blk_sep[p.n_blocks] = n_sep;
@@ -244,9 +253,12 @@ hipError_t launch_plan(const sa_mask_t& m, const sa_plan_header_t& lay, void* pl
   p.hdr = reinterpret_cast<sa_plan_header_t*>(base);
   p.lay = lay;
   const unsigned wg = (unsigned)ceil_div(lay.n_blocks, 4);
-  hipLaunchKernelGGL(plan_sep_blocks, dim3(wg), dim3(256), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
+  if (p.sep != nullptr) {  // separator flags to read (otherwise plan_finish zeroes the bits)
+    hipLaunchKernelGGL(plan_sep_blocks, dim3(wg), dim3(256), 0, s, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(plan_finish, dim3(1), dim3(FIN_THREADS), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
