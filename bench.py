@@ -385,13 +385,18 @@ def cpu_baseline(wl, inp, budget_s):
     t0 = time.time()
     _CPU["deadline"] = t0 + budget_s
     pairs = done = 0
-    with mp.get_context("fork").Pool(cores, initializer=_cpu_worker_init) as pool:
+    # Tasks past the deadline return at once, so the queue drains within the
+    # running tasks' time; the pool is then closed and joined without signals
+    # (a profiler's signal handler in the forked workers can keep a terminated
+    # worker from exiting).
+    pool = mp.get_context("fork").Pool(cores, initializer=_cpu_worker_init)
+    try:
         for pr, n in pool.imap_unordered(_cpu_tile, tasks, chunksize=1):
             pairs += pr
             done += n
-            if time.time() > _CPU["deadline"]:
-                break
-        pool.terminate()
+    finally:
+        pool.close()
+        pool.join()
     el = time.time() - t0
     return {"value": 4.0 * wl.d * pairs / el / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "cpu_model": cpu_model(),
