@@ -629,6 +629,9 @@ BWD_SMALL = [
     (W.SEGMENT, dict(m=600, P=200), 10000.0, None),
     (W.SEGMENT, dict(m=129, P=1, h_q=4, h_kv=2), 10000.0, None),
     (W.SEPLLM, dict(m=1, a=4, w=64, p_sep=0.5), 10000.0, None),
+    # initial tokens over two 128-key groups (both dispatched first and walked
+    # last to first with the separator groups), GQA
+    (W.SEPLLM, dict(m=900, a=150, w=64, p_sep=0.15, h_q=4, h_kv=2), 10000.0, None),
 ]
 
 
