@@ -116,7 +116,9 @@ typedef struct {
 /*
  * Forward arguments.  Tensors are [batch, heads, tokens, d] with the last
  * dimension contiguous; *_stride give the element strides of the batch, head
- * and token dimensions.
+ * and token dimensions (the token stride at most 64 MiB in bytes, else
+ * SA_EUNSUPPORTED: the kernels address the rows of a 64-row block with 32-bit
+ * offsets).
  *   dtype       SA_F32 or SA_BF16 for q, k, v and o.
  *   d           head dimension: 64 or 128 (bf16 and f32).
  *   h_q, h_kv   h_q % h_kv == 0; query head h reads kv head h / (h_q/h_kv).

@@ -85,6 +85,9 @@ int check_tensor(const char* name, const void* p, const int64_t st[3], int esz) 
     if (st[i] < 0 || (st[i] * esz) % 16 != 0)
       return fail(SA_EINVAL, "%s stride[%d] = %lld must be >= 0 and a multiple of 16 bytes", name, i,
                   (long long)st[i]);
+  // rows of a 64-row block are addressed with 32-bit byte offsets
+  if (st[2] * esz > (int64_t)1 << 26)
+    return fail(SA_EUNSUPPORTED, "%s token stride = %lld elements exceeds 64 MiB", name, (long long)st[2]);
   return SA_OK;
 }
 

@@ -821,10 +821,9 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_bf16(BwdArgs p, BwdOut fo) {
       dma_block(static_cast<const char*>(p.dout) + (b * p.dsB + hq * p.dsH + (int64_t)qc0 * p.dsT) * 2, p.dsT * 2,
                 qvalid, Dd, wid & 3, lane);
     if (wid == 0 || wid == 4) {
-      const int64_t ri = ((int64_t)b * p.h_q + hq) * p.n_q + qc0 + min(lane, qvalid - 1);
-      const float* src = wid == 0 ? p.lse + ri : p.Dv + ri;
-      __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(LDd[wid >> 2]),
-                                       4, 0, 0);
+      const int64_t r0 = ((int64_t)b * p.h_q + hq) * p.n_q + qc0;
+      const float* src = wid == 0 ? p.lse + r0 : p.Dv + r0;
+      lds_dma<4>(src, (uint32_t)min(lane, qvalid - 1) * 4u, LDd[wid >> 2]);
     }
   };
 

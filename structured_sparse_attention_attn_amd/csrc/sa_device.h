@@ -396,6 +396,25 @@ __device__ inline void add_alibi(const Unit& u, int qi, int hl, float m2, float 
   }
 }
 
+// Direct global -> LDS load of BYTES per lane (4 or 16) from the wave-uniform
+// address base + voff (voff per lane, bytes), written lane after lane from
+// the wave-uniform LDS address lds.  It is issued in the buffer (MUBUF) form
+// with a raw resource over base, not in the global (FLAT) form: while a FLAT
+// instruction that writes LDS is in flight, the compiler cannot count LDS
+// reads one by one and makes every later LDS read wait for all earlier ones
+// (lgkmcnt(0)), which defeats reading MFMA operands ahead.  voff + BYTES must
+// stay below 2^32 (callers keep row strides at most 64 MiB).
+template <int BYTES>
+__device__ __attribute__((always_inline)) inline void lds_dma(const void* base, uint32_t voff, void* lds) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, -1, 0x00020000);
+  static_assert(BYTES == 4 || BYTES == 16, "4 or 16 bytes per lane");
+  if constexpr (BYTES == 16)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+  else
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+}
+
 // Direct global -> LDS loads of a 64-row x 256-byte block into the swizzled
 // layout (16-byte chunk c of row r at chunk c ^ swzf(r & 15)): wave w moves
 // rows 16w .. 16w+15, four rows per instruction, each lane fetching the
@@ -409,8 +428,7 @@ __device__ __attribute__((always_inline)) inline void dma_block(const char* base
   for (int j = 0; j < 4; ++j) {
     const int i = wid * 4 + j;
     const int r = min(4 * i + lrow, valid - 1);
-    __builtin_amdgcn_global_load_lds((const void*)(base + (int64_t)r * stride + ((lchunk ^ j) << 4)),
-                                     (__attribute__((address_space(3))) void*)(lds + i * 1024), 16, 0, 0);
+    lds_dma<16>(base, (uint32_t)(r * (uint32_t)stride) + (uint32_t)((lchunk ^ j) << 4), lds + i * 1024);
   }
 }
 

@@ -232,13 +232,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16(FwdArgs p) {
       for (int j = 0; j < NJ; ++j) {
         const int i = wid * NJ + j;
         const uint32_t o = lo ^ (uint32_t)(j << XSH);
-        const char* kj = u.kbase + j * 1024;
-        const char* vj = u.vbase + j * 1024;
-        __asm__ volatile("" : "+s"(kj), "+s"(vj));  // uniform bases: one scalar add each
-        __builtin_amdgcn_global_load_lds((const void*)(kj + o),
-                                         (__attribute__((address_space(3))) void*)(Kb + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(vj + o),
-                                         (__attribute__((address_space(3))) void*)(Vb + i * 1024), 16, 0, 0);
+        lds_dma<16>(u.kbase, o + (uint32_t)(j * 1024), Kb + i * 1024);
+        lds_dma<16>(u.vbase, o + (uint32_t)(j * 1024), Vb + i * 1024);
       }
       return;
     }
@@ -250,10 +245,8 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16(FwdArgs p) {
       const uint32_t ch = c0 ^ (uint32_t)(j << XSH);
       const int kr = min(r0 + RPI * j, u.kvalid - 1);
       const int vr = min(r0 + RPI * j, u.vvalid - 1);
-      __builtin_amdgcn_global_load_lds((const void*)(u.kbase + (int64_t)kr * u.kstride + ch),
-                                       (__attribute__((address_space(3))) void*)(Kb + i * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void*)(u.vbase + (int64_t)vr * u.vstride + ch),
-                                       (__attribute__((address_space(3))) void*)(Vb + i * 1024), 16, 0, 0);
+      lds_dma<16>(u.kbase, (uint32_t)kr * (uint32_t)u.kstride + ch, Kb + i * 1024);
+      lds_dma<16>(u.vbase, (uint32_t)vr * (uint32_t)u.vstride + ch, Vb + i * 1024);
     }
   };
 

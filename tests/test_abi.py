@@ -176,6 +176,11 @@ def test_fwd_workspace_and_validation():
     bad_stride.v_stride[2] = 100  # 200 bytes: not a multiple of 16
     assert lib.sparse_attn_fwd(ctypes.byref(m), 256, plan_bytes, ctypes.byref(bad_stride), 512, ws,
                                None) == sa.SA_EINVAL
+    # a token stride past 64 MiB: block rows are addressed with 32-bit offsets
+    huge_stride = _args()
+    huge_stride.k_stride[2] = (1 << 25) + 8  # bf16 elements: 64 MiB + 16 bytes
+    assert lib.sparse_attn_fwd(ctypes.byref(m), 256, plan_bytes, ctypes.byref(huge_stride), 512, ws,
+                               None) == sa.SA_EUNSUPPORTED
     assert lib.sparse_attn_fwd(ctypes.byref(m), 256, plan_bytes - 1, ctypes.byref(a), 512, ws,
                                None) == sa.SA_ENOSPACE
     assert lib.sparse_attn_fwd(ctypes.byref(m), 256, plan_bytes, ctypes.byref(a), 512, ws - 1,
