@@ -314,6 +314,21 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16(FwdArgs p) {
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     __syncthreads();
     if (u > 0) pv(pb, vs_prev);
+    const char* Kb = smem + buf * BLKB;
+    // the first three k-steps' K fragments of S(u) are requested before the
+    // next unit's loads are issued (K(u) is visible since this step's
+    // barrier), so their LDS latency passes while those loads go out
+    const char* kl = Kb + l32 * ROWB;
+    auto kfrag = [&](int mb, int ks) {
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + mb * 32 * ROWB + (((2 * ks) ^ kf) << 4)));
+    };
+    bf16x8 a0[3], a1[3];
+    a0[0] = kfrag(0, 0);
+    a1[0] = kfrag(1, 0);
+    a0[1] = kfrag(0, 1);
+    a1[1] = kfrag(1, 1);
+    a0[2] = kfrag(0, 2);
+    a1[2] = kfrag(1, 2);
     Unit nxt;
     if (u + 1 < n_units) {
       nxt = unit(u + 1);
@@ -321,23 +336,11 @@ __global__ __launch_bounds__(256, D == 64 ? 3 : 2) void fwd_bf16(FwdArgs p) {
     }
     vs_prev = vs_prev == 2 ? 0 : vs_prev + 1;
     vs_next = vs_next == 2 ? 0 : vs_next + 1;
-    const char* Kb = smem + buf * BLKB;
 
     // --- S^T = K Q^T - m_ref: both 32-key halves interleaved, K fragments
     //     read two k-steps ahead of their MFMAs ---
     f32x16 s[2];
     {
-      const char* kl = Kb + l32 * ROWB;
-      auto kfrag = [&](int mb, int ks) {
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kl + mb * 32 * ROWB + (((2 * ks) ^ kf) << 4)));
-      };
-      bf16x8 a0[3], a1[3];
-      a0[0] = kfrag(0, 0);
-      a1[0] = kfrag(1, 0);
-      a0[1] = kfrag(0, 1);
-      a1[1] = kfrag(1, 1);
-      a0[2] = kfrag(0, 2);
-      a1[2] = kfrag(1, 2);
       // the first k-step reads -m_ref as C and writes fresh accumulators
       __builtin_amdgcn_s_setprio(1);
       f32x16 c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[0], qf[0], negm, 0, 0, 0);
